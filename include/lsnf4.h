@@ -1,0 +1,254 @@
+/*
+ * lsnf4.h - C ABI of liblsnf4.so: exact layer-streamed NF4 LoRA on MI355X (gfx950).
+ *
+ * The library computes, for one adapted projection of a decoder layer, the per-visit NF4
+ * dequantisation of the frozen base, the frozen-base linear and the rank-r LoRA adapter,
+ * forward and backward, and streams decoder layers through a small pool of device slots
+ * filled from pinned host memory on a separate stream.
+ *
+ * Sources (the pages this library implements):
+ *  - "Exact Layer Streaming: LoRA Fine-Tuning of an 8B Model on a 4 GB Laptop GPU",
+ *    Abstract: layer streaming holds a small pool of decoder layers in GPU memory and fetches
+ *    the rest from host RAM on demand; the streamed run must be bit-identical to a resident
+ *    run of the same numerics; per-layer NF4 dequantisation is the largest streaming-specific
+ *    cost.
+ *  - "Can You Fine-Tune a 27B Model on a Laptop? (I Did the Math)", transcript @1:25-1:58
+ *    (frozen base plus a thin pair of trainable matrices), @2:19-2:29 (NF4 and the second
+ *    quantisation pass over the block constants), @7:11-7:32 (one layer at a time is copied
+ *    into a small on-card buffer on a separate stream while the previous layer computes;
+ *    each layer is read twice per step, forward and backward recompute).
+ *  - "An 8B Fine-Tune Now Fits in 4 GB of VRAM": layers stream through pre-allocated device
+ *    buffers; only the adapters and their gradients stay resident.
+ *  - Soup v0.73.0 benchmarks README, reading conventions: the fit decision refuses instead
+ *    of warning; forward and backward exactness are separate claims.
+ *
+ * Conventions for every entry point
+ *  - Status: every call returns lsn_status. On a non-OK status, lsn_last_error() returns a
+ *    thread-local message. Validation is synchronous; no exception crosses the ABI.
+ *  - Memory: the caller allocates every device buffer (weights, slots, activations,
+ *    outputs, workspaces) and keeps ownership. The library allocates only its pool object
+ *    (host struct and HIP events) and, in audit mode, a small device array of checksums.
+ *    Hot-path calls (nf4_dequant, lora_linear_*, layer_pool_prefetch/acquire/release)
+ *    neither allocate nor synchronise: they enqueue work on the given stream and return.
+ *  - Pointers marked "device" must be device memory of the current HIP device; "host" ones
+ *    host memory. Streams are hipStream_t passed as void* (NULL = the null stream).
+ *  - bf16 tensors are passed as uint16_t bit patterns; all matrices are dense row-major.
+ *  - No output may overlap any input of the same call (LSN_E_ARG).
+ *  - Determinism: results depend only on shapes and input bytes, never on addresses,
+ *    streams, pool slots or timing. No floating-point atomics are used.
+ *  - Asynchronous device faults surface at the caller's next synchronisation; the next
+ *    library call then returns LSN_E_HIP.
+ *  - The library runs only on gfx950; on any other device calls return LSN_E_STATE.
+ */
+#ifndef LSNF4_H
+#define LSNF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LSN_OK = 0,
+  LSN_E_ARG = 1,    /* invalid argument: null pointer, bad shape, overlap, non-finite input */
+  LSN_E_NOFIT = 2,  /* does not fit: refused rather than spilled (pool slots, device memory) */
+  LSN_E_STATE = 3,  /* call not valid in the current state (pool misuse, wrong device) */
+  LSN_E_HIP = 4,    /* the HIP runtime reported an error */
+  LSN_E_AUDIT = 5   /* the pool's aliasing audit found a mismatch */
+} lsn_status;
+
+/* Thread-local text of the last non-OK status returned on this thread ("" if none). */
+const char *lsn_last_error(void);
+
+/* ABI version of this header (incremented on any incompatible change). */
+#define LSN_ABI_VERSION 1
+int32_t lsn_abi_version(void);
+
+/*
+ * The NF4 codebook the kernels use, computed by the library on the host: 16 ascending levels
+ * (levels[0] = -1, levels[7] = 0, levels[15] = +1) at standard-normal quantiles of evenly
+ * spaced probabilities between P = ((1 - 1/30) + (1 - 1/32)) / 2 and 1/2, normalised by the
+ * quantile at P, rounded to fp32; midpoints[i] = fl32((levels[i] + levels[i+1]) / 2).
+ * ("Can You Fine-Tune a 27B Model on a Laptop?", transcript @2:19: levels placed where
+ * normally distributed weights fall; construction of QLoRA, arXiv 2305.14314.)
+ * Host-only; needs no GPU. Either pointer may be NULL.
+ */
+void lsn_nf4_codebook(float levels[16], float midpoints[15]);
+
+/* ------------------------------------------------------------------------------------------
+ * NF4 weight storage (transcript @2:19-2:29: 4-bit codes plus per-block constants, and a
+ * second quantisation pass over those constants).
+ *
+ * W[rows][cols] (rows = output features N, cols = input features K), n = rows*cols,
+ * blocks of 64 consecutive row-major elements, groups of 256 consecutive blocks:
+ *   codes    u8[n/2]      byte j = code[2j] << 4 | code[2j+1]          (device)
+ *   qabsmax  i8[n/64]     int8 code v_b in [-127, 127] of block b      (device)
+ *   absmax2  f32[n/16384] fp32 scale s2_g of group g                   (device)
+ *   mean     f32          per-tensor offset mu                          (host value)
+ * Decoded block constant:  c'_b = fl32( fl32( fl32(v_b / 127) * s2_g ) + mu )
+ * Dequantised weight:      w = fl32( q[code] * c'_b ), then bf16 round-to-nearest-even.
+ * Requirements: cols % 64 == 0 and n % 16384 == 0 (LSN_E_ARG otherwise).
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+  int64_t rows;
+  int64_t cols;
+  const uint8_t *codes;
+  const int8_t *qabsmax;
+  const float *absmax2;
+  float mean;
+} lsn_nf4;
+
+enum { LSN_W_NF4 = 0, LSN_W_BF16 = 1 };
+
+/* A frozen base weight W[N][K]: NF4-packed, or un-quantised bf16 (no dequantisation). */
+typedef struct {
+  int32_t kind;           /* LSN_W_NF4 or LSN_W_BF16 */
+  lsn_nf4 nf4;            /* used when kind == LSN_W_NF4 (rows = N, cols = K) */
+  const uint16_t *bf16;   /* used when kind == LSN_W_BF16: device bf16 W[N][K] */
+} lsn_weight;
+
+/* Device workspace bytes nf4_pack needs for a rows x cols weight. */
+size_t nf4_pack_ws_bytes(int64_t rows, int64_t cols);
+
+/*
+ * nf4_pack - quantise fp32 W[rows][cols] (device) into the NF4 storage above.
+ * First pass per block b: c_b = max|w| (exact), x = fl32(w / c_b) (x = 0 if c_b = 0),
+ * code = number of midpoints m_i with x > m_i (an exact tie takes the lower level).
+ * Second pass: mu = fl32(S / n_b) with S the left-to-right fp64 sum of the c_b (computed on
+ * the host); d_b = fl32(c_b - mu); s2_g = max|d_b| over the group; y = fl32(d_b / s2_g)
+ * (0 if s2_g = 0); v_b = -127 + number of midpoints between consecutive fl32(v/127) that y
+ * exceeds.
+ * Outputs codes/qabsmax/absmax2 are device buffers; *mean_out is a host float.
+ * ws: device, at least nf4_pack_ws_bytes(rows, cols). Non-finite input gives LSN_E_ARG.
+ * Set-up time only: SYNCHRONISES the stream (it reads the block constants back).
+ */
+lsn_status nf4_pack(const float *w, int64_t rows, int64_t cols, uint8_t *codes,
+                    int8_t *qabsmax, float *absmax2, float *mean_out, void *ws,
+                    size_t ws_bytes, void *stream);
+
+enum { LSN_OUT_BF16 = 0, LSN_OUT_F32 = 1 };
+
+/*
+ * nf4_dequant - standalone dequantisation of a whole NF4 tensor into a dense row-major
+ * device buffer `out` of rows*cols elements: bf16 (LSN_OUT_BF16, the GEMM operand) or the
+ * fp32 product before rounding (LSN_OUT_F32). Bit-exact with the definition above.
+ * ("Exact Layer Streaming", Abstract: per-layer NF4 dequantisation.) Async on `stream`.
+ */
+lsn_status nf4_dequant(const lsn_nf4 *w, void *out, int32_t out_dtype, void *stream);
+
+/* ------------------------------------------------------------------------------------------
+ * LoRA linear on a frozen base (transcript @1:25-1:58), rank r, scale s (= alpha / r):
+ *   forward   U = bf16(X A^T);  Y = bf16( X W^T + s U B^T )   (fp32 accumulation)
+ *             adapters off:     Y = bf16( X W^T )
+ *   backward  G = bf16(dY B);   dX = dY W + s G A;  dB = s dY^T U;  dA = s G^T X
+ * Shapes: X [T][K], W [N][K], A [r][K], B [N][r], Y and dY [T][N], U and G [T][r],
+ * dX [T][K], dA [r][K] fp32, dB [N][r] fp32. W is re-dequantised on every call from the
+ * bytes the descriptor points at (a pool slot or a resident buffer): nothing is cached.
+ * Requirements: T >= 1, K % 64 == 0, N % 64 == 0, 1 <= r <= 32, and the NF4 rules for W.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+  int64_t T, K, N, r;
+  float scale;
+  lsn_weight W;
+  const uint16_t *A;   /* device bf16 [r][K] */
+  const uint16_t *B;   /* device bf16 [N][r] */
+} lsn_lora_linear;
+
+/* Device workspace bytes lora_linear_fwd / lora_linear_bwd need for these shapes. */
+size_t lora_linear_ws_bytes(int64_t T, int64_t K, int64_t N, int64_t r);
+
+/*
+ * lora_linear_fwd - Y = bf16(X W^T + s U B^T) with U = bf16(X A^T) written to U (device
+ * [T][r], required when adapters != 0, ignored otherwise). With adapters == 0 the adapter is
+ * skipped and Y = bf16(X W^T), bit-identical to the adapters-on result with B = 0.
+ * ws: device, at least lora_linear_ws_bytes(T, K, N, r). Async on `stream`.
+ */
+lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uint16_t *X,
+                           uint16_t *Y, uint16_t *U, void *ws, size_t ws_bytes, void *stream);
+
+enum { LSN_DX_BF16_SET = 0, LSN_DX_F32_ADD = 1 };
+enum { LSN_GRAD_SET = 0, LSN_GRAD_ADD = 1 };
+
+/*
+ * lora_linear_bwd - given X, dY and U = bf16(X A^T) from the (recomputed) forward:
+ *   dX: LSN_DX_BF16_SET writes bf16(dY W + s G A) to a bf16 [T][K] buffer;
+ *       LSN_DX_F32_ADD adds fp32 (dY W + s G A) into an fp32 [T][K] buffer (for inputs shared
+ *       by several projections; the sum order is the caller's call order).
+ *   dA, dB (fp32): LSN_GRAD_SET overwrites, LSN_GRAD_ADD accumulates. The reductions over T
+ *       run as fixed-order partial sums in `ws`; no atomics, so results are deterministic.
+ * ws: device, at least lora_linear_ws_bytes(T, K, N, r). Async on `stream`.
+ */
+lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const uint16_t *dY,
+                           const uint16_t *U, void *dX, int32_t dx_mode, float *dA, float *dB,
+                           int32_t grad_mode, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Layer pool ("Exact Layer Streaming", Abstract; transcript @7:11-7:32; "An 8B Fine-Tune
+ * Now Fits in 4 GB of VRAM"): n_slots caller-owned device slots hold decoder-layer images;
+ * each layer's image lives in pinned host memory; copies run on the pool's copy stream and
+ * are ordered against compute by events:
+ *   prefetch(l)  picks a free slot (never one acquired or holding a pending prefetch), makes
+ *                the copy stream wait for that slot's release event, copies the image,
+ *                records the slot's ready event. If every slot is busy: LSN_E_STATE.
+ *   acquire(l)   makes the compute stream wait for the ready event and returns the slot's
+ *                device address; a layer not prefetched is prefetched first (a miss).
+ *   release(l)   records the slot's release event on the compute stream; the slot may be
+ *                refilled only after that event. Releasing a layer not held: LSN_E_STATE.
+ * Every visit copies the layer again (each layer is read twice per step) unless
+ * LSN_POOL_KEEP_AT_TURN is set, in which case a layer still in a free slot is reused.
+ * Refusal (Soup benchmarks README: the fit decision refuses rather than warns): create
+ * returns LSN_E_NOFIT if the slots exceed free device memory, register returns LSN_E_NOFIT
+ * for an image larger than slot_bytes. Nothing ever spills to host-mapped memory.
+ * Aliasing audit (LSN_POOL_AUDIT; the pages' silent wrong-gradient defect was aliasing): a
+ * 64-bit checksum of the slot is taken on the compute stream at every acquire and release
+ * and compared with the host image's checksum by layer_pool_audit; released slots are
+ * poisoned (0xFF bytes, which decode to NaN) so a stale read cannot go unnoticed.
+ * LSN_FAULT_* flags plant deterministic defects for the gate's same-process controls.
+ * LSN_POOL_HOST_SIM runs the same state machine on host memory (memcpy, no GPU).
+ * ---------------------------------------------------------------------------------------- */
+typedef struct lsn_pool lsn_pool;
+
+enum {
+  LSN_POOL_AUDIT = 1u << 0,
+  LSN_POOL_KEEP_AT_TURN = 1u << 1,
+  LSN_POOL_HOST_SIM = 1u << 2,
+  LSN_FAULT_STALE_REFETCH = 1u << 8,   /* a layer's second visit skips its copy (stale slot) */
+  LSN_FAULT_WRONG_SLOT = 1u << 9       /* a layer's second visit returns another slot */
+};
+
+typedef struct {
+  uint64_t copies;          /* host->device copies enqueued */
+  uint64_t bytes_copied;
+  uint64_t hits;            /* acquires served by KEEP_AT_TURN reuse */
+  uint64_t misses;          /* acquires without a prior prefetch */
+  uint64_t acquires;
+  uint64_t releases;
+  uint64_t audit_checks;    /* checksums compared by layer_pool_audit */
+  uint64_t audit_failures;
+} lsn_pool_stats;
+
+/* slots: n_slots device pointers of slot_bytes each (caller-owned, 256-byte aligned);
+ * copy_stream: the stream the copies run on (must differ from the compute streams). */
+lsn_status layer_pool_create(int32_t n_slots, size_t slot_bytes, void *const *slots,
+                             int32_t n_layers, void *copy_stream, uint32_t flags,
+                             lsn_pool **out);
+/* host_image: pinned host memory (hipHostMalloc), bytes <= slot_bytes; not modified after. */
+lsn_status layer_pool_register(lsn_pool *pool, int32_t layer, const void *host_image,
+                               size_t bytes);
+lsn_status layer_pool_prefetch(lsn_pool *pool, int32_t layer);
+lsn_status layer_pool_acquire(lsn_pool *pool, int32_t layer, void *compute_stream,
+                              const void **dev_image);
+lsn_status layer_pool_release(lsn_pool *pool, int32_t layer, void *compute_stream);
+lsn_status layer_pool_stats(const lsn_pool *pool, lsn_pool_stats *out);
+/* Synchronises; compares every recorded slot checksum with its layer's host checksum.
+ * LSN_E_AUDIT (with the first mismatching layer and visit in the message) on any mismatch. */
+lsn_status layer_pool_audit(lsn_pool *pool);
+/* Waits for in-flight copies, destroys events; never frees caller memory. */
+lsn_status layer_pool_destroy(lsn_pool *pool);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSNF4_H */

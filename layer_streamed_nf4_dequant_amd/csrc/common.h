@@ -1,0 +1,56 @@
+// Internal helpers shared by the HIP sources of liblsnf4 (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/lsnf4.h"
+
+namespace lsn {
+
+// ---- error reporting (thread-local message, see lsn_last_error) ---------------------------
+lsn_status fail(lsn_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+lsn_status check_hip(hipError_t e, const char *what);
+
+// ---- the NF4 tables the kernels use, computed on the host at first use -------------------
+struct Nf4Table {
+  float q[16];   // levels, ascending
+  float m[15];   // midpoints between consecutive levels
+};
+const Nf4Table &nf4_table();
+
+// ---- small device helpers ------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Round fp32 to bf16 (nearest even) with the gfx950 conversion; returns the 16-bit pattern.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
+  return __builtin_bit_cast(float, h16 << 16);
+}
+
+// c'_b = fl32( fl32(code8[v] * s2) + mu ), two separately rounded operations (no contraction).
+__device__ __forceinline__ float decode_absmax(float code8, float s2, float mu) {
+  return __fadd_rn(__fmul_rn(code8, s2), mu);
+}
+
+// code8[v] = fl32(v / 127), correctly rounded division.
+__device__ __forceinline__ float int8_level(int v) { return __fdiv_rn((float)v, 127.0f); }
+
+// ---- launchers (host side), defined in the .hip files --------------------------------------
+lsn_status launch_pack_codes(const float *w, int64_t n, uint8_t *codes, float *absmax,
+                             int *nonfinite_flag, hipStream_t s);
+lsn_status launch_pack_second(const float *absmax, int64_t n_blocks, float mu, int8_t *qabsmax,
+                              float *absmax2, hipStream_t s);
+lsn_status launch_dequant(const lsn_nf4 &w, void *out, int out_dtype, hipStream_t s);
+
+}  // namespace lsn

@@ -1,0 +1,385 @@
+// The layer pool: K device slots, a copy stream, and events that order each slot's refill
+// after the compute that last read it.
+//
+// "Can You Fine-Tune a 27B Model on a Laptop? (I Did the Math)", transcript @7:11-7:32: the
+// frozen base sits in host RAM; one decoder layer at a time is copied into a small on-card
+// buffer on a separate stream, so the copy lands while the previous layer computes; each
+// layer is read twice per step (forward, and the backward's recompute). "An 8B Fine-Tune Now
+// Fits in 4 GB of VRAM": the buffers are pre-allocated. "Exact Layer Streaming", Abstract:
+// the silent wrong-gradient defect at large layer sizes was aliasing, not a race; the audit
+// below checks that every visit reads exactly its own layer's bytes.
+//
+// State of a slot: FREE (may be refilled once its release event has fired), PENDING (a copy
+// for `layer` has been enqueued, ready event recorded), ACQUIRED (compute is using it).
+// Two backends share the state machine: HIP (device slots, hipMemcpyAsync on the copy stream,
+// hipEvents) and HOST_SIM (host slots, memcpy, no events) for tests without a GPU.
+
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "pool_checksum.h"
+
+namespace lsn {
+lsn_status require_gfx950();
+}
+
+using namespace lsn;
+
+namespace {
+
+enum SlotState { FREE = 0, PENDING = 1, ACQUIRED = 2 };
+
+struct Slot {
+  void *mem = nullptr;
+  int layer = -1;          // layer whose image the slot holds or is receiving
+  bool valid = false;      // holds an intact copy of `layer` (poisoned slots are not valid)
+  SlotState state = FREE;
+  uint64_t gen = 0;        // number of fills
+  uint64_t acquired_gen = 0;
+  uint64_t released_tick = 0;
+  bool release_recorded = false;
+  hipEvent_t ready = nullptr;
+  hipEvent_t released = nullptr;
+};
+
+struct LayerInfo {
+  const void *host = nullptr;
+  size_t bytes = 0;
+  uint64_t checksum = 0;
+  int visits = 0;           // prefetches so far (a layer's first visit is 1)
+};
+
+struct AuditRecord {
+  int layer;
+  int visit;
+  int at_release;           // 0 = taken at acquire, 1 = at release
+};
+
+constexpr size_t kAuditCapacity = 16384;
+
+}  // namespace
+
+struct lsn_pool {
+  int n_slots = 0;
+  size_t slot_bytes = 0;
+  int n_layers = 0;
+  hipStream_t copy = nullptr;
+  uint32_t flags = 0;
+  bool sim = false;
+  std::vector<Slot> slots;
+  std::vector<LayerInfo> layers;
+  lsn_pool_stats stats{};
+  uint64_t tick = 0;
+  // audit
+  unsigned long long *d_sums = nullptr;      // device checksums, one per record
+  std::vector<uint64_t> h_sums;              // host-sim checksums
+  std::vector<AuditRecord> records;
+};
+
+namespace {
+
+bool audit_on(const lsn_pool *p) { return (p->flags & LSN_POOL_AUDIT) != 0; }
+
+lsn_status check_pool(const lsn_pool *p, const char *what) {
+  if (!p) return fail(LSN_E_ARG, "%s: null pool", what);
+  return LSN_OK;
+}
+
+lsn_status check_layer(const lsn_pool *p, int layer, const char *what) {
+  if (layer < 0 || layer >= p->n_layers)
+    return fail(LSN_E_ARG, "%s: layer %d out of range [0, %d)", what, layer, p->n_layers);
+  if (!p->layers[layer].host) return fail(LSN_E_STATE, "%s: layer %d not registered", what, layer);
+  return LSN_OK;
+}
+
+int find_slot(const lsn_pool *p, int layer, SlotState st) {
+  for (int i = 0; i < p->n_slots; ++i)
+    if (p->slots[i].layer == layer && p->slots[i].state == st) return i;
+  return -1;
+}
+
+lsn_status record_checksum(lsn_pool *p, const void *mem, size_t bytes, int layer, int at_release,
+                           hipStream_t s) {
+  if (p->records.size() >= kAuditCapacity)
+    return fail(LSN_E_STATE, "audit capacity (%zu checksums) exhausted: call layer_pool_audit",
+                kAuditCapacity);
+  const size_t idx = p->records.size();
+  p->records.push_back({layer, p->layers[layer].visits, at_release});
+  if (p->sim) {
+    p->h_sums[idx] = checksum_host(mem, bytes);
+    return LSN_OK;
+  }
+  return check_hip(launch_checksum(mem, bytes, p->d_sums + idx, s), "audit checksum launch");
+}
+
+lsn_status do_prefetch(lsn_pool *p, int layer) {
+  if (find_slot(p, layer, PENDING) >= 0) return LSN_OK;   // already in flight
+  if (find_slot(p, layer, ACQUIRED) >= 0)
+    return fail(LSN_E_STATE, "layer_pool_prefetch: layer %d is acquired; release it first", layer);
+  LayerInfo &L = p->layers[layer];
+  // reuse a free slot that still holds this layer intact (KEEP_AT_TURN only)
+  if (p->flags & LSN_POOL_KEEP_AT_TURN) {
+    for (int i = 0; i < p->n_slots; ++i) {
+      Slot &s = p->slots[i];
+      if (s.state == FREE && s.layer == layer && s.valid) {
+        s.state = PENDING;
+        ++p->stats.hits;
+        ++L.visits;
+        return LSN_OK;
+      }
+    }
+  }
+  // victim: a free slot, never-used first, else the one released longest ago
+  int victim = -1;
+  for (int i = 0; i < p->n_slots; ++i) {
+    const Slot &s = p->slots[i];
+    if (s.state != FREE) continue;
+    if (victim < 0) { victim = i; continue; }
+    const Slot &v = p->slots[victim];
+    const bool s_unused = s.layer < 0, v_unused = v.layer < 0;
+    if ((s_unused && !v_unused) || (s_unused == v_unused && s.released_tick < v.released_tick)) victim = i;
+  }
+  if (victim < 0)
+    return fail(LSN_E_STATE, "layer_pool_prefetch: all %d slots are acquired or pending", p->n_slots);
+  Slot &s = p->slots[victim];
+  ++L.visits;
+  const bool refetch = L.visits >= 2;
+  const bool skip_copy = refetch && (p->flags & LSN_FAULT_STALE_REFETCH);
+  if (p->sim) {
+    if (!skip_copy) std::memcpy(s.mem, L.host, L.bytes);
+  } else {
+    hipError_t e = hipSuccess;
+    if (s.release_recorded) e = hipStreamWaitEvent(p->copy, s.released, 0);
+    if (e == hipSuccess && !skip_copy)
+      e = hipMemcpyAsync(s.mem, L.host, L.bytes, hipMemcpyHostToDevice, p->copy);
+    if (e == hipSuccess) e = hipEventRecord(s.ready, p->copy);
+    if (e != hipSuccess) return check_hip(e, "layer_pool_prefetch copy");
+  }
+  s.layer = layer;
+  s.valid = !skip_copy;
+  s.state = PENDING;
+  ++s.gen;
+  if (!skip_copy) {
+    ++p->stats.copies;
+    p->stats.bytes_copied += L.bytes;
+  }
+  return LSN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lsn_status layer_pool_create(int32_t n_slots, size_t slot_bytes, void *const *slots, int32_t n_layers,
+                             void *copy_stream, uint32_t flags, lsn_pool **out) {
+  if (!out) return fail(LSN_E_ARG, "layer_pool_create: null out");
+  *out = nullptr;
+  if (n_slots < 1 || n_layers < 1 || slot_bytes == 0 || !slots)
+    return fail(LSN_E_ARG, "layer_pool_create: need n_slots >= 1, n_layers >= 1, slot_bytes > 0, slots");
+  if (slot_bytes % 256 != 0) return fail(LSN_E_ARG, "layer_pool_create: slot_bytes must be a multiple of 256");
+  for (int i = 0; i < n_slots; ++i) {
+    if (!slots[i] || ((uintptr_t)slots[i] & 255))
+      return fail(LSN_E_ARG, "layer_pool_create: slot %d is null or not 256-byte aligned", i);
+    for (int j = 0; j < i; ++j) {
+      const uintptr_t a = (uintptr_t)slots[i], b = (uintptr_t)slots[j];
+      if (a < b + slot_bytes && b < a + slot_bytes)
+        return fail(LSN_E_ARG, "layer_pool_create: slots %d and %d overlap", j, i);
+    }
+  }
+  const bool sim = (flags & LSN_POOL_HOST_SIM) != 0;
+  if (!sim) {
+    lsn_status st = require_gfx950();
+    if (st != LSN_OK) return st;
+    if (!copy_stream) return fail(LSN_E_ARG, "layer_pool_create: the copy stream must be a created stream");
+  }
+  lsn_pool *p = new lsn_pool();
+  p->n_slots = n_slots;
+  p->slot_bytes = slot_bytes;
+  p->n_layers = n_layers;
+  p->copy = (hipStream_t)copy_stream;
+  p->flags = flags;
+  p->sim = sim;
+  p->slots.resize(n_slots);
+  p->layers.resize(n_layers);
+  for (int i = 0; i < n_slots; ++i) p->slots[i].mem = slots[i];
+  hipError_t e = hipSuccess;
+  if (!sim) {
+    for (int i = 0; i < n_slots && e == hipSuccess; ++i) {
+      e = hipEventCreateWithFlags(&p->slots[i].ready, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&p->slots[i].released, hipEventDisableTiming);
+    }
+    if (e == hipSuccess && audit_on(p)) {
+      e = hipMalloc(&p->d_sums, kAuditCapacity * sizeof(unsigned long long));
+      if (e == hipSuccess) e = hipMemset(p->d_sums, 0, kAuditCapacity * sizeof(unsigned long long));
+    }
+  } else if (audit_on(p)) {
+    p->h_sums.assign(kAuditCapacity, 0);
+  }
+  if (e != hipSuccess) {
+    lsn_status st = check_hip(e, "layer_pool_create");
+    layer_pool_destroy(p);
+    return st;
+  }
+  *out = p;
+  return LSN_OK;
+}
+
+lsn_status layer_pool_register(lsn_pool *p, int32_t layer, const void *host_image, size_t bytes) {
+  lsn_status st = check_pool(p, "layer_pool_register");
+  if (st != LSN_OK) return st;
+  if (layer < 0 || layer >= p->n_layers)
+    return fail(LSN_E_ARG, "layer_pool_register: layer %d out of range [0, %d)", layer, p->n_layers);
+  if (!host_image || bytes == 0) return fail(LSN_E_ARG, "layer_pool_register: empty image");
+  if (bytes % 256 != 0) return fail(LSN_E_ARG, "layer_pool_register: image bytes must be a multiple of 256");
+  if (bytes > p->slot_bytes)
+    return fail(LSN_E_NOFIT, "layer_pool_register: layer %d image (%zu B) does not fit a slot (%zu B)",
+                layer, bytes, p->slot_bytes);
+  if (!p->sim) {
+    hipPointerAttribute_t attr;
+    const hipError_t e = hipPointerGetAttributes(&attr, host_image);
+    if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();
+      return fail(LSN_E_ARG, "layer_pool_register: layer %d image is not pinned host memory", layer);
+    }
+  }
+  LayerInfo &L = p->layers[layer];
+  L.host = host_image;
+  L.bytes = bytes;
+  L.visits = 0;
+  L.checksum = audit_on(p) ? checksum_host(host_image, bytes) : 0;
+  return LSN_OK;
+}
+
+lsn_status layer_pool_prefetch(lsn_pool *p, int32_t layer) {
+  lsn_status st = check_pool(p, "layer_pool_prefetch");
+  if (st != LSN_OK) return st;
+  if ((st = check_layer(p, layer, "layer_pool_prefetch")) != LSN_OK) return st;
+  return do_prefetch(p, layer);
+}
+
+lsn_status layer_pool_acquire(lsn_pool *p, int32_t layer, void *compute_stream, const void **dev_image) {
+  lsn_status st = check_pool(p, "layer_pool_acquire");
+  if (st != LSN_OK) return st;
+  if ((st = check_layer(p, layer, "layer_pool_acquire")) != LSN_OK) return st;
+  if (!dev_image) return fail(LSN_E_ARG, "layer_pool_acquire: null dev_image");
+  if (!p->sim && compute_stream == (void *)p->copy)
+    return fail(LSN_E_ARG, "layer_pool_acquire: the compute stream must differ from the copy stream");
+  if (find_slot(p, layer, ACQUIRED) >= 0)
+    return fail(LSN_E_STATE, "layer_pool_acquire: layer %d is already acquired", layer);
+  int i = find_slot(p, layer, PENDING);
+  if (i < 0) {
+    ++p->stats.misses;
+    if ((st = do_prefetch(p, layer)) != LSN_OK) return st;
+    i = find_slot(p, layer, PENDING);
+  }
+  Slot &s = p->slots[i];
+  if (!p->sim) {
+    const hipError_t e = hipStreamWaitEvent((hipStream_t)compute_stream, s.ready, 0);
+    if (e != hipSuccess) return check_hip(e, "layer_pool_acquire wait");
+  }
+  s.state = ACQUIRED;
+  s.acquired_gen = s.gen;
+  ++p->stats.acquires;
+  void *mem = s.mem;
+  if ((p->flags & LSN_FAULT_WRONG_SLOT) && p->layers[layer].visits >= 2 && p->n_slots >= 2)
+    mem = p->slots[(i + 1) % p->n_slots].mem;
+  if (audit_on(p) &&
+      (st = record_checksum(p, mem, p->layers[layer].bytes, layer, 0, (hipStream_t)compute_stream)) != LSN_OK)
+    return st;
+  *dev_image = mem;
+  return LSN_OK;
+}
+
+lsn_status layer_pool_release(lsn_pool *p, int32_t layer, void *compute_stream) {
+  lsn_status st = check_pool(p, "layer_pool_release");
+  if (st != LSN_OK) return st;
+  if (layer < 0 || layer >= p->n_layers)
+    return fail(LSN_E_ARG, "layer_pool_release: layer %d out of range", layer);
+  const int i = find_slot(p, layer, ACQUIRED);
+  if (i < 0) return fail(LSN_E_STATE, "layer_pool_release: layer %d is not acquired", layer);
+  Slot &s = p->slots[i];
+  if (s.gen != s.acquired_gen)
+    return fail(LSN_E_AUDIT, "layer_pool_release: slot %d was refilled while layer %d held it", i, layer);
+  hipStream_t cs = (hipStream_t)compute_stream;
+  if (audit_on(p)) {
+    void *mem = s.mem;
+    if ((p->flags & LSN_FAULT_WRONG_SLOT) && p->layers[layer].visits >= 2 && p->n_slots >= 2)
+      mem = p->slots[(i + 1) % p->n_slots].mem;
+    if ((st = record_checksum(p, mem, p->layers[layer].bytes, layer, 1, cs)) != LSN_OK) return st;
+    if (!(p->flags & LSN_POOL_KEEP_AT_TURN)) {
+      if (p->sim) std::memset(s.mem, 0xFF, p->slot_bytes);
+      else if ((st = check_hip(launch_poison(s.mem, p->slot_bytes, cs), "poison launch")) != LSN_OK) return st;
+      s.valid = false;
+    }
+  }
+  if (!p->sim) {
+    const hipError_t e = hipEventRecord(s.released, cs);
+    if (e != hipSuccess) return check_hip(e, "layer_pool_release record");
+    s.release_recorded = true;
+  }
+  s.state = FREE;
+  s.released_tick = ++p->tick;
+  ++p->stats.releases;
+  return LSN_OK;
+}
+
+lsn_status layer_pool_stats(const lsn_pool *p, lsn_pool_stats *out) {
+  lsn_status st = check_pool(p, "layer_pool_stats");
+  if (st != LSN_OK) return st;
+  if (!out) return fail(LSN_E_ARG, "layer_pool_stats: null out");
+  *out = p->stats;
+  return LSN_OK;
+}
+
+lsn_status layer_pool_audit(lsn_pool *p) {
+  lsn_status st = check_pool(p, "layer_pool_audit");
+  if (st != LSN_OK) return st;
+  if (!audit_on(p)) return fail(LSN_E_STATE, "layer_pool_audit: pool created without LSN_POOL_AUDIT");
+  const size_t n = p->records.size();
+  std::vector<uint64_t> sums(n);
+  if (p->sim) {
+    for (size_t i = 0; i < n; ++i) sums[i] = p->h_sums[i];
+  } else if (n > 0) {
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(sums.data(), p->d_sums, n * 8, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemset(p->d_sums, 0, n * 8);
+    if (e != hipSuccess) return check_hip(e, "layer_pool_audit");
+  }
+  uint64_t failures = 0;
+  std::string first;
+  for (size_t i = 0; i < n; ++i) {
+    const AuditRecord &r = p->records[i];
+    if (sums[i] != p->layers[r.layer].checksum) {
+      if (failures == 0)
+        first = "layer " + std::to_string(r.layer) + " visit " + std::to_string(r.visit) +
+                (r.at_release ? " at release" : " at acquire");
+      ++failures;
+    }
+  }
+  p->stats.audit_checks += n;
+  p->stats.audit_failures += failures;
+  p->records.clear();
+  if (failures)
+    return fail(LSN_E_AUDIT, "layer_pool_audit: %llu of %zu slot checksums differ from their layer's "
+                "image (first: %s)", (unsigned long long)failures, n, first.c_str());
+  return LSN_OK;
+}
+
+lsn_status layer_pool_destroy(lsn_pool *p) {
+  if (!p) return LSN_OK;
+  hipError_t e = hipSuccess;
+  if (!p->sim) {
+    if (p->copy) e = hipStreamSynchronize(p->copy);
+    for (Slot &s : p->slots) {
+      if (s.ready) (void)hipEventDestroy(s.ready);
+      if (s.released) (void)hipEventDestroy(s.released);
+    }
+    if (p->d_sums) (void)hipFree(p->d_sums);
+  }
+  delete p;
+  return check_hip(e, "layer_pool_destroy");
+}
+
+}  // extern "C"

@@ -1,0 +1,272 @@
+"""ctypes binding to liblsnf4.so (the C ABI of include/lsnf4.h).
+
+Argument marshalling only: every step of the path runs in the library's gfx950 kernels.
+torch tensors are used as device memory (their data pointers are passed through) and torch
+streams as HIP streams.  There is no fallback: if the library is missing or a call fails,
+an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblsnf4.so")
+
+LSN_OK, LSN_E_ARG, LSN_E_NOFIT, LSN_E_STATE, LSN_E_HIP, LSN_E_AUDIT = range(6)
+STATUS_NAMES = {0: "LSN_OK", 1: "LSN_E_ARG", 2: "LSN_E_NOFIT", 3: "LSN_E_STATE", 4: "LSN_E_HIP",
+                5: "LSN_E_AUDIT"}
+W_NF4, W_BF16 = 0, 1
+OUT_BF16, OUT_F32 = 0, 1
+DX_BF16_SET, DX_F32_ADD = 0, 1
+GRAD_SET, GRAD_ADD = 0, 1
+POOL_AUDIT, POOL_KEEP_AT_TURN, POOL_HOST_SIM = 1, 2, 4
+FAULT_STALE_REFETCH, FAULT_WRONG_SLOT = 1 << 8, 1 << 9
+
+EXPORTS = (
+    "lsn_last_error", "lsn_abi_version", "lsn_nf4_codebook", "nf4_pack_ws_bytes", "nf4_pack",
+    "nf4_dequant", "lora_linear_ws_bytes", "lora_linear_fwd", "lora_linear_bwd",
+    "layer_pool_create", "layer_pool_register", "layer_pool_prefetch", "layer_pool_acquire",
+    "layer_pool_release", "layer_pool_stats", "layer_pool_audit", "layer_pool_destroy",
+)
+
+
+class LsnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class NF4Desc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("qabsmax", ctypes.c_void_p), ("absmax2", ctypes.c_void_p), ("mean", ctypes.c_float)]
+
+
+class WeightDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("nf4", NF4Desc), ("bf16", ctypes.c_void_p)]
+
+
+class LoraLinearDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("r", ctypes.c_int64), ("scale", ctypes.c_float), ("W", WeightDesc),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p)]
+
+
+class PoolStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("copies", "bytes_copied", "hits", "misses",
+                                                "acquires", "releases", "audit_checks",
+                                                "audit_failures")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def load():
+    """Load liblsnf4.so once and declare its signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                          "(or python -m layer_streamed_nf4_dequant_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "lsn_last_error": (ctypes.c_char_p, []),
+        "lsn_abi_version": (i32, []),
+        "lsn_nf4_codebook": (None, [vp, vp]),
+        "nf4_pack_ws_bytes": (sz, [i64, i64]),
+        "nf4_pack": (i32, [vp, i64, i64, vp, vp, vp, vp, vp, sz, vp]),
+        "nf4_dequant": (i32, [ctypes.POINTER(NF4Desc), vp, i32, vp]),
+        "lora_linear_ws_bytes": (sz, [i64, i64, i64, i64]),
+        "lora_linear_fwd": (i32, [ctypes.POINTER(LoraLinearDesc), i32, vp, vp, vp, vp, sz, vp]),
+        "lora_linear_bwd": (i32, [ctypes.POINTER(LoraLinearDesc), vp, vp, vp, vp, i32, vp, vp, i32,
+                                  vp, sz, vp]),
+        "layer_pool_create": (i32, [i32, sz, ctypes.POINTER(vp), i32, vp, ctypes.c_uint32,
+                                    ctypes.POINTER(vp)]),
+        "layer_pool_register": (i32, [vp, i32, vp, sz]),
+        "layer_pool_prefetch": (i32, [vp, i32]),
+        "layer_pool_acquire": (i32, [vp, i32, vp, ctypes.POINTER(vp)]),
+        "layer_pool_release": (i32, [vp, i32, vp]),
+        "layer_pool_stats": (i32, [vp, ctypes.POINTER(PoolStats)]),
+        "layer_pool_audit": (i32, [vp]),
+        "layer_pool_destroy": (i32, [vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != LSN_OK:
+        raise LsnError(status, load().lsn_last_error().decode(errors="replace"))
+
+
+def codebook() -> tuple[np.ndarray, np.ndarray]:
+    """(levels[16], midpoints[15]) as the library's kernels use them (host call, no GPU)."""
+    q = np.zeros(16, dtype=np.float32)
+    m = np.zeros(15, dtype=np.float32)
+    load().lsn_nf4_codebook(q.ctypes.data, m.ctypes.data)
+    return q, m
+
+
+# ---------------------------------------------------------------------------------------------
+# torch-facing helpers (torch only owns memory and streams)
+# ---------------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+@dataclass
+class NF4Tensor:
+    """An NF4-packed weight W[rows][cols] whose arrays are torch device tensors."""
+    rows: int
+    cols: int
+    codes: object      # uint8 [rows*cols/2]
+    qabsmax: object    # int8 [rows*cols/64]
+    absmax2: object    # float32 [rows*cols/16384]
+    mean: float
+
+    def desc(self) -> NF4Desc:
+        return NF4Desc(self.rows, self.cols, _ptr(self.codes), _ptr(self.qabsmax),
+                       _ptr(self.absmax2), float(self.mean))
+
+    @staticmethod
+    def nbytes_for(rows: int, cols: int) -> int:
+        n = rows * cols
+        return n // 2 + n // 64 + 4 * (n // 16384)
+
+
+def nf4_pack(w, stream=None) -> NF4Tensor:
+    """Pack fp32 device W[rows][cols] to NF4 (synchronises the stream)."""
+    torch = _torch()
+    assert w.dtype == torch.float32 and w.is_cuda and w.dim() == 2 and w.is_contiguous()
+    rows, cols = w.shape
+    n = rows * cols
+    dev = w.device
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    qabs = torch.empty(max(n // 64, 1), dtype=torch.int8, device=dev)
+    abs2 = torch.empty(max(n // 16384, 1), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(load().nf4_pack_ws_bytes(rows, cols), 256), dtype=torch.uint8, device=dev)
+    mean = ctypes.c_float(0.0)
+    check(load().nf4_pack(_ptr(w), rows, cols, _ptr(codes), _ptr(qabs), _ptr(abs2),
+                          ctypes.addressof(mean), _ptr(ws), ws.numel(), _stream_handle(stream)))
+    return NF4Tensor(rows, cols, codes, qabs, abs2, float(mean.value))
+
+
+def nf4_pack_into(w, codes, qabsmax, absmax2, ws, stream=None) -> float:
+    """Pack into caller-provided device arrays; returns the per-tensor mean."""
+    rows, cols = w.shape
+    mean = ctypes.c_float(0.0)
+    check(load().nf4_pack(_ptr(w), rows, cols, _ptr(codes), _ptr(qabsmax), _ptr(absmax2),
+                          ctypes.addressof(mean), _ptr(ws), ws.numel() * ws.element_size(),
+                          _stream_handle(stream)))
+    return float(mean.value)
+
+
+def nf4_dequant(w: NF4Tensor, out_dtype: str = "bf16", out=None, stream=None):
+    torch = _torch()
+    dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    if out is None:
+        out = torch.empty((w.rows, w.cols), dtype=dt, device=w.codes.device)
+    d = w.desc()
+    check(load().nf4_dequant(ctypes.byref(d), _ptr(out), OUT_BF16 if out_dtype == "bf16" else OUT_F32,
+                             _stream_handle(stream)))
+    return out
+
+
+def weight_desc(W) -> WeightDesc:
+    """W is an NF4Tensor or a bf16 device tensor [N][K]."""
+    if isinstance(W, NF4Tensor):
+        return WeightDesc(W_NF4, W.desc(), None)
+    return WeightDesc(W_BF16, NF4Desc(), _ptr(W))
+
+
+def linear_desc(T: int, K: int, N: int, r: int, scale: float, W, A, B) -> LoraLinearDesc:
+    return LoraLinearDesc(T, K, N, r, float(scale), weight_desc(W), _ptr(A), _ptr(B))
+
+
+def ws_bytes(T: int, K: int, N: int, r: int) -> int:
+    return int(load().lora_linear_ws_bytes(T, K, N, r))
+
+
+def lora_linear_fwd(desc: LoraLinearDesc, X, Y, U=None, adapters: bool = True, ws=None,
+                    stream=None) -> None:
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    check(load().lora_linear_fwd(ctypes.byref(desc), 1 if adapters else 0, _ptr(X), _ptr(Y), _ptr(U),
+                                 _ptr(ws), nbytes, _stream_handle(stream)))
+
+
+def lora_linear_bwd(desc: LoraLinearDesc, X, dY, U, dX, dA, dB, dx_mode: int = DX_BF16_SET,
+                    grad_mode: int = GRAD_SET, ws=None, stream=None) -> None:
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    check(load().lora_linear_bwd(ctypes.byref(desc), _ptr(X), _ptr(dY), _ptr(U), _ptr(dX), dx_mode,
+                                 _ptr(dA), _ptr(dB), grad_mode, _ptr(ws), nbytes, _stream_handle(stream)))
+
+
+class LayerPool:
+    """Owner of an lsn_pool handle. Slots are caller memory (torch tensors or host buffers)."""
+
+    def __init__(self, slot_ptrs, slot_bytes: int, n_layers: int, copy_stream_handle: int | None,
+                 flags: int = 0):
+        arr = (ctypes.c_void_p * len(slot_ptrs))(*slot_ptrs)
+        h = ctypes.c_void_p()
+        check(load().layer_pool_create(len(slot_ptrs), slot_bytes, arr, n_layers, copy_stream_handle,
+                                       flags, ctypes.byref(h)))
+        self.h = h
+        self.flags = flags
+
+    def register(self, layer: int, host_ptr: int, nbytes: int) -> None:
+        check(load().layer_pool_register(self.h, layer, host_ptr, nbytes))
+
+    def prefetch(self, layer: int) -> None:
+        check(load().layer_pool_prefetch(self.h, layer))
+
+    def acquire(self, layer: int, compute_stream_handle: int | None) -> int:
+        out = ctypes.c_void_p()
+        check(load().layer_pool_acquire(self.h, layer, compute_stream_handle, ctypes.byref(out)))
+        return int(out.value)
+
+    def release(self, layer: int, compute_stream_handle: int | None) -> None:
+        check(load().layer_pool_release(self.h, layer, compute_stream_handle))
+
+    def stats(self) -> dict:
+        s = PoolStats()
+        check(load().layer_pool_stats(self.h, ctypes.byref(s)))
+        return s.as_dict()
+
+    def audit(self) -> None:
+        check(load().layer_pool_audit(self.h))
+
+    def close(self) -> None:
+        if self.h is not None and self.h.value:
+            check(load().layer_pool_destroy(self.h))
+        self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

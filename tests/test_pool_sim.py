@@ -1,0 +1,157 @@
+"""The layer pool's state machine on the host-simulated backend (no GPU): slot choice, event
+ordering rules, refusal, misuse errors, KEEP_AT_TURN reuse, the aliasing audit and the planted
+faults the exactness gate's controls rely on."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from layer_streamed_nf4_dequant_amd import lib
+
+SLOT = 4096
+
+
+def aligned(n):
+    """A zeroed uint8 array of n bytes whose data starts on a 256-byte boundary."""
+    raw = np.zeros(n + 256, dtype=np.uint8)
+    off = (-raw.ctypes.data) % 256
+    return raw[off:off + n]
+
+
+class SimPool:
+    def __init__(self, n_slots=2, n_layers=4, flags=0, sizes=None):
+        self.slots = [aligned(SLOT) for _ in range(n_slots)]
+        self.images = []
+        rng = np.random.default_rng(0)
+        for l in range(n_layers):
+            n = SLOT if sizes is None else sizes[l]
+            self.images.append(rng.integers(0, 255, n, dtype=np.uint8))
+        self.pool = lib.LayerPool([s.ctypes.data for s in self.slots], SLOT, n_layers, None,
+                                  flags | lib.POOL_HOST_SIM)
+        for l, img in enumerate(self.images):
+            self.pool.register(l, img.ctypes.data, img.size)
+
+    def view(self, ptr, layer):
+        n = self.images[layer].size
+        return np.ctypeslib.as_array((ctypes.c_uint8 * n).from_address(ptr))
+
+    def visit(self, layer):
+        ptr = self.pool.acquire(layer, None)
+        data = self.view(ptr, layer).copy()
+        self.pool.release(layer, None)
+        return data
+
+
+def forward_backward(p: SimPool, n_layers: int):
+    """One step's visiting order: forward 0..L-1, then backward L-1..0, prefetching one ahead."""
+    seen = []
+    p.pool.prefetch(0)
+    for l in range(n_layers):
+        if l + 1 < n_layers:
+            p.pool.prefetch(l + 1)
+        seen.append(("f", l, p.visit(l)))
+    p.pool.prefetch(n_layers - 1)
+    for l in reversed(range(n_layers)):
+        if l > 0:
+            p.pool.prefetch(l - 1)
+        seen.append(("b", l, p.visit(l)))
+    return seen
+
+
+def test_every_visit_sees_its_own_layer_and_layers_are_read_twice():
+    p = SimPool(n_slots=2, n_layers=5)
+    for kind, l, data in forward_backward(p, 5):
+        np.testing.assert_array_equal(data, p.images[l], err_msg=f"{kind} visit of layer {l}")
+    st = p.pool.stats()
+    assert st["copies"] == 10 and st["acquires"] == 10 and st["releases"] == 10
+    assert st["misses"] == 0 and st["hits"] == 0
+    assert st["bytes_copied"] == 10 * SLOT
+
+
+def test_keep_at_turn_reuses_the_turnaround_layer():
+    p = SimPool(n_slots=2, n_layers=5, flags=lib.POOL_KEEP_AT_TURN)
+    for kind, l, data in forward_backward(p, 5):
+        np.testing.assert_array_equal(data, p.images[l])
+    st = p.pool.stats()
+    assert st["hits"] >= 1 and st["copies"] < 10
+
+
+def test_single_slot_pool_works_without_prefetch_ahead():
+    p = SimPool(n_slots=1, n_layers=3)
+    for l in (0, 1, 2, 2, 1, 0):
+        np.testing.assert_array_equal(p.visit(l), p.images[l])
+    assert p.pool.stats()["misses"] == 6
+
+
+def test_prefetch_refuses_when_all_slots_busy():
+    p = SimPool(n_slots=2, n_layers=4)
+    p.pool.prefetch(0)
+    p.pool.prefetch(1)
+    with pytest.raises(lib.LsnError) as e:
+        p.pool.prefetch(2)
+    assert e.value.status == lib.LSN_E_STATE
+    p.pool.acquire(0, None)
+    with pytest.raises(lib.LsnError):
+        p.pool.prefetch(2)           # slot 0 acquired, slot 1 pending
+    p.pool.release(0, None)
+    p.pool.prefetch(2)               # slot 0 is free again
+
+
+def test_misuse_errors():
+    p = SimPool(n_slots=2, n_layers=3)
+    with pytest.raises(lib.LsnError) as e:
+        p.pool.release(0, None)
+    assert e.value.status == lib.LSN_E_STATE
+    p.pool.acquire(1, None)
+    with pytest.raises(lib.LsnError) as e:
+        p.pool.acquire(1, None)
+    assert e.value.status == lib.LSN_E_STATE
+    with pytest.raises(lib.LsnError) as e:
+        p.pool.prefetch(1)
+    assert e.value.status == lib.LSN_E_STATE
+    with pytest.raises(lib.LsnError) as e:
+        p.pool.acquire(7, None)
+    assert e.value.status == lib.LSN_E_ARG
+
+
+def test_register_refuses_an_image_larger_than_a_slot():
+    slots = [aligned(SLOT)]
+    pool = lib.LayerPool([slots[0].ctypes.data], SLOT, 1, None, lib.POOL_HOST_SIM)
+    big = np.zeros(2 * SLOT, dtype=np.uint8)
+    with pytest.raises(lib.LsnError) as e:
+        pool.register(0, big.ctypes.data, big.size)
+    assert e.value.status == lib.LSN_E_NOFIT
+
+
+def test_create_rejects_overlapping_or_misaligned_slots():
+    buf = np.zeros(3 * SLOT + 512, dtype=np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    with pytest.raises(lib.LsnError):
+        lib.LayerPool([base, base + 256], SLOT, 1, None, lib.POOL_HOST_SIM)
+    with pytest.raises(lib.LsnError):
+        lib.LayerPool([base + 8], SLOT, 1, None, lib.POOL_HOST_SIM)
+
+
+def test_audit_passes_on_a_clean_step_and_poisons_released_slots():
+    p = SimPool(n_slots=2, n_layers=4, flags=lib.POOL_AUDIT)
+    forward_backward(p, 4)
+    p.pool.audit()
+    st = p.pool.stats()
+    assert st["audit_checks"] == 16 and st["audit_failures"] == 0
+    assert all(np.all(s == 0xFF) for s in p.slots), "released slots must be poisoned"
+
+
+@pytest.mark.parametrize("fault", [lib.FAULT_STALE_REFETCH, lib.FAULT_WRONG_SLOT])
+def test_planted_faults_corrupt_only_the_second_visit_and_the_audit_catches_them(fault):
+    p = SimPool(n_slots=2, n_layers=4, flags=fault)
+    seen = forward_backward(p, 4)
+    fwd_ok = all(np.array_equal(d, p.images[l]) for k, l, d in seen if k == "f")
+    bwd_ok = all(np.array_equal(d, p.images[l]) for k, l, d in seen if k == "b")
+    assert fwd_ok and not bwd_ok
+    q = SimPool(n_slots=2, n_layers=4, flags=fault | lib.POOL_AUDIT)
+    forward_backward(q, 4)
+    with pytest.raises(lib.LsnError) as e:
+        q.pool.audit()
+    assert e.value.status == lib.LSN_E_AUDIT
+    assert q.pool.stats()["audit_failures"] > 0
