@@ -146,7 +146,7 @@ lsn_status nf4_dequant(const lsn_nf4 *w, void *out, int32_t out_dtype, void *str
  * Shapes: X [T][K], W [N][K], A [r][K], B [N][r], Y and dY [T][N], U and G [T][r],
  * dX [T][K], dA [r][K] fp32, dB [N][r] fp32. W is re-dequantised on every call from the
  * bytes the descriptor points at (a pool slot or a resident buffer): nothing is cached.
- * Requirements: T >= 1, K % 64 == 0, N % 64 == 0, 1 <= r <= 32, and the NF4 rules for W.
+ * Requirements: T >= 1, K % 64 == 0, N % 64 == 0, r in {8, 16, 24, 32}, and the NF4 rules for W.
  * ---------------------------------------------------------------------------------------- */
 typedef struct {
   int64_t T, K, N, r;

@@ -1,0 +1,51 @@
+// Internal interface of the fused GEMM kernels (gemm.hip) and the skinny LoRA kernels
+// (lora_small.hip).
+#pragma once
+
+#include "common.h"
+
+namespace lsn {
+
+enum { GEMM_NT = 0, GEMM_NN = 1 };        // forward Y = act W^T ; backward dX = act W
+enum { W_IS_NF4 = 0, W_IS_BF16 = 1 };
+enum { EPI_BF16 = 0, EPI_F32_ADD = 1 };
+
+struct GemmArgs {
+  int64_t M;            // rows of act and out (tokens)
+  int64_t Nout;         // columns of out
+  int64_t Kred;         // reduction length (columns of act)
+  const uint16_t *act;  // bf16 [M][Kred]: X (forward) or dY (backward)
+  // frozen base W: forward [Nout][Kred], backward [Kred][Nout]; ldw = elements per W row
+  int64_t ldw;
+  const uint16_t *w16;  // bf16 W
+  const uint8_t *codes; // NF4 W
+  const int8_t *qabsmax;
+  const float *absmax2;
+  float mean;
+  float q[16];          // NF4 levels (filled by launch_gemm)
+  // LoRA term: forward s * U B^T (lr_act = U [M][r], lr_w = B [Nout][r]);
+  //            backward s * G A  (lr_act = G [M][r], lr_w = A [r][Nout])
+  const uint16_t *lr_act;
+  const uint16_t *lr_w;
+  int r;
+  float scale;
+  int adapters;
+  void *out;            // bf16 or fp32 [M][Nout]
+};
+
+lsn_status launch_gemm(int layout, int wkind, int epi, GemmArgs a, hipStream_t s);
+
+// out[m][j] = bf16( sum_k act[m][k] * P[j][k] ), j < r   (U = X A^T, or G = dY B with P = B^T)
+lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const uint16_t *P, int r,
+                          uint16_t *out, hipStream_t s);
+// P^T: B [N][r] -> Bt [r][N]
+lsn_status launch_transpose_b(const uint16_t *B, int64_t N, int r, uint16_t *Bt, hipStream_t s);
+// partial[c][p][j] = sum over t in chunk c of Z[t][p] * V[t][j]   (chunks of TN_CHUNK rows)
+constexpr int TN_CHUNK = 256;
+lsn_status launch_tn_partial(const uint16_t *Z, int64_t T, int64_t P, const uint16_t *V, int r,
+                             float *partial, hipStream_t s);
+// out = s * sum_c partial[c] (fixed order), set or accumulate; transposed: out[j][p], else out[p][j]
+lsn_status launch_tn_reduce(const float *partial, int64_t n_chunks, int64_t P, int r, float scale,
+                            int accumulate, int transposed, float *out, hipStream_t s);
+
+}  // namespace lsn

@@ -1,27 +1,206 @@
-// C ABI of the LoRA linear (forward and backward). Contracts in include/lsnf4.h.
+// C ABI of the LoRA linear on a frozen (NF4 or bf16) base: validation, workspace layout and
+// the kernel sequence. Contracts in include/lsnf4.h.
+//
+// forward:  U = bf16(X A^T)                                  k_rowproj
+//           Y = bf16(s U B^T + X W^T)                        k_gemm NT (NF4 dequantised in LDS)
+// backward: Bt = B^T ; G = bf16(dY B)                        k_transpose_b, k_rowproj
+//           dX = s G A + dY W                                k_gemm NN (bf16 store or fp32 add)
+//           dB = s sum_t dY^T U ; dA = s sum_t G^T X         k_tn_partial + k_tn_reduce
+
 #include "common.h"
+#include "gemm.h"
+
+namespace lsn {
+lsn_status require_gfx950();
+bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb);
+lsn_status check_nf4(const lsn_nf4 *w, const char *what);
+}  // namespace lsn
 
 using namespace lsn;
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct BwdWs {
+  uint16_t *G;
+  uint16_t *Bt;
+  float *part_dB;
+  float *part_dA;
+  size_t bytes;
+};
+
+BwdWs bwd_layout(void *ws, int64_t T, int64_t K, int64_t N, int64_t r) {
+  const int64_t nc = (T + TN_CHUNK - 1) / TN_CHUNK;
+  char *p = static_cast<char *>(ws);
+  BwdWs w;
+  size_t off = 0;
+  w.G = reinterpret_cast<uint16_t *>(p + off);
+  off += align256((size_t)(T * r * 2));
+  w.Bt = reinterpret_cast<uint16_t *>(p + off);
+  off += align256((size_t)(r * N * 2));
+  w.part_dB = reinterpret_cast<float *>(p + off);
+  off += align256((size_t)(nc * N * r * 4));
+  w.part_dA = reinterpret_cast<float *>(p + off);
+  off += align256((size_t)(nc * K * r * 4));
+  w.bytes = off;
+  return w;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+lsn_status check_linear(const lsn_lora_linear *L, const char *what) {
+  if (!L) return fail(LSN_E_ARG, "%s: null linear descriptor", what);
+  if (L->T < 1 || L->K < 64 || L->N < 64 || L->K % 64 || L->N % 64)
+    return fail(LSN_E_ARG, "%s: need T >= 1 and K, N positive multiples of 64 (got T=%lld K=%lld N=%lld)", what,
+                (long long)L->T, (long long)L->K, (long long)L->N);
+  if (L->r < 8 || L->r > 32 || L->r % 8)
+    return fail(LSN_E_ARG, "%s: rank r must be 8, 16, 24 or 32 (got %lld)", what, (long long)L->r);
+  if (L->W.kind == LSN_W_NF4) {
+    lsn_status st = check_nf4(&L->W.nf4, what);
+    if (st != LSN_OK) return st;
+    if (L->W.nf4.rows != L->N || L->W.nf4.cols != L->K)
+      return fail(LSN_E_ARG, "%s: NF4 W is %lld x %lld, expected N x K = %lld x %lld", what,
+                  (long long)L->W.nf4.rows, (long long)L->W.nf4.cols, (long long)L->N, (long long)L->K);
+  } else if (L->W.kind == LSN_W_BF16) {
+    if (!L->W.bf16 || !aligned16(L->W.bf16)) return fail(LSN_E_ARG, "%s: bf16 W null or not 16-byte aligned", what);
+  } else {
+    return fail(LSN_E_ARG, "%s: unknown weight kind %d", what, L->W.kind);
+  }
+  if (!L->A || !L->B || !aligned16(L->A) || !aligned16(L->B))
+    return fail(LSN_E_ARG, "%s: A and B must be non-null and 16-byte aligned", what);
+  return LSN_OK;
+}
+
+// The input byte ranges of a linear's frozen weight (three arrays for NF4, one for bf16).
+int w_ranges(const lsn_lora_linear *L, const void **p, size_t *n) {
+  if (L->W.kind == LSN_W_NF4) {
+    const size_t e = (size_t)(L->N * L->K);
+    p[0] = L->W.nf4.codes;   n[0] = e / 2;
+    p[1] = L->W.nf4.qabsmax; n[1] = e / 64;
+    p[2] = L->W.nf4.absmax2; n[2] = e / 16384 * 4;
+    return 3;
+  }
+  p[0] = L->W.bf16;
+  n[0] = (size_t)(L->N * L->K * 2);
+  return 1;
+}
+
+GemmArgs base_args(const lsn_lora_linear *L) {
+  GemmArgs a{};
+  a.r = (int)L->r;
+  a.scale = L->scale;
+  if (L->W.kind == LSN_W_NF4) {
+    a.codes = L->W.nf4.codes;
+    a.qabsmax = L->W.nf4.qabsmax;
+    a.absmax2 = L->W.nf4.absmax2;
+    a.mean = L->W.nf4.mean;
+  } else {
+    a.w16 = L->W.bf16;
+  }
+  return a;
+}
+
+}  // namespace
 
 extern "C" {
 
 size_t lora_linear_ws_bytes(int64_t T, int64_t K, int64_t N, int64_t r) {
-  (void)T; (void)K; (void)N; (void)r;
-  return 0;
+  if (T < 1 || K < 1 || N < 1 || r < 1) return 0;
+  return bwd_layout(nullptr, T, K, N, r).bytes;
 }
 
-lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uint16_t *X,
-                           uint16_t *Y, uint16_t *U, void *ws, size_t ws_bytes, void *stream) {
-  (void)L; (void)adapters; (void)X; (void)Y; (void)U; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(LSN_E_STATE, "lora_linear_fwd: not built yet");
+lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uint16_t *X, uint16_t *Y,
+                           uint16_t *U, void *ws, size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  lsn_status st = check_linear(L, "lora_linear_fwd");
+  if (st != LSN_OK) return st;
+  const int64_t T = L->T, K = L->K, N = L->N, r = L->r;
+  if (!X || !Y || !aligned16(X) || !aligned16(Y))
+    return fail(LSN_E_ARG, "lora_linear_fwd: X and Y must be non-null and 16-byte aligned");
+  if (adapters && (!U || !aligned16(U)))
+    return fail(LSN_E_ARG, "lora_linear_fwd: U must be non-null and 16-byte aligned when adapters are on");
+  const size_t yb = (size_t)(T * N * 2), ub = (size_t)(T * r * 2);
+  const void *ins[6] = {X, L->A, L->B};
+  size_t inb[6] = {(size_t)(T * K * 2), (size_t)(r * K * 2), (size_t)(N * r * 2)};
+  const int n_in = 3 + w_ranges(L, ins + 3, inb + 3);
+  for (int i = 0; i < n_in; ++i) {
+    if (ranges_overlap(Y, yb, ins[i], inb[i]) || (adapters && ranges_overlap(U, ub, ins[i], inb[i])))
+      return fail(LSN_E_ARG, "lora_linear_fwd: an output overlaps an input");
+  }
+  if (adapters && ranges_overlap(Y, yb, U, ub)) return fail(LSN_E_ARG, "lora_linear_fwd: Y overlaps U");
+  if ((st = require_gfx950()) != LSN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (adapters && (st = launch_rowproj(X, T, K, L->A, (int)r, U, s)) != LSN_OK) return st;
+  GemmArgs a = base_args(L);
+  a.M = T;
+  a.Nout = N;
+  a.Kred = K;
+  a.act = X;
+  a.ldw = K;
+  a.lr_act = U;
+  a.lr_w = L->B;
+  a.adapters = adapters ? 1 : 0;
+  a.out = Y;
+  return launch_gemm(GEMM_NT, L->W.kind == LSN_W_NF4 ? W_IS_NF4 : W_IS_BF16, EPI_BF16, a, s);
 }
 
-lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const uint16_t *dY,
-                           const uint16_t *U, void *dX, int32_t dx_mode, float *dA, float *dB,
-                           int32_t grad_mode, void *ws, size_t ws_bytes, void *stream) {
-  (void)L; (void)X; (void)dY; (void)U; (void)dX; (void)dx_mode; (void)dA; (void)dB;
-  (void)grad_mode; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(LSN_E_STATE, "lora_linear_bwd: not built yet");
+lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const uint16_t *dY, const uint16_t *U,
+                           void *dX, int32_t dx_mode, float *dA, float *dB, int32_t grad_mode, void *ws,
+                           size_t ws_bytes, void *stream) {
+  lsn_status st = check_linear(L, "lora_linear_bwd");
+  if (st != LSN_OK) return st;
+  const int64_t T = L->T, K = L->K, N = L->N, r = L->r;
+  if (!X || !dY || !U || !dX || !dA || !dB || !ws)
+    return fail(LSN_E_ARG, "lora_linear_bwd: null pointer argument");
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(U) || !aligned16(dX) || ((uintptr_t)ws & 255))
+    return fail(LSN_E_ARG, "lora_linear_bwd: X, dY, U, dX must be 16-byte and ws 256-byte aligned");
+  if (dx_mode != LSN_DX_BF16_SET && dx_mode != LSN_DX_F32_ADD)
+    return fail(LSN_E_ARG, "lora_linear_bwd: unknown dX mode %d", dx_mode);
+  if (grad_mode != LSN_GRAD_SET && grad_mode != LSN_GRAD_ADD)
+    return fail(LSN_E_ARG, "lora_linear_bwd: unknown gradient mode %d", grad_mode);
+  const BwdWs need = bwd_layout(ws, T, K, N, r);
+  if (ws_bytes < need.bytes)
+    return fail(LSN_E_ARG, "lora_linear_bwd: workspace too small (%zu < %zu)", ws_bytes, need.bytes);
+  const size_t dxb = (size_t)(T * K * (dx_mode == LSN_DX_F32_ADD ? 4 : 2));
+  const void *outs[] = {dX, dA, dB, ws};
+  const size_t outb[] = {dxb, (size_t)(r * K * 4), (size_t)(N * r * 4), need.bytes};
+  const void *ins[8] = {X, dY, U, L->A, L->B};
+  size_t inb[8] = {(size_t)(T * K * 2), (size_t)(T * N * 2), (size_t)(T * r * 2), (size_t)(r * K * 2),
+                   (size_t)(N * r * 2)};
+  const int n_in = 5 + w_ranges(L, ins + 5, inb + 5);
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < n_in; ++i)
+      if (ranges_overlap(outs[o], outb[o], ins[i], inb[i]))
+        return fail(LSN_E_ARG, "lora_linear_bwd: an output overlaps an input");
+    for (int p = 0; p < o; ++p)
+      if (ranges_overlap(outs[o], outb[o], outs[p], outb[p]))
+        return fail(LSN_E_ARG, "lora_linear_bwd: two outputs overlap");
+  }
+  if ((st = require_gfx950()) != LSN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nc = (T + TN_CHUNK - 1) / TN_CHUNK;
+  if ((st = launch_transpose_b(L->B, N, (int)r, need.Bt, s)) != LSN_OK) return st;
+  if ((st = launch_rowproj(dY, T, N, need.Bt, (int)r, need.G, s)) != LSN_OK) return st;
+  GemmArgs a = base_args(L);
+  a.M = T;
+  a.Nout = K;
+  a.Kred = N;
+  a.act = dY;
+  a.ldw = K;
+  a.lr_act = need.G;
+  a.lr_w = L->A;
+  a.adapters = 1;
+  a.out = dX;
+  if ((st = launch_gemm(GEMM_NN, L->W.kind == LSN_W_NF4 ? W_IS_NF4 : W_IS_BF16,
+                        dx_mode == LSN_DX_F32_ADD ? EPI_F32_ADD : EPI_BF16, a, s)) != LSN_OK)
+    return st;
+  const int acc = grad_mode == LSN_GRAD_ADD;
+  if ((st = launch_tn_partial(dY, T, N, U, (int)r, need.part_dB, s)) != LSN_OK) return st;
+  if ((st = launch_tn_reduce(need.part_dB, nc, N, (int)r, L->scale, acc, 0, dB, s)) != LSN_OK) return st;
+  if ((st = launch_tn_partial(X, T, K, need.G, (int)r, need.part_dA, s)) != LSN_OK) return st;
+  return launch_tn_reduce(need.part_dA, nc, K, (int)r, L->scale, acc, 1, dA, s);
 }
 
 }  // extern "C"
