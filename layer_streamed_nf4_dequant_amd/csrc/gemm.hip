@@ -52,34 +52,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4_t v) { return __builtin_bit_ca
 // operand tile loaders
 // ---------------------------------------------------------------------------------------------
 
-// A 256 x 64 bf16 tile of a row-major [rows][ld] matrix whose reduction dimension is
-// contiguous (X and dY, and W in the forward). Thread t loads chunk t%8 of rows t/8 + 32 i.
-struct RowTile {
-  u32x4_t v[8];
-};
-
-__device__ __forceinline__ void load_rows(RowTile &st, const uint16_t *__restrict__ base, int64_t rows,
-                                          int64_t ld, int64_t r0, int64_t k0, int t) {
-  const int c = t & 7, rr = t >> 3;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t row = r0 + rr + 32 * i;
-    if (row < rows)
-      st.v[i] = *reinterpret_cast<const u32x4_t *>(base + row * ld + k0 + 8 * c);
-    else
-      st.v[i] = u32x4_t{0, 0, 0, 0};
-  }
-}
-
-__device__ __forceinline__ void store_rows(char *lds, const RowTile &st, int t) {
-  const int c = t & 7, rr = t >> 3;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = rr + 32 * i;
-    *reinterpret_cast<u32x4_t *>(lds + lds_off(row, c)) = st.v[i];
-  }
-}
-
 // Forward, NF4 W[N][K]: rows n0 .. n0+255, columns k0 .. k0+63 (exactly one NF4 block per
 // row). Thread t handles half (t%2) of row (t/2) and of row 128 + t/2: 32 codes each.
 struct Nf4RowTile {
@@ -93,18 +65,12 @@ __device__ __forceinline__ void load_nf4_rows(Nf4RowTile &st, const GemmArgs &a,
   const int half = t & 1;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const int64_t n = n0 + p * 128 + (t >> 1);
-    if (n < a.Nout) {
-      const int64_t e = n * a.Kred + k0;                 // element index of the block start
-      st.codes[p] = *reinterpret_cast<const u32x4_t *>(a.codes + e / 2 + 16 * half);
-      const int64_t b = e >> 6;
-      st.v[p] = a.qabsmax[b];
-      st.s2[p] = a.absmax2[b >> 8];
-    } else {
-      st.codes[p] = u32x4_t{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};   // level 0
-      st.v[p] = 0;
-      st.s2[p] = 0.0f;
-    }
+    const int64_t n = min(n0 + p * 128 + (t >> 1), a.Nout - 1);   // clamped: unstored columns
+    const int64_t e = n * a.Kred + k0;                               // element index of the block
+    st.codes[p] = *reinterpret_cast<const u32x4_t *>(a.codes + e / 2 + 16 * half);
+    const int64_t b = e >> 6;
+    st.v[p] = a.qabsmax[b];
+    st.s2[p] = a.absmax2[b >> 8];
   }
 }
 
@@ -120,22 +86,6 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t w, float c, const float *__
                  pack_bf16x2(f[6], f[7])};
 }
 
-__device__ __forceinline__ void store_nf4_rows(char *lds, const Nf4RowTile &st, int t, float mu,
-                                               const float *__restrict__ sq,
-                                               const float *__restrict__ scode8) {
-  const int half = t & 1;
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int row = p * 128 + (t >> 1);
-    const float c = decode_absmax(scode8[st.v[p] + 127], st.s2[p], mu);
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const uint32_t w = st.codes[p][cc];
-      *reinterpret_cast<u32x4_t *>(lds + lds_off(row, 4 * half + cc)) = dequant8(w, c, sq);
-    }
-  }
-}
-
 // Backward (dX), W[N][K] read transposed: the tile covers W rows (reduction) n0 .. n0+63 and
 // columns (output) k0 .. k0+255, and is stored in LDS as [256 output columns][64 reductions].
 // Thread t handles the 8 x 8 block rows n0 + 8 (t/32) + i, columns k0 + 8 (t%32) + e.
@@ -146,38 +96,12 @@ struct Bf16ColTile {
 __device__ __forceinline__ void load_bf16_cols(Bf16ColTile &st, const GemmArgs &a, int64_t n0, int64_t k0,
                                                int t) {
   const int rg = t >> 5, cg = t & 31;
-  const int64_t col = k0 + 8 * cg;
+  const int64_t col = min(k0 + 8 * cg, a.Nout - 8);     // clamped: unstored output columns
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t n = n0 + 8 * rg + i;
-    if (col < a.Nout)
-      st.v[i] = *reinterpret_cast<const u32x4_t *>(a.w16 + n * a.ldw + col);
-    else
-      st.v[i] = u32x4_t{0, 0, 0, 0};
+    st.v[i] = *reinterpret_cast<const u32x4_t *>(a.w16 + n * a.ldw + col);
   }
-}
-
-// out[e] holds column e of the 8 x 8 bf16 block: {in[0].e, in[1].e, ..., in[7].e}
-__device__ __forceinline__ void transpose8x8(const uint32_t (&in)[8][4], u32x4_t (&out)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) out[e][q] = __builtin_amdgcn_perm(in[2 * q + 1][e >> 1], in[2 * q][e >> 1], sel);
-  }
-}
-
-__device__ __forceinline__ void store_bf16_cols(char *lds, const Bf16ColTile &st, int t) {
-  const int rg = t >> 5, cg = t & 31;
-  uint32_t in[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) in[i][q] = st.v[i][q];
-  u32x4_t out[8];
-  transpose8x8(in, out);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4_t *>(lds + lds_off(8 * cg + e, rg)) = out[e];
 }
 
 struct Nf4ColTile {
@@ -189,69 +113,134 @@ struct Nf4ColTile {
 __device__ __forceinline__ void load_nf4_cols(Nf4ColTile &st, const GemmArgs &a, int64_t n0, int64_t k0,
                                               int t) {
   const int rg = t >> 5, cg = t & 31;
-  const int64_t col = k0 + 8 * cg;
+  const int64_t col = min(k0 + 8 * cg, a.Nout - 8);     // clamped: unstored output columns
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t n = n0 + 8 * rg + i;
-    if (col < a.Nout) {
-      const int64_t e = n * a.ldw + col;
-      st.codes[i] = *reinterpret_cast<const uint32_t *>(a.codes + e / 2);
-      const int64_t b = e >> 6;
-      st.v[i] = a.qabsmax[b];
-      st.s2[i] = a.absmax2[b >> 8];
-    } else {
-      st.codes[i] = 0x77777777u;
-      st.v[i] = 0;
-      st.s2[i] = 0.0f;
-    }
+    const int64_t e = n * a.ldw + col;
+    st.codes[i] = *reinterpret_cast<const uint32_t *>(a.codes + e / 2);
+    const int64_t b = e >> 6;
+    st.v[i] = a.qabsmax[b];
+    st.s2[i] = a.absmax2[b >> 8];
   }
 }
 
-__device__ __forceinline__ void store_nf4_cols(char *lds, const Nf4ColTile &st, int t, float mu,
-                                               const float *__restrict__ sq,
-                                               const float *__restrict__ scode8) {
-  const int rg = t >> 5, cg = t & 31;
-  uint32_t in[8][4];
+// ---------------------------------------------------------------------------------------------
+// direct-to-LDS loads (gfx950 global_load_lds_dwordx4): lane l of one wave instruction writes the
+// 16 bytes at (wave-uniform LDS base) + 16 l, so each instruction fills one 1 KB LDS segment =
+// 8 rows of 128 B. Lane l loads the global chunk that belongs at its slot: row 8 sg + l/8,
+// physical chunk l%8, i.e. logical chunk (l%8) ^ f(row).
+// ---------------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Per-lane byte offsets of the 8 chunks a lane loads for one 256 x 64 tile; they do not depend on
+// the K-step (the step's byte offset goes in the scalar offset), so they stay in 8 VGPRs.
+struct DirectRows {
+  uint32_t voff[8];
+};
+
+__device__ __forceinline__ void make_direct_rows(DirectRows &d, int64_t rows, int64_t ld, int64_t r0, int wave,
+                                                 int lane) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float c = decode_absmax(scode8[st.v[i] + 127], st.s2[i], mu);
-    const u32x4_t d = dequant8(st.codes[i], c, sq);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) in[i][q] = d[q];
+    const int sg = wave * 8 + i;
+    const int row = sg * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+    const int64_t grow = min(r0 + row, rows - 1);     // clamped rows feed only unstored outputs
+    d.voff[i] = (uint32_t)((grow * ld + 8 * c) * 2);
   }
-  u32x4_t out[8];
-  transpose8x8(in, out);
+}
+
+__device__ __forceinline__ void issue_rows_direct(char *lds_tile, __amdgpu_buffer_rsrc_t rsrc, const DirectRows &d,
+                                                  uint32_t k_bytes, int wave) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4_t *>(lds + lds_off(8 * cg + e, rg)) = out[e];
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(lds_tile + (wave * 8 + i) * 1024), 16, d.voff[i],
+                                             k_bytes, 0, 0);
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  // raw buffer, no stride; loads past num_records return 0 (never fault)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// wait until every vector-memory operation of this wave has completed (incl. direct-to-LDS)
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---------------------------------------------------------------------------------------------
-// the kernel
+// register path for W (NF4, or transposed bf16 in the backward): the staged codes or values are
+// turned into eight 16-byte chunks of bf16, produced two at a time during the MFMA sub-steps.
 // ---------------------------------------------------------------------------------------------
+struct NoStage {};
 
 template <int LAYOUT, int WKIND>
-struct BTile;
-template <> struct BTile<GEMM_NT, W_IS_BF16> { typedef RowTile type; };
-template <> struct BTile<GEMM_NT, W_IS_NF4> { typedef Nf4RowTile type; };
-template <> struct BTile<GEMM_NN, W_IS_BF16> { typedef Bf16ColTile type; };
-template <> struct BTile<GEMM_NN, W_IS_NF4> { typedef Nf4ColTile type; };
+struct BStage;
+template <> struct BStage<GEMM_NT, W_IS_BF16> { typedef NoStage type; };
+template <> struct BStage<GEMM_NT, W_IS_NF4> { typedef Nf4RowTile type; };
+template <> struct BStage<GEMM_NN, W_IS_BF16> { typedef Bf16ColTile type; };
+template <> struct BStage<GEMM_NN, W_IS_NF4> { typedef Nf4ColTile type; };
+
+// decoded block constants of a staged NF4 tile (2 rows forward, 8 rows backward)
+template <int LAYOUT> struct Decoded;
+template <> struct Decoded<GEMM_NT> { float c[2]; };
+template <> struct Decoded<GEMM_NN> { float c[8]; };
 
 template <int LAYOUT, int WKIND>
-__device__ __forceinline__ void load_b(typename BTile<LAYOUT, WKIND>::type &st, const GemmArgs &a,
-                                       int64_t n0, int64_t kstep0, int t) {
-  if constexpr (LAYOUT == GEMM_NT && WKIND == W_IS_BF16) load_rows(st, a.w16, a.Nout, a.ldw, n0, kstep0, t);
-  else if constexpr (LAYOUT == GEMM_NT) load_nf4_rows(st, a, n0, kstep0, t);
-  else if constexpr (WKIND == W_IS_BF16) load_bf16_cols(st, a, kstep0, n0, t);
-  else load_nf4_cols(st, a, kstep0, n0, t);
+__device__ __forceinline__ void load_b(typename BStage<LAYOUT, WKIND>::type &st, const GemmArgs &a, int64_t n0,
+                                       int64_t kstep0, int t) {
+  if constexpr (LAYOUT == GEMM_NT && WKIND == W_IS_NF4) load_nf4_rows(st, a, n0, kstep0, t);
+  else if constexpr (LAYOUT == GEMM_NN && WKIND == W_IS_BF16) load_bf16_cols(st, a, kstep0, n0, t);
+  else if constexpr (LAYOUT == GEMM_NN && WKIND == W_IS_NF4) load_nf4_cols(st, a, kstep0, n0, t);
 }
 
 template <int LAYOUT, int WKIND>
-__device__ __forceinline__ void store_b(char *lds, const typename BTile<LAYOUT, WKIND>::type &st, int t,
-                                        float mu, const float *sq, const float *scode8) {
-  if constexpr (LAYOUT == GEMM_NT && WKIND == W_IS_BF16) store_rows(lds, st, t);
-  else if constexpr (LAYOUT == GEMM_NT) store_nf4_rows(lds, st, t, mu, sq, scode8);
-  else if constexpr (WKIND == W_IS_BF16) store_bf16_cols(lds, st, t);
-  else store_nf4_cols(lds, st, t, mu, sq, scode8);
+__device__ __forceinline__ Decoded<LAYOUT> decode_b(const typename BStage<LAYOUT, WKIND>::type &st, float mu,
+                                                    const float *__restrict__ scode8) {
+  Decoded<LAYOUT> d;
+  if constexpr (WKIND == W_IS_NF4) {
+    constexpr int R = (LAYOUT == GEMM_NT) ? 2 : 8;
+#pragma unroll
+    for (int i = 0; i < R; ++i) d.c[i] = decode_absmax(scode8[st.v[i] + 127], st.s2[i], mu);
+  }
+  return d;
+}
+
+__device__ __forceinline__ float deq1(uint32_t w, int e, float c, const float *__restrict__ sq) {
+  const int shift = 8 * (e >> 1) + ((e & 1) ? 0 : 4);
+  return __fmul_rn(sq[(w >> shift) & 15u], c);
+}
+
+// chunk idx of the staged tile, and its LDS offset
+template <int LAYOUT, int WKIND>
+__device__ __forceinline__ u32x4_t make_chunk(const typename BStage<LAYOUT, WKIND>::type &st,
+                                              const Decoded<LAYOUT> &d, int idx, const float *__restrict__ sq) {
+  if constexpr (LAYOUT == GEMM_NT && WKIND == W_IS_NF4) {
+    return dequant8(st.codes[idx >> 2][idx & 3], d.c[idx >> 2], sq);
+  } else if constexpr (LAYOUT == GEMM_NN && WKIND == W_IS_NF4) {
+    u32x4_t o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = pack_bf16x2(deq1(st.codes[2 * q], idx, d.c[2 * q], sq), deq1(st.codes[2 * q + 1], idx, d.c[2 * q + 1], sq));
+    return o;
+  } else if constexpr (LAYOUT == GEMM_NN && WKIND == W_IS_BF16) {
+    const uint32_t sel = (idx & 1) ? 0x07060302u : 0x05040100u;
+    u32x4_t o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(st.v[2 * q + 1][idx >> 1], st.v[2 * q][idx >> 1], sel);
+    return o;
+  } else {
+    return u32x4_t{0, 0, 0, 0};
+  }
+}
+
+template <int LAYOUT>
+__device__ __forceinline__ int chunk_off(int idx, int t) {
+  if constexpr (LAYOUT == GEMM_NT) {
+    const int row = (idx >> 2) * 128 + (t >> 1);
+    return lds_off(row, 4 * (t & 1) + (idx & 3));
+  } else {
+    return lds_off(8 * (t & 31) + idx, t >> 5);
+  }
 }
 
 // LoRA operand fragments for one 32x32x16 step over r-columns j0 .. j0+15.
@@ -282,8 +271,15 @@ __device__ __forceinline__ bf16x8 lora_w_frag(const GemmArgs &a, int64_t n, int 
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// the kernel. MFMA operands are (W fragment, activation fragment), so the accumulator holds
+// out^T: lane l has output row m = 32 i + l%32 and columns n = 32 j + 8 (e/4) + 4 (l/32) + e%4,
+// four consecutive columns per group e/4, stored 8 (bf16) or 16 (fp32) bytes at a time.
+// ---------------------------------------------------------------------------------------------
 template <int LAYOUT, int WKIND, int EPI>
 __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs a) {
+  constexpr bool B_DIRECT = (LAYOUT == GEMM_NT && WKIND == W_IS_BF16);
+  typedef typename BStage<LAYOUT, WKIND>::type Stage;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char *lds_a = smem;                              // 2 buffers
   char *lds_b = smem + 2 * TILE_BYTES;             // 2 buffers
@@ -295,27 +291,30 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs a) {
   const int wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // tile coordinates: consecutive workgroups walk down M (the activation tiles) for one N tile,
-  // so the workgroups resident at a time share W tiles
+  // tile coordinates: consecutive workgroups walk down M for one N tile, so the workgroups
+  // resident at a time share W tiles
   const int64_t tiles_m = (a.M + BM - 1) / BM;
   const int64_t m0 = (int64_t)(blockIdx.x % tiles_m) * BM;
   const int64_t n0 = (int64_t)(blockIdx.x / tiles_m) * BN;
 
-  if (WKIND == W_IS_NF4) {
+  if constexpr (WKIND == W_IS_NF4) {
     if (t < 16) sq[t] = a.q[t];
     if (t < 255) scode8[t] = int8_level(t - 127);
   }
 
   floatx16_t acc[4][4];
-  // ---- LoRA prologue: acc = s * (lr_act . lr_w^T) over r, or +0 ----
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  // ---- LoRA prologue: acc = s * (lr_w . lr_act^T) over r, or +0 with adapters off ----
   if (a.adapters) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    for (int j0 = 0; j0 < a.r; j0 += 16) {
+    for (int h = 0; h < 2; ++h) {
+      const int j0 = 16 * h;
+      if (j0 >= a.r) break;
       bf16x8 fa[4], fb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) fa[i] = lora_act_frag(a, m0 + wm * 128 + 32 * i + (lane & 31), j0, lane);
@@ -324,7 +323,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -332,77 +331,109 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs a) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = __fmul_rn(a.scale, acc[i][j][e]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   }
 
-  // ---- main loop over the reduction dimension ----
-  const int64_t nk = a.Kred / BK;
-  RowTile sa;
-  typename BTile<LAYOUT, WKIND>::type sb;
-  load_rows(sa, a.act, a.M, a.Kred, m0, 0, t);
-  load_b<LAYOUT, WKIND>(sb, a, n0, 0, t);
+  const int nk = (int)(a.Kred / BK);
+  Stage S0, S1;
+  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.act, a.M * a.Kred * 2);
+  DirectRows da;
+  make_direct_rows(da, a.M, a.Kred, m0, wave, lane);
+  __amdgpu_buffer_rsrc_t rs_b;
+  DirectRows db;
+  if constexpr (B_DIRECT) {
+    rs_b = make_rsrc(a.w16, a.Nout * a.ldw * 2);
+    make_direct_rows(db, a.Nout, a.ldw, n0, wave, lane);
+  }
+
+  // ---- prologue: step 0 into buffer 0; W of step 1 into registers ----
+  // Prefetches past the last K-step are clamped to it: they re-load valid memory into the buffer
+  // or staging set that is never read again, which keeps the loop free of tail code.
+  const int k_last = nk - 1;
+  issue_rows_direct(lds_a, rs_a, da, 0, wave);
+  if constexpr (B_DIRECT) {
+    issue_rows_direct(lds_b, rs_b, db, 0, wave);
+  } else {
+    load_b<LAYOUT, WKIND>(S0, a, n0, 0, t);
+    load_b<LAYOUT, WKIND>(S1, a, n0, (int64_t)min(1, k_last) * BK, t);
+  }
   __syncthreads();   // codebook tables visible
-  store_rows(lds_a, sa, t);
-  store_b<LAYOUT, WKIND>(lds_b, sb, t, a.mean, sq, scode8);
+  if constexpr (!B_DIRECT) {
+    const Decoded<LAYOUT> d = decode_b<LAYOUT, WKIND>(S0, a.mean, scode8);
+#pragma unroll
+    for (int idx = 0; idx < 8; ++idx)
+      *reinterpret_cast<u32x4_t *>(lds_b + chunk_off<LAYOUT>(idx, t)) = make_chunk<LAYOUT, WKIND>(S0, d, idx, sq);
+  }
+  wait_vm_all();
   __syncthreads();
 
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = (int)(kt & 1);
+  // one K-step on buffer kt%2 while step kt+1 lands in the other buffer and (register path)
+  // the W of step kt+2 is loaded into the free staging set
+  auto step = [&](int kt, Stage &s_next, Stage &s_free) {
+    const int cur = kt & 1;
     const char *la = lds_a + cur * TILE_BYTES;
     const char *lb = lds_b + cur * TILE_BYTES;
-    if (kt + 1 < nk) {
-      load_rows(sa, a.act, a.M, a.Kred, m0, (kt + 1) * BK, t);
-      load_b<LAYOUT, WKIND>(sb, a, n0, (kt + 1) * BK, t);
-    }
+    char *lb_next = lds_b + (cur ^ 1) * TILE_BYTES;
+    if constexpr (!B_DIRECT) load_b<LAYOUT, WKIND>(s_free, a, n0, (int64_t)min(kt + 2, k_last) * BK, t);
+    const uint32_t kb = (uint32_t)min(kt + 1, k_last) * BK * 2;
+    issue_rows_direct(lds_a + (cur ^ 1) * TILE_BYTES, rs_a, da, kb, wave);
+    if constexpr (B_DIRECT) issue_rows_direct(lb_next, rs_b, db, kb, wave);
+    Decoded<LAYOUT> d;
+    if constexpr (!B_DIRECT) d = decode_b<LAYOUT, WKIND>(s_next, a.mean, scode8);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       const int chunk = 2 * s + (lane >> 5);
       bf16x8 fa[4], fb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + 32 * i + (lane & 31);
-        fa[i] = *reinterpret_cast<const bf16x8 *>(la + lds_off(row, chunk));
-      }
+      for (int i = 0; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8 *>(la + lds_off(wm * 128 + 32 * i + (lane & 31), chunk));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wn * 128 + 32 * j + (lane & 31);
-        fb[j] = *reinterpret_cast<const bf16x8 *>(lb + lds_off(row, chunk));
-      }
+      for (int j = 0; j < 4; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8 *>(lb + lds_off(wn * 128 + 32 * j + (lane & 31), chunk));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+      if constexpr (!B_DIRECT) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          *reinterpret_cast<u32x4_t *>(lb_next + chunk_off<LAYOUT>(2 * s + h, t)) =
+              make_chunk<LAYOUT, WKIND>(s_next, d, 2 * s + h, sq);
+      }
     }
-    if (kt + 1 < nk) {
-      store_rows(lds_a + (cur ^ 1) * TILE_BYTES, sa, t);
-      store_b<LAYOUT, WKIND>(lds_b + (cur ^ 1) * TILE_BYTES, sb, t, a.mean, sq, scode8);
-    }
+    wait_vm_all();
     __syncthreads();
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, S1, S0);
+    if (kt + 1 < nk) step(kt + 1, S0, S1);
   }
 
-  // ---- epilogue: lane holds column (lane % 32) and rows 8 (e/4) + 4 (lane/32) + e%4 ----
+  // ---- epilogue ----
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + wm * 128 + 32 * i + (lane & 31);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 128 + 32 * j + (lane & 31);
-      if (n >= a.Nout) continue;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (m >= a.M) continue;
-        if (EPI == EPI_BF16) {
-          const __bf16 h = (__bf16)acc[i][j][e];
-          reinterpret_cast<uint16_t *>(a.out)[m * a.Nout + n] = __builtin_bit_cast(uint16_t, h);
-        } else {
-          float *o = reinterpret_cast<float *>(a.out) + m * a.Nout + n;
-          *o = __fadd_rn(*o, acc[i][j][e]);
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + wn * 128 + 32 * j + 8 * g + 4 * (lane >> 5);
+        if (m < a.M && n < a.Nout) {
+          const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1], v2 = acc[i][j][4 * g + 2],
+                      v3 = acc[i][j][4 * g + 3];
+          if constexpr (EPI == EPI_BF16) {
+            uint2 o;
+            o.x = pack_bf16x2(v0, v1);
+            o.y = pack_bf16x2(v2, v3);
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + m * a.Nout + n) = o;
+          } else {
+            floatx4_t *o = reinterpret_cast<floatx4_t *>(reinterpret_cast<float *>(a.out) + m * a.Nout + n);
+            floatx4_t cur = *o;
+            cur[0] = __fadd_rn(cur[0], v0);
+            cur[1] = __fadd_rn(cur[1], v1);
+            cur[2] = __fadd_rn(cur[2], v2);
+            cur[3] = __fadd_rn(cur[3], v3);
+            *o = cur;
+          }
         }
       }
     }
