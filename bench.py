@@ -1,0 +1,181 @@
+"""Benchmark: training tokens/s through the 8B-shaped NF4 LoRA projection stack on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode streamed|resident|no_h2d]
+                    [--config C3] [--no-cpu-baseline]
+
+Workload (Llama-3.1-8B projection shapes): 32 decoder layers, hidden 4096, q/o 4096x4096,
+k/v 4096->1024, gate/up 4096->14336, down 14336->4096, NF4 base with double-quantised
+absmax, LoRA r=16 alpha=32 on all seven projections, T = 4096 token rows (2 x 2048), bf16
+activations; the base streams from pinned host memory through a 2-slot device pool. One step
+= forward over all layers, then per layer (in reverse) the re-fetch, the recomputed forward and
+the backward (dX, dA, dB). Inputs are seeded synthetic tensors resident in HBM (the base in
+pinned host memory, as the method keeps it) before the timed region starts.
+
+Prints one JSON line. `value` = T * steps / wall time of the K timed steps. `roofline` is the
+dominant kernel, the fused NF4-dequant forward GEMM (k_gemm NT/NF4): achieved = algorithmic
+FLOPs of its launches in the timed steps / their summed durations, measured with HIP events
+recorded around every launch on the compute stream. `cpu_baseline` times the CPU oracle on a
+bounded sample (one layer, a subset of token rows) and scales it to the workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "training tokens/sec through 8B-shaped NF4 LoRA stack; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def traffic_from_profiles():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter summary,
+    if one exists for the current kernel build (null otherwise)."""
+    path = os.path.join(ROOT, "profiles", "gemm_nt_nf4_llama8b_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        return d.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, seed: int = 0, rows: int = 32):
+    """Oracle (numpy, fp64 LoRA + fp32 NF4) on one layer of the workload with `rows` token rows:
+    dequant of all 7 projections twice (forward and backward visit) plus forward, recomputed
+    forward and backward on the sampled rows. Scaled to the workload as
+    T / (L * (t_dequant + (T / rows) * t_rows))."""
+    import numpy as np
+    from layer_streamed_nf4_dequant_amd import inputs
+    from oracle import lora as olora
+    from oracle import nf4 as onf4
+
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(seed)
+    t_deq = 0.0
+    t_rows = 0.0
+    for name, K, N in cfg.projections():
+        W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+        p = onf4.pack(W)
+        del W
+        t0 = time.perf_counter()
+        Wh = onf4.bf16_to_f32(onf4.dequant_bf16(p))          # forward visit
+        Wh = onf4.bf16_to_f32(onf4.dequant_bf16(p))          # backward visit (re-dequantised)
+        t_deq += time.perf_counter() - t0
+        A = onf4.bf16_to_f32(inputs.to_bf16_bits(rng.uniform(-K ** -0.5, K ** -0.5, (cfg.r, K)).astype(np.float32)))
+        B = onf4.bf16_to_f32(inputs.to_bf16_bits((rng.standard_normal((N, cfg.r)) * 0.01).astype(np.float32)))
+        X = onf4.bf16_to_f32(inputs.to_bf16_bits(rng.standard_normal((rows, K), dtype=np.float32)))
+        dY = onf4.bf16_to_f32(inputs.to_bf16_bits(rng.standard_normal((rows, N), dtype=np.float32)))
+        t0 = time.perf_counter()
+        olora.forward(X, Wh, A, B, cfg.scale)                # forward
+        olora.forward(X, Wh, A, B, cfg.scale)                # recomputed forward
+        olora.backward(X, dY, Wh, A, B, cfg.scale)           # backward
+        t_rows += time.perf_counter() - t0
+        del Wh
+    per_layer_full_T = t_deq + (cfg.T / rows) * t_rows
+    tok_s = cfg.T / (cfg.layers * per_layer_full_T)
+    return {"value": round(tok_s, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"1 of {cfg.layers} layers, {rows} of {cfg.T} token rows: NF4 dequant of all 7 "
+                       f"projections twice ({t_deq:.2f} s) + fp64 fwd/recompute/bwd on the sampled rows "
+                       f"({t_rows:.2f} s); derived tokens/s = T / (L * (t_dequant + T/rows * t_rows))")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--mode", default="streamed", choices=["streamed", "resident", "no_h2d"])
+    ap.add_argument("--config", default="C3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the method streams one GPU's layers; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from layer_streamed_nf4_dequant_amd import configs, lib
+    from layer_streamed_nf4_dequant_amd.stack import Stack
+
+    lib.load()
+    cfg = configs.CONFIGS[args.config]
+    print(f"[bench] setting up {cfg.name}: {cfg.layers} layers, T={cfg.T}, mode={args.mode}", flush=True)
+    t0 = time.perf_counter()
+    stack = Stack(cfg, modes=(args.mode,))
+    torch.cuda.synchronize()
+    print(f"[bench] setup {time.perf_counter() - t0:.1f} s; image {stack.image_bytes / 1e6:.2f} MB/layer",
+          flush=True)
+    for i in range(args.warmup):
+        ms = stack.step(args.mode)
+        print(f"[bench] warmup {i}: {ms:.1f} ms", flush=True)
+
+    gemm_events = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    step_ms = []
+    for i in range(args.steps):
+        step_ms.append(stack.step(args.mode, gemm_events=gemm_events))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    print(f"[bench] {args.steps} steps: {wall * 1e3 / args.steps:.1f} ms/step (events median "
+          f"{sorted(step_ms)[len(step_ms) // 2]:.1f} ms)", flush=True)
+
+    # dominant kernel: the fused forward GEMM launches of the timed steps
+    dur_ms, flops = 0.0, 0
+    for j, e0, e1 in gemm_events:
+        _, K, N = cfg.projections()[j]
+        dur_ms += e0.elapsed_time(e1)
+        flops += 2 * cfg.T * K * N + 2 * cfg.T * cfg.r * N
+    n_launch = len(gemm_events)
+    achieved = flops / (dur_ms * 1e-3) / 1e12 if dur_ms > 0 else 0.0
+    kernel = "k_gemm<NT,NF4> (fused NF4 dequant-into-LDS + bf16 MFMA + LoRA epilogue)" if cfg.base == "nf4" \
+        else "k_gemm<NT,BF16>"
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_from_profiles(),
+                "kernel": kernel, "launches": n_launch,
+                "avg_launch_us": round(dur_ms * 1e3 / max(n_launch, 1), 2)}
+
+    tokens = cfg.T * args.steps
+    value = tokens / wall
+    pool = stack.pool.stats() if stack.pool is not None else None
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} NF4-LoRA projection stack" if cfg.base == "nf4"
+                   else f"{cfg.name} LoRA projection stack",
+                   "layers": cfg.layers, "tokens_per_step": cfg.T, "hidden": cfg.hidden, "kv": cfg.kv,
+                   "inter": cfg.inter, "lora_rank": cfg.r, "lora_alpha": cfg.alpha, "base": cfg.base,
+                   "mode": args.mode, "pool_slots": cfg.pool_slots,
+                   "flops_per_step": cfg.flops_per_step(),
+                   "stack_tflops": round(cfg.flops_per_step() / (wall / args.steps) / 1e12, 1),
+                   "h2d_bytes_per_step": (pool["bytes_copied"] // (args.steps + args.warmup)) if pool else 0},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    stack.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

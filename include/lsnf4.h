@@ -159,11 +159,26 @@ typedef struct {
 /* Device workspace bytes lora_linear_fwd / lora_linear_bwd need for these shapes. */
 size_t lora_linear_ws_bytes(int64_t T, int64_t K, int64_t N, int64_t r);
 
+enum { LSN_ADAPTERS_OFF = 0, LSN_ADAPTERS_ON = 1, LSN_ADAPTERS_U_READY = 2 };
+
 /*
- * lora_linear_fwd - Y = bf16(X W^T + s U B^T) with U = bf16(X A^T) written to U (device
- * [T][r], required when adapters != 0, ignored otherwise). With adapters == 0 the adapter is
- * skipped and Y = bf16(X W^T), bit-identical to the adapters-on result with B = 0.
- * ws: device, at least lora_linear_ws_bytes(T, K, N, r). Async on `stream`.
+ * lora_down - the adapters' down-projections of up to 8 linears that share one input X [T][K]
+ * (device bf16): U_g = bf16(X A_g^T) for g < n, with A_g device bf16 [r_g][K] and U_g device
+ * bf16 [T][r_g]; r_g in {8, 16, 24, 32}, sum of r_g <= 128, K % 64 == 0. X is read once for all
+ * of them (in a decoder layer, q, k, v, gate and up all read the same input). A, r and U are
+ * host arrays of n entries. Async on `stream`.
+ */
+lsn_status lora_down(int64_t T, int64_t K, const uint16_t *X, int32_t n, const uint16_t *const *A,
+                     const int32_t *r, uint16_t *const *U, void *stream);
+
+/*
+ * lora_linear_fwd - Y = bf16(X W^T + s U B^T).
+ *   adapters == LSN_ADAPTERS_ON:      computes U = bf16(X A^T) into U (device [T][r]) first;
+ *   adapters == LSN_ADAPTERS_U_READY: U already holds bf16(X A^T) (from lora_down): one GEMM;
+ *   adapters == LSN_ADAPTERS_OFF:     the adapter is skipped and Y = bf16(X W^T), bit-identical
+ *                                     to the adapters-on result with B = 0; U is ignored.
+ * ws: device, at least lora_linear_ws_bytes(T, K, N, r) (may be NULL for the forward).
+ * Async on `stream`.
  */
 lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uint16_t *X,
                            uint16_t *Y, uint16_t *U, void *ws, size_t ws_bytes, void *stream);

@@ -35,6 +35,16 @@ struct GemmArgs {
 
 lsn_status launch_gemm(int layout, int wkind, int epi, GemmArgs a, hipStream_t s);
 
+// up to 8 low-rank row projections sharing one activation: out_g = bf16(act P_g^T)
+struct RowProjSet {
+  int n;                  // number of matrices
+  int total;              // sum of ranks (<= 128)
+  const uint16_t *P[8];   // P_g [r_g][K]
+  uint16_t *out[8];       // out_g [M][r_g]
+  int r[8];
+  int start[8];           // first concatenated column of matrix g
+};
+lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const RowProjSet &set, hipStream_t s);
 // out[m][j] = bf16( sum_k act[m][k] * P[j][k] ), j < r   (U = X A^T, or G = dY B with P = B^T)
 lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const uint16_t *P, int r,
                           uint16_t *out, hipStream_t s);

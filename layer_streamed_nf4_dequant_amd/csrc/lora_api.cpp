@@ -105,6 +105,41 @@ GemmArgs base_args(const lsn_lora_linear *L) {
 
 extern "C" {
 
+lsn_status lora_down(int64_t T, int64_t K, const uint16_t *X, int32_t n, const uint16_t *const *A, const int32_t *r,
+                     uint16_t *const *U, void *stream) {
+  if (T < 1 || K < 64 || K % 64) return fail(LSN_E_ARG, "lora_down: need T >= 1 and K a positive multiple of 64");
+  if (n < 1 || n > 8 || !A || !r || !U) return fail(LSN_E_ARG, "lora_down: need 1 <= n <= 8 and non-null arrays");
+  if (!X || !aligned16(X)) return fail(LSN_E_ARG, "lora_down: X null or not 16-byte aligned");
+  RowProjSet set{};
+  set.n = n;
+  int total = 0;
+  for (int g = 0; g < n; ++g) {
+    if (r[g] < 8 || r[g] > 32 || r[g] % 8) return fail(LSN_E_ARG, "lora_down: rank %d must be 8, 16, 24 or 32", r[g]);
+    if (!A[g] || !U[g] || !aligned16(A[g]) || !aligned16(U[g]))
+      return fail(LSN_E_ARG, "lora_down: A[%d] / U[%d] null or not 16-byte aligned", g, g);
+    set.P[g] = A[g];
+    set.out[g] = U[g];
+    set.r[g] = r[g];
+    set.start[g] = total;
+    total += r[g];
+  }
+  if (total > 128) return fail(LSN_E_ARG, "lora_down: total rank %d exceeds 128", total);
+  set.total = total;
+  for (int g = 0; g < n; ++g) {
+    const size_t ub = (size_t)(T * r[g] * 2);
+    if (ranges_overlap(U[g], ub, X, (size_t)(T * K * 2))) return fail(LSN_E_ARG, "lora_down: U overlaps X");
+    for (int h = 0; h < n; ++h) {
+      if (ranges_overlap(U[g], ub, A[h], (size_t)(r[h] * K * 2)))
+        return fail(LSN_E_ARG, "lora_down: U overlaps an A");
+      if (h < g && ranges_overlap(U[g], ub, U[h], (size_t)(T * r[h] * 2)))
+        return fail(LSN_E_ARG, "lora_down: two outputs overlap");
+    }
+  }
+  lsn_status st = require_gfx950();
+  if (st != LSN_OK) return st;
+  return launch_rowproj(X, T, K, set, (hipStream_t)stream);
+}
+
 size_t lora_linear_ws_bytes(int64_t T, int64_t K, int64_t N, int64_t r) {
   if (T < 1 || K < 1 || N < 1 || r < 1) return 0;
   return bwd_layout(nullptr, T, K, N, r).bytes;
@@ -119,6 +154,8 @@ lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uin
   const int64_t T = L->T, K = L->K, N = L->N, r = L->r;
   if (!X || !Y || !aligned16(X) || !aligned16(Y))
     return fail(LSN_E_ARG, "lora_linear_fwd: X and Y must be non-null and 16-byte aligned");
+  if (adapters != LSN_ADAPTERS_OFF && adapters != LSN_ADAPTERS_ON && adapters != LSN_ADAPTERS_U_READY)
+    return fail(LSN_E_ARG, "lora_linear_fwd: unknown adapters mode %d", adapters);
   if (adapters && (!U || !aligned16(U)))
     return fail(LSN_E_ARG, "lora_linear_fwd: U must be non-null and 16-byte aligned when adapters are on");
   const size_t yb = (size_t)(T * N * 2), ub = (size_t)(T * r * 2);
@@ -126,13 +163,14 @@ lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uin
   size_t inb[6] = {(size_t)(T * K * 2), (size_t)(r * K * 2), (size_t)(N * r * 2)};
   const int n_in = 3 + w_ranges(L, ins + 3, inb + 3);
   for (int i = 0; i < n_in; ++i) {
-    if (ranges_overlap(Y, yb, ins[i], inb[i]) || (adapters && ranges_overlap(U, ub, ins[i], inb[i])))
+    if (ranges_overlap(Y, yb, ins[i], inb[i]) ||
+        (adapters == LSN_ADAPTERS_ON && ranges_overlap(U, ub, ins[i], inb[i])))
       return fail(LSN_E_ARG, "lora_linear_fwd: an output overlaps an input");
   }
   if (adapters && ranges_overlap(Y, yb, U, ub)) return fail(LSN_E_ARG, "lora_linear_fwd: Y overlaps U");
   if ((st = require_gfx950()) != LSN_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (adapters && (st = launch_rowproj(X, T, K, L->A, (int)r, U, s)) != LSN_OK) return st;
+  if (adapters == LSN_ADAPTERS_ON && (st = launch_rowproj(X, T, K, L->A, (int)r, U, s)) != LSN_OK) return st;
   GemmArgs a = base_args(L);
   a.M = T;
   a.Nout = N;

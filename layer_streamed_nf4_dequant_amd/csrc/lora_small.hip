@@ -19,56 +19,72 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---------------------------------------------------------------------------------------------
-// row projection: out[m][j] = bf16( sum_k act[m][k] P[j][k] ), j < r <= 32.
+// row projections sharing one activation: out_g[m][j] = bf16( sum_k act[m][k] P_g[j][k] ), j < r_g,
+// for up to 8 low-rank matrices P_g (ranks multiples of 8, total <= 128), so act is read once.
 // One 256-thread workgroup per 16 rows; wave w takes the 32-wide K-steps w, w+4, w+8, ...; the
-// four partial results are added in wave order through LDS.
+// four partial results are added in wave order through LDS. Column block cb (16 columns of the
+// concatenated P) is one MFMA 16x16x32 accumulator.
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_rowproj(const uint16_t *__restrict__ act, int64_t M, int64_t K,
-                                                 const uint16_t *__restrict__ P, int r,
-                                                 uint16_t *__restrict__ out) {
-  __shared__ floatx4_t part[4][2][64];
+                                                 RowProjSet set) {
+  __shared__ floatx4_t part[4][8][64];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t m0 = (int64_t)blockIdx.x * 16;
-  const int64_t m = m0 + (lane & 15);
+  const int64_t m = min(m0 + (lane & 15), M - 1);      // clamped rows are never stored
   const int kq = 8 * (lane >> 4);
   const int64_t nks = K / 32;
-  floatx4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-  const bool row_ok = m < M;
-  const int j0 = lane & 15, j1 = 16 + (lane & 15);
+  const int nblk = (set.total + 15) / 16;
+  // the concatenated row c of P: group g, local row c - start[g]
+  const uint16_t *prow[8];
+  bool pok[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    const int c = 16 * cb + (lane & 15);
+    int g = 0;
+#pragma unroll
+    for (int q = 1; q < 8; ++q) g += (q < set.n && c >= set.start[q]) ? 1 : 0;
+    pok[cb] = cb < nblk && c < set.total;
+    prow[cb] = set.P[g] + (int64_t)(pok[cb] ? c - set.start[g] : 0) * K;
+  }
+  floatx4_t acc[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) acc[cb] = floatx4_t{0, 0, 0, 0};
   for (int64_t ks = wave; ks < nks; ks += 4) {
     const int64_t k = ks * 32 + kq;
-    u32x4_t va = {0, 0, 0, 0}, vb0 = {0, 0, 0, 0}, vb1 = {0, 0, 0, 0};
-    if (row_ok) va = *reinterpret_cast<const u32x4_t *>(act + m * K + k);
-    if (j0 < r) vb0 = *reinterpret_cast<const u32x4_t *>(P + (int64_t)j0 * K + k);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(vb0), acc0, 0, 0, 0);
-    if (r > 16) {
-      if (j1 < r) vb1 = *reinterpret_cast<const u32x4_t *>(P + (int64_t)j1 * K + k);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(vb1), acc1, 0, 0, 0);
+    const u32x4_t va = *reinterpret_cast<const u32x4_t *>(act + m * K + k);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      if (cb < nblk) {
+        u32x4_t vb = {0, 0, 0, 0};
+        if (pok[cb]) vb = *reinterpret_cast<const u32x4_t *>(prow[cb] + k);
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(vb), acc[cb], 0, 0, 0);
+      }
     }
   }
-  part[wave][0][lane] = acc0;
-  part[wave][1][lane] = acc1;
-  __syncthreads();
-  if (wave != 0) return;
-  // lane holds column j = lane % 16 (+16) and rows 4 (lane / 16) + e
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (h == 1 && r <= 16) break;
-    floatx4_t s = part[0][h][lane];
+  for (int cb = 0; cb < 8; ++cb) part[wave][cb][lane] = acc[cb];
+  __syncthreads();
+  // 4 waves finish 4 column blocks at a time; lane holds column c = 16 cb + lane % 16 and rows
+  // 4 (lane / 16) + e
+  for (int cb = wave; cb < nblk; cb += 4) {
+    floatx4_t sum = part[0][cb][lane];
 #pragma unroll
     for (int w = 1; w < 4; ++w) {
-      const floatx4_t p = part[w][h][lane];
+      const floatx4_t p = part[w][cb][lane];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[e] = __fadd_rn(s[e], p[e]);
+      for (int e = 0; e < 4; ++e) sum[e] = __fadd_rn(sum[e], p[e]);
     }
-    const int j = 16 * h + (lane & 15);
-    if (j >= r) continue;
+    const int c = 16 * cb + (lane & 15);
+    if (c >= set.total) continue;
+    int g = 0;
+    for (int q = 1; q < set.n; ++q) g += c >= set.start[q] ? 1 : 0;
+    const int j = c - set.start[g], r = set.r[g];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t row = m0 + 4 * (lane >> 4) + e;
       if (row < M) {
-        const __bf16 b = (__bf16)s[e];
-        out[row * r + j] = __builtin_bit_cast(uint16_t, b);
+        const __bf16 b = (__bf16)sum[e];
+        set.out[g][row * r + j] = __builtin_bit_cast(uint16_t, b);
       }
     }
   }
@@ -182,10 +198,21 @@ __global__ __launch_bounds__(256) void k_tn_reduce(const float *__restrict__ par
 
 }  // namespace
 
+lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const RowProjSet &set, hipStream_t s) {
+  hipLaunchKernelGGL(k_rowproj, dim3((unsigned)((M + 15) / 16)), dim3(256), 0, s, act, M, K, set);
+  return check_hip(hipGetLastError(), "k_rowproj launch");
+}
+
 lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const uint16_t *P, int r, uint16_t *out,
                           hipStream_t s) {
-  hipLaunchKernelGGL(k_rowproj, dim3((unsigned)((M + 15) / 16)), dim3(256), 0, s, act, M, K, P, r, out);
-  return check_hip(hipGetLastError(), "k_rowproj launch");
+  RowProjSet set{};
+  set.n = 1;
+  set.total = r;
+  set.P[0] = P;
+  set.out[0] = out;
+  set.r[0] = r;
+  set.start[0] = 0;
+  return launch_rowproj(act, M, K, set, s);
 }
 
 lsn_status launch_transpose_b(const uint16_t *B, int64_t N, int r, uint16_t *Bt, hipStream_t s) {

@@ -22,6 +22,7 @@ STATUS_NAMES = {0: "LSN_OK", 1: "LSN_E_ARG", 2: "LSN_E_NOFIT", 3: "LSN_E_STATE",
                 5: "LSN_E_AUDIT"}
 W_NF4, W_BF16 = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
+ADAPTERS_OFF, ADAPTERS_ON, ADAPTERS_U_READY = 0, 1, 2
 DX_BF16_SET, DX_F32_ADD = 0, 1
 GRAD_SET, GRAD_ADD = 0, 1
 POOL_AUDIT, POOL_KEEP_AT_TURN, POOL_HOST_SIM = 1, 2, 4
@@ -29,7 +30,7 @@ FAULT_STALE_REFETCH, FAULT_WRONG_SLOT = 1 << 8, 1 << 9
 
 EXPORTS = (
     "lsn_last_error", "lsn_abi_version", "lsn_nf4_codebook", "nf4_pack_ws_bytes", "nf4_pack",
-    "nf4_dequant", "lora_linear_ws_bytes", "lora_linear_fwd", "lora_linear_bwd",
+    "nf4_dequant", "lora_down", "lora_linear_ws_bytes", "lora_linear_fwd", "lora_linear_bwd",
     "layer_pool_create", "layer_pool_register", "layer_pool_prefetch", "layer_pool_acquire",
     "layer_pool_release", "layer_pool_stats", "layer_pool_audit", "layer_pool_destroy",
 )
@@ -85,6 +86,7 @@ def load():
         "nf4_pack_ws_bytes": (sz, [i64, i64]),
         "nf4_pack": (i32, [vp, i64, i64, vp, vp, vp, vp, vp, sz, vp]),
         "nf4_dequant": (i32, [ctypes.POINTER(NF4Desc), vp, i32, vp]),
+        "lora_down": (i32, [i64, i64, vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(vp), vp]),
         "lora_linear_ws_bytes": (sz, [i64, i64, i64, i64]),
         "lora_linear_fwd": (i32, [ctypes.POINTER(LoraLinearDesc), i32, vp, vp, vp, vp, sz, vp]),
         "lora_linear_bwd": (i32, [ctypes.POINTER(LoraLinearDesc), vp, vp, vp, vp, i32, vp, vp, i32,
@@ -212,10 +214,22 @@ def ws_bytes(T: int, K: int, N: int, r: int) -> int:
     return int(load().lora_linear_ws_bytes(T, K, N, r))
 
 
-def lora_linear_fwd(desc: LoraLinearDesc, X, Y, U=None, adapters: bool = True, ws=None,
-                    stream=None) -> None:
+def lora_down(X, A_list, U_list, stream=None) -> None:
+    """U_g = bf16(X A_g^T) for all g, reading X once (linears that share the input X)."""
+    T, K = X.shape
+    n = len(A_list)
+    A = (ctypes.c_void_p * n)(*[_ptr(a) for a in A_list])
+    U = (ctypes.c_void_p * n)(*[_ptr(u) for u in U_list])
+    r = (ctypes.c_int32 * n)(*[int(a.shape[0]) for a in A_list])
+    check(load().lora_down(T, K, _ptr(X), n, A, r, U, _stream_handle(stream)))
+
+
+def lora_linear_fwd(desc: LoraLinearDesc, X, Y, U=None, adapters=True, ws=None, stream=None) -> None:
+    """adapters: True/False, or ADAPTERS_U_READY when U already holds bf16(X A^T)."""
+    mode = adapters if isinstance(adapters, int) and not isinstance(adapters, bool) else (
+        ADAPTERS_ON if adapters else ADAPTERS_OFF)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    check(load().lora_linear_fwd(ctypes.byref(desc), 1 if adapters else 0, _ptr(X), _ptr(Y), _ptr(U),
+    check(load().lora_linear_fwd(ctypes.byref(desc), mode, _ptr(X), _ptr(Y), _ptr(U),
                                  _ptr(ws), nbytes, _stream_handle(stream)))
 
 

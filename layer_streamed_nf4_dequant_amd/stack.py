@@ -1,0 +1,312 @@
+"""The layer-streamed projection stack: one training step's forward, recomputed forward and
+backward through every adapted projection of every decoder layer, with the frozen base
+streamed through a small device pool.
+
+"Can You Fine-Tune a 27B Model on a Laptop? (I Did the Math)", transcript @7:11-7:32: the
+frozen base sits in host RAM, one decoder layer at a time is copied into a small on-card
+buffer on a separate stream while the previous layer computes, and each layer is read twice
+per step (forward, and the backward's recompute). "Exact Layer Streaming", Abstract: the
+streamed run must be bit-identical to a resident run of the same numerics, forward and every
+LoRA gradient checked separately; the pages' own probe deletes every host-to-device byte.
+
+Modes
+  streamed  layers stream from pinned host images through the C-ABI layer pool (K slots)
+  resident  every layer image lives in its own device buffer (byte-identical); no copies
+  no_h2d    the pool's slots, but no copies at all: a timing probe (results are not valid)
+
+Every kernel call goes through the C ABI (layer_streamed_nf4_dequant_amd.lib); torch only
+allocates memory, provides streams and times them.
+
+The synthetic stack (the projections are the path; attention, norms and the MLP activation
+sit outside it): every layer reads the same seeded inputs X_h (attention input, read by q, k,
+v, gate, up), X_o (attention output, read by o) and X_d (MLP intermediate, read by down); W, A
+and B are distinct per layer. Upstream gradients: q, k, v and o always get their own seeded
+dY; the top layer's gate, up and down do too, but below it the backward is chained the way a
+residual stream chains it, so that every layer's LoRA gradients depend on the base weights of
+the layer above: for layer l < L-1, down's dY is dX_o of layer l+1 and gate's and up's dY is
+dX_d of layer l+1 (both bf16, and both computed from seeded gradients, so the chain stays
+bounded). A layer that read another layer's bytes therefore changes the forward outputs, the
+input gradients and the LoRA gradients below it.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import inputs, lib
+from .configs import PROJ_INPUT, StackConfig
+
+ALIGN = 256
+
+
+def _align(x: int) -> int:
+    return (x + ALIGN - 1) // ALIGN * ALIGN
+
+
+@dataclass
+class ProjLayout:
+    name: str
+    K: int
+    N: int
+    off: int              # byte offset of the projection inside the layer image
+    codes: int = 0        # offsets relative to the image (NF4)
+    qabsmax: int = 0
+    absmax2: int = 0
+    w16: int = 0          # offset of the bf16 W (bf16 base)
+
+
+def layer_layout(cfg: StackConfig) -> tuple[list[ProjLayout], int]:
+    """Byte layout of one layer image: each projection's arrays at 256-byte aligned offsets."""
+    projs, off = [], 0
+    for name, K, N in cfg.projections():
+        n = K * N
+        p = ProjLayout(name, K, N, off)
+        if cfg.base == "nf4":
+            p.codes = off
+            off = _align(off + n // 2)
+            p.qabsmax = off
+            off = _align(off + n // 64)
+            p.absmax2 = off
+            off = _align(off + 4 * (n // 16384))
+        else:
+            p.w16 = off
+            off = _align(off + 2 * n)
+        projs.append(p)
+    return projs, _align(off)
+
+
+class Stack:
+    """Owns the host images, device state and buffers of one configuration."""
+
+    def __init__(self, cfg: StackConfig, seed: int = 0, modes=("streamed",), audit: bool = False,
+                 keep_at_turn: bool = False, fault: int = 0, record: bool = False, layers=None):
+        import torch
+        self.torch = torch
+        self.cfg = cfg
+        self.L = cfg.layers if layers is None else layers
+        self.seed = seed
+        self.dev = torch.device("cuda")
+        self.layout, self.image_bytes = layer_layout(cfg)
+        self.record = record
+        self.compute = torch.cuda.Stream()
+        self.copy_stream = torch.cuda.Stream()
+        T, r = cfg.T, cfg.r
+        bf16 = torch.bfloat16
+
+        # ---- frozen base: generated on the device per layer, packed, kept in pinned host images
+        self.means = np.zeros((self.L, len(self.layout)), dtype=np.float32)
+        self.host_images = []
+        self.resident = [] if "resident" in modes else None
+        scratch_w = None
+        for l in range(self.L):
+            img = torch.empty(self.image_bytes, dtype=torch.uint8, pin_memory=True)
+            dev_img = torch.zeros(self.image_bytes, dtype=torch.uint8, device=self.dev)
+            for j, p in enumerate(self.layout):
+                w = inputs.device_normal((p.N, p.K), inputs.STD["W"], seed, cfg.name, l, p.name, "W")
+                if cfg.base == "nf4":
+                    n = p.K * p.N
+                    codes = dev_img[p.codes:p.codes + n // 2]
+                    qabs = dev_img[p.qabsmax:p.qabsmax + n // 64].view(torch.int8)
+                    abs2 = dev_img[p.absmax2:p.absmax2 + 4 * (n // 16384)].view(torch.float32)
+                    nb = lib.load().nf4_pack_ws_bytes(p.N, p.K)
+                    if scratch_w is None or scratch_w.numel() < nb:
+                        scratch_w = torch.empty(nb, dtype=torch.uint8, device=self.dev)
+                    self.means[l, j] = lib.nf4_pack_into(w, codes, qabs, abs2, scratch_w)
+                else:
+                    dev_img[p.w16:p.w16 + 2 * p.K * p.N].view(bf16).copy_(w.view(-1).to(bf16))
+                del w
+            img.copy_(dev_img)
+            self.host_images.append(img)
+            if self.resident is not None:
+                self.resident.append(dev_img)
+            else:
+                del dev_img
+        torch.cuda.synchronize()
+
+        # ---- trainable adapters and their gradients (resident) ----
+        self.A, self.B, self.dA, self.dB = [], [], [], []
+        for l in range(self.L):
+            Al, Bl, dAl, dBl = [], [], [], []
+            for p in self.layout:
+                key = (cfg.name, l, p.name)
+                Al.append(inputs.device_uniform((r, p.K), 1.0 / np.sqrt(p.K), seed, *key, "A", dtype=bf16))
+                Bl.append(inputs.device_normal((p.N, r), inputs.STD["B"], seed, *key, "B", dtype=bf16))
+                dAl.append(torch.zeros((r, p.K), dtype=torch.float32, device=self.dev))
+                dBl.append(torch.zeros((p.N, r), dtype=torch.float32, device=self.dev))
+            self.A.append(Al)
+            self.B.append(Bl)
+            self.dA.append(dAl)
+            self.dB.append(dBl)
+
+        # ---- shared activations and upstream gradients ----
+        self.X = {w: inputs.device_normal((T, cfg.input_width(w)), 1.0, seed, cfg.name, "X", w, dtype=bf16)
+                  for w in ("h", "o", "d")}
+        self.dY = [inputs.device_normal((T, p.N), 1.0, seed, cfg.name, "dY", p.name, dtype=bf16)
+                   for p in self.layout]
+        self.Y = [torch.empty((T, p.N), dtype=bf16, device=self.dev) for p in self.layout]
+        self.Yre = [torch.empty((T, p.N), dtype=bf16, device=self.dev) for p in self.layout]
+        self.U = [torch.empty((T, r), dtype=bf16, device=self.dev) for p in self.layout]
+        self.dX_h = torch.zeros((T, cfg.hidden), dtype=torch.float32, device=self.dev)
+        # dX_o and dX_d ping-pong by layer parity: layer l reads layer l+1's as upstream gradients
+        self.dX_o_pp = [torch.empty((T, cfg.hidden), dtype=bf16, device=self.dev) for _ in range(2)]
+        self.dX_d_pp = [torch.empty((T, cfg.inter), dtype=bf16, device=self.dev) for _ in range(2)]
+        ws = max(lib.ws_bytes(T, p.K, p.N, r) for p in self.layout)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=self.dev)
+
+        # ---- pool (streamed) or fixed slots (no_h2d) ----
+        self.pool = None
+        self.slots = None
+        if "streamed" in modes or "no_h2d" in modes:
+            free, _ = torch.cuda.mem_get_info()
+            need = cfg.pool_slots * self.image_bytes
+            if need > free:
+                raise MemoryError(f"pool of {cfg.pool_slots} x {self.image_bytes} B does not fit "
+                                  f"({free} B free): refused")
+            self.slots = [torch.empty(self.image_bytes, dtype=torch.uint8, device=self.dev)
+                          for _ in range(cfg.pool_slots)]
+        if "streamed" in modes:
+            flags = (lib.POOL_AUDIT if audit else 0) | (lib.POOL_KEEP_AT_TURN if keep_at_turn else 0) | fault
+            self.reset_pool(flags)
+        self.checks = {}
+        torch.cuda.synchronize()
+
+    def reset_pool(self, flags: int = 0, n_slots: int | None = None):
+        """(Re)create the layer pool with the given flags and slot count over the same images."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        if self.pool is not None:
+            self.pool.close()
+        if n_slots is not None and n_slots != len(self.slots):
+            self.slots = [torch.empty(self.image_bytes, dtype=torch.uint8, device=self.dev)
+                          for _ in range(n_slots)]
+        self.pool = lib.LayerPool([t.data_ptr() for t in self.slots], self.image_bytes, self.L,
+                                  self.copy_stream.cuda_stream, flags)
+        for l in range(self.L):
+            self.pool.register(l, self.host_images[l].data_ptr(), self.image_bytes)
+
+    # ------------------------------------------------------------------------------------------
+    def _desc(self, base: int, l: int, j: int) -> lib.LoraLinearDesc:
+        p, cfg = self.layout[j], self.cfg
+        if cfg.base == "nf4":
+            w = lib.WeightDesc(lib.W_NF4, lib.NF4Desc(p.N, p.K, base + p.codes, base + p.qabsmax,
+                                                      base + p.absmax2, float(self.means[l, j])), None)
+        else:
+            w = lib.WeightDesc(lib.W_BF16, lib.NF4Desc(), base + p.w16)
+        return lib.LoraLinearDesc(cfg.T, p.K, p.N, cfg.r, cfg.scale, w, self.A[l][j].data_ptr(),
+                                  self.B[l][j].data_ptr())
+
+    def _forward_layer(self, base: int, l: int, Y, s, gemm_events=None):
+        # the adapters' down-projections, once per shared input (q, k, v, gate, up read X_h)
+        for which in ("h", "o", "d"):
+            js = [j for j, p in enumerate(self.layout) if PROJ_INPUT[p.name] == which]
+            if js:
+                lib.lora_down(self.X[which], [self.A[l][j] for j in js], [self.U[j] for j in js], stream=s)
+        for j, p in enumerate(self.layout):
+            if gemm_events is not None:
+                gemm_events.append((j, self.torch.cuda.Event(enable_timing=True),
+                                    self.torch.cuda.Event(enable_timing=True)))
+                gemm_events[-1][1].record(s)
+            lib.lora_linear_fwd(self._desc(base, l, j), self.X[PROJ_INPUT[p.name]], Y[j], self.U[j],
+                                adapters=lib.ADAPTERS_U_READY, ws=self.ws, stream=s)
+            if gemm_events is not None:
+                gemm_events[-1][2].record(s)
+
+    def upstream(self, l: int, j: int):
+        """The upstream gradient dY of projection j in layer l (see the module docstring)."""
+        name = self.layout[j].name
+        if l < self.L - 1:
+            if name == "down" and not self.cfg.single:
+                return self.dX_o_pp[(l + 1) % 2]
+            if name in ("gate", "up"):
+                return self.dX_d_pp[(l + 1) % 2]
+        return self.dY[j]
+
+    @property
+    def dX_o(self):
+        return self.dX_o_pp[0]
+
+    @property
+    def dX_d(self):
+        return self.dX_d_pp[0]
+
+    def _backward_layer(self, base: int, l: int, s):
+        self.dX_h.zero_()
+        for j, p in enumerate(self.layout):
+            which = PROJ_INPUT[p.name]
+            if which == "h":
+                dX, mode = self.dX_h, lib.DX_F32_ADD
+            else:
+                dX, mode = (self.dX_o_pp[l % 2] if which == "o" else self.dX_d_pp[l % 2]), lib.DX_BF16_SET
+            lib.lora_linear_bwd(self._desc(base, l, j), self.X[which], self.upstream(l, j), self.U[j], dX,
+                                self.dA[l][j], self.dB[l][j], dx_mode=mode, grad_mode=lib.GRAD_SET,
+                                ws=self.ws, stream=s)
+
+    def _record(self, tag: str, l: int, tensors):
+        """Position-weighted integer checksums of the outputs (exact, order-independent sums
+        modulo 2^64), kept on the device."""
+        torch = self.torch
+        for j, t in enumerate(tensors):
+            v = (t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)).reshape(-1)
+            n = v.numel()
+            if getattr(self, "_wvec", None) is None or self._wvec.numel() < n:
+                self._wvec = torch.arange(1, n + 1, device=v.device, dtype=torch.int64)
+            self.checks[(tag, l, j)] = (v.to(torch.int64) * self._wvec[:n]).sum()
+
+    def step(self, mode: str = "streamed", gemm_events=None) -> float:
+        """One training step of the projection stack; returns its time in ms (compute stream).
+        gemm_events: optional list; (projection, start, end) HIP events around every fused
+        forward GEMM launch are appended to it."""
+        torch = self.torch
+        s = self.compute
+        sh = s.cuda_stream
+        L = self.L
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            start.record(s)
+            # with K slots, up to K-1 layers are in flight ahead of the one being computed
+            ahead = len(self.slots) - 1 if self.slots is not None else 0
+            # ---- forward: layers 0 .. L-1 ----
+            for l in range(L):
+                if mode == "streamed":
+                    for a in range(l, min(L, l + 1 + ahead)):
+                        self.pool.prefetch(a)
+                    base = self.pool.acquire(l, sh)
+                elif mode == "resident":
+                    base = self.resident[l].data_ptr()
+                else:
+                    base = self.slots[l % len(self.slots)].data_ptr()
+                self._forward_layer(base, l, self.Y, s, gemm_events)
+                if self.record:
+                    self._record("fwd", l, self.Y)
+                if mode == "streamed":
+                    self.pool.release(l, sh)
+            # ---- backward: layers L-1 .. 0, each re-read and recomputed ----
+            for l in reversed(range(L)):
+                if mode == "streamed":
+                    for a in range(l, max(-1, l - 1 - ahead), -1):
+                        self.pool.prefetch(a)
+                    base = self.pool.acquire(l, sh)
+                elif mode == "resident":
+                    base = self.resident[l].data_ptr()
+                else:
+                    base = self.slots[l % len(self.slots)].data_ptr()
+                self._forward_layer(base, l, self.Yre, s, gemm_events)   # recompute
+                self._backward_layer(base, l, s)
+                if self.record:
+                    self._record("re", l, self.Yre)
+                    self._record("dx", l, [self.dX_h, self.dX_o_pp[l % 2], self.dX_d_pp[l % 2]])
+                if mode == "streamed":
+                    self.pool.release(l, sh)
+            end.record(s)
+        end.synchronize()
+        return start.elapsed_time(end)
+
+    def grads(self):
+        return self.dA, self.dB
+
+    def close(self):
+        if self.pool is not None:
+            self.pool.close()
+            self.pool = None

@@ -1,0 +1,177 @@
+"""The exactness protocol on the GPU: the streamed stack must be bit-identical to a resident run
+of the same numerics, forward outputs and every LoRA gradient tensor checked separately
+("Exact Layer Streaming", Abstract; Soup v0.73.0 benchmarks README, reading conventions), with
+same-process controls: planted pool defects must break the backward while the forward stays
+exact, and the aliasing audit must flag them.  Plus oracle parity on sampled layers.
+"""
+
+import numpy as np
+import pytest
+
+from layer_streamed_nf4_dequant_amd import configs, inputs, lib
+from layer_streamed_nf4_dequant_amd.configs import PROJ_INPUT
+from layer_streamed_nf4_dequant_amd.stack import Stack
+
+pytestmark = pytest.mark.gpu
+
+
+def snapshot(st):
+    import torch
+    torch.cuda.synchronize()
+    checks = {k: int(v.item()) for k, v in st.checks.items()}
+    grads = [[(a.clone(), b.clone()) for a, b in zip(dA, dB)] for dA, dB in zip(st.dA, st.dB)]
+    st.checks = {}
+    return checks, grads
+
+
+def compare(ref, got):
+    """Returns (forward_equal, recompute_equal, dx_equal, n_grad_tensors_equal, n_grad_tensors)."""
+    import torch
+    (rc, rg), (gc, gg) = ref, got
+    fwd = all(rc[k] == gc[k] for k in rc if k[0] == "fwd")
+    re = all(rc[k] == gc[k] for k in rc if k[0] == "re")
+    dx = all(rc[k] == gc[k] for k in rc if k[0] == "dx")
+    eq = n = 0
+    for lr, lg in zip(rg, gg):
+        for (a1, b1), (a2, b2) in zip(lr, lg):
+            eq += int(torch.equal(a1.view(torch.int32), a2.view(torch.int32)))
+            eq += int(torch.equal(b1.view(torch.int32), b2.view(torch.int32)))
+            n += 2
+    return fwd, re, dx, eq, n
+
+
+def recompute_matches_forward(checks, L, n_proj):
+    return all(checks[("fwd", l, j)] == checks[("re", l, j)] for l in range(L) for j in range(n_proj))
+
+
+def test_toy_8b_shapes_exactness_and_controls(gpu):
+    """Three 8B-shaped layers: streamed (2, 1 and 3 slots; KEEP_AT_TURN; audit on) equals
+    resident bit for bit; each planted defect leaves the forward exact but breaks gradients,
+    and the audit reports it."""
+    cfg = configs.C3
+    print("case: 3-layer 8B-shaped toy", flush=True)
+    st = Stack(cfg, modes=("streamed", "resident"), record=True, layers=3)
+    st.step("resident")
+    ref = snapshot(st)
+    assert recompute_matches_forward(ref[0], 3, 7)
+    variants = [("2 slots", 0, None), ("1 slot", 0, 1), ("3 slots", 0, 3),
+                ("keep at turn", lib.POOL_KEEP_AT_TURN, 2), ("audit", lib.POOL_AUDIT, 2)]
+    for name, flags, n_slots in variants:
+        print(f"  variant {name}", flush=True)
+        st.reset_pool(flags, n_slots)
+        st.step("streamed")
+        if flags & lib.POOL_AUDIT:
+            st.pool.audit()
+        fwd, re, dx, eq, n = compare(ref, snapshot(st))
+        assert fwd and re and dx and eq == n, (name, fwd, re, dx, eq, n)
+    for name, fault in (("stale re-fetch", lib.FAULT_STALE_REFETCH), ("wrong slot", lib.FAULT_WRONG_SLOT)):
+        print(f"  control {name}", flush=True)
+        st.reset_pool(fault, 2)
+        st.step("streamed")
+        got = snapshot(st)
+        fwd, re, dx, eq, n = compare(ref, got)
+        assert fwd, f"{name}: the forward must stay exact"
+        assert eq < n and not re and not dx, \
+            f"{name}: the planted defect must break the backward ({eq}/{n} gradient tensors equal)"
+        assert not recompute_matches_forward(got[0], 3, 7)
+        st.reset_pool(fault | lib.POOL_AUDIT, 2)
+        st.step("streamed")
+        with pytest.raises(lib.LsnError) as e:
+            st.pool.audit()
+        assert e.value.status == lib.LSN_E_AUDIT
+        snapshot(st)
+    st.close()
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", ["C2", "C4", "C3", "C5"])
+def test_streamed_equals_resident_full_stack(gpu, name):
+    cfg = configs.CONFIGS[name]
+    print(f"case: {cfg.name} ({cfg.layers} layers) streamed vs resident", flush=True)
+    st = Stack(cfg, modes=("streamed", "resident"), record=True)
+    st.step("resident")
+    ref = snapshot(st)
+    st.step("streamed")
+    got = snapshot(st)
+    fwd, re, dx, eq, n = compare(ref, got)
+    ledger = {"config": cfg.name, "base": cfg.base, "MiB_per_layer": round(st.image_bytes / 2 ** 20, 1),
+              "forward_exact": fwd, "recompute_exact": re, "dX_exact": dx,
+              "lora_grad_tensors_exact": f"{eq}/{n}"}
+    print("ledger", ledger, flush=True)
+    assert fwd and re and dx and eq == n == 2 * 7 * cfg.layers
+    assert recompute_matches_forward(got[0], cfg.layers, 7)
+    stats = st.pool.stats()
+    assert stats["copies"] == 2 * cfg.layers and stats["misses"] == 0
+    st.close()
+
+
+def _oracle_stack(cfg, st, rows):
+    """Oracle forward (sampled rows) and backward of every projection of every layer, on the
+    stack's own inputs, with the same layer-to-layer chaining of upstream gradients (the
+    oracle's own dX_o / dX_d of layer l+1, rounded to bf16 at the same boundary)."""
+    import torch
+    from oracle import lora as olora
+    from oracle import nf4 as onf4
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731  (bf16 values, exact)
+    to_bf16 = lambda a: onf4.bf16_to_f32(onf4.bf16_rne(a.astype(np.float32))).astype(np.float64)  # noqa: E731
+    L = st.L
+    out = {}
+    above = None                      # (dX_o, dX_d) of layer l+1 as bf16 values
+    for l in reversed(range(L)):
+        layer = {}
+        for j, p in enumerate(st.layout):
+            W = inputs.device_normal((p.N, p.K), inputs.STD["W"], st.seed, cfg.name, l, p.name, "W").cpu().numpy()
+            if cfg.base == "nf4":
+                Wh = onf4.bf16_to_f32(onf4.dequant_bf16(onf4.pack(W)))
+            else:
+                Wh = torch.from_numpy(W).to(torch.bfloat16).float().numpy()
+            X = f(st.X[PROJ_INPUT[p.name]])
+            if above is not None and p.name == "down":
+                dY = above[0]
+            elif above is not None and p.name in ("gate", "up"):
+                dY = above[1]
+            else:
+                dY = f(st.dY[j])
+            A, B = f(st.A[l][j]), f(st.B[l][j])
+            Y, _ = olora.forward(X[rows], Wh, A, B, cfg.scale)
+            dX, dA, dB, _ = olora.backward(X, dY, Wh, A, B, cfg.scale)
+            layer[p.name] = (Y, dX, dA, dB)
+        out[l] = layer
+        above = (to_bf16(layer["o"][1]), to_bf16(layer["down"][1]))
+    return out
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,layers", [("C2", 3), ("C4", 2)])
+def test_stack_matches_oracle_on_sampled_layers(gpu, name, layers):
+    """After one streamed step: layer L-1's forward outputs, layer 0's recomputed outputs and
+    input gradients, and every layer's dA, dB against the oracle on the same inputs."""
+    import torch
+    from oracle import lora as olora
+    cfg = configs.CONFIGS[name]
+    print(f"case: {cfg.name} first {layers} layers vs oracle", flush=True)
+    st = Stack(cfg, modes=("streamed",), layers=layers)
+    st.step("streamed")
+    torch.cuda.synchronize()
+    rows = np.arange(0, cfg.T, 7)
+    o = _oracle_stack(cfg, st, rows)
+    L = layers
+    dx_h = np.zeros((cfg.T, cfg.hidden))
+    errs = []
+    for j, p in enumerate(st.layout):
+        errs.append(olora.rel_l2(st.Y[j].float().cpu().numpy()[rows], o[L - 1][p.name][0]))
+        assert errs[-1] <= 5e-3, ("Y", p.name)
+        errs.append(olora.rel_l2(st.Yre[j].float().cpu().numpy()[rows], o[0][p.name][0]))
+        assert errs[-1] <= 5e-3, ("Yre", p.name)
+        for l in range(L):
+            errs.append(olora.rel_l2(st.dA[l][j].cpu().numpy(), o[l][p.name][2]))
+            assert errs[-1] <= 1e-2, ("dA", l, p.name)
+            errs.append(olora.rel_l2(st.dB[l][j].cpu().numpy(), o[l][p.name][3]))
+            assert errs[-1] <= 1e-2, ("dB", l, p.name)
+        if PROJ_INPUT[p.name] == "h":
+            dx_h += o[0][p.name][1]
+    assert olora.rel_l2(st.dX_h.cpu().numpy(), dx_h) <= 5e-3
+    assert olora.rel_l2(st.dX_o_pp[0].float().cpu().numpy(), o[0]["o"][1]) <= 5e-3
+    assert olora.rel_l2(st.dX_d_pp[0].float().cpu().numpy(), o[0]["down"][1]) <= 5e-3
+    print(f"max rel L2 over {len(errs)} tensors: {max(errs):.2e}")
+    st.close()
