@@ -94,6 +94,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--mode", default="streamed", choices=["streamed", "resident", "no_h2d"])
     ap.add_argument("--config", default="C3")
+    ap.add_argument("--dequant", default="staged", choices=["staged", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -110,7 +111,7 @@ def main():
     cfg = configs.CONFIGS[args.config]
     print(f"[bench] setting up {cfg.name}: {cfg.layers} layers, T={cfg.T}, mode={args.mode}", flush=True)
     t0 = time.perf_counter()
-    stack = Stack(cfg, modes=(args.mode,))
+    stack = Stack(cfg, modes=(args.mode,), dequant=args.dequant)
     torch.cuda.synchronize()
     print(f"[bench] setup {time.perf_counter() - t0:.1f} s; image {stack.image_bytes / 1e6:.2f} MB/layer",
           flush=True)
@@ -137,8 +138,10 @@ def main():
         flops += 2 * cfg.T * K * N + 2 * cfg.T * cfg.r * N
     n_launch = len(gemm_events)
     achieved = flops / (dur_ms * 1e-3) / 1e12 if dur_ms > 0 else 0.0
-    kernel = "k_gemm<NT,NF4> (fused NF4 dequant-into-LDS + bf16 MFMA + LoRA epilogue)" if cfg.base == "nf4" \
-        else "k_gemm<NT,BF16>"
+    if cfg.base == "nf4" and stack.dequant == "fused":
+        kernel = "k_gemm<NT,NF4> (fused NF4 dequant-into-LDS + bf16 MFMA + LoRA prologue)"
+    else:
+        kernel = "k_gemm<NT,BF16> (bf16 MFMA + LoRA prologue; W dequantised per visit by k_dequant)"
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_from_profiles(),
                 "kernel": kernel, "launches": n_launch,
@@ -164,7 +167,7 @@ def main():
                    else f"{cfg.name} LoRA projection stack",
                    "layers": cfg.layers, "tokens_per_step": cfg.T, "hidden": cfg.hidden, "kv": cfg.kv,
                    "inter": cfg.inter, "lora_rank": cfg.r, "lora_alpha": cfg.alpha, "base": cfg.base,
-                   "mode": args.mode, "pool_slots": cfg.pool_slots,
+                   "mode": args.mode, "pool_slots": cfg.pool_slots, "dequant": stack.dequant,
                    "flops_per_step": cfg.flops_per_step(),
                    "stack_tflops": round(cfg.flops_per_step() / (wall / args.steps) / 1e12, 1),
                    "h2d_bytes_per_step": (pool["bytes_copied"] // (args.steps + args.warmup)) if pool else 0},

@@ -31,6 +31,7 @@ input gradients and the LoRA gradients below it.
 
 from __future__ import annotations
 
+import ctypes
 from dataclasses import dataclass
 
 import numpy as np
@@ -81,7 +82,8 @@ class Stack:
     """Owns the host images, device state and buffers of one configuration."""
 
     def __init__(self, cfg: StackConfig, seed: int = 0, modes=("streamed",), audit: bool = False,
-                 keep_at_turn: bool = False, fault: int = 0, record: bool = False, layers=None):
+                 keep_at_turn: bool = False, fault: int = 0, record: bool = False, layers=None,
+                 dequant: str = "staged"):
         import torch
         self.torch = torch
         self.cfg = cfg
@@ -90,6 +92,14 @@ class Stack:
         self.dev = torch.device("cuda")
         self.layout, self.image_bytes = layer_layout(cfg)
         self.record = record
+        # "staged": each visit dequantises every NF4 projection once (nf4_dequant, HBM-bound) into
+        #           a bf16 staging buffer that the visit's GEMMs read (the backward visit's
+        #           recompute and dX GEMMs share it);
+        # "fused":  the GEMMs dequantise their W tiles straight into LDS (no staging buffer).
+        # Both hand the matrix cores the same bf16 operand, so both give identical bits.
+        if dequant not in ("staged", "fused"):
+            raise ValueError(dequant)
+        self.dequant = dequant if cfg.base == "nf4" else "fused"
         self.compute = torch.cuda.Stream()
         self.copy_stream = torch.cuda.Stream()
         T, r = cfg.T, cfg.r
@@ -154,6 +164,9 @@ class Stack:
         self.dX_d_pp = [torch.empty((T, cfg.inter), dtype=bf16, device=self.dev) for _ in range(2)]
         ws = max(lib.ws_bytes(T, p.K, p.N, r) for p in self.layout)
         self.ws = torch.empty(ws, dtype=torch.uint8, device=self.dev)
+        self.w_stage = None
+        if self.dequant == "staged":
+            self.w_stage = [torch.empty((p.N, p.K), dtype=bf16, device=self.dev) for p in self.layout]
 
         # ---- pool (streamed) or fixed slots (no_h2d) ----
         self.pool = None
@@ -187,8 +200,23 @@ class Stack:
             self.pool.register(l, self.host_images[l].data_ptr(), self.image_bytes)
 
     # ------------------------------------------------------------------------------------------
+    def _nf4_desc(self, base: int, l: int, j: int) -> lib.NF4Desc:
+        p = self.layout[j]
+        return lib.NF4Desc(p.N, p.K, base + p.codes, base + p.qabsmax, base + p.absmax2, float(self.means[l, j]))
+
+    def _stage(self, base: int, l: int, s):
+        """Dequantise every projection of the layer image at `base` into the staging buffers."""
+        for j in range(len(self.layout)):
+            d = self._nf4_desc(base, l, j)
+            lib.check(lib.load().nf4_dequant(ctypes.byref(d), self.w_stage[j].data_ptr(), lib.OUT_BF16,
+                                             s.cuda_stream))
+
     def _desc(self, base: int, l: int, j: int) -> lib.LoraLinearDesc:
         p, cfg = self.layout[j], self.cfg
+        if self.dequant == "staged":
+            w = lib.WeightDesc(lib.W_BF16, lib.NF4Desc(), self.w_stage[j].data_ptr())
+            return lib.LoraLinearDesc(cfg.T, p.K, p.N, cfg.r, cfg.scale, w, self.A[l][j].data_ptr(),
+                                      self.B[l][j].data_ptr())
         if cfg.base == "nf4":
             w = lib.WeightDesc(lib.W_NF4, lib.NF4Desc(p.N, p.K, base + p.codes, base + p.qabsmax,
                                                       base + p.absmax2, float(self.means[l, j])), None)
@@ -277,6 +305,8 @@ class Stack:
                     base = self.resident[l].data_ptr()
                 else:
                     base = self.slots[l % len(self.slots)].data_ptr()
+                if self.dequant == "staged":
+                    self._stage(base, l, s)
                 self._forward_layer(base, l, self.Y, s, gemm_events)
                 if self.record:
                     self._record("fwd", l, self.Y)
@@ -292,6 +322,8 @@ class Stack:
                     base = self.resident[l].data_ptr()
                 else:
                     base = self.slots[l % len(self.slots)].data_ptr()
+                if self.dequant == "staged":
+                    self._stage(base, l, s)                               # re-dequantised per visit
                 self._forward_layer(base, l, self.Yre, s, gemm_events)   # recompute
                 self._backward_layer(base, l, s)
                 if self.record:
