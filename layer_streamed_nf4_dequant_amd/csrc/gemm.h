@@ -35,6 +35,27 @@ struct GemmArgs {
 
 lsn_status launch_gemm(int layout, int wkind, int epi, GemmArgs a, hipStream_t s);
 
+// direct-load NT GEMM on bf16 W: out_seg = bf16/f32+= ( act W_seg^T + s U_seg B_seg^T ) for up to 4
+// segments sharing act [M][K] (K % 32 == 0)
+struct GemmSeg {
+  int64_t ntile0;          // first N tile of the segment (filled by launch_gemm_direct)
+  int64_t N;
+  const uint16_t *w;       // bf16 W [N][K]
+  const uint16_t *lr_w;    // LoRA B [N][r]
+  const uint16_t *lr_act;  // U [M][r]
+  void *out;               // [M][N]
+};
+struct DirectArgs {
+  int64_t M, K;
+  const uint16_t *act;
+  int nseg;
+  GemmSeg seg[4];
+  int r;
+  float scale;
+  int adapters;
+};
+lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s);
+
 // up to 8 low-rank row projections sharing one activation: out_g = bf16(act P_g^T)
 struct RowProjSet {
   int n;                  // number of matrices

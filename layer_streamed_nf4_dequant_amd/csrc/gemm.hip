@@ -440,6 +440,264 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs a) {
   }
 }
 
+// =============================================================================================
+// Direct-load NT GEMM (both operands bf16 and K-contiguous): out_seg = act W_seg^T (+ LoRA term)
+// for up to 4 output segments that share the activation (e.g. q, k and v of a layer read the
+// same input). K-steps of 32 stream through a 4-stage LDS ring; buffer_load...lds fills a stage
+// three steps ahead, and a step only waits for its own stage (the oldest loads in flight), so
+// up to three K-steps of memory latency are hidden behind the matrix cores.
+// LDS rows are 64 B (32 bf16, four 16-byte chunks); chunk p of row r sits at slot
+// 4 r + (p ^ ((r >> 2) & 3)): with gfx950's 64 four-byte banks a 16-lane group of a fragment
+// read (16 consecutive rows, one logical chunk) then covers all 64 banks once, and the direct
+// writes are contiguous 1 KB segments.
+// =============================================================================================
+constexpr int DBK = 32;
+constexpr int DSTAGES = 4;
+constexpr int DTILE = 256 * DBK * 2;           // 16 KB: one operand, one stage
+
+__device__ __forceinline__ int dlds_off(int row, int chunk) { return (row * 4 + (chunk ^ ((row >> 2) & 3))) * 16; }
+
+struct DirectRows4 {
+  uint32_t voff[4];
+};
+
+// wave w fills LDS segments 4w .. 4w+3 (1 KB = 16 rows each) of a 256 x 32 tile
+__device__ __forceinline__ void make_direct_rows4(DirectRows4 &d, int64_t rows, int64_t ld, int64_t r0, int wave,
+                                                  int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sg = wave * 4 + i;
+    const int row = sg * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    const int64_t grow = min(r0 + row, rows - 1);     // clamped rows feed only unstored outputs
+    d.voff[i] = (uint32_t)((grow * ld + 8 * c) * 2);
+  }
+}
+
+__device__ __forceinline__ void issue_direct4(char *lds_tile, __amdgpu_buffer_rsrc_t rsrc, const DirectRows4 &d,
+                                              uint32_t k_bytes, int wave) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(lds_tile + (wave * 4 + i) * 1024), 16, d.voff[i],
+                                             k_bytes, 0, 0);
+}
+
+// wait until at most 16 vector-memory operations of this wave are outstanding (the two newest
+// stages, 8 loads each): the oldest stage in flight has landed
+__device__ __forceinline__ void wait_vm_16() { __builtin_amdgcn_s_waitcnt((16 & 15) | (7 << 4) | (15 << 8) | ((16 >> 4) << 14)); }
+
+// Workgroup barrier for the direct-load ring. __syncthreads() would wait for every outstanding
+// vector-memory operation (the direct-to-LDS loads count as LDS writes), draining the three
+// stages in flight. Here each wave first waits for its own loads of the next stage (vmcnt) and
+// for its own LDS reads (lgkmcnt), then meets the others; the scheduling barriers keep the
+// compiler from moving LDS accesses across.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm_16();
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char *lds_a = smem;                               // DSTAGES stages
+  char *lds_b = smem + DSTAGES * DTILE;             // DSTAGES stages
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // tile -> (m tile, segment, n tile within the segment); consecutive workgroups walk down M
+  const int64_t tiles_m = (a.M + BM - 1) / BM;
+  const int64_t mt = blockIdx.x % tiles_m;
+  int64_t nt = blockIdx.x / tiles_m;
+  int sidx = 0;
+#pragma unroll
+  for (int q = 1; q < 4; ++q)
+    if (q < a.nseg && nt >= a.seg[q].ntile0) sidx = q;
+  const GemmSeg sg = a.seg[sidx];
+  nt -= sg.ntile0;
+  const int64_t m0 = mt * BM;
+  const int64_t n0 = nt * BN;
+
+  floatx16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  // ---- LoRA prologue: acc = s * (B_seg . U_seg^T) over r (B_seg [N][r], U_seg [M][r]) ----
+  if (a.adapters) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j0 = 16 * h;
+      if (j0 >= a.r) break;
+      const int jl = j0 + 8 * (lane >> 5);
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + wm * 128 + 32 * i + (lane & 31);
+        u32x4_t v = {0, 0, 0, 0};
+        if (m < a.M && jl < a.r) v = *reinterpret_cast<const u32x4_t *>(sg.lr_act + m * a.r + jl);
+        fa[i] = as_bf16x8(v);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + wn * 128 + 32 * j + (lane & 31);
+        u32x4_t v = {0, 0, 0, 0};
+        if (n < sg.N && jl < a.r) v = *reinterpret_cast<const u32x4_t *>(sg.lr_w + n * a.r + jl);
+        fb[j] = as_bf16x8(v);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = __fmul_rn(a.scale, acc[i][j][e]);
+  }
+
+  const int nk = (int)(a.K / DBK);
+  const int k_last = nk - 1;
+  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.act, a.M * a.K * 2);
+  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(sg.w, sg.N * a.K * 2);
+  DirectRows4 da, db;
+  make_direct_rows4(da, a.M, a.K, m0, wave, lane);
+  make_direct_rows4(db, sg.N, a.K, n0, wave, lane);
+
+  // fragments of one 16-wide sub-step: 4 activation rows-blocks and 4 weight row-blocks
+  // read order fa0, fb0..fb3, fa1..fa3: the first MFMAs of the batch that consumes them, which
+  // walk j fastest, find their operands earliest
+  auto load_frags = [&](int stage, int s2, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+    const char *la = lds_a + stage * DTILE;
+    const char *lb = lds_b + stage * DTILE;
+    const int chunk = 2 * s2 + (lane >> 5);
+    fa[0] = *reinterpret_cast<const bf16x8 *>(la + dlds_off(wm * 128 + (lane & 31), chunk));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      fb[j] = *reinterpret_cast<const bf16x8 *>(lb + dlds_off(wn * 128 + 32 * j + (lane & 31), chunk));
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+      fa[i] = *reinterpret_cast<const bf16x8 *>(la + dlds_off(wm * 128 + 32 * i + (lane & 31), chunk));
+  };
+  auto mfmas = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  };
+
+  // prologue: stages 0, 1, 2 in flight (steps past the end re-load the last step into stages
+  // that are never read); stage 0 visible; fragments of step 0, sub-step 0 loaded
+#pragma unroll
+  for (int p = 0; p < DSTAGES - 1; ++p) {
+    const uint32_t kb = (uint32_t)min(p, k_last) * DBK * 2;
+    issue_direct4(lds_a + p * DTILE, rs_a, da, kb, wave);
+    issue_direct4(lds_b + p * DTILE, rs_b, db, kb, wave);
+  }
+  ring_barrier();
+  bf16x8 ca[4], cb[4], na[4], nb[4];
+  load_frags(0, 0, ca, cb);
+  // Step kt: stage kt is visible and its sub-step 0 fragments are in (ca, cb).
+  //  1. refill stage kt-1 (read by every wave before the previous barrier) with step kt+3;
+  //  2. load sub-step 1 of step kt, run sub-step 0;
+  //  3. wait for the own loads of step kt+1, barrier (the sub-step 0 MFMAs keep running);
+  //  4. load sub-step 0 of step kt+1, run sub-step 1 of step kt.
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & (DSTAGES - 1);
+    {
+      const int nx = (kt + DSTAGES - 1) & (DSTAGES - 1);
+      const uint32_t kb = (uint32_t)min(kt + DSTAGES - 1, k_last) * DBK * 2;
+      issue_direct4(lds_a + nx * DTILE, rs_a, da, kb, wave);
+      issue_direct4(lds_b + nx * DTILE, rs_b, db, kb, wave);
+    }
+    load_frags(st, 1, na, nb);
+    mfmas(ca, cb);
+    // interleave: the next fragments are read two per MFMA at the head of the batch (so they
+    // land long before the next batch needs them) and the direct loads one per MFMA, so neither
+    // the LDS nor the vector-memory queue sees a burst while the matrix core waits
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    ring_barrier();
+    load_frags((kt + 1) & (DSTAGES - 1), 0, ca, cb);
+    mfmas(na, nb);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_vm_all();
+
+  // ---- epilogue: lane holds row m = 32 i + lane%32, columns 32 j + 8 g + 4 (lane/32) .. +3 ----
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + wm * 128 + 32 * i + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + wn * 128 + 32 * j + 8 * g + 4 * (lane >> 5);
+        if (m < a.M && n < sg.N) {
+          const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1], v2 = acc[i][j][4 * g + 2],
+                      v3 = acc[i][j][4 * g + 3];
+          if constexpr (EPI == EPI_BF16) {
+            uint2 o;
+            o.x = pack_bf16x2(v0, v1);
+            o.y = pack_bf16x2(v2, v3);
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(sg.out) + m * sg.N + n) = o;
+          } else {
+            floatx4_t *o = reinterpret_cast<floatx4_t *>(reinterpret_cast<float *>(sg.out) + m * sg.N + n);
+            floatx4_t cur = *o;
+            cur[0] = __fadd_rn(cur[0], v0);
+            cur[1] = __fadd_rn(cur[1], v1);
+            cur[2] = __fadd_rn(cur[2], v2);
+            cur[3] = __fadd_rn(cur[3], v3);
+            *o = cur;
+          }
+        }
+      }
+    }
+  }
+}
+
+constexpr size_t kDirectSmemBytes = 2 * DSTAGES * DTILE;
+
+template <int EPI>
+lsn_status launch_direct_one(const DirectArgs &a, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_direct<EPI>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDirectSmemBytes);
+    if (e != hipSuccess) return check_hip(e, "gemm_direct smem attribute");
+    attr_set = true;
+  }
+  int64_t ntiles_n = 0;
+  for (int q = 0; q < a.nseg; ++q) ntiles_n += (a.seg[q].N + BN - 1) / BN;
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ntiles_n;
+  hipLaunchKernelGGL((k_gemm_direct<EPI>), dim3((unsigned)tiles), dim3(NT), kDirectSmemBytes, s, a);
+  return check_hip(hipGetLastError(), "k_gemm_direct launch");
+}
+
 constexpr size_t kSmemBytes = 4 * TILE_BYTES + (16 + 256) * sizeof(float);
 
 template <int LAYOUT, int WKIND, int EPI>
@@ -457,6 +715,15 @@ lsn_status launch_one(const GemmArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s) {
+  int64_t t0 = 0;
+  for (int q = 0; q < a.nseg; ++q) {
+    a.seg[q].ntile0 = t0;
+    t0 += (a.seg[q].N + BN - 1) / BN;
+  }
+  return epi == EPI_BF16 ? launch_direct_one<EPI_BF16>(a, s) : launch_direct_one<EPI_F32_ADD>(a, s);
+}
 
 lsn_status launch_gemm(int layout, int wkind, int epi, GemmArgs a, hipStream_t s) {
   const Nf4Table &tab = nf4_table();

@@ -171,6 +171,22 @@ lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uin
   if ((st = require_gfx950()) != LSN_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (adapters == LSN_ADAPTERS_ON && (st = launch_rowproj(X, T, K, L->A, (int)r, U, s)) != LSN_OK) return st;
+  if (L->W.kind == LSN_W_BF16) {
+    DirectArgs d{};
+    d.M = T;
+    d.K = K;
+    d.act = X;
+    d.nseg = 1;
+    d.seg[0].N = N;
+    d.seg[0].w = L->W.bf16;
+    d.seg[0].lr_w = L->B;
+    d.seg[0].lr_act = U;
+    d.seg[0].out = Y;
+    d.r = (int)r;
+    d.scale = L->scale;
+    d.adapters = adapters ? 1 : 0;
+    return launch_gemm_direct(d, EPI_BF16, s);
+  }
   GemmArgs a = base_args(L);
   a.M = T;
   a.Nout = N;
@@ -181,7 +197,7 @@ lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uin
   a.lr_w = L->B;
   a.adapters = adapters ? 1 : 0;
   a.out = Y;
-  return launch_gemm(GEMM_NT, L->W.kind == LSN_W_NF4 ? W_IS_NF4 : W_IS_BF16, EPI_BF16, a, s);
+  return launch_gemm(GEMM_NT, W_IS_NF4, EPI_BF16, a, s);
 }
 
 lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const uint16_t *dY, const uint16_t *U,
