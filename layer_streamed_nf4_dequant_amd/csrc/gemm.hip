@@ -474,12 +474,15 @@ __device__ __forceinline__ void make_direct_rows4(DirectRows4 &d, int64_t rows, 
   }
 }
 
+__device__ __forceinline__ void issue_direct1(char *lds_tile, __amdgpu_buffer_rsrc_t rsrc, const DirectRows4 &d,
+                                              uint32_t k_bytes, int wave, int i) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(lds_tile + (wave * 4 + i) * 1024), 16, d.voff[i],
+                                           k_bytes, 0, 0);
+}
 __device__ __forceinline__ void issue_direct4(char *lds_tile, __amdgpu_buffer_rsrc_t rsrc, const DirectRows4 &d,
                                               uint32_t k_bytes, int wave) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(lds_tile + (wave * 4 + i) * 1024), 16, d.voff[i],
-                                             k_bytes, 0, 0);
+  for (int i = 0; i < 4; ++i) issue_direct1(lds_tile, rsrc, d, k_bytes, wave, i);
 }
 
 // wait until at most 16 vector-memory operations of this wave are outstanding (the two newest
@@ -506,7 +509,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   char *lds_b = smem + DSTAGES * DTILE;             // DSTAGES stages
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  // the wave index is uniform: keep it in a scalar register so that the LDS destinations of the
+  // direct loads (the M0 operand) are scalar arithmetic
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   // tile -> (m tile, segment, n tile within the segment); consecutive workgroups walk down M
@@ -587,6 +592,17 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     for (int i = 1; i < 4; ++i)
       fa[i] = *reinterpret_cast<const bf16x8 *>(la + dlds_off(wm * 128 + 32 * i + (lane & 31), chunk));
   };
+  // fragment q of a sub-step in the same order: 0 -> fa0, 1..4 -> fb0..fb3, 5..7 -> fa1..fa3
+  auto read_frag = [&](int stage, int s2, int q, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+    const int chunk = 2 * s2 + (lane >> 5);
+    if (q == 0 || q >= 5) {
+      const int i = q == 0 ? 0 : q - 4;
+      fa[i] = *reinterpret_cast<const bf16x8 *>(lds_a + stage * DTILE + dlds_off(wm * 128 + 32 * i + (lane & 31), chunk));
+    } else {
+      const int j = q - 1;
+      fb[j] = *reinterpret_cast<const bf16x8 *>(lds_b + stage * DTILE + dlds_off(wn * 128 + 32 * j + (lane & 31), chunk));
+    }
+  };
   auto mfmas = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -606,44 +622,36 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   bf16x8 ca[4], cb[4], na[4], nb[4];
   load_frags(0, 0, ca, cb);
   // Step kt: stage kt is visible and its sub-step 0 fragments are in (ca, cb).
-  //  1. refill stage kt-1 (read by every wave before the previous barrier) with step kt+3;
-  //  2. load sub-step 1 of step kt, run sub-step 0;
-  //  3. wait for the own loads of step kt+1, barrier (the sub-step 0 MFMAs keep running);
-  //  4. load sub-step 0 of step kt+1, run sub-step 1 of step kt.
+  //  1. load sub-step 1 of step kt; run sub-step 0, with the refill of stage kt-1 (read by every
+  //     wave before the previous barrier) with step kt+3 spread over its MFMAs, one direct load
+  //     per two MFMAs, so that the loads issue in the matrix core's shadow;
+  //  2. wait for the own loads of step kt+1, barrier (the last sub-step 0 MFMAs keep running);
+  //  3. load sub-step 0 of step kt+1, run sub-step 1 of step kt.
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & (DSTAGES - 1);
-    {
-      const int nx = (kt + DSTAGES - 1) & (DSTAGES - 1);
-      const uint32_t kb = (uint32_t)min(kt + DSTAGES - 1, k_last) * DBK * 2;
-      issue_direct4(lds_a + nx * DTILE, rs_a, da, kb, wave);
-      issue_direct4(lds_b + nx * DTILE, rs_b, db, kb, wave);
-    }
-    load_frags(st, 1, na, nb);
-    mfmas(ca, cb);
-    // interleave: the next fragments are read two per MFMA at the head of the batch (so they
-    // land long before the next batch needs them) and the direct loads one per MFMA, so neither
-    // the LDS nor the vector-memory queue sees a burst while the matrix core waits
+    const int nx = (kt + DSTAGES - 1) & (DSTAGES - 1);
+    const uint32_t kb = (uint32_t)min(kt + DSTAGES - 1, k_last) * DBK * 2;
+    // fixed order, one group per scheduling fence: read one sub-step 1 fragment, two MFMAs,
+    // one direct load
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+    for (int q = 0; q < 8; ++q) {
+      read_frag(st, 1, q, na, nb);
+      const int i = q >> 1, j0 = 2 * (q & 1);
+      acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[j0], ca[i], acc[i][j0], 0, 0, 0);
+      acc[i][j0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[j0 + 1], ca[i], acc[i][j0 + 1], 0, 0, 0);
+      if (q < 4) issue_direct1(lds_a + nx * DTILE, rs_a, da, kb, wave, q);
+      else issue_direct1(lds_b + nx * DTILE, rs_b, db, kb, wave, q - 4);
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     ring_barrier();
     load_frags((kt + 1) & (DSTAGES - 1), 0, ca, cb);
     mfmas(na, nb);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   wait_vm_all();
