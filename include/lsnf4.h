@@ -100,13 +100,18 @@ typedef struct {
   float mean;
 } lsn_nf4;
 
-enum { LSN_W_NF4 = 0, LSN_W_BF16 = 1 };
+enum { LSN_W_NF4 = 0, LSN_W_BF16 = 1, LSN_W_BF16_T = 2 };
 
-/* A frozen base weight W[N][K]: NF4-packed, or un-quantised bf16 (no dequantisation). */
+/*
+ * A frozen base weight W[N][K]: NF4-packed, un-quantised (or already dequantised) bf16, or
+ * bf16 in the transposed layout W^T[K][N] (what nf4_dequant writes with LSN_OUT_BF16_T). The
+ * transposed layout serves the backward only: there the product dY W reduces over N, which is
+ * then the contiguous dimension of both operands; lora_linear_fwd rejects it (LSN_E_ARG).
+ */
 typedef struct {
-  int32_t kind;           /* LSN_W_NF4 or LSN_W_BF16 */
+  int32_t kind;           /* LSN_W_NF4, LSN_W_BF16 or LSN_W_BF16_T */
   lsn_nf4 nf4;            /* used when kind == LSN_W_NF4 (rows = N, cols = K) */
-  const uint16_t *bf16;   /* used when kind == LSN_W_BF16: device bf16 W[N][K] */
+  const uint16_t *bf16;   /* LSN_W_BF16: device bf16 W[N][K]; LSN_W_BF16_T: device bf16 W^T[K][N] */
 } lsn_weight;
 
 /* Device workspace bytes nf4_pack needs for a rows x cols weight. */
@@ -128,12 +133,14 @@ lsn_status nf4_pack(const float *w, int64_t rows, int64_t cols, uint8_t *codes,
                     int8_t *qabsmax, float *absmax2, float *mean_out, void *ws,
                     size_t ws_bytes, void *stream);
 
-enum { LSN_OUT_BF16 = 0, LSN_OUT_F32 = 1 };
+enum { LSN_OUT_BF16 = 0, LSN_OUT_F32 = 1, LSN_OUT_BF16_T = 2 };
 
 /*
- * nf4_dequant - standalone dequantisation of a whole NF4 tensor into a dense row-major
- * device buffer `out` of rows*cols elements: bf16 (LSN_OUT_BF16, the GEMM operand) or the
- * fp32 product before rounding (LSN_OUT_F32). Bit-exact with the definition above.
+ * nf4_dequant - standalone dequantisation of a whole NF4 tensor into a dense device buffer
+ * `out` (16-byte aligned) of rows*cols elements: row-major bf16 (LSN_OUT_BF16, the GEMM
+ * operand), the row-major fp32 product before rounding (LSN_OUT_F32), or bf16 transposed,
+ * out[c][r] = w_hat[r][c] (LSN_OUT_BF16_T, the backward's operand; needs rows % 8 == 0).
+ * Bit-exact with the definition above in every layout. `out` must not overlap the NF4 arrays.
  * ("Exact Layer Streaming", Abstract: per-layer NF4 dequantisation.) Async on `stream`.
  */
 lsn_status nf4_dequant(const lsn_nf4 *w, void *out, int32_t out_dtype, void *stream);
@@ -143,7 +150,7 @@ lsn_status nf4_dequant(const lsn_nf4 *w, void *out, int32_t out_dtype, void *str
  *   forward   U = bf16(X A^T);  Y = bf16( X W^T + s U B^T )   (fp32 accumulation)
  *             adapters off:     Y = bf16( X W^T )
  *   backward  G = bf16(dY B);   dX = dY W + s G A;  dB = s dY^T U;  dA = s G^T X
- * Shapes: X [T][K], W [N][K], A [r][K], B [N][r], Y and dY [T][N], U and G [T][r],
+ * Shapes: X [T][K], W [N][K] (or W^T [K][N], backward only), A [r][K], B [N][r], Y and dY [T][N], U and G [T][r],
  * dX [T][K], dA [r][K] fp32, dB [N][r] fp32. W is re-dequantised on every call from the
  * bytes the descriptor points at (a pool slot or a resident buffer): nothing is cached.
  * Requirements: T >= 1, K % 64 == 0, N % 64 == 0, r in {8, 16, 24, 32}, and the NF4 rules for W.

@@ -154,11 +154,13 @@ lsn_status nf4_dequant(const lsn_nf4 *w, void *out, int32_t out_dtype, void *str
   lsn_status st = check_nf4(w, "nf4_dequant");
   if (st != LSN_OK) return st;
   if (!out) return fail(LSN_E_ARG, "nf4_dequant: null output");
-  if (out_dtype != LSN_OUT_BF16 && out_dtype != LSN_OUT_F32)
+  if (out_dtype != LSN_OUT_BF16 && out_dtype != LSN_OUT_F32 && out_dtype != LSN_OUT_BF16_T)
     return fail(LSN_E_ARG, "nf4_dequant: unknown output dtype %d", out_dtype);
   if ((uintptr_t)out & 15) return fail(LSN_E_ARG, "nf4_dequant: output must be 16-byte aligned");
+  if (out_dtype == LSN_OUT_BF16_T && w->rows % 8)
+    return fail(LSN_E_ARG, "nf4_dequant: the transposed output needs rows %% 8 == 0 (got %lld)", (long long)w->rows);
   const size_t n = (size_t)(w->rows * w->cols);
-  const size_t out_bytes = n * (out_dtype == LSN_OUT_BF16 ? 2 : 4);
+  const size_t out_bytes = n * (out_dtype == LSN_OUT_F32 ? 4 : 2);
   if (ranges_overlap(out, out_bytes, w->codes, n / 2) || ranges_overlap(out, out_bytes, w->qabsmax, n / 64) ||
       ranges_overlap(out, out_bytes, w->absmax2, n / 16384 * 4))
     return fail(LSN_E_ARG, "nf4_dequant: output overlaps the NF4 input");

@@ -69,8 +69,8 @@ lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const RowPr
 // out[m][j] = bf16( sum_k act[m][k] * P[j][k] ), j < r   (U = X A^T, or G = dY B with P = B^T)
 lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const uint16_t *P, int r,
                           uint16_t *out, hipStream_t s);
-// P^T: B [N][r] -> Bt [r][N]
-lsn_status launch_transpose_b(const uint16_t *B, int64_t N, int r, uint16_t *Bt, hipStream_t s);
+// dst [cols][rows] = src [rows][cols]^T (small bf16 matrices: B -> B^T, A -> A^T)
+lsn_status launch_transpose(const uint16_t *src, int64_t rows, int64_t cols, uint16_t *dst, hipStream_t s);
 // partial[c][p][j] = sum over t in chunk c of Z[t][p] * V[t][j]   (chunks of TN_CHUNK rows)
 constexpr int TN_CHUNK = 256;
 lsn_status launch_tn_partial(const uint16_t *Z, int64_t T, int64_t P, const uint16_t *V, int r,

@@ -3,8 +3,10 @@
 //
 // forward:  U = bf16(X A^T)                                  k_rowproj
 //           Y = bf16(s U B^T + X W^T)                        k_gemm NT (NF4 dequantised in LDS)
-// backward: Bt = B^T ; G = bf16(dY B)                        k_transpose_b, k_rowproj
-//           dX = s G A + dY W                                k_gemm NN (bf16 store or fp32 add)
+// backward: Bt = B^T ; G = bf16(dY B)                        k_transpose, k_rowproj
+//           dX = s G A + dY W                                k_gemm NN (NF4 or bf16 W[N][K]), or
+//                                                            k_gemm_direct NT on W^T[K][N] with A^T
+//                                                            (bf16 store or fp32 add)
 //           dB = s sum_t dY^T U ; dA = s sum_t G^T X         k_tn_partial + k_tn_reduce
 
 #include "common.h"
@@ -25,6 +27,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct BwdWs {
   uint16_t *G;
   uint16_t *Bt;
+  uint16_t *At;
   float *part_dB;
   float *part_dA;
   size_t bytes;
@@ -39,6 +42,8 @@ BwdWs bwd_layout(void *ws, int64_t T, int64_t K, int64_t N, int64_t r) {
   off += align256((size_t)(T * r * 2));
   w.Bt = reinterpret_cast<uint16_t *>(p + off);
   off += align256((size_t)(r * N * 2));
+  w.At = reinterpret_cast<uint16_t *>(p + off);
+  off += align256((size_t)(K * r * 2));
   w.part_dB = reinterpret_cast<float *>(p + off);
   off += align256((size_t)(nc * N * r * 4));
   w.part_dA = reinterpret_cast<float *>(p + off);
@@ -62,7 +67,7 @@ lsn_status check_linear(const lsn_lora_linear *L, const char *what) {
     if (L->W.nf4.rows != L->N || L->W.nf4.cols != L->K)
       return fail(LSN_E_ARG, "%s: NF4 W is %lld x %lld, expected N x K = %lld x %lld", what,
                   (long long)L->W.nf4.rows, (long long)L->W.nf4.cols, (long long)L->N, (long long)L->K);
-  } else if (L->W.kind == LSN_W_BF16) {
+  } else if (L->W.kind == LSN_W_BF16 || L->W.kind == LSN_W_BF16_T) {
     if (!L->W.bf16 || !aligned16(L->W.bf16)) return fail(LSN_E_ARG, "%s: bf16 W null or not 16-byte aligned", what);
   } else {
     return fail(LSN_E_ARG, "%s: unknown weight kind %d", what, L->W.kind);
@@ -151,6 +156,8 @@ lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uin
   (void)ws_bytes;
   lsn_status st = check_linear(L, "lora_linear_fwd");
   if (st != LSN_OK) return st;
+  if (L->W.kind == LSN_W_BF16_T)
+    return fail(LSN_E_ARG, "lora_linear_fwd: the transposed bf16 layout is for the backward only");
   const int64_t T = L->T, K = L->K, N = L->N, r = L->r;
   if (!X || !Y || !aligned16(X) || !aligned16(Y))
     return fail(LSN_E_ARG, "lora_linear_fwd: X and Y must be non-null and 16-byte aligned");
@@ -235,21 +242,40 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
   if ((st = require_gfx950()) != LSN_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   const int64_t nc = (T + TN_CHUNK - 1) / TN_CHUNK;
-  if ((st = launch_transpose_b(L->B, N, (int)r, need.Bt, s)) != LSN_OK) return st;
+  if ((st = launch_transpose(L->B, N, r, need.Bt, s)) != LSN_OK) return st;
   if ((st = launch_rowproj(dY, T, N, need.Bt, (int)r, need.G, s)) != LSN_OK) return st;
-  GemmArgs a = base_args(L);
-  a.M = T;
-  a.Nout = K;
-  a.Kred = N;
-  a.act = dY;
-  a.ldw = K;
-  a.lr_act = need.G;
-  a.lr_w = L->A;
-  a.adapters = 1;
-  a.out = dX;
-  if ((st = launch_gemm(GEMM_NN, L->W.kind == LSN_W_NF4 ? W_IS_NF4 : W_IS_BF16,
-                        dx_mode == LSN_DX_F32_ADD ? EPI_F32_ADD : EPI_BF16, a, s)) != LSN_OK)
-    return st;
+  const int epi = dx_mode == LSN_DX_F32_ADD ? EPI_F32_ADD : EPI_BF16;
+  if (L->W.kind == LSN_W_BF16_T) {
+    // dX = dY (W^T)^T + s G (A^T)^T: an NT product over N with both operands N-contiguous
+    if ((st = launch_transpose(L->A, r, K, need.At, s)) != LSN_OK) return st;
+    DirectArgs d{};
+    d.M = T;
+    d.K = N;
+    d.act = dY;
+    d.nseg = 1;
+    d.seg[0].N = K;
+    d.seg[0].w = L->W.bf16;
+    d.seg[0].lr_w = need.At;
+    d.seg[0].lr_act = need.G;
+    d.seg[0].out = dX;
+    d.r = (int)r;
+    d.scale = L->scale;
+    d.adapters = 1;
+    if ((st = launch_gemm_direct(d, epi, s)) != LSN_OK) return st;
+  } else {
+    GemmArgs a = base_args(L);
+    a.M = T;
+    a.Nout = K;
+    a.Kred = N;
+    a.act = dY;
+    a.ldw = K;
+    a.lr_act = need.G;
+    a.lr_w = L->A;
+    a.adapters = 1;
+    a.out = dX;
+    if ((st = launch_gemm(GEMM_NN, L->W.kind == LSN_W_NF4 ? W_IS_NF4 : W_IS_BF16, epi, a, s)) != LSN_OK)
+      return st;
+  }
   const int acc = grad_mode == LSN_GRAD_ADD;
   if ((st = launch_tn_partial(dY, T, N, U, (int)r, need.part_dB, s)) != LSN_OK) return st;
   if ((st = launch_tn_reduce(need.part_dB, nc, N, (int)r, L->scale, acc, 0, dB, s)) != LSN_OK) return st;

@@ -90,12 +90,13 @@ __global__ __launch_bounds__(256) void k_rowproj(const uint16_t *__restrict__ ac
   }
 }
 
-__global__ __launch_bounds__(256) void k_transpose_b(const uint16_t *__restrict__ B, int64_t N, int r,
-                                                     uint16_t *__restrict__ Bt) {
+// dst[c][r] = src[r][c] for a small bf16 matrix (a LoRA factor): one element per thread
+__global__ __launch_bounds__(256) void k_transpose(const uint16_t *__restrict__ src, int64_t rows, int64_t cols,
+                                                   uint16_t *__restrict__ dst) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= N * r) return;
-  const int64_t n = i / r, j = i % r;
-  Bt[j * N + n] = B[i];
+  if (i >= rows * cols) return;
+  const int64_t r = i / cols, c = i % cols;
+  dst[c * rows + r] = src[i];
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -215,9 +216,10 @@ lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const uint1
   return launch_rowproj(act, M, K, set, s);
 }
 
-lsn_status launch_transpose_b(const uint16_t *B, int64_t N, int r, uint16_t *Bt, hipStream_t s) {
-  hipLaunchKernelGGL(k_transpose_b, dim3((unsigned)((N * r + 255) / 256)), dim3(256), 0, s, B, N, r, Bt);
-  return check_hip(hipGetLastError(), "k_transpose_b launch");
+lsn_status launch_transpose(const uint16_t *src, int64_t rows, int64_t cols, uint16_t *dst, hipStream_t s) {
+  hipLaunchKernelGGL(k_transpose, dim3((unsigned)((rows * cols + 255) / 256)), dim3(256), 0, s, src, rows, cols,
+                     dst);
+  return check_hip(hipGetLastError(), "k_transpose launch");
 }
 
 lsn_status launch_tn_partial(const uint16_t *Z, int64_t T, int64_t P, const uint16_t *V, int r, float *partial,

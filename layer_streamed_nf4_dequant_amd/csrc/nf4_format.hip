@@ -169,6 +169,66 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t *__restrict__ co
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// dequantise into the transposed layout: out[k][n] = w_hat[n][k] (bf16), for a backward GEMM
+// that reduces over n with both operands n-contiguous. Same arithmetic as k_dequant, so the
+// values are bit-identical. Workgroup tile: 128 rows n x 256 columns k. Thread t decodes
+// rows n0 + 8 (t % 16) .. +7 at the 8-column groups k0 + 8 (t / 16) and k0 + 128 + 8 (t / 16)
+// (one 4-byte code word per row and group; four neighbouring lanes read 16 contiguous bytes of
+// a row and every 128-byte line of codes is read by one workgroup), then stores each of the 8
+// columns as 8 consecutive n (16 bytes; 16 lanes write 256 contiguous bytes of an out row).
+// Requires rows % 8 == 0 (checked by the caller); cols % 64 == 0 by the format.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_dequant_t(const uint32_t *__restrict__ codes,
+                                                   const int8_t *__restrict__ qabsmax,
+                                                   const float *__restrict__ absmax2, float mu, int64_t rows,
+                                                   int64_t cols, uint16_t *__restrict__ out,
+                                                   Nf4KernelTable tab) {
+  __shared__ float sq[16];
+  __shared__ float scode8[256];
+  const int t = threadIdx.x;
+  if (t < 16) sq[t] = tab.q[t];
+  if (t < 255) scode8[t] = int8_level(t - 127);
+  const int64_t n = (int64_t)blockIdx.x * 128 + 8 * (t & 15);
+  const int64_t kc[2] = {(int64_t)blockIdx.y * 256 + 8 * (t >> 4), (int64_t)blockIdx.y * 256 + 128 + 8 * (t >> 4)};
+  const bool row_ok = n < rows;
+  uint32_t word[2][8];
+  int v[2][8];
+  float s2[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bool ok = row_ok && kc[h] < cols;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t e = (n + i) * cols + kc[h];      // element index of the group's first weight
+      word[h][i] = ok ? codes[e >> 3] : 0u;
+      v[h][i] = ok ? qabsmax[e >> 6] : 0;
+      s2[h][i] = ok ? absmax2[e >> 14] : 0.0f;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (!row_ok || kc[h] >= cols) continue;
+    float c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = decode_absmax(scode8[v[h][i] + 127], s2[h][i], mu);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int shift = 8 * (e >> 1) + ((e & 1) ? 0 : 4);
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = __fmul_rn(sq[(word[h][i] >> shift) & 15u], c[i]);
+      u32x4_t o;
+      o.x = pack_bf16x2(f[0], f[1]);
+      o.y = pack_bf16x2(f[2], f[3]);
+      o.z = pack_bf16x2(f[4], f[5]);
+      o.w = pack_bf16x2(f[6], f[7]);
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t *>(out + (kc[h] + e) * rows + n));
+    }
+  }
+}
+
 }  // namespace
 
 lsn_status launch_pack_codes(const float *w, int64_t n, uint8_t *codes, float *absmax,
@@ -192,7 +252,11 @@ lsn_status launch_dequant(const lsn_nf4 &w, void *out, int out_dtype, hipStream_
   const int64_t n = w.rows * w.cols;
   const dim3 grid((unsigned)(n / 8192));
   const uint32_t *codes = reinterpret_cast<const uint32_t *>(w.codes);
-  if (out_dtype == LSN_OUT_BF16)
+  if (out_dtype == LSN_OUT_BF16_T) {
+    const dim3 tgrid((unsigned)((w.rows + 127) / 128), (unsigned)((w.cols + 255) / 256));
+    hipLaunchKernelGGL(k_dequant_t, tgrid, dim3(256), 0, s, codes, w.qabsmax, w.absmax2, w.mean, w.rows, w.cols,
+                       reinterpret_cast<uint16_t *>(out), kernel_table());
+  } else if (out_dtype == LSN_OUT_BF16)
     hipLaunchKernelGGL(k_dequant<LSN_OUT_BF16>, grid, dim3(256), 0, s, codes, w.qabsmax, w.absmax2,
                        w.mean, out, kernel_table());
   else

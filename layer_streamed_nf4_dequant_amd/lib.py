@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(HERE, "liblsnf4.so")
 LSN_OK, LSN_E_ARG, LSN_E_NOFIT, LSN_E_STATE, LSN_E_HIP, LSN_E_AUDIT = range(6)
 STATUS_NAMES = {0: "LSN_OK", 1: "LSN_E_ARG", 2: "LSN_E_NOFIT", 3: "LSN_E_STATE", 4: "LSN_E_HIP",
                 5: "LSN_E_AUDIT"}
-W_NF4, W_BF16 = 0, 1
-OUT_BF16, OUT_F32 = 0, 1
+W_NF4, W_BF16, W_BF16_T = 0, 1, 2
+OUT_BF16, OUT_F32, OUT_BF16_T = 0, 1, 2
 ADAPTERS_OFF, ADAPTERS_ON, ADAPTERS_U_READY = 0, 1, 2
 DX_BF16_SET, DX_F32_ADD = 0, 1
 GRAD_SET, GRAD_ADD = 0, 1
@@ -189,25 +189,27 @@ def nf4_pack_into(w, codes, qabsmax, absmax2, ws, stream=None) -> float:
 
 
 def nf4_dequant(w: NF4Tensor, out_dtype: str = "bf16", out=None, stream=None):
+    """out_dtype: "bf16" ([rows][cols]), "f32" ([rows][cols]) or "bf16_t" (transposed, [cols][rows])."""
     torch = _torch()
-    dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    code = {"bf16": OUT_BF16, "f32": OUT_F32, "bf16_t": OUT_BF16_T}[out_dtype]
     if out is None:
-        out = torch.empty((w.rows, w.cols), dtype=dt, device=w.codes.device)
+        shape = (w.cols, w.rows) if code == OUT_BF16_T else (w.rows, w.cols)
+        out = torch.empty(shape, dtype=torch.float32 if code == OUT_F32 else torch.bfloat16,
+                          device=w.codes.device)
     d = w.desc()
-    check(load().nf4_dequant(ctypes.byref(d), _ptr(out), OUT_BF16 if out_dtype == "bf16" else OUT_F32,
-                             _stream_handle(stream)))
+    check(load().nf4_dequant(ctypes.byref(d), _ptr(out), code, _stream_handle(stream)))
     return out
 
 
-def weight_desc(W) -> WeightDesc:
-    """W is an NF4Tensor or a bf16 device tensor [N][K]."""
+def weight_desc(W, transposed: bool = False) -> WeightDesc:
+    """W is an NF4Tensor or a bf16 device tensor: [N][K], or W^T [K][N] with transposed=True."""
     if isinstance(W, NF4Tensor):
         return WeightDesc(W_NF4, W.desc(), None)
-    return WeightDesc(W_BF16, NF4Desc(), _ptr(W))
+    return WeightDesc(W_BF16_T if transposed else W_BF16, NF4Desc(), _ptr(W))
 
 
-def linear_desc(T: int, K: int, N: int, r: int, scale: float, W, A, B) -> LoraLinearDesc:
-    return LoraLinearDesc(T, K, N, r, float(scale), weight_desc(W), _ptr(A), _ptr(B))
+def linear_desc(T: int, K: int, N: int, r: int, scale: float, W, A, B, transposed: bool = False) -> LoraLinearDesc:
+    return LoraLinearDesc(T, K, N, r, float(scale), weight_desc(W, transposed), _ptr(A), _ptr(B))
 
 
 def ws_bytes(T: int, K: int, N: int, r: int) -> int:

@@ -92,9 +92,10 @@ class Stack:
         self.dev = torch.device("cuda")
         self.layout, self.image_bytes = layer_layout(cfg)
         self.record = record
-        # "staged": each visit dequantises every NF4 projection once (nf4_dequant, HBM-bound) into
-        #           a bf16 staging buffer that the visit's GEMMs read (the backward visit's
-        #           recompute and dX GEMMs share it);
+        # "staged": each visit dequantises every NF4 projection (nf4_dequant, HBM-bound) into
+        #           bf16 staging buffers that the visit's GEMMs read: W [N][K] for the forward
+        #           and the recompute, and, on the backward visit, also W^T [K][N], so that the
+        #           dX product (a reduction over N) runs as the same direct-load NT GEMM;
         # "fused":  the GEMMs dequantise their W tiles straight into LDS (no staging buffer).
         # Both hand the matrix cores the same bf16 operand, so both give identical bits.
         if dequant not in ("staged", "fused"):
@@ -164,9 +165,10 @@ class Stack:
         self.dX_d_pp = [torch.empty((T, cfg.inter), dtype=bf16, device=self.dev) for _ in range(2)]
         ws = max(lib.ws_bytes(T, p.K, p.N, r) for p in self.layout)
         self.ws = torch.empty(ws, dtype=torch.uint8, device=self.dev)
-        self.w_stage = None
+        self.w_stage = self.w_stage_t = None
         if self.dequant == "staged":
             self.w_stage = [torch.empty((p.N, p.K), dtype=bf16, device=self.dev) for p in self.layout]
+            self.w_stage_t = [torch.empty((p.K, p.N), dtype=bf16, device=self.dev) for p in self.layout]
 
         # ---- pool (streamed) or fixed slots (no_h2d) ----
         self.pool = None
@@ -204,17 +206,24 @@ class Stack:
         p = self.layout[j]
         return lib.NF4Desc(p.N, p.K, base + p.codes, base + p.qabsmax, base + p.absmax2, float(self.means[l, j]))
 
-    def _stage(self, base: int, l: int, s):
-        """Dequantise every projection of the layer image at `base` into the staging buffers."""
+    def _stage(self, base: int, l: int, s, transposed: bool = False):
+        """Dequantise every projection of the layer image at `base` into the staging buffers
+        (and into the transposed ones too, for the backward visit)."""
         for j in range(len(self.layout)):
             d = self._nf4_desc(base, l, j)
             lib.check(lib.load().nf4_dequant(ctypes.byref(d), self.w_stage[j].data_ptr(), lib.OUT_BF16,
                                              s.cuda_stream))
+            if transposed:
+                lib.check(lib.load().nf4_dequant(ctypes.byref(d), self.w_stage_t[j].data_ptr(), lib.OUT_BF16_T,
+                                                 s.cuda_stream))
 
-    def _desc(self, base: int, l: int, j: int) -> lib.LoraLinearDesc:
+    def _desc(self, base: int, l: int, j: int, backward: bool = False) -> lib.LoraLinearDesc:
         p, cfg = self.layout[j], self.cfg
         if self.dequant == "staged":
-            w = lib.WeightDesc(lib.W_BF16, lib.NF4Desc(), self.w_stage[j].data_ptr())
+            if backward:
+                w = lib.WeightDesc(lib.W_BF16_T, lib.NF4Desc(), self.w_stage_t[j].data_ptr())
+            else:
+                w = lib.WeightDesc(lib.W_BF16, lib.NF4Desc(), self.w_stage[j].data_ptr())
             return lib.LoraLinearDesc(cfg.T, p.K, p.N, cfg.r, cfg.scale, w, self.A[l][j].data_ptr(),
                                       self.B[l][j].data_ptr())
         if cfg.base == "nf4":
@@ -267,7 +276,7 @@ class Stack:
                 dX, mode = self.dX_h, lib.DX_F32_ADD
             else:
                 dX, mode = (self.dX_o_pp[l % 2] if which == "o" else self.dX_d_pp[l % 2]), lib.DX_BF16_SET
-            lib.lora_linear_bwd(self._desc(base, l, j), self.X[which], self.upstream(l, j), self.U[j], dX,
+            lib.lora_linear_bwd(self._desc(base, l, j, backward=True), self.X[which], self.upstream(l, j), self.U[j], dX,
                                 self.dA[l][j], self.dB[l][j], dx_mode=mode, grad_mode=lib.GRAD_SET,
                                 ws=self.ws, stream=s)
 
@@ -323,7 +332,7 @@ class Stack:
                 else:
                     base = self.slots[l % len(self.slots)].data_ptr()
                 if self.dequant == "staged":
-                    self._stage(base, l, s)                               # re-dequantised per visit
+                    self._stage(base, l, s, transposed=True)              # re-dequantised per visit
                 self._forward_layer(base, l, self.Yre, s, gemm_events)   # recompute
                 self._backward_layer(base, l, s)
                 if self.record:

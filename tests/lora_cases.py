@@ -51,9 +51,16 @@ class Case:
             self.Wd = bf16_dev(self.W_hat_bits, torch)
         self.ws = torch.empty(max(lib.ws_bytes(T, K, N, r), 256), dtype=torch.uint8, device="cuda")
 
-    def desc(self, W=None):
+    def desc(self, W=None, transposed=False):
         return lib.linear_desc(self.T, self.K, self.N, self.r, self.s, self.Wd if W is None else W,
-                               self.Ad, self.Bd)
+                               self.Ad, self.Bd, transposed=transposed)
+
+    def w_transposed(self):
+        """The bf16 W^T [K][N] the backward's transposed path reads: nf4_dequant's transposed
+        output for an NF4 base, else the bf16 W transposed by torch."""
+        if self.base == "nf4":
+            return lib.nf4_dequant(self.Wd, "bf16_t")
+        return self.Wd.t().contiguous()
 
     def gpu_fwd(self, adapters=True, W=None):
         import torch
@@ -62,7 +69,7 @@ class Case:
         lib.lora_linear_fwd(self.desc(W), self.Xd, Y, U, adapters=adapters, ws=self.ws)
         return Y, U
 
-    def gpu_bwd(self, U, dx_mode=lib.DX_BF16_SET, grad_mode=lib.GRAD_SET, W=None):
+    def gpu_bwd(self, U, dx_mode=lib.DX_BF16_SET, grad_mode=lib.GRAD_SET, W=None, transposed=False):
         import torch
         if dx_mode == lib.DX_F32_ADD:
             dX = torch.from_numpy(self.dX_init).cuda()
@@ -71,7 +78,7 @@ class Case:
         g0 = torch.from_numpy(self.g_init).cuda()
         dA = g0[: self.r * self.K].view(self.r, self.K).clone()
         dB = g0[self.r * self.K:].view(self.N, self.r).clone()
-        lib.lora_linear_bwd(self.desc(W), self.Xd, self.dYd, U, dX, dA, dB, dx_mode=dx_mode,
+        lib.lora_linear_bwd(self.desc(W, transposed), self.Xd, self.dYd, U, dX, dA, dB, dx_mode=dx_mode,
                             grad_mode=grad_mode, ws=self.ws)
         return dX, dA, dB
 

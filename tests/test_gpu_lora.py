@@ -22,10 +22,14 @@ def _eq(a, b):
     return torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
-def _full_parity(c: Case):
+def _full_parity(c: Case, transposed=False):
+    """transposed: the backward reads W^T [K][N] (LSN_W_BF16_T) instead of W."""
     import torch
     Y, U = c.gpu_fwd()
-    dX, dA, dB = c.gpu_bwd(U)
+    if transposed:
+        dX, dA, dB = c.gpu_bwd(U, W=c.w_transposed(), transposed=True)
+    else:
+        dX, dA, dB = c.gpu_bwd(U)
     torch.cuda.synchronize()
     Yo, Uo = c.oracle_fwd()
     dXo, dAo, dBo, Go = c.oracle_bwd()
@@ -41,25 +45,32 @@ def _full_parity(c: Case):
     return Y, U, dX, dA, dB
 
 
+@pytest.mark.parametrize("transposed", [False, True], ids=["W", "WT"])
 @pytest.mark.parametrize("base", ["nf4", "bf16"])
-def test_single_linear_parity(gpu, base):
-    print(f"case: single linear T=512 K=N=896 r=16 base={base}", flush=True)
-    _full_parity(Case(512, 896, 896, base=base, tag="single"))
+def test_single_linear_parity(gpu, base, transposed):
+    print(f"case: single linear T=512 K=N=896 r=16 base={base} transposed={transposed}", flush=True)
+    _full_parity(Case(512, 896, 896, base=base, tag="single"), transposed)
 
 
+@pytest.mark.parametrize("transposed", [False, True], ids=["W", "WT"])
 @pytest.mark.parametrize("T,K,N,r", [(300, 256, 192, 16), (1, 128, 128, 8), (777, 512, 1344, 32),
                                      (256, 64, 256, 24), (2048, 896, 128, 16)])
-def test_ragged_and_rank_shapes(gpu, T, K, N, r):
-    print(f"case: T={T} K={K} N={N} r={r}", flush=True)
-    _full_parity(Case(T, K, N, r=r, tag="ragged"))
+def test_ragged_and_rank_shapes(gpu, T, K, N, r, transposed):
+    print(f"case: T={T} K={K} N={N} r={r} transposed={transposed}", flush=True)
+    _full_parity(Case(T, K, N, r=r, tag="ragged"), transposed)
 
 
-def test_accumulate_modes(gpu):
+@pytest.mark.parametrize("transposed", [False, True], ids=["W", "WT"])
+def test_accumulate_modes(gpu, transposed):
     import torch
     c = Case(384, 512, 320, tag="accum")
-    print("case: accumulate modes T=384 K=512 N=320", flush=True)
+    print(f"case: accumulate modes T=384 K=512 N=320 transposed={transposed}", flush=True)
     Y, U = c.gpu_fwd()
-    dX, dA, dB = c.gpu_bwd(U, dx_mode=lib.DX_F32_ADD, grad_mode=lib.GRAD_ADD)
+    if transposed:
+        dX, dA, dB = c.gpu_bwd(U, dx_mode=lib.DX_F32_ADD, grad_mode=lib.GRAD_ADD, W=c.w_transposed(),
+                               transposed=True)
+    else:
+        dX, dA, dB = c.gpu_bwd(U, dx_mode=lib.DX_F32_ADD, grad_mode=lib.GRAD_ADD)
     torch.cuda.synchronize()
     dXo, dAo, dBo, _ = c.oracle_bwd()
     r, K = c.r, c.K
@@ -128,6 +139,9 @@ def test_argument_validation(gpu):
     dB = torch.empty((128, 16), dtype=torch.float32, device="cuda")
     with pytest.raises(lib.LsnError):
         lib.lora_linear_bwd(c.desc(), c.Xd, c.dYd, U, dX, dA, dB, ws=small)
+    with pytest.raises(lib.LsnError) as e:     # the transposed layout is for the backward only
+        lib.lora_linear_fwd(c.desc(c.w_transposed(), transposed=True), c.Xd, Y, U, ws=c.ws)
+    assert e.value.status == lib.LSN_E_ARG
 
 
 @pytest.mark.parametrize("label,T,K,N", [("8B gate", 4096, 4096, 14336), ("8B down", 4096, 14336, 4096),
@@ -139,8 +153,11 @@ def test_full_size_sampled_parity(gpu, label, T, K, N):
     print(f"case: {label} T={T} K={K} N={N}", flush=True)
     c = Case(T, K, N, tag="full")
     Y, U = c.gpu_fwd()
-    dX, dA, dB = c.gpu_bwd(U)
+    dX, dA, dB = c.gpu_bwd(U, W=c.w_transposed(), transposed=True)   # the stack's backward path
+    dX_nn, dA_nn, dB_nn = c.gpu_bwd(U)
     torch.cuda.synchronize()
+    # the LoRA gradients do not involve W: both backward paths run the same kernels for them
+    assert _eq(dA, dA_nn) and _eq(dB, dB_nn)
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(T, 48, replace=False))
     from oracle import nf4 as onf4
@@ -152,6 +169,7 @@ def test_full_size_sampled_parity(gpu, label, T, K, N):
     dYr = onf4.bf16_to_f32(c.dY[rows])
     dXo = dYr.astype(np.float64) @ Wh.astype(np.float64) + c.s * ((dYr.astype(np.float64) @ B) @ A)
     assert_close("dX", to_np(dX)[rows], dXo)
+    assert_close("dX", to_np(dX_nn)[rows], dXo)
     cols_n = np.sort(rng.choice(N, 64, replace=False))
     cols_k = np.sort(rng.choice(K, 64, replace=False))
     X = onf4.bf16_to_f32(c.X).astype(np.float64)

@@ -37,11 +37,14 @@ def _check_dequant(p, torch):
     dev = _oracle_packed_on_device(p, torch)
     got16 = lib.nf4_dequant(dev, "bf16")
     got32 = lib.nf4_dequant(dev, "f32")
+    got16t = lib.nf4_dequant(dev, "bf16_t")
     torch.cuda.synchronize()
     want32 = nf4.dequant_f32(p)
     np.testing.assert_array_equal(got32.cpu().numpy().view(np.uint32), want32.view(np.uint32))
-    np.testing.assert_array_equal(got16.view(torch.int16).cpu().numpy().view(np.uint16),
-                                  nf4.bf16_rne(want32))
+    want16 = nf4.bf16_rne(want32)
+    np.testing.assert_array_equal(got16.view(torch.int16).cpu().numpy().view(np.uint16), want16)
+    assert tuple(got16t.shape) == (p["cols"], p["rows"])
+    np.testing.assert_array_equal(got16t.view(torch.int16).cpu().numpy().view(np.uint16), want16.T)
 
 
 def test_pack_and_dequant_single_linear(gpu):
@@ -91,6 +94,25 @@ def test_pack_and_dequant_full_size(gpu, shape, label):
     p = _check_pack(w_host, gp)
     del w_host
     _check_dequant(p, torch)
+
+
+@pytest.mark.parametrize("shape", [(136, 2048), (256, 320), (8, 2048)])
+def test_transposed_dequant_ragged_tiles(gpu, shape):
+    """Row and column counts that end inside a 128 x 256 tile of the transposed kernel."""
+    import torch
+    print(f"case: transposed dequant {shape}", flush=True)
+    w = inputs.host_normal(shape, 0.02, 0, "nf4-t", shape)
+    p = nf4.pack(w)
+    _check_dequant(p, torch)
+
+
+def test_transposed_dequant_needs_rows_multiple_of_8(gpu):
+    import torch
+    p = nf4.pack(inputs.host_normal((4, 4096), 0.02, 0, "nf4-t4"))
+    dev = _oracle_packed_on_device(p, torch)
+    with pytest.raises(lib.LsnError) as e:
+        lib.nf4_dequant(dev, "bf16_t")
+    assert e.value.status == lib.LSN_E_ARG
 
 
 def test_pack_rejects_non_finite(gpu):
