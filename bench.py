@@ -132,10 +132,11 @@ def main():
 
     # dominant kernel: the fused forward GEMM launches of the timed steps
     dur_ms, flops = 0.0, 0
-    for j, e0, e1 in gemm_events:
-        _, K, N = cfg.projections()[j]
+    for js, e0, e1 in gemm_events:
         dur_ms += e0.elapsed_time(e1)
-        flops += 2 * cfg.T * K * N + 2 * cfg.T * cfg.r * N
+        for j in js:
+            _, K, N = cfg.projections()[j]
+            flops += 2 * cfg.T * K * N + 2 * cfg.T * cfg.r * N
     n_launch = len(gemm_events)
     achieved = flops / (dur_ms * 1e-3) / 1e12 if dur_ms > 0 else 0.0
     if cfg.base == "nf4" and stack.dequant == "fused":

@@ -190,6 +190,20 @@ lsn_status lora_down(int64_t T, int64_t K, const uint16_t *X, int32_t n, const u
 lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uint16_t *X,
                            uint16_t *Y, uint16_t *U, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * lora_linear_fwd_group - the forwards of n (1 <= n <= 8) linears that read the same input
+ * X [T][K] (in a decoder layer q, k, v, gate and up all read the attention input; transcript
+ * @1:25-1:58 puts an adapter on each): Y_g = bf16(X W_g^T + s U_g B_g^T) for g < n, bit-identical
+ * to n calls of lora_linear_fwd. L is an array of n descriptors that share T, K, r and the scale
+ * (their N and weights differ); Y and U are host arrays of n device pointers (U ignored with
+ * adapters off). With bf16 weights the n products run as one GEMM launch over the concatenated
+ * output columns (fewer, fuller waves of tiles); with any NF4 member each runs on its own.
+ * Output/input overlaps give LSN_E_ARG. Async on `stream`.
+ */
+lsn_status lora_linear_fwd_group(int32_t n, const lsn_lora_linear *L, int32_t adapters, const uint16_t *X,
+                                 uint16_t *const *Y, uint16_t *const *U, void *ws, size_t ws_bytes,
+                                 void *stream);
+
 enum { LSN_DX_BF16_SET = 0, LSN_DX_F32_ADD = 1 };
 enum { LSN_GRAD_SET = 0, LSN_GRAD_ADD = 1 };
 

@@ -35,8 +35,9 @@ struct GemmArgs {
 
 lsn_status launch_gemm(int layout, int wkind, int epi, GemmArgs a, hipStream_t s);
 
-// direct-load NT GEMM on bf16 W: out_seg = bf16/f32+= ( act W_seg^T + s U_seg B_seg^T ) for up to 4
-// segments sharing act [M][K] (K % 32 == 0)
+// direct-load NT GEMM on bf16 W: out_seg = bf16/f32+= ( act W_seg^T + s U_seg B_seg^T ) for up to
+// kMaxSegs segments sharing act [M][K] (K % 32 == 0)
+constexpr int kMaxSegs = 8;
 struct GemmSeg {
   int64_t ntile0;          // first N tile of the segment (filled by launch_gemm_direct)
   int64_t N;
@@ -49,7 +50,7 @@ struct DirectArgs {
   int64_t M, K;
   const uint16_t *act;
   int nseg;
-  GemmSeg seg[4];
+  GemmSeg seg[kMaxSegs];
   int r;
   float scale;
   int adapters;

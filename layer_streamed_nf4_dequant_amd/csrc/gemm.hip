@@ -452,7 +452,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs a) {
 // writes are contiguous 1 KB segments.
 // =============================================================================================
 constexpr int DBK = 32;
-constexpr int DSTAGES = 4;
+constexpr int DSTAGES = 5;
 constexpr int DTILE = 256 * DBK * 2;           // 16 KB: one operand, one stage
 
 __device__ __forceinline__ int dlds_off(int row, int chunk) { return (row * 4 + (chunk ^ ((row >> 2) & 3))) * 16; }
@@ -485,9 +485,11 @@ __device__ __forceinline__ void issue_direct4(char *lds_tile, __amdgpu_buffer_rs
   for (int i = 0; i < 4; ++i) issue_direct1(lds_tile, rsrc, d, k_bytes, wave, i);
 }
 
-// wait until at most 16 vector-memory operations of this wave are outstanding (the two newest
-// stages, 8 loads each): the oldest stage in flight has landed
-__device__ __forceinline__ void wait_vm_16() { __builtin_amdgcn_s_waitcnt((16 & 15) | (7 << 4) | (15 << 8) | ((16 >> 4) << 14)); }
+// each wave issues 8 direct loads per stage; waiting until the loads of the DSTAGES - 2 newest
+// stages are the only ones outstanding means the oldest stage in flight has landed
+// gfx9 s_waitcnt immediate: vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+template <int N>
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14)); }
 
 // Workgroup barrier for the direct-load ring. __syncthreads() would wait for every outstanding
 // vector-memory operation (the direct-to-LDS loads count as LDS writes), draining the three
@@ -496,10 +498,31 @@ __device__ __forceinline__ void wait_vm_16() { __builtin_amdgcn_s_waitcnt((16 & 
 // compiler from moving LDS accesses across.
 __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_sched_barrier(0);
-  wait_vm_16();
+  wait_vm<8 * (DSTAGES - 2)>();
   __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD b % 8) and each
+// XCD has its own L2. Tile order: groups of GROUP_M m-tiles walk across all n-tiles, m fastest,
+// and each XCD takes a contiguous run of that order, so the ~32 tiles an XCD holds at once span
+// 4 m-tiles x 8 n-tiles and share their operand slices in that XCD's L2.
+constexpr int GROUP_M = 4;
+constexpr bool kXcdRemap = true;
+__device__ __forceinline__ void tile_coords(int64_t b, int64_t ntiles, int64_t tiles_m, int64_t &mt, int64_t &nt) {
+  int64_t id = b;
+  if (kXcdRemap) {
+    const int64_t n8 = ntiles / 8 * 8;
+    if (b < n8) id = (b % 8) * (n8 / 8) + b / 8;
+  }
+  const int64_t tiles_n = ntiles / tiles_m;
+  const int64_t per_group = GROUP_M * tiles_n;
+  const int64_t g = id / per_group;
+  const int64_t gm = min((int64_t)GROUP_M, tiles_m - g * GROUP_M);
+  const int64_t in = id - g * per_group;
+  mt = g * GROUP_M + in % gm;
+  nt = in / gm;
 }
 
 template <int EPI>
@@ -514,13 +537,13 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // tile -> (m tile, segment, n tile within the segment); consecutive workgroups walk down M
+  // tile -> (m tile, segment, n tile within the segment)
   const int64_t tiles_m = (a.M + BM - 1) / BM;
-  const int64_t mt = blockIdx.x % tiles_m;
-  int64_t nt = blockIdx.x / tiles_m;
+  int64_t mt, nt;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, mt, nt);
   int sidx = 0;
 #pragma unroll
-  for (int q = 1; q < 4; ++q)
+  for (int q = 1; q < kMaxSegs; ++q)
     if (q < a.nseg && nt >= a.seg[q].ntile0) sidx = q;
   const GemmSeg sg = a.seg[sidx];
   nt -= sg.ntile0;
@@ -610,8 +633,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
 
-  // prologue: stages 0, 1, 2 in flight (steps past the end re-load the last step into stages
-  // that are never read); stage 0 visible; fragments of step 0, sub-step 0 loaded
+  // prologue: stages 0 .. DSTAGES-2 in flight (steps past the end re-load the last step into
+  // stages that are never read); stage 0 visible; fragments of step 0, sub-step 0 loaded
 #pragma unroll
   for (int p = 0; p < DSTAGES - 1; ++p) {
     const uint32_t kb = (uint32_t)min(p, k_last) * DBK * 2;
@@ -623,13 +646,13 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   load_frags(0, 0, ca, cb);
   // Step kt: stage kt is visible and its sub-step 0 fragments are in (ca, cb).
   //  1. load sub-step 1 of step kt; run sub-step 0, with the refill of stage kt-1 (read by every
-  //     wave before the previous barrier) with step kt+3 spread over its MFMAs, one direct load
+  //     wave before the previous barrier) with step kt+DSTAGES-1 spread over its MFMAs, one direct load
   //     per two MFMAs, so that the loads issue in the matrix core's shadow;
   //  2. wait for the own loads of step kt+1, barrier (the last sub-step 0 MFMAs keep running);
   //  3. load sub-step 0 of step kt+1, run sub-step 1 of step kt.
+  int st = 0;                                           // stage of step kt
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & (DSTAGES - 1);
-    const int nx = (kt + DSTAGES - 1) & (DSTAGES - 1);
+    const int nx = st == 0 ? DSTAGES - 1 : st - 1;        // the stage read in step kt-1
     const uint32_t kb = (uint32_t)min(kt + DSTAGES - 1, k_last) * DBK * 2;
     // fixed order, one group per scheduling fence: read one sub-step 1 fragment, two MFMAs,
     // one direct load
@@ -644,7 +667,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     ring_barrier();
-    load_frags((kt + 1) & (DSTAGES - 1), 0, ca, cb);
+    st = st == DSTAGES - 1 ? 0 : st + 1;
+    load_frags(st, 0, ca, cb);
     mfmas(na, nb);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {

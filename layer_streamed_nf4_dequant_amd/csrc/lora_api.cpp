@@ -207,6 +207,105 @@ lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uin
   return launch_gemm(GEMM_NT, W_IS_NF4, EPI_BF16, a, s);
 }
 
+lsn_status lora_linear_fwd_group(int32_t n, const lsn_lora_linear *L, int32_t adapters, const uint16_t *X,
+                                 uint16_t *const *Y, uint16_t *const *U, void *ws, size_t ws_bytes, void *stream) {
+  if (n < 1 || n > kMaxSegs || !L || !Y || (adapters && !U))
+    return fail(LSN_E_ARG, "lora_linear_fwd_group: need 1 <= n <= %d and non-null arrays", kMaxSegs);
+  bool all_bf16 = true;
+  for (int g = 0; g < n; ++g) {
+    lsn_status st = check_linear(&L[g], "lora_linear_fwd_group");
+    if (st != LSN_OK) return st;
+    if (L[g].T != L[0].T || L[g].K != L[0].K || L[g].r != L[0].r || L[g].scale != L[0].scale)
+      return fail(LSN_E_ARG, "lora_linear_fwd_group: members must share T, K, r and the scale");
+    if (L[g].W.kind == LSN_W_BF16_T)
+      return fail(LSN_E_ARG, "lora_linear_fwd_group: the transposed bf16 layout is for the backward only");
+    all_bf16 = all_bf16 && L[g].W.kind == LSN_W_BF16;
+  }
+  if (adapters != LSN_ADAPTERS_OFF && adapters != LSN_ADAPTERS_ON && adapters != LSN_ADAPTERS_U_READY)
+    return fail(LSN_E_ARG, "lora_linear_fwd_group: unknown adapters mode %d", adapters);
+  const int64_t T = L[0].T, K = L[0].K, r = L[0].r;
+  if (!X || !aligned16(X)) return fail(LSN_E_ARG, "lora_linear_fwd_group: X null or not 16-byte aligned");
+  // every output against every input, and the outputs pairwise
+  const void *outs[2 * kMaxSegs];
+  size_t outb[2 * kMaxSegs];
+  int n_out = 0;
+  for (int g = 0; g < n; ++g) {
+    if (!Y[g] || !aligned16(Y[g])) return fail(LSN_E_ARG, "lora_linear_fwd_group: Y[%d] null or not 16-byte aligned", g);
+    outs[n_out] = Y[g];
+    outb[n_out++] = (size_t)(T * L[g].N * 2);
+    if (adapters) {
+      if (!U[g] || !aligned16(U[g]))
+        return fail(LSN_E_ARG, "lora_linear_fwd_group: U[%d] null or not 16-byte aligned", g);
+      if (adapters == LSN_ADAPTERS_ON) {
+        outs[n_out] = U[g];
+        outb[n_out++] = (size_t)(T * r * 2);
+      }
+    }
+  }
+  for (int o = 0; o < n_out; ++o) {
+    if (ranges_overlap(outs[o], outb[o], X, (size_t)(T * K * 2)))
+      return fail(LSN_E_ARG, "lora_linear_fwd_group: an output overlaps X");
+    for (int p = 0; p < o; ++p)
+      if (ranges_overlap(outs[o], outb[o], outs[p], outb[p]))
+        return fail(LSN_E_ARG, "lora_linear_fwd_group: two outputs overlap");
+    for (int g = 0; g < n; ++g) {
+      const void *ins[5] = {L[g].A, L[g].B};
+      size_t inb[5] = {(size_t)(r * K * 2), (size_t)(L[g].N * r * 2)};
+      const int n_in = 2 + w_ranges(&L[g], ins + 2, inb + 2);
+      for (int i = 0; i < n_in; ++i)
+        if (ranges_overlap(outs[o], outb[o], ins[i], inb[i]))
+          return fail(LSN_E_ARG, "lora_linear_fwd_group: an output overlaps an input");
+    }
+  }
+  if (adapters == LSN_ADAPTERS_U_READY)
+    for (int g = 0; g < n; ++g)
+      for (int h = 0; h < n; ++h)
+        if (ranges_overlap(Y[g], (size_t)(T * L[g].N * 2), U[h], (size_t)(T * r * 2)))
+          return fail(LSN_E_ARG, "lora_linear_fwd_group: a Y overlaps a U");
+  lsn_status st = require_gfx950();
+  if (st != LSN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (adapters == LSN_ADAPTERS_ON) {
+    // the down-projections in as few passes over X as the 128-column limit of one pass allows
+    for (int g0 = 0; g0 < n;) {
+      RowProjSet set{};
+      while (g0 < n && set.total + r <= 128) {
+        set.P[set.n] = L[g0].A;
+        set.out[set.n] = U[g0];
+        set.r[set.n] = (int)r;
+        set.start[set.n] = set.total;
+        set.total += (int)r;
+        ++set.n;
+        ++g0;
+      }
+      if ((st = launch_rowproj(X, T, K, set, s)) != LSN_OK) return st;
+    }
+  }
+  const int mode = adapters ? LSN_ADAPTERS_U_READY : LSN_ADAPTERS_OFF;
+  if (!all_bf16) {
+    for (int g = 0; g < n; ++g)
+      if ((st = lora_linear_fwd(&L[g], mode, X, Y[g], adapters ? U[g] : nullptr, ws, ws_bytes, stream)) != LSN_OK)
+        return st;
+    return LSN_OK;
+  }
+  DirectArgs d{};
+  d.M = T;
+  d.K = K;
+  d.act = X;
+  d.nseg = n;
+  for (int g = 0; g < n; ++g) {
+    d.seg[g].N = L[g].N;
+    d.seg[g].w = L[g].W.bf16;
+    d.seg[g].lr_w = L[g].B;
+    d.seg[g].lr_act = adapters ? U[g] : nullptr;
+    d.seg[g].out = Y[g];
+  }
+  d.r = (int)r;
+  d.scale = L[0].scale;
+  d.adapters = adapters ? 1 : 0;
+  return launch_gemm_direct(d, EPI_BF16, s);
+}
+
 lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const uint16_t *dY, const uint16_t *U,
                            void *dX, int32_t dx_mode, float *dA, float *dB, int32_t grad_mode, void *ws,
                            size_t ws_bytes, void *stream) {

@@ -24,21 +24,25 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4_t v) { return __builtin_bit_ca
 // One 256-thread workgroup per 16 rows; wave w takes the 32-wide K-steps w, w+4, w+8, ...; the
 // four partial results are added in wave order through LDS. Column block cb (16 columns of the
 // concatenated P) is one MFMA 16x16x32 accumulator.
+// The work per K-step is tiny (one activation fragment, NBMAX weight fragments, NBMAX MFMAs), so
+// the loop is latency-bound unless many loads are in flight: each wave keeps the operands of
+// DEPTH K-steps in registers and issues the loads of step i + DEPTH as it consumes step i.
 // ---------------------------------------------------------------------------------------------
+template <int NBMAX, int DEPTH>
 __global__ __launch_bounds__(256) void k_rowproj(const uint16_t *__restrict__ act, int64_t M, int64_t K,
                                                  RowProjSet set) {
-  __shared__ floatx4_t part[4][8][64];
+  __shared__ floatx4_t part[4][NBMAX][64];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t m0 = (int64_t)blockIdx.x * 16;
   const int64_t m = min(m0 + (lane & 15), M - 1);      // clamped rows are never stored
   const int kq = 8 * (lane >> 4);
-  const int64_t nks = K / 32;
+  const int nks = (int)(K / 32);
   const int nblk = (set.total + 15) / 16;
   // the concatenated row c of P: group g, local row c - start[g]
-  const uint16_t *prow[8];
-  bool pok[8];
+  const uint16_t *prow[NBMAX];
+  bool pok[NBMAX];
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) {
+  for (int cb = 0; cb < NBMAX; ++cb) {
     const int c = 16 * cb + (lane & 15);
     int g = 0;
 #pragma unroll
@@ -46,23 +50,38 @@ __global__ __launch_bounds__(256) void k_rowproj(const uint16_t *__restrict__ ac
     pok[cb] = cb < nblk && c < set.total;
     prow[cb] = set.P[g] + (int64_t)(pok[cb] ? c - set.start[g] : 0) * K;
   }
-  floatx4_t acc[8];
+  const uint16_t *arow = act + m * K + kq;
+  floatx4_t acc[NBMAX];
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) acc[cb] = floatx4_t{0, 0, 0, 0};
-  for (int64_t ks = wave; ks < nks; ks += 4) {
-    const int64_t k = ks * 32 + kq;
-    const u32x4_t va = *reinterpret_cast<const u32x4_t *>(act + m * K + k);
+  for (int cb = 0; cb < NBMAX; ++cb) acc[cb] = floatx4_t{0, 0, 0, 0};
+  u32x4_t va[DEPTH], vb[DEPTH][NBMAX];
+  // K-step of this wave's i-th iteration, clamped (a clamped step is loaded but not used)
+  auto load = [&](int i, u32x4_t &a_, u32x4_t (&b_)[NBMAX]) {
+    const int64_t k = (int64_t)min(wave + 4 * i, nks - 1) * 32;
+    a_ = *reinterpret_cast<const u32x4_t *>(arow + k);
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      if (cb < nblk) {
-        u32x4_t vb = {0, 0, 0, 0};
-        if (pok[cb]) vb = *reinterpret_cast<const u32x4_t *>(prow[cb] + k);
-        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(vb), acc[cb], 0, 0, 0);
+    for (int cb = 0; cb < NBMAX; ++cb) {
+      b_[cb] = u32x4_t{0, 0, 0, 0};
+      if (pok[cb]) b_[cb] = *reinterpret_cast<const u32x4_t *>(prow[cb] + k + kq);
+    }
+  };
+  const int iters = (nks - wave + 3) / 4;                // K-steps of this wave
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) load(d, va[d], vb[d]);
+  for (int i0 = 0; i0 < iters; i0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      if (i0 + d < iters) {
+#pragma unroll
+        for (int cb = 0; cb < NBMAX; ++cb)
+          if (cb < nblk)
+            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[d]), as_bf16x8(vb[d][cb]), acc[cb], 0, 0, 0);
       }
+      load(i0 + d + DEPTH, va[d], vb[d]);
     }
   }
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) part[wave][cb][lane] = acc[cb];
+  for (int cb = 0; cb < NBMAX; ++cb) part[wave][cb][lane] = acc[cb];
   __syncthreads();
   // 4 waves finish 4 column blocks at a time; lane holds column c = 16 cb + lane % 16 and rows
   // 4 (lane / 16) + e
@@ -200,7 +219,14 @@ __global__ __launch_bounds__(256) void k_tn_reduce(const float *__restrict__ par
 }  // namespace
 
 lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const RowProjSet &set, hipStream_t s) {
-  hipLaunchKernelGGL(k_rowproj, dim3((unsigned)((M + 15) / 16)), dim3(256), 0, s, act, M, K, set);
+  const dim3 grid((unsigned)((M + 15) / 16));
+  const int nblk = (set.total + 15) / 16;
+  if (nblk <= 2)
+    hipLaunchKernelGGL((k_rowproj<2, 8>), grid, dim3(256), 0, s, act, M, K, set);
+  else if (nblk <= 5)
+    hipLaunchKernelGGL((k_rowproj<5, 4>), grid, dim3(256), 0, s, act, M, K, set);
+  else
+    hipLaunchKernelGGL((k_rowproj<8, 3>), grid, dim3(256), 0, s, act, M, K, set);
   return check_hip(hipGetLastError(), "k_rowproj launch");
 }
 

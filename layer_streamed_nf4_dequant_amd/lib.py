@@ -30,7 +30,8 @@ FAULT_STALE_REFETCH, FAULT_WRONG_SLOT = 1 << 8, 1 << 9
 
 EXPORTS = (
     "lsn_last_error", "lsn_abi_version", "lsn_nf4_codebook", "nf4_pack_ws_bytes", "nf4_pack",
-    "nf4_dequant", "lora_down", "lora_linear_ws_bytes", "lora_linear_fwd", "lora_linear_bwd",
+    "nf4_dequant", "lora_down", "lora_linear_ws_bytes", "lora_linear_fwd", "lora_linear_fwd_group",
+    "lora_linear_bwd",
     "layer_pool_create", "layer_pool_register", "layer_pool_prefetch", "layer_pool_acquire",
     "layer_pool_release", "layer_pool_stats", "layer_pool_audit", "layer_pool_destroy",
 )
@@ -89,6 +90,8 @@ def load():
         "lora_down": (i32, [i64, i64, vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(vp), vp]),
         "lora_linear_ws_bytes": (sz, [i64, i64, i64, i64]),
         "lora_linear_fwd": (i32, [ctypes.POINTER(LoraLinearDesc), i32, vp, vp, vp, vp, sz, vp]),
+        "lora_linear_fwd_group": (i32, [i32, ctypes.POINTER(LoraLinearDesc), i32, vp, ctypes.POINTER(vp),
+                                        ctypes.POINTER(vp), vp, sz, vp]),
         "lora_linear_bwd": (i32, [ctypes.POINTER(LoraLinearDesc), vp, vp, vp, vp, i32, vp, vp, i32,
                                   vp, sz, vp]),
         "layer_pool_create": (i32, [i32, sz, ctypes.POINTER(vp), i32, vp, ctypes.c_uint32,
@@ -233,6 +236,18 @@ def lora_linear_fwd(desc: LoraLinearDesc, X, Y, U=None, adapters=True, ws=None, 
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     check(load().lora_linear_fwd(ctypes.byref(desc), mode, _ptr(X), _ptr(Y), _ptr(U),
                                  _ptr(ws), nbytes, _stream_handle(stream)))
+
+
+def lora_linear_fwd_group(descs, X, Y_list, U_list=None, adapters=True, ws=None, stream=None) -> None:
+    """The forwards of linears sharing the input X (one GEMM launch for bf16 weights)."""
+    mode = adapters if isinstance(adapters, int) and not isinstance(adapters, bool) else (
+        ADAPTERS_ON if adapters else ADAPTERS_OFF)
+    n = len(descs)
+    arr = (LoraLinearDesc * n)(*descs)
+    Y = (ctypes.c_void_p * n)(*[_ptr(y) for y in Y_list])
+    U = (ctypes.c_void_p * n)(*[_ptr(u) for u in U_list]) if U_list is not None else None
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    check(load().lora_linear_fwd_group(n, arr, mode, _ptr(X), Y, U, _ptr(ws), nbytes, _stream_handle(stream)))
 
 
 def lora_linear_bwd(desc: LoraLinearDesc, X, dY, U, dX, dA, dB, dx_mode: int = DX_BF16_SET,

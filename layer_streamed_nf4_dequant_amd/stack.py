@@ -235,18 +235,21 @@ class Stack:
                                   self.B[l][j].data_ptr())
 
     def _forward_layer(self, base: int, l: int, Y, s, gemm_events=None):
-        # the adapters' down-projections, once per shared input (q, k, v, gate, up read X_h)
+        # per shared input (q, k, v, gate and up read X_h; o reads X_o; down reads X_d): the
+        # adapters' down-projections in one pass over the input, then the projections' forward
+        # GEMMs as one grouped launch
         for which in ("h", "o", "d"):
             js = [j for j, p in enumerate(self.layout) if PROJ_INPUT[p.name] == which]
-            if js:
-                lib.lora_down(self.X[which], [self.A[l][j] for j in js], [self.U[j] for j in js], stream=s)
-        for j, p in enumerate(self.layout):
+            if not js:
+                continue
+            lib.lora_down(self.X[which], [self.A[l][j] for j in js], [self.U[j] for j in js], stream=s)
             if gemm_events is not None:
-                gemm_events.append((j, self.torch.cuda.Event(enable_timing=True),
+                gemm_events.append((js, self.torch.cuda.Event(enable_timing=True),
                                     self.torch.cuda.Event(enable_timing=True)))
                 gemm_events[-1][1].record(s)
-            lib.lora_linear_fwd(self._desc(base, l, j), self.X[PROJ_INPUT[p.name]], Y[j], self.U[j],
-                                adapters=lib.ADAPTERS_U_READY, ws=self.ws, stream=s)
+            lib.lora_linear_fwd_group([self._desc(base, l, j) for j in js], self.X[which], [Y[j] for j in js],
+                                      [self.U[j] for j in js], adapters=lib.ADAPTERS_U_READY, ws=self.ws,
+                                      stream=s)
             if gemm_events is not None:
                 gemm_events[-1][2].record(s)
 
@@ -293,8 +296,8 @@ class Stack:
 
     def step(self, mode: str = "streamed", gemm_events=None) -> float:
         """One training step of the projection stack; returns its time in ms (compute stream).
-        gemm_events: optional list; (projection, start, end) HIP events around every fused
-        forward GEMM launch are appended to it."""
+        gemm_events: optional list; (projections, start, end) HIP events around every forward
+        GEMM launch (one per group of projections sharing an input) are appended to it."""
         torch = self.torch
         s = self.compute
         sh = s.cuda_stream

@@ -11,6 +11,7 @@ import pytest
 from layer_streamed_nf4_dequant_amd import lib
 from lora_cases import Case, assert_close, to_np
 from oracle import lora as olora
+from oracle.nf4 import bf16_to_f32 as onf4_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -95,6 +96,39 @@ def test_fused_nf4_equals_bf16_gemm_on_dequantised_weights(gpu, T, K, N):
     torch.cuda.synchronize()
     for a, b in ((Y1, Y2), (U1, U2), (dX1, dX2), (dA1, dA2), (dB1, dB2)):
         assert _eq(a, b)
+
+
+@pytest.mark.parametrize("base", ["nf4", "bf16"])
+def test_grouped_forward_equals_single_forwards(gpu, base):
+    """Five linears sharing one input (a decoder layer's q, k, v, gate, up at small widths),
+    with ragged T: the grouped forward is bit-identical to one call per linear, and matches
+    the oracle."""
+    import torch
+    T, K, r = 300, 512, 16
+    Ns = [512, 128, 128, 1344, 1344]
+    cs = [Case(T, K, N, r=r, base=base, tag=f"group{i}") for i, N in enumerate(Ns)]
+    X = cs[0].Xd
+    print(f"case: grouped forward T={T} K={K} N={Ns} base={base}", flush=True)
+    for mode in (lib.ADAPTERS_ON, lib.ADAPTERS_OFF):
+        Yg = [torch.empty((T, N), dtype=torch.bfloat16, device="cuda") for N in Ns]
+        Ug = [torch.empty((T, r), dtype=torch.bfloat16, device="cuda") for _ in Ns]
+        lib.lora_linear_fwd_group([c.desc() for c in cs], X, Yg, Ug, adapters=mode, ws=cs[0].ws)
+        for c, y, u in zip(cs, Yg, Ug):
+            Y1 = torch.empty_like(y)
+            U1 = torch.empty_like(u)
+            lib.lora_linear_fwd(c.desc(), X, Y1, U1, adapters=mode, ws=c.ws)
+            torch.cuda.synchronize()
+            assert _eq(y, Y1)
+            if mode == lib.ADAPTERS_ON:
+                assert _eq(u, U1)
+            Yo, _ = olora.forward(onf4_f32(cs[0].X), onf4_f32(c.W_hat_bits), onf4_f32(c.A),
+                                  onf4_f32(c.B), c.s, mode == lib.ADAPTERS_ON)
+            assert_close("Y", to_np(y), Yo)
+    with pytest.raises(lib.LsnError):          # members must share K
+        bad = Case(T, 256, 128, r=r, base=base, tag="group-bad")
+        lib.lora_linear_fwd_group([cs[0].desc(), bad.desc()], X, Yg[:2], Ug[:2], ws=cs[0].ws)
+    with pytest.raises(lib.LsnError):          # a Y overlapping X
+        lib.lora_linear_fwd_group([cs[0].desc(), cs[1].desc()], X, [Yg[0], X], Ug[:2], ws=cs[0].ws)
 
 
 def test_b_zero_equals_adapters_off_and_recompute_equals_forward(gpu):
