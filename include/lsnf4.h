@@ -234,9 +234,10 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
  *                refilled only after that event. Releasing a layer not held: LSN_E_STATE.
  * Every visit copies the layer again (each layer is read twice per step) unless
  * LSN_POOL_KEEP_AT_TURN is set, in which case a layer still in a free slot is reused.
- * Refusal (Soup benchmarks README: the fit decision refuses rather than warns): create
- * returns LSN_E_NOFIT if the slots exceed free device memory, register returns LSN_E_NOFIT
- * for an image larger than slot_bytes. Nothing ever spills to host-mapped memory.
+ * Refusal (Soup benchmarks README: the fit decision refuses rather than warns): the slots are
+ * caller memory, so whether n_slots x slot_bytes fits in free device memory is decided (and
+ * refused) by the caller before it allocates them; register returns LSN_E_NOFIT for an image
+ * larger than slot_bytes. Nothing ever spills to host-mapped memory.
  * Aliasing audit (LSN_POOL_AUDIT; the pages' silent wrong-gradient defect was aliasing): a
  * 64-bit checksum of the slot is taken on the compute stream at every acquire and release
  * and compared with the host image's checksum by layer_pool_audit; released slots are
