@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--config", default="C3")
     ap.add_argument("--dequant", default="staged", choices=["staged", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-modes", action="store_true",
+                    help="skip the resident and no-H2D comparison timings")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -111,7 +113,8 @@ def main():
     cfg = configs.CONFIGS[args.config]
     print(f"[bench] setting up {cfg.name}: {cfg.layers} layers, T={cfg.T}, mode={args.mode}", flush=True)
     t0 = time.perf_counter()
-    stack = Stack(cfg, modes=(args.mode,), dequant=args.dequant)
+    modes = (args.mode,) if args.no_other_modes else tuple(dict.fromkeys((args.mode, "streamed", "resident", "no_h2d")))
+    stack = Stack(cfg, modes=modes, dequant=args.dequant)
     torch.cuda.synchronize()
     print(f"[bench] setup {time.perf_counter() - t0:.1f} s; image {stack.image_bytes / 1e6:.2f} MB/layer",
           flush=True)
@@ -119,12 +122,12 @@ def main():
         ms = stack.step(args.mode)
         print(f"[bench] warmup {i}: {ms:.1f} ms", flush=True)
 
-    gemm_events = []
+    gemm_events, dequant_events = [], []
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     step_ms = []
     for i in range(args.steps):
-        step_ms.append(stack.step(args.mode, gemm_events=gemm_events))
+        step_ms.append(stack.step(args.mode, gemm_events=gemm_events, dequant_events=dequant_events))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     print(f"[bench] {args.steps} steps: {wall * 1e3 / args.steps:.1f} ms/step (events median "
@@ -147,6 +150,38 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_from_profiles(),
                 "kernel": kernel, "launches": n_launch,
                 "avg_launch_us": round(dur_ms * 1e3 / max(n_launch, 1), 2)}
+
+    dequant = None
+    if dequant_events:
+        # algorithmic bytes per staged visit: read the NF4 image, write bf16 W (and bf16 W^T on the
+        # backward visit)
+        n_params = sum(K * N for _, K, N in cfg.projections())
+        nf4_b = cfg.nf4_bytes_per_layer()
+        d_ms, d_bytes = 0.0, 0
+        for transposed, e0, e1 in dequant_events:
+            d_ms += e0.elapsed_time(e1)
+            d_bytes += (2 if transposed else 1) * (nf4_b + 2 * n_params)
+        gbs = d_bytes / (d_ms * 1e-3) / 1e9
+        dequant = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": round(gbs / PEAK_HBM_GBS, 4), "kernels": "k_dequant + k_dequant_t (per-visit staging)",
+                   "bytes_per_param": round(nf4_b / n_params + 2, 4), "visits": len(dequant_events)}
+
+    other = {}
+    if not args.no_other_modes:
+        for m in ("resident", "no_h2d"):
+            if m == args.mode:
+                continue
+            stack.step(m)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            n = max(3, args.steps // 2)
+            for _ in range(n):
+                stack.step(m)
+            torch.cuda.synchronize()
+            other[m] = round(cfg.T * n / (time.perf_counter() - t0), 1)
+            print(f"[bench] {m}: {other[m]} tokens/s", flush=True)
+        if stack.slots is not None:
+            other["h2d_GBs"] = round(stack.h2d_rate(), 1)
 
     tokens = cfg.T * args.steps
     value = tokens / wall
@@ -174,6 +209,10 @@ def main():
                    "h2d_bytes_per_step": (pool["bytes_copied"] // (args.steps + args.warmup)) if pool else 0},
         "roofline": roofline,
     }
+    if dequant is not None:
+        out["dequant"] = dequant
+    if other:
+        out["other_modes_tokens_per_s"] = other
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg)

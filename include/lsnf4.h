@@ -145,6 +145,15 @@ enum { LSN_OUT_BF16 = 0, LSN_OUT_F32 = 1, LSN_OUT_BF16_T = 2 };
  */
 lsn_status nf4_dequant(const lsn_nf4 *w, void *out, int32_t out_dtype, void *stream);
 
+/*
+ * nf4_dequant_batch - nf4_dequant of n (1 <= n <= 8) tensors, all into the same layout, as one
+ * launch (a decoder layer's seven projections per visit: "Exact Layer Streaming", Abstract,
+ * per-layer dequantisation). w is a host array of n descriptors, out a host array of n device
+ * pointers. Bit-identical to n nf4_dequant calls; the same rules per tensor; no output may
+ * overlap any input or another output (LSN_E_ARG). Async on `stream`.
+ */
+lsn_status nf4_dequant_batch(int32_t n, const lsn_nf4 *w, void *const *out, int32_t out_dtype, void *stream);
+
 /* ------------------------------------------------------------------------------------------
  * LoRA linear on a frozen base (transcript @1:25-1:58), rank r, scale s (= alpha / r):
  *   forward   U = bf16(X A^T);  Y = bf16( X W^T + s U B^T )   (fp32 accumulation)

@@ -150,22 +150,40 @@ lsn_status nf4_pack(const float *w, int64_t rows, int64_t cols, uint8_t *codes, 
   return LSN_OK;
 }
 
-lsn_status nf4_dequant(const lsn_nf4 *w, void *out, int32_t out_dtype, void *stream) {
-  lsn_status st = check_nf4(w, "nf4_dequant");
-  if (st != LSN_OK) return st;
-  if (!out) return fail(LSN_E_ARG, "nf4_dequant: null output");
+lsn_status nf4_dequant_batch(int32_t n, const lsn_nf4 *w, void *const *out, int32_t out_dtype, void *stream) {
+  if (n < 1 || n > kMaxDqJobs || !w || !out)
+    return fail(LSN_E_ARG, "nf4_dequant: need 1 <= n <= %d tensors and non-null arrays", kMaxDqJobs);
   if (out_dtype != LSN_OUT_BF16 && out_dtype != LSN_OUT_F32 && out_dtype != LSN_OUT_BF16_T)
     return fail(LSN_E_ARG, "nf4_dequant: unknown output dtype %d", out_dtype);
-  if ((uintptr_t)out & 15) return fail(LSN_E_ARG, "nf4_dequant: output must be 16-byte aligned");
-  if (out_dtype == LSN_OUT_BF16_T && w->rows % 8)
-    return fail(LSN_E_ARG, "nf4_dequant: the transposed output needs rows %% 8 == 0 (got %lld)", (long long)w->rows);
-  const size_t n = (size_t)(w->rows * w->cols);
-  const size_t out_bytes = n * (out_dtype == LSN_OUT_F32 ? 4 : 2);
-  if (ranges_overlap(out, out_bytes, w->codes, n / 2) || ranges_overlap(out, out_bytes, w->qabsmax, n / 64) ||
-      ranges_overlap(out, out_bytes, w->absmax2, n / 16384 * 4))
-    return fail(LSN_E_ARG, "nf4_dequant: output overlaps the NF4 input");
-  if ((st = require_gfx950()) != LSN_OK) return st;
-  return launch_dequant(*w, out, out_dtype, (hipStream_t)stream);
+  for (int g = 0; g < n; ++g) {
+    lsn_status st = check_nf4(&w[g], "nf4_dequant");
+    if (st != LSN_OK) return st;
+    if (!out[g]) return fail(LSN_E_ARG, "nf4_dequant: null output %d", g);
+    if ((uintptr_t)out[g] & 15) return fail(LSN_E_ARG, "nf4_dequant: output %d must be 16-byte aligned", g);
+    if (out_dtype == LSN_OUT_BF16_T && w[g].rows % 8)
+      return fail(LSN_E_ARG, "nf4_dequant: the transposed output needs rows %% 8 == 0 (got %lld)",
+                  (long long)w[g].rows);
+  }
+  for (int g = 0; g < n; ++g) {
+    const size_t ne = (size_t)(w[g].rows * w[g].cols);
+    const size_t ob = ne * (out_dtype == LSN_OUT_F32 ? 4 : 2);
+    for (int h = 0; h < n; ++h) {
+      const size_t nh = (size_t)(w[h].rows * w[h].cols);
+      if (ranges_overlap(out[g], ob, w[h].codes, nh / 2) || ranges_overlap(out[g], ob, w[h].qabsmax, nh / 64) ||
+          ranges_overlap(out[g], ob, w[h].absmax2, nh / 16384 * 4))
+        return fail(LSN_E_ARG, "nf4_dequant: an output overlaps an NF4 input");
+      if (h < g && ranges_overlap(out[g], ob, out[h], nh * (out_dtype == LSN_OUT_F32 ? 4 : 2)))
+        return fail(LSN_E_ARG, "nf4_dequant: two outputs overlap");
+    }
+  }
+  lsn_status st = require_gfx950();
+  if (st != LSN_OK) return st;
+  return launch_dequant(n, w, out, out_dtype, (hipStream_t)stream);
+}
+
+lsn_status nf4_dequant(const lsn_nf4 *w, void *out, int32_t out_dtype, void *stream) {
+  void *outs[1] = {out};
+  return nf4_dequant_batch(1, w, outs, out_dtype, stream);
 }
 
 }  // extern "C"

@@ -51,6 +51,8 @@ lsn_status launch_pack_codes(const float *w, int64_t n, uint8_t *codes, float *a
                              int *nonfinite_flag, hipStream_t s);
 lsn_status launch_pack_second(const float *absmax, int64_t n_blocks, float mu, int8_t *qabsmax,
                               float *absmax2, hipStream_t s);
-lsn_status launch_dequant(const lsn_nf4 &w, void *out, int out_dtype, hipStream_t s);
+// dequantise n (<= kMaxDqJobs) tensors into out[g] in one launch (all in the same layout)
+constexpr int kMaxDqJobs = 8;
+lsn_status launch_dequant(int n, const lsn_nf4 *w, void *const *out, int out_dtype, hipStream_t s);
 
 }  // namespace lsn

@@ -117,21 +117,45 @@ __global__ __launch_bounds__(256) void k_pack_second(const float *__restrict__ a
 }
 
 // ---------------------------------------------------------------------------------------------
-// standalone dequantisation: a 256-thread workgroup covers 8192 weights; thread t handles
-// the 8-weight groups t, t+256, t+512, t+768 of its chunk, so every load and store of a wave
-// is contiguous (4 B of codes in, 16 B of bf16 or 32 B of fp32 out per lane).
+// standalone dequantisation of up to kMaxDqJobs tensors in one launch (a decoder layer's seven
+// projections: one ramp and one tail instead of seven). Each job owns a contiguous range of
+// workgroups starting at wg0; a workgroup finds its job by comparing blockIdx.x with the wg0.
 // ---------------------------------------------------------------------------------------------
+struct DqJob {
+  const uint8_t *codes;
+  const int8_t *qabsmax;
+  const float *absmax2;
+  float mu;
+  int64_t rows, cols;
+  void *out;
+  int64_t wg0;
+};
+struct DqJobs {
+  int n;
+  DqJob job[kMaxDqJobs];
+};
+
+__device__ __forceinline__ int find_job(const DqJobs &jobs, int64_t b) {
+  int g = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxDqJobs; ++q)
+    if (q < jobs.n && b >= jobs.job[q].wg0) g = q;
+  return g;
+}
+
+// Row-major: a 256-thread workgroup covers 8192 weights; thread t handles the 8-weight groups
+// t, t+256, t+512, t+768 of its chunk, so every load and store of a wave is contiguous (4 B of
+// codes in, 16 B of bf16 or 32 B of fp32 out per lane).
 template <int OUT>
-__global__ __launch_bounds__(256) void k_dequant(const uint32_t *__restrict__ codes,
-                                                 const int8_t *__restrict__ qabsmax,
-                                                 const float *__restrict__ absmax2, float mu,
-                                                 void *__restrict__ out, Nf4KernelTable tab) {
+__global__ __launch_bounds__(256) void k_dequant(DqJobs jobs, Nf4KernelTable tab) {
   __shared__ float sq[16];
   __shared__ float scode8[256];
   const int t = threadIdx.x;
   if (t < 16) sq[t] = tab.q[t];
   if (t < 255) scode8[t] = int8_level(t - 127);
-  const int64_t g0 = (int64_t)blockIdx.x * 1024 + t;
+  const DqJob &J = jobs.job[find_job(jobs, blockIdx.x)];
+  const uint32_t *codes = reinterpret_cast<const uint32_t *>(J.codes);
+  const int64_t g0 = ((int64_t)blockIdx.x - J.wg0) * 1024 + t;
   uint32_t word[4];
   int v[4];
   float s2[4];
@@ -139,10 +163,12 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t *__restrict__ co
   for (int i = 0; i < 4; ++i) {
     const int64_t g = g0 + 256 * i;
     word[i] = __builtin_nontemporal_load(&codes[g]);
-    v[i] = qabsmax[g >> 3];
-    s2[i] = absmax2[g >> 11];
+    v[i] = J.qabsmax[g >> 3];
+    s2[i] = J.absmax2[g >> 11];
   }
   __syncthreads();
+  const float mu = J.mu;
+  void *out = J.out;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t g = g0 + 256 * i;
@@ -172,60 +198,58 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t *__restrict__ co
 // ---------------------------------------------------------------------------------------------
 // dequantise into the transposed layout: out[k][n] = w_hat[n][k] (bf16), for a backward GEMM
 // that reduces over n with both operands n-contiguous. Same arithmetic as k_dequant, so the
-// values are bit-identical. Workgroup tile: 128 rows n x 256 columns k. Thread t decodes
-// rows n0 + 8 (t % 16) .. +7 at the 8-column groups k0 + 8 (t / 16) and k0 + 128 + 8 (t / 16)
-// (one 4-byte code word per row and group; four neighbouring lanes read 16 contiguous bytes of
-// a row and every 128-byte line of codes is read by one workgroup), then stores each of the 8
-// columns as 8 consecutive n (16 bytes; 16 lanes write 256 contiguous bytes of an out row).
+// values are bit-identical. Workgroup tile: 512 rows n x 64 columns k (one 64-weight block per
+// row). Thread t decodes rows n0 + 8 (t % 64) .. +7 at columns k0 + 16 (t / 64) .. +15 (8 code
+// bytes per row), then stores each of its 16 columns as 8 consecutive n (16 bytes), so a wave's
+// store covers 1 KB of one out row (long write runs keep the HBM pages open). Tiles walk k
+// fastest, so the workgroups that share a 128-byte line of codes run side by side.
 // Requires rows % 8 == 0 (checked by the caller); cols % 64 == 0 by the format.
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_dequant_t(const uint32_t *__restrict__ codes,
-                                                   const int8_t *__restrict__ qabsmax,
-                                                   const float *__restrict__ absmax2, float mu, int64_t rows,
-                                                   int64_t cols, uint16_t *__restrict__ out,
-                                                   Nf4KernelTable tab) {
+__global__ __launch_bounds__(256) void k_dequant_t(DqJobs jobs, Nf4KernelTable tab) {
   __shared__ float sq[16];
   __shared__ float scode8[256];
   const int t = threadIdx.x;
   if (t < 16) sq[t] = tab.q[t];
   if (t < 255) scode8[t] = int8_level(t - 127);
-  const int64_t n = (int64_t)blockIdx.x * 128 + 8 * (t & 15);
-  const int64_t kc[2] = {(int64_t)blockIdx.y * 256 + 8 * (t >> 4), (int64_t)blockIdx.y * 256 + 128 + 8 * (t >> 4)};
-  const bool row_ok = n < rows;
-  uint32_t word[2][8];
-  int v[2][8];
-  float s2[2][8];
+  const DqJob &J = jobs.job[find_job(jobs, blockIdx.x)];
+  const int64_t tile = (int64_t)blockIdx.x - J.wg0;
+  const int64_t kt = J.cols / 64;
+  const int64_t rows = J.rows, cols = J.cols;
+  const int64_t k = (tile % kt) * 64 + 16 * (t >> 6);
+  const int64_t n = (tile / kt) * 512 + 8 * (t & 63);
+  const bool ok = n < rows;
+  uint2 word[8];
+  int v[8];
+  float s2[8];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const bool ok = row_ok && kc[h] < cols;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t e = (n + i) * cols + kc[h];      // element index of the group's first weight
-      word[h][i] = ok ? codes[e >> 3] : 0u;
-      v[h][i] = ok ? qabsmax[e >> 6] : 0;
-      s2[h][i] = ok ? absmax2[e >> 14] : 0.0f;
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int64_t e = (n + i) * cols + k;            // element index of the thread's first weight in row n+i
+    word[i] = ok ? *reinterpret_cast<const uint2 *>(J.codes + (e >> 1)) : make_uint2(0u, 0u);
+    v[i] = ok ? J.qabsmax[e >> 6] : 0;
+    s2[i] = ok ? J.absmax2[e >> 14] : 0.0f;
   }
   __syncthreads();
+  if (!ok) return;
+  const float mu = J.mu;
+  uint16_t *out = reinterpret_cast<uint16_t *>(J.out);
+  float c[8];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (!row_ok || kc[h] >= cols) continue;
-    float c[8];
+  for (int i = 0; i < 8; ++i) c[i] = decode_absmax(scode8[v[i] + 127], s2[i], mu);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = decode_absmax(scode8[v[h][i] + 127], s2[h][i], mu);
+  for (int e = 0; e < 16; ++e) {
+    const int shift = 8 * ((e >> 1) & 3) + ((e & 1) ? 0 : 4);
+    float f[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int shift = 8 * (e >> 1) + ((e & 1) ? 0 : 4);
-      float f[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = __fmul_rn(sq[(word[h][i] >> shift) & 15u], c[i]);
-      u32x4_t o;
-      o.x = pack_bf16x2(f[0], f[1]);
-      o.y = pack_bf16x2(f[2], f[3]);
-      o.z = pack_bf16x2(f[4], f[5]);
-      o.w = pack_bf16x2(f[6], f[7]);
-      __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t *>(out + (kc[h] + e) * rows + n));
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = (e < 8) ? word[i].x : word[i].y;
+      f[i] = __fmul_rn(sq[(w >> shift) & 15u], c[i]);
     }
+    u32x4_t o;
+    o.x = pack_bf16x2(f[0], f[1]);
+    o.y = pack_bf16x2(f[2], f[3]);
+    o.z = pack_bf16x2(f[4], f[5]);
+    o.w = pack_bf16x2(f[6], f[7]);
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t *>(out + (k + e) * rows + n));
   }
 }
 
@@ -248,20 +272,29 @@ lsn_status launch_pack_second(const float *absmax, int64_t n_blocks, float mu, i
   return check_hip(hipGetLastError(), "k_pack_second launch");
 }
 
-lsn_status launch_dequant(const lsn_nf4 &w, void *out, int out_dtype, hipStream_t s) {
-  const int64_t n = w.rows * w.cols;
-  const dim3 grid((unsigned)(n / 8192));
-  const uint32_t *codes = reinterpret_cast<const uint32_t *>(w.codes);
-  if (out_dtype == LSN_OUT_BF16_T) {
-    const dim3 tgrid((unsigned)((w.rows + 127) / 128), (unsigned)((w.cols + 255) / 256));
-    hipLaunchKernelGGL(k_dequant_t, tgrid, dim3(256), 0, s, codes, w.qabsmax, w.absmax2, w.mean, w.rows, w.cols,
-                       reinterpret_cast<uint16_t *>(out), kernel_table());
-  } else if (out_dtype == LSN_OUT_BF16)
-    hipLaunchKernelGGL(k_dequant<LSN_OUT_BF16>, grid, dim3(256), 0, s, codes, w.qabsmax, w.absmax2,
-                       w.mean, out, kernel_table());
+lsn_status launch_dequant(int n, const lsn_nf4 *w, void *const *out, int out_dtype, hipStream_t s) {
+  DqJobs jobs{};
+  jobs.n = n;
+  int64_t wg = 0;
+  for (int g = 0; g < n; ++g) {
+    DqJob &J = jobs.job[g];
+    J.codes = w[g].codes;
+    J.qabsmax = w[g].qabsmax;
+    J.absmax2 = w[g].absmax2;
+    J.mu = w[g].mean;
+    J.rows = w[g].rows;
+    J.cols = w[g].cols;
+    J.out = out[g];
+    J.wg0 = wg;
+    wg += out_dtype == LSN_OUT_BF16_T ? (w[g].cols / 64) * ((w[g].rows + 511) / 512) : w[g].rows * w[g].cols / 8192;
+  }
+  const dim3 grid((unsigned)wg);
+  if (out_dtype == LSN_OUT_BF16_T)
+    hipLaunchKernelGGL(k_dequant_t, grid, dim3(256), 0, s, jobs, kernel_table());
+  else if (out_dtype == LSN_OUT_BF16)
+    hipLaunchKernelGGL(k_dequant<LSN_OUT_BF16>, grid, dim3(256), 0, s, jobs, kernel_table());
   else
-    hipLaunchKernelGGL(k_dequant<LSN_OUT_F32>, grid, dim3(256), 0, s, codes, w.qabsmax, w.absmax2,
-                       w.mean, out, kernel_table());
+    hipLaunchKernelGGL(k_dequant<LSN_OUT_F32>, grid, dim3(256), 0, s, jobs, kernel_table());
   return check_hip(hipGetLastError(), "k_dequant launch");
 }
 

@@ -30,7 +30,7 @@ FAULT_STALE_REFETCH, FAULT_WRONG_SLOT = 1 << 8, 1 << 9
 
 EXPORTS = (
     "lsn_last_error", "lsn_abi_version", "lsn_nf4_codebook", "nf4_pack_ws_bytes", "nf4_pack",
-    "nf4_dequant", "lora_down", "lora_linear_ws_bytes", "lora_linear_fwd", "lora_linear_fwd_group",
+    "nf4_dequant", "nf4_dequant_batch", "lora_down", "lora_linear_ws_bytes", "lora_linear_fwd", "lora_linear_fwd_group",
     "lora_linear_bwd",
     "layer_pool_create", "layer_pool_register", "layer_pool_prefetch", "layer_pool_acquire",
     "layer_pool_release", "layer_pool_stats", "layer_pool_audit", "layer_pool_destroy",
@@ -87,6 +87,7 @@ def load():
         "nf4_pack_ws_bytes": (sz, [i64, i64]),
         "nf4_pack": (i32, [vp, i64, i64, vp, vp, vp, vp, vp, sz, vp]),
         "nf4_dequant": (i32, [ctypes.POINTER(NF4Desc), vp, i32, vp]),
+        "nf4_dequant_batch": (i32, [i32, ctypes.POINTER(NF4Desc), ctypes.POINTER(vp), i32, vp]),
         "lora_down": (i32, [i64, i64, vp, i32, ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(vp), vp]),
         "lora_linear_ws_bytes": (sz, [i64, i64, i64, i64]),
         "lora_linear_fwd": (i32, [ctypes.POINTER(LoraLinearDesc), i32, vp, vp, vp, vp, sz, vp]),
@@ -202,6 +203,15 @@ def nf4_dequant(w: NF4Tensor, out_dtype: str = "bf16", out=None, stream=None):
     d = w.desc()
     check(load().nf4_dequant(ctypes.byref(d), _ptr(out), code, _stream_handle(stream)))
     return out
+
+
+def nf4_dequant_batch(descs, outs, out_dtype: str = "bf16", stream=None) -> None:
+    """nf4_dequant of several NF4 tensors (NF4Desc list) into caller-allocated outputs, one launch."""
+    code = {"bf16": OUT_BF16, "f32": OUT_F32, "bf16_t": OUT_BF16_T}[out_dtype]
+    n = len(descs)
+    arr = (NF4Desc * n)(*descs)
+    ptrs = (ctypes.c_void_p * n)(*[o if isinstance(o, int) else _ptr(o) for o in outs])
+    check(load().nf4_dequant_batch(n, arr, ptrs, code, _stream_handle(stream)))
 
 
 def weight_desc(W, transposed: bool = False) -> WeightDesc:

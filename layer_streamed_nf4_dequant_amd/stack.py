@@ -31,7 +31,6 @@ input gradients and the LoRA gradients below it.
 
 from __future__ import annotations
 
-import ctypes
 from dataclasses import dataclass
 
 import numpy as np
@@ -209,13 +208,10 @@ class Stack:
     def _stage(self, base: int, l: int, s, transposed: bool = False):
         """Dequantise every projection of the layer image at `base` into the staging buffers
         (and into the transposed ones too, for the backward visit)."""
-        for j in range(len(self.layout)):
-            d = self._nf4_desc(base, l, j)
-            lib.check(lib.load().nf4_dequant(ctypes.byref(d), self.w_stage[j].data_ptr(), lib.OUT_BF16,
-                                             s.cuda_stream))
-            if transposed:
-                lib.check(lib.load().nf4_dequant(ctypes.byref(d), self.w_stage_t[j].data_ptr(), lib.OUT_BF16_T,
-                                                 s.cuda_stream))
+        descs = [self._nf4_desc(base, l, j) for j in range(len(self.layout))]
+        lib.nf4_dequant_batch(descs, self.w_stage, "bf16", stream=s)
+        if transposed:
+            lib.nf4_dequant_batch(descs, self.w_stage_t, "bf16_t", stream=s)
 
     def _desc(self, base: int, l: int, j: int, backward: bool = False) -> lib.LoraLinearDesc:
         p, cfg = self.layout[j], self.cfg
@@ -294,10 +290,11 @@ class Stack:
                 self._wvec = torch.arange(1, n + 1, device=v.device, dtype=torch.int64)
             self.checks[(tag, l, j)] = (v.to(torch.int64) * self._wvec[:n]).sum()
 
-    def step(self, mode: str = "streamed", gemm_events=None) -> float:
+    def step(self, mode: str = "streamed", gemm_events=None, dequant_events=None) -> float:
         """One training step of the projection stack; returns its time in ms (compute stream).
         gemm_events: optional list; (projections, start, end) HIP events around every forward
-        GEMM launch (one per group of projections sharing an input) are appended to it."""
+        GEMM launch (one per group of projections sharing an input) are appended to it.
+        dequant_events: optional list; (transposed, start, end) around every visit's staging."""
         torch = self.torch
         s = self.compute
         sh = s.cuda_stream
@@ -318,7 +315,7 @@ class Stack:
                 else:
                     base = self.slots[l % len(self.slots)].data_ptr()
                 if self.dequant == "staged":
-                    self._stage(base, l, s)
+                    self._timed(dequant_events, False, s, lambda: self._stage(base, l, s))
                 self._forward_layer(base, l, self.Y, s, gemm_events)
                 if self.record:
                     self._record("fwd", l, self.Y)
@@ -334,8 +331,8 @@ class Stack:
                     base = self.resident[l].data_ptr()
                 else:
                     base = self.slots[l % len(self.slots)].data_ptr()
-                if self.dequant == "staged":
-                    self._stage(base, l, s, transposed=True)              # re-dequantised per visit
+                if self.dequant == "staged":                              # re-dequantised per visit
+                    self._timed(dequant_events, True, s, lambda: self._stage(base, l, s, transposed=True))
                 self._forward_layer(base, l, self.Yre, s, gemm_events)   # recompute
                 self._backward_layer(base, l, s)
                 if self.record:
@@ -346,6 +343,28 @@ class Stack:
             end.record(s)
         end.synchronize()
         return start.elapsed_time(end)
+
+    def _timed(self, events, tag, s, fn):
+        if events is None:
+            return fn()
+        e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        fn()
+        e1.record(s)
+        events.append((tag, e0, e1))
+
+    def h2d_rate(self, reps: int = 4) -> float:
+        """Host-to-device bandwidth (GB/s) of one layer image into a slot on the copy stream."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.copy_stream):
+            e0.record(self.copy_stream)
+            for i in range(reps):
+                self.slots[i % len(self.slots)].copy_(self.host_images[i % self.L], non_blocking=True)
+            e1.record(self.copy_stream)
+        e1.synchronize()
+        return reps * self.image_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
     def grads(self):
         return self.dA, self.dB

@@ -115,6 +115,33 @@ def test_transposed_dequant_needs_rows_multiple_of_8(gpu):
     assert e.value.status == lib.LSN_E_ARG
 
 
+@pytest.mark.parametrize("layout", ["bf16", "f32", "bf16_t"])
+def test_batched_dequant_equals_oracle_per_tensor(gpu, layout):
+    """One launch over tensors of different shapes (a small layer's projections): every output
+    equals the oracle bit for bit, in every layout."""
+    import torch
+    shapes = [(896, 896), (128, 896), (128, 896), (896, 896), (4864, 896), (4864, 896), (896, 4864)]
+    print(f"case: batched dequant {layout}", flush=True)
+    ps = [nf4.pack(inputs.host_normal(sh, 0.02, 0, "nf4-batch", i)) for i, sh in enumerate(shapes)]
+    devs = [_oracle_packed_on_device(p, torch) for p in ps]
+    dt = torch.float32 if layout == "f32" else torch.bfloat16
+    outs = [torch.empty((p["cols"], p["rows"]) if layout == "bf16_t" else (p["rows"], p["cols"]), dtype=dt,
+                        device="cuda") for p in ps]
+    lib.nf4_dequant_batch([d.desc() for d in devs], outs, layout)
+    torch.cuda.synchronize()
+    for p, o in zip(ps, outs):
+        want32 = nf4.dequant_f32(p)
+        if layout == "f32":
+            np.testing.assert_array_equal(o.cpu().numpy().view(np.uint32), want32.view(np.uint32))
+        else:
+            got = o.view(torch.int16).cpu().numpy().view(np.uint16)
+            want = nf4.bf16_rne(want32)
+            np.testing.assert_array_equal(got, want.T if layout == "bf16_t" else want)
+    with pytest.raises(lib.LsnError) as e:          # two outputs overlapping
+        lib.nf4_dequant_batch([devs[0].desc(), devs[3].desc()], [outs[0], outs[0]], layout)
+    assert e.value.status == lib.LSN_E_ARG
+
+
 def test_pack_rejects_non_finite(gpu):
     import torch
     w = torch.zeros((256, 64), dtype=torch.float32, device="cuda")
