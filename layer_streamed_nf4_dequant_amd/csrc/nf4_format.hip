@@ -201,8 +201,11 @@ __global__ __launch_bounds__(256) void k_dequant(DqJobs jobs, Nf4KernelTable tab
 // values are bit-identical. Workgroup tile: 512 rows n x 64 columns k (one 64-weight block per
 // row). Thread t decodes rows n0 + 8 (t % 64) .. +7 at columns k0 + 16 (t / 64) .. +15 (8 code
 // bytes per row), then stores each of its 16 columns as 8 consecutive n (16 bytes), so a wave's
-// store covers 1 KB of one out row (long write runs keep the HBM pages open). Tiles walk k
-// fastest, so the workgroups that share a 128-byte line of codes run side by side.
+// store covers 1 KB of one out row (long write runs keep the HBM pages open).
+// A 128-byte line of codes spans 4 k-tiles. Tiles walk k fastest, and each job's workgroups
+// start at a multiple of 32 so that the permutation below hands the 4 tiles of a line to 4
+// workgroups on the same XCD (workgroup b runs on XCD b % 8): the line is fetched from HBM once
+// into that XCD's L2 instead of once per XCD.
 // Requires rows % 8 == 0 (checked by the caller); cols % 64 == 0 by the format.
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_dequant_t(DqJobs jobs, Nf4KernelTable tab) {
@@ -212,8 +215,10 @@ __global__ __launch_bounds__(256) void k_dequant_t(DqJobs jobs, Nf4KernelTable t
   if (t < 16) sq[t] = tab.q[t];
   if (t < 255) scode8[t] = int8_level(t - 127);
   const DqJob &J = jobs.job[find_job(jobs, blockIdx.x)];
-  const int64_t tile = (int64_t)blockIdx.x - J.wg0;
+  const int64_t b = (int64_t)blockIdx.x - J.wg0;          // J.wg0 % 32 == 0, so b % 8 is the XCD
+  const int64_t tile = (b & ~(int64_t)31) + 4 * (b & 7) + ((b >> 3) & 3);
   const int64_t kt = J.cols / 64;
+  if (tile >= kt * ((J.rows + 511) / 512)) return;         // padding up to a multiple of 32
   const int64_t rows = J.rows, cols = J.cols;
   const int64_t k = (tile % kt) * 64 + 16 * (t >> 6);
   const int64_t n = (tile / kt) * 512 + 8 * (t & 63);
@@ -286,7 +291,10 @@ lsn_status launch_dequant(int n, const lsn_nf4 *w, void *const *out, int out_dty
     J.cols = w[g].cols;
     J.out = out[g];
     J.wg0 = wg;
-    wg += out_dtype == LSN_OUT_BF16_T ? (w[g].cols / 64) * ((w[g].rows + 511) / 512) : w[g].rows * w[g].cols / 8192;
+    if (out_dtype == LSN_OUT_BF16_T)
+      wg += ((w[g].cols / 64) * ((w[g].rows + 511) / 512) + 31) / 32 * 32;   // whole groups of 32 (see k_dequant_t)
+    else
+      wg += w[g].rows * w[g].cols / 8192;
   }
   const dim3 grid((unsigned)wg);
   if (out_dtype == LSN_OUT_BF16_T)
