@@ -28,6 +28,8 @@
 // Determinism: the reduction order is fixed by the tiling (which depends only on shapes);
 // there are no atomics.
 
+#include <type_traits>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -442,67 +444,70 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs a) {
 
 // =============================================================================================
 // Direct-load NT GEMM (both operands bf16 and K-contiguous): out_seg = act W_seg^T (+ LoRA term)
-// for up to 4 output segments that share the activation (e.g. q, k and v of a layer read the
-// same input). K-steps of 32 stream through a 4-stage LDS ring; buffer_load...lds fills a stage
-// three steps ahead, and a step only waits for its own stage (the oldest loads in flight), so
-// up to three K-steps of memory latency are hidden behind the matrix cores.
-// LDS rows are 64 B (32 bf16, four 16-byte chunks); chunk p of row r sits at slot
-// 4 r + (p ^ ((r >> 2) & 3)): with gfx950's 64 four-byte banks a 16-lane group of a fragment
-// read (16 consecutive rows, one logical chunk) then covers all 64 banks once, and the direct
-// writes are contiguous 1 KB segments.
+// for up to kMaxSegs output segments that share the activation (e.g. q, k, v, gate and up of a
+// layer read the same input). K-steps of 64 stream through two LDS stages (64 KB each:
+// 256 rows x 128 B per operand); buffer_load...lds fills the next stage while the matrix cores
+// work on the current one.
+// Each direct load moves 8 whole rows of 128 B, i.e. whole 128-byte lines: the CU's address
+// unit processes a load per cache line, so half-line segments (a 32-wide K-step) would double
+// its work per byte and its queue would stall the waves.
+// LDS rows are 128 B (64 bf16, eight 16-byte chunks); chunk p of row r sits at slot
+// 8 r + (p ^ ((r ^ (r >> 3)) & 7)): a 16-lane group of a fragment read (16 consecutive rows,
+// one logical chunk) then covers all 64 four-byte banks once, and the direct writes are
+// contiguous 1 KB segments.
 // =============================================================================================
-constexpr int DBK = 32;
-constexpr int DSTAGES = 5;
-constexpr int DTILE = 256 * DBK * 2;           // 16 KB: one operand, one stage
+constexpr int DBK = 64;
+constexpr int DTILE = 256 * DBK * 2;           // 32 KB: one operand, one stage
+constexpr int kEpiPitch = 256 * 2 + 16;        // bytes per LDS row of the bf16 output tile
 
-__device__ __forceinline__ int dlds_off(int row, int chunk) { return (row * 4 + (chunk ^ ((row >> 2) & 3))) * 16; }
+__device__ __forceinline__ int dlds_off(int row, int chunk) {
+  return (row * 8 + (chunk ^ ((row ^ (row >> 3)) & 7))) * 16;
+}
 
-struct DirectRows4 {
-  uint32_t voff[4];
+struct DirectRows8 {
+  uint32_t voff[8];
 };
 
-// wave w fills LDS segments 4w .. 4w+3 (1 KB = 16 rows each) of a 256 x 32 tile
-__device__ __forceinline__ void make_direct_rows4(DirectRows4 &d, int64_t rows, int64_t ld, int64_t r0, int wave,
+// wave w fills the LDS segments 8w .. 8w+7 (1 KB = 8 rows each) of a 256 x 64 tile
+__device__ __forceinline__ void make_direct_rows8(DirectRows8 &d, int64_t rows, int64_t ld, int64_t r0, int wave,
                                                   int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int sg = wave * 4 + i;
-    const int row = sg * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 2) & 3);
+  for (int i = 0; i < 8; ++i) {
+    const int row = (wave * 8 + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
     const int64_t grow = min(r0 + row, rows - 1);     // clamped rows feed only unstored outputs
     d.voff[i] = (uint32_t)((grow * ld + 8 * c) * 2);
   }
 }
 
-__device__ __forceinline__ void issue_direct1(char *lds_tile, __amdgpu_buffer_rsrc_t rsrc, const DirectRows4 &d,
+__device__ __forceinline__ void issue_direct1(char *lds_tile, __amdgpu_buffer_rsrc_t rsrc, const DirectRows8 &d,
                                               uint32_t k_bytes, int wave, int i) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(lds_tile + (wave * 4 + i) * 1024), 16, d.voff[i],
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(lds_tile + (wave * 8 + i) * 1024), 16, d.voff[i],
                                            k_bytes, 0, 0);
 }
-__device__ __forceinline__ void issue_direct4(char *lds_tile, __amdgpu_buffer_rsrc_t rsrc, const DirectRows4 &d,
-                                              uint32_t k_bytes, int wave) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) issue_direct1(lds_tile, rsrc, d, k_bytes, wave, i);
-}
 
-// each wave issues 8 direct loads per stage; waiting until the loads of the DSTAGES - 2 newest
-// stages are the only ones outstanding means the oldest stage in flight has landed
 // gfx9 s_waitcnt immediate: vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
 template <int N>
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14)); }
 
-// Workgroup barrier for the direct-load ring. __syncthreads() would wait for every outstanding
-// vector-memory operation (the direct-to-LDS loads count as LDS writes), draining the three
-// stages in flight. Here each wave first waits for its own loads of the next stage (vmcnt) and
-// for its own LDS reads (lgkmcnt), then meets the others; the scheduling barriers keep the
-// compiler from moving LDS accesses across.
+// Workgroup barrier of the double buffer: each wave waits for its own direct loads (the stage
+// about to be read) and its own LDS reads (of the stage about to be refilled), then meets the
+// others. __syncthreads() is not used because its memory fence is not needed here; the
+// scheduling barriers keep the compiler from moving LDS accesses across.
 __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_sched_barrier(0);
-  wait_vm<8 * (DSTAGES - 2)>();
+  wait_vm<0>();
   __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 }
+
+// The 16 direct loads of a step (8 per operand) are spread over the first kLoadSpread
+// sub-steps of the step before it, at most one per MFMA pair, so that the address unit is never
+// asked for more than its ~64 B/clock while the MFMAs keep issuing.
+constexpr int kLoadSpread = 2;
+__device__ constexpr bool load_at(int g) { return kLoadSpread == 2 ? g < 16 : (g < 24 && g % 3 != 1); }
+__device__ constexpr int load_index(int g) { return kLoadSpread == 2 ? g : g - (g + 1) / 3; }
 
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD b % 8) and each
 // XCD has its own L2. Tile order: groups of GROUP_M m-tiles walk across all n-tiles, m fastest,
@@ -528,8 +533,8 @@ __device__ __forceinline__ void tile_coords(int64_t b, int64_t ntiles, int64_t t
 template <int EPI>
 __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char *lds_a = smem;                               // DSTAGES stages
-  char *lds_b = smem + DSTAGES * DTILE;             // DSTAGES stages
+  char *lds_a = smem;                               // 2 stages
+  char *lds_b = smem + 2 * DTILE;                   // 2 stages
   const int t = threadIdx.x;
   const int lane = t & 63;
   // the wave index is uniform: keep it in a scalar register so that the LDS destinations of the
@@ -557,32 +562,53 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  const int nk = (int)(a.K / DBK);
+  const int k_last = nk - 1;
+  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.act, a.M * a.K * 2);
+  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(sg.w, sg.N * a.K * 2);
+  DirectRows8 da, db;
+  make_direct_rows8(da, a.M, a.K, m0, wave, lane);
+  make_direct_rows8(db, sg.N, a.K, n0, wave, lane);
+
   // ---- LoRA prologue: acc = s * (B_seg . U_seg^T) over r (B_seg [N][r], U_seg [M][r]) ----
+  // Its fragment loads go first, then the ring's first stages, so that both sets of loads are in
+  // flight together; the MFMAs below wait only for the (older) LoRA loads.
+  bf16x8 la[2][4], lb[2][4];
   if (a.adapters) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int j0 = 16 * h;
-      if (j0 >= a.r) break;
-      const int jl = j0 + 8 * (lane >> 5);
-      bf16x8 fa[4], fb[4];
+      const int jl = 16 * h + 8 * (lane >> 5);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + wm * 128 + 32 * i + (lane & 31);
         u32x4_t v = {0, 0, 0, 0};
         if (m < a.M && jl < a.r) v = *reinterpret_cast<const u32x4_t *>(sg.lr_act + m * a.r + jl);
-        fa[i] = as_bf16x8(v);
+        la[h][i] = as_bf16x8(v);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t n = n0 + wn * 128 + 32 * j + (lane & 31);
         u32x4_t v = {0, 0, 0, 0};
         if (n < sg.N && jl < a.r) v = *reinterpret_cast<const u32x4_t *>(sg.lr_w + n * a.r + jl);
-        fb[j] = as_bf16x8(v);
+        lb[h][j] = as_bf16x8(v);
       }
+    }
+  }
+  // stage 0 <- step 0
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    issue_direct1(lds_a, rs_a, da, 0, wave, i);
+    issue_direct1(lds_b, rs_b, db, 0, wave, i);
+  }
+  if (a.adapters) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (16 * h >= a.r) break;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lb[h][j], la[h][i], acc[i][j], 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -592,30 +618,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
         for (int e = 0; e < 16; ++e) acc[i][j][e] = __fmul_rn(a.scale, acc[i][j][e]);
   }
 
-  const int nk = (int)(a.K / DBK);
-  const int k_last = nk - 1;
-  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.act, a.M * a.K * 2);
-  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(sg.w, sg.N * a.K * 2);
-  DirectRows4 da, db;
-  make_direct_rows4(da, a.M, a.K, m0, wave, lane);
-  make_direct_rows4(db, sg.N, a.K, n0, wave, lane);
-
-  // fragments of one 16-wide sub-step: 4 activation rows-blocks and 4 weight row-blocks
-  // read order fa0, fb0..fb3, fa1..fa3: the first MFMAs of the batch that consumes them, which
-  // walk j fastest, find their operands earliest
-  auto load_frags = [&](int stage, int s2, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
-    const char *la = lds_a + stage * DTILE;
-    const char *lb = lds_b + stage * DTILE;
-    const int chunk = 2 * s2 + (lane >> 5);
-    fa[0] = *reinterpret_cast<const bf16x8 *>(la + dlds_off(wm * 128 + (lane & 31), chunk));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      fb[j] = *reinterpret_cast<const bf16x8 *>(lb + dlds_off(wn * 128 + 32 * j + (lane & 31), chunk));
-#pragma unroll
-    for (int i = 1; i < 4; ++i)
-      fa[i] = *reinterpret_cast<const bf16x8 *>(la + dlds_off(wm * 128 + 32 * i + (lane & 31), chunk));
-  };
-  // fragment q of a sub-step in the same order: 0 -> fa0, 1..4 -> fb0..fb3, 5..7 -> fa1..fa3
+  // fragment q of sub-step s2 (16 K-columns) of a stage, in consumption order: 0 -> fa0,
+  // 1..4 -> fb0..fb3, 5..7 -> fa1..fa3 (the first MFMAs of a batch walk j fastest)
   auto read_frag = [&](int stage, int s2, int q, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
     const int chunk = 2 * s2 + (lane >> 5);
     if (q == 0 || q >= 5) {
@@ -626,61 +630,86 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       fb[j] = *reinterpret_cast<const bf16x8 *>(lds_b + stage * DTILE + dlds_off(wn * 128 + 32 * j + (lane & 31), chunk));
     }
   };
-  auto mfmas = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-  };
-
-  // prologue: stages 0 .. DSTAGES-2 in flight (steps past the end re-load the last step into
-  // stages that are never read); stage 0 visible; fragments of step 0, sub-step 0 loaded
-#pragma unroll
-  for (int p = 0; p < DSTAGES - 1; ++p) {
-    const uint32_t kb = (uint32_t)min(p, k_last) * DBK * 2;
-    issue_direct4(lds_a + p * DTILE, rs_a, da, kb, wave);
-    issue_direct4(lds_b + p * DTILE, rs_b, db, kb, wave);
-  }
-  ring_barrier();
-  bf16x8 ca[4], cb[4], na[4], nb[4];
-  load_frags(0, 0, ca, cb);
-  // Step kt: stage kt is visible and its sub-step 0 fragments are in (ca, cb).
-  //  1. load sub-step 1 of step kt; run sub-step 0, with the refill of stage kt-1 (read by every
-  //     wave before the previous barrier) with step kt+DSTAGES-1 spread over its MFMAs, one direct load
-  //     per two MFMAs, so that the loads issue in the matrix core's shadow;
-  //  2. wait for the own loads of step kt+1, barrier (the last sub-step 0 MFMAs keep running);
-  //  3. load sub-step 0 of step kt+1, run sub-step 1 of step kt.
-  int st = 0;                                           // stage of step kt
-  for (int kt = 0; kt < nk; ++kt) {
-    const int nx = st == 0 ? DSTAGES - 1 : st - 1;        // the stage read in step kt-1
-    const uint32_t kb = (uint32_t)min(kt + DSTAGES - 1, k_last) * DBK * 2;
-    // fixed order, one group per scheduling fence: read one sub-step 1 fragment, two MFMAs,
-    // one direct load
+  // One sub-step: its 16 MFMAs on (cA, cB) in pairs; before each pair, one fragment of the
+  // sub-step that follows is read into (nA, nB) from stage `rstage` at K-slice `rs2`, and in the
+  // first sub-steps one direct load of K-step kt+1 goes out to stage `nstage`; each group is
+  // fenced so the interleaving holds.
+  auto substep = [&](auto S_, int rstage, int rs2, int nstage, uint32_t kb, bf16x8 (&cA)[4], bf16x8 (&cB)[4],
+                     bf16x8 (&nA)[4], bf16x8 (&nB)[4]) {
+    constexpr int S = decltype(S_)::value;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      read_frag(st, 1, q, na, nb);
+      read_frag(rstage, rs2, q, nA, nB);
       const int i = q >> 1, j0 = 2 * (q & 1);
-      acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[j0], ca[i], acc[i][j0], 0, 0, 0);
-      acc[i][j0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[j0 + 1], ca[i], acc[i][j0 + 1], 0, 0, 0);
-      if (q < 4) issue_direct1(lds_a + nx * DTILE, rs_a, da, kb, wave, q);
-      else issue_direct1(lds_b + nx * DTILE, rs_b, db, kb, wave, q - 4);
+      acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cB[j0], cA[i], acc[i][j0], 0, 0, 0);
+      acc[i][j0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cB[j0 + 1], cA[i], acc[i][j0 + 1], 0, 0, 0);
+      const int g = 8 * S + q;
+      if (load_at(g)) {
+        const int li = load_index(g);
+        if (li < 8) issue_direct1(lds_a + nstage * DTILE, rs_a, da, kb, wave, li);
+        else issue_direct1(lds_b + nstage * DTILE, rs_b, db, kb, wave, li - 8);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    ring_barrier();
-    st = st == DSTAGES - 1 ? 0 : st + 1;
-    load_frags(st, 0, ca, cb);
-    mfmas(na, nb);
+  };
+
+  // step 0 visible; its first fragments loaded
+  ring_barrier();
+  bf16x8 ca[4], cb[4], na[4], nb[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int q = 0; q < 8; ++q) read_frag(0, 0, q, ca, cb);
+  // Step kt (stage st, its sub-step 0 fragments in (ca, cb)):
+  //   sub-steps 0 and 1 send the direct loads of step kt+1 to stage st^1 (no wave reads it any
+  //   more: its last reads came before the previous barrier);
+  //   after sub-step 2 (whose MFMAs read fragments loaded before), each wave waits for its own
+  //   loads and LDS reads, and all meet: step kt+1 is then visible, so sub-step 3 can read the
+  //   next step's first fragments while its MFMAs run, and the matrix cores never wait on LDS
+  //   after the barrier. The last step re-loads itself into the unused stage (no branch).
+  int st = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int nx = st ^ 1;
+    const uint32_t kb = (uint32_t)min(kt + 1, k_last) * DBK * 2;
+    substep(std::integral_constant<int, 0>{}, st, 1, nx, kb, ca, cb, na, nb);
+    substep(std::integral_constant<int, 1>{}, st, 2, nx, kb, na, nb, ca, cb);
+    substep(std::integral_constant<int, 2>{}, st, 3, nx, kb, ca, cb, na, nb);
+    ring_barrier();
+    substep(std::integral_constant<int, 3>{}, nx, 0, nx, kb, na, nb, ca, cb);
+    st = nx;
   }
   wait_vm_all();
 
   // ---- epilogue: lane holds row m = 32 i + lane%32, columns 32 j + 8 g + 4 (lane/32) .. +3 ----
+  if constexpr (EPI == EPI_BF16) {
+    // through LDS (free once every wave is past the loop): the 256 x 256 bf16 tile is written
+    // with 8-byte stores at a 528-byte row pitch (2-way bank conflicts at most), then read back
+    // as 16-byte row chunks so that every global store is a 16-byte piece of a 512-byte row run
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + 32 * i + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = wn * 128 + 32 * j + 8 * g + 4 * (lane >> 5);
+          uint2 o;
+          o.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+          o.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          *reinterpret_cast<uint2 *>(smem + r * kEpiPitch + c * 2) = o;
+        }
+    }
+    __syncthreads();
+    const int chunk = t & 31;
+    const int64_t n = n0 + 8 * chunk;
+#pragma unroll 4
+    for (int p = 0; p < BM / (NT / 32); ++p) {
+      const int r = p * (NT / 32) + (t >> 5);
+      const int64_t m = m0 + r;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + chunk * 16);
+      if (m < a.M && n < sg.N) *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(sg.out) + m * sg.N + n) = v;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + wm * 128 + 32 * i + (lane & 31);
@@ -692,12 +721,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
         if (m < a.M && n < sg.N) {
           const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1], v2 = acc[i][j][4 * g + 2],
                       v3 = acc[i][j][4 * g + 3];
-          if constexpr (EPI == EPI_BF16) {
-            uint2 o;
-            o.x = pack_bf16x2(v0, v1);
-            o.y = pack_bf16x2(v2, v3);
-            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(sg.out) + m * sg.N + n) = o;
-          } else {
+          {
             floatx4_t *o = reinterpret_cast<floatx4_t *>(reinterpret_cast<float *>(sg.out) + m * sg.N + n);
             floatx4_t cur = *o;
             cur[0] = __fadd_rn(cur[0], v0);
@@ -712,7 +736,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   }
 }
 
-constexpr size_t kDirectSmemBytes = 2 * DSTAGES * DTILE;
+constexpr size_t kDirectSmemBytes = 256 * kEpiPitch > 4 * DTILE ? 256 * kEpiPitch : 4 * DTILE;
+static_assert(256 * kEpiPitch <= kDirectSmemBytes, "the epilogue tile must fit in the ring's LDS");
 
 template <int EPI>
 lsn_status launch_direct_one(const DirectArgs &a, hipStream_t s) {
