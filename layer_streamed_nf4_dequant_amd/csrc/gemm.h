@@ -54,6 +54,7 @@ struct DirectArgs {
   int r;
   float scale;
   int adapters;
+  int scale_pow2;        // set by launch_gemm_direct
 };
 lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s);
 

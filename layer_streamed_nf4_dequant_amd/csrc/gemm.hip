@@ -28,6 +28,7 @@
 // Determinism: the reduction order is fixed by the tiling (which depends only on shapes);
 // there are no atomics.
 
+#include <cmath>
 #include <type_traits>
 
 #include "common.h"
@@ -570,52 +571,58 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   make_direct_rows8(da, a.M, a.K, m0, wave, lane);
   make_direct_rows8(db, sg.N, a.K, n0, wave, lane);
 
+  // stage 0 <- step 0 (first, so that its latency overlaps the LoRA prologue)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    issue_direct1(lds_a, rs_a, da, 0, wave, i);
+    issue_direct1(lds_b, rs_b, db, 0, wave, i);
+  }
   // ---- LoRA prologue: acc = s * (B_seg . U_seg^T) over r (B_seg [N][r], U_seg [M][r]) ----
-  // Its fragment loads go first, then the ring's first stages, so that both sets of loads are in
-  // flight together; the MFMAs below wait only for the (older) LoRA loads.
-  bf16x8 la[2][4], lb[2][4];
   if (a.adapters) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      if (16 * h >= a.r) break;
       const int jl = 16 * h + 8 * (lane >> 5);
+      bf16x8 la[4], lb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + wm * 128 + 32 * i + (lane & 31);
         u32x4_t v = {0, 0, 0, 0};
         if (m < a.M && jl < a.r) v = *reinterpret_cast<const u32x4_t *>(sg.lr_act + m * a.r + jl);
-        la[h][i] = as_bf16x8(v);
+        la[i] = as_bf16x8(v);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t n = n0 + wn * 128 + 32 * j + (lane & 31);
         u32x4_t v = {0, 0, 0, 0};
         if (n < sg.N && jl < a.r) v = *reinterpret_cast<const u32x4_t *>(sg.lr_w + n * a.r + jl);
-        lb[h][j] = as_bf16x8(v);
+        lb[j] = as_bf16x8(v);
       }
-    }
-  }
-  // stage 0 <- step 0
+      if (a.scale_pow2) {
+        // s = 2^e: scaling the bf16 U fragments is exact (as are all the fp32 partial sums of
+        // the products), so the result is bit-identical to scaling the fp32 sum afterwards
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    issue_direct1(lds_a, rs_a, da, 0, wave, i);
-    issue_direct1(lds_b, rs_b, db, 0, wave, i);
-  }
-  if (a.adapters) {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (16 * h >= a.r) break;
+          for (int e = 0; e < 8; ++e) la[i][e] = (__bf16)((float)la[i][e] * a.scale);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lb[h][j], la[h][i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lb[j], la[i], acc[i][j], 0, 0, 0);
     }
+    if (!a.scale_pow2) {
+      // one accumulator block at a time (the fences keep the compiler from moving all 256
+      // accumulators into vector registers at once)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = __fmul_rn(a.scale, acc[i][j][e]);
+          for (int e = 0; e < 16; ++e) acc[i][j][e] = __fmul_rn(a.scale, acc[i][j][e]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
   }
 
   // fragment q of sub-step s2 (16 K-columns) of a stage, in consumption order: 0 -> fa0,
@@ -774,6 +781,12 @@ lsn_status launch_one(const GemmArgs &a, hipStream_t s) {
 }  // namespace
 
 lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s) {
+  // a power-of-two scale s >= 1 (s = alpha / r with alpha and r powers of two, the usual case)
+  // is applied exactly to the bf16 U fragments instead of to the fp32 accumulators
+  int e2 = 0;
+  // (s >= 1, so no scaled bf16 value can lose bits by turning subnormal; exact unless s * U
+  // overflows)
+  a.scale_pow2 = std::isfinite(a.scale) && a.scale >= 1.0f && std::frexp(a.scale, &e2) == 0.5f && e2 <= 64;
   int64_t t0 = 0;
   for (int q = 0; q < a.nseg; ++q) {
     a.seg[q].ntile0 = t0;
