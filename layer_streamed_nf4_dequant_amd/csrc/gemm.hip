@@ -503,13 +503,6 @@ __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// The 16 direct loads of a step (8 per operand) are spread over the first kLoadSpread
-// sub-steps of the step before it, at most one per MFMA pair, so that the address unit is never
-// asked for more than its ~64 B/clock while the MFMAs keep issuing.
-constexpr int kLoadSpread = 2;
-__device__ constexpr bool load_at(int g) { return kLoadSpread == 2 ? g < 16 : (g < 24 && g % 3 != 1); }
-__device__ constexpr int load_index(int g) { return kLoadSpread == 2 ? g : g - (g + 1) / 3; }
-
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD b % 8) and each
 // XCD has its own L2. Tile order: groups of GROUP_M m-tiles walk across all n-tiles, m fastest,
 // and each XCD takes a contiguous run of that order, so the ~32 tiles an XCD holds at once span
@@ -638,49 +631,52 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     }
   };
   // One sub-step: its 16 MFMAs on (cA, cB) in pairs; before each pair, one fragment of the
-  // sub-step that follows is read into (nA, nB) from stage `rstage` at K-slice `rs2`, and in the
-  // first sub-steps one direct load of K-step kt+1 goes out to stage `nstage`; each group is
-  // fenced so the interleaving holds.
-  auto substep = [&](auto S_, int rstage, int rs2, int nstage, uint32_t kb, bf16x8 (&cA)[4], bf16x8 (&cB)[4],
+  // sub-step that follows is read into (nA, nB) from stage `rstage` at K-slice `rs2`, and, when
+  // `lhalf` >= 0, one of the 8 direct loads of half `lhalf` (0: operand A, 1: operand B) of a
+  // K-step goes out to stage `lstage`; each group is fenced so the interleaving holds.
+  auto substep = [&](int rstage, int rs2, int lhalf, int lstage, uint32_t kb, bf16x8 (&cA)[4], bf16x8 (&cB)[4],
                      bf16x8 (&nA)[4], bf16x8 (&nB)[4]) {
-    constexpr int S = decltype(S_)::value;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       read_frag(rstage, rs2, q, nA, nB);
       const int i = q >> 1, j0 = 2 * (q & 1);
       acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cB[j0], cA[i], acc[i][j0], 0, 0, 0);
       acc[i][j0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cB[j0 + 1], cA[i], acc[i][j0 + 1], 0, 0, 0);
-      const int g = 8 * S + q;
-      if (load_at(g)) {
-        const int li = load_index(g);
-        if (li < 8) issue_direct1(lds_a + nstage * DTILE, rs_a, da, kb, wave, li);
-        else issue_direct1(lds_b + nstage * DTILE, rs_b, db, kb, wave, li - 8);
-      }
+      if (lhalf == 0) issue_direct1(lds_a + lstage * DTILE, rs_a, da, kb, wave, q);
+      if (lhalf == 1) issue_direct1(lds_b + lstage * DTILE, rs_b, db, kb, wave, q);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // step 0 visible; its first fragments loaded
-  ring_barrier();
+  // operand A of step 1 to stage 1 (free); then wait for step 0 only, and read its first fragments
+#pragma unroll
+  for (int i = 0; i < 8; ++i) issue_direct1(lds_a + DTILE, rs_a, da, (uint32_t)min(1, k_last) * DBK * 2, wave, i);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm<8>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   bf16x8 ca[4], cb[4], na[4], nb[4];
 #pragma unroll
   for (int q = 0; q < 8; ++q) read_frag(0, 0, q, ca, cb);
-  // Step kt (stage st, its sub-step 0 fragments in (ca, cb)):
-  //   sub-steps 0 and 1 send the direct loads of step kt+1 to stage st^1 (no wave reads it any
-  //   more: its last reads came before the previous barrier);
-  //   after sub-step 2 (whose MFMAs read fragments loaded before), each wave waits for its own
-  //   loads and LDS reads, and all meet: step kt+1 is then visible, so sub-step 3 can read the
-  //   next step's first fragments while its MFMAs run, and the matrix cores never wait on LDS
-  //   after the barrier. The last step re-loads itself into the unused stage (no branch).
+  // Step kt (stage st, its sub-step 0 fragments in (ca, cb); operand A of step kt+1 already on
+  // its way to stage st^1):
+  //   sub-step 0 sends operand B of step kt+1 to stage st^1;
+  //   after sub-step 2 each wave waits for its own loads and LDS reads, and all meet: step
+  //   kt+1 is visible, and no wave reads stage st any more;
+  //   sub-step 3 reads the first fragments of step kt+1 while its MFMAs run (the matrix cores
+  //   never wait on LDS after the barrier) and sends operand A of step kt+2 to stage st.
+  // Every load has at least two sub-steps to land. The last steps re-load the last K-step into
+  // stages that are never read again, so the loop needs no branch.
   int st = 0;
   for (int kt = 0; kt < nk; ++kt) {
     const int nx = st ^ 1;
-    const uint32_t kb = (uint32_t)min(kt + 1, k_last) * DBK * 2;
-    substep(std::integral_constant<int, 0>{}, st, 1, nx, kb, ca, cb, na, nb);
-    substep(std::integral_constant<int, 1>{}, st, 2, nx, kb, na, nb, ca, cb);
-    substep(std::integral_constant<int, 2>{}, st, 3, nx, kb, ca, cb, na, nb);
+    const uint32_t kb1 = (uint32_t)min(kt + 1, k_last) * DBK * 2;
+    const uint32_t kb2 = (uint32_t)min(kt + 2, k_last) * DBK * 2;
+    substep(st, 1, 1, nx, kb1, ca, cb, na, nb);
+    substep(st, 2, -1, 0, 0, na, nb, ca, cb);
+    substep(st, 3, -1, 0, 0, ca, cb, na, nb);
     ring_barrier();
-    substep(std::integral_constant<int, 3>{}, nx, 0, nx, kb, na, nb, ca, cb);
+    substep(nx, 0, 0, st, kb2, na, nb, ca, cb);
     st = nx;
   }
   wait_vm_all();
