@@ -667,8 +667,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   //   never wait on LDS after the barrier) and sends operand A of step kt+2 to stage st.
   // Every load has at least two sub-steps to land. The last steps re-load the last K-step into
   // stages that are never read again, so the loop needs no branch.
-  int st = 0;
-  for (int kt = 0; kt < nk; ++kt) {
+  // (unrolled by two so that the stage of each step is a constant)
+  auto step = [&](int kt, int st) {
     const int nx = st ^ 1;
     const uint32_t kb1 = (uint32_t)min(kt + 1, k_last) * DBK * 2;
     const uint32_t kb2 = (uint32_t)min(kt + 2, k_last) * DBK * 2;
@@ -677,7 +677,10 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     substep(st, 3, -1, 0, 0, ca, cb, na, nb);
     ring_barrier();
     substep(nx, 0, 0, st, kb2, na, nb, ca, cb);
-    st = nx;
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, 0);
+    if (kt + 1 < nk) step(kt + 1, 1);
   }
   wait_vm_all();
 
