@@ -35,15 +35,29 @@ PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_direct_llama8b_traffic.md")
+GEMM_SOURCE = os.path.join(ROOT, "layer_streamed_nf4_dequant_amd", "csrc", "gemm.hip")
+
+
 def traffic_from_profiles():
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter summary,
-    if one exists for the current kernel build (null otherwise)."""
-    path = os.path.join(ROOT, "profiles", "gemm_nt_nf4_llama8b_traffic.json")
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter summary
+    (its `traffic_bytes_per_launch:` line), provided the summary was taken on the current kernel
+    source (its `gemm_source_sha256:` line matches); null otherwise."""
+    import hashlib
     try:
-        with open(path) as f:
-            d = json.load(f)
-        return d.get("bytes_per_launch")
-    except (OSError, ValueError):
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+        with open(GEMM_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(line.strip("` ").split(": ", 1) for line in text.splitlines()
+                  if line.strip("` ").startswith(("traffic_bytes_per_launch: ", "gemm_source_sha256: ")))
+    if fields.get("gemm_source_sha256") != sha:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
         return None
 
 
@@ -98,6 +112,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-modes", action="store_true",
                     help="skip the resident and no-H2D comparison timings")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the steps, run one device-to-device copy of MIB MiB (a plain copy kernel of "
+                         "known size, to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -118,6 +135,14 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] setup {time.perf_counter() - t0:.1f} s; image {stack.image_bytes / 1e6:.2f} MB/layer",
           flush=True)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         ms = stack.step(args.mode)
         print(f"[bench] warmup {i}: {ms:.1f} ms", flush=True)
@@ -145,7 +170,7 @@ def main():
     if cfg.base == "nf4" and stack.dequant == "fused":
         kernel = "k_gemm<NT,NF4> (fused NF4 dequant-into-LDS + bf16 MFMA + LoRA prologue)"
     else:
-        kernel = "k_gemm<NT,BF16> (bf16 MFMA + LoRA prologue; W dequantised per visit by k_dequant)"
+        kernel = "k_gemm_direct (bf16 MFMA + LoRA prologue; W dequantised per visit by k_dequant)"
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_from_profiles(),
                 "kernel": kernel, "launches": n_launch,
