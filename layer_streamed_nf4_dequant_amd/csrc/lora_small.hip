@@ -119,12 +119,22 @@ __global__ __launch_bounds__(256) void k_transpose(const uint16_t *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------------------------
-// split-T partial products: partial[c][p][j] = sum_{t in chunk c} Z[t][p] V[t][j].
-// Workgroup = (64 columns p, one chunk of 256 rows t). Both operands are t-major in memory,
-// so each is loaded in 8 x 8 blocks and transposed in registers into LDS as [p][t] and [j][t]
-// (rows padded to 528 B so the 16-row fragment reads hit distinct banks).
+// split-T partial products: partial[c][p][j] = sum over t in chunk c (TN_CHUNK = 256 rows) of
+// Z[t][p] V[t][j]. Workgroup = (256 columns p, one chunk), walked in 4 blocks of 64 rows. Both
+// operands are t-major in memory, so each thread loads an 8 x 8 block (8 rows, 16 bytes each;
+// 32 lanes cover 512 contiguous bytes of a row) and transposes it in registers into LDS as
+// [p][t] rows (128 bytes; 16-byte chunk ch of row w sits at slot ch ^ ((w ^ w >> 3) & 7), which
+// keeps both the transposed writes and the fragment reads free of bank conflicts), V likewise
+// as [j][t]; then each
+// wave runs its 64 columns against V on 16x16x32 MFMAs. The next block's loads are issued
+// before the current block's MFMAs. The t order of the sums (steps of 32 in increasing t) is
+// the same as a single pass over the chunk.
 // ---------------------------------------------------------------------------------------------
-constexpr int TPITCH = 256 * 2 + 16;   // bytes per LDS row of 256 bf16 (+16 B pad)
+constexpr int TN_COLS = 256;          // columns p per workgroup
+constexpr int TN_ROWS = 64;           // rows t per LDS block
+constexpr int TPITCH = TN_ROWS * 2;       // bytes per LDS row of 64 bf16
+
+__device__ __forceinline__ int tn_off(int row, int ch) { return row * TPITCH + 16 * (ch ^ ((row ^ (row >> 3)) & 7)); }
 
 __device__ __forceinline__ void transpose8(const uint32_t (&in)[8][4], u32x4_t (&out)[8]) {
 #pragma unroll
@@ -135,72 +145,110 @@ __device__ __forceinline__ void transpose8(const uint32_t (&in)[8][4], u32x4_t (
   }
 }
 
+template <bool WIDE>   // r > 16: two 16-column blocks of V
 __global__ __launch_bounds__(256) void k_tn_partial(const uint16_t *__restrict__ Z, int64_t T, int64_t P,
                                                     const uint16_t *__restrict__ V, int r,
                                                     float *__restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) char zt[64 * TPITCH];
+  __shared__ __attribute__((aligned(16))) char zt[TN_COLS * TPITCH];
   __shared__ __attribute__((aligned(16))) char vt[32 * TPITCH];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int64_t p0 = (int64_t)blockIdx.x * 64;
+  const int64_t p0 = (int64_t)blockIdx.x * TN_COLS;
   const int64_t c = blockIdx.y;
   const int64_t t0 = c * TN_CHUNK;
-
-  {  // Z block: rows t0 + 8 tb + i, columns p0 + 8 pb + e
-    const int tb = t & 31, pb = t >> 5;
-    uint32_t in[8][4];
+  const int cg = t & 31, rg = t >> 5;         // Z: columns p0 + 8 cg .. +7, rows 8 rg .. +7 of a block
+  const bool col_ok = p0 + 8 * cg < P;
+  const int vjg = t & 3, vrg = (t >> 2) & 7;  // V (threads < 32): columns 8 vjg .. +7, rows 8 vrg .. +7
+  uint32_t zin[8][4], vin[8][4];
+  auto load = [&](int rb) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t row = t0 + 8 * tb + i;
+      const int64_t row = t0 + TN_ROWS * rb + 8 * rg + i;
       u32x4_t v = {0, 0, 0, 0};
-      if (row < T) v = *reinterpret_cast<const u32x4_t *>(Z + row * P + p0 + 8 * pb);
+      if (row < T && col_ok) v = *reinterpret_cast<const u32x4_t *>(Z + row * P + p0 + 8 * cg);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) in[i][q] = v[q];
+      for (int q = 0; q < 4; ++q) zin[i][q] = v[q];
     }
-    u32x4_t o[8];
-    transpose8(in, o);
+    if (t < 32) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4_t *>(zt + (8 * pb + e) * TPITCH + 16 * tb) = o[e];
-  }
-  if (t < 128) {  // V block: rows t0 + 8 tb + i, columns 8 jb + e (zero beyond r)
-    const int tb = t & 31, jb = t >> 5;
-    uint32_t in[8][4];
+      for (int i = 0; i < 8; ++i) {
+        const int64_t row = t0 + TN_ROWS * rb + 8 * vrg + i;
+        u32x4_t v = {0, 0, 0, 0};
+        if (row < T && 8 * vjg < r) v = *reinterpret_cast<const u32x4_t *>(V + row * r + 8 * vjg);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t row = t0 + 8 * tb + i;
-      u32x4_t v = {0, 0, 0, 0};
-      if (row < T && 8 * jb < r) v = *reinterpret_cast<const u32x4_t *>(V + row * r + 8 * jb);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) in[i][q] = v[q];
+        for (int q = 0; q < 4; ++q) vin[i][q] = v[q];
+      }
     }
-    u32x4_t o[8];
-    transpose8(in, o);
+  };
+  floatx4_t acc[4][WIDE ? 2 : 1];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4_t *>(vt + (8 * jb + e) * TPITCH + 16 * tb) = o[e];
-  }
-  __syncthreads();
-
-  floatx4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-  const int prow = 16 * wave + (lane & 15);
-  const int tq = 16 * (lane >> 4);       // byte offset of this lane's 8 t values inside a step
+  for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-  for (int ts = 0; ts < TN_CHUNK / 32; ++ts) {
-    const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(zt + prow * TPITCH + 64 * ts + tq);
-    const bf16x8 fb0 = *reinterpret_cast<const bf16x8 *>(vt + (lane & 15) * TPITCH + 64 * ts + tq);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb0, acc0, 0, 0, 0);
-    if (r > 16) {
-      const bf16x8 fb1 = *reinterpret_cast<const bf16x8 *>(vt + (16 + (lane & 15)) * TPITCH + 64 * ts + tq);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb1, acc1, 0, 0, 0);
+    for (int jb = 0; jb < (WIDE ? 2 : 1); ++jb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[pb][jb][e] = 0.0f;
+  load(0);
+  for (int rb = 0; rb < TN_CHUNK / TN_ROWS; ++rb) {
+    {
+      u32x4_t o[8];
+      transpose8(zin, o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4_t *>(zt + tn_off(8 * cg + e, rg)) = o[e];
+      if (t < 32) {
+        transpose8(vin, o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4_t *>(vt + tn_off(8 * vjg + e, vrg)) = o[e];
+      }
+    }
+    __syncthreads();
+    if (rb + 1 < TN_CHUNK / TN_ROWS) load(rb + 1);
+    // All fragments of the block are read first and stay live until after the closing barrier:
+    // with the reads interleaved, the compiler reused an MFMA's source registers for address
+    // arithmetic right after issuing it, and rows i % 4 in {2, 3} of that MFMA came out wrong
+    // (no wait states were inserted between the MFMA and the overwrite).
+    bf16x8 fa[TN_ROWS / 32][4], fb[TN_ROWS / 32][WIDE ? 2 : 1];
+#pragma unroll
+    for (int ks = 0; ks < TN_ROWS / 32; ++ks) {
+      const int ch = 4 * ks + (lane >> 4);    // chunk of this lane's 8 t values
+#pragma unroll
+      for (int jb = 0; jb < (WIDE ? 2 : 1); ++jb)
+        fb[ks][jb] = *reinterpret_cast<const bf16x8 *>(vt + tn_off(16 * jb + (lane & 15), ch));
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb)
+        fa[ks][pb] = *reinterpret_cast<const bf16x8 *>(zt + tn_off(64 * wave + 16 * pb + (lane & 15), ch));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < TN_ROWS / 32; ++ks)
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+        for (int jb = 0; jb < (WIDE ? 2 : 1); ++jb)
+          acc[pb][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][pb], fb[ks][jb], acc[pb][jb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7");   // 16 wait states before anything may overwrite them
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < TN_ROWS / 32; ++ks) {
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) asm volatile("" ::"v"(fa[ks][pb]));
+#pragma unroll
+      for (int jb = 0; jb < (WIDE ? 2 : 1); ++jb) asm volatile("" ::"v"(fb[ks][jb]));
     }
   }
-  // lane holds column j = lane % 16 (+16) and rows p = 4 (lane / 16) + e of this wave's 16
+  // lane holds column j = lane % 16 (+16) and rows p = 4 (lane / 16) + e of each 16-row block
   float *out = partial + c * P * r;
+  const int j = lane & 15;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int64_t p = p0 + 16 * wave + 4 * (lane >> 4) + e;
-    const int j = lane & 15;
-    if (j < r) out[p * r + j] = acc0[e];
-    if (r > 16 && 16 + j < r) out[p * r + 16 + j] = acc1[e];
-  }
+  for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t p = p0 + 64 * wave + 16 * pb + 4 * (lane >> 4) + e;
+      if (p < P) {
+        if (j < r) out[p * r + j] = acc[pb][0][e];
+        if constexpr (WIDE)
+          if (16 + j < r) out[p * r + 16 + j] = acc[pb][WIDE ? 1 : 0][e];
+      }
+    }
 }
 
 __global__ __launch_bounds__(256) void k_tn_reduce(const float *__restrict__ partial, int64_t n_chunks,
@@ -251,8 +299,11 @@ lsn_status launch_transpose(const uint16_t *src, int64_t rows, int64_t cols, uin
 lsn_status launch_tn_partial(const uint16_t *Z, int64_t T, int64_t P, const uint16_t *V, int r, float *partial,
                              hipStream_t s) {
   const int64_t n_chunks = (T + TN_CHUNK - 1) / TN_CHUNK;
-  hipLaunchKernelGGL(k_tn_partial, dim3((unsigned)(P / 64), (unsigned)n_chunks), dim3(256), 0, s, Z, T, P, V,
-                     r, partial);
+  const dim3 grid((unsigned)((P + TN_COLS - 1) / TN_COLS), (unsigned)n_chunks);
+  if (r > 16)
+    hipLaunchKernelGGL(k_tn_partial<true>, grid, dim3(256), 0, s, Z, T, P, V, r, partial);
+  else
+    hipLaunchKernelGGL(k_tn_partial<false>, grid, dim3(256), 0, s, Z, T, P, V, r, partial);
   return check_hip(hipGetLastError(), "k_tn_partial launch");
 }
 

@@ -198,16 +198,21 @@ __global__ __launch_bounds__(256) void k_dequant(DqJobs jobs, Nf4KernelTable tab
 // ---------------------------------------------------------------------------------------------
 // dequantise into the transposed layout: out[k][n] = w_hat[n][k] (bf16), for a backward GEMM
 // that reduces over n with both operands n-contiguous. Same arithmetic as k_dequant, so the
-// values are bit-identical. Workgroup tile: 512 rows n x 64 columns k (one 64-weight block per
-// row). Thread t decodes rows n0 + 8 (t % 64) .. +7 at columns k0 + 16 (t / 64) .. +15 (8 code
-// bytes per row), then stores each of its 16 columns as 8 consecutive n (16 bytes), so a wave's
-// store covers 1 KB of one out row (long write runs keep the HBM pages open).
-// A 128-byte line of codes spans 4 k-tiles. Tiles walk k fastest, and each job's workgroups
-// start at a multiple of 32 so that the permutation below hands the 4 tiles of a line to 4
-// workgroups on the same XCD (workgroup b runs on XCD b % 8): the line is fetched from HBM once
-// into that XCD's L2 instead of once per XCD.
+// values are bit-identical. Workgroup tile: 256 rows n x 256 columns k (a whole 128-byte line of
+// codes per row), in 2 passes of 128 columns whose loads are all issued up front: thread t
+// decodes rows n0 + 8 (t % 32) .. +7 at columns k0 + 16 (t / 32) .. +15 of the pass (8 code
+// bytes per row, one 64-weight block), then stores each of its 16 columns as 8 consecutive n
+// (16 bytes), so 32 lanes write a 512-byte run of one out row. Tiles walk n fastest:
+// neighbouring workgroups write neighbouring runs of the same out rows, which keeps the pages
+// (and translations) they touch few; in k order an out row is 2 x rows bytes long and a run of
+// tiles would touch every page of the output.
 // Requires rows % 8 == 0 (checked by the caller); cols % 64 == 0 by the format.
 // ---------------------------------------------------------------------------------------------
+constexpr int kDqtRows = 256, kDqtCols = 256;
+__host__ __device__ inline int64_t dqt_tiles(int64_t rows, int64_t cols) {
+  return ((rows + kDqtRows - 1) / kDqtRows) * ((cols + kDqtCols - 1) / kDqtCols);
+}
+
 __global__ __launch_bounds__(256) void k_dequant_t(DqJobs jobs, Nf4KernelTable tab) {
   __shared__ float sq[16];
   __shared__ float scode8[256];
@@ -215,46 +220,54 @@ __global__ __launch_bounds__(256) void k_dequant_t(DqJobs jobs, Nf4KernelTable t
   if (t < 16) sq[t] = tab.q[t];
   if (t < 255) scode8[t] = int8_level(t - 127);
   const DqJob &J = jobs.job[find_job(jobs, blockIdx.x)];
-  const int64_t b = (int64_t)blockIdx.x - J.wg0;          // J.wg0 % 32 == 0, so b % 8 is the XCD
-  const int64_t tile = (b & ~(int64_t)31) + 4 * (b & 7) + ((b >> 3) & 3);
-  const int64_t kt = J.cols / 64;
-  if (tile >= kt * ((J.rows + 511) / 512)) return;         // padding up to a multiple of 32
+  const int64_t tile = (int64_t)blockIdx.x - J.wg0;
   const int64_t rows = J.rows, cols = J.cols;
-  const int64_t k = (tile % kt) * 64 + 16 * (t >> 6);
-  const int64_t n = (tile / kt) * 512 + 8 * (t & 63);
-  const bool ok = n < rows;
-  uint2 word[8];
-  int v[8];
-  float s2[8];
+  const int64_t ntn = (rows + kDqtRows - 1) / kDqtRows;
+  const int64_t n = (tile % ntn) * kDqtRows + 8 * (t & 31);
+  const int64_t kbase = (tile / ntn) * kDqtCols + 16 * (t >> 5);
+  const bool row_ok = n < rows;
+  constexpr int NP = kDqtCols / 128;
+  uint2 word[NP][8];
+  int v[NP][8];
+  float s2[NP][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t e = (n + i) * cols + k;            // element index of the thread's first weight in row n+i
-    word[i] = ok ? *reinterpret_cast<const uint2 *>(J.codes + (e >> 1)) : make_uint2(0u, 0u);
-    v[i] = ok ? J.qabsmax[e >> 6] : 0;
-    s2[i] = ok ? J.absmax2[e >> 14] : 0.0f;
-  }
-  __syncthreads();
-  if (!ok) return;
-  const float mu = J.mu;
-  uint16_t *out = reinterpret_cast<uint16_t *>(J.out);
-  float c[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = decode_absmax(scode8[v[i] + 127], s2[i], mu);
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int shift = 8 * ((e >> 1) & 3) + ((e & 1) ? 0 : 4);
-    float f[8];
+  for (int ps = 0; ps < NP; ++ps) {
+    const int64_t k = kbase + 128 * ps;
+    const bool ok = row_ok && k < cols;              // whole 64-column blocks: cols % 64 == 0
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t w = (e < 8) ? word[i].x : word[i].y;
-      f[i] = __fmul_rn(sq[(w >> shift) & 15u], c[i]);
+      const int64_t e = (n + i) * cols + k;          // element index of the thread's first weight in row n+i
+      word[ps][i] = ok ? *reinterpret_cast<const uint2 *>(J.codes + (e >> 1)) : make_uint2(0u, 0u);
+      v[ps][i] = ok ? J.qabsmax[e >> 6] : 0;
+      s2[ps][i] = ok ? J.absmax2[e >> 14] : 0.0f;
     }
-    u32x4_t o;
-    o.x = pack_bf16x2(f[0], f[1]);
-    o.y = pack_bf16x2(f[2], f[3]);
-    o.z = pack_bf16x2(f[4], f[5]);
-    o.w = pack_bf16x2(f[6], f[7]);
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t *>(out + (k + e) * rows + n));
+  }
+  __syncthreads();
+  const float mu = J.mu;
+  uint16_t *out = reinterpret_cast<uint16_t *>(J.out);
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps) {
+    const int64_t k = kbase + 128 * ps;
+    if (!row_ok || k >= cols) continue;
+    float c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = decode_absmax(scode8[v[ps][i] + 127], s2[ps][i], mu);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int shift = 8 * ((e >> 1) & 3) + ((e & 1) ? 0 : 4);
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t w = (e < 8) ? word[ps][i].x : word[ps][i].y;
+        f[i] = __fmul_rn(sq[(w >> shift) & 15u], c[i]);
+      }
+      u32x4_t o;
+      o.x = pack_bf16x2(f[0], f[1]);
+      o.y = pack_bf16x2(f[2], f[3]);
+      o.z = pack_bf16x2(f[4], f[5]);
+      o.w = pack_bf16x2(f[6], f[7]);
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t *>(out + (k + e) * rows + n));
+    }
   }
 }
 
@@ -292,7 +305,7 @@ lsn_status launch_dequant(int n, const lsn_nf4 *w, void *const *out, int out_dty
     J.out = out[g];
     J.wg0 = wg;
     if (out_dtype == LSN_OUT_BF16_T)
-      wg += ((w[g].cols / 64) * ((w[g].rows + 511) / 512) + 31) / 32 * 32;   // whole groups of 32 (see k_dequant_t)
+      wg += dqt_tiles(w[g].rows, w[g].cols);
     else
       wg += w[g].rows * w[g].cols / 8192;
   }
