@@ -229,6 +229,26 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
                            const uint16_t *U, void *dX, int32_t dx_mode, float *dA, float *dB,
                            int32_t grad_mode, void *ws, size_t ws_bytes, void *stream);
 
+/* Device workspace bytes lora_linear_bwd_group needs for these n linears. */
+size_t lora_linear_group_ws_bytes(int32_t n, const lsn_lora_linear *L);
+
+/*
+ * lora_linear_bwd_group - the backwards of n (1 <= n <= 8) linears that read the same input X
+ * [T][K] (a decoder layer's q, k, v, gate and up), whose input gradients add up in one dX:
+ *   dX:  LSN_DX_BF16_SET writes bf16( sum_g (dY_g W_g + s G_g A_g) );
+ *        LSN_DX_F32_ADD adds the fp32 sum into dX;
+ *   dA_g, dB_g as lora_linear_bwd (LSN_GRAD_SET / LSN_GRAD_ADD), bit-identical to it.
+ * L: host array of n descriptors sharing T, K, r and the scale; dY, U, dA, dB: host arrays of
+ * n device pointers. With every W in the transposed bf16 layout the n dX products run as one
+ * GEMM whose reduction walks the members' N in turn (one fp32 accumulator, member order);
+ * otherwise the members run one after another (fp32 dX only when n > 1).
+ * ws: device, at least lora_linear_group_ws_bytes(n, L). Overlaps give LSN_E_ARG. Async.
+ */
+lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint16_t *X,
+                                 const uint16_t *const *dY, const uint16_t *const *U, void *dX,
+                                 int32_t dx_mode, float *const *dA, float *const *dB, int32_t grad_mode,
+                                 void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------------------------------
  * Layer pool ("Exact Layer Streaming", Abstract; transcript @7:11-7:32; "An 8B Fine-Tune
  * Now Fits in 4 GB of VRAM"): n_slots caller-owned device slots hold decoder-layer images;

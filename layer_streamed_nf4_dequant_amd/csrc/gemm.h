@@ -46,11 +46,23 @@ struct GemmSeg {
   const uint16_t *lr_act;  // U [M][r]
   void *out;               // [M][N]
 };
+// reduction segments: out = sum_p ( act_p W_p^T + s lr_act_p lr_w_p^T ), one output, the K-steps
+// of the segments run back to back (each K_p % 64 == 0)
+struct KSeg {
+  const uint16_t *act;     // [M][K_p]
+  const uint16_t *w;       // [N][K_p]
+  int64_t K;
+  const uint16_t *lr_act;  // [M][r]
+  const uint16_t *lr_w;    // [N][r]
+  int step0;               // first K-step of the segment (filled by launch_gemm_direct)
+};
 struct DirectArgs {
-  int64_t M, K;
+  int64_t M, K;            // K: total reduction length (the sum of the K_p in reduction-segment mode)
   const uint16_t *act;
   int nseg;
   GemmSeg seg[kMaxSegs];
+  int nkseg;               // > 0: reduction-segment mode (nseg must be 1; act, seg[0].w/lr_* unused)
+  KSeg kseg[kMaxSegs];
   int r;
   float scale;
   int adapters;

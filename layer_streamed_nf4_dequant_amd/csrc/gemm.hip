@@ -524,7 +524,7 @@ __device__ __forceinline__ void tile_coords(int64_t b, int64_t ntiles, int64_t t
   nt = in / gm;
 }
 
-template <int EPI>
+template <int EPI, bool KSEG>
 __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char *lds_a = smem;                               // 2 stages
@@ -558,11 +558,47 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   const int nk = (int)(a.K / DBK);
   const int k_last = nk - 1;
-  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.act, a.M * a.K * 2);
-  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(sg.w, sg.N * a.K * 2);
+  // Operand sources. In reduction-segment mode the A loads (one step ahead of the B loads)
+  // and the B loads each follow their own segment, switched when their step crosses into it.
+  __amdgpu_buffer_rsrc_t rs_a, rs_b;
   DirectRows8 da, db;
-  make_direct_rows8(da, a.M, a.K, m0, wave, lane);
-  make_direct_rows8(db, sg.N, a.K, n0, wave, lane);
+  int pa = 0, pb = 0;                               // segment of the next A / B load step
+  if constexpr (KSEG) {
+    rs_a = make_rsrc(a.kseg[0].act, a.M * a.kseg[0].K * 2);
+    rs_b = make_rsrc(a.kseg[0].w, sg.N * a.kseg[0].K * 2);
+    make_direct_rows8(da, a.M, a.kseg[0].K, m0, wave, lane);
+    make_direct_rows8(db, sg.N, a.kseg[0].K, n0, wave, lane);
+  } else {
+    rs_a = make_rsrc(a.act, a.M * a.K * 2);
+    rs_b = make_rsrc(sg.w, sg.N * a.K * 2);
+    make_direct_rows8(da, a.M, a.K, m0, wave, lane);
+    make_direct_rows8(db, sg.N, a.K, n0, wave, lane);
+  }
+  // byte offset along K of global step `step` inside its segment (moving pa / pb forward)
+  auto a_kb = [&](int step) -> uint32_t {
+    if constexpr (KSEG) {
+      while (pa + 1 < a.nkseg && step >= a.kseg[pa + 1].step0) {
+        ++pa;
+        rs_a = make_rsrc(a.kseg[pa].act, a.M * a.kseg[pa].K * 2);
+        make_direct_rows8(da, a.M, a.kseg[pa].K, m0, wave, lane);
+      }
+      return (uint32_t)(step - a.kseg[pa].step0) * DBK * 2;
+    } else {
+      return (uint32_t)step * DBK * 2;
+    }
+  };
+  auto b_kb = [&](int step) -> uint32_t {
+    if constexpr (KSEG) {
+      while (pb + 1 < a.nkseg && step >= a.kseg[pb + 1].step0) {
+        ++pb;
+        rs_b = make_rsrc(a.kseg[pb].w, sg.N * a.kseg[pb].K * 2);
+        make_direct_rows8(db, sg.N, a.kseg[pb].K, n0, wave, lane);
+      }
+      return (uint32_t)(step - a.kseg[pb].step0) * DBK * 2;
+    } else {
+      return (uint32_t)step * DBK * 2;
+    }
+  };
 
   // stage 0 <- step 0 (first, so that its latency overlaps the LoRA prologue)
 #pragma unroll
@@ -571,7 +607,12 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     issue_direct1(lds_b, rs_b, db, 0, wave, i);
   }
   // ---- LoRA prologue: acc = s * (B_seg . U_seg^T) over r (B_seg [N][r], U_seg [M][r]) ----
+  // (reduction-segment mode: the sum of the segments' terms, in segment order)
   if (a.adapters) {
+#pragma unroll 1
+   for (int p = 0; p < (KSEG ? a.nkseg : 1); ++p) {
+    const uint16_t *lr_act = KSEG ? a.kseg[p].lr_act : sg.lr_act;
+    const uint16_t *lr_w = KSEG ? a.kseg[p].lr_w : sg.lr_w;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (16 * h >= a.r) break;
@@ -581,14 +622,14 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + wm * 128 + 32 * i + (lane & 31);
         u32x4_t v = {0, 0, 0, 0};
-        if (m < a.M && jl < a.r) v = *reinterpret_cast<const u32x4_t *>(sg.lr_act + m * a.r + jl);
+        if (m < a.M && jl < a.r) v = *reinterpret_cast<const u32x4_t *>(lr_act + m * a.r + jl);
         la[i] = as_bf16x8(v);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t n = n0 + wn * 128 + 32 * j + (lane & 31);
         u32x4_t v = {0, 0, 0, 0};
-        if (n < sg.N && jl < a.r) v = *reinterpret_cast<const u32x4_t *>(sg.lr_w + n * a.r + jl);
+        if (n < sg.N && jl < a.r) v = *reinterpret_cast<const u32x4_t *>(lr_w + n * a.r + jl);
         lb[j] = as_bf16x8(v);
       }
       if (a.scale_pow2) {
@@ -604,6 +645,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lb[j], la[i], acc[i][j], 0, 0, 0);
     }
+   }
     if (!a.scale_pow2) {
       // one accumulator block at a time (the fences keep the compiler from moving all 256
       // accumulators into vector registers at once)
@@ -649,8 +691,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   };
 
   // operand A of step 1 to stage 1 (free); then wait for step 0 only, and read its first fragments
+  {
+    const uint32_t kb = a_kb(min(1, k_last));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) issue_direct1(lds_a + DTILE, rs_a, da, (uint32_t)min(1, k_last) * DBK * 2, wave, i);
+    for (int i = 0; i < 8; ++i) issue_direct1(lds_a + DTILE, rs_a, da, kb, wave, i);
+  }
   __builtin_amdgcn_sched_barrier(0);
   wait_vm<8>();
   __builtin_amdgcn_s_barrier();
@@ -670,8 +715,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   // (unrolled by two so that the stage of each step is a constant)
   auto step = [&](int kt, int st) {
     const int nx = st ^ 1;
-    const uint32_t kb1 = (uint32_t)min(kt + 1, k_last) * DBK * 2;
-    const uint32_t kb2 = (uint32_t)min(kt + 2, k_last) * DBK * 2;
+    const uint32_t kb1 = b_kb(min(kt + 1, k_last));
+    const uint32_t kb2 = a_kb(min(kt + 2, k_last));
     substep(st, 1, 1, nx, kb1, ca, cb, na, nb);
     substep(st, 2, -1, 0, 0, na, nb, ca, cb);
     substep(st, 3, -1, 0, 0, ca, cb, na, nb);
@@ -745,11 +790,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
 constexpr size_t kDirectSmemBytes = 256 * kEpiPitch > 4 * DTILE ? 256 * kEpiPitch : 4 * DTILE;
 static_assert(256 * kEpiPitch <= kDirectSmemBytes, "the epilogue tile must fit in the ring's LDS");
 
-template <int EPI>
+template <int EPI, bool KSEG>
 lsn_status launch_direct_one(const DirectArgs &a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_direct<EPI>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_direct<EPI, KSEG>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDirectSmemBytes);
     if (e != hipSuccess) return check_hip(e, "gemm_direct smem attribute");
     attr_set = true;
@@ -757,7 +802,7 @@ lsn_status launch_direct_one(const DirectArgs &a, hipStream_t s) {
   int64_t ntiles_n = 0;
   for (int q = 0; q < a.nseg; ++q) ntiles_n += (a.seg[q].N + BN - 1) / BN;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ntiles_n;
-  hipLaunchKernelGGL((k_gemm_direct<EPI>), dim3((unsigned)tiles), dim3(NT), kDirectSmemBytes, s, a);
+  hipLaunchKernelGGL((k_gemm_direct<EPI, KSEG>), dim3((unsigned)tiles), dim3(NT), kDirectSmemBytes, s, a);
   return check_hip(hipGetLastError(), "k_gemm_direct launch");
 }
 
@@ -791,7 +836,16 @@ lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s) {
     a.seg[q].ntile0 = t0;
     t0 += (a.seg[q].N + BN - 1) / BN;
   }
-  return epi == EPI_BF16 ? launch_direct_one<EPI_BF16>(a, s) : launch_direct_one<EPI_F32_ADD>(a, s);
+  if (a.nkseg > 0) {
+    int64_t step = 0;
+    for (int p = 0; p < a.nkseg; ++p) {
+      a.kseg[p].step0 = (int)step;
+      step += a.kseg[p].K / DBK;
+    }
+    a.K = step * DBK;
+    return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, true>(a, s) : launch_direct_one<EPI_F32_ADD, true>(a, s);
+  }
+  return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, false>(a, s) : launch_direct_one<EPI_F32_ADD, false>(a, s);
 }
 
 lsn_status launch_gemm(int layout, int wkind, int epi, GemmArgs a, hipStream_t s) {

@@ -382,4 +382,124 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
   return launch_tn_reduce(need.part_dA, nc, K, (int)r, L->scale, acc, 1, dA, s);
 }
 
+size_t lora_linear_group_ws_bytes(int32_t n, const lsn_lora_linear *L) {
+  if (n < 1 || n > kMaxSegs || !L) return 0;
+  size_t total = 0;
+  for (int g = 0; g < n; ++g) {
+    if (L[g].T < 1 || L[g].K < 1 || L[g].N < 1 || L[g].r < 1) return 0;
+    total += bwd_layout(nullptr, L[g].T, L[g].K, L[g].N, L[g].r).bytes;
+  }
+  return total;
+}
+
+lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint16_t *X, const uint16_t *const *dY,
+                                 const uint16_t *const *U, void *dX, int32_t dx_mode, float *const *dA,
+                                 float *const *dB, int32_t grad_mode, void *ws, size_t ws_bytes, void *stream) {
+  if (n < 1 || n > kMaxSegs || !L || !dY || !U || !dA || !dB)
+    return fail(LSN_E_ARG, "lora_linear_bwd_group: need 1 <= n <= %d and non-null arrays", kMaxSegs);
+  bool all_t = true;
+  for (int g = 0; g < n; ++g) {
+    lsn_status st = check_linear(&L[g], "lora_linear_bwd_group");
+    if (st != LSN_OK) return st;
+    if (L[g].T != L[0].T || L[g].K != L[0].K || L[g].r != L[0].r || L[g].scale != L[0].scale)
+      return fail(LSN_E_ARG, "lora_linear_bwd_group: members must share T, K, r and the scale");
+    all_t = all_t && L[g].W.kind == LSN_W_BF16_T;
+  }
+  if (dx_mode != LSN_DX_BF16_SET && dx_mode != LSN_DX_F32_ADD)
+    return fail(LSN_E_ARG, "lora_linear_bwd_group: unknown dX mode %d", dx_mode);
+  if (grad_mode != LSN_GRAD_SET && grad_mode != LSN_GRAD_ADD)
+    return fail(LSN_E_ARG, "lora_linear_bwd_group: unknown gradient mode %d", grad_mode);
+  if (!all_t && dx_mode == LSN_DX_BF16_SET && n > 1)
+    return fail(LSN_E_ARG, "lora_linear_bwd_group: a bf16 dX summed over several members needs their weights "
+                           "in the transposed bf16 layout");
+  const int64_t T = L[0].T, K = L[0].K, r = L[0].r;
+  if (!X || !dX || !ws || !aligned16(X) || !aligned16(dX) || ((uintptr_t)ws & 255))
+    return fail(LSN_E_ARG, "lora_linear_bwd_group: X, dX must be non-null and 16-byte, ws 256-byte aligned");
+  const size_t need = lora_linear_group_ws_bytes(n, L);
+  if (ws_bytes < need)
+    return fail(LSN_E_ARG, "lora_linear_bwd_group: workspace too small (%zu < %zu)", ws_bytes, need);
+  // every output against every input, and the outputs pairwise
+  const void *outs[2 + 2 * kMaxSegs];
+  size_t outb[2 + 2 * kMaxSegs];
+  int n_out = 0;
+  outs[n_out] = dX;
+  outb[n_out++] = (size_t)(T * K * (dx_mode == LSN_DX_F32_ADD ? 4 : 2));
+  outs[n_out] = ws;
+  outb[n_out++] = need;
+  for (int g = 0; g < n; ++g) {
+    if (!dY[g] || !U[g] || !dA[g] || !dB[g] || !aligned16(dY[g]) || !aligned16(U[g]))
+      return fail(LSN_E_ARG, "lora_linear_bwd_group: member %d: null or misaligned dY, U, dA or dB", g);
+    outs[n_out] = dA[g];
+    outb[n_out++] = (size_t)(r * K * 4);
+    outs[n_out] = dB[g];
+    outb[n_out++] = (size_t)(L[g].N * r * 4);
+  }
+  for (int o = 0; o < n_out; ++o) {
+    for (int p = 0; p < o; ++p)
+      if (ranges_overlap(outs[o], outb[o], outs[p], outb[p]))
+        return fail(LSN_E_ARG, "lora_linear_bwd_group: two outputs overlap");
+    if (ranges_overlap(outs[o], outb[o], X, (size_t)(T * K * 2)))
+      return fail(LSN_E_ARG, "lora_linear_bwd_group: an output overlaps X");
+    for (int g = 0; g < n; ++g) {
+      const void *ins[8] = {dY[g], U[g], L[g].A, L[g].B};
+      size_t inb[8] = {(size_t)(T * L[g].N * 2), (size_t)(T * r * 2), (size_t)(r * K * 2), (size_t)(L[g].N * r * 2)};
+      const int n_in = 4 + w_ranges(&L[g], ins + 4, inb + 4);
+      for (int i = 0; i < n_in; ++i)
+        if (ranges_overlap(outs[o], outb[o], ins[i], inb[i]))
+          return fail(LSN_E_ARG, "lora_linear_bwd_group: an output overlaps an input of member %d", g);
+    }
+  }
+  lsn_status st = require_gfx950();
+  if (st != LSN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (!all_t) {
+    // one member at a time (fp32 accumulation into dX in member order)
+    char *w = static_cast<char *>(ws);
+    for (int g = 0; g < n; ++g) {
+      const size_t b = bwd_layout(nullptr, T, K, L[g].N, r).bytes;
+      if ((st = lora_linear_bwd(&L[g], X, dY[g], U[g], dX, dx_mode, dA[g], dB[g], grad_mode, w, b, stream)) != LSN_OK)
+        return st;
+      w += b;
+    }
+    return LSN_OK;
+  }
+  // G_g = bf16(dY_g B_g) and A_g^T for every member, then the n dX products as one GEMM whose
+  // reduction runs over the members' N in turn, then dA_g, dB_g
+  BwdWs part[kMaxSegs];
+  char *w = static_cast<char *>(ws);
+  DirectArgs d{};
+  d.M = T;
+  d.nseg = 1;
+  d.seg[0].N = K;
+  d.seg[0].out = dX;
+  d.nkseg = n;
+  d.r = (int)r;
+  d.scale = L[0].scale;
+  d.adapters = 1;
+  for (int g = 0; g < n; ++g) {
+    const int64_t N = L[g].N;
+    part[g] = bwd_layout(w, T, K, N, r);
+    w += part[g].bytes;
+    if ((st = launch_transpose(L[g].B, N, r, part[g].Bt, s)) != LSN_OK) return st;
+    if ((st = launch_rowproj(dY[g], T, N, part[g].Bt, (int)r, part[g].G, s)) != LSN_OK) return st;
+    if ((st = launch_transpose(L[g].A, r, K, part[g].At, s)) != LSN_OK) return st;
+    d.kseg[g].act = dY[g];
+    d.kseg[g].w = L[g].W.bf16;
+    d.kseg[g].K = N;
+    d.kseg[g].lr_act = part[g].G;
+    d.kseg[g].lr_w = part[g].At;
+  }
+  if ((st = launch_gemm_direct(d, dx_mode == LSN_DX_F32_ADD ? EPI_F32_ADD : EPI_BF16, s)) != LSN_OK) return st;
+  const int64_t nc = (T + TN_CHUNK - 1) / TN_CHUNK;
+  const int acc = grad_mode == LSN_GRAD_ADD;
+  for (int g = 0; g < n; ++g) {
+    const int64_t N = L[g].N;
+    if ((st = launch_tn_partial(dY[g], T, N, U[g], (int)r, part[g].part_dB, s)) != LSN_OK) return st;
+    if ((st = launch_tn_reduce(part[g].part_dB, nc, N, (int)r, L[g].scale, acc, 0, dB[g], s)) != LSN_OK) return st;
+    if ((st = launch_tn_partial(X, T, K, part[g].G, (int)r, part[g].part_dA, s)) != LSN_OK) return st;
+    if ((st = launch_tn_reduce(part[g].part_dA, nc, K, (int)r, L[g].scale, acc, 1, dA[g], s)) != LSN_OK) return st;
+  }
+  return LSN_OK;
+}
+
 }  // extern "C"

@@ -31,7 +31,7 @@ FAULT_STALE_REFETCH, FAULT_WRONG_SLOT = 1 << 8, 1 << 9
 EXPORTS = (
     "lsn_last_error", "lsn_abi_version", "lsn_nf4_codebook", "nf4_pack_ws_bytes", "nf4_pack",
     "nf4_dequant", "nf4_dequant_batch", "lora_down", "lora_linear_ws_bytes", "lora_linear_fwd", "lora_linear_fwd_group",
-    "lora_linear_bwd",
+    "lora_linear_bwd", "lora_linear_group_ws_bytes", "lora_linear_bwd_group",
     "layer_pool_create", "layer_pool_register", "layer_pool_prefetch", "layer_pool_acquire",
     "layer_pool_release", "layer_pool_stats", "layer_pool_audit", "layer_pool_destroy",
 )
@@ -95,6 +95,10 @@ def load():
                                         ctypes.POINTER(vp), vp, sz, vp]),
         "lora_linear_bwd": (i32, [ctypes.POINTER(LoraLinearDesc), vp, vp, vp, vp, i32, vp, vp, i32,
                                   vp, sz, vp]),
+        "lora_linear_group_ws_bytes": (sz, [i32, ctypes.POINTER(LoraLinearDesc)]),
+        "lora_linear_bwd_group": (i32, [i32, ctypes.POINTER(LoraLinearDesc), vp, ctypes.POINTER(vp),
+                                        ctypes.POINTER(vp), vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32,
+                                        vp, sz, vp]),
         "layer_pool_create": (i32, [i32, sz, ctypes.POINTER(vp), i32, vp, ctypes.c_uint32,
                                     ctypes.POINTER(vp)]),
         "layer_pool_register": (i32, [vp, i32, vp, sz]),
@@ -265,6 +269,24 @@ def lora_linear_bwd(desc: LoraLinearDesc, X, dY, U, dX, dA, dB, dx_mode: int = D
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     check(load().lora_linear_bwd(ctypes.byref(desc), _ptr(X), _ptr(dY), _ptr(U), _ptr(dX), dx_mode,
                                  _ptr(dA), _ptr(dB), grad_mode, _ptr(ws), nbytes, _stream_handle(stream)))
+
+
+def group_ws_bytes(descs) -> int:
+    n = len(descs)
+    return int(load().lora_linear_group_ws_bytes(n, (LoraLinearDesc * n)(*descs)))
+
+
+def lora_linear_bwd_group(descs, X, dY_list, U_list, dX, dA_list, dB_list, dx_mode: int = DX_F32_ADD,
+                          grad_mode: int = GRAD_SET, ws=None, stream=None) -> None:
+    """Backwards of linears sharing X whose input gradients add up in dX (one GEMM for
+    transposed bf16 weights)."""
+    n = len(descs)
+    arr = (LoraLinearDesc * n)(*descs)
+    ptrs = lambda ts: (ctypes.c_void_p * n)(*[_ptr(t) for t in ts])  # noqa: E731
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    check(load().lora_linear_bwd_group(n, arr, _ptr(X), ptrs(dY_list), ptrs(U_list), _ptr(dX), dx_mode,
+                                       ptrs(dA_list), ptrs(dB_list), grad_mode, _ptr(ws), nbytes,
+                                       _stream_handle(stream)))
 
 
 class LayerPool:

@@ -163,6 +163,11 @@ class Stack:
         self.dX_o_pp = [torch.empty((T, cfg.hidden), dtype=bf16, device=self.dev) for _ in range(2)]
         self.dX_d_pp = [torch.empty((T, cfg.inter), dtype=bf16, device=self.dev) for _ in range(2)]
         ws = max(lib.ws_bytes(T, p.K, p.N, r) for p in self.layout)
+        self.h_group = [j for j, p in enumerate(self.layout) if PROJ_INPUT[p.name] == "h"]
+        if len(self.h_group) > 1:
+            probe = [lib.LoraLinearDesc(T, self.layout[j].K, self.layout[j].N, r, cfg.scale, lib.WeightDesc(), None,
+                                        None) for j in self.h_group]
+            ws = max(ws, lib.group_ws_bytes(probe))
         self.ws = torch.empty(ws, dtype=torch.uint8, device=self.dev)
         self.w_stage = self.w_stage_t = None
         if self.dequant == "staged":
@@ -268,15 +273,21 @@ class Stack:
         return self.dX_d_pp[0]
 
     def _backward_layer(self, base: int, l: int, s):
+        # q, k, v, gate and up read X_h: their input gradients add up in dX_h (fp32), as one
+        # grouped backward (a single GEMM over their concatenated N when staged)
         self.dX_h.zero_()
+        hj = self.h_group
+        lib.lora_linear_bwd_group([self._desc(base, l, j, backward=True) for j in hj], self.X["h"],
+                                  [self.upstream(l, j) for j in hj], [self.U[j] for j in hj], self.dX_h,
+                                  [self.dA[l][j] for j in hj], [self.dB[l][j] for j in hj],
+                                  dx_mode=lib.DX_F32_ADD, grad_mode=lib.GRAD_SET, ws=self.ws, stream=s)
         for j, p in enumerate(self.layout):
             which = PROJ_INPUT[p.name]
             if which == "h":
-                dX, mode = self.dX_h, lib.DX_F32_ADD
-            else:
-                dX, mode = (self.dX_o_pp[l % 2] if which == "o" else self.dX_d_pp[l % 2]), lib.DX_BF16_SET
+                continue
+            dX = self.dX_o_pp[l % 2] if which == "o" else self.dX_d_pp[l % 2]
             lib.lora_linear_bwd(self._desc(base, l, j, backward=True), self.X[which], self.upstream(l, j), self.U[j], dX,
-                                self.dA[l][j], self.dB[l][j], dx_mode=mode, grad_mode=lib.GRAD_SET,
+                                self.dA[l][j], self.dB[l][j], dx_mode=lib.DX_BF16_SET, grad_mode=lib.GRAD_SET,
                                 ws=self.ws, stream=s)
 
     def _record(self, tag: str, l: int, tensors):

@@ -131,6 +131,80 @@ def test_grouped_forward_equals_single_forwards(gpu, base):
         lib.lora_linear_fwd_group([cs[0].desc(), cs[1].desc()], X, [Yg[0], X], Ug[:2], ws=cs[0].ws)
 
 
+@pytest.mark.parametrize("base", ["nf4", "bf16"])
+def test_grouped_backward(gpu, base):
+    """Five linears sharing X (ragged T, mixed N): the grouped backward gives each member's dA,
+    dB bit-identical to its own backward, and dX equal to the sum of the members' dX (one GEMM
+    over the concatenated N for transposed weights; member order otherwise), matching the
+    oracle; the fp32 accumulate mode adds onto what dX held."""
+    import torch
+    T, K, r = 300, 512, 16
+    Ns = [512, 128, 128, 1344, 1344]
+    cs = [Case(T, K, N, r=r, base=base, tag=f"gbwd{i}") for i, N in enumerate(Ns)]
+    X = cs[0].Xd
+    print(f"case: grouped backward T={T} K={K} N={Ns} base={base}", flush=True)
+    Us = []
+    for c in cs:
+        Y = torch.empty((T, c.N), dtype=torch.bfloat16, device="cuda")
+        U = torch.empty((T, r), dtype=torch.bfloat16, device="cuda")
+        lib.lora_linear_fwd(c.desc(), X, Y, U, adapters=True, ws=c.ws)
+        Us.append(U)
+    wts = [c.w_transposed() for c in cs]
+    descs = [c.desc(wt, transposed=True) for c, wt in zip(cs, wts)]
+    ws = torch.empty(lib.group_ws_bytes(descs), dtype=torch.uint8, device="cuda")
+    dX0 = torch.from_numpy(cs[0].dX_init).cuda()
+    dX = dX0.clone()
+    dA = [torch.empty((r, K), dtype=torch.float32, device="cuda") for _ in cs]
+    dB = [torch.empty((c.N, r), dtype=torch.float32, device="cuda") for c in cs]
+    lib.lora_linear_bwd_group(descs, X, [c.dYd for c in cs], Us, dX, dA, dB, dx_mode=lib.DX_F32_ADD, ws=ws)
+    dX16 = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    dA2 = [torch.empty_like(a) for a in dA]
+    dB2 = [torch.empty_like(b) for b in dB]
+    lib.lora_linear_bwd_group(descs, X, [c.dYd for c in cs], Us, dX16, dA2, dB2, dx_mode=lib.DX_BF16_SET, ws=ws)
+    # members one by one
+    dX_seq = dX0.clone()
+    for c, wt, U, a, b in zip(cs, wts, Us, dA2, dB2):
+        a1, b1 = torch.empty_like(a), torch.empty_like(b)
+        lib.lora_linear_bwd(c.desc(wt, transposed=True), X, c.dYd, U, dX_seq, a1, b1, dx_mode=lib.DX_F32_ADD,
+                            ws=c.ws)
+        torch.cuda.synchronize()
+        assert _eq(a, a1) and _eq(b, b1)
+    torch.cuda.synchronize()
+    for a, a2, b, b2 in zip(dA, dA2, dB, dB2):
+        assert _eq(a, a2) and _eq(b, b2)
+    want = np.zeros((T, K))
+    for c in cs:
+        dXo, dAo, dBo, _ = olora.backward(onf4_f32(cs[0].X), onf4_f32(c.dY), onf4_f32(c.W_hat_bits),
+                                         onf4_f32(c.A), onf4_f32(c.B), c.s)
+        want += dXo
+    assert_close("dX", to_np(dX).astype(np.float64) - cs[0].dX_init, want)
+    assert_close("dX", to_np(dX16), want)
+    assert_close("dX", to_np(dX_seq).astype(np.float64) - cs[0].dX_init, want)
+    # the fused sum differs from the member-order sum only by fp32 rounding
+    assert olora.rel_l2(to_np(dX).astype(np.float64), to_np(dX_seq).astype(np.float64)) < 1e-6
+    # weights not transposed: one member after another, bit-identical to separate calls
+    dXn = dX0.clone()
+    dA3 = [torch.empty_like(a) for a in dA]
+    dB3 = [torch.empty_like(b) for b in dB]
+    lib.lora_linear_bwd_group([c.desc() for c in cs], X, [c.dYd for c in cs], Us, dXn, dA3, dB3,
+                              dx_mode=lib.DX_F32_ADD, ws=ws)
+    dXm = dX0.clone()
+    for c, U in zip(cs, Us):
+        a1, b1 = torch.empty((r, K), dtype=torch.float32, device="cuda"), torch.empty((c.N, r), dtype=torch.float32,
+                                                                                      device="cuda")
+        lib.lora_linear_bwd(c.desc(), X, c.dYd, U, dXm, a1, b1, dx_mode=lib.DX_F32_ADD, ws=c.ws)
+    torch.cuda.synchronize()
+    assert _eq(dXn, dXm)
+    with pytest.raises(lib.LsnError):          # bf16 dX over several untransposed members
+        lib.lora_linear_bwd_group([c.desc() for c in cs], X, [c.dYd for c in cs], Us, dX16, dA3, dB3,
+                                  dx_mode=lib.DX_BF16_SET, ws=ws)
+    with pytest.raises(lib.LsnError):          # workspace too small
+        lib.lora_linear_bwd_group(descs, X, [c.dYd for c in cs], Us, dX, dA, dB, ws=ws[:1024])
+    with pytest.raises(lib.LsnError):          # an output overlapping an input
+        lib.lora_linear_bwd_group(descs, X, [c.dYd for c in cs], Us, dX, [dA[0], dA[1], dA[2], dA[3], dB[4]], dB,
+                                  ws=ws)
+
+
 def test_b_zero_equals_adapters_off_and_recompute_equals_forward(gpu):
     import torch
     c = Case(512, 896, 896, B_zero=True, tag="bzero")
