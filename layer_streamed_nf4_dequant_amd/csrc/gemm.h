@@ -83,8 +83,16 @@ lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const RowPr
 // out[m][j] = bf16( sum_k act[m][k] * P[j][k] ), j < r   (U = X A^T, or G = dY B with P = B^T)
 lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const uint16_t *P, int r,
                           uint16_t *out, hipStream_t s);
-// dst [cols][rows] = src [rows][cols]^T (small bf16 matrices: B -> B^T, A -> A^T)
-lsn_status launch_transpose(const uint16_t *src, int64_t rows, int64_t cols, uint16_t *dst, hipStream_t s);
+// up to kMaxTransposes small transposes in one launch, dst_g [cols][rows] = src_g [rows][cols]^T
+// (LoRA factors: B -> B^T, A -> A^T; first[] filled by the launcher)
+constexpr int kMaxTransposes = 16;
+struct TransposeSet {
+  int n;
+  const uint16_t *src[kMaxTransposes];
+  uint16_t *dst[kMaxTransposes];
+  int64_t rows[kMaxTransposes], cols[kMaxTransposes], first[kMaxTransposes];
+};
+lsn_status launch_transpose_many(TransposeSet set, hipStream_t s);
 // partial[c][p][j] = sum over t in chunk c of Z[t][p] * V[t][j]   (chunks of TN_CHUNK rows)
 constexpr int TN_CHUNK = 256;
 lsn_status launch_tn_partial(const uint16_t *Z, int64_t T, int64_t P, const uint16_t *V, int r,

@@ -3,7 +3,7 @@
 //
 // forward:  U = bf16(X A^T)                                  k_rowproj
 //           Y = bf16(s U B^T + X W^T)                        k_gemm NT (NF4 dequantised in LDS)
-// backward: Bt = B^T ; G = bf16(dY B)                        k_transpose, k_rowproj
+// backward: Bt = B^T (and A^T) ; G = bf16(dY B)             k_transpose_many, k_rowproj
 //           dX = s G A + dY W                                k_gemm NN (NF4 or bf16 W[N][K]), or
 //                                                            k_gemm_direct NT on W^T[K][N] with A^T
 //                                                            (bf16 store or fp32 add)
@@ -341,12 +341,26 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
   if ((st = require_gfx950()) != LSN_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   const int64_t nc = (T + TN_CHUNK - 1) / TN_CHUNK;
-  if ((st = launch_transpose(L->B, N, r, need.Bt, s)) != LSN_OK) return st;
+  {
+    TransposeSet ts{};
+    ts.src[0] = L->B;
+    ts.dst[0] = need.Bt;
+    ts.rows[0] = N;
+    ts.cols[0] = r;
+    ts.n = 1;
+    if (L->W.kind == LSN_W_BF16_T) {
+      ts.src[1] = L->A;
+      ts.dst[1] = need.At;
+      ts.rows[1] = r;
+      ts.cols[1] = K;
+      ts.n = 2;
+    }
+    if ((st = launch_transpose_many(ts, s)) != LSN_OK) return st;
+  }
   if ((st = launch_rowproj(dY, T, N, need.Bt, (int)r, need.G, s)) != LSN_OK) return st;
   const int epi = dx_mode == LSN_DX_F32_ADD ? EPI_F32_ADD : EPI_BF16;
   if (L->W.kind == LSN_W_BF16_T) {
     // dX = dY (W^T)^T + s G (A^T)^T: an NT product over N with both operands N-contiguous
-    if ((st = launch_transpose(L->A, r, K, need.At, s)) != LSN_OK) return st;
     DirectArgs d{};
     d.M = T;
     d.K = N;
@@ -476,13 +490,23 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
   d.r = (int)r;
   d.scale = L[0].scale;
   d.adapters = 1;
+  TransposeSet ts{};
+  for (int g = 0; g < n; ++g) {
+    part[g] = bwd_layout(w, T, K, L[g].N, r);
+    w += part[g].bytes;
+    ts.src[ts.n] = L[g].B;
+    ts.dst[ts.n] = part[g].Bt;
+    ts.rows[ts.n] = L[g].N;
+    ts.cols[ts.n++] = r;
+    ts.src[ts.n] = L[g].A;
+    ts.dst[ts.n] = part[g].At;
+    ts.rows[ts.n] = r;
+    ts.cols[ts.n++] = K;
+  }
+  if ((st = launch_transpose_many(ts, s)) != LSN_OK) return st;
   for (int g = 0; g < n; ++g) {
     const int64_t N = L[g].N;
-    part[g] = bwd_layout(w, T, K, N, r);
-    w += part[g].bytes;
-    if ((st = launch_transpose(L[g].B, N, r, part[g].Bt, s)) != LSN_OK) return st;
     if ((st = launch_rowproj(dY[g], T, N, part[g].Bt, (int)r, part[g].G, s)) != LSN_OK) return st;
-    if ((st = launch_transpose(L[g].A, r, K, part[g].At, s)) != LSN_OK) return st;
     d.kseg[g].act = dY[g];
     d.kseg[g].w = L[g].W.bf16;
     d.kseg[g].K = N;

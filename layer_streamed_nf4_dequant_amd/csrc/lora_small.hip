@@ -109,14 +109,20 @@ __global__ __launch_bounds__(256) void k_rowproj(const uint16_t *__restrict__ ac
   }
 }
 
-// dst[c][r] = src[r][c] for a small bf16 matrix (a LoRA factor): one element per thread
-__global__ __launch_bounds__(256) void k_transpose(const uint16_t *__restrict__ src, int64_t rows, int64_t cols,
-                                                   uint16_t *__restrict__ dst) {
+// several small transposes in one launch (a layer's B -> B^T and A -> A^T): job g owns the
+// elements [first[g], first[g] + rows[g] * cols[g]) of the flattened index space
+__global__ __launch_bounds__(256) void k_transpose_many(TransposeSet set) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * cols) return;
-  const int64_t r = i / cols, c = i % cols;
-  dst[c * rows + r] = src[i];
+  int g = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxTransposes; ++q)
+    if (q < set.n && i >= set.first[q]) g = q;
+  const int64_t li = i - set.first[g];
+  if (li >= set.rows[g] * set.cols[g]) return;
+  const int64_t r = li / set.cols[g], c = li % set.cols[g];
+  set.dst[g][c * set.rows[g] + r] = set.src[g][li];
 }
+
 
 // ---------------------------------------------------------------------------------------------
 // split-T partial products: partial[c][p][j] = sum over t in chunk c (TN_CHUNK = 256 rows) of
@@ -290,10 +296,16 @@ lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const uint1
   return launch_rowproj(act, M, K, set, s);
 }
 
-lsn_status launch_transpose(const uint16_t *src, int64_t rows, int64_t cols, uint16_t *dst, hipStream_t s) {
-  hipLaunchKernelGGL(k_transpose, dim3((unsigned)((rows * cols + 255) / 256)), dim3(256), 0, s, src, rows, cols,
-                     dst);
-  return check_hip(hipGetLastError(), "k_transpose launch");
+
+lsn_status launch_transpose_many(TransposeSet set, hipStream_t s) {
+  int64_t total = 0;
+  for (int g = 0; g < set.n; ++g) {
+    set.first[g] = total;
+    total += set.rows[g] * set.cols[g];
+  }
+  if (total == 0) return LSN_OK;
+  hipLaunchKernelGGL(k_transpose_many, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, set);
+  return check_hip(hipGetLastError(), "k_transpose_many launch");
 }
 
 lsn_status launch_tn_partial(const uint16_t *Z, int64_t T, int64_t P, const uint16_t *V, int r, float *partial,
