@@ -12,9 +12,10 @@ the backward (dX, dA, dB). Inputs are seeded synthetic tensors resident in HBM (
 pinned host memory, as the method keeps it) before the timed region starts.
 
 Prints one JSON line. `value` = T * steps / wall time of the K timed steps. `roofline` is the
-dominant kernel, the fused NF4-dequant forward GEMM (k_gemm NT/NF4): achieved = algorithmic
-FLOPs of its launches in the timed steps / their summed durations, measured with HIP events
-recorded around every launch on the compute stream. `cpu_baseline` times the CPU oracle on a
+dominant kernel, the forward/recompute GEMM (k_gemm_direct on the staged bf16 W, LoRA term in its
+prologue): achieved = algorithmic FLOPs of its launches in the timed steps / their summed
+durations, measured with HIP events recorded around every launch on the compute stream; traffic =
+the calibrated byte counters of the same launches from the committed profile summary. `cpu_baseline` times the CPU oracle on a
 bounded sample (one layer, a subset of token rows) and scales it to the workload.
 """
 
