@@ -21,74 +21,86 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4_t v) { return __builtin_bit_ca
 // ---------------------------------------------------------------------------------------------
 // row projections sharing one activation: out_g[m][j] = bf16( sum_k act[m][k] P_g[j][k] ), j < r_g,
 // for up to 8 low-rank matrices P_g (ranks multiples of 8, total <= 128), so act is read once.
-// One 256-thread workgroup per 16 rows; wave w takes the 32-wide K-steps w, w+4, w+8, ...; the
-// four partial results are added in wave order through LDS. Column block cb (16 columns of the
-// concatenated P) is one MFMA 16x16x32 accumulator.
-// The work per K-step is tiny (one activation fragment, NBMAX weight fragments, NBMAX MFMAs), so
-// the loop is latency-bound unless many loads are in flight: each wave keeps the operands of
-// DEPTH K-steps in registers and issues the loads of step i + DEPTH as it consumes step i.
+// One workgroup of RP_WAVES waves per 16 rows; wave w takes the 32-wide K-steps w, w + RP_WAVES,
+// ...; the partial results are added in wave order through LDS. Column block cb (16 columns of the
+// concatenated P) is one MFMA 16x16x32 accumulator; NB is the exact number of column blocks.
+// The work per K-step is tiny (one activation fragment, NB weight fragments, NB MFMAs), so the
+// loop is latency-bound unless many loads are in flight: each wave keeps the operands of DEPTH
+// K-steps in registers and issues the loads of step i + DEPTH as it consumes step i. Every load is
+// unconditional (columns past the total read a valid row and are never stored; steps past the
+// wave's last re-read its last step), so the load counter waits stay exact.
 // ---------------------------------------------------------------------------------------------
-template <int NBMAX, int DEPTH>
-__global__ __launch_bounds__(256) void k_rowproj(const uint16_t *__restrict__ act, int64_t M, int64_t K,
-                                                 RowProjSet set) {
-  __shared__ floatx4_t part[4][NBMAX][64];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+constexpr int RP_WAVES = 8;
+template <int NB, int DEPTH>
+__global__ __launch_bounds__(64 * RP_WAVES) void k_rowproj(const uint16_t *__restrict__ act, int64_t M, int64_t K,
+                                                          RowProjSet set) {
+  __shared__ floatx4_t part[RP_WAVES][NB][64];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t m0 = (int64_t)blockIdx.x * 16;
   const int64_t m = min(m0 + (lane & 15), M - 1);      // clamped rows are never stored
   const int kq = 8 * (lane >> 4);
   const int nks = (int)(K / 32);
-  const int nblk = (set.total + 15) / 16;
-  // the concatenated row c of P: group g, local row c - start[g]
-  const uint16_t *prow[NBMAX];
-  bool pok[NBMAX];
+  // the concatenated row c of P: group g, local row c - start[g] (c clamped to the last row)
+  const uint16_t *prow[NB];
 #pragma unroll
-  for (int cb = 0; cb < NBMAX; ++cb) {
-    const int c = 16 * cb + (lane & 15);
+  for (int cb = 0; cb < NB; ++cb) {
+    const int c = min(16 * cb + (lane & 15), set.total - 1);
     int g = 0;
 #pragma unroll
     for (int q = 1; q < 8; ++q) g += (q < set.n && c >= set.start[q]) ? 1 : 0;
-    pok[cb] = cb < nblk && c < set.total;
-    prow[cb] = set.P[g] + (int64_t)(pok[cb] ? c - set.start[g] : 0) * K;
+    prow[cb] = set.P[g] + (int64_t)(c - set.start[g]) * K + kq;
   }
   const uint16_t *arow = act + m * K + kq;
-  floatx4_t acc[NBMAX];
+  floatx4_t acc[NB];
 #pragma unroll
-  for (int cb = 0; cb < NBMAX; ++cb) acc[cb] = floatx4_t{0, 0, 0, 0};
-  u32x4_t va[DEPTH], vb[DEPTH][NBMAX];
+  for (int cb = 0; cb < NB; ++cb) acc[cb] = floatx4_t{0, 0, 0, 0};
+  u32x4_t va[DEPTH], vb[DEPTH][NB];
   // K-step of this wave's i-th iteration, clamped (a clamped step is loaded but not used)
-  auto load = [&](int i, u32x4_t &a_, u32x4_t (&b_)[NBMAX]) {
-    const int64_t k = (int64_t)min(wave + 4 * i, nks - 1) * 32;
+  auto load = [&](int i, u32x4_t &a_, u32x4_t (&b_)[NB]) {
+    const int64_t k = (int64_t)min(wave + RP_WAVES * i, nks - 1) * 32;
     a_ = *reinterpret_cast<const u32x4_t *>(arow + k);
 #pragma unroll
-    for (int cb = 0; cb < NBMAX; ++cb) {
-      b_[cb] = u32x4_t{0, 0, 0, 0};
-      if (pok[cb]) b_[cb] = *reinterpret_cast<const u32x4_t *>(prow[cb] + k + kq);
-    }
+    for (int cb = 0; cb < NB; ++cb) b_[cb] = *reinterpret_cast<const u32x4_t *>(prow[cb] + k);
   };
-  const int iters = (nks - wave + 3) / 4;                // K-steps of this wave
+  const int iters = (nks - wave + RP_WAVES - 1) / RP_WAVES;   // K-steps of this wave (may be 0)
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load(d, va[d], vb[d]);
-  for (int i0 = 0; i0 < iters; i0 += DEPTH) {
+  for (int d = 0; d < DEPTH; ++d) {
+    load(d, va[d], vb[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // at least one pass, with no guard between the loads above and the loop: a guard lets the
+  // compiler sink some of those loads past it, and the load waits inside the loop then merge two
+  // different load orders and come out too strict
+  int i0 = 0;
+  do {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
-      if (i0 + d < iters) {
+      // a step past the wave's last contributes zero (a select, not a branch, so the loop body
+      // is straight-line code and its load waits are exact)
+      const uint32_t keep = i0 + d < iters ? 0xffffffffu : 0u;
+      u32x4_t a_ = va[d];
 #pragma unroll
-        for (int cb = 0; cb < NBMAX; ++cb)
-          if (cb < nblk)
-            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[d]), as_bf16x8(vb[d][cb]), acc[cb], 0, 0, 0);
-      }
+      for (int e = 0; e < 4; ++e) a_[e] &= keep;
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb)
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_), as_bf16x8(vb[d][cb]), acc[cb], 0, 0, 0);
       load(i0 + d + DEPTH, va[d], vb[d]);
+      // keep the loads in program order: the scheduler would otherwise sink them to their uses
+      // and undo the pipelining
+      __builtin_amdgcn_sched_barrier(0);
     }
-  }
+    i0 += DEPTH;
+  } while (i0 < iters);
 #pragma unroll
-  for (int cb = 0; cb < NBMAX; ++cb) part[wave][cb][lane] = acc[cb];
+  for (int cb = 0; cb < NB; ++cb) part[wave][cb][lane] = acc[cb];
   __syncthreads();
-  // 4 waves finish 4 column blocks at a time; lane holds column c = 16 cb + lane % 16 and rows
+  // the waves finish the column blocks; lane holds column c = 16 cb + lane % 16 and rows
   // 4 (lane / 16) + e
-  for (int cb = wave; cb < nblk; cb += 4) {
+  for (int cb = wave; cb < NB; cb += RP_WAVES) {
     floatx4_t sum = part[0][cb][lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
+    for (int w = 1; w < RP_WAVES; ++w) {
       const floatx4_t p = part[w][cb][lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) sum[e] = __fadd_rn(sum[e], p[e]);
@@ -273,14 +285,18 @@ __global__ __launch_bounds__(256) void k_tn_reduce(const float *__restrict__ par
 }  // namespace
 
 lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const RowProjSet &set, hipStream_t s) {
-  const dim3 grid((unsigned)((M + 15) / 16));
-  const int nblk = (set.total + 15) / 16;
-  if (nblk <= 2)
-    hipLaunchKernelGGL((k_rowproj<2, 8>), grid, dim3(256), 0, s, act, M, K, set);
-  else if (nblk <= 5)
-    hipLaunchKernelGGL((k_rowproj<5, 4>), grid, dim3(256), 0, s, act, M, K, set);
-  else
-    hipLaunchKernelGGL((k_rowproj<8, 3>), grid, dim3(256), 0, s, act, M, K, set);
+  const dim3 grid((unsigned)((M + 15) / 16)), block(64 * RP_WAVES);
+  switch ((set.total + 15) / 16) {
+    case 1: hipLaunchKernelGGL((k_rowproj<1, 8>), grid, block, 0, s, act, M, K, set); break;
+    case 2: hipLaunchKernelGGL((k_rowproj<2, 6>), grid, block, 0, s, act, M, K, set); break;
+    case 3: hipLaunchKernelGGL((k_rowproj<3, 4>), grid, block, 0, s, act, M, K, set); break;
+    case 4: hipLaunchKernelGGL((k_rowproj<4, 4>), grid, block, 0, s, act, M, K, set); break;
+    case 5: hipLaunchKernelGGL((k_rowproj<5, 3>), grid, block, 0, s, act, M, K, set); break;
+    case 6: hipLaunchKernelGGL((k_rowproj<6, 3>), grid, block, 0, s, act, M, K, set); break;
+    case 7: hipLaunchKernelGGL((k_rowproj<7, 2>), grid, block, 0, s, act, M, K, set); break;
+    case 8: hipLaunchKernelGGL((k_rowproj<8, 2>), grid, block, 0, s, act, M, K, set); break;
+    default: return LSN_E_ARG;
+  }
   return check_hip(hipGetLastError(), "k_rowproj launch");
 }
 

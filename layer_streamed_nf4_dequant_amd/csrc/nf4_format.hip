@@ -198,17 +198,16 @@ __global__ __launch_bounds__(256) void k_dequant(DqJobs jobs, Nf4KernelTable tab
 // ---------------------------------------------------------------------------------------------
 // dequantise into the transposed layout: out[k][n] = w_hat[n][k] (bf16), for a backward GEMM
 // that reduces over n with both operands n-contiguous. Same arithmetic as k_dequant, so the
-// values are bit-identical. Workgroup tile: 256 rows n x 256 columns k (a whole 128-byte line of
-// codes per row), in 2 passes of 128 columns whose loads are all issued up front: thread t
-// decodes rows n0 + 8 (t % 32) .. +7 at columns k0 + 16 (t / 32) .. +15 of the pass (8 code
-// bytes per row, one 64-weight block), then stores each of its 16 columns as 8 consecutive n
-// (16 bytes), so 32 lanes write a 512-byte run of one out row. Tiles walk n fastest:
-// neighbouring workgroups write neighbouring runs of the same out rows, which keeps the pages
-// (and translations) they touch few; in k order an out row is 2 x rows bytes long and a run of
-// tiles would touch every page of the output.
+// values are bit-identical. Workgroup tile: 64 rows n x 512 columns k, one pass: thread t decodes
+// rows n0 + 8 (t % 8) .. +7 at columns k0 + 16 (t / 8) .. +15 (8 code bytes per row, inside one
+// 64-weight block), then stores each of its 16 columns as 8 consecutive n (16 bytes), so 8 lanes
+// write one whole 128-byte line of an out row and a wave instruction covers 8 out rows. Tiles
+// walk n fastest. Measured against wider tiles (512-byte and longer row runs per tile) after a
+// layer's row-major dequant, as the backward visit runs them, this shape writes fastest: the
+// output lines in flight spread over many rows instead of long runs of few.
 // Requires rows % 8 == 0 (checked by the caller); cols % 64 == 0 by the format.
 // ---------------------------------------------------------------------------------------------
-constexpr int kDqtRows = 256, kDqtCols = 256;
+constexpr int kDqtRows = 64, kDqtCols = 512;
 __host__ __device__ inline int64_t dqt_tiles(int64_t rows, int64_t cols) {
   return ((rows + kDqtRows - 1) / kDqtRows) * ((cols + kDqtCols - 1) / kDqtCols);
 }
@@ -222,17 +221,19 @@ __global__ __launch_bounds__(256) void k_dequant_t(DqJobs jobs, Nf4KernelTable t
   const DqJob &J = jobs.job[find_job(jobs, blockIdx.x)];
   const int64_t tile = (int64_t)blockIdx.x - J.wg0;
   const int64_t rows = J.rows, cols = J.cols;
+  // threads: kDqtRows / 8 along n (8 rows each), the rest along k (16 columns per pass)
+  constexpr int NG = kDqtRows / 8, KG = 256 / NG, KSTRIDE = 16 * KG;
   const int64_t ntn = (rows + kDqtRows - 1) / kDqtRows;
-  const int64_t n = (tile % ntn) * kDqtRows + 8 * (t & 31);
-  const int64_t kbase = (tile / ntn) * kDqtCols + 16 * (t >> 5);
+  const int64_t n = (tile % ntn) * kDqtRows + 8 * (t % NG);
+  const int64_t kbase = (tile / ntn) * kDqtCols + 16 * (t / NG);
   const bool row_ok = n < rows;
-  constexpr int NP = kDqtCols / 128;
+  constexpr int NP = kDqtCols / KSTRIDE;
   uint2 word[NP][8];
   int v[NP][8];
   float s2[NP][8];
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps) {
-    const int64_t k = kbase + 128 * ps;
+    const int64_t k = kbase + KSTRIDE * ps;
     const bool ok = row_ok && k < cols;              // whole 64-column blocks: cols % 64 == 0
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(256) void k_dequant_t(DqJobs jobs, Nf4KernelTable t
   uint16_t *out = reinterpret_cast<uint16_t *>(J.out);
 #pragma unroll
   for (int ps = 0; ps < NP; ++ps) {
-    const int64_t k = kbase + 128 * ps;
+    const int64_t k = kbase + KSTRIDE * ps;
     if (!row_ok || k >= cols) continue;
     float c[8];
 #pragma unroll
