@@ -80,6 +80,18 @@ struct RowProjSet {
   int start[8];           // first concatenated column of matrix g
 };
 lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const RowProjSet &set, hipStream_t s);
+// up to 8 row-projection jobs with activations of their own, one launch (all jobs: the same M and
+// the same number of 16-column blocks)
+struct RowProjJob {
+  const uint16_t *act;    // [M][K]
+  int64_t K;
+  RowProjSet set;
+};
+struct RowProjJobs {
+  int n;
+  RowProjJob job[8];
+};
+lsn_status launch_rowproj_jobs(int64_t M, const RowProjJobs &jobs, hipStream_t s);
 // out[m][j] = bf16( sum_k act[m][k] * P[j][k] ), j < r   (U = X A^T, or G = dY B with P = B^T)
 lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const uint16_t *P, int r,
                           uint16_t *out, hipStream_t s);
@@ -100,5 +112,35 @@ lsn_status launch_tn_partial(const uint16_t *Z, int64_t T, int64_t P, const uint
 // out = s * sum_c partial[c] (fixed order), set or accumulate; transposed: out[j][p], else out[p][j]
 lsn_status launch_tn_reduce(const float *partial, int64_t n_chunks, int64_t P, int r, float scale,
                             int accumulate, int transposed, float *out, hipStream_t s);
+// several split-T partial products (all with the same T), then several reductions, one launch
+// each; every job computes exactly what the single-job launch computes
+constexpr int kMaxTn = 2 * kMaxSegs;
+struct TnJob {
+  const uint16_t *Z;      // [T][P]
+  int64_t P;
+  const uint16_t *V;      // [T][r]
+  int r;
+  float *partial;         // [T / TN_CHUNK][P][r]
+  int64_t wg0;            // first workgroup (filled by the launcher)
+};
+struct TnJobs {
+  int n;
+  TnJob job[kMaxTn];
+};
+lsn_status launch_tn_partial_jobs(int64_t T, TnJobs jobs, hipStream_t s);
+struct TnRedJob {
+  const float *partial;
+  int64_t P;
+  int r;
+  float scale;
+  int accumulate, transposed;
+  float *out;
+  int64_t i0;             // first element of the flattened index space (filled by the launcher)
+};
+struct TnRedJobs {
+  int n;
+  TnRedJob job[kMaxTn];
+};
+lsn_status launch_tn_reduce_jobs(int64_t n_chunks, TnRedJobs jobs, hipStream_t s);
 
 }  // namespace lsn

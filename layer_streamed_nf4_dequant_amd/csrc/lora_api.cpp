@@ -389,11 +389,19 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
     if ((st = launch_gemm(GEMM_NN, L->W.kind == LSN_W_NF4 ? W_IS_NF4 : W_IS_BF16, epi, a, s)) != LSN_OK)
       return st;
   }
+  // dB = s dY^T U and dA = s G^T X (stored as A's [r][K]): both partials in one launch, then both
+  // reductions in one launch
   const int acc = grad_mode == LSN_GRAD_ADD;
-  if ((st = launch_tn_partial(dY, T, N, U, (int)r, need.part_dB, s)) != LSN_OK) return st;
-  if ((st = launch_tn_reduce(need.part_dB, nc, N, (int)r, L->scale, acc, 0, dB, s)) != LSN_OK) return st;
-  if ((st = launch_tn_partial(X, T, K, need.G, (int)r, need.part_dA, s)) != LSN_OK) return st;
-  return launch_tn_reduce(need.part_dA, nc, K, (int)r, L->scale, acc, 1, dA, s);
+  TnJobs tj{};
+  tj.n = 2;
+  tj.job[0] = TnJob{dY, N, U, (int)r, need.part_dB, 0};
+  tj.job[1] = TnJob{X, K, need.G, (int)r, need.part_dA, 0};
+  if ((st = launch_tn_partial_jobs(T, tj, s)) != LSN_OK) return st;
+  TnRedJobs rj{};
+  rj.n = 2;
+  rj.job[0] = TnRedJob{need.part_dB, N, (int)r, L->scale, acc, 0, dB, 0};
+  rj.job[1] = TnRedJob{need.part_dA, K, (int)r, L->scale, acc, 1, dA, 0};
+  return launch_tn_reduce_jobs(nc, rj, s);
 }
 
 size_t lora_linear_group_ws_bytes(int32_t n, const lsn_lora_linear *L) {
@@ -504,26 +512,41 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
     ts.cols[ts.n++] = K;
   }
   if ((st = launch_transpose_many(ts, s)) != LSN_OK) return st;
+  RowProjJobs gj{};
+  gj.n = n;
   for (int g = 0; g < n; ++g) {
     const int64_t N = L[g].N;
-    if ((st = launch_rowproj(dY[g], T, N, part[g].Bt, (int)r, part[g].G, s)) != LSN_OK) return st;
+    RowProjJob &J = gj.job[g];
+    J.act = dY[g];
+    J.K = N;
+    J.set.n = 1;
+    J.set.total = (int)r;
+    J.set.P[0] = part[g].Bt;
+    J.set.out[0] = part[g].G;
+    J.set.r[0] = (int)r;
     d.kseg[g].act = dY[g];
     d.kseg[g].w = L[g].W.bf16;
     d.kseg[g].K = N;
     d.kseg[g].lr_act = part[g].G;
     d.kseg[g].lr_w = part[g].At;
   }
+  // every member's G in one launch
+  if ((st = launch_rowproj_jobs(T, gj, s)) != LSN_OK) return st;
   if ((st = launch_gemm_direct(d, dx_mode == LSN_DX_F32_ADD ? EPI_F32_ADD : EPI_BF16, s)) != LSN_OK) return st;
+  // every member's dB and dA partials in one launch, then every reduction in one launch
   const int64_t nc = (T + TN_CHUNK - 1) / TN_CHUNK;
   const int acc = grad_mode == LSN_GRAD_ADD;
+  TnJobs tj{};
+  TnRedJobs rj{};
   for (int g = 0; g < n; ++g) {
     const int64_t N = L[g].N;
-    if ((st = launch_tn_partial(dY[g], T, N, U[g], (int)r, part[g].part_dB, s)) != LSN_OK) return st;
-    if ((st = launch_tn_reduce(part[g].part_dB, nc, N, (int)r, L[g].scale, acc, 0, dB[g], s)) != LSN_OK) return st;
-    if ((st = launch_tn_partial(X, T, K, part[g].G, (int)r, part[g].part_dA, s)) != LSN_OK) return st;
-    if ((st = launch_tn_reduce(part[g].part_dA, nc, K, (int)r, L[g].scale, acc, 1, dA[g], s)) != LSN_OK) return st;
+    tj.job[tj.n++] = TnJob{dY[g], N, U[g], (int)r, part[g].part_dB, 0};
+    tj.job[tj.n++] = TnJob{X, K, part[g].G, (int)r, part[g].part_dA, 0};
+    rj.job[rj.n++] = TnRedJob{part[g].part_dB, N, (int)r, L[g].scale, acc, 0, dB[g], 0};
+    rj.job[rj.n++] = TnRedJob{part[g].part_dA, K, (int)r, L[g].scale, acc, 1, dA[g], 0};
   }
-  return LSN_OK;
+  if ((st = launch_tn_partial_jobs(T, tj, s)) != LSN_OK) return st;
+  return launch_tn_reduce_jobs(nc, rj, s);
 }
 
 }  // extern "C"

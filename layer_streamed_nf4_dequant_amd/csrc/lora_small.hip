@@ -21,6 +21,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4_t v) { return __builtin_bit_ca
 // ---------------------------------------------------------------------------------------------
 // row projections sharing one activation: out_g[m][j] = bf16( sum_k act[m][k] P_g[j][k] ), j < r_g,
 // for up to 8 low-rank matrices P_g (ranks multiples of 8, total <= 128), so act is read once.
+// Several jobs (activations of their own, the same M) run as grid rows of one launch.
 // One workgroup of RP_WAVES waves per 16 rows; wave w takes the 32-wide K-steps w, w + RP_WAVES,
 // ...; the partial results are added in wave order through LDS. Column block cb (16 columns of the
 // concatenated P) is one MFMA 16x16x32 accumulator; NB is the exact number of column blocks.
@@ -32,9 +33,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4_t v) { return __builtin_bit_ca
 // ---------------------------------------------------------------------------------------------
 constexpr int RP_WAVES = 8;
 template <int NB, int DEPTH>
-__global__ __launch_bounds__(64 * RP_WAVES) void k_rowproj(const uint16_t *__restrict__ act, int64_t M, int64_t K,
-                                                          RowProjSet set) {
+__global__ __launch_bounds__(64 * RP_WAVES) void k_rowproj(int64_t M, RowProjJobs jobs) {
   __shared__ floatx4_t part[RP_WAVES][NB][64];
+  // job blockIdx.y: its own activation [M][K] and matrices
+  const RowProjJob &J = jobs.job[blockIdx.y];
+  const uint16_t *__restrict__ act = J.act;
+  const int64_t K = J.K;
+  const RowProjSet &set = J.set;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t m0 = (int64_t)blockIdx.x * 16;
@@ -163,15 +168,27 @@ __device__ __forceinline__ void transpose8(const uint32_t (&in)[8][4], u32x4_t (
   }
 }
 
+// Several jobs in one launch: job g owns workgroups wg0 .. wg0 + (its column blocks x chunks) - 1,
+// column block fastest.
 template <bool WIDE>   // r > 16: two 16-column blocks of V
-__global__ __launch_bounds__(256) void k_tn_partial(const uint16_t *__restrict__ Z, int64_t T, int64_t P,
-                                                    const uint16_t *__restrict__ V, int r,
-                                                    float *__restrict__ partial) {
+__global__ __launch_bounds__(256) void k_tn_partial(int64_t T, TnJobs jobs) {
   __shared__ __attribute__((aligned(16))) char zt[TN_COLS * TPITCH];
   __shared__ __attribute__((aligned(16))) char vt[32 * TPITCH];
+  int g = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxTn; ++q)
+    if (q < jobs.n && (int64_t)blockIdx.x >= jobs.job[q].wg0) g = q;
+  const TnJob &J = jobs.job[g];
+  const uint16_t *__restrict__ Z = J.Z;
+  const uint16_t *__restrict__ V = J.V;
+  const int64_t P = J.P;
+  const int r = J.r;
+  float *__restrict__ partial = J.partial;
+  const int64_t npb = (P + TN_COLS - 1) / TN_COLS;
+  const int64_t local = (int64_t)blockIdx.x - J.wg0;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int64_t p0 = (int64_t)blockIdx.x * TN_COLS;
-  const int64_t c = blockIdx.y;
+  const int64_t p0 = (local % npb) * TN_COLS;
+  const int64_t c = local / npb;
   const int64_t t0 = c * TN_CHUNK;
   const int cg = t & 31, rg = t >> 5;         // Z: columns p0 + 8 cg .. +7, rows 8 rg .. +7 of a block
   const bool col_ok = p0 + 8 * cg < P;
@@ -269,10 +286,21 @@ __global__ __launch_bounds__(256) void k_tn_partial(const uint16_t *__restrict__
     }
 }
 
-__global__ __launch_bounds__(256) void k_tn_reduce(const float *__restrict__ partial, int64_t n_chunks,
-                                                   int64_t P, int r, float scale, int accumulate,
-                                                   int transposed, float *__restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // index p * r + j
+// job g owns the elements i0 .. i0 + P r - 1 of the flattened index space (whole workgroups)
+__global__ __launch_bounds__(256) void k_tn_reduce(int64_t n_chunks, TnRedJobs jobs) {
+  const int64_t b = (int64_t)blockIdx.x * 256;
+  int g = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxTn; ++q)
+    if (q < jobs.n && b >= jobs.job[q].i0) g = q;
+  const TnRedJob &J = jobs.job[g];
+  const float *__restrict__ partial = J.partial;
+  const int64_t P = J.P;
+  const int r = J.r;
+  const float scale = J.scale;
+  float *__restrict__ out = J.out;
+  const int accumulate = J.accumulate, transposed = J.transposed;
+  const int64_t i = b - J.i0 + threadIdx.x;   // index p * r + j
   if (i >= P * r) return;
   float s = partial[i];
   for (int64_t c = 1; c < n_chunks; ++c) s = __fadd_rn(s, partial[c * P * r + i]);
@@ -284,20 +312,33 @@ __global__ __launch_bounds__(256) void k_tn_reduce(const float *__restrict__ par
 
 }  // namespace
 
-lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const RowProjSet &set, hipStream_t s) {
-  const dim3 grid((unsigned)((M + 15) / 16)), block(64 * RP_WAVES);
-  switch ((set.total + 15) / 16) {
-    case 1: hipLaunchKernelGGL((k_rowproj<1, 8>), grid, block, 0, s, act, M, K, set); break;
-    case 2: hipLaunchKernelGGL((k_rowproj<2, 6>), grid, block, 0, s, act, M, K, set); break;
-    case 3: hipLaunchKernelGGL((k_rowproj<3, 4>), grid, block, 0, s, act, M, K, set); break;
-    case 4: hipLaunchKernelGGL((k_rowproj<4, 4>), grid, block, 0, s, act, M, K, set); break;
-    case 5: hipLaunchKernelGGL((k_rowproj<5, 3>), grid, block, 0, s, act, M, K, set); break;
-    case 6: hipLaunchKernelGGL((k_rowproj<6, 3>), grid, block, 0, s, act, M, K, set); break;
-    case 7: hipLaunchKernelGGL((k_rowproj<7, 2>), grid, block, 0, s, act, M, K, set); break;
-    case 8: hipLaunchKernelGGL((k_rowproj<8, 2>), grid, block, 0, s, act, M, K, set); break;
+lsn_status launch_rowproj_jobs(int64_t M, const RowProjJobs &jobs, hipStream_t s) {
+  if (jobs.n < 1 || jobs.n > 8) return LSN_E_ARG;
+  const int nb = (jobs.job[0].set.total + 15) / 16;
+  for (int g = 1; g < jobs.n; ++g)
+    if ((jobs.job[g].set.total + 15) / 16 != nb) return LSN_E_ARG;
+  const dim3 grid((unsigned)((M + 15) / 16), (unsigned)jobs.n), block(64 * RP_WAVES);
+  switch (nb) {
+    case 1: hipLaunchKernelGGL((k_rowproj<1, 8>), grid, block, 0, s, M, jobs); break;
+    case 2: hipLaunchKernelGGL((k_rowproj<2, 6>), grid, block, 0, s, M, jobs); break;
+    case 3: hipLaunchKernelGGL((k_rowproj<3, 4>), grid, block, 0, s, M, jobs); break;
+    case 4: hipLaunchKernelGGL((k_rowproj<4, 4>), grid, block, 0, s, M, jobs); break;
+    case 5: hipLaunchKernelGGL((k_rowproj<5, 3>), grid, block, 0, s, M, jobs); break;
+    case 6: hipLaunchKernelGGL((k_rowproj<6, 3>), grid, block, 0, s, M, jobs); break;
+    case 7: hipLaunchKernelGGL((k_rowproj<7, 2>), grid, block, 0, s, M, jobs); break;
+    case 8: hipLaunchKernelGGL((k_rowproj<8, 2>), grid, block, 0, s, M, jobs); break;
     default: return LSN_E_ARG;
   }
   return check_hip(hipGetLastError(), "k_rowproj launch");
+}
+
+lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const RowProjSet &set, hipStream_t s) {
+  RowProjJobs jobs{};
+  jobs.n = 1;
+  jobs.job[0].act = act;
+  jobs.job[0].K = K;
+  jobs.job[0].set = set;
+  return launch_rowproj_jobs(M, jobs, s);
 }
 
 lsn_status launch_rowproj(const uint16_t *act, int64_t M, int64_t K, const uint16_t *P, int r, uint16_t *out,
@@ -324,22 +365,48 @@ lsn_status launch_transpose_many(TransposeSet set, hipStream_t s) {
   return check_hip(hipGetLastError(), "k_transpose_many launch");
 }
 
+lsn_status launch_tn_partial_jobs(int64_t T, TnJobs jobs, hipStream_t s) {
+  if (jobs.n < 1 || jobs.n > kMaxTn) return LSN_E_ARG;
+  const int64_t n_chunks = (T + TN_CHUNK - 1) / TN_CHUNK;
+  int64_t wg = 0;
+  bool wide = false;
+  for (int g = 0; g < jobs.n; ++g) {
+    jobs.job[g].wg0 = wg;
+    wg += ((jobs.job[g].P + TN_COLS - 1) / TN_COLS) * n_chunks;
+    wide = wide || jobs.job[g].r > 16;
+  }
+  if (wide)
+    hipLaunchKernelGGL(k_tn_partial<true>, dim3((unsigned)wg), dim3(256), 0, s, T, jobs);
+  else
+    hipLaunchKernelGGL(k_tn_partial<false>, dim3((unsigned)wg), dim3(256), 0, s, T, jobs);
+  return check_hip(hipGetLastError(), "k_tn_partial launch");
+}
+
 lsn_status launch_tn_partial(const uint16_t *Z, int64_t T, int64_t P, const uint16_t *V, int r, float *partial,
                              hipStream_t s) {
-  const int64_t n_chunks = (T + TN_CHUNK - 1) / TN_CHUNK;
-  const dim3 grid((unsigned)((P + TN_COLS - 1) / TN_COLS), (unsigned)n_chunks);
-  if (r > 16)
-    hipLaunchKernelGGL(k_tn_partial<true>, grid, dim3(256), 0, s, Z, T, P, V, r, partial);
-  else
-    hipLaunchKernelGGL(k_tn_partial<false>, grid, dim3(256), 0, s, Z, T, P, V, r, partial);
-  return check_hip(hipGetLastError(), "k_tn_partial launch");
+  TnJobs jobs{};
+  jobs.n = 1;
+  jobs.job[0] = TnJob{Z, P, V, r, partial, 0};
+  return launch_tn_partial_jobs(T, jobs, s);
+}
+
+lsn_status launch_tn_reduce_jobs(int64_t n_chunks, TnRedJobs jobs, hipStream_t s) {
+  if (jobs.n < 1 || jobs.n > kMaxTn) return LSN_E_ARG;
+  int64_t i0 = 0;
+  for (int g = 0; g < jobs.n; ++g) {
+    jobs.job[g].i0 = i0;
+    i0 += (jobs.job[g].P * jobs.job[g].r + 255) / 256 * 256;     // whole workgroups per job
+  }
+  hipLaunchKernelGGL(k_tn_reduce, dim3((unsigned)(i0 / 256)), dim3(256), 0, s, n_chunks, jobs);
+  return check_hip(hipGetLastError(), "k_tn_reduce launch");
 }
 
 lsn_status launch_tn_reduce(const float *partial, int64_t n_chunks, int64_t P, int r, float scale,
                             int accumulate, int transposed, float *out, hipStream_t s) {
-  hipLaunchKernelGGL(k_tn_reduce, dim3((unsigned)((P * r + 255) / 256)), dim3(256), 0, s, partial, n_chunks, P,
-                     r, scale, accumulate, transposed, out);
-  return check_hip(hipGetLastError(), "k_tn_reduce launch");
+  TnRedJobs jobs{};
+  jobs.n = 1;
+  jobs.job[0] = TnRedJob{partial, P, r, scale, accumulate, transposed, out, 0};
+  return launch_tn_reduce_jobs(n_chunks, jobs, s);
 }
 
 }  // namespace lsn
