@@ -188,9 +188,22 @@ def main():
             d_ms += e0.elapsed_time(e1)
             d_bytes += (2 if transposed else 1) * (nf4_b + 2 * n_params)
         gbs = d_bytes / (d_ms * 1e-3) / 1e9
+        # each kernel on its own: the row-major staging runs on every visit; the backward visit
+        # adds the transposed one (events of the backward visit cover both launches)
+        fwd = [e0.elapsed_time(e1) for tr, e0, e1 in dequant_events if not tr]
+        bwd = [e0.elapsed_time(e1) for tr, e0, e1 in dequant_events if tr]
+        per_kernel = {}
+        if fwd:
+            rm_gbs = len(fwd) * (nf4_b + 2 * n_params) / (sum(fwd) * 1e-3) / 1e9
+            per_kernel["k_dequant (forward visits)"] = {"achieved": round(rm_gbs, 1), "frac": round(rm_gbs / PEAK_HBM_GBS, 4)}
+        if bwd:
+            pair_gbs = len(bwd) * 2 * (nf4_b + 2 * n_params) / (sum(bwd) * 1e-3) / 1e9
+            per_kernel["k_dequant + k_dequant_t (backward visits)"] = {"achieved": round(pair_gbs, 1),
+                                                                       "frac": round(pair_gbs / PEAK_HBM_GBS, 4)}
         dequant = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": round(gbs / PEAK_HBM_GBS, 4), "kernels": "k_dequant + k_dequant_t (per-visit staging)",
-                   "bytes_per_param": round(nf4_b / n_params + 2, 4), "visits": len(dequant_events)}
+                   "bytes_per_param": round(nf4_b / n_params + 2, 4), "visits": len(dequant_events),
+                   "by_visit": per_kernel}
 
     other = {}
     if not args.no_other_modes:
