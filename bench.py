@@ -62,6 +62,64 @@ def traffic_from_profiles():
         return None
 
 
+def smi_start():
+    """rocm-smi clocks and power, sampled in a child process while the timed steps run."""
+    import subprocess
+    try:
+        return subprocess.Popen(["rocm-smi", "--showclocks", "--showpower", "--json"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+
+
+def smi_finish(p):
+    import subprocess
+    if p is None:
+        return None
+    try:
+        out, _ = p.communicate(timeout=30)
+    except subprocess.TimeoutExpired:
+        p.kill()
+        p.communicate()
+        return None
+    try:
+        d = json.loads(out)
+    except ValueError:
+        return None
+    cards = [v for v in d.values() if isinstance(v, dict)]
+    if not cards:
+        return None
+    return {k: v for k, v in cards[0].items()
+            if any(w in k.lower() for w in ("sclk", "mclk", "fclk", "socclk", "power"))}
+
+
+def hipblaslt_ceiling(cfg, iters: int = 10):
+    """Same-session reference: torch.matmul (hipBLASLt) bf16 X W^T at the stack's projection shapes
+    and T, TFLOP/s per shape (no LoRA term)."""
+    import torch
+    res = {}
+    seen = set()
+    for name, K, N in cfg.projections():
+        if (K, N) in seen:
+            continue
+        seen.add((K, N))
+        g = torch.Generator(device="cuda").manual_seed(0)
+        X = torch.randn((cfg.T, K), device="cuda", generator=g).to(torch.bfloat16)
+        W = torch.randn((N, K), device="cuda", generator=g).to(torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(X, W.t())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            torch.matmul(X, W.t())
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        res[f"{name} {K}->{N}"] = round(2 * cfg.T * K * N / (ms * 1e-3) / 1e12, 1)
+        del X, W
+    return res
+
+
 def cpu_baseline(cfg, seed: int = 0, rows: int = 32):
     """Oracle (numpy, fp64 LoRA + fp32 NF4) on one layer of the workload with `rows` token rows:
     dequant of all 7 projections twice (forward and backward visit) plus forward, recomputed
@@ -96,7 +154,16 @@ def cpu_baseline(cfg, seed: int = 0, rows: int = 32):
         del Wh
     per_layer_full_T = t_deq + (cfg.T / rows) * t_rows
     tok_s = cfg.T / (cfg.layers * per_layer_full_T)
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    n_params = sum(K * N for _, K, N in cfg.projections())
+    deq_bytes = 2 * (cfg.nf4_bytes_per_layer() + 2 * n_params)
     return {"value": round(tok_s, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model, "dequant_GBs": round(deq_bytes / t_deq / 1e9, 3),
             "sample": (f"1 of {cfg.layers} layers, {rows} of {cfg.T} token rows: NF4 dequant of all 7 "
                        f"projections twice ({t_deq:.2f} s) + fp64 fwd/recompute/bwd on the sampled rows "
                        f"({t_rows:.2f} s); derived tokens/s = T / (L * (t_dequant + T/rows * t_rows))")}
@@ -118,8 +185,8 @@ def main():
                          "known size, to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the method streams one GPU's layers; see DESIGN.md for how it would shard)",
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the stack streams one GPU's layers; no sharding across GPUs is built)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -149,13 +216,17 @@ def main():
         print(f"[bench] warmup {i}: {ms:.1f} ms", flush=True)
 
     gemm_events, dequant_events = [], []
+    torch.cuda.reset_peak_memory_stats()
     torch.cuda.synchronize()
+    smi = smi_start()
     t_start = time.perf_counter()
     step_ms = []
     for i in range(args.steps):
         step_ms.append(stack.step(args.mode, gemm_events=gemm_events, dequant_events=dequant_events))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    peak_alloc = torch.cuda.max_memory_allocated()
+    clocks = smi_finish(smi)
     print(f"[bench] {args.steps} steps: {wall * 1e3 / args.steps:.1f} ms/step (events median "
           f"{sorted(step_ms)[len(step_ms) // 2]:.1f} ms)", flush=True)
 
@@ -252,6 +323,14 @@ def main():
         out["dequant"] = dequant
     if other:
         out["other_modes_tokens_per_s"] = other
+    # context for the numbers above (same session)
+    context = {"events_median_ms_per_step": round(sorted(step_ms)[len(step_ms) // 2], 2),
+               "peak_hbm_allocated_GB_during_timed_steps": round(peak_alloc / 1e9, 2)}
+    if clocks:
+        context["rocm_smi_during_timed_steps"] = clocks
+    if not args.no_other_modes:
+        context["hipblaslt_bf16_tflops_same_shapes"] = hipblaslt_ceiling(cfg)
+    out["context"] = context
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg)
