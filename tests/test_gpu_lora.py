@@ -131,18 +131,20 @@ def test_grouped_forward_equals_single_forwards(gpu, base):
         lib.lora_linear_fwd_group([cs[0].desc(), cs[1].desc()], X, [Yg[0], X], Ug[:2], ws=cs[0].ws)
 
 
+@pytest.mark.parametrize("T,r", [(300, 16), (129, 32)])
 @pytest.mark.parametrize("base", ["nf4", "bf16"])
-def test_grouped_backward(gpu, base):
+def test_grouped_backward(gpu, base, T, r):
     """Five linears sharing X (ragged T, mixed N): the grouped backward gives each member's dA,
     dB bit-identical to its own backward, and dX equal to the sum of the members' dX (one GEMM
     over the concatenated N for transposed weights; member order otherwise), matching the
-    oracle; the fp32 accumulate mode adds onto what dX held."""
+    oracle; the fp32 accumulate mode adds onto what dX held. (All members' G in one launch,
+    all dA/dB partials in one launch, all reductions in one launch.)"""
     import torch
-    T, K, r = 300, 512, 16
+    K = 512
     Ns = [512, 128, 128, 1344, 1344]
     cs = [Case(T, K, N, r=r, base=base, tag=f"gbwd{i}") for i, N in enumerate(Ns)]
     X = cs[0].Xd
-    print(f"case: grouped backward T={T} K={K} N={Ns} base={base}", flush=True)
+    print(f"case: grouped backward T={T} K={K} N={Ns} r={r} base={base}", flush=True)
     Us = []
     for c in cs:
         Y = torch.empty((T, c.N), dtype=torch.bfloat16, device="cuda")
