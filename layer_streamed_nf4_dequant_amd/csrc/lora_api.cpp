@@ -9,6 +9,8 @@
 //                                                            (bf16 store or fp32 add)
 //           dB = s sum_t dY^T U ; dA = s sum_t G^T X         k_tn_partial + k_tn_reduce
 
+#include <utility>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -512,11 +514,19 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
     ts.cols[ts.n++] = K;
   }
   if ((st = launch_transpose_many(ts, s)) != LSN_OK) return st;
+  // the G jobs run longest first (a workgroup's work grows with N), so that the short ones fill
+  // the end of the launch
+  int order[kMaxSegs];
+  for (int g = 0; g < n; ++g) order[g] = g;
+  for (int i = 1; i < n; ++i)
+    for (int j = i; j > 0 && L[order[j]].N > L[order[j - 1]].N; --j) std::swap(order[j], order[j - 1]);
+  int slot[kMaxSegs];
+  for (int i = 0; i < n; ++i) slot[order[i]] = i;
   RowProjJobs gj{};
   gj.n = n;
   for (int g = 0; g < n; ++g) {
     const int64_t N = L[g].N;
-    RowProjJob &J = gj.job[g];
+    RowProjJob &J = gj.job[slot[g]];
     J.act = dY[g];
     J.K = N;
     J.set.n = 1;
