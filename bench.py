@@ -62,35 +62,59 @@ def traffic_from_profiles():
         return None
 
 
-def smi_start():
-    """rocm-smi clocks and power, sampled in a child process while the timed steps run."""
-    import subprocess
-    try:
-        return subprocess.Popen(["rocm-smi", "--showclocks", "--showpower", "--json"], stdout=subprocess.PIPE,
-                                stderr=subprocess.DEVNULL, text=True)
-    except OSError:
+def clock_sampler():
+    """Samples the GPU's current sclk and mclk (the sysfs pp_dpm_* entry marked '*') and its
+    power reading every 50 ms in a thread while the timed steps run (no child process). Returns
+    a stop function giving the medians, or None where sysfs has no such files."""
+    import glob
+    import re
+    import threading
+    dev = next((d for d in sorted(glob.glob("/sys/class/drm/card*/device"))
+                if os.path.exists(os.path.join(d, "pp_dpm_sclk"))), None)
+    if dev is None:
+        return None
+    power = sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_average")) +
+                   glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_input")))
+    samples = {"sclk_MHz": [], "mclk_MHz": [], "power_W": []}
+    stop = threading.Event()
+
+    def current(name):
+        try:
+            with open(os.path.join(dev, name)) as f:
+                for ln in f:
+                    if ln.strip().endswith("*"):
+                        m = re.search(r"(\d+)\s*[Mm][Hh]z", ln)
+                        return int(m.group(1)) if m else None
+        except OSError:
+            return None
         return None
 
+    def run():
+        while not stop.is_set():
+            for key, name in (("sclk_MHz", "pp_dpm_sclk"), ("mclk_MHz", "pp_dpm_mclk")):
+                v = current(name)
+                if v is not None:
+                    samples[key].append(v)
+            if power:
+                try:
+                    with open(power[0]) as f:
+                        samples["power_W"].append(int(f.read()) / 1e6)
+                except (OSError, ValueError):
+                    pass
+            stop.wait(0.05)
 
-def smi_finish(p):
-    import subprocess
-    if p is None:
-        return None
-    try:
-        out, _ = p.communicate(timeout=30)
-    except subprocess.TimeoutExpired:
-        p.kill()
-        p.communicate()
-        return None
-    try:
-        d = json.loads(out)
-    except ValueError:
-        return None
-    cards = [v for v in d.values() if isinstance(v, dict)]
-    if not cards:
-        return None
-    return {k: v for k, v in cards[0].items()
-            if any(w in k.lower() for w in ("sclk", "mclk", "fclk", "socclk", "power"))}
+    th = threading.Thread(target=run, daemon=True)
+    th.start()
+
+    def finish():
+        stop.set()
+        th.join(timeout=5)
+        out = {k: sorted(v)[len(v) // 2] for k, v in samples.items() if v}
+        if out:
+            out["samples"] = max(len(v) for v in samples.values())
+            out["source"] = os.path.basename(os.path.dirname(dev)) + " sysfs"
+        return out or None
+    return finish
 
 
 def hipblaslt_ceiling(cfg, iters: int = 10):
@@ -218,7 +242,7 @@ def main():
     gemm_events, dequant_events = [], []
     torch.cuda.reset_peak_memory_stats()
     torch.cuda.synchronize()
-    smi = smi_start()
+    clocks_done = clock_sampler()
     t_start = time.perf_counter()
     step_ms = []
     for i in range(args.steps):
@@ -226,7 +250,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     peak_alloc = torch.cuda.max_memory_allocated()
-    clocks = smi_finish(smi)
+    clocks = clocks_done() if clocks_done else None
     print(f"[bench] {args.steps} steps: {wall * 1e3 / args.steps:.1f} ms/step (events median "
           f"{sorted(step_ms)[len(step_ms) // 2]:.1f} ms)", flush=True)
 
@@ -327,7 +351,7 @@ def main():
     context = {"events_median_ms_per_step": round(sorted(step_ms)[len(step_ms) // 2], 2),
                "peak_hbm_allocated_GB_during_timed_steps": round(peak_alloc / 1e9, 2)}
     if clocks:
-        context["rocm_smi_during_timed_steps"] = clocks
+        context["gpu_clocks_during_timed_steps"] = clocks
     if not args.no_other_modes:
         context["hipblaslt_bf16_tflops_same_shapes"] = hipblaslt_ceiling(cfg)
     out["context"] = context

