@@ -107,6 +107,8 @@ enum { LSN_W_NF4 = 0, LSN_W_BF16 = 1, LSN_W_BF16_T = 2 };
  * bf16 in the transposed layout W^T[K][N] (what nf4_dequant writes with LSN_OUT_BF16_T). The
  * transposed layout serves the backward only: there the product dY W reduces over N, which is
  * then the contiguous dimension of both operands; lora_linear_fwd rejects it (LSN_E_ARG).
+ * The backward reads a bf16 W[N][K] as it is (the GEMM turns its tiles in LDS), with results
+ * bit-identical to the transposed layout's, so one row-major copy serves a whole visit.
  */
 typedef struct {
   int32_t kind;           /* LSN_W_NF4, LSN_W_BF16 or LSN_W_BF16_T */
@@ -239,9 +241,10 @@ size_t lora_linear_group_ws_bytes(int32_t n, const lsn_lora_linear *L);
  *        LSN_DX_F32_ADD adds the fp32 sum into dX;
  *   dA_g, dB_g as lora_linear_bwd (LSN_GRAD_SET / LSN_GRAD_ADD), bit-identical to it.
  * L: host array of n descriptors sharing T, K, r and the scale; dY, U, dA, dB: host arrays of
- * n device pointers. With every W in the transposed bf16 layout the n dX products run as one
- * GEMM whose reduction walks the members' N in turn (one fp32 accumulator, member order);
- * otherwise the members run one after another (fp32 dX only when n > 1).
+ * n device pointers. With every W in bf16, all in the same layout (LSN_W_BF16 or
+ * LSN_W_BF16_T), the n dX products run as one GEMM whose reduction walks the members' N in
+ * turn (one fp32 accumulator, member order; the two layouts give identical bits); otherwise the
+ * members run one after another (fp32 dX only when n > 1).
  * ws: device, at least lora_linear_group_ws_bytes(n, L). Overlaps give LSN_E_ARG. Async.
  */
 lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint16_t *X,

@@ -41,7 +41,7 @@ constexpr int kMaxSegs = 8;
 struct GemmSeg {
   int64_t ntile0;          // first N tile of the segment (filled by launch_gemm_direct)
   int64_t N;
-  const uint16_t *w;       // bf16 W [N][K]
+  const uint16_t *w;       // bf16 W [N][K] (reduction-major B: [K][N])
   const uint16_t *lr_w;    // LoRA B [N][r]
   const uint16_t *lr_act;  // U [M][r]
   void *out;               // [M][N]
@@ -50,7 +50,7 @@ struct GemmSeg {
 // of the segments run back to back (each K_p % 64 == 0)
 struct KSeg {
   const uint16_t *act;     // [M][K_p]
-  const uint16_t *w;       // [N][K_p]
+  const uint16_t *w;       // [N][K_p] (reduction-major B: [K_p][N])
   int64_t K;
   const uint16_t *lr_act;  // [M][r]
   const uint16_t *lr_w;    // [N][r]
@@ -66,6 +66,7 @@ struct DirectArgs {
   int r;
   float scale;
   int adapters;
+  int b_red_major;       // B operand stored [K][N] (N contiguous) instead of [N][K]
   int scale_pow2;        // set by launch_gemm_direct
 };
 lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s);

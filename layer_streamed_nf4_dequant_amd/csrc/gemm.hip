@@ -456,6 +456,13 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs a) {
 // 8 r + (p ^ ((r ^ (r >> 3)) & 7)): a 16-lane group of a fragment read (16 consecutive rows,
 // one logical chunk) then covers all 64 four-byte banks once, and the direct writes are
 // contiguous 1 KB segments.
+// Reduction-major B (template flag BT): W is given as [K][N] (N contiguous), as a weight W[N'][K']
+// is for the input-gradient product dY W, whose reduction runs over W's rows. A stage then holds
+// 64 K-rows of 512 B (the tile's 256 N); each direct load moves two of them, and the fragment
+// reads use the gfx950 LDS transpose read (ds_read_b64_tr_b16), which hands each lane four
+// K-consecutive values of one column, so the matrix cores see the same fragments as from a
+// [N][K] operand and the result is bit-identical. 16-byte chunk c of K-row k sits at slot
+// c ^ 4 (k % 4): the four K-rows one transpose read spans then fall on different banks.
 // =============================================================================================
 constexpr int DBK = 64;
 constexpr int DTILE = 256 * DBK * 2;           // 32 KB: one operand, one stage
@@ -479,6 +486,33 @@ __device__ __forceinline__ void make_direct_rows8(DirectRows8 &d, int64_t rows, 
     const int64_t grow = min(r0 + row, rows - 1);     // clamped rows feed only unstored outputs
     d.voff[i] = (uint32_t)((grow * ld + 8 * c) * 2);
   }
+}
+
+// reduction-major B: wave w fills K-rows 16w .. 16w+15 of a 64 x 256 tile, two per load
+// (lanes 0-31 the first row, 32-63 the second; chunk slot = lane % 32). Columns past N (a ragged
+// last tile) read the next row's start, or zeros past the end of the buffer: they feed only
+// unstored outputs.
+__device__ __forceinline__ void make_direct_rows8_t(DirectRows8 &d, int64_t ld, int64_t c0, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = (wave * 8 + i) * 2 + (lane >> 5);
+    const int c = (lane & 31) ^ (4 * (row & 3));
+    d.voff[i] = (uint32_t)((row * ld + c0 + 8 * c) * 2);
+  }
+}
+
+__device__ __forceinline__ int dlds_off_t(int row, int chunk) { return row * 512 + ((chunk ^ (4 * (row & 3))) << 4); }
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// The restrict-qualified parameter gives the inlined read alias-scope metadata. Without it the
+// compiler cannot tell the read from the direct loads still landing in the other stage and waits
+// for all of them before every read; the reads of a stage are ordered after that stage's loads
+// by the explicit waits of the ring barrier, as the plain LDS reads are.
+__device__ __forceinline__ bf16x4 tr_read(lds_char_t *__restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)p);
 }
 
 __device__ __forceinline__ void issue_direct1(char *lds_tile, __amdgpu_buffer_rsrc_t rsrc, const DirectRows8 &d,
@@ -524,7 +558,7 @@ __device__ __forceinline__ void tile_coords(int64_t b, int64_t ntiles, int64_t t
   nt = in / gm;
 }
 
-template <int EPI, bool KSEG>
+template <int EPI, bool KSEG, bool BT>
 __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char *lds_a = smem;                               // 2 stages
@@ -567,13 +601,17 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     rs_a = make_rsrc(a.kseg[0].act, a.M * a.kseg[0].K * 2);
     rs_b = make_rsrc(a.kseg[0].w, sg.N * a.kseg[0].K * 2);
     make_direct_rows8(da, a.M, a.kseg[0].K, m0, wave, lane);
-    make_direct_rows8(db, sg.N, a.kseg[0].K, n0, wave, lane);
   } else {
     rs_a = make_rsrc(a.act, a.M * a.K * 2);
     rs_b = make_rsrc(sg.w, sg.N * a.K * 2);
     make_direct_rows8(da, a.M, a.K, m0, wave, lane);
-    make_direct_rows8(db, sg.N, a.K, n0, wave, lane);
   }
+  if constexpr (BT)
+    make_direct_rows8_t(db, sg.N, n0, wave, lane);   // the same for every reduction segment
+  else
+    make_direct_rows8(db, sg.N, KSEG ? a.kseg[0].K : a.K, n0, wave, lane);
+  // bytes from one K-step of B to the next
+  const int64_t b_step_bytes = BT ? (int64_t)DBK * sg.N * 2 : (int64_t)DBK * 2;
   // byte offset along K of global step `step` inside its segment (moving pa / pb forward)
   auto a_kb = [&](int step) -> uint32_t {
     if constexpr (KSEG) {
@@ -592,11 +630,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       while (pb + 1 < a.nkseg && step >= a.kseg[pb + 1].step0) {
         ++pb;
         rs_b = make_rsrc(a.kseg[pb].w, sg.N * a.kseg[pb].K * 2);
-        make_direct_rows8(db, sg.N, a.kseg[pb].K, n0, wave, lane);
+        if constexpr (!BT) make_direct_rows8(db, sg.N, a.kseg[pb].K, n0, wave, lane);
       }
-      return (uint32_t)(step - a.kseg[pb].step0) * DBK * 2;
+      return (uint32_t)((step - a.kseg[pb].step0) * b_step_bytes);
     } else {
-      return (uint32_t)step * DBK * 2;
+      return (uint32_t)(step * b_step_bytes);
     }
   };
 
@@ -669,7 +707,20 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       fa[i] = *reinterpret_cast<const bf16x8 *>(lds_a + stage * DTILE + dlds_off(wm * 128 + 32 * i + (lane & 31), chunk));
     } else {
       const int j = q - 1;
-      fb[j] = *reinterpret_cast<const bf16x8 *>(lds_b + stage * DTILE + dlds_off(wn * 128 + 32 * j + (lane & 31), chunk));
+      if constexpr (BT) {
+        // 16-lane group g: columns 16 (g % 2) .. +15 of fragment j, K-rows 8 (g / 2) + 0..3 and
+        // + 4..7 of the sub-step; source lane l of a group points at K-row l / 4, columns
+        // 4 (l % 4) .. +3, and receives column l, K-rows 0..3 of the group's block
+        const int g = lane >> 4, sl = lane & 15;
+        const int row = 16 * s2 + 8 * (g >> 1) + (sl >> 2);
+        const int c = wn * 16 + 4 * j + 2 * (g & 1) + ((sl & 3) >> 1);
+        lds_char_t *p = (lds_char_t *)(lds_b + stage * DTILE) + dlds_off_t(row, c) + 8 * (sl & 1);
+        const bf16x4 lo = tr_read(p);
+        const bf16x4 hi = tr_read(p + 4 * 512);
+        fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {
+        fb[j] = *reinterpret_cast<const bf16x8 *>(lds_b + stage * DTILE + dlds_off(wn * 128 + 32 * j + (lane & 31), chunk));
+      }
     }
   };
   // One sub-step: its 16 MFMAs on (cA, cB) in pairs; before each pair, one fragment of the
@@ -792,11 +843,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
 constexpr size_t kDirectSmemBytes = 256 * kEpiPitch > 4 * DTILE ? 256 * kEpiPitch : 4 * DTILE;
 static_assert(256 * kEpiPitch <= kDirectSmemBytes, "the epilogue tile must fit in the ring's LDS");
 
-template <int EPI, bool KSEG>
+template <int EPI, bool KSEG, bool BT>
 lsn_status launch_direct_one(const DirectArgs &a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_direct<EPI, KSEG>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_direct<EPI, KSEG, BT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDirectSmemBytes);
     if (e != hipSuccess) return check_hip(e, "gemm_direct smem attribute");
     attr_set = true;
@@ -804,7 +855,7 @@ lsn_status launch_direct_one(const DirectArgs &a, hipStream_t s) {
   int64_t ntiles_n = 0;
   for (int q = 0; q < a.nseg; ++q) ntiles_n += (a.seg[q].N + BN - 1) / BN;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ntiles_n;
-  hipLaunchKernelGGL((k_gemm_direct<EPI, KSEG>), dim3((unsigned)tiles), dim3(NT), kDirectSmemBytes, s, a);
+  hipLaunchKernelGGL((k_gemm_direct<EPI, KSEG, BT>), dim3((unsigned)tiles), dim3(NT), kDirectSmemBytes, s, a);
   return check_hip(hipGetLastError(), "k_gemm_direct launch");
 }
 
@@ -845,9 +896,17 @@ lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s) {
       step += a.kseg[p].K / DBK;
     }
     a.K = step * DBK;
-    return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, true>(a, s) : launch_direct_one<EPI_F32_ADD, true>(a, s);
+    if (a.b_red_major)
+      return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, true, true>(a, s)
+                             : launch_direct_one<EPI_F32_ADD, true, true>(a, s);
+    return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, true, false>(a, s)
+                           : launch_direct_one<EPI_F32_ADD, true, false>(a, s);
   }
-  return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, false>(a, s) : launch_direct_one<EPI_F32_ADD, false>(a, s);
+  if (a.b_red_major)
+    return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, false, true>(a, s)
+                           : launch_direct_one<EPI_F32_ADD, false, true>(a, s);
+  return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, false, false>(a, s)
+                         : launch_direct_one<EPI_F32_ADD, false, false>(a, s);
 }
 
 lsn_status launch_gemm(int layout, int wkind, int epi, GemmArgs a, hipStream_t s) {

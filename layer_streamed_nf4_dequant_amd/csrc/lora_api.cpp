@@ -350,7 +350,7 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
     ts.rows[0] = N;
     ts.cols[0] = r;
     ts.n = 1;
-    if (L->W.kind == LSN_W_BF16_T) {
+    if (L->W.kind != LSN_W_NF4) {
       ts.src[1] = L->A;
       ts.dst[1] = need.At;
       ts.rows[1] = r;
@@ -361,8 +361,9 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
   }
   if ((st = launch_rowproj(dY, T, N, need.Bt, (int)r, need.G, s)) != LSN_OK) return st;
   const int epi = dx_mode == LSN_DX_F32_ADD ? EPI_F32_ADD : EPI_BF16;
-  if (L->W.kind == LSN_W_BF16_T) {
-    // dX = dY (W^T)^T + s G (A^T)^T: an NT product over N with both operands N-contiguous
+  if (L->W.kind != LSN_W_NF4) {
+    // dX = dY W + s G (A^T)^T, a product over N: from W^T [K][N] both operands are N-contiguous;
+    // from W [N][K] the GEMM reads its B operand reduction-major (same fragments, same bits)
     DirectArgs d{};
     d.M = T;
     d.K = N;
@@ -376,6 +377,7 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
     d.r = (int)r;
     d.scale = L->scale;
     d.adapters = 1;
+    d.b_red_major = L->W.kind == LSN_W_BF16;
     if ((st = launch_gemm_direct(d, epi, s)) != LSN_OK) return st;
   } else {
     GemmArgs a = base_args(L);
@@ -421,21 +423,22 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
                                  float *const *dB, int32_t grad_mode, void *ws, size_t ws_bytes, void *stream) {
   if (n < 1 || n > kMaxSegs || !L || !dY || !U || !dA || !dB)
     return fail(LSN_E_ARG, "lora_linear_bwd_group: need 1 <= n <= %d and non-null arrays", kMaxSegs);
-  bool all_t = true;
+  // one GEMM over the members' concatenated N when every W is bf16 in the same layout
+  bool fused = L && L[0].W.kind != LSN_W_NF4;
   for (int g = 0; g < n; ++g) {
     lsn_status st = check_linear(&L[g], "lora_linear_bwd_group");
     if (st != LSN_OK) return st;
     if (L[g].T != L[0].T || L[g].K != L[0].K || L[g].r != L[0].r || L[g].scale != L[0].scale)
       return fail(LSN_E_ARG, "lora_linear_bwd_group: members must share T, K, r and the scale");
-    all_t = all_t && L[g].W.kind == LSN_W_BF16_T;
+    fused = fused && L[g].W.kind == L[0].W.kind;
   }
   if (dx_mode != LSN_DX_BF16_SET && dx_mode != LSN_DX_F32_ADD)
     return fail(LSN_E_ARG, "lora_linear_bwd_group: unknown dX mode %d", dx_mode);
   if (grad_mode != LSN_GRAD_SET && grad_mode != LSN_GRAD_ADD)
     return fail(LSN_E_ARG, "lora_linear_bwd_group: unknown gradient mode %d", grad_mode);
-  if (!all_t && dx_mode == LSN_DX_BF16_SET && n > 1)
+  if (!fused && dx_mode == LSN_DX_BF16_SET && n > 1)
     return fail(LSN_E_ARG, "lora_linear_bwd_group: a bf16 dX summed over several members needs their weights "
-                           "in the transposed bf16 layout");
+                           "in bf16, all in the same layout");
   const int64_t T = L[0].T, K = L[0].K, r = L[0].r;
   if (!X || !dX || !ws || !aligned16(X) || !aligned16(dX) || ((uintptr_t)ws & 255))
     return fail(LSN_E_ARG, "lora_linear_bwd_group: X, dX must be non-null and 16-byte, ws 256-byte aligned");
@@ -476,7 +479,7 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
   lsn_status st = require_gfx950();
   if (st != LSN_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (!all_t) {
+  if (!fused) {
     // one member at a time (fp32 accumulation into dX in member order)
     char *w = static_cast<char *>(ws);
     for (int g = 0; g < n; ++g) {
@@ -500,6 +503,7 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
   d.r = (int)r;
   d.scale = L[0].scale;
   d.adapters = 1;
+  d.b_red_major = L[0].W.kind == LSN_W_BF16;
   TransposeSet ts{};
   for (int g = 0; g < n; ++g) {
     part[g] = bwd_layout(w, T, K, L[g].N, r);

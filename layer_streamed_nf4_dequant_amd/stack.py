@@ -91,13 +91,15 @@ class Stack:
         self.dev = torch.device("cuda")
         self.layout, self.image_bytes = layer_layout(cfg)
         self.record = record
-        # "staged": each visit dequantises every NF4 projection (nf4_dequant, HBM-bound) into
-        #           bf16 staging buffers that the visit's GEMMs read: W [N][K] for the forward
-        #           and the recompute, and, on the backward visit, also W^T [K][N], so that the
-        #           dX product (a reduction over N) runs as the same direct-load NT GEMM;
-        # "fused":  the GEMMs dequantise their W tiles straight into LDS (no staging buffer).
-        # Both hand the matrix cores the same bf16 operand, so both give identical bits.
-        if dequant not in ("staged", "fused"):
+        # "staged":   each visit dequantises every NF4 projection (nf4_dequant, HBM-bound) into
+        #             bf16 staging buffers W [N][K] that all the visit's GEMMs read: the forward,
+        #             the recompute and the dX product (a reduction over N, which reads W
+        #             reduction-major);
+        # "staged_t": as "staged", but the backward visit also stages W^T [K][N] and the dX
+        #             product reads that (both operands N-contiguous);
+        # "fused":    the GEMMs dequantise their W tiles straight into LDS (no staging buffer).
+        # All three hand the matrix cores the same bf16 fragments, so all give identical bits.
+        if dequant not in ("staged", "staged_t", "fused"):
             raise ValueError(dequant)
         self.dequant = dequant if cfg.base == "nf4" else "fused"
         self.compute = torch.cuda.Stream()
@@ -170,8 +172,9 @@ class Stack:
             ws = max(ws, lib.group_ws_bytes(probe))
         self.ws = torch.empty(ws, dtype=torch.uint8, device=self.dev)
         self.w_stage = self.w_stage_t = None
-        if self.dequant == "staged":
+        if self.dequant in ("staged", "staged_t"):
             self.w_stage = [torch.empty((p.N, p.K), dtype=bf16, device=self.dev) for p in self.layout]
+        if self.dequant == "staged_t":
             self.w_stage_t = [torch.empty((p.K, p.N), dtype=bf16, device=self.dev) for p in self.layout]
 
         # ---- pool (streamed) or fixed slots (no_h2d) ----
@@ -210,18 +213,18 @@ class Stack:
         p = self.layout[j]
         return lib.NF4Desc(p.N, p.K, base + p.codes, base + p.qabsmax, base + p.absmax2, float(self.means[l, j]))
 
-    def _stage(self, base: int, l: int, s, transposed: bool = False):
+    def _stage(self, base: int, l: int, s, backward: bool = False):
         """Dequantise every projection of the layer image at `base` into the staging buffers
-        (and into the transposed ones too, for the backward visit)."""
+        (and, in "staged_t" mode on the backward visit, into the transposed ones too)."""
         descs = [self._nf4_desc(base, l, j) for j in range(len(self.layout))]
         lib.nf4_dequant_batch(descs, self.w_stage, "bf16", stream=s)
-        if transposed:
+        if backward and self.dequant == "staged_t":
             lib.nf4_dequant_batch(descs, self.w_stage_t, "bf16_t", stream=s)
 
     def _desc(self, base: int, l: int, j: int, backward: bool = False) -> lib.LoraLinearDesc:
         p, cfg = self.layout[j], self.cfg
-        if self.dequant == "staged":
-            if backward:
+        if self.dequant in ("staged", "staged_t"):
+            if backward and self.dequant == "staged_t":
                 w = lib.WeightDesc(lib.W_BF16_T, lib.NF4Desc(), self.w_stage_t[j].data_ptr())
             else:
                 w = lib.WeightDesc(lib.W_BF16, lib.NF4Desc(), self.w_stage[j].data_ptr())
@@ -305,7 +308,8 @@ class Stack:
         """One training step of the projection stack; returns its time in ms (compute stream).
         gemm_events: optional list; (projections, start, end) HIP events around every forward
         GEMM launch (one per group of projections sharing an input) are appended to it.
-        dequant_events: optional list; (transposed, start, end) around every visit's staging."""
+        dequant_events: optional list; ((visit, with_transposed), start, end) around every visit's
+        staging, visit "fwd" or "bwd", with_transposed when the visit also staged W^T."""
         torch = self.torch
         s = self.compute
         sh = s.cuda_stream
@@ -325,8 +329,8 @@ class Stack:
                     base = self.resident[l].data_ptr()
                 else:
                     base = self.slots[l % len(self.slots)].data_ptr()
-                if self.dequant == "staged":
-                    self._timed(dequant_events, False, s, lambda: self._stage(base, l, s))
+                if self.dequant != "fused":
+                    self._timed(dequant_events, ("fwd", False), s, lambda: self._stage(base, l, s))
                 self._forward_layer(base, l, self.Y, s, gemm_events)
                 if self.record:
                     self._record("fwd", l, self.Y)
@@ -342,8 +346,9 @@ class Stack:
                     base = self.resident[l].data_ptr()
                 else:
                     base = self.slots[l % len(self.slots)].data_ptr()
-                if self.dequant == "staged":                              # re-dequantised per visit
-                    self._timed(dequant_events, True, s, lambda: self._stage(base, l, s, transposed=True))
+                if self.dequant != "fused":                               # re-dequantised per visit
+                    self._timed(dequant_events, ("bwd", self.dequant == "staged_t"), s,
+                                lambda: self._stage(base, l, s, backward=True))
                 self._forward_layer(base, l, self.Yre, s, gemm_events)   # recompute
                 self._backward_layer(base, l, s)
                 if self.record:

@@ -61,6 +61,31 @@ def test_ragged_and_rank_shapes(gpu, T, K, N, r, transposed):
     _full_parity(Case(T, K, N, r=r, tag="ragged"), transposed)
 
 
+@pytest.mark.parametrize("T,K,N,r", [(300, 256, 192, 16), (777, 512, 1344, 32), (256, 64, 256, 24),
+                                     (2048, 896, 128, 16), (513, 960, 896, 8), (1, 128, 64, 16)])
+def test_bf16_w_backward_equals_transposed_layout(gpu, T, K, N, r):
+    """The backward on a bf16 W [N][K] reads it reduction-major (LDS transpose reads) and must hand
+    the matrix cores the same fragments as W^T [K][N]: dX, dA and dB bit-identical in both dX
+    modes (ragged T, K and N tiles, K = 64, every rank), and dX within tolerance of the oracle."""
+    import torch
+    c = Case(T, K, N, r=r, base="bf16", tag="wlayout")
+    print(f"case: W vs W^T backward T={T} K={K} N={N} r={r}", flush=True)
+    Y, U = c.gpu_fwd()
+    wt = c.w_transposed()
+    for dx_mode, grad_mode in ((lib.DX_BF16_SET, lib.GRAD_SET), (lib.DX_F32_ADD, lib.GRAD_ADD)):
+        got = c.gpu_bwd(U, dx_mode=dx_mode, grad_mode=grad_mode)
+        want = c.gpu_bwd(U, dx_mode=dx_mode, grad_mode=grad_mode, W=wt, transposed=True)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dX", "dA", "dB"), got, want):
+            assert _eq(a, b), (name, dx_mode)
+    dX, dA, dB = c.gpu_bwd(U)
+    torch.cuda.synchronize()
+    dXo, dAo, dBo, _ = c.oracle_bwd()
+    assert_close("dX", to_np(dX), dXo)
+    assert_close("dA", to_np(dA), dAo)
+    assert_close("dB", to_np(dB), dBo)
+
+
 @pytest.mark.parametrize("transposed", [False, True], ids=["W", "WT"])
 def test_accumulate_modes(gpu, transposed):
     import torch
@@ -136,9 +161,9 @@ def test_grouped_forward_equals_single_forwards(gpu, base):
 def test_grouped_backward(gpu, base, T, r):
     """Five linears sharing X (ragged T, mixed N): the grouped backward gives each member's dA,
     dB bit-identical to its own backward, and dX equal to the sum of the members' dX (one GEMM
-    over the concatenated N for transposed weights; member order otherwise), matching the
-    oracle; the fp32 accumulate mode adds onto what dX held. (All members' G in one launch,
-    all dA/dB partials in one launch, all reductions in one launch.)"""
+    over the concatenated N for bf16 weights, bit-identical for W and W^T; member order for
+    NF4 weights), matching the oracle; the fp32 accumulate mode adds onto what dX held. (All
+    members' G in one launch, all dA/dB partials in one launch, all reductions in one launch.)"""
     import torch
     K = 512
     Ns = [512, 128, 128, 1344, 1344]
@@ -184,22 +209,36 @@ def test_grouped_backward(gpu, base, T, r):
     assert_close("dX", to_np(dX_seq).astype(np.float64) - cs[0].dX_init, want)
     # the fused sum differs from the member-order sum only by fp32 rounding
     assert olora.rel_l2(to_np(dX).astype(np.float64), to_np(dX_seq).astype(np.float64)) < 1e-6
-    # weights not transposed: one member after another, bit-identical to separate calls
+    # weights as given (W [N][K]): bf16 members run the same single GEMM, reading W reduction-
+    # major, with the transposed layout's bits; NF4 members run one after another, bit-identical
+    # to separate calls
     dXn = dX0.clone()
     dA3 = [torch.empty_like(a) for a in dA]
     dB3 = [torch.empty_like(b) for b in dB]
     lib.lora_linear_bwd_group([c.desc() for c in cs], X, [c.dYd for c in cs], Us, dXn, dA3, dB3,
                               dx_mode=lib.DX_F32_ADD, ws=ws)
-    dXm = dX0.clone()
-    for c, U in zip(cs, Us):
-        a1, b1 = torch.empty((r, K), dtype=torch.float32, device="cuda"), torch.empty((c.N, r), dtype=torch.float32,
-                                                                                      device="cuda")
-        lib.lora_linear_bwd(c.desc(), X, c.dYd, U, dXm, a1, b1, dx_mode=lib.DX_F32_ADD, ws=c.ws)
-    torch.cuda.synchronize()
-    assert _eq(dXn, dXm)
-    with pytest.raises(lib.LsnError):          # bf16 dX over several untransposed members
-        lib.lora_linear_bwd_group([c.desc() for c in cs], X, [c.dYd for c in cs], Us, dX16, dA3, dB3,
+    if base == "bf16":
+        dX16n = torch.empty_like(dX16)
+        lib.lora_linear_bwd_group([c.desc() for c in cs], X, [c.dYd for c in cs], Us, dX16n, dA3, dB3,
                                   dx_mode=lib.DX_BF16_SET, ws=ws)
+        torch.cuda.synchronize()
+        assert _eq(dXn, dX) and _eq(dX16n, dX16)
+        for a, a3, b, b3 in zip(dA, dA3, dB, dB3):
+            assert _eq(a, a3) and _eq(b, b3)
+        with pytest.raises(lib.LsnError):      # mixed layouts: no single GEMM, so no bf16 sum
+            lib.lora_linear_bwd_group([descs[0]] + [c.desc() for c in cs[1:]], X, [c.dYd for c in cs], Us,
+                                      dX16n, dA3, dB3, dx_mode=lib.DX_BF16_SET, ws=ws)
+    else:
+        dXm = dX0.clone()
+        for c, U in zip(cs, Us):
+            a1 = torch.empty((r, K), dtype=torch.float32, device="cuda")
+            b1 = torch.empty((c.N, r), dtype=torch.float32, device="cuda")
+            lib.lora_linear_bwd(c.desc(), X, c.dYd, U, dXm, a1, b1, dx_mode=lib.DX_F32_ADD, ws=c.ws)
+        torch.cuda.synchronize()
+        assert _eq(dXn, dXm)
+        with pytest.raises(lib.LsnError):      # bf16 dX over several NF4 members
+            lib.lora_linear_bwd_group([c.desc() for c in cs], X, [c.dYd for c in cs], Us, dX16, dA3, dB3,
+                                      dx_mode=lib.DX_BF16_SET, ws=ws)
     with pytest.raises(lib.LsnError):          # workspace too small
         lib.lora_linear_bwd_group(descs, X, [c.dYd for c in cs], Us, dX, dA, dB, ws=ws[:1024])
     with pytest.raises(lib.LsnError):          # an output overlapping an input
@@ -263,11 +302,14 @@ def test_full_size_sampled_parity(gpu, label, T, K, N):
     print(f"case: {label} T={T} K={K} N={N}", flush=True)
     c = Case(T, K, N, tag="full")
     Y, U = c.gpu_fwd()
-    dX, dA, dB = c.gpu_bwd(U, W=c.w_transposed(), transposed=True)   # the stack's backward path
+    dX, dA, dB = c.gpu_bwd(U, W=c.w_transposed(), transposed=True)
+    dX_w, dA_w, dB_w = c.gpu_bwd(U, W=lib.nf4_dequant(c.Wd, "bf16"))   # the stack's backward path
     dX_nn, dA_nn, dB_nn = c.gpu_bwd(U)
     torch.cuda.synchronize()
-    # the LoRA gradients do not involve W: both backward paths run the same kernels for them
-    assert _eq(dA, dA_nn) and _eq(dB, dB_nn)
+    # the LoRA gradients do not involve W: every backward path runs the same kernels for them;
+    # the staged W [N][K] and W^T [K][N] give the same dX bits
+    assert _eq(dA, dA_nn) and _eq(dB, dB_nn) and _eq(dA, dA_w) and _eq(dB, dB_w)
+    assert _eq(dX, dX_w)
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(T, 48, replace=False))
     from oracle import nf4 as onf4

@@ -83,6 +83,22 @@ def test_toy_8b_shapes_exactness_and_controls(gpu):
     st.close()
 
 
+def test_staged_w_equals_staged_transposed(gpu):
+    """Three 8B-shaped layers: the backward on the staged W [N][K] (the dX GEMM reads it
+    reduction-major) and on a staged W^T [K][N] give identical bits: forward, recompute and dX
+    checksums and every LoRA gradient tensor."""
+    cfg = configs.C3
+    print("case: 3-layer 8B-shaped toy, staged W vs staged W^T", flush=True)
+    runs = []
+    for dequant in ("staged", "staged_t"):
+        st = Stack(cfg, modes=("resident",), record=True, layers=3, dequant=dequant)
+        st.step("resident")
+        runs.append(snapshot(st))
+        st.close()
+    fwd, re, dx, eq, n = compare(runs[0], runs[1])
+    assert fwd and re and dx and eq == n == 2 * 7 * 3, (fwd, re, dx, eq, n)
+
+
 @pytest.mark.timeout(1200)
 @pytest.mark.parametrize("name", ["C2", "C4", "C3", "C5"])
 def test_streamed_equals_resident_full_stack(gpu, name):
