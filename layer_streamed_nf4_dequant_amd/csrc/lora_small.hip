@@ -22,19 +22,29 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4_t v) { return __builtin_bit_ca
 // row projections sharing one activation: out_g[m][j] = bf16( sum_k act[m][k] P_g[j][k] ), j < r_g,
 // for up to 8 low-rank matrices P_g (ranks multiples of 8, total <= 128), so act is read once.
 // Several jobs (activations of their own, the same M) run as grid rows of one launch.
-// One workgroup of RP_WAVES waves per 16 rows; wave w takes the 32-wide K-steps w, w + RP_WAVES,
+// One workgroup of RP_WAVES waves per 16 rows; wave w takes the 64-wide K-steps w, w + RP_WAVES,
 // ...; the partial results are added in wave order through LDS. Column block cb (16 columns of the
 // concatenated P) is one MFMA 16x16x32 accumulator; NB is the exact number of column blocks.
-// The work per K-step is tiny (one activation fragment, NB weight fragments, NB MFMAs), so the
-// loop is latency-bound unless many loads are in flight: each wave keeps the operands of DEPTH
-// K-steps in registers and issues the loads of step i + DEPTH as it consumes step i. Every load is
-// unconditional (columns past the total read a valid row and are never stored; steps past the
-// wave's last re-read its last step), so the load counter waits stay exact.
+// The activation is read in whole 128-byte lines (a lane loads 16 bytes of row lane / 8 and its
+// twin 8 rows down, eight lanes per line): an MFMA fragment spans only 64 bytes of each of 16
+// rows, and half-line loads ran the stream about 30% slower. The wave turns its 16 x 64 block
+// into fragments through its own 2 KB of LDS (chunk c of row r at slot c ^ ((r ^ r >> 3) & 7), so
+// neither the row writes nor the 16-row fragment reads conflict). P is small and read from L2 in
+// fragment layout.
+// The work per K-step is tiny (two activation fragments, 2 NB weight fragments, 2 NB MFMAs), so
+// the loads run ahead: each wave keeps the operands of DEPTH K-steps in registers and issues the
+// loads of step i + DEPTH as it consumes step i (1-2 steps measured fastest; deeper queues ran
+// 10-20% slower). Every
+// load is unconditional (columns past the total read a valid row and are never stored; steps
+// past the wave's last re-read its last step), so the load counter waits stay exact.
 // ---------------------------------------------------------------------------------------------
 constexpr int RP_WAVES = 8;
+__device__ __forceinline__ int rp_xoff(int r, int c) { return r * 128 + 16 * (c ^ ((r ^ (r >> 3)) & 7)); }
+
 template <int NB, int DEPTH>
 __global__ __launch_bounds__(64 * RP_WAVES) void k_rowproj(int64_t M, RowProjJobs jobs) {
   __shared__ floatx4_t part[RP_WAVES][NB][64];
+  __shared__ __attribute__((aligned(16))) char xs[RP_WAVES][16 * 128];
   // job blockIdx.y: its own activation [M][K] and matrices
   const RowProjJob &J = jobs.job[blockIdx.y];
   const uint16_t *__restrict__ act = J.act;
@@ -43,9 +53,8 @@ __global__ __launch_bounds__(64 * RP_WAVES) void k_rowproj(int64_t M, RowProjJob
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t m0 = (int64_t)blockIdx.x * 16;
-  const int64_t m = min(m0 + (lane & 15), M - 1);      // clamped rows are never stored
   const int kq = 8 * (lane >> 4);
-  const int nks = (int)(K / 32);
+  const int nks = (int)(K / 64);
   // the concatenated row c of P: group g, local row c - start[g] (c clamped to the last row)
   const uint16_t *prow[NB];
 #pragma unroll
@@ -56,17 +65,27 @@ __global__ __launch_bounds__(64 * RP_WAVES) void k_rowproj(int64_t M, RowProjJob
     for (int q = 1; q < 8; ++q) g += (q < set.n && c >= set.start[q]) ? 1 : 0;
     prow[cb] = set.P[g] + (int64_t)(c - set.start[g]) * K + kq;
   }
-  const uint16_t *arow = act + m * K + kq;
+  // activation lines: rows xr and 8 + xr of the block (clamped rows are never stored), chunk xc
+  const int xr = lane >> 3, xc = lane & 7;
+  const uint16_t *xa0 = act + min(m0 + xr, M - 1) * K + 8 * xc;
+  const uint16_t *xa1 = act + min(m0 + 8 + xr, M - 1) * K + 8 * xc;
+  char *xw = xs[wave];
+  const int wo0 = rp_xoff(xr, xc), wo1 = rp_xoff(8 + xr, xc);
+  const int ro0 = rp_xoff(lane & 15, lane >> 4), ro1 = rp_xoff(lane & 15, 4 + (lane >> 4));
   floatx4_t acc[NB];
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) acc[cb] = floatx4_t{0, 0, 0, 0};
-  u32x4_t va[DEPTH], vb[DEPTH][NB];
+  u32x4_t va[DEPTH][2], vb[DEPTH][NB][2];
   // K-step of this wave's i-th iteration, clamped (a clamped step is loaded but not used)
-  auto load = [&](int i, u32x4_t &a_, u32x4_t (&b_)[NB]) {
-    const int64_t k = (int64_t)min(wave + RP_WAVES * i, nks - 1) * 32;
-    a_ = *reinterpret_cast<const u32x4_t *>(arow + k);
+  auto load = [&](int i, u32x4_t (&a_)[2], u32x4_t (&b_)[NB][2]) {
+    const int64_t k = (int64_t)min(wave + RP_WAVES * i, nks - 1) * 64;
+    a_[0] = *reinterpret_cast<const u32x4_t *>(xa0 + k);
+    a_[1] = *reinterpret_cast<const u32x4_t *>(xa1 + k);
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) b_[cb] = *reinterpret_cast<const u32x4_t *>(prow[cb] + k);
+    for (int cb = 0; cb < NB; ++cb) {
+      b_[cb][0] = *reinterpret_cast<const u32x4_t *>(prow[cb] + k);
+      b_[cb][1] = *reinterpret_cast<const u32x4_t *>(prow[cb] + k + 32);
+    }
   };
   const int iters = (nks - wave + RP_WAVES - 1) / RP_WAVES;   // K-steps of this wave (may be 0)
 #pragma unroll
@@ -81,15 +100,25 @@ __global__ __launch_bounds__(64 * RP_WAVES) void k_rowproj(int64_t M, RowProjJob
   do {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
+      // the wave's 16 x 64 block into fragment layout (LDS operations of a wave run in order, so
+      // the reads see these writes, and the next step's writes follow these reads)
+      *reinterpret_cast<u32x4_t *>(xw + wo0) = va[d][0];
+      *reinterpret_cast<u32x4_t *>(xw + wo1) = va[d][1];
+      u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(xw + ro0);
+      u32x4_t a1 = *reinterpret_cast<const u32x4_t *>(xw + ro1);
       // a step past the wave's last contributes zero (a select, not a branch, so the loop body
       // is straight-line code and its load waits are exact)
       const uint32_t keep = i0 + d < iters ? 0xffffffffu : 0u;
-      u32x4_t a_ = va[d];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a_[e] &= keep;
+      for (int e = 0; e < 4; ++e) {
+        a0[e] &= keep;
+        a1[e] &= keep;
+      }
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb)
-        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_), as_bf16x8(vb[d][cb]), acc[cb], 0, 0, 0);
+      for (int cb = 0; cb < NB; ++cb) {
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(vb[d][cb][0]), acc[cb], 0, 0, 0);
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(vb[d][cb][1]), acc[cb], 0, 0, 0);
+      }
       load(i0 + d + DEPTH, va[d], vb[d]);
       // keep the loads in program order: the scheduler would otherwise sink them to their uses
       // and undo the pipelining
@@ -319,14 +348,14 @@ lsn_status launch_rowproj_jobs(int64_t M, const RowProjJobs &jobs, hipStream_t s
     if ((jobs.job[g].set.total + 15) / 16 != nb) return LSN_E_ARG;
   const dim3 grid((unsigned)((M + 15) / 16), (unsigned)jobs.n), block(64 * RP_WAVES);
   switch (nb) {
-    case 1: hipLaunchKernelGGL((k_rowproj<1, 8>), grid, block, 0, s, M, jobs); break;
-    case 2: hipLaunchKernelGGL((k_rowproj<2, 6>), grid, block, 0, s, M, jobs); break;
-    case 3: hipLaunchKernelGGL((k_rowproj<3, 4>), grid, block, 0, s, M, jobs); break;
-    case 4: hipLaunchKernelGGL((k_rowproj<4, 4>), grid, block, 0, s, M, jobs); break;
-    case 5: hipLaunchKernelGGL((k_rowproj<5, 3>), grid, block, 0, s, M, jobs); break;
-    case 6: hipLaunchKernelGGL((k_rowproj<6, 3>), grid, block, 0, s, M, jobs); break;
-    case 7: hipLaunchKernelGGL((k_rowproj<7, 2>), grid, block, 0, s, M, jobs); break;
-    case 8: hipLaunchKernelGGL((k_rowproj<8, 2>), grid, block, 0, s, M, jobs); break;
+    case 1: hipLaunchKernelGGL((k_rowproj<1, 2>), grid, block, 0, s, M, jobs); break;
+    case 2: hipLaunchKernelGGL((k_rowproj<2, 2>), grid, block, 0, s, M, jobs); break;
+    case 3: hipLaunchKernelGGL((k_rowproj<3, 1>), grid, block, 0, s, M, jobs); break;
+    case 4: hipLaunchKernelGGL((k_rowproj<4, 1>), grid, block, 0, s, M, jobs); break;
+    case 5: hipLaunchKernelGGL((k_rowproj<5, 1>), grid, block, 0, s, M, jobs); break;
+    case 6: hipLaunchKernelGGL((k_rowproj<6, 1>), grid, block, 0, s, M, jobs); break;
+    case 7: hipLaunchKernelGGL((k_rowproj<7, 1>), grid, block, 0, s, M, jobs); break;
+    case 8: hipLaunchKernelGGL((k_rowproj<8, 1>), grid, block, 0, s, M, jobs); break;
     default: return LSN_E_ARG;
   }
   return check_hip(hipGetLastError(), "k_rowproj launch");
