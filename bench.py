@@ -64,7 +64,9 @@ def traffic_from_profiles():
 
 def clock_sampler():
     """Samples the GPU's current sclk and mclk (the sysfs pp_dpm_* entry marked '*') and its
-    power reading every 50 ms in a thread while the timed steps run (no child process). Returns
+    power reading every 250 ms in a thread while the timed steps run (no child process; each
+    sysfs clock read queries the power-management firmware, and sampling every 50 ms cost the
+    timed steps about 0.8%). Returns
     a stop function giving the medians, or None where sysfs has no such files."""
     import glob
     import re
@@ -101,7 +103,7 @@ def clock_sampler():
                         samples["power_W"].append(int(f.read()) / 1e6)
                 except (OSError, ValueError):
                     pass
-            stop.wait(0.05)
+            stop.wait(0.25)
 
     th = threading.Thread(target=run, daemon=True)
     th.start()
@@ -239,7 +241,10 @@ def main():
         ms = stack.step(args.mode)
         print(f"[bench] warmup {i}: {ms:.1f} ms", flush=True)
 
-    gemm_events, dequant_events = [], []
+    # the staging kernels are timed in a pass of their own below when that pass runs (their events
+    # in the streamed pass would also count copy waits); the GEMM events stay in the timed steps
+    dequant_separately = not args.no_other_modes and stack.slots is not None and stack.dequant != "fused"
+    gemm_events, dequant_events = [], ([] if not dequant_separately else None)
     torch.cuda.reset_peak_memory_stats()
     torch.cuda.synchronize()
     clocks_done = clock_sampler()
@@ -247,9 +252,11 @@ def main():
     step_ms = []
     for i in range(args.steps):
         step_ms.append(stack.step(args.mode, gemm_events=gemm_events, dequant_events=dequant_events))
+    dequant_events = dequant_events or []
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     peak_alloc = torch.cuda.max_memory_allocated()
+    pool = stack.pool.stats() if stack.pool is not None else None   # before any pool reset below
     clocks = clocks_done() if clocks_done else None
     print(f"[bench] {args.steps} steps: {wall * 1e3 / args.steps:.1f} ms/step (events median "
           f"{sorted(step_ms)[len(step_ms) // 2]:.1f} ms)", flush=True)
@@ -277,7 +284,7 @@ def main():
     # they would also count the wait. The staging kernels are therefore timed in a pass over layer
     # images already in the pool slots (same kernels, same bytes, no copies), when that pass exists.
     dequant_source = f"{args.mode} pass (events may include waits for layer copies)"
-    if not args.no_other_modes and stack.slots is not None and stack.dequant != "fused":
+    if dequant_separately:
         stack.step("no_h2d")
         dequant_events = []
         for _ in range(max(2, args.steps // 2)):
@@ -327,12 +334,25 @@ def main():
             torch.cuda.synchronize()
             other[m] = round(cfg.T * n / (time.perf_counter() - t0), 1)
             print(f"[bench] {m}: {other[m]} tokens/s", flush=True)
+        if stack.pool is not None:
+            # the pool reusing the layers still in a slot at the forward/backward and step
+            # boundaries (LSN_POOL_KEEP_AT_TURN) instead of copying every visit
+            stack.reset_pool(lib.POOL_KEEP_AT_TURN)
+            stack.step("streamed")
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            n = max(3, args.steps // 2)
+            for _ in range(n):
+                stack.step("streamed")
+            torch.cuda.synchronize()
+            other["streamed_keep_at_turn"] = round(cfg.T * n / (time.perf_counter() - t0), 1)
+            print(f"[bench] streamed, keep at turn: {other['streamed_keep_at_turn']} tokens/s", flush=True)
+            stack.reset_pool(0)
         if stack.slots is not None:
             other["h2d_GBs"] = round(stack.h2d_rate(), 1)
 
     tokens = cfg.T * args.steps
     value = tokens / wall
-    pool = stack.pool.stats() if stack.pool is not None else None
     out = {
         "metric": METRIC,
         "value": round(value, 1),

@@ -304,12 +304,14 @@ class Stack:
                 self._wvec = torch.arange(1, n + 1, device=v.device, dtype=torch.int64)
             self.checks[(tag, l, j)] = (v.to(torch.int64) * self._wvec[:n]).sum()
 
-    def step(self, mode: str = "streamed", gemm_events=None, dequant_events=None) -> float:
+    def step(self, mode: str = "streamed", gemm_events=None, dequant_events=None, wait: bool = True):
         """One training step of the projection stack; returns its time in ms (compute stream).
         gemm_events: optional list; (projections, start, end) HIP events around every forward
         GEMM launch (one per group of projections sharing an input) are appended to it.
         dequant_events: optional list; ((visit, with_transposed), start, end) around every visit's
-        staging, visit "fwd" or "bwd", with_transposed when the visit also staged W^T."""
+        staging, visit "fwd" or "bwd", with_transposed when the visit also staged W^T.
+        wait=False returns the step's (start, end) events without waiting for them, so the next
+        step's first layer copies can be queued while this step's last visits still run."""
         torch = self.torch
         s = self.compute
         sh = s.cuda_stream
@@ -357,6 +359,8 @@ class Stack:
                 if mode == "streamed":
                     self.pool.release(l, sh)
             end.record(s)
+        if not wait:
+            return start, end
         end.synchronize()
         return start.elapsed_time(end)
 
