@@ -348,6 +348,22 @@ def main():
             other["streamed_keep_at_turn"] = round(cfg.T * n / (time.perf_counter() - t0), 1)
             print(f"[bench] streamed, keep at turn: {other['streamed_keep_at_turn']} tokens/s", flush=True)
             stack.reset_pool(0)
+            # a DPO-style step: the frozen reference model's forward (one more streamed sweep with
+            # the adapters off) before the training step
+            torch.cuda.reset_peak_memory_stats()
+            stack.step("streamed", reference=True)
+            torch.cuda.synchronize()
+            c0 = stack.pool.stats()["copies"]
+            t0 = time.perf_counter()
+            for _ in range(n):
+                stack.step("streamed", reference=True)
+            torch.cuda.synchronize()
+            other["streamed_with_reference_sweep"] = round(cfg.T * n / (time.perf_counter() - t0), 1)
+            other["reference_sweep_layer_reads_ratio"] = round((stack.pool.stats()["copies"] - c0) / n / (2 * stack.L), 3)
+            other["reference_sweep_peak_hbm_ratio"] = round(torch.cuda.max_memory_allocated() / peak_alloc, 3)
+            print(f"[bench] streamed with the reference sweep: {other['streamed_with_reference_sweep']} tokens/s",
+                  flush=True)
+            stack.reset_pool(0)
         if stack.slots is not None:
             other["h2d_GBs"] = round(stack.h2d_rate(), 1)
 

@@ -238,22 +238,23 @@ class Stack:
         return lib.LoraLinearDesc(cfg.T, p.K, p.N, cfg.r, cfg.scale, w, self.A[l][j].data_ptr(),
                                   self.B[l][j].data_ptr())
 
-    def _forward_layer(self, base: int, l: int, Y, s, gemm_events=None):
+    def _forward_layer(self, base: int, l: int, Y, s, gemm_events=None, adapters: bool = True):
         # per shared input (q, k, v, gate and up read X_h; o reads X_o; down reads X_d): the
         # adapters' down-projections in one pass over the input, then the projections' forward
-        # GEMMs as one grouped launch
+        # GEMMs as one grouped launch (adapters off: the frozen base alone, Y = bf16(X W^T))
         for which in ("h", "o", "d"):
             js = [j for j, p in enumerate(self.layout) if PROJ_INPUT[p.name] == which]
             if not js:
                 continue
-            lib.lora_down(self.X[which], [self.A[l][j] for j in js], [self.U[j] for j in js], stream=s)
+            if adapters:
+                lib.lora_down(self.X[which], [self.A[l][j] for j in js], [self.U[j] for j in js], stream=s)
             if gemm_events is not None:
                 gemm_events.append((js, self.torch.cuda.Event(enable_timing=True),
                                     self.torch.cuda.Event(enable_timing=True)))
                 gemm_events[-1][1].record(s)
             lib.lora_linear_fwd_group([self._desc(base, l, j) for j in js], self.X[which], [Y[j] for j in js],
-                                      [self.U[j] for j in js], adapters=lib.ADAPTERS_U_READY, ws=self.ws,
-                                      stream=s)
+                                      [self.U[j] for j in js], adapters=lib.ADAPTERS_U_READY if adapters else False,
+                                      ws=self.ws, stream=s)
             if gemm_events is not None:
                 gemm_events[-1][2].record(s)
 
@@ -304,14 +305,21 @@ class Stack:
                 self._wvec = torch.arange(1, n + 1, device=v.device, dtype=torch.int64)
             self.checks[(tag, l, j)] = (v.to(torch.int64) * self._wvec[:n]).sum()
 
-    def step(self, mode: str = "streamed", gemm_events=None, dequant_events=None, wait: bool = True):
+    def step(self, mode: str = "streamed", gemm_events=None, dequant_events=None, wait: bool = True,
+             reference: bool = False):
         """One training step of the projection stack; returns its time in ms (compute stream).
         gemm_events: optional list; (projections, start, end) HIP events around every forward
         GEMM launch (one per group of projections sharing an input) are appended to it.
         dequant_events: optional list; ((visit, with_transposed), start, end) around every visit's
         staging, visit "fwd" or "bwd", with_transposed when the visit also staged W^T.
         wait=False returns the step's (start, end) events without waiting for them, so the next
-        step's first layer copies can be queued while this step's last visits still run."""
+        step's first layer copies can be queued while this step's last visits still run.
+        reference=True first runs the frozen reference model's forward: one more streamed sweep
+        over every layer with the adapters off, into Yref ("An 8B Fine-Tune Now Fits in 4 GB of
+        VRAM": for DPO-style objectives the streamed base with the adapters switched off is the
+        reference model, at the cost of more layer reads per step; here 3 per layer instead of 2).
+        It changes no training state: the step's outputs and gradients are those of a step
+        without it."""
         torch = self.torch
         s = self.compute
         sh = s.cuda_stream
@@ -321,16 +329,22 @@ class Stack:
             start.record(s)
             # with K slots, up to K-1 layers are in flight ahead of the one being computed
             ahead = len(self.slots) - 1 if self.slots is not None else 0
+            # ---- reference model (adapters off): layers 0 .. L-1 ----
+            if reference:
+                if getattr(self, "Yref", None) is None:
+                    self.Yref = [torch.empty_like(y) for y in self.Y]
+                for l in range(L):
+                    base = self._visit_base(mode, l, sh, ahead, forward=True)
+                    if self.dequant != "fused":
+                        self._stage(base, l, s)
+                    self._forward_layer(base, l, self.Yref, s, adapters=False)
+                    if self.record:
+                        self._record("ref", l, self.Yref)
+                    if mode == "streamed":
+                        self.pool.release(l, sh)
             # ---- forward: layers 0 .. L-1 ----
             for l in range(L):
-                if mode == "streamed":
-                    for a in range(l, min(L, l + 1 + ahead)):
-                        self.pool.prefetch(a)
-                    base = self.pool.acquire(l, sh)
-                elif mode == "resident":
-                    base = self.resident[l].data_ptr()
-                else:
-                    base = self.slots[l % len(self.slots)].data_ptr()
+                base = self._visit_base(mode, l, sh, ahead, forward=True)
                 if self.dequant != "fused":
                     self._timed(dequant_events, ("fwd", False), s, lambda: self._stage(base, l, s))
                 self._forward_layer(base, l, self.Y, s, gemm_events)
@@ -340,14 +354,7 @@ class Stack:
                     self.pool.release(l, sh)
             # ---- backward: layers L-1 .. 0, each re-read and recomputed ----
             for l in reversed(range(L)):
-                if mode == "streamed":
-                    for a in range(l, max(-1, l - 1 - ahead), -1):
-                        self.pool.prefetch(a)
-                    base = self.pool.acquire(l, sh)
-                elif mode == "resident":
-                    base = self.resident[l].data_ptr()
-                else:
-                    base = self.slots[l % len(self.slots)].data_ptr()
+                base = self._visit_base(mode, l, sh, ahead, forward=False)
                 if self.dequant != "fused":                               # re-dequantised per visit
                     self._timed(dequant_events, ("bwd", self.dequant == "staged_t"), s,
                                 lambda: self._stage(base, l, s, backward=True))
@@ -363,6 +370,18 @@ class Stack:
             return start, end
         end.synchronize()
         return start.elapsed_time(end)
+
+    def _visit_base(self, mode: str, l: int, sh, ahead: int, forward: bool) -> int:
+        """Device address of layer l's image for this visit (streamed: prefetch the next layers in
+        the sweep's direction and acquire l; the caller releases it)."""
+        if mode == "streamed":
+            nxt = range(l, min(self.L, l + 1 + ahead)) if forward else range(l, max(-1, l - 1 - ahead), -1)
+            for a in nxt:
+                self.pool.prefetch(a)
+            return self.pool.acquire(l, sh)
+        if mode == "resident":
+            return self.resident[l].data_ptr()
+        return self.slots[l % len(self.slots)].data_ptr()
 
     def _timed(self, events, tag, s, fn):
         if events is None:

@@ -99,6 +99,49 @@ def test_staged_w_equals_staged_transposed(gpu):
     assert fwd and re and dx and eq == n == 2 * 7 * 3, (fwd, re, dx, eq, n)
 
 
+def test_reference_pass_adapters_off(gpu):
+    """The DPO-style reference sweep ("An 8B Fine-Tune Now Fits in 4 GB of VRAM": the streamed
+    base with the adapters off is the reference model): three 8B-shaped layers. The sweep changes
+    no training state (every forward, recompute, dX checksum and every LoRA gradient equals a step
+    without it); streamed equals resident on the reference outputs too; the pool copies each
+    layer three times per step; and the reference outputs of k and o match the oracle's
+    adapters-off forward on sampled rows."""
+    import torch
+    from oracle import lora as olora
+    from oracle import nf4 as onf4
+    cfg = configs.C3
+    print("case: 3-layer 8B-shaped toy, reference sweep", flush=True)
+    st = Stack(cfg, modes=("streamed", "resident"), record=True, layers=3)
+    st.step("resident")
+    plain = snapshot(st)
+    st.step("resident", reference=True)
+    with_ref = snapshot(st)
+    fwd, re, dx, eq, n = compare(plain, with_ref)
+    assert fwd and re and dx and eq == n == 2 * 7 * 3, (fwd, re, dx, eq, n)
+    st.reset_pool(0, 2)
+    st.step("streamed", reference=True)
+    ref_out = [y.clone() for y in st.Yref]          # layer 2's reference outputs
+    streamed = snapshot(st)
+    fwd, re, dx, eq, n = compare(with_ref, streamed)
+    assert fwd and re and dx and eq == n
+    ref_keys = [k for k in with_ref[0] if k[0] == "ref"]
+    assert len(ref_keys) == 3 * 7 and all(with_ref[0][k] == streamed[0][k] for k in ref_keys)
+    assert st.pool.stats()["copies"] == 3 * 3
+    rows = np.sort(np.random.default_rng(1).choice(cfg.T, 24, replace=False))
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    for j, p in enumerate(st.layout):
+        if p.name not in ("k", "o"):     # one projection per input width keeps the oracle's packing short
+            continue
+        W = inputs.device_normal((p.N, p.K), inputs.STD["W"], st.seed, cfg.name, 2, p.name, "W").cpu().numpy()
+        Wh = onf4.bf16_to_f32(onf4.dequant_bf16(onf4.pack(W)))
+        X = f(st.X[PROJ_INPUT[p.name]])[rows]
+        Yo, _ = olora.forward(X, Wh, f(st.A[2][j]), f(st.B[2][j]), cfg.scale, False)
+        got = ref_out[j].float().cpu().numpy()[rows]
+        err = olora.rel_l2(got.astype(np.float64), Yo)
+        assert err < 5e-3, (p.name, err)
+    st.close()
+
+
 @pytest.mark.timeout(1200)
 @pytest.mark.parametrize("name", ["C2", "C4", "C3", "C5"])
 def test_streamed_equals_resident_full_stack(gpu, name):
