@@ -78,6 +78,14 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
                           "(or python -m layer_streamed_nf4_dequant_amd.build)")
+    # One HIP runtime per process: torch ships its own copy of libamdhip64 under the same soname
+    # as the system one this library links. Loaded after torch, the library binds to torch's
+    # copy; loaded first, it would pull in the system copy and torch would later load its own,
+    # and two runtimes in one process do not share devices or memory. So torch goes first.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     sig = {

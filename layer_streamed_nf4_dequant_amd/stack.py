@@ -77,16 +77,113 @@ def layer_layout(cfg: StackConfig) -> tuple[list[ProjLayout], int]:
     return projs, _align(off)
 
 
+MIB2 = 2 << 20
+
+
+def workspace_bytes(cfg: StackConfig) -> int:
+    """The shared backward workspace the stack allocates (the largest single-linear need, or the
+    grouped need of the linears that read X_h)."""
+    T, r = cfg.T, cfg.r
+    layout, _ = layer_layout(cfg)
+    ws = max(lib.ws_bytes(T, p.K, p.N, r) for p in layout)
+    hj = [p for p in layout if PROJ_INPUT[p.name] == "h"]
+    if len(hj) > 1:
+        probe = [lib.LoraLinearDesc(T, p.K, p.N, r, cfg.scale, lib.WeightDesc(), None, None) for p in hj]
+        ws = max(ws, lib.group_ws_bytes(probe))
+    return ws
+
+
+def buffer_plan(cfg: StackConfig, modes=("streamed",), dequant: str = "staged", layers=None,
+                reference: bool = False) -> list:
+    """Every device buffer a training step uses, in arena order: [(key, part, nbytes)]. The stack
+    carves them all from one arena allocated up front (the pages' pre-allocated device buffers),
+    so a step allocates nothing."""
+    L = cfg.layers if layers is None else layers
+    layout, image = layer_layout(cfg)
+    T, r = cfg.T, cfg.r
+    if cfg.base != "nf4":
+        dequant = "fused"
+    plan = []
+    for l in range(L):
+        for j, p in enumerate(layout):
+            plan += [(("A", l, j), "adapters", r * p.K * 2), (("B", l, j), "adapters", p.N * r * 2),
+                     (("dA", l, j), "adapter_grads", r * p.K * 4), (("dB", l, j), "adapter_grads", p.N * r * 4)]
+    plan += [(("X", w), "inputs", T * cfg.input_width(w) * 2) for w in ("h", "o", "d")]
+    plan += [(("dY", j), "upstream_grads", T * p.N * 2) for j, p in enumerate(layout)]
+    for name in ("Y", "Yre"):
+        plan += [((name, j), "outputs", T * p.N * 2) for j, p in enumerate(layout)]
+    plan += [(("U", j), "outputs", T * r * 2) for j, _ in enumerate(layout)]
+    plan += [(("dX_h",), "input_grads", T * cfg.hidden * 4)]
+    plan += [(("dX_o", i), "input_grads", T * cfg.hidden * 2) for i in range(2)]
+    plan += [(("dX_d", i), "input_grads", T * cfg.inter * 2) for i in range(2)]
+    plan += [(("ws",), "workspace", workspace_bytes(cfg))]
+    if dequant in ("staged", "staged_t"):
+        plan += [(("w_stage", j), "staging", p.N * p.K * 2) for j, p in enumerate(layout)]
+    if dequant == "staged_t":
+        plan += [(("w_stage_t", j), "staging", p.K * p.N * 2) for j, p in enumerate(layout)]
+    if "streamed" in modes or "no_h2d" in modes:
+        plan += [(("slot", i), "pool_slots", image) for i in range(cfg.pool_slots)]
+    if "resident" in modes:
+        plan += [(("resident", l), "resident_images", image) for l in range(L)]
+    if reference:
+        plan += [(("Yref", j), "reference_outputs", T * p.N * 2) for j, p in enumerate(layout)]
+    return plan
+
+
+def arena_offsets(plan) -> tuple[dict, int]:
+    """Byte offset of every buffer (256-byte aligned) and the arena size (a whole number of
+    2 MiB, the caching allocator's large-segment granule, so that it books exactly this size)."""
+    off, at = {}, 0
+    for key, _, nbytes in plan:
+        at = _align(at)
+        off[key] = at
+        at += nbytes
+    return off, (at + MIB2 - 1) // MIB2 * MIB2
+
+
+def predict_device_bytes(cfg: StackConfig, modes=("streamed",), dequant: str = "staged", layers=None,
+                         reference: bool = False) -> dict:
+    """Peak device memory of a training step, from the shapes alone ("Soup v0.73.0 benchmarks
+    README", record index: a peak-VRAM predictor, and a fit decision that refuses instead of
+    warning). Every buffer a step uses lives in the stack's arena and a step allocates nothing
+    more, so the step's peak is the arena: adapters and their gradients, the shared activations,
+    upstream gradients and outputs, the workspace, the staging buffers, and the pool slots
+    (streamed) or the resident images. Also returned: the set-up's extra temporaries (one
+    weight generated in fp32, a layer image being packed, and the packing workspace), which the
+    fit decision adds. Returns the parts, their "total" and "setup_extra"."""
+    plan = buffer_plan(cfg, modes, dequant, layers, reference)
+    parts = {}
+    for _, part, nbytes in plan:
+        parts[part] = parts.get(part, 0) + nbytes
+    _, parts["total"] = arena_offsets(plan)
+    layout, image = layer_layout(cfg)
+    big = max(layout, key=lambda p: p.K * p.N)
+    pack_ws = lib.load().nf4_pack_ws_bytes(big.N, big.K) if cfg.base == "nf4" else 0
+    parts["setup_extra"] = big.K * big.N * 4 + (image if "resident" not in modes else 0) + pack_ws
+    return parts
+
+
 class Stack:
     """Owns the host images, device state and buffers of one configuration."""
 
     def __init__(self, cfg: StackConfig, seed: int = 0, modes=("streamed",), audit: bool = False,
                  keep_at_turn: bool = False, fault: int = 0, record: bool = False, layers=None,
-                 dequant: str = "staged"):
+                 dequant: str = "staged", hbm_budget: int | None = None, reference: bool = False):
+        """hbm_budget: device bytes the stack may take; by default the free memory the device
+        reports. The predicted arena plus the set-up's temporaries (predict_device_bytes) must
+        fit, else MemoryError before anything is allocated. reference: also place the reference
+        sweep's outputs in the arena (otherwise the first reference step allocates them)."""
         import torch
         self.torch = torch
         self.cfg = cfg
         self.L = cfg.layers if layers is None else layers
+        pred = predict_device_bytes(cfg, modes, dequant, self.L, reference)
+        need = pred["total"] + pred["setup_extra"]
+        budget = hbm_budget if hbm_budget is not None else torch.cuda.mem_get_info()[0]
+        if need > budget:
+            raise MemoryError(f"{cfg.name}: the stack needs {need} B of device memory (predicted: "
+                              f"{pred['total']} B arena + {pred['setup_extra']} B during set-up), "
+                              f"{budget} B available: refused")
         self.seed = seed
         self.dev = torch.device("cuda")
         self.layout, self.image_bytes = layer_layout(cfg)
@@ -107,6 +204,16 @@ class Stack:
         T, r = cfg.T, cfg.r
         bf16 = torch.bfloat16
 
+        # ---- the arena: every buffer a step uses, allocated once, first ----
+        plan = buffer_plan(cfg, modes, self.dequant, self.L, reference)
+        offsets, arena_bytes = arena_offsets(plan)
+        self.arena = torch.empty(arena_bytes, dtype=torch.uint8, device=self.dev)
+        sizes = {key: nbytes for key, _, nbytes in plan}
+
+        def buf(key, shape, dtype):
+            o = offsets[key]
+            return self.arena[o:o + sizes[key]].view(dtype).view(shape)
+
         # ---- frozen base: generated on the device per layer, packed, kept in pinned host images
         self.means = np.zeros((self.L, len(self.layout)), dtype=np.float32)
         self.host_images = []
@@ -114,7 +221,11 @@ class Stack:
         scratch_w = None
         for l in range(self.L):
             img = torch.empty(self.image_bytes, dtype=torch.uint8, pin_memory=True)
-            dev_img = torch.zeros(self.image_bytes, dtype=torch.uint8, device=self.dev)
+            if self.resident is not None:
+                dev_img = buf(("resident", l), (self.image_bytes,), torch.uint8)
+                dev_img.zero_()
+            else:
+                dev_img = torch.zeros(self.image_bytes, dtype=torch.uint8, device=self.dev)
             for j, p in enumerate(self.layout):
                 w = inputs.device_normal((p.N, p.K), inputs.STD["W"], seed, cfg.name, l, p.name, "W")
                 if cfg.base == "nf4":
@@ -141,53 +252,49 @@ class Stack:
         self.A, self.B, self.dA, self.dB = [], [], [], []
         for l in range(self.L):
             Al, Bl, dAl, dBl = [], [], [], []
-            for p in self.layout:
+            for j, p in enumerate(self.layout):
                 key = (cfg.name, l, p.name)
-                Al.append(inputs.device_uniform((r, p.K), 1.0 / np.sqrt(p.K), seed, *key, "A", dtype=bf16))
-                Bl.append(inputs.device_normal((p.N, r), inputs.STD["B"], seed, *key, "B", dtype=bf16))
-                dAl.append(torch.zeros((r, p.K), dtype=torch.float32, device=self.dev))
-                dBl.append(torch.zeros((p.N, r), dtype=torch.float32, device=self.dev))
+                Al.append(buf(("A", l, j), (r, p.K), bf16))
+                Al[-1].copy_(inputs.device_uniform((r, p.K), 1.0 / np.sqrt(p.K), seed, *key, "A", dtype=bf16))
+                Bl.append(buf(("B", l, j), (p.N, r), bf16))
+                Bl[-1].copy_(inputs.device_normal((p.N, r), inputs.STD["B"], seed, *key, "B", dtype=bf16))
+                dAl.append(buf(("dA", l, j), (r, p.K), torch.float32).zero_())
+                dBl.append(buf(("dB", l, j), (p.N, r), torch.float32).zero_())
             self.A.append(Al)
             self.B.append(Bl)
             self.dA.append(dAl)
             self.dB.append(dBl)
 
         # ---- shared activations and upstream gradients ----
-        self.X = {w: inputs.device_normal((T, cfg.input_width(w)), 1.0, seed, cfg.name, "X", w, dtype=bf16)
-                  for w in ("h", "o", "d")}
-        self.dY = [inputs.device_normal((T, p.N), 1.0, seed, cfg.name, "dY", p.name, dtype=bf16)
-                   for p in self.layout]
-        self.Y = [torch.empty((T, p.N), dtype=bf16, device=self.dev) for p in self.layout]
-        self.Yre = [torch.empty((T, p.N), dtype=bf16, device=self.dev) for p in self.layout]
-        self.U = [torch.empty((T, r), dtype=bf16, device=self.dev) for p in self.layout]
-        self.dX_h = torch.zeros((T, cfg.hidden), dtype=torch.float32, device=self.dev)
+        self.X = {}
+        for w in ("h", "o", "d"):
+            self.X[w] = buf(("X", w), (T, cfg.input_width(w)), bf16)
+            self.X[w].copy_(inputs.device_normal((T, cfg.input_width(w)), 1.0, seed, cfg.name, "X", w, dtype=bf16))
+        self.dY = []
+        for j, p in enumerate(self.layout):
+            self.dY.append(buf(("dY", j), (T, p.N), bf16))
+            self.dY[-1].copy_(inputs.device_normal((T, p.N), 1.0, seed, cfg.name, "dY", p.name, dtype=bf16))
+        self.Y = [buf(("Y", j), (T, p.N), bf16) for j, p in enumerate(self.layout)]
+        self.Yre = [buf(("Yre", j), (T, p.N), bf16) for j, p in enumerate(self.layout)]
+        self.Yref = [buf(("Yref", j), (T, p.N), bf16) for j, p in enumerate(self.layout)] if reference else None
+        self.U = [buf(("U", j), (T, r), bf16) for j, _ in enumerate(self.layout)]
+        self.dX_h = buf(("dX_h",), (T, cfg.hidden), torch.float32).zero_()
         # dX_o and dX_d ping-pong by layer parity: layer l reads layer l+1's as upstream gradients
-        self.dX_o_pp = [torch.empty((T, cfg.hidden), dtype=bf16, device=self.dev) for _ in range(2)]
-        self.dX_d_pp = [torch.empty((T, cfg.inter), dtype=bf16, device=self.dev) for _ in range(2)]
-        ws = max(lib.ws_bytes(T, p.K, p.N, r) for p in self.layout)
+        self.dX_o_pp = [buf(("dX_o", i), (T, cfg.hidden), bf16) for i in range(2)]
+        self.dX_d_pp = [buf(("dX_d", i), (T, cfg.inter), bf16) for i in range(2)]
         self.h_group = [j for j, p in enumerate(self.layout) if PROJ_INPUT[p.name] == "h"]
-        if len(self.h_group) > 1:
-            probe = [lib.LoraLinearDesc(T, self.layout[j].K, self.layout[j].N, r, cfg.scale, lib.WeightDesc(), None,
-                                        None) for j in self.h_group]
-            ws = max(ws, lib.group_ws_bytes(probe))
-        self.ws = torch.empty(ws, dtype=torch.uint8, device=self.dev)
+        self.ws = buf(("ws",), (sizes[("ws",)],), torch.uint8)
         self.w_stage = self.w_stage_t = None
         if self.dequant in ("staged", "staged_t"):
-            self.w_stage = [torch.empty((p.N, p.K), dtype=bf16, device=self.dev) for p in self.layout]
+            self.w_stage = [buf(("w_stage", j), (p.N, p.K), bf16) for j, p in enumerate(self.layout)]
         if self.dequant == "staged_t":
-            self.w_stage_t = [torch.empty((p.K, p.N), dtype=bf16, device=self.dev) for p in self.layout]
+            self.w_stage_t = [buf(("w_stage_t", j), (p.K, p.N), bf16) for j, p in enumerate(self.layout)]
 
         # ---- pool (streamed) or fixed slots (no_h2d) ----
         self.pool = None
         self.slots = None
         if "streamed" in modes or "no_h2d" in modes:
-            free, _ = torch.cuda.mem_get_info()
-            need = cfg.pool_slots * self.image_bytes
-            if need > free:
-                raise MemoryError(f"pool of {cfg.pool_slots} x {self.image_bytes} B does not fit "
-                                  f"({free} B free): refused")
-            self.slots = [torch.empty(self.image_bytes, dtype=torch.uint8, device=self.dev)
-                          for _ in range(cfg.pool_slots)]
+            self.slots = [buf(("slot", i), (self.image_bytes,), torch.uint8) for i in range(cfg.pool_slots)]
         if "streamed" in modes:
             flags = (lib.POOL_AUDIT if audit else 0) | (lib.POOL_KEEP_AT_TURN if keep_at_turn else 0) | fault
             self.reset_pool(flags)
@@ -331,7 +438,7 @@ class Stack:
             ahead = len(self.slots) - 1 if self.slots is not None else 0
             # ---- reference model (adapters off): layers 0 .. L-1 ----
             if reference:
-                if getattr(self, "Yref", None) is None:
+                if self.Yref is None:          # not planned in the arena: allocated on first use
                     self.Yref = [torch.empty_like(y) for y in self.Y]
                 for l in range(L):
                     base = self._visit_base(mode, l, sh, ahead, forward=True)

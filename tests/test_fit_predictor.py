@@ -1,0 +1,76 @@
+"""The fit decision ("Soup v0.73.0 benchmarks README", record index: a peak-VRAM predictor, and a
+fit decision that refuses instead of warning): every buffer a step uses lives in one arena the
+stack allocates up front, the predicted peak of a step is that arena, and a stack whose arena and
+set-up temporaries exceed the budget is refused before anything is allocated. The GPU test checks
+the prediction against the torch allocator's measured peak of real steps (the pages' predictor:
+0.85% worst-case error)."""
+
+import gc
+
+import pytest
+
+from layer_streamed_nf4_dequant_amd import configs, lib
+from layer_streamed_nf4_dequant_amd.stack import (Stack, arena_offsets, buffer_plan, layer_layout,
+                                                  predict_device_bytes)
+
+
+def test_prediction_parts_add_up_and_follow_the_modes():
+    cfg = configs.C3
+    p = predict_device_bytes(cfg)
+    raw = sum(v for k, v in p.items() if k not in ("total", "setup_extra"))
+    n_buffers = len(buffer_plan(cfg))
+    # the arena: every buffer, each 256-byte aligned, rounded up to whole 2 MiB
+    assert raw <= p["total"] < raw + 256 * n_buffers + (2 << 20) and p["total"] % (2 << 20) == 0
+    _, image = layer_layout(cfg)
+    assert p["pool_slots"] == 2 * image
+    assert "resident_images" not in p and "reference_outputs" not in p
+    r = predict_device_bytes(cfg, modes=("streamed", "resident"), reference=True)
+    assert r["resident_images"] == cfg.layers * image
+    assert r["reference_outputs"] == sum(cfg.T * n * 2 for _, _, n in cfg.projections())
+    t = predict_device_bytes(cfg, dequant="staged_t")
+    assert t["staging"] == 2 * p["staging"]
+    # a bf16 base has no staging buffers
+    assert "staging" not in predict_device_bytes(configs.C4)
+    # adapters and their gradients scale with the layer count; the activations do not
+    p3 = predict_device_bytes(cfg, layers=3)
+    assert p3["adapters"] * cfg.layers == p["adapters"] * 3 and p3["inputs"] == p["inputs"]
+    # the arena offsets are 256-byte aligned and do not overlap
+    off, size = arena_offsets(buffer_plan(cfg, modes=("streamed", "resident"), reference=True))
+    spans = sorted((o, o + n) for (key, _, n), o in zip(buffer_plan(cfg, modes=("streamed", "resident"),
+                                                                       reference=True), off.values()))
+    assert all(o % 256 == 0 for o, _ in spans)
+    assert all(a_end <= b0 for (_, a_end), (b0, _) in zip(spans, spans[1:])) and spans[-1][1] <= size
+
+
+def test_refused_before_allocating():
+    pred = predict_device_bytes(configs.C3)
+    with pytest.raises(MemoryError, match="refused"):
+        Stack(configs.C3, hbm_budget=pred["total"] + pred["setup_extra"] - 1)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,layers,modes,reference",
+                         [("C3", 3, ("streamed",), False), ("C3", 3, ("streamed", "resident"), True),
+                          ("C2", None, ("streamed",), True), ("C4", 4, ("streamed",), False)])
+def test_predicted_peak_matches_measured(gpu, name, layers, modes, reference):
+    import torch
+    cfg = configs.CONFIGS[name]
+    print(f"case: predictor {name} layers={layers} modes={modes} reference={reference}", flush=True)
+    gc.collect()
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    st = Stack(cfg, modes=modes, layers=layers, reference=reference)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    for m in modes:
+        st.step(m, reference=reference)
+    torch.cuda.synchronize()
+    measured = torch.cuda.max_memory_allocated() - before
+    want = predict_device_bytes(cfg, modes, layers=layers, reference=reference)["total"]
+    print(f"  predicted {want} B, measured {measured} B", flush=True)
+    # the arena is the only allocation a step holds; the caching allocator may book it in a
+    # cached block up to 1 MiB larger
+    assert 0 <= measured - want <= (1 << 20)
+    st.close()
+    del st
+    gc.collect()
