@@ -363,6 +363,17 @@ def main():
             other["reference_sweep_peak_hbm_ratio"] = round(torch.cuda.max_memory_allocated() / peak_alloc, 3)
             print(f"[bench] streamed with the reference sweep: {other['streamed_with_reference_sweep']} tokens/s",
                   flush=True)
+            # the layers streamed from one file through the pool's file tier (just written, so
+            # the reads come from the page cache)
+            stack.reset_pool(0, source="file")
+            stack.step("streamed")
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                stack.step("streamed")
+            torch.cuda.synchronize()
+            other["streamed_from_file_page_cached"] = round(cfg.T * n / (time.perf_counter() - t0), 1)
+            print(f"[bench] streamed from a file: {other['streamed_from_file_page_cached']} tokens/s", flush=True)
             stack.reset_pool(0)
         if stack.slots is not None:
             other["h2d_GBs"] = round(stack.h2d_rate(), 1)

@@ -276,6 +276,15 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
  * poisoned (0xFF bytes, which decode to NaN) so a stale read cannot go unnoticed.
  * LSN_FAULT_* flags plant deterministic defects for the gate's same-process controls.
  * LSN_POOL_HOST_SIM runs the same state machine on host memory (memcpy, no GPU).
+ * File tier (LSN_POOL_FILE_TIER; "Soup v0.73.0 benchmarks README", record index, the disk tier;
+ * "An 8B Fine-Tune Now Fits in 4 GB of VRAM": the base stays in host RAM, or on NVMe when RAM is
+ * short): layer_pool_create then also allocates two pinned bounce buffers of slot_bytes and
+ * starts an I/O thread. Layers registered with layer_pool_register_file are read by that thread
+ * (8 reader threads per image) into the bounce buffers, alternately, and copied from there on
+ * the copy stream; prefetch() posts the read and returns, and acquire() blocks the calling
+ * host thread until the layer's copy has been enqueued. An I/O failure is reported by the
+ * acquire that needs it (LSN_E_HIP, with the reason). Planted faults and the audit behave as
+ * for host images.
  * ---------------------------------------------------------------------------------------- */
 typedef struct lsn_pool lsn_pool;
 
@@ -283,6 +292,7 @@ enum {
   LSN_POOL_AUDIT = 1u << 0,
   LSN_POOL_KEEP_AT_TURN = 1u << 1,
   LSN_POOL_HOST_SIM = 1u << 2,
+  LSN_POOL_FILE_TIER = 1u << 3,
   LSN_FAULT_STALE_REFETCH = 1u << 8,   /* a layer's second visit skips its copy (stale slot) */
   LSN_FAULT_WRONG_SLOT = 1u << 9       /* a layer's second visit returns another slot */
 };
@@ -306,6 +316,12 @@ lsn_status layer_pool_create(int32_t n_slots, size_t slot_bytes, void *const *sl
 /* host_image: pinned host memory (hipHostMalloc), bytes <= slot_bytes; not modified after. */
 lsn_status layer_pool_register(lsn_pool *pool, int32_t layer, const void *host_image,
                                size_t bytes);
+/* File tier only: the layer's image is `bytes` at `offset` of the file at `path` (opened
+ * read-only and kept open until layer_pool_destroy; the file must not change meanwhile).
+ * LSN_E_ARG if it cannot be opened or is too short; LSN_E_NOFIT if bytes > slot_bytes;
+ * LSN_E_STATE on a pool without LSN_POOL_FILE_TIER or while the layer is in flight. */
+lsn_status layer_pool_register_file(lsn_pool *pool, int32_t layer, const char *path,
+                                    uint64_t offset, size_t bytes);
 lsn_status layer_pool_prefetch(lsn_pool *pool, int32_t layer);
 lsn_status layer_pool_acquire(lsn_pool *pool, int32_t layer, void *compute_stream,
                               const void **dev_image);
@@ -314,7 +330,8 @@ lsn_status layer_pool_stats(const lsn_pool *pool, lsn_pool_stats *out);
 /* Synchronises; compares every recorded slot checksum with its layer's host checksum.
  * LSN_E_AUDIT (with the first mismatching layer and visit in the message) on any mismatch. */
 lsn_status layer_pool_audit(lsn_pool *pool);
-/* Waits for in-flight copies, destroys events; never frees caller memory. */
+/* Finishes the posted reads, waits for in-flight copies, destroys events, frees the bounce
+ * buffers and closes the files; never frees caller memory. */
 lsn_status layer_pool_destroy(lsn_pool *pool);
 
 #ifdef __cplusplus

@@ -13,9 +13,28 @@
 // for `layer` has been enqueued, ready event recorded), ACQUIRED (compute is using it).
 // Two backends share the state machine: HIP (device slots, hipMemcpyAsync on the copy stream,
 // hipEvents) and HOST_SIM (host slots, memcpy, no events) for tests without a GPU.
+//
+// File tier (LSN_POOL_FILE_TIER; "Soup v0.73.0 benchmarks README", record index: the disk tier,
+// and "An 8B Fine-Tune Now Fits in 4 GB of VRAM": the frozen base stays in host RAM, or on NVMe
+// when RAM is short): a layer registered from a file is read by the pool's I/O thread, split
+// over kReaders reader threads, into one of two pinned bounce buffers, and copied from there on
+// the copy stream. The bounce buffers alternate, so the next layer is read while the last one
+// crosses the link; a bounce buffer is reused only after its copy's event. prefetch() posts the
+// fill and returns; acquire() waits (on the host) until the I/O thread has enqueued that fill's
+// copy and recorded its ready event, then makes the compute stream wait for the event.
 
+#include <fcntl.h>
+#include <unistd.h>
+
+#include <atomic>
+#include <cerrno>
+#include <condition_variable>
+#include <cstdlib>
 #include <cstring>
+#include <deque>
+#include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "common.h"
@@ -36,6 +55,7 @@ struct Slot {
   int layer = -1;          // layer whose image the slot holds or is receiving
   bool valid = false;      // holds an intact copy of `layer` (poisoned slots are not valid)
   SlotState state = FREE;
+  uint64_t fill_ticket = 0;  // file tier: the I/O job filling the slot (0: none)
   uint64_t gen = 0;        // number of fills
   uint64_t acquired_gen = 0;
   uint64_t released_tick = 0;
@@ -46,10 +66,21 @@ struct Slot {
 
 struct LayerInfo {
   const void *host = nullptr;
+  int fd = -1;              // file tier: the image is bytes at file_off of this file
+  uint64_t file_off = 0;
   size_t bytes = 0;
   uint64_t checksum = 0;
   int visits = 0;           // prefetches so far (a layer's first visit is 1)
 };
+
+struct FillJob {
+  uint64_t ticket;
+  int slot;
+  int layer;
+  bool skip;                // a planted stale re-fetch: no read, no copy
+};
+
+constexpr int kReaders = 8;
 
 struct AuditRecord {
   int layer;
@@ -76,6 +107,20 @@ struct lsn_pool {
   unsigned long long *d_sums = nullptr;      // device checksums, one per record
   std::vector<uint64_t> h_sums;              // host-sim checksums
   std::vector<AuditRecord> records;
+  // file tier
+  bool file_tier = false;
+  void *bounce[2] = {nullptr, nullptr};      // pinned (host-sim: plain) read buffers
+  hipEvent_t bounce_free[2] = {nullptr, nullptr};
+  bool bounce_used[2] = {false, false};
+  int next_bounce = 0;
+  std::thread io;
+  std::mutex mu;
+  std::condition_variable cv_job, cv_done;
+  std::deque<FillJob> jobs;
+  uint64_t tickets = 0;                      // last ticket handed out
+  uint64_t done = 0;                         // every ticket <= done has been enqueued (in order)
+  bool stop = false;
+  std::string io_error;                      // first I/O-thread failure, reported by acquire
 };
 
 namespace {
@@ -90,7 +135,8 @@ lsn_status check_pool(const lsn_pool *p, const char *what) {
 lsn_status check_layer(const lsn_pool *p, int layer, const char *what) {
   if (layer < 0 || layer >= p->n_layers)
     return fail(LSN_E_ARG, "%s: layer %d out of range [0, %d)", what, layer, p->n_layers);
-  if (!p->layers[layer].host) return fail(LSN_E_STATE, "%s: layer %d not registered", what, layer);
+  if (!p->layers[layer].host && p->layers[layer].fd < 0)
+    return fail(LSN_E_STATE, "%s: layer %d not registered", what, layer);
   return LSN_OK;
 }
 
@@ -147,7 +193,14 @@ lsn_status do_prefetch(lsn_pool *p, int layer) {
   ++L.visits;
   const bool refetch = L.visits >= 2;
   const bool skip_copy = refetch && (p->flags & LSN_FAULT_STALE_REFETCH);
-  if (p->sim) {
+  s.fill_ticket = 0;
+  if (L.fd >= 0) {
+    // file tier: the I/O thread reads and copies; the slot's events are its from here on
+    std::lock_guard<std::mutex> g(p->mu);
+    s.fill_ticket = ++p->tickets;
+    p->jobs.push_back({s.fill_ticket, victim, layer, skip_copy});
+    p->cv_job.notify_one();
+  } else if (p->sim) {
     if (!skip_copy) std::memcpy(s.mem, L.host, L.bytes);
   } else {
     hipError_t e = hipSuccess;
@@ -166,6 +219,77 @@ lsn_status do_prefetch(lsn_pool *p, int layer) {
     p->stats.bytes_copied += L.bytes;
   }
   return LSN_OK;
+}
+
+// Reads bytes at off of fd into dst, split over kReaders threads; false (with errno text in
+// err) on a short or failed read.
+bool read_parallel(int fd, uint64_t off, size_t bytes, void *dst, std::string &err) {
+  std::atomic<bool> ok{true};
+  std::string first_err;
+  std::mutex emu;
+  auto part = [&](int k) {
+    const size_t chunk = (bytes + kReaders - 1) / kReaders;
+    size_t a = (size_t)k * chunk, b = a + chunk < bytes ? a + chunk : bytes;
+    while (a < b) {
+      const ssize_t n = pread(fd, static_cast<char *>(dst) + a, b - a, (off_t)(off + a));
+      if (n <= 0) {
+        std::lock_guard<std::mutex> g(emu);
+        if (first_err.empty()) first_err = n == 0 ? "unexpected end of file" : std::strerror(errno);
+        ok = false;
+        return;
+      }
+      a += (size_t)n;
+    }
+  };
+  std::vector<std::thread> th;
+  for (int k = 1; k < kReaders; ++k) th.emplace_back(part, k);
+  part(0);
+  for (auto &t : th) t.join();
+  if (!ok) err = first_err;
+  return ok;
+}
+
+// The I/O thread: takes fill jobs in order, reads each layer into the next bounce buffer, and
+// enqueues its copy into the job's slot on the copy stream (after the slot's release event).
+void io_loop(lsn_pool *p) {
+  for (;;) {
+    FillJob job;
+    {
+      std::unique_lock<std::mutex> g(p->mu);
+      p->cv_job.wait(g, [&] { return p->stop || !p->jobs.empty(); });
+      if (p->jobs.empty()) return;           // stop requested and nothing left
+      job = p->jobs.front();
+      p->jobs.pop_front();
+    }
+    Slot &s = p->slots[job.slot];
+    const LayerInfo &L = p->layers[job.layer];
+    std::string err;
+    hipError_t e = hipSuccess;
+    if (!job.skip) {
+      const int b = p->next_bounce;
+      p->next_bounce ^= 1;
+      if (!p->sim && p->bounce_used[b]) e = hipEventSynchronize(p->bounce_free[b]);
+      if (e == hipSuccess && !read_parallel(L.fd, L.file_off, L.bytes, p->bounce[b], err)) err = "read: " + err;
+      if (err.empty() && e == hipSuccess) {
+        if (p->sim) {
+          std::memcpy(s.mem, p->bounce[b], L.bytes);
+        } else {
+          if (s.release_recorded) e = hipStreamWaitEvent(p->copy, s.released, 0);
+          if (e == hipSuccess) e = hipMemcpyAsync(s.mem, p->bounce[b], L.bytes, hipMemcpyHostToDevice, p->copy);
+          if (e == hipSuccess) e = hipEventRecord(p->bounce_free[b], p->copy);
+          p->bounce_used[b] = true;
+        }
+      }
+    }
+    if (err.empty() && e == hipSuccess && !p->sim) e = hipEventRecord(s.ready, p->copy);
+    if (e != hipSuccess) err = std::string("HIP: ") + hipGetErrorString(e);
+    {
+      std::lock_guard<std::mutex> g(p->mu);
+      if (!err.empty() && p->io_error.empty()) p->io_error = err;
+      p->done = job.ticket;
+    }
+    p->cv_done.notify_all();
+  }
 }
 
 }  // namespace
@@ -195,6 +319,7 @@ lsn_status layer_pool_create(int32_t n_slots, size_t slot_bytes, void *const *sl
     if (!copy_stream) return fail(LSN_E_ARG, "layer_pool_create: the copy stream must be a created stream");
   }
   lsn_pool *p = new lsn_pool();
+  p->file_tier = (flags & LSN_POOL_FILE_TIER) != 0;
   p->n_slots = n_slots;
   p->slot_bytes = slot_bytes;
   p->n_layers = n_layers;
@@ -216,6 +341,18 @@ lsn_status layer_pool_create(int32_t n_slots, size_t slot_bytes, void *const *sl
     }
   } else if (audit_on(p)) {
     p->h_sums.assign(kAuditCapacity, 0);
+  }
+  if (e == hipSuccess && p->file_tier) {
+    for (int b = 0; b < 2 && e == hipSuccess; ++b) {
+      if (sim) {
+        p->bounce[b] = std::malloc(slot_bytes);
+        if (!p->bounce[b]) e = hipErrorOutOfMemory;
+      } else {
+        e = hipHostMalloc(&p->bounce[b], slot_bytes, hipHostMallocDefault);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->bounce_free[b], hipEventDisableTiming);
+      }
+    }
+    if (e == hipSuccess) p->io = std::thread(io_loop, p);
   }
   if (e != hipSuccess) {
     lsn_status st = check_hip(e, "layer_pool_create");
@@ -245,10 +382,53 @@ lsn_status layer_pool_register(lsn_pool *p, int32_t layer, const void *host_imag
     }
   }
   LayerInfo &L = p->layers[layer];
+  if (L.fd >= 0) {
+    close(L.fd);
+    L.fd = -1;
+  }
   L.host = host_image;
   L.bytes = bytes;
   L.visits = 0;
   L.checksum = audit_on(p) ? checksum_host(host_image, bytes) : 0;
+  return LSN_OK;
+}
+
+lsn_status layer_pool_register_file(lsn_pool *p, int32_t layer, const char *path, uint64_t offset, size_t bytes) {
+  lsn_status st = check_pool(p, "layer_pool_register_file");
+  if (st != LSN_OK) return st;
+  if (!p->file_tier) return fail(LSN_E_STATE, "layer_pool_register_file: pool created without LSN_POOL_FILE_TIER");
+  if (layer < 0 || layer >= p->n_layers)
+    return fail(LSN_E_ARG, "layer_pool_register_file: layer %d out of range [0, %d)", layer, p->n_layers);
+  if (!path || bytes == 0) return fail(LSN_E_ARG, "layer_pool_register_file: empty image");
+  if (bytes % 256 != 0) return fail(LSN_E_ARG, "layer_pool_register_file: image bytes must be a multiple of 256");
+  if (bytes > p->slot_bytes)
+    return fail(LSN_E_NOFIT, "layer_pool_register_file: layer %d image (%zu B) does not fit a slot (%zu B)",
+                layer, bytes, p->slot_bytes);
+  if (find_slot(p, layer, PENDING) >= 0 || find_slot(p, layer, ACQUIRED) >= 0)
+    return fail(LSN_E_STATE, "layer_pool_register_file: layer %d is in flight", layer);
+  const int fd = open(path, O_RDONLY | O_CLOEXEC);
+  if (fd < 0) return fail(LSN_E_ARG, "layer_pool_register_file: cannot open %s: %s", path, std::strerror(errno));
+  const off_t end = lseek(fd, 0, SEEK_END);
+  if (end < 0 || (uint64_t)end < offset + bytes) {
+    close(fd);
+    return fail(LSN_E_ARG, "layer_pool_register_file: %s holds %lld B, the image needs %llu B at offset %llu",
+                path, (long long)end, (unsigned long long)bytes, (unsigned long long)offset);
+  }
+  LayerInfo &L = p->layers[layer];
+  if (L.fd >= 0) close(L.fd);
+  L.host = nullptr;
+  L.fd = fd;
+  L.file_off = offset;
+  L.bytes = bytes;
+  L.visits = 0;
+  L.checksum = 0;
+  if (audit_on(p)) {
+    std::vector<uint64_t> tmp(bytes / 8);
+    std::string err;
+    if (!read_parallel(fd, offset, bytes, tmp.data(), err))
+      return fail(LSN_E_ARG, "layer_pool_register_file: reading %s: %s", path, err.c_str());
+    L.checksum = checksum_host(tmp.data(), bytes);
+  }
   return LSN_OK;
 }
 
@@ -275,6 +455,11 @@ lsn_status layer_pool_acquire(lsn_pool *p, int32_t layer, void *compute_stream, 
     i = find_slot(p, layer, PENDING);
   }
   Slot &s = p->slots[i];
+  if (s.fill_ticket) {
+    std::unique_lock<std::mutex> g(p->mu);
+    p->cv_done.wait(g, [&] { return p->done >= s.fill_ticket || !p->io_error.empty(); });
+    if (!p->io_error.empty()) return fail(LSN_E_HIP, "layer_pool_acquire: file tier: %s", p->io_error.c_str());
+  }
   if (!p->sim) {
     const hipError_t e = hipStreamWaitEvent((hipStream_t)compute_stream, s.ready, 0);
     if (e != hipSuccess) return check_hip(e, "layer_pool_acquire wait");
@@ -370,6 +555,16 @@ lsn_status layer_pool_audit(lsn_pool *p) {
 lsn_status layer_pool_destroy(lsn_pool *p) {
   if (!p) return LSN_OK;
   hipError_t e = hipSuccess;
+  if (p->io.joinable()) {
+    {
+      std::lock_guard<std::mutex> g(p->mu);
+      p->stop = true;
+    }
+    p->cv_job.notify_all();
+    p->io.join();                            // finishes the jobs already posted
+  }
+  for (LayerInfo &L : p->layers)
+    if (L.fd >= 0) close(L.fd);
   if (!p->sim) {
     if (p->copy) e = hipStreamSynchronize(p->copy);
     for (Slot &s : p->slots) {
@@ -377,6 +572,12 @@ lsn_status layer_pool_destroy(lsn_pool *p) {
       if (s.released) (void)hipEventDestroy(s.released);
     }
     if (p->d_sums) (void)hipFree(p->d_sums);
+    for (int b = 0; b < 2; ++b) {
+      if (p->bounce[b]) (void)hipHostFree(p->bounce[b]);
+      if (p->bounce_free[b]) (void)hipEventDestroy(p->bounce_free[b]);
+    }
+  } else {
+    for (int b = 0; b < 2; ++b) std::free(p->bounce[b]);
   }
   delete p;
   return check_hip(e, "layer_pool_destroy");

@@ -25,14 +25,14 @@ OUT_BF16, OUT_F32, OUT_BF16_T = 0, 1, 2
 ADAPTERS_OFF, ADAPTERS_ON, ADAPTERS_U_READY = 0, 1, 2
 DX_BF16_SET, DX_F32_ADD = 0, 1
 GRAD_SET, GRAD_ADD = 0, 1
-POOL_AUDIT, POOL_KEEP_AT_TURN, POOL_HOST_SIM = 1, 2, 4
+POOL_AUDIT, POOL_KEEP_AT_TURN, POOL_HOST_SIM, POOL_FILE_TIER = 1, 2, 4, 8
 FAULT_STALE_REFETCH, FAULT_WRONG_SLOT = 1 << 8, 1 << 9
 
 EXPORTS = (
     "lsn_last_error", "lsn_abi_version", "lsn_nf4_codebook", "nf4_pack_ws_bytes", "nf4_pack",
     "nf4_dequant", "nf4_dequant_batch", "lora_down", "lora_linear_ws_bytes", "lora_linear_fwd", "lora_linear_fwd_group",
     "lora_linear_bwd", "lora_linear_group_ws_bytes", "lora_linear_bwd_group",
-    "layer_pool_create", "layer_pool_register", "layer_pool_prefetch", "layer_pool_acquire",
+    "layer_pool_create", "layer_pool_register", "layer_pool_register_file", "layer_pool_prefetch", "layer_pool_acquire",
     "layer_pool_release", "layer_pool_stats", "layer_pool_audit", "layer_pool_destroy",
 )
 
@@ -110,6 +110,7 @@ def load():
         "layer_pool_create": (i32, [i32, sz, ctypes.POINTER(vp), i32, vp, ctypes.c_uint32,
                                     ctypes.POINTER(vp)]),
         "layer_pool_register": (i32, [vp, i32, vp, sz]),
+        "layer_pool_register_file": (i32, [vp, i32, ctypes.c_char_p, ctypes.c_uint64, sz]),
         "layer_pool_prefetch": (i32, [vp, i32]),
         "layer_pool_acquire": (i32, [vp, i32, vp, ctypes.POINTER(vp)]),
         "layer_pool_release": (i32, [vp, i32, vp]),
@@ -311,6 +312,10 @@ class LayerPool:
 
     def register(self, layer: int, host_ptr: int, nbytes: int) -> None:
         check(load().layer_pool_register(self.h, layer, host_ptr, nbytes))
+
+    def register_file(self, layer: int, path: str, offset: int, nbytes: int) -> None:
+        """File tier: the layer's image is nbytes at offset of the file at path."""
+        check(load().layer_pool_register_file(self.h, layer, os.fsencode(path), offset, nbytes))
 
     def prefetch(self, layer: int) -> None:
         check(load().layer_pool_prefetch(self.h, layer))

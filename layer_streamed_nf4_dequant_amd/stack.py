@@ -31,6 +31,7 @@ input gradients and the LoRA gradients below it.
 
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -301,8 +302,10 @@ class Stack:
         self.checks = {}
         torch.cuda.synchronize()
 
-    def reset_pool(self, flags: int = 0, n_slots: int | None = None):
-        """(Re)create the layer pool with the given flags and slot count over the same images."""
+    def reset_pool(self, flags: int = 0, n_slots: int | None = None, source: str = "ram"):
+        """(Re)create the layer pool with the given flags and slot count over the same images.
+        source "ram": the pinned host images; "file": the same bytes in one file (the pool's
+        file tier reads them; the file is written on first use, see write_image_file)."""
         torch = self.torch
         torch.cuda.synchronize()
         if self.pool is not None:
@@ -310,10 +313,31 @@ class Stack:
         if n_slots is not None and n_slots != len(self.slots):
             self.slots = [torch.empty(self.image_bytes, dtype=torch.uint8, device=self.dev)
                           for _ in range(n_slots)]
+        if source == "file":
+            path = self.write_image_file()
+            flags |= lib.POOL_FILE_TIER
+        elif source != "ram":
+            raise ValueError(source)
         self.pool = lib.LayerPool([t.data_ptr() for t in self.slots], self.image_bytes, self.L,
                                   self.copy_stream.cuda_stream, flags)
         for l in range(self.L):
-            self.pool.register(l, self.host_images[l].data_ptr(), self.image_bytes)
+            if source == "file":
+                self.pool.register_file(l, path, l * self.image_bytes, self.image_bytes)
+            else:
+                self.pool.register(l, self.host_images[l].data_ptr(), self.image_bytes)
+
+    def write_image_file(self, directory: str | None = None) -> str:
+        """Writes the layer images, back to back, to one file (in `directory`, else a new
+        temporary directory) for the pool's file tier; returns its path. Removed by close()."""
+        if getattr(self, "image_file", None) is None:
+            import tempfile
+            d = tempfile.mkdtemp(prefix="lsnf4_images_", dir=directory)
+            path = os.path.join(d, "layers.bin")
+            with open(path, "wb") as f:
+                for img in self.host_images:
+                    f.write(memoryview(img.numpy()))
+            self.image_file = path
+        return self.image_file
 
     # ------------------------------------------------------------------------------------------
     def _nf4_desc(self, base: int, l: int, j: int) -> lib.NF4Desc:
@@ -519,3 +543,8 @@ class Stack:
         if self.pool is not None:
             self.pool.close()
             self.pool = None
+        path = getattr(self, "image_file", None)
+        if path is not None:
+            os.remove(path)
+            os.rmdir(os.path.dirname(path))
+            self.image_file = None

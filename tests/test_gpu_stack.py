@@ -45,28 +45,32 @@ def recompute_matches_forward(checks, L, n_proj):
 
 
 def test_toy_8b_shapes_exactness_and_controls(gpu):
-    """Three 8B-shaped layers: streamed (2, 1 and 3 slots; KEEP_AT_TURN; audit on) equals
-    resident bit for bit; each planted defect leaves the forward exact but breaks gradients,
-    and the audit reports it."""
+    """Three 8B-shaped layers: streamed (2, 1 and 3 slots; KEEP_AT_TURN; audit on; from pinned
+    host memory and from a file through the pool's file tier) equals resident bit for bit; each
+    planted defect leaves the forward exact but breaks gradients, and the audit reports it."""
     cfg = configs.C3
     print("case: 3-layer 8B-shaped toy", flush=True)
     st = Stack(cfg, modes=("streamed", "resident"), record=True, layers=3)
     st.step("resident")
     ref = snapshot(st)
     assert recompute_matches_forward(ref[0], 3, 7)
-    variants = [("2 slots", 0, None), ("1 slot", 0, 1), ("3 slots", 0, 3),
-                ("keep at turn", lib.POOL_KEEP_AT_TURN, 2), ("audit", lib.POOL_AUDIT, 2)]
-    for name, flags, n_slots in variants:
+    variants = [("2 slots", 0, None, "ram"), ("1 slot", 0, 1, "ram"), ("3 slots", 0, 3, "ram"),
+                ("keep at turn", lib.POOL_KEEP_AT_TURN, 2, "ram"), ("audit", lib.POOL_AUDIT, 2, "ram"),
+                ("file", 0, 2, "file"), ("file, audit", lib.POOL_AUDIT, 2, "file"),
+                ("file, 1 slot, keep at turn", lib.POOL_KEEP_AT_TURN, 1, "file")]
+    for name, flags, n_slots, source in variants:
         print(f"  variant {name}", flush=True)
-        st.reset_pool(flags, n_slots)
+        st.reset_pool(flags, n_slots, source)
         st.step("streamed")
         if flags & lib.POOL_AUDIT:
             st.pool.audit()
         fwd, re, dx, eq, n = compare(ref, snapshot(st))
         assert fwd and re and dx and eq == n, (name, fwd, re, dx, eq, n)
-    for name, fault in (("stale re-fetch", lib.FAULT_STALE_REFETCH), ("wrong slot", lib.FAULT_WRONG_SLOT)):
+    for name, fault, source in (("stale re-fetch", lib.FAULT_STALE_REFETCH, "ram"),
+                                ("wrong slot", lib.FAULT_WRONG_SLOT, "ram"),
+                                ("stale re-fetch, file", lib.FAULT_STALE_REFETCH, "file")):
         print(f"  control {name}", flush=True)
-        st.reset_pool(fault, 2)
+        st.reset_pool(fault, 2, source)
         st.step("streamed")
         got = snapshot(st)
         fwd, re, dx, eq, n = compare(ref, got)
@@ -74,7 +78,7 @@ def test_toy_8b_shapes_exactness_and_controls(gpu):
         assert eq < n and not re and not dx, \
             f"{name}: the planted defect must break the backward ({eq}/{n} gradient tensors equal)"
         assert not recompute_matches_forward(got[0], 3, 7)
-        st.reset_pool(fault | lib.POOL_AUDIT, 2)
+        st.reset_pool(fault | lib.POOL_AUDIT, 2, source)
         st.step("streamed")
         with pytest.raises(lib.LsnError) as e:
             st.pool.audit()

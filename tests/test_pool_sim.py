@@ -155,3 +155,93 @@ def test_planted_faults_corrupt_only_the_second_visit_and_the_audit_catches_them
         q.pool.audit()
     assert e.value.status == lib.LSN_E_AUDIT
     assert q.pool.stats()["audit_failures"] > 0
+
+
+# ---- file tier (LSN_POOL_FILE_TIER): the images are read from files by the pool's I/O thread ----
+
+class FilePool(SimPool):
+    """SimPool whose layers live in one file (each image at its own offset), read by the pool."""
+
+    def __init__(self, tmp_path, n_slots=2, n_layers=4, flags=0, offset0=512):
+        self.slots = [aligned(SLOT) for _ in range(n_slots)]
+        rng = np.random.default_rng(1)
+        self.images = [rng.integers(0, 255, SLOT, dtype=np.uint8) for _ in range(n_layers)]
+        self.path = str(tmp_path / "base.bin")
+        self.offsets = [offset0 + l * (SLOT + 256) for l in range(n_layers)]
+        blob = np.zeros(self.offsets[-1] + SLOT, dtype=np.uint8)
+        for off, img in zip(self.offsets, self.images):
+            blob[off:off + SLOT] = img
+        blob.tofile(self.path)
+        self.pool = lib.LayerPool([s.ctypes.data for s in self.slots], SLOT, n_layers, None,
+                                  flags | lib.POOL_HOST_SIM | lib.POOL_FILE_TIER)
+        for l, off in enumerate(self.offsets):
+            self.pool.register_file(l, self.path, off, SLOT)
+
+
+def test_file_tier_every_visit_sees_its_own_layer(tmp_path):
+    p = FilePool(tmp_path, n_slots=2, n_layers=5)
+    for kind, l, data in forward_backward(p, 5):
+        np.testing.assert_array_equal(data, p.images[l], err_msg=f"{kind} visit of layer {l}")
+    st = p.pool.stats()
+    assert st["copies"] == 10 and st["bytes_copied"] == 10 * SLOT and st["misses"] == 0
+    p.pool.close()
+
+
+@pytest.mark.parametrize("n_slots", [2, 3])
+def test_file_tier_other_slot_counts_and_keep_at_turn(tmp_path, n_slots):
+    p = FilePool(tmp_path, n_slots=n_slots, n_layers=4, flags=lib.POOL_KEEP_AT_TURN)
+    for kind, l, data in forward_backward(p, 4):
+        np.testing.assert_array_equal(data, p.images[l], err_msg=f"{kind} visit of layer {l}")
+    assert p.pool.stats()["hits"] >= 1
+    p.pool.close()
+
+
+def test_file_tier_single_slot_without_prefetch_ahead(tmp_path):
+    p = FilePool(tmp_path, n_slots=1, n_layers=3)
+    for l in (0, 1, 2, 2, 1, 0):
+        np.testing.assert_array_equal(p.visit(l), p.images[l])
+    assert p.pool.stats()["misses"] == 6
+    p.pool.close()
+
+
+def test_file_tier_audit_and_planted_fault(tmp_path):
+    p = FilePool(tmp_path, n_layers=4, flags=lib.POOL_AUDIT)
+    forward_backward(p, 4)
+    p.pool.audit()                                   # clean run: every checksum matches the file
+    q = FilePool(tmp_path, n_layers=4, flags=lib.POOL_AUDIT | lib.FAULT_STALE_REFETCH)
+    forward_backward(q, 4)
+    with pytest.raises(lib.LsnError) as e:
+        q.pool.audit()
+    assert e.value.status == lib.LSN_E_AUDIT
+    p.pool.close()
+    q.pool.close()
+
+
+def test_file_tier_refusals(tmp_path):
+    p = FilePool(tmp_path, n_layers=2)
+    with pytest.raises(lib.LsnError) as e:           # missing file
+        p.pool.register_file(0, str(tmp_path / "nope.bin"), 0, SLOT)
+    assert e.value.status == lib.LSN_E_ARG
+    with pytest.raises(lib.LsnError) as e:           # image past the end of the file
+        p.pool.register_file(0, p.path, p.offsets[-1] + 256, SLOT)
+    assert e.value.status == lib.LSN_E_ARG
+    with pytest.raises(lib.LsnError) as e:           # larger than a slot
+        p.pool.register_file(0, p.path, 0, 2 * SLOT)
+    assert e.value.status == lib.LSN_E_NOFIT
+    plain = SimPool(n_layers=2)                      # a pool without the file tier
+    with pytest.raises(lib.LsnError) as e:
+        plain.pool.register_file(0, p.path, 0, SLOT)
+    assert e.value.status == lib.LSN_E_STATE
+    p.pool.close()
+
+
+def test_file_tier_read_error_is_reported_by_acquire(tmp_path):
+    p = FilePool(tmp_path, n_layers=2)
+    # shrink the file behind the pool's back: the read of layer 1 comes up short
+    with open(p.path, "r+b") as f:
+        f.truncate(p.offsets[1] + 16)
+    p.pool.prefetch(1)
+    with pytest.raises(lib.LsnError) as e:
+        p.pool.acquire(1, None)
+    assert e.value.status == lib.LSN_E_HIP and "end of file" in str(e.value)
+    p.pool.close()
