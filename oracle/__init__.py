@@ -20,10 +20,15 @@ lora
     The LoRA linear on a frozen base, forward and analytic backward, in float64.
     Source: "Can You Fine-Tune a 27B Model on a Laptop?", transcript @1:25-1:58 (frozen base,
     a thin pair of trainable matrices per layer); the formulas are the standard LoRA ones.
+ce
+    The frozen embedding lookup and token-level cross-entropy through the frozen LM head
+    (loss, logit gradient, hidden-state gradient), in float64.  Source: "Can You Fine-Tune a
+    27B Model on a Laptop?", transcript @7:42-7:55 (resident, unquantised embedding and output
+    head); the formulas are the standard cross-entropy ones.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms, invariants,
 brute force and finite differences. Parity with the pages themselves is unpinned where
 the pages print no values (they print no codebook, tensor or checksum).
 """
 
-from . import nf4, lora  # noqa: F401
+from . import ce, nf4, lora  # noqa: F401
