@@ -253,6 +253,41 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
                                  void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------------------------
+ * The resident ends of the stack ("Can You Fine-Tune a 27B Model on a Laptop? (I Did the
+ * Math)", transcript @7:42-7:55: the embedding table and the output head stay resident and
+ * unquantised; "Exact Layer Streaming", Abstract: the cross-entropy logits term, 14 bytes per
+ * logit element measured against 6 by first principles).
+ * ---------------------------------------------------------------------------------------- */
+
+/* Device workspace bytes lm_head_ce needs: 6 bytes per logit element of one chunk
+ * (fp32 logits and bf16 logit gradients of min(chunk_rows, T) rows x V). */
+size_t lm_head_ce_ws_bytes(int64_t chunk_rows, int64_t V);
+
+/*
+ * lm_head_ce - cross-entropy through a frozen LM head W [V][H] (bf16, device) for the final
+ * hidden states h [T][H] (bf16, device) and labels [T] (int32, device; a label outside [0, V)
+ * marks an ignored row), chunked over rows so that only chunk_rows x V logits exist at a time:
+ *   z = h W^T (fp32 accumulate), lse_t = log sum_j exp z_tj,
+ *   loss[t] = lse_t - z_t,label_t (fp32, device; 0 for ignored rows),
+ *   dh = bf16( (softmax(z) - onehot(label)) * grad_scale ) W, rounded to bf16 (device [T][H];
+ *        zero rows for ignored rows). grad_scale is typically 1 / (number of counted rows).
+ * Rows are independent, so the results do not depend on chunk_rows. H, V: multiples of 64.
+ * ws: device, 256-byte aligned, at least lm_head_ce_ws_bytes(chunk_rows, V). Overlaps between
+ * outputs and inputs give LSN_E_ARG. Async on `stream`.
+ */
+lsn_status lm_head_ce(int64_t T, int64_t H, int64_t V, const uint16_t *h, const uint16_t *W,
+                      const int32_t *labels, float grad_scale, float *loss, uint16_t *dh,
+                      int64_t chunk_rows, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * embedding_gather - X[t] = E[ids[t]] for a frozen embedding table E [V][H] (bf16, device) and
+ * ids [T] (int32, device); X [T][H] bf16 (device). An id outside [0, V) gives a zero row and
+ * adds 1 to *bad_ids (device int32; may be null). H: a multiple of 8. Async on `stream`.
+ */
+lsn_status embedding_gather(int64_t T, int64_t H, int64_t V, const int32_t *ids, const uint16_t *E,
+                            uint16_t *X, int32_t *bad_ids, void *stream);
+
+/* ------------------------------------------------------------------------------------------
  * Layer pool ("Exact Layer Streaming", Abstract; transcript @7:11-7:32; "An 8B Fine-Tune
  * Now Fits in 4 GB of VRAM"): n_slots caller-owned device slots hold decoder-layer images;
  * each layer's image lives in pinned host memory; copies run on the pool's copy stream and

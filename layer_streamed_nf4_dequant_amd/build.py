@@ -32,6 +32,7 @@ SOURCES = [
     "gemm.hip",
     "lora_small.hip",
     "pool_kernels.hip",
+    "ce.hip",
 ]
 
 COMMON = [

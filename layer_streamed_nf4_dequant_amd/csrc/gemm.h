@@ -8,7 +8,7 @@ namespace lsn {
 
 enum { GEMM_NT = 0, GEMM_NN = 1 };        // forward Y = act W^T ; backward dX = act W
 enum { W_IS_NF4 = 0, W_IS_BF16 = 1 };
-enum { EPI_BF16 = 0, EPI_F32_ADD = 1 };
+enum { EPI_BF16 = 0, EPI_F32_ADD = 1, EPI_F32_SET = 2 };   // bf16 store, fp32 add into, fp32 store
 
 struct GemmArgs {
   int64_t M;            // rows of act and out (tokens)

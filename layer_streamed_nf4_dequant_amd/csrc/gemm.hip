@@ -825,8 +825,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
         if (m < a.M && n < sg.N) {
           const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1], v2 = acc[i][j][4 * g + 2],
                       v3 = acc[i][j][4 * g + 3];
-          {
-            floatx4_t *o = reinterpret_cast<floatx4_t *>(reinterpret_cast<float *>(sg.out) + m * sg.N + n);
+          floatx4_t *o = reinterpret_cast<floatx4_t *>(reinterpret_cast<float *>(sg.out) + m * sg.N + n);
+          if constexpr (EPI == EPI_F32_SET) {
+            const floatx4_t v = {v0, v1, v2, v3};
+            __builtin_nontemporal_store(v, o);
+          } else {
             floatx4_t cur = *o;
             cur[0] = __fadd_rn(cur[0], v0);
             cur[1] = __fadd_rn(cur[1], v1);
@@ -905,6 +908,7 @@ lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s) {
   if (a.b_red_major)
     return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, false, true>(a, s)
                            : launch_direct_one<EPI_F32_ADD, false, true>(a, s);
+  if (epi == EPI_F32_SET) return launch_direct_one<EPI_F32_SET, false, false>(a, s);
   return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, false, false>(a, s)
                          : launch_direct_one<EPI_F32_ADD, false, false>(a, s);
 }

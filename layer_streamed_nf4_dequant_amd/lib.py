@@ -34,6 +34,7 @@ EXPORTS = (
     "lora_linear_bwd", "lora_linear_group_ws_bytes", "lora_linear_bwd_group",
     "layer_pool_create", "layer_pool_register", "layer_pool_register_file", "layer_pool_prefetch", "layer_pool_acquire",
     "layer_pool_release", "layer_pool_stats", "layer_pool_audit", "layer_pool_destroy",
+    "lm_head_ce_ws_bytes", "lm_head_ce", "embedding_gather",
 )
 
 
@@ -117,6 +118,9 @@ def load():
         "layer_pool_stats": (i32, [vp, ctypes.POINTER(PoolStats)]),
         "layer_pool_audit": (i32, [vp]),
         "layer_pool_destroy": (i32, [vp]),
+        "lm_head_ce_ws_bytes": (sz, [i64, i64]),
+        "lm_head_ce": (i32, [i64, i64, i64, vp, vp, vp, f32, vp, vp, i64, vp, sz, vp]),
+        "embedding_gather": (i32, [i64, i64, i64, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -346,3 +350,23 @@ class LayerPool:
             self.close()
         except Exception:
             pass
+
+
+def lm_head_ce_ws_bytes(chunk_rows: int, V: int) -> int:
+    return int(load().lm_head_ce_ws_bytes(chunk_rows, V))
+
+
+def lm_head_ce(h, W, labels, grad_scale: float, loss, dh, chunk_rows: int, ws, stream=None) -> None:
+    """loss[t] = logsumexp(h W^T)_t - (h W^T)_t,label (fp32) and dh = bf16(bf16(dlogits) W), chunked
+    over rows (labels outside [0, V): ignored rows)."""
+    T, H = h.shape
+    V = W.shape[0]
+    check(load().lm_head_ce(T, H, V, _ptr(h), _ptr(W), _ptr(labels), float(grad_scale), _ptr(loss), _ptr(dh),
+                            chunk_rows, _ptr(ws), ws.numel() * ws.element_size(), _stream_handle(stream)))
+
+
+def embedding_gather(ids, E, X, bad_ids=None, stream=None) -> None:
+    """X[t] = E[ids[t]]; out-of-range ids give zero rows and are counted in bad_ids (int32)."""
+    T = ids.shape[0]
+    V, H = E.shape
+    check(load().embedding_gather(T, H, V, _ptr(ids), _ptr(E), _ptr(X), _ptr(bad_ids), _stream_handle(stream)))
