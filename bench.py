@@ -119,6 +119,40 @@ def clock_sampler():
     return finish
 
 
+def lm_head_figure(cfg, vocab: int = 128256, chunk: int = 512, iters: int = 5):
+    """The resident LM head's cross-entropy (lm_head_ce) at the workload's T and hidden width with
+    a Llama-3.1 vocabulary: time per call, its two GEMMs' rate (4 T V H FLOPs per call), and the
+    workspace per logit element of a chunk."""
+    import torch
+    from layer_streamed_nf4_dequant_amd import inputs, lib
+    T, H, V = cfg.T, cfg.hidden, vocab
+    h = inputs.device_normal((T, H), 1.0, 0, "bench ce", "h", dtype=torch.bfloat16)
+    W = inputs.device_normal((V, H), 0.02, 0, "bench ce", "W", dtype=torch.bfloat16)
+    labels = torch.randint(0, V, (T,), generator=inputs.device_generator(0, "bench ce", "labels"),
+                           device="cuda", dtype=torch.int32)
+    loss = torch.empty(T, dtype=torch.float32, device="cuda")
+    dh = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws_bytes = lib.lm_head_ce_ws_bytes(chunk, H, V)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    lib.lm_head_ce(h, W, labels, 1.0 / T, loss, dh, chunk, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        lib.lm_head_ce(h, W, labels, 1.0 / T, loss, dh, chunk, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    out = {"vocab": V, "hidden": H, "tokens": T, "chunk_rows": chunk, "ms_per_call": round(ms, 3),
+           "gemm_tflops": round(4 * T * V * H / (ms * 1e-3) / 1e12, 1),
+           "workspace_bytes_per_logit_element": round(ws_bytes / (chunk * V), 3),
+           "logits_bytes_per_logit_element": 6,
+           "mean_loss": round(float(loss.mean()), 4)}
+    del h, W, labels, loss, dh, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def hipblaslt_ceiling(cfg, iters: int = 10):
     """Same-session reference: torch.matmul (hipBLASLt) bf16 X W^T at the stack's projection shapes
     and T, TFLOP/s per shape (no LoRA term)."""
@@ -377,6 +411,8 @@ def main():
             stack.reset_pool(0)
         if stack.slots is not None:
             other["h2d_GBs"] = round(stack.h2d_rate(), 1)
+        other["lm_head_ce"] = lm_head_figure(cfg)
+        print(f"[bench] lm_head_ce: {other['lm_head_ce']}", flush=True)
 
     tokens = cfg.T * args.steps
     value = tokens / wall

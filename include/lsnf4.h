@@ -260,8 +260,9 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
  * ---------------------------------------------------------------------------------------- */
 
 /* Device workspace bytes lm_head_ce needs: 6 bytes per logit element of one chunk
- * (fp32 logits and bf16 logit gradients of min(chunk_rows, T) rows x V). */
-size_t lm_head_ce_ws_bytes(int64_t chunk_rows, int64_t V);
+ * (fp32 logits and bf16 logit gradients of min(chunk_rows, T) rows x V), plus the fp32 partial
+ * products of the chunk's hidden-state gradient (up to 8 x chunk_rows x H x 4 bytes). */
+size_t lm_head_ce_ws_bytes(int64_t chunk_rows, int64_t H, int64_t V);
 
 /*
  * lm_head_ce - cross-entropy through a frozen LM head W [V][H] (bf16, device) for the final
@@ -272,7 +273,7 @@ size_t lm_head_ce_ws_bytes(int64_t chunk_rows, int64_t V);
  *   dh = bf16( (softmax(z) - onehot(label)) * grad_scale ) W, rounded to bf16 (device [T][H];
  *        zero rows for ignored rows). grad_scale is typically 1 / (number of counted rows).
  * Rows are independent, so the results do not depend on chunk_rows. H, V: multiples of 64.
- * ws: device, 256-byte aligned, at least lm_head_ce_ws_bytes(chunk_rows, V). Overlaps between
+ * ws: device, 256-byte aligned, at least lm_head_ce_ws_bytes(chunk_rows, H, V). Overlaps between
  * outputs and inputs give LSN_E_ARG. Async on `stream`.
  */
 lsn_status lm_head_ce(int64_t T, int64_t H, int64_t V, const uint16_t *h, const uint16_t *W,

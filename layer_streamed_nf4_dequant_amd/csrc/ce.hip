@@ -11,7 +11,9 @@
 //   z  = h_c W^T          (fp32, [rows][V])
 //   lse_t = max_j z_tj + log sum_j exp(z_tj - max_j z_tj),  loss_t = lse_t - z_t,label_t
 //   dz = bf16( (softmax(z)_tj - [j == label_t]) * scale )
-//   dh_c = bf16( dz W )   (a reduction over the vocabulary: W read reduction-major)
+//   dh_c = bf16( dz W )   (a reduction over the vocabulary: W read reduction-major, split over
+//                          kCeSplit ranges of the vocabulary whose fp32 partials are then added
+//                          in order: a chunk has few output tiles and a very long reduction)
 // A row whose label is negative is ignored: loss 0, dz 0.
 
 #include <cmath>
@@ -26,6 +28,9 @@ bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb);
 namespace {
 
 constexpr int kCeThreads = 256;
+constexpr int kCeSplit = 8;   // vocabulary ranges of the dh product (fixed: results do not depend on the chunk)
+
+int ce_splits(int64_t V) { return (int)(V / 64 < kCeSplit ? V / 64 : kCeSplit); }
 
 // (max, sum of exp(x - max)) pairs combined in a fixed order: the result depends only on the row
 __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2) {
@@ -121,9 +126,10 @@ using namespace lsn;
 
 extern "C" {
 
-size_t lm_head_ce_ws_bytes(int64_t chunk_rows, int64_t V) {
-  if (chunk_rows < 1 || V < 1) return 0;
-  return align256((size_t)(chunk_rows * V * 4)) + align256((size_t)(chunk_rows * V * 2));
+size_t lm_head_ce_ws_bytes(int64_t chunk_rows, int64_t H, int64_t V) {
+  if (chunk_rows < 1 || H < 1 || V < 64) return 0;
+  return align256((size_t)(chunk_rows * V * 4)) + align256((size_t)(chunk_rows * V * 2)) +
+         align256((size_t)(ce_splits(V) * chunk_rows * H * 4));
 }
 
 lsn_status lm_head_ce(int64_t T, int64_t H, int64_t V, const uint16_t *h, const uint16_t *W, const int32_t *labels,
@@ -139,7 +145,7 @@ lsn_status lm_head_ce(int64_t T, int64_t H, int64_t V, const uint16_t *h, const 
     return fail(LSN_E_ARG, "lm_head_ce: h, W, dh must be 16-byte and ws 256-byte aligned");
   if (!std::isfinite(grad_scale)) return fail(LSN_E_ARG, "lm_head_ce: grad_scale must be finite");
   const int64_t rows_max = chunk_rows < T ? chunk_rows : T;
-  const size_t need = lm_head_ce_ws_bytes(rows_max, V);
+  const size_t need = lm_head_ce_ws_bytes(rows_max, H, V);
   if (ws_bytes < need)
     return fail(LSN_E_ARG, "lm_head_ce: workspace too small (%zu < %zu)", ws_bytes, need);
   const size_t hb = (size_t)(T * H * 2), wb = (size_t)(V * H * 2);
@@ -159,6 +165,8 @@ lsn_status lm_head_ce(int64_t T, int64_t H, int64_t V, const uint16_t *h, const 
   hipStream_t s = (hipStream_t)stream;
   float *z = static_cast<float *>(ws);
   uint16_t *dz = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + align256((size_t)(rows_max * V * 4)));
+  float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(dz) + align256((size_t)(rows_max * V * 2)));
+  const int S = ce_splits(V);
   for (int64_t c0 = 0; c0 < T; c0 += rows_max) {
     const int64_t rows = T - c0 < rows_max ? T - c0 : rows_max;
     DirectArgs d{};                                   // z = h_c W^T, fp32
@@ -173,16 +181,24 @@ lsn_status lm_head_ce(int64_t T, int64_t H, int64_t V, const uint16_t *h, const 
     hipLaunchKernelGGL(k_ce_rows, dim3((unsigned)rows), dim3(kCeThreads), 0, s, z, V, labels + c0, grad_scale,
                        loss + c0, dz);
     if ((st = check_hip(hipGetLastError(), "k_ce_rows launch")) != LSN_OK) return st;
-    DirectArgs e{};                                   // dh_c = dz W, a reduction over V
+    DirectArgs e{};                                   // dh_c = dz W, a reduction over V, split
     e.M = rows;
     e.K = V;
     e.act = dz;
     e.nseg = 1;
     e.seg[0].N = H;
     e.seg[0].w = W;
-    e.seg[0].out = dh + c0 * H;
+    e.seg[0].out = part;
     e.b_red_major = 1;
-    if ((st = launch_gemm_direct(e, EPI_BF16, s)) != LSN_OK) return st;
+    e.ksplit = S;
+    if (S > 1) {
+      if ((st = launch_gemm_direct(e, EPI_F32_SET, s)) != LSN_OK) return st;
+      if ((st = launch_splitk_reduce(part, S, rows * H, dh + c0 * H, s)) != LSN_OK) return st;
+    } else {
+      e.ksplit = 0;
+      e.seg[0].out = dh + c0 * H;
+      if ((st = launch_gemm_direct(e, EPI_BF16, s)) != LSN_OK) return st;
+    }
   }
   return LSN_OK;
 }

@@ -67,9 +67,12 @@ struct DirectArgs {
   float scale;
   int adapters;
   int b_red_major;       // B operand stored [K][N] (N contiguous) instead of [N][K]
+  int ksplit;            // > 1: split-K into fp32 partials out + s M N (reduction-major B, fp32 store)
   int scale_pow2;        // set by launch_gemm_direct
 };
 lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s);
+// out[i] = bf16( sum_{s < S} partial[s][i] ), in split order, for i < n (n % 4 == 0)
+lsn_status launch_splitk_reduce(const float *partial, int S, int64_t n, uint16_t *out, hipStream_t s);
 
 // up to 8 low-rank row projections sharing one activation: out_g = bf16(act P_g^T)
 struct RowProjSet {

@@ -558,7 +558,10 @@ __device__ __forceinline__ void tile_coords(int64_t b, int64_t ntiles, int64_t t
   nt = in / gm;
 }
 
-template <int EPI, bool KSEG, bool BT>
+// SPLIT (split-K): the grid holds a.ksplit copies of the tile grid; copy s reduces over K-steps
+// [s nk / S, (s+1) nk / S) and stores its fp32 partial product to out + s M N (the caller adds
+// the partials in split order). Used where a product has few output tiles and a long reduction.
+template <int EPI, bool KSEG, bool BT, bool SPLIT>
 __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char *lds_a = smem;                               // 2 stages
@@ -573,7 +576,12 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   // tile -> (m tile, segment, n tile within the segment)
   const int64_t tiles_m = (a.M + BM - 1) / BM;
   int64_t mt, nt;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, mt, nt);
+  int64_t tiles_here = gridDim.x, split = 0;
+  if constexpr (SPLIT) {
+    tiles_here = gridDim.x / a.ksplit;
+    split = blockIdx.x / tiles_here;
+  }
+  tile_coords(SPLIT ? blockIdx.x % tiles_here : blockIdx.x, tiles_here, tiles_m, mt, nt);
   int sidx = 0;
 #pragma unroll
   for (int q = 1; q < kMaxSegs; ++q)
@@ -590,7 +598,13 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  const int nk = (int)(a.K / DBK);
+  int nk = (int)(a.K / DBK);
+  int64_t kt0 = 0;                                  // first K-step of this split
+  if constexpr (SPLIT) {
+    const int nk_all = nk;
+    kt0 = split * nk_all / a.ksplit;
+    nk = (int)((split + 1) * nk_all / a.ksplit - kt0);
+  }
   const int k_last = nk - 1;
   // Operand sources. In reduction-segment mode the A loads (one step ahead of the B loads)
   // and the B loads each follow their own segment, switched when their step crosses into it.
@@ -602,8 +616,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     rs_b = make_rsrc(a.kseg[0].w, sg.N * a.kseg[0].K * 2);
     make_direct_rows8(da, a.M, a.kseg[0].K, m0, wave, lane);
   } else {
-    rs_a = make_rsrc(a.act, a.M * a.K * 2);
-    rs_b = make_rsrc(sg.w, sg.N * a.K * 2);
+    rs_a = make_rsrc(a.act + kt0 * DBK, a.M * a.K * 2 - kt0 * DBK * 2);
+    rs_b = BT ? make_rsrc(sg.w + kt0 * DBK * sg.N, (a.K - kt0 * DBK) * sg.N * 2)
+              : make_rsrc(sg.w + kt0 * DBK, sg.N * a.K * 2 - kt0 * DBK * 2);
     make_direct_rows8(da, a.M, a.K, m0, wave, lane);
   }
   if constexpr (BT)
@@ -825,7 +840,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
         if (m < a.M && n < sg.N) {
           const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1], v2 = acc[i][j][4 * g + 2],
                       v3 = acc[i][j][4 * g + 3];
-          floatx4_t *o = reinterpret_cast<floatx4_t *>(reinterpret_cast<float *>(sg.out) + m * sg.N + n);
+          floatx4_t *o = reinterpret_cast<floatx4_t *>(reinterpret_cast<float *>(sg.out) + split * a.M * sg.N +
+                                                      m * sg.N + n);
           if constexpr (EPI == EPI_F32_SET) {
             const floatx4_t v = {v0, v1, v2, v3};
             __builtin_nontemporal_store(v, o);
@@ -846,19 +862,19 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
 constexpr size_t kDirectSmemBytes = 256 * kEpiPitch > 4 * DTILE ? 256 * kEpiPitch : 4 * DTILE;
 static_assert(256 * kEpiPitch <= kDirectSmemBytes, "the epilogue tile must fit in the ring's LDS");
 
-template <int EPI, bool KSEG, bool BT>
+template <int EPI, bool KSEG, bool BT, bool SPLIT = false>
 lsn_status launch_direct_one(const DirectArgs &a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_direct<EPI, KSEG, BT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_direct<EPI, KSEG, BT, SPLIT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDirectSmemBytes);
     if (e != hipSuccess) return check_hip(e, "gemm_direct smem attribute");
     attr_set = true;
   }
   int64_t ntiles_n = 0;
   for (int q = 0; q < a.nseg; ++q) ntiles_n += (a.seg[q].N + BN - 1) / BN;
-  const int64_t tiles = ((a.M + BM - 1) / BM) * ntiles_n;
-  hipLaunchKernelGGL((k_gemm_direct<EPI, KSEG, BT>), dim3((unsigned)tiles), dim3(NT), kDirectSmemBytes, s, a);
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ntiles_n * (SPLIT ? a.ksplit : 1);
+  hipLaunchKernelGGL((k_gemm_direct<EPI, KSEG, BT, SPLIT>), dim3((unsigned)tiles), dim3(NT), kDirectSmemBytes, s, a);
   return check_hip(hipGetLastError(), "k_gemm_direct launch");
 }
 
@@ -905,12 +921,43 @@ lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s) {
     return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, true, false>(a, s)
                            : launch_direct_one<EPI_F32_ADD, true, false>(a, s);
   }
+  if (a.ksplit > 1) {
+    // split-K: fp32 partials of a reduction-major product (the caller adds them)
+    if (!a.b_red_major || epi != EPI_F32_SET || a.nseg != 1 || a.adapters || a.ksplit > a.K / DBK)
+      return LSN_E_ARG;
+    return launch_direct_one<EPI_F32_SET, false, true, true>(a, s);
+  }
   if (a.b_red_major)
     return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, false, true>(a, s)
                            : launch_direct_one<EPI_F32_ADD, false, true>(a, s);
   if (epi == EPI_F32_SET) return launch_direct_one<EPI_F32_SET, false, false>(a, s);
   return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, false, false>(a, s)
                          : launch_direct_one<EPI_F32_ADD, false, false>(a, s);
+}
+
+namespace {
+// out[i] = bf16(partial[0][i] + partial[1][i] + ... ), four elements per thread, fixed order
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ partial, int S, int64_t n,
+                                                       uint16_t *__restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  floatx4_t acc = __builtin_nontemporal_load(reinterpret_cast<const floatx4_t *>(partial + i));
+  for (int sp = 1; sp < S; ++sp) {
+    const floatx4_t v = __builtin_nontemporal_load(reinterpret_cast<const floatx4_t *>(partial + sp * n + i));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = __fadd_rn(acc[e], v[e]);
+  }
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  *reinterpret_cast<u32x2_t *>(out + i) = o;
+}
+}  // namespace
+
+lsn_status launch_splitk_reduce(const float *partial, int S, int64_t n, uint16_t *out, hipStream_t s) {
+  if (S < 1 || n < 1 || n % 4) return LSN_E_ARG;
+  const int64_t blocks = (n / 4 + 255) / 256;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)blocks), dim3(256), 0, s, partial, S, n, out);
+  return check_hip(hipGetLastError(), "k_splitk_reduce launch");
 }
 
 lsn_status launch_gemm(int layout, int wkind, int epi, GemmArgs a, hipStream_t s) {

@@ -118,7 +118,7 @@ def load():
         "layer_pool_stats": (i32, [vp, ctypes.POINTER(PoolStats)]),
         "layer_pool_audit": (i32, [vp]),
         "layer_pool_destroy": (i32, [vp]),
-        "lm_head_ce_ws_bytes": (sz, [i64, i64]),
+        "lm_head_ce_ws_bytes": (sz, [i64, i64, i64]),
         "lm_head_ce": (i32, [i64, i64, i64, vp, vp, vp, f32, vp, vp, i64, vp, sz, vp]),
         "embedding_gather": (i32, [i64, i64, i64, vp, vp, vp, vp, vp]),
     }
@@ -352,8 +352,8 @@ class LayerPool:
             pass
 
 
-def lm_head_ce_ws_bytes(chunk_rows: int, V: int) -> int:
-    return int(load().lm_head_ce_ws_bytes(chunk_rows, V))
+def lm_head_ce_ws_bytes(chunk_rows: int, H: int, V: int) -> int:
+    return int(load().lm_head_ce_ws_bytes(chunk_rows, H, V))
 
 
 def lm_head_ce(h, W, labels, grad_scale: float, loss, dh, chunk_rows: int, ws, stream=None) -> None:

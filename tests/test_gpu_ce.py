@@ -33,7 +33,7 @@ def _run(h, W, lab, scale, chunk):
     T, H = h.shape
     loss = torch.empty(T, dtype=torch.float32, device="cuda")
     dh = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(lib.lm_head_ce_ws_bytes(chunk, W.shape[0]), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(lib.lm_head_ce_ws_bytes(chunk, H, W.shape[0]), dtype=torch.uint8, device="cuda")
     lib.lm_head_ce(h, W, lab, scale, loss, dh, chunk, ws)
     torch.cuda.synchronize()
     return loss, dh
@@ -81,7 +81,7 @@ def test_ce_argument_validation(gpu):
     _, _, _, h, W, lab = _case(64, 64, 128)
     loss = torch.empty(64, dtype=torch.float32, device="cuda")
     dh = torch.empty((64, 64), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(lib.lm_head_ce_ws_bytes(64, 128), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(lib.lm_head_ce_ws_bytes(64, 64, 128), dtype=torch.uint8, device="cuda")
     with pytest.raises(lib.LsnError):          # workspace too small
         lib.lm_head_ce(h, W, lab, 1.0, loss, dh, 64, ws[:1024])
     with pytest.raises(lib.LsnError):          # dh overlapping h
