@@ -397,6 +397,16 @@ def main():
             other["reference_sweep_peak_hbm_ratio"] = round(torch.cuda.max_memory_allocated() / peak_alloc, 3)
             print(f"[bench] streamed with the reference sweep: {other['streamed_with_reference_sweep']} tokens/s",
                   flush=True)
+            # gradient accumulation: two micro-batches per step (each streams every layer twice)
+            stack.step("streamed", micro_batches=2)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                stack.step("streamed", micro_batches=2)
+            torch.cuda.synchronize()
+            other["streamed_2_micro_batches"] = round(2 * cfg.T * n / (time.perf_counter() - t0), 1)
+            print(f"[bench] streamed, 2 micro-batches per step: {other['streamed_2_micro_batches']} tokens/s",
+                  flush=True)
             # the layers streamed from one file through the pool's file tier (just written, so
             # the reads come from the page cache)
             stack.reset_pool(0, source="file")

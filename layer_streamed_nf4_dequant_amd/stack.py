@@ -407,7 +407,7 @@ class Stack:
     def dX_d(self):
         return self.dX_d_pp[0]
 
-    def _backward_layer(self, base: int, l: int, s):
+    def _backward_layer(self, base: int, l: int, s, grad_mode: int = lib.GRAD_SET):
         # q, k, v, gate and up read X_h: their input gradients add up in dX_h (fp32), as one
         # grouped backward (a single GEMM over their concatenated N when staged)
         self.dX_h.zero_()
@@ -415,14 +415,14 @@ class Stack:
         lib.lora_linear_bwd_group([self._desc(base, l, j, backward=True) for j in hj], self.X["h"],
                                   [self.upstream(l, j) for j in hj], [self.U[j] for j in hj], self.dX_h,
                                   [self.dA[l][j] for j in hj], [self.dB[l][j] for j in hj],
-                                  dx_mode=lib.DX_F32_ADD, grad_mode=lib.GRAD_SET, ws=self.ws, stream=s)
+                                  dx_mode=lib.DX_F32_ADD, grad_mode=grad_mode, ws=self.ws, stream=s)
         for j, p in enumerate(self.layout):
             which = PROJ_INPUT[p.name]
             if which == "h":
                 continue
             dX = self.dX_o_pp[l % 2] if which == "o" else self.dX_d_pp[l % 2]
             lib.lora_linear_bwd(self._desc(base, l, j, backward=True), self.X[which], self.upstream(l, j), self.U[j], dX,
-                                self.dA[l][j], self.dB[l][j], dx_mode=lib.DX_BF16_SET, grad_mode=lib.GRAD_SET,
+                                self.dA[l][j], self.dB[l][j], dx_mode=lib.DX_BF16_SET, grad_mode=grad_mode,
                                 ws=self.ws, stream=s)
 
     def _record(self, tag: str, l: int, tensors):
@@ -437,7 +437,7 @@ class Stack:
             self.checks[(tag, l, j)] = (v.to(torch.int64) * self._wvec[:n]).sum()
 
     def step(self, mode: str = "streamed", gemm_events=None, dequant_events=None, wait: bool = True,
-             reference: bool = False):
+             reference: bool = False, micro_batches: int = 1):
         """One training step of the projection stack; returns its time in ms (compute stream).
         gemm_events: optional list; (projections, start, end) HIP events around every forward
         GEMM launch (one per group of projections sharing an input) are appended to it.
@@ -450,7 +450,12 @@ class Stack:
         VRAM": for DPO-style objectives the streamed base with the adapters switched off is the
         reference model, at the cost of more layer reads per step; here 3 per layer instead of 2).
         It changes no training state: the step's outputs and gradients are those of a step
-        without it."""
+        without it.
+        micro_batches=k: gradient accumulation ("Exact Layer Streaming", Abstract: accumulation is
+        per-token I/O-neutral): k forward/backward passes, each streaming every layer twice, the
+        first setting dA, dB and the others adding into them (a step then trains on k x T
+        tokens). The stack's inputs are the same for every micro-batch, so after k = 2 each
+        gradient is exactly twice the single pass's (x + x is exact in fp32)."""
         torch = self.torch
         s = self.compute
         sh = s.cuda_stream
@@ -473,29 +478,31 @@ class Stack:
                         self._record("ref", l, self.Yref)
                     if mode == "streamed":
                         self.pool.release(l, sh)
-            # ---- forward: layers 0 .. L-1 ----
-            for l in range(L):
-                base = self._visit_base(mode, l, sh, ahead, forward=True)
-                if self.dequant != "fused":
-                    self._timed(dequant_events, ("fwd", False), s, lambda: self._stage(base, l, s))
-                self._forward_layer(base, l, self.Y, s, gemm_events)
-                if self.record:
-                    self._record("fwd", l, self.Y)
-                if mode == "streamed":
-                    self.pool.release(l, sh)
-            # ---- backward: layers L-1 .. 0, each re-read and recomputed ----
-            for l in reversed(range(L)):
-                base = self._visit_base(mode, l, sh, ahead, forward=False)
-                if self.dequant != "fused":                               # re-dequantised per visit
-                    self._timed(dequant_events, ("bwd", self.dequant == "staged_t"), s,
-                                lambda: self._stage(base, l, s, backward=True))
-                self._forward_layer(base, l, self.Yre, s, gemm_events)   # recompute
-                self._backward_layer(base, l, s)
-                if self.record:
-                    self._record("re", l, self.Yre)
-                    self._record("dx", l, [self.dX_h, self.dX_o_pp[l % 2], self.dX_d_pp[l % 2]])
-                if mode == "streamed":
-                    self.pool.release(l, sh)
+            for mb in range(micro_batches):
+                grad_mode = lib.GRAD_SET if mb == 0 else lib.GRAD_ADD
+                # ---- forward: layers 0 .. L-1 ----
+                for l in range(L):
+                    base = self._visit_base(mode, l, sh, ahead, forward=True)
+                    if self.dequant != "fused":
+                        self._timed(dequant_events, ("fwd", False), s, lambda: self._stage(base, l, s))
+                    self._forward_layer(base, l, self.Y, s, gemm_events)
+                    if self.record:
+                        self._record("fwd", l, self.Y)
+                    if mode == "streamed":
+                        self.pool.release(l, sh)
+                # ---- backward: layers L-1 .. 0, each re-read and recomputed ----
+                for l in reversed(range(L)):
+                    base = self._visit_base(mode, l, sh, ahead, forward=False)
+                    if self.dequant != "fused":                               # re-dequantised per visit
+                        self._timed(dequant_events, ("bwd", self.dequant == "staged_t"), s,
+                                    lambda: self._stage(base, l, s, backward=True))
+                    self._forward_layer(base, l, self.Yre, s, gemm_events)   # recompute
+                    self._backward_layer(base, l, s, grad_mode)
+                    if self.record:
+                        self._record("re", l, self.Yre)
+                        self._record("dx", l, [self.dX_h, self.dX_o_pp[l % 2], self.dX_d_pp[l % 2]])
+                    if mode == "streamed":
+                        self.pool.release(l, sh)
             end.record(s)
         if not wait:
             return start, end

@@ -103,6 +103,33 @@ def test_staged_w_equals_staged_transposed(gpu):
     assert fwd and re and dx and eq == n == 2 * 7 * 3, (fwd, re, dx, eq, n)
 
 
+def test_gradient_accumulation_over_micro_batches(gpu):
+    """Three 8B-shaped layers, two micro-batches per step ("Exact Layer Streaming", Abstract:
+    accumulation is per-token I/O-neutral): the first micro-batch sets dA, dB and the second adds
+    into them; the stack's inputs repeat, so every gradient is exactly twice a single pass's.
+    Streamed equals resident, and the pool copies every layer twice per micro-batch."""
+    import torch
+    cfg = configs.C3
+    print("case: 3-layer 8B-shaped toy, two micro-batches", flush=True)
+    st = Stack(cfg, modes=("streamed", "resident"), layers=3)
+    st.step("resident")
+    single = snapshot(st)[1]
+    st.step("resident", micro_batches=2)
+    double = snapshot(st)[1]
+    for l1, l2 in zip(single, double):
+        for (a1, b1), (a2, b2) in zip(l1, l2):
+            assert torch.equal(a2, 2 * a1) and torch.equal(b2, 2 * b1)
+    st.reset_pool(0, 2)
+    st.step("streamed", micro_batches=2)
+    streamed = snapshot(st)[1]
+    for l1, l2 in zip(double, streamed):
+        for (a1, b1), (a2, b2) in zip(l1, l2):
+            assert torch.equal(a1.view(torch.int32), a2.view(torch.int32))
+            assert torch.equal(b1.view(torch.int32), b2.view(torch.int32))
+    assert st.pool.stats()["copies"] == 2 * 2 * 3
+    st.close()
+
+
 def test_reference_pass_adapters_off(gpu):
     """The DPO-style reference sweep ("An 8B Fine-Tune Now Fits in 4 GB of VRAM": the streamed
     base with the adapters off is the reference model): three 8B-shaped layers. The sweep changes
