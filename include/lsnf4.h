@@ -215,12 +215,13 @@ lsn_status lora_linear_fwd_group(int32_t n, const lsn_lora_linear *L, int32_t ad
                                  uint16_t *const *Y, uint16_t *const *U, void *ws, size_t ws_bytes,
                                  void *stream);
 
-enum { LSN_DX_BF16_SET = 0, LSN_DX_F32_ADD = 1 };
+enum { LSN_DX_BF16_SET = 0, LSN_DX_F32_ADD = 1, LSN_DX_F32_SET = 2 };
 enum { LSN_GRAD_SET = 0, LSN_GRAD_ADD = 1 };
 
 /*
  * lora_linear_bwd - given X, dY and U = bf16(X A^T) from the (recomputed) forward:
  *   dX: LSN_DX_BF16_SET writes bf16(dY W + s G A) to a bf16 [T][K] buffer;
+ *       LSN_DX_F32_SET writes fp32 (dY W + s G A) to an fp32 [T][K] buffer;
  *       LSN_DX_F32_ADD adds fp32 (dY W + s G A) into an fp32 [T][K] buffer (for inputs shared
  *       by several projections; the sum order is the caller's call order).
  *   dA, dB (fp32): LSN_GRAD_SET overwrites, LSN_GRAD_ADD accumulates. The reductions over T
@@ -238,7 +239,7 @@ size_t lora_linear_group_ws_bytes(int32_t n, const lsn_lora_linear *L);
  * lora_linear_bwd_group - the backwards of n (1 <= n <= 8) linears that read the same input X
  * [T][K] (a decoder layer's q, k, v, gate and up), whose input gradients add up in one dX:
  *   dX:  LSN_DX_BF16_SET writes bf16( sum_g (dY_g W_g + s G_g A_g) );
- *        LSN_DX_F32_ADD adds the fp32 sum into dX;
+ *        LSN_DX_F32_ADD adds the fp32 sum into dX; LSN_DX_F32_SET writes it (fp32);
  *   dA_g, dB_g as lora_linear_bwd (LSN_GRAD_SET / LSN_GRAD_ADD), bit-identical to it.
  * L: host array of n descriptors sharing T, K, r and the scale; dY, U, dA, dB: host arrays of
  * n device pointers. With every W in bf16, all in the same layout (LSN_W_BF16 or

@@ -71,6 +71,8 @@ struct DirectArgs {
   int scale_pow2;        // set by launch_gemm_direct
 };
 lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s);
+// zero bytes (a multiple of 16) at p, with a kernel (no memset node in captured graphs)
+lsn_status launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 // out[i] = bf16( sum_{s < S} partial[s][i] ), in split order, for i < n (n % 4 == 0)
 lsn_status launch_splitk_reduce(const float *partial, int S, int64_t n, uint16_t *out, hipStream_t s);
 

@@ -896,6 +896,15 @@ lsn_status launch_one(const GemmArgs &a, hipStream_t s) {
 
 }  // namespace
 
+namespace {
+template <bool KSEG, bool BT>
+lsn_status launch_direct_epi(const DirectArgs &a, int epi, hipStream_t s) {
+  if (epi == EPI_BF16) return launch_direct_one<EPI_BF16, KSEG, BT>(a, s);
+  if (epi == EPI_F32_ADD) return launch_direct_one<EPI_F32_ADD, KSEG, BT>(a, s);
+  return launch_direct_one<EPI_F32_SET, KSEG, BT>(a, s);
+}
+}  // namespace
+
 lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s) {
   // a power-of-two scale s >= 1 (s = alpha / r with alpha and r powers of two, the usual case)
   // is applied exactly to the bf16 U fragments instead of to the fp32 accumulators
@@ -915,11 +924,7 @@ lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s) {
       step += a.kseg[p].K / DBK;
     }
     a.K = step * DBK;
-    if (a.b_red_major)
-      return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, true, true>(a, s)
-                             : launch_direct_one<EPI_F32_ADD, true, true>(a, s);
-    return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, true, false>(a, s)
-                           : launch_direct_one<EPI_F32_ADD, true, false>(a, s);
+    return a.b_red_major ? launch_direct_epi<true, true>(a, epi, s) : launch_direct_epi<true, false>(a, epi, s);
   }
   if (a.ksplit > 1) {
     // split-K: fp32 partials of a reduction-major product (the caller adds them)
@@ -927,12 +932,7 @@ lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s) {
       return LSN_E_ARG;
     return launch_direct_one<EPI_F32_SET, false, true, true>(a, s);
   }
-  if (a.b_red_major)
-    return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, false, true>(a, s)
-                           : launch_direct_one<EPI_F32_ADD, false, true>(a, s);
-  if (epi == EPI_F32_SET) return launch_direct_one<EPI_F32_SET, false, false>(a, s);
-  return epi == EPI_BF16 ? launch_direct_one<EPI_BF16, false, false>(a, s)
-                         : launch_direct_one<EPI_F32_ADD, false, false>(a, s);
+  return a.b_red_major ? launch_direct_epi<false, true>(a, epi, s) : launch_direct_epi<false, false>(a, epi, s);
 }
 
 namespace {
@@ -952,6 +952,21 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
   *reinterpret_cast<u32x2_t *>(out + i) = o;
 }
 }  // namespace
+
+namespace {
+__global__ __launch_bounds__(256) void k_fill_zero(u32x4_t *p, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n16) p[i] = u32x4_t{0, 0, 0, 0};
+}
+}  // namespace
+
+lsn_status launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
+  if (bytes % 16) return LSN_E_ARG;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return LSN_OK;
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s, static_cast<u32x4_t *>(p), n16);
+  return check_hip(hipGetLastError(), "k_fill_zero launch");
+}
 
 lsn_status launch_splitk_reduce(const float *partial, int S, int64_t n, uint16_t *out, hipStream_t s) {
   if (S < 1 || n < 1 || n % 4) return LSN_E_ARG;

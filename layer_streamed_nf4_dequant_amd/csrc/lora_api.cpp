@@ -318,14 +318,14 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
     return fail(LSN_E_ARG, "lora_linear_bwd: null pointer argument");
   if (!aligned16(X) || !aligned16(dY) || !aligned16(U) || !aligned16(dX) || ((uintptr_t)ws & 255))
     return fail(LSN_E_ARG, "lora_linear_bwd: X, dY, U, dX must be 16-byte and ws 256-byte aligned");
-  if (dx_mode != LSN_DX_BF16_SET && dx_mode != LSN_DX_F32_ADD)
+  if (dx_mode != LSN_DX_BF16_SET && dx_mode != LSN_DX_F32_ADD && dx_mode != LSN_DX_F32_SET)
     return fail(LSN_E_ARG, "lora_linear_bwd: unknown dX mode %d", dx_mode);
   if (grad_mode != LSN_GRAD_SET && grad_mode != LSN_GRAD_ADD)
     return fail(LSN_E_ARG, "lora_linear_bwd: unknown gradient mode %d", grad_mode);
   const BwdWs need = bwd_layout(ws, T, K, N, r);
   if (ws_bytes < need.bytes)
     return fail(LSN_E_ARG, "lora_linear_bwd: workspace too small (%zu < %zu)", ws_bytes, need.bytes);
-  const size_t dxb = (size_t)(T * K * (dx_mode == LSN_DX_F32_ADD ? 4 : 2));
+  const size_t dxb = (size_t)(T * K * (dx_mode == LSN_DX_BF16_SET ? 2 : 4));
   const void *outs[] = {dX, dA, dB, ws};
   const size_t outb[] = {dxb, (size_t)(r * K * 4), (size_t)(N * r * 4), need.bytes};
   const void *ins[8] = {X, dY, U, L->A, L->B};
@@ -360,7 +360,7 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
     if ((st = launch_transpose_many(ts, s)) != LSN_OK) return st;
   }
   if ((st = launch_rowproj(dY, T, N, need.Bt, (int)r, need.G, s)) != LSN_OK) return st;
-  const int epi = dx_mode == LSN_DX_F32_ADD ? EPI_F32_ADD : EPI_BF16;
+  const int epi = dx_mode == LSN_DX_F32_ADD ? EPI_F32_ADD : dx_mode == LSN_DX_F32_SET ? EPI_F32_SET : EPI_BF16;
   if (L->W.kind != LSN_W_NF4) {
     // dX = dY W + s G (A^T)^T, a product over N: from W^T [K][N] both operands are N-contiguous;
     // from W [N][K] the GEMM reads its B operand reduction-major (same fragments, same bits)
@@ -390,7 +390,10 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
     a.lr_w = L->A;
     a.adapters = 1;
     a.out = dX;
-    if ((st = launch_gemm(GEMM_NN, L->W.kind == LSN_W_NF4 ? W_IS_NF4 : W_IS_BF16, epi, a, s)) != LSN_OK)
+    // (this kernel adds or stores bf16: an fp32 store is a zero fill and an add)
+    if (epi == EPI_F32_SET && (st = launch_fill_zero(dX, dxb, s)) != LSN_OK) return st;
+    if ((st = launch_gemm(GEMM_NN, L->W.kind == LSN_W_NF4 ? W_IS_NF4 : W_IS_BF16,
+                          epi == EPI_F32_SET ? EPI_F32_ADD : epi, a, s)) != LSN_OK)
       return st;
   }
   // dB = s dY^T U and dA = s G^T X (stored as A's [r][K]): both partials in one launch, then both
@@ -432,7 +435,7 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
       return fail(LSN_E_ARG, "lora_linear_bwd_group: members must share T, K, r and the scale");
     fused = fused && L[g].W.kind == L[0].W.kind;
   }
-  if (dx_mode != LSN_DX_BF16_SET && dx_mode != LSN_DX_F32_ADD)
+  if (dx_mode != LSN_DX_BF16_SET && dx_mode != LSN_DX_F32_ADD && dx_mode != LSN_DX_F32_SET)
     return fail(LSN_E_ARG, "lora_linear_bwd_group: unknown dX mode %d", dx_mode);
   if (grad_mode != LSN_GRAD_SET && grad_mode != LSN_GRAD_ADD)
     return fail(LSN_E_ARG, "lora_linear_bwd_group: unknown gradient mode %d", grad_mode);
@@ -450,7 +453,7 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
   size_t outb[2 + 2 * kMaxSegs];
   int n_out = 0;
   outs[n_out] = dX;
-  outb[n_out++] = (size_t)(T * K * (dx_mode == LSN_DX_F32_ADD ? 4 : 2));
+  outb[n_out++] = (size_t)(T * K * (dx_mode == LSN_DX_BF16_SET ? 2 : 4));
   outs[n_out] = ws;
   outb[n_out++] = need;
   for (int g = 0; g < n; ++g) {
@@ -484,7 +487,9 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
     char *w = static_cast<char *>(ws);
     for (int g = 0; g < n; ++g) {
       const size_t b = bwd_layout(nullptr, T, K, L[g].N, r).bytes;
-      if ((st = lora_linear_bwd(&L[g], X, dY[g], U[g], dX, dx_mode, dA[g], dB[g], grad_mode, w, b, stream)) != LSN_OK)
+      // an fp32 store: the first member stores, the others add
+      const int32_t mode = (dx_mode == LSN_DX_F32_SET && g > 0) ? LSN_DX_F32_ADD : dx_mode;
+      if ((st = lora_linear_bwd(&L[g], X, dY[g], U[g], dX, mode, dA[g], dB[g], grad_mode, w, b, stream)) != LSN_OK)
         return st;
       w += b;
     }
@@ -546,7 +551,8 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
   }
   // every member's G in one launch
   if ((st = launch_rowproj_jobs(T, gj, s)) != LSN_OK) return st;
-  if ((st = launch_gemm_direct(d, dx_mode == LSN_DX_F32_ADD ? EPI_F32_ADD : EPI_BF16, s)) != LSN_OK) return st;
+  const int epi = dx_mode == LSN_DX_F32_ADD ? EPI_F32_ADD : dx_mode == LSN_DX_F32_SET ? EPI_F32_SET : EPI_BF16;
+  if ((st = launch_gemm_direct(d, epi, s)) != LSN_OK) return st;
   // every member's dB and dA partials in one launch, then every reduction in one launch
   const int64_t nc = (T + TN_CHUNK - 1) / TN_CHUNK;
   const int acc = grad_mode == LSN_GRAD_ADD;

@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "LSN_OK", 1: "LSN_E_ARG", 2: "LSN_E_NOFIT", 3: "LSN_E_STATE",
 W_NF4, W_BF16, W_BF16_T = 0, 1, 2
 OUT_BF16, OUT_F32, OUT_BF16_T = 0, 1, 2
 ADAPTERS_OFF, ADAPTERS_ON, ADAPTERS_U_READY = 0, 1, 2
-DX_BF16_SET, DX_F32_ADD = 0, 1
+DX_BF16_SET, DX_F32_ADD, DX_F32_SET = 0, 1, 2
 GRAD_SET, GRAD_ADD = 0, 1
 POOL_AUDIT, POOL_KEEP_AT_TURN, POOL_HOST_SIM, POOL_FILE_TIER = 1, 2, 4, 8
 FAULT_STALE_REFETCH, FAULT_WRONG_SLOT = 1 << 8, 1 << 9

@@ -410,12 +410,11 @@ class Stack:
     def _backward_layer(self, base: int, l: int, s, grad_mode: int = lib.GRAD_SET):
         # q, k, v, gate and up read X_h: their input gradients add up in dX_h (fp32), as one
         # grouped backward (a single GEMM over their concatenated N when staged)
-        self.dX_h.zero_()
         hj = self.h_group
         lib.lora_linear_bwd_group([self._desc(base, l, j, backward=True) for j in hj], self.X["h"],
                                   [self.upstream(l, j) for j in hj], [self.U[j] for j in hj], self.dX_h,
                                   [self.dA[l][j] for j in hj], [self.dB[l][j] for j in hj],
-                                  dx_mode=lib.DX_F32_ADD, grad_mode=grad_mode, ws=self.ws, stream=s)
+                                  dx_mode=lib.DX_F32_SET, grad_mode=grad_mode, ws=self.ws, stream=s)
         for j, p in enumerate(self.layout):
             which = PROJ_INPUT[p.name]
             if which == "h":

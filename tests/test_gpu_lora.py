@@ -106,6 +106,50 @@ def test_accumulate_modes(gpu, transposed):
     assert_close("dB", to_np(dB).astype(np.float64) - c.g_init[r * K:].reshape(c.N, r), dBo)
 
 
+@pytest.mark.parametrize("base,transposed", [("nf4", False), ("bf16", False), ("bf16", True)])
+def test_f32_store_mode_equals_add_into_zeros(gpu, base, transposed):
+    """LSN_DX_F32_SET writes what LSN_DX_F32_ADD adds into a zeroed buffer (single linear, and a
+    group of three whose members share X), with identical LoRA gradients."""
+    import torch
+    c = Case(300, 512, 320, base=base, tag="f32set")
+    print(f"case: fp32 store mode base={base} transposed={transposed}", flush=True)
+    Y, U = c.gpu_fwd()
+    W = c.w_transposed() if transposed else None
+    desc = c.desc(W, transposed)
+    outs = {}
+    for mode in (lib.DX_F32_SET, lib.DX_F32_ADD):
+        dX = torch.full((c.T, c.K), 7.0 if mode == lib.DX_F32_SET else 0.0, dtype=torch.float32, device="cuda")
+        dA = torch.empty((c.r, c.K), dtype=torch.float32, device="cuda")
+        dB = torch.empty((c.N, c.r), dtype=torch.float32, device="cuda")
+        lib.lora_linear_bwd(desc, c.Xd, c.dYd, U, dX, dA, dB, dx_mode=mode, ws=c.ws)
+        outs[mode] = (dX, dA, dB)
+    torch.cuda.synchronize()
+    for a, b in zip(outs[lib.DX_F32_SET], outs[lib.DX_F32_ADD]):
+        assert torch.equal(a, b)
+    cs = [Case(300, 512, N, base=base, tag=f"f32setg{i}") for i, N in enumerate((320, 128, 448))]
+    X = cs[0].Xd
+    Us = []
+    for m in cs:
+        Ym = torch.empty((300, m.N), dtype=torch.bfloat16, device="cuda")
+        Um = torch.empty((300, 16), dtype=torch.bfloat16, device="cuda")
+        lib.lora_linear_fwd(m.desc(), X, Ym, Um, adapters=True, ws=m.ws)
+        Us.append(Um)
+    wts = [m.w_transposed() for m in cs] if transposed else [None] * len(cs)   # kept alive: descs hold pointers
+    descs = [m.desc(wt, True) if transposed else m.desc() for m, wt in zip(cs, wts)]
+    ws = torch.empty(lib.group_ws_bytes(descs), dtype=torch.uint8, device="cuda")
+    res = {}
+    for mode in (lib.DX_F32_SET, lib.DX_F32_ADD):
+        dX = torch.full((300, 512), -3.0 if mode == lib.DX_F32_SET else 0.0, dtype=torch.float32, device="cuda")
+        dA = [torch.empty((16, 512), dtype=torch.float32, device="cuda") for _ in cs]
+        dB = [torch.empty((m.N, 16), dtype=torch.float32, device="cuda") for m in cs]
+        lib.lora_linear_bwd_group(descs, X, [m.dYd for m in cs], Us, dX, dA, dB, dx_mode=mode, ws=ws)
+        res[mode] = (dX, dA, dB)
+    torch.cuda.synchronize()
+    assert torch.equal(res[lib.DX_F32_SET][0], res[lib.DX_F32_ADD][0])
+    for a, b in zip(res[lib.DX_F32_SET][1] + res[lib.DX_F32_SET][2], res[lib.DX_F32_ADD][1] + res[lib.DX_F32_ADD][2]):
+        assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("T,K,N", [(512, 896, 896), (300, 1024, 640)])
 def test_fused_nf4_equals_bf16_gemm_on_dequantised_weights(gpu, T, K, N):
     """The dequant-into-LDS path must hand the matrix cores exactly the bf16 W that the
