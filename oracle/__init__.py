@@ -20,6 +20,10 @@ lora
     The LoRA linear on a frozen base, forward and analytic backward, in float64.
     Source: "Can You Fine-Tune a 27B Model on a Laptop?", transcript @1:25-1:58 (frozen base,
     a thin pair of trainable matrices per layer); the formulas are the standard LoRA ones.
+glue
+    The decoder-layer glue around the projections: RMSNorm, rotary position embedding and the
+    SwiGLU gate, forward and backward, in float64 (the published definitions of the Llama and Qwen
+    layers the pages train; the pages print none of them).
 ce
     The frozen embedding lookup and token-level cross-entropy through the frozen LM head
     (loss, logit gradient, hidden-state gradient), in float64.  Source: "Can You Fine-Tune a
@@ -31,4 +35,4 @@ brute force and finite differences. Parity with the pages themselves is unpinned
 the pages print no values (they print no codebook, tensor or checksum).
 """
 
-from . import ce, nf4, lora  # noqa: F401
+from . import ce, glue, nf4, lora  # noqa: F401
