@@ -252,6 +252,7 @@ def main():
 
     import torch
     from layer_streamed_nf4_dequant_amd import configs, lib
+    from layer_streamed_nf4_dequant_amd.microbench import glue_figure
     from layer_streamed_nf4_dequant_amd.stack import Stack
 
     lib.load()
@@ -423,6 +424,8 @@ def main():
             other["h2d_GBs"] = round(stack.h2d_rate(), 1)
         other["lm_head_ce"] = lm_head_figure(cfg)
         print(f"[bench] lm_head_ce: {other['lm_head_ce']}", flush=True)
+        other["glue"] = glue_figure(cfg)   # layer_streamed_nf4_dequant_amd/microbench.py
+        print(f"[bench] glue: {other['glue']}", flush=True)
 
     tokens = cfg.T * args.steps
     value = tokens / wall

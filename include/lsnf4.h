@@ -290,6 +290,59 @@ lsn_status embedding_gather(int64_t T, int64_t H, int64_t V, const int32_t *ids,
                             uint16_t *X, int32_t *bad_ids, void *stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Decoder-layer glue around the seven projections. The pages train Llama-3.1 and Qwen2.5
+ * decoder layers ("Exact Layer Streaming", Abstract; "An 8B Fine-Tune Now Fits in 4 GB of
+ * VRAM": the decoder layer is the streamed unit) but print none of these formulas; these are
+ * those models' published layer definitions. fp32 arithmetic on bf16 tensors, every product and
+ * sum separately rounded, every row reduction in a fixed order (bitwise reproducible).
+ * All pointers are device pointers; bf16 tensors are row-major and 16-byte aligned. Bad sizes,
+ * null or misaligned pointers and output/input overlaps give LSN_E_ARG. Async on `stream`.
+ * ---------------------------------------------------------------------------------------- */
+
+/*
+ * rmsnorm_fwd - y[t] = bf16( x[t] * rstd[t] * gain ), rstd[t] = 1 / sqrt(mean_j x_tj^2 + eps)
+ * (RMSNorm with a frozen gain). x, y [T][H] bf16; gain [H] bf16; rstd [T] fp32 (kept for the
+ * backward). H: a multiple of 8; eps >= 0.
+ */
+lsn_status rmsnorm_fwd(int64_t T, int64_t H, const uint16_t *x, const uint16_t *gain, float eps,
+                       uint16_t *y, float *rstd, void *stream);
+
+/*
+ * rmsnorm_bwd - gradient of rmsnorm_fwd with respect to x (the gain is frozen):
+ *   dx[t] = rstd_t (gain dy[t]) - x[t] rstd_t^3 sum_j (gain dy x)_tj / H
+ * x [T][H] bf16; gain [H] bf16; rstd [T] fp32 from rmsnorm_fwd; dy [T][H] fp32 (the normalised
+ * input's gradient as the projections' fp32 dX modes leave it); dx [T][H] fp32, stored
+ * (accumulate = 0) or added to what it holds (accumulate != 0: the residual stream's gradient).
+ */
+lsn_status rmsnorm_bwd(int64_t T, int64_t H, const uint16_t *x, const uint16_t *gain, const float *rstd,
+                       const float *dy, float *dx, int32_t accumulate, void *stream);
+
+/*
+ * rope_apply - rotary position embedding, in place, on n_heads heads of width head_dim at the
+ * start of each row of x (bf16, row stride ld elements, so q and k of a fused projection output
+ * are rotated by two calls on offsets into it). In head h of row t, pair (i, i + head_dim/2)
+ * turns by a = positions[t] * theta^(-2i/head_dim) (the frequencies are computed on the host
+ * in fp64 and rounded to fp32; the angle is an fp32 product); inverse != 0 turns by -a, which
+ * is the backward. positions [T] int32. head_dim even and <= 512.
+ */
+lsn_status rope_apply(int64_t T, int32_t n_heads, int32_t head_dim, uint16_t *x, int64_t ld,
+                      const int32_t *positions, float theta, int32_t inverse, void *stream);
+
+/*
+ * swiglu_fwd - m = bf16( silu(g) u ), silu(z) = z / (1 + e^-z), elementwise over n values
+ * (the gated MLP's gate and up projections in, the down projection's input out).
+ * g, u, m: bf16 [n], n a multiple of 8.
+ */
+lsn_status swiglu_fwd(int64_t n, const uint16_t *g, const uint16_t *u, uint16_t *m, void *stream);
+
+/*
+ * swiglu_bwd - dg = bf16( dm u sigma(g) (1 + g (1 - sigma(g))) ), du = bf16( dm silu(g) ).
+ * g, u, dm, dg, du: bf16 [n], n a multiple of 8.
+ */
+lsn_status swiglu_bwd(int64_t n, const uint16_t *g, const uint16_t *u, const uint16_t *dm, uint16_t *dg,
+                      uint16_t *du, void *stream);
+
+/* ------------------------------------------------------------------------------------------
  * Layer pool ("Exact Layer Streaming", Abstract; transcript @7:11-7:32; "An 8B Fine-Tune
  * Now Fits in 4 GB of VRAM"): n_slots caller-owned device slots hold decoder-layer images;
  * each layer's image lives in pinned host memory; copies run on the pool's copy stream and

@@ -33,6 +33,7 @@ SOURCES = [
     "lora_small.hip",
     "pool_kernels.hip",
     "ce.hip",
+    "glue.hip",
 ]
 
 COMMON = [

@@ -1,0 +1,435 @@
+// The decoder-layer glue around the seven projections: RMSNorm, rotary position embedding and the
+// SwiGLU gate, forward and backward. The pages train Llama-3.1 and Qwen2.5 decoder layers
+// ("Exact Layer Streaming", Abstract; "An 8B Fine-Tune Now Fits in 4 GB of VRAM": the decoder
+// layer is the streamed unit) and print none of these formulas; these are those models' published
+// layer definitions. All of them are bandwidth-bound elementwise or row work: fp32 arithmetic on
+// bf16 tensors, every product and sum separately rounded (no contraction), and every row
+// reduction in a fixed order, so the bits depend only on the inputs.
+
+#include <cmath>
+#include <vector>
+
+#include "common.h"
+
+namespace lsn {
+lsn_status require_gfx950();
+bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb);
+
+namespace {
+
+constexpr int kGlueThreads = 256;
+constexpr int kMaxRopePairs = 256;   // head_dim <= 512
+
+__device__ __forceinline__ float bf16f(uint16_t h) { return bf16_bits_to_f32(h); }
+__device__ __forceinline__ uint16_t f2bf(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu); }
+
+// sum over the NT threads of a workgroup: a fixed butterfly in each wave (every lane of a wave
+// ends with the same bits: each level adds the same two values on both lanes of a pair), then
+// the waves' sums in wave order
+template <int NT>
+__device__ __forceinline__ float team_sum(float v, float *scratch) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = __fadd_rn(v, __shfl_xor(v, off));
+  if constexpr (NT == 64) {
+    return v;
+  } else {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) scratch[wave] = v;
+    __syncthreads();
+    float s = scratch[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) s = __fadd_rn(s, scratch[w]);
+    return s;
+  }
+}
+
+// y = bf16( (x * rstd) * g ), rstd = 1 / sqrt(mean x^2 + eps). One workgroup of NT threads per
+// row (NT sized to the row: 8 values per thread step); the second pass re-reads the row (L2).
+template <int NT>
+__global__ __launch_bounds__(NT) void k_rmsnorm_fwd(int64_t H, const uint16_t *__restrict__ x,
+                                                    const uint16_t *__restrict__ g, float eps,
+                                                    uint16_t *__restrict__ y, float *__restrict__ rstd) {
+  __shared__ float scratch[NT / 64];
+  const int64_t row = blockIdx.x;
+  const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x + row * H);
+  float ss = 0.0f;
+  for (int64_t c = threadIdx.x; c < H / 8; c += NT) {
+    const u32x4_t v = xr[c];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = bf16f((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+      ss = __fadd_rn(ss, __fmul_rn(f, f));
+    }
+  }
+  ss = team_sum<NT>(ss, scratch);
+  const float r = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(ss, (float)H), eps)));
+  if (threadIdx.x == 0) rstd[row] = r;
+  const u32x4_t *gr = reinterpret_cast<const u32x4_t *>(g);
+  u32x4_t *yr = reinterpret_cast<u32x4_t *>(y + row * H);
+  for (int64_t c = threadIdx.x; c < H / 8; c += NT) {
+    const u32x4_t v = xr[c], gv = gr[c];
+    u32x4_t o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float t[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float f = bf16f((uint16_t)(v[q] >> (16 * h)));
+        const float w = bf16f((uint16_t)(gv[q] >> (16 * h)));
+        t[h] = __fmul_rn(__fmul_rn(f, r), w);
+      }
+      o[q] = pack_bf16x2(t[0], t[1]);
+    }
+    yr[c] = o;
+  }
+}
+
+// dx = rstd (g dy) - x rstd^3 (sum_j g_j dy_j x_j) / H; dy and dx fp32, dx stored or added to.
+// One workgroup of NT threads per row.
+template <int NT>
+__global__ __launch_bounds__(NT) void k_rmsnorm_bwd(int64_t H, const uint16_t *__restrict__ x,
+                                                    const uint16_t *__restrict__ g, const float *__restrict__ rstd,
+                                                    const float *__restrict__ dy, float *__restrict__ dx,
+                                                    int accumulate) {
+  __shared__ float scratch[NT / 64];
+  const int64_t row = blockIdx.x;
+  const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x + row * H);
+  const floatx4_t *dr = reinterpret_cast<const floatx4_t *>(dy + row * H);
+  const u32x4_t *gr = reinterpret_cast<const u32x4_t *>(g);
+  float dot = 0.0f;
+  for (int64_t c = threadIdx.x; c < H / 8; c += NT) {
+    const u32x4_t v = xr[c], gv = gr[c];
+    const floatx4_t d0 = dr[2 * c], d1 = dr[2 * c + 1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int q = e >> 1, h = 16 * (e & 1);
+      const float gd = __fmul_rn(bf16f((uint16_t)(gv[q] >> h)), e < 4 ? d0[e & 3] : d1[e & 3]);
+      dot = __fadd_rn(dot, __fmul_rn(gd, bf16f((uint16_t)(v[q] >> h))));
+    }
+  }
+  dot = team_sum<NT>(dot, scratch);
+  const float r = rstd[row];
+  const float k = __fdiv_rn(__fmul_rn(__fmul_rn(__fmul_rn(r, r), r), dot), (float)H);
+  floatx4_t *o = reinterpret_cast<floatx4_t *>(dx + row * H);
+  for (int64_t c = threadIdx.x; c < H / 8; c += NT) {
+    const u32x4_t v = xr[c], gv = gr[c];
+    const floatx4_t d0 = dr[2 * c], d1 = dr[2 * c + 1];
+    float res[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int q = e >> 1, h = 16 * (e & 1);
+      const float gd = __fmul_rn(bf16f((uint16_t)(gv[q] >> h)), e < 4 ? d0[e & 3] : d1[e & 3]);
+      res[e] = __fsub_rn(__fmul_rn(r, gd), __fmul_rn(bf16f((uint16_t)(v[q] >> h)), k));
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      floatx4_t cur = accumulate ? o[2 * c + half] : floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cur[e] = accumulate ? __fadd_rn(cur[e], res[4 * half + e]) : res[4 * half + e];
+      o[2 * c + half] = cur;
+    }
+  }
+}
+
+// threads per row: the row's 16-byte chunks rounded up to whole waves, at most 256
+int rms_team(int64_t H) {
+  const int64_t chunks = H / 8;
+  return chunks > 128 ? 256 : chunks > 64 ? 128 : 64;
+}
+
+struct RopeTable {
+  float inv_freq[kMaxRopePairs];
+};
+
+__device__ __forceinline__ void rope_pair(float x1, float x2, float c, float s, float &y1, float &y2) {
+  y1 = __fsub_rn(__fmul_rn(x1, c), __fmul_rn(x2, s));
+  y2 = __fadd_rn(__fmul_rn(x2, c), __fmul_rn(x1, s));
+}
+
+// In place on n_heads heads of width 2 half in each row (row stride ld elements): pair
+// (i, i + half) of a head turns by pos * inv_freq[i] (minus that for the backward).
+// Vector form (half % 8 == 0, 16-byte aligned rows): a thread takes 8 consecutive pairs of
+// up to `hg` heads of one row, computes the 8 angles' sine and cosine once and applies them to
+// each of its heads with 16-byte loads and stores; threads are ordered pair-block fastest, so
+// neighbouring lanes cover a head's two contiguous halves.
+__global__ __launch_bounds__(kGlueThreads) void k_rope_v(int64_t T, int n_heads, int half, int hg, int64_t ld,
+                                                         uint16_t *__restrict__ x,
+                                                         const int32_t *__restrict__ positions, RopeTable tab,
+                                                         float sign) {
+  const int nblk = half / 8, ngroups = (n_heads + hg - 1) / hg;
+  const int64_t per_row = (int64_t)ngroups * nblk;
+  const int64_t item = (int64_t)blockIdx.x * kGlueThreads + threadIdx.x;
+  if (item >= T * per_row) return;
+  const int64_t row = item / per_row;
+  const int rem = (int)(item - row * per_row);
+  const int group = rem / nblk, blk = rem - group * nblk;
+  const float p = (float)positions[row];
+  float c[8], sn[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float a = __fmul_rn(p, tab.inv_freq[blk * 8 + e]);
+    float sv, cv;
+    sincosf(a, &sv, &cv);
+    c[e] = cv;
+    sn[e] = __fmul_rn(sign, sv);
+  }
+  const int h1 = min(n_heads, (group + 1) * hg);
+  for (int h = group * hg; h < h1; ++h) {
+    uint16_t *base = x + row * ld + (int64_t)h * 2 * half + blk * 8;
+    u32x4_t *p1 = reinterpret_cast<u32x4_t *>(base);
+    u32x4_t *p2 = reinterpret_cast<u32x4_t *>(base + half);
+    const u32x4_t v1 = *p1, v2 = *p2;
+    u32x4_t o1, o2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float y1[2], y2[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int e = 2 * q + hh;
+        rope_pair(bf16f((uint16_t)(v1[q] >> (16 * hh))), bf16f((uint16_t)(v2[q] >> (16 * hh))), c[e], sn[e],
+                  y1[hh], y2[hh]);
+      }
+      o1[q] = pack_bf16x2(y1[0], y1[1]);
+      o2[q] = pack_bf16x2(y2[0], y2[1]);
+    }
+    *p1 = o1;
+    *p2 = o2;
+  }
+}
+
+// Scalar form for any even head width: one thread per pair.
+__global__ __launch_bounds__(kGlueThreads) void k_rope_s(int64_t T, int n_heads, int half, int64_t ld,
+                                                         uint16_t *__restrict__ x,
+                                                         const int32_t *__restrict__ positions, RopeTable tab,
+                                                         float sign) {
+  const int64_t per_row = (int64_t)n_heads * half;
+  const int64_t item = (int64_t)blockIdx.x * kGlueThreads + threadIdx.x;
+  if (item >= T * per_row) return;
+  const int64_t row = item / per_row;
+  const int p = (int)(item - row * per_row);
+  const int head = p / half, i = p - head * half;
+  const float a = __fmul_rn((float)positions[row], tab.inv_freq[i]);
+  float sv, cv;
+  sincosf(a, &sv, &cv);
+  uint16_t *xr = x + row * ld + (int64_t)head * 2 * half;
+  float y1, y2;
+  rope_pair(bf16f(xr[i]), bf16f(xr[i + half]), cv, __fmul_rn(sign, sv), y1, y2);
+  xr[i] = f2bf(y1);
+  xr[i + half] = f2bf(y2);
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return __fdiv_rn(1.0f, __fadd_rn(1.0f, expf(-z))); }
+
+constexpr int kEltChunks = 2;   // SwiGLU: 16-byte chunks (8 values) per thread, loads issued together
+
+__device__ __forceinline__ u32x4_t swiglu8(u32x4_t gv, u32x4_t uv) {
+  u32x4_t o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float t[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float z = bf16f((uint16_t)(gv[q] >> (16 * h)));
+      t[h] = __fmul_rn(__fmul_rn(z, sigmoidf_(z)), bf16f((uint16_t)(uv[q] >> (16 * h))));
+    }
+    o[q] = pack_bf16x2(t[0], t[1]);
+  }
+  return o;
+}
+
+// m = bf16( silu(g) u ); thread chunks c0 and c0 + kGlueThreads of its workgroup's range
+__global__ __launch_bounds__(kGlueThreads) void k_swiglu_fwd(int64_t n8, const uint16_t *__restrict__ g,
+                                                             const uint16_t *__restrict__ u, uint16_t *__restrict__ m) {
+  const int64_t c0 = (int64_t)blockIdx.x * kGlueThreads * kEltChunks + threadIdx.x;
+  const u32x4_t *gp = reinterpret_cast<const u32x4_t *>(g), *up = reinterpret_cast<const u32x4_t *>(u);
+  u32x4_t gv[kEltChunks], uv[kEltChunks];
+#pragma unroll
+  for (int k = 0; k < kEltChunks; ++k) {
+    const int64_t c = c0 + k * kGlueThreads;
+    if (c < n8) {
+      gv[k] = gp[c];
+      uv[k] = up[c];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kEltChunks; ++k) {
+    const int64_t c = c0 + k * kGlueThreads;
+    if (c < n8) reinterpret_cast<u32x4_t *>(m)[c] = swiglu8(gv[k], uv[k]);
+  }
+}
+
+__device__ __forceinline__ void swiglu8_bwd(u32x4_t gv, u32x4_t uv, u32x4_t dv, u32x4_t &og, u32x4_t &ou) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float tg[2], tu[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float z = bf16f((uint16_t)(gv[q] >> (16 * h)));
+      const float uu = bf16f((uint16_t)(uv[q] >> (16 * h)));
+      const float d = bf16f((uint16_t)(dv[q] >> (16 * h)));
+      const float sg = sigmoidf_(z);
+      const float dsilu = __fmul_rn(sg, __fadd_rn(1.0f, __fmul_rn(z, __fsub_rn(1.0f, sg))));
+      tg[h] = __fmul_rn(__fmul_rn(d, uu), dsilu);
+      tu[h] = __fmul_rn(d, __fmul_rn(z, sg));
+    }
+    og[q] = pack_bf16x2(tg[0], tg[1]);
+    ou[q] = pack_bf16x2(tu[0], tu[1]);
+  }
+}
+
+// dg = bf16( dm u sigma (1 + g (1 - sigma)) ), du = bf16( dm silu(g) )
+__global__ __launch_bounds__(kGlueThreads) void k_swiglu_bwd(int64_t n8, const uint16_t *__restrict__ g,
+                                                             const uint16_t *__restrict__ u,
+                                                             const uint16_t *__restrict__ dm, uint16_t *__restrict__ dg,
+                                                             uint16_t *__restrict__ du) {
+  const int64_t c0 = (int64_t)blockIdx.x * kGlueThreads * kEltChunks + threadIdx.x;
+  const u32x4_t *gp = reinterpret_cast<const u32x4_t *>(g), *up = reinterpret_cast<const u32x4_t *>(u),
+                *dp = reinterpret_cast<const u32x4_t *>(dm);
+  u32x4_t gv[kEltChunks], uv[kEltChunks], dv[kEltChunks];
+#pragma unroll
+  for (int k = 0; k < kEltChunks; ++k) {
+    const int64_t c = c0 + k * kGlueThreads;
+    if (c < n8) {
+      gv[k] = gp[c];
+      uv[k] = up[c];
+      dv[k] = dp[c];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kEltChunks; ++k) {
+    const int64_t c = c0 + k * kGlueThreads;
+    if (c < n8) {
+      u32x4_t og, ou;
+      swiglu8_bwd(gv[k], uv[k], dv[k], og, ou);
+      reinterpret_cast<u32x4_t *>(dg)[c] = og;
+      reinterpret_cast<u32x4_t *>(du)[c] = ou;
+    }
+  }
+}
+
+bool a16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+}  // namespace lsn
+
+using namespace lsn;
+
+extern "C" {
+
+lsn_status rmsnorm_fwd(int64_t T, int64_t H, const uint16_t *x, const uint16_t *gain, float eps, uint16_t *y,
+                       float *rstd, void *stream) {
+  if (T < 1 || T > 0x7fffffff || H < 8 || H % 8)
+    return fail(LSN_E_ARG, "rmsnorm_fwd: need 1 <= T < 2^31 and H a positive multiple of 8");
+  if (!x || !gain || !y || !rstd || !a16(x) || !a16(gain) || !a16(y))
+    return fail(LSN_E_ARG, "rmsnorm_fwd: null or misaligned pointer");
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(LSN_E_ARG, "rmsnorm_fwd: eps must be finite and >= 0");
+  const size_t xb = (size_t)(T * H * 2), rb = (size_t)T * 4;
+  if (ranges_overlap(y, xb, x, xb) || ranges_overlap(y, xb, gain, (size_t)H * 2) ||
+      ranges_overlap(rstd, rb, x, xb) || ranges_overlap(rstd, rb, gain, (size_t)H * 2) ||
+      ranges_overlap(rstd, rb, y, xb))
+    return fail(LSN_E_ARG, "rmsnorm_fwd: an output overlaps an input or the other output");
+  lsn_status st = require_gfx950();
+  if (st != LSN_OK) return st;
+  const hipStream_t hs = (hipStream_t)stream;
+  switch (rms_team(H)) {
+    case 64: hipLaunchKernelGGL(k_rmsnorm_fwd<64>, dim3((unsigned)T), dim3(64), 0, hs, H, x, gain, eps, y, rstd); break;
+    case 128: hipLaunchKernelGGL(k_rmsnorm_fwd<128>, dim3((unsigned)T), dim3(128), 0, hs, H, x, gain, eps, y, rstd); break;
+    default: hipLaunchKernelGGL(k_rmsnorm_fwd<256>, dim3((unsigned)T), dim3(256), 0, hs, H, x, gain, eps, y, rstd);
+  }
+  return check_hip(hipGetLastError(), "k_rmsnorm_fwd launch");
+}
+
+lsn_status rmsnorm_bwd(int64_t T, int64_t H, const uint16_t *x, const uint16_t *gain, const float *rstd,
+                       const float *dy, float *dx, int32_t accumulate, void *stream) {
+  if (T < 1 || T > 0x7fffffff || H < 8 || H % 8)
+    return fail(LSN_E_ARG, "rmsnorm_bwd: need 1 <= T < 2^31 and H a positive multiple of 8");
+  if (!x || !gain || !rstd || !dy || !dx || !a16(x) || !a16(gain) || !a16(dy) || !a16(dx))
+    return fail(LSN_E_ARG, "rmsnorm_bwd: null or misaligned pointer");
+  const size_t fb = (size_t)(T * H * 4);
+  if (ranges_overlap(dx, fb, x, (size_t)(T * H * 2)) || ranges_overlap(dx, fb, dy, fb) ||
+      ranges_overlap(dx, fb, rstd, (size_t)T * 4))
+    return fail(LSN_E_ARG, "rmsnorm_bwd: dx overlaps an input");
+  lsn_status st = require_gfx950();
+  if (st != LSN_OK) return st;
+  const hipStream_t hs = (hipStream_t)stream;
+  const int acc = accumulate ? 1 : 0;
+  switch (rms_team(H)) {
+    case 64:
+      hipLaunchKernelGGL(k_rmsnorm_bwd<64>, dim3((unsigned)T), dim3(64), 0, hs, H, x, gain, rstd, dy, dx, acc);
+      break;
+    case 128:
+      hipLaunchKernelGGL(k_rmsnorm_bwd<128>, dim3((unsigned)T), dim3(128), 0, hs, H, x, gain, rstd, dy, dx, acc);
+      break;
+    default:
+      hipLaunchKernelGGL(k_rmsnorm_bwd<256>, dim3((unsigned)T), dim3(256), 0, hs, H, x, gain, rstd, dy, dx, acc);
+  }
+  return check_hip(hipGetLastError(), "k_rmsnorm_bwd launch");
+}
+
+lsn_status rope_apply(int64_t T, int32_t n_heads, int32_t head_dim, uint16_t *x, int64_t ld, const int32_t *positions,
+                      float theta, int32_t inverse, void *stream) {
+  if (T < 1 || n_heads < 1 || head_dim < 2 || head_dim % 2 || head_dim / 2 > kMaxRopePairs)
+    return fail(LSN_E_ARG, "rope_apply: need T >= 1, n_heads >= 1 and an even head_dim <= %d", 2 * kMaxRopePairs);
+  if (ld < (int64_t)n_heads * head_dim) return fail(LSN_E_ARG, "rope_apply: ld smaller than n_heads x head_dim");
+  if (!x || !positions) return fail(LSN_E_ARG, "rope_apply: null pointer");
+  if (!(theta > 1.0f) || !std::isfinite(theta)) return fail(LSN_E_ARG, "rope_apply: theta must be finite and > 1");
+  if (T > ((int64_t)1 << 38) / ((int64_t)n_heads * head_dim))
+    return fail(LSN_E_ARG, "rope_apply: more than 2^37 pairs in one call");
+  lsn_status st = require_gfx950();
+  if (st != LSN_OK) return st;
+  RopeTable tab{};
+  const int half = head_dim / 2;
+  for (int i = 0; i < half; ++i) tab.inv_freq[i] = (float)std::pow((double)theta, -2.0 * i / head_dim);
+  const bool vec = half % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x & 15) == 0;
+  if (vec) {
+    // heads per thread: as many as keep the grid at >= 2048 workgroups (up to 8), so the sine
+    // and cosine of a row's angles are shared by several heads
+    const int64_t nblk = half / 8;
+    int hg = 8;
+    while (hg > 1 && T * nblk * ((n_heads + hg - 1) / hg) < 2048LL * kGlueThreads) hg /= 2;
+    const int64_t items = T * nblk * ((n_heads + hg - 1) / hg);
+    hipLaunchKernelGGL(k_rope_v, dim3((unsigned)((items + kGlueThreads - 1) / kGlueThreads)), dim3(kGlueThreads), 0,
+                       (hipStream_t)stream, T, (int)n_heads, half, hg, ld, x, positions, tab, inverse ? -1.0f : 1.0f);
+  } else {
+    const int64_t items = T * n_heads * half;
+    hipLaunchKernelGGL(k_rope_s, dim3((unsigned)((items + kGlueThreads - 1) / kGlueThreads)), dim3(kGlueThreads), 0,
+                       (hipStream_t)stream, T, (int)n_heads, half, ld, x, positions, tab, inverse ? -1.0f : 1.0f);
+  }
+  return check_hip(hipGetLastError(), "k_rope launch");
+}
+
+lsn_status swiglu_fwd(int64_t n, const uint16_t *g, const uint16_t *u, uint16_t *m, void *stream) {
+  if (n < 8 || n % 8 || n > ((int64_t)1 << 40)) return fail(LSN_E_ARG, "swiglu_fwd: need n a positive multiple of 8, at most 2^40");
+  if (!g || !u || !m || !a16(g) || !a16(u) || !a16(m)) return fail(LSN_E_ARG, "swiglu_fwd: null or misaligned pointer");
+  if (ranges_overlap(m, (size_t)n * 2, g, (size_t)n * 2) || ranges_overlap(m, (size_t)n * 2, u, (size_t)n * 2))
+    return fail(LSN_E_ARG, "swiglu_fwd: m overlaps an input");
+  lsn_status st = require_gfx950();
+  if (st != LSN_OK) return st;
+  const int64_t n8 = n / 8;
+  const int64_t per_block = (int64_t)kGlueThreads * kEltChunks;
+  hipLaunchKernelGGL(k_swiglu_fwd, dim3((unsigned)((n8 + per_block - 1) / per_block)), dim3(kGlueThreads), 0,
+                     (hipStream_t)stream, n8, g, u, m);
+  return check_hip(hipGetLastError(), "k_swiglu_fwd launch");
+}
+
+lsn_status swiglu_bwd(int64_t n, const uint16_t *g, const uint16_t *u, const uint16_t *dm, uint16_t *dg, uint16_t *du,
+                      void *stream) {
+  if (n < 8 || n % 8 || n > ((int64_t)1 << 40)) return fail(LSN_E_ARG, "swiglu_bwd: need n a positive multiple of 8, at most 2^40");
+  if (!g || !u || !dm || !dg || !du || !a16(g) || !a16(u) || !a16(dm) || !a16(dg) || !a16(du))
+    return fail(LSN_E_ARG, "swiglu_bwd: null or misaligned pointer");
+  const size_t b = (size_t)n * 2;
+  const void *ins[] = {g, u, dm};
+  for (const void *in : ins)
+    if (ranges_overlap(dg, b, in, b) || ranges_overlap(du, b, in, b))
+      return fail(LSN_E_ARG, "swiglu_bwd: an output overlaps an input");
+  if (ranges_overlap(dg, b, du, b)) return fail(LSN_E_ARG, "swiglu_bwd: dg overlaps du");
+  lsn_status st = require_gfx950();
+  if (st != LSN_OK) return st;
+  const int64_t n8 = n / 8;
+  const int64_t per_block = (int64_t)kGlueThreads * kEltChunks;
+  hipLaunchKernelGGL(k_swiglu_bwd, dim3((unsigned)((n8 + per_block - 1) / per_block)), dim3(kGlueThreads), 0,
+                     (hipStream_t)stream, n8, g, u, dm, dg, du);
+  return check_hip(hipGetLastError(), "k_swiglu_bwd launch");
+}
+
+}  // extern "C"

@@ -35,6 +35,7 @@ EXPORTS = (
     "layer_pool_create", "layer_pool_register", "layer_pool_register_file", "layer_pool_prefetch", "layer_pool_acquire",
     "layer_pool_release", "layer_pool_stats", "layer_pool_audit", "layer_pool_destroy",
     "lm_head_ce_ws_bytes", "lm_head_ce", "embedding_gather",
+    "rmsnorm_fwd", "rmsnorm_bwd", "rope_apply", "swiglu_fwd", "swiglu_bwd",
 )
 
 
@@ -121,6 +122,11 @@ def load():
         "lm_head_ce_ws_bytes": (sz, [i64, i64, i64]),
         "lm_head_ce": (i32, [i64, i64, i64, vp, vp, vp, f32, vp, vp, i64, vp, sz, vp]),
         "embedding_gather": (i32, [i64, i64, i64, vp, vp, vp, vp, vp]),
+        "rmsnorm_fwd": (i32, [i64, i64, vp, vp, f32, vp, vp, vp]),
+        "rmsnorm_bwd": (i32, [i64, i64, vp, vp, vp, vp, vp, i32, vp]),
+        "rope_apply": (i32, [i64, i32, i32, vp, i64, vp, f32, i32, vp]),
+        "swiglu_fwd": (i32, [i64, vp, vp, vp, vp]),
+        "swiglu_bwd": (i32, [i64, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -370,3 +376,34 @@ def embedding_gather(ids, E, X, bad_ids=None, stream=None) -> None:
     T = ids.shape[0]
     V, H = E.shape
     check(load().embedding_gather(T, H, V, _ptr(ids), _ptr(E), _ptr(X), _ptr(bad_ids), _stream_handle(stream)))
+
+
+def rmsnorm_fwd(x, gain, eps: float, y, rstd, stream=None) -> None:
+    """y = bf16(x * rstd * gain), rstd = 1 / sqrt(mean x^2 + eps) per row (fp32, kept for the backward)."""
+    T, H = x.shape
+    check(load().rmsnorm_fwd(T, H, _ptr(x), _ptr(gain), float(eps), _ptr(y), _ptr(rstd), _stream_handle(stream)))
+
+
+def rmsnorm_bwd(x, gain, rstd, dy, dx, accumulate: bool = False, stream=None) -> None:
+    """dx (fp32) = gradient of rmsnorm_fwd with respect to x, stored or added into dx."""
+    T, H = x.shape
+    check(load().rmsnorm_bwd(T, H, _ptr(x), _ptr(gain), _ptr(rstd), _ptr(dy), _ptr(dx), int(bool(accumulate)),
+                             _stream_handle(stream)))
+
+
+def rope_apply(x, positions, n_heads: int, head_dim: int, theta: float, inverse: bool = False, stream=None) -> None:
+    """Rotary embedding in place on the first n_heads * head_dim columns of each row of x (a 2-D
+    bf16 tensor or a column slice of one); inverse turns the other way (the backward)."""
+    T = x.shape[0]
+    check(load().rope_apply(T, n_heads, head_dim, _ptr(x), x.stride(0), _ptr(positions), float(theta),
+                            int(bool(inverse)), _stream_handle(stream)))
+
+
+def swiglu_fwd(g, u, m, stream=None) -> None:
+    """m = bf16(silu(g) u), elementwise."""
+    check(load().swiglu_fwd(g.numel(), _ptr(g), _ptr(u), _ptr(m), _stream_handle(stream)))
+
+
+def swiglu_bwd(g, u, dm, dg, du, stream=None) -> None:
+    """dg, du = gradients of swiglu_fwd (bf16)."""
+    check(load().swiglu_bwd(g.numel(), _ptr(g), _ptr(u), _ptr(dm), _ptr(dg), _ptr(du), _stream_handle(stream)))
