@@ -24,6 +24,10 @@ glue
     The decoder-layer glue around the projections: RMSNorm, rotary position embedding and the
     SwiGLU gate, forward and backward, in float64 (the published definitions of the Llama and Qwen
     layers the pages train; the pages print none of them).
+attention
+    Causal multi-head attention with grouped key/value heads on packed equal-length sequences,
+    forward (output and row log-sum-exp) and backward, in float64 (the published definition of
+    the Llama and Qwen attention the pages' models use; the pages print none of it).
 ce
     The frozen embedding lookup and token-level cross-entropy through the frozen LM head
     (loss, logit gradient, hidden-state gradient), in float64.  Source: "Can You Fine-Tune a
@@ -35,4 +39,4 @@ brute force and finite differences. Parity with the pages themselves is unpinned
 the pages print no values (they print no codebook, tensor or checksum).
 """
 
-from . import ce, glue, nf4, lora  # noqa: F401
+from . import attention, ce, glue, nf4, lora  # noqa: F401
