@@ -342,6 +342,44 @@ lsn_status swiglu_fwd(int64_t n, const uint16_t *g, const uint16_t *u, uint16_t 
 lsn_status swiglu_bwd(int64_t n, const uint16_t *g, const uint16_t *u, const uint16_t *dm, uint16_t *dg,
                       uint16_t *du, void *stream);
 
+/*
+ * attention_fwd - causal scaled dot-product attention with grouped key/value heads (the
+ * attention of the Llama-3.1 and Qwen2.5 layers the pages train; they print no formula):
+ * n_seq packed sequences of S rows each (T = n_seq x S rows; sequence b is rows b S .. b S + S - 1);
+ * query head h (of n_q) reads key/value head h / (n_q / n_kv). For row i and key rows j <= i of
+ * its sequence:
+ *   s_ij = scale (q_i . k_j),  lse_i = log sum_j exp s_ij,  o_i = sum_j exp(s_ij - lse_i) v_j.
+ * q [T][>= n_q head_dim] (row stride ldq elements), k and v [T][>= n_kv head_dim] (ldk, ldv):
+ * head h in columns h head_dim .. ; they may be column ranges of one fused projection output.
+ * o (bf16, ldo) like q; lse [T][n_q] fp32 (natural log; kept for the backward). head_dim 64
+ * or 128; rows 16-byte aligned (ld a multiple of 8); scale > 0 (1/sqrt(head_dim) for these
+ * models). Products on bf16 MFMA with fp32 accumulation; the probabilities enter the value
+ * product as bf16. Deterministic (no atomics).
+ */
+lsn_status attention_fwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                         const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk,
+                         const uint16_t *v, int64_t ldv, float scale, uint16_t *o, int64_t ldo,
+                         float *lse, void *stream);
+
+/* Device workspace bytes attention_bwd needs: T x n_q fp32 (the row dots D_i = dO_i . o_i). */
+size_t attention_bwd_ws_bytes(int64_t n_seq, int64_t S, int32_t n_q);
+
+/*
+ * attention_bwd - gradients of attention_fwd for an upstream gradient dO (bf16, like o):
+ *   P_ij = exp(s_ij - lse_i), dv_j = sum_i P_ij dO_i, dS_ij = P_ij (dO_i . v_j - dO_i . o_i),
+ *   dq_i = scale sum_j dS_ij k_j, dk_j = scale sum_i dS_ij q_i,
+ * with dk and dv of a shared key/value head summed over its query heads (bf16 outputs dq like
+ * q, dk and dv like k and v, each with its own row stride; stored, not accumulated). o and lse
+ * are attention_fwd's outputs. ws: device, 16-byte aligned, at least attention_bwd_ws_bytes.
+ * Deterministic: dk and dv have one writer per row, dq is computed by a separate pass.
+ */
+lsn_status attention_bwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                         const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk,
+                         const uint16_t *v, int64_t ldv, const uint16_t *o, int64_t ldo,
+                         const float *lse, const uint16_t *dO, int64_t lddo, float scale,
+                         uint16_t *dq, int64_t lddq, uint16_t *dk, int64_t lddk, uint16_t *dv,
+                         int64_t lddv, void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------------------------------
  * Layer pool ("Exact Layer Streaming", Abstract; transcript @7:11-7:32; "An 8B Fine-Tune
  * Now Fits in 4 GB of VRAM"): n_slots caller-owned device slots hold decoder-layer images;

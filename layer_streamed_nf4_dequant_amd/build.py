@@ -34,6 +34,7 @@ SOURCES = [
     "pool_kernels.hip",
     "ce.hip",
     "glue.hip",
+    "attention.hip",
 ]
 
 COMMON = [

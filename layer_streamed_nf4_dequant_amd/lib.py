@@ -36,6 +36,7 @@ EXPORTS = (
     "layer_pool_release", "layer_pool_stats", "layer_pool_audit", "layer_pool_destroy",
     "lm_head_ce_ws_bytes", "lm_head_ce", "embedding_gather",
     "rmsnorm_fwd", "rmsnorm_bwd", "rope_apply", "swiglu_fwd", "swiglu_bwd",
+    "attention_fwd", "attention_bwd_ws_bytes", "attention_bwd",
 )
 
 
@@ -127,6 +128,10 @@ def load():
         "rope_apply": (i32, [i64, i32, i32, vp, i64, vp, f32, i32, vp]),
         "swiglu_fwd": (i32, [i64, vp, vp, vp, vp]),
         "swiglu_bwd": (i32, [i64, vp, vp, vp, vp, vp, vp]),
+        "attention_fwd": (i32, [i64, i64, i32, i32, i32, vp, i64, vp, i64, vp, i64, f32, vp, i64, vp, vp]),
+        "attention_bwd_ws_bytes": (sz, [i64, i64, i32]),
+        "attention_bwd": (i32, [i64, i64, i32, i32, i32, vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, i64, f32,
+                                vp, i64, vp, i64, vp, i64, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -407,3 +412,30 @@ def swiglu_fwd(g, u, m, stream=None) -> None:
 def swiglu_bwd(g, u, dm, dg, du, stream=None) -> None:
     """dg, du = gradients of swiglu_fwd (bf16)."""
     check(load().swiglu_bwd(g.numel(), _ptr(g), _ptr(u), _ptr(dm), _ptr(dg), _ptr(du), _stream_handle(stream)))
+
+
+def attention_fwd(q, k, v, o, lse, n_seq: int, n_q: int, n_kv: int, head_dim: int, scale: float | None = None,
+                  stream=None) -> None:
+    """Causal grouped-query attention over n_seq packed sequences of equal length: q, k, v and o are
+    2-D bf16 tensors or column slices (head h in columns h*head_dim ..); lse [T][n_q] fp32."""
+    T = q.shape[0]
+    S = T // n_seq
+    sc = 1.0 / float(head_dim) ** 0.5 if scale is None else float(scale)
+    check(load().attention_fwd(n_seq, S, n_q, n_kv, head_dim, _ptr(q), q.stride(0), _ptr(k), k.stride(0),
+                               _ptr(v), v.stride(0), sc, _ptr(o), o.stride(0), _ptr(lse), _stream_handle(stream)))
+
+
+def attention_bwd_ws_bytes(n_seq: int, S: int, n_q: int) -> int:
+    return int(load().attention_bwd_ws_bytes(n_seq, S, n_q))
+
+
+def attention_bwd(q, k, v, o, lse, dO, dq, dk, dv, ws, n_seq: int, n_q: int, n_kv: int, head_dim: int,
+                  scale: float | None = None, stream=None) -> None:
+    """dq, dk, dv (bf16, stored) of attention_fwd for the upstream gradient dO."""
+    T = q.shape[0]
+    S = T // n_seq
+    sc = 1.0 / float(head_dim) ** 0.5 if scale is None else float(scale)
+    check(load().attention_bwd(n_seq, S, n_q, n_kv, head_dim, _ptr(q), q.stride(0), _ptr(k), k.stride(0),
+                               _ptr(v), v.stride(0), _ptr(o), o.stride(0), _ptr(lse), _ptr(dO), dO.stride(0), sc,
+                               _ptr(dq), dq.stride(0), _ptr(dk), dk.stride(0), _ptr(dv), dv.stride(0), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream_handle(stream)))

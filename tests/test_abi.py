@@ -78,3 +78,29 @@ def test_glue_argument_errors_without_gpu():
     assert b"ld" in L.lsn_last_error()
     assert L.swiglu_fwd(7, None, None, None, None) == lib.LSN_E_ARG
     assert L.swiglu_bwd(16, None, None, None, None, None, None) == lib.LSN_E_ARG
+
+
+def test_attention_argument_errors_without_gpu():
+    """Shape, stride and overlap checks of the attention entry points run before any device
+    call: column ranges of one fused buffer are accepted (the call then stops at the device
+    check), overlapping ones are refused."""
+    L = lib.load()
+    base = 1 << 20                      # a fake, 16-byte aligned device address (never dereferenced)
+    T, nq, nkv, d = 8, 4, 2, 64
+    W = (nq + 2 * nkv) * d
+    q, k, v = base, base + 2 * nq * d, base + 2 * (nq + nkv) * d
+    o, lse = base + 2 * T * W + 4096, base + 4 * T * W + 8192
+    args = lambda hd, oo: (2, 4, nq, nkv, hd, q, W, k, W, v, W, 0.125, oo, nq * d, lse, None)  # noqa: E731
+    assert L.attention_fwd(*args(96, o)) == lib.LSN_E_ARG
+    assert b"head_dim" in L.lsn_last_error()
+    assert L.attention_fwd(*args(d, q)) == lib.LSN_E_ARG          # o on top of q
+    assert L.attention_fwd(*args(d, o)) not in (lib.LSN_OK, lib.LSN_E_ARG)   # valid: reaches the device check
+    g = base + 6 * T * W + 16384       # fused gradient buffer: dq, dk, dv column ranges
+    dq, dk, dv = g, g + 2 * nq * d, g + 2 * (nq + nkv) * d
+    ws = g + 2 * T * W + 4096
+    bwd = lambda a, b_, c_: (2, 4, nq, nkv, d, q, W, k, W, v, W, o, nq * d, lse, o + 2 * T * nq * d + 256,  # noqa: E731
+                             nq * d, 0.125, a, W, b_, W, c_, W, ws, 1 << 20, None)
+    assert L.attention_bwd(*bwd(dq, dk, dv)) not in (lib.LSN_OK, lib.LSN_E_ARG)
+    assert L.attention_bwd(*bwd(dq, dq + 64, dv)) == lib.LSN_E_ARG     # dk overlaps dq's columns
+    assert b"overlap" in L.lsn_last_error()
+    assert L.attention_bwd_ws_bytes(2, 4, nq) == 2 * 4 * nq * 4
