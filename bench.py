@@ -252,7 +252,7 @@ def main():
 
     import torch
     from layer_streamed_nf4_dequant_amd import configs, lib
-    from layer_streamed_nf4_dequant_amd.microbench import glue_figure
+    from layer_streamed_nf4_dequant_amd.microbench import attention_figure, glue_figure
     from layer_streamed_nf4_dequant_amd.stack import Stack
 
     lib.load()
@@ -426,6 +426,8 @@ def main():
         print(f"[bench] lm_head_ce: {other['lm_head_ce']}", flush=True)
         other["glue"] = glue_figure(cfg)   # layer_streamed_nf4_dequant_amd/microbench.py
         print(f"[bench] glue: {other['glue']}", flush=True)
+        other["attention"] = attention_figure(cfg)
+        print(f"[bench] attention: {other['attention']}", flush=True)
 
     tokens = cfg.T * args.steps
     value = tokens / wall

@@ -31,6 +31,7 @@ class StackConfig:
     pool_slots: int = 2
     single: bool = False      # single linear (no stack)
     head_dim: int = 128       # attention head width (q has hidden/head_dim heads, k and v kv/head_dim)
+    seq_len: int = 1024       # rows per sequence: the T rows are T/seq_len packed sequences
 
     @property
     def scale(self) -> float:

@@ -1,5 +1,6 @@
 """Micro-benchmarks of kernels that sit beside the streamed projection step: the decoder-layer
-glue (RMSNorm, rotary embedding, SwiGLU), at a stack configuration's token count and widths.
+glue (RMSNorm, rotary embedding, SwiGLU) and causal attention, at a stack configuration's token
+count, widths and heads.
 
     python -m layer_streamed_nf4_dequant_amd.microbench [--config C3] [--iters 20]
 
@@ -99,6 +100,41 @@ def glue_figure(cfg, iters: int = 20):
     return out
 
 
+def attention_figure(cfg, iters: int = 10):
+    """Causal grouped-query attention at the configuration's T rows as T / seq_len sequences, its
+    heads and head width: microseconds per forward and per backward call (graph-replayed) and
+    the algorithmic rate against the 2.5 PFLOP/s bf16 peak. Algorithmic FLOPs: the forward's
+    two products over the causal half, 2 n_seq n_q S^2 d; the backward's five (scores
+    recomputed, dP, dV, dQ, dK), 2.5 times that."""
+    import torch
+    from layer_streamed_nf4_dequant_amd import inputs, lib
+    T, S, d = cfg.T, cfg.seq_len, cfg.head_dim
+    n_seq, nq, nkv = T // S, cfg.hidden // d, cfg.kv // d
+    W = (nq + 2 * nkv) * d
+    qkv = inputs.device_normal((T, W), 1.0, 0, "bench attention", "qkv", dtype=torch.bfloat16)
+    q, k, v = qkv[:, : nq * d], qkv[:, nq * d:(nq + nkv) * d], qkv[:, (nq + nkv) * d:]
+    o = torch.empty((T, nq * d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, nq), dtype=torch.float32, device="cuda")
+    dO = inputs.device_normal((T, nq * d), 1.0, 0, "bench attention", "dO", dtype=torch.bfloat16)
+    g = torch.empty_like(qkv)
+    dq, dk, dv = g[:, : nq * d], g[:, nq * d:(nq + nkv) * d], g[:, (nq + nkv) * d:]
+    ws = torch.empty(lib.attention_bwd_ws_bytes(n_seq, S, nq), dtype=torch.uint8, device="cuda")
+    fwd = lambda: lib.attention_fwd(q, k, v, o, lse, n_seq, nq, nkv, d)  # noqa: E731
+    bwd = lambda: lib.attention_bwd(q, k, v, o, lse, dO, dq, dk, dv, ws, n_seq, nq, nkv, d)  # noqa: E731
+    flops_f = 2 * n_seq * nq * S * S * d
+    out = {"tokens": T, "seq_len": S, "sequences": n_seq, "heads": [nq, nkv, d], "timing": "graph"}
+    for name, fn, fl in (("forward", fwd, flops_f), ("backward", bwd, flops_f * 5 // 2)):
+        us = _time_calls(fn, iters)
+        if us is None:
+            out["timing"] = "eager"
+            us = _time_calls(fn, iters, graph=False)
+        tf = fl / (us * 1e-6) / 1e12
+        out[name] = {"us": round(us, 1), "flops": fl, "TFLOPs": round(tf, 1), "frac": round(tf / 2500.0, 3)}
+    del qkv, o, lse, dO, g, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> None:
     from layer_streamed_nf4_dequant_amd import configs
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
@@ -106,7 +142,7 @@ def main() -> None:
     ap.add_argument("--iters", type=int, default=20)
     args = ap.parse_args()
     cfg = getattr(configs, args.config)
-    print(json.dumps(glue_figure(cfg, args.iters)), flush=True)
+    print(json.dumps({"glue": glue_figure(cfg, args.iters), "attention": attention_figure(cfg)}), flush=True)
 
 
 if __name__ == "__main__":
