@@ -342,6 +342,15 @@ lsn_status swiglu_fwd(int64_t n, const uint16_t *g, const uint16_t *u, uint16_t 
 lsn_status swiglu_bwd(int64_t n, const uint16_t *g, const uint16_t *u, const uint16_t *dm, uint16_t *dg,
                       uint16_t *du, void *stream);
 
+/* add_bf16 - out = bf16(a + b) elementwise over n bf16 values (the residual stream's additions);
+ * out may be a or b itself. n a multiple of 8. */
+lsn_status add_bf16(int64_t n, const uint16_t *a, const uint16_t *b, uint16_t *out, void *stream);
+
+/* convert_f32_bf16 - out = bf16(in) (round to nearest even); convert_bf16_f32 - out = in
+ * (exact). n values, a multiple of 8. Used where an fp32 gradient feeds a bf16 operand and back. */
+lsn_status convert_f32_bf16(int64_t n, const float *in, uint16_t *out, void *stream);
+lsn_status convert_bf16_f32(int64_t n, const uint16_t *in, float *out, void *stream);
+
 /*
  * attention_fwd - causal scaled dot-product attention with grouped key/value heads (the
  * attention of the Llama-3.1 and Qwen2.5 layers the pages train; they print no formula):

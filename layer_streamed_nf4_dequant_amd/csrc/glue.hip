@@ -307,6 +307,46 @@ __global__ __launch_bounds__(kGlueThreads) void k_swiglu_bwd(int64_t n8, const u
   }
 }
 
+// out = bf16( a + b ) for bf16 a, b (the residual stream's additions), 8 values per thread
+__global__ __launch_bounds__(kGlueThreads) void k_add_bf16(int64_t n8, const uint16_t *__restrict__ a,
+                                                           const uint16_t *__restrict__ b, uint16_t *__restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * kGlueThreads + threadIdx.x;
+  if (c >= n8) return;
+  const u32x4_t x = reinterpret_cast<const u32x4_t *>(a)[c], y = reinterpret_cast<const u32x4_t *>(b)[c];
+  u32x4_t o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = pack_bf16x2(__fadd_rn(bf16f((uint16_t)x[q]), bf16f((uint16_t)y[q])),
+                       __fadd_rn(bf16f((uint16_t)(x[q] >> 16)), bf16f((uint16_t)(y[q] >> 16))));
+  reinterpret_cast<u32x4_t *>(out)[c] = o;
+}
+
+// fp32 -> bf16 (round to nearest even), 8 values per thread
+__global__ __launch_bounds__(kGlueThreads) void k_f32_to_bf16(int64_t n8, const float *__restrict__ in,
+                                                              uint16_t *__restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * kGlueThreads + threadIdx.x;
+  if (c >= n8) return;
+  const floatx4_t x0 = reinterpret_cast<const floatx4_t *>(in)[2 * c], x1 = reinterpret_cast<const floatx4_t *>(in)[2 * c + 1];
+  reinterpret_cast<u32x4_t *>(out)[c] =
+      u32x4_t{pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]), pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
+}
+
+// bf16 -> fp32 (exact), 8 values per thread
+__global__ __launch_bounds__(kGlueThreads) void k_bf16_to_f32(int64_t n8, const uint16_t *__restrict__ in,
+                                                              float *__restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * kGlueThreads + threadIdx.x;
+  if (c >= n8) return;
+  const u32x4_t x = reinterpret_cast<const u32x4_t *>(in)[c];
+  floatx4_t lo, hi;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo[e] = bf16f((uint16_t)(x[e >> 1] >> (16 * (e & 1))));
+    hi[e] = bf16f((uint16_t)(x[2 + (e >> 1)] >> (16 * (e & 1))));
+  }
+  reinterpret_cast<floatx4_t *>(out)[2 * c] = lo;
+  reinterpret_cast<floatx4_t *>(out)[2 * c + 1] = hi;
+}
+
 bool a16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
@@ -430,6 +470,45 @@ lsn_status swiglu_bwd(int64_t n, const uint16_t *g, const uint16_t *u, const uin
   hipLaunchKernelGGL(k_swiglu_bwd, dim3((unsigned)((n8 + per_block - 1) / per_block)), dim3(kGlueThreads), 0,
                      (hipStream_t)stream, n8, g, u, dm, dg, du);
   return check_hip(hipGetLastError(), "k_swiglu_bwd launch");
+}
+
+lsn_status add_bf16(int64_t n, const uint16_t *a, const uint16_t *b, uint16_t *out, void *stream) {
+  if (n < 8 || n % 8 || n > ((int64_t)1 << 40)) return fail(LSN_E_ARG, "add_bf16: need n a positive multiple of 8, at most 2^40");
+  if (!a || !b || !out || !a16(a) || !a16(b) || !a16(out)) return fail(LSN_E_ARG, "add_bf16: null or misaligned pointer");
+  // out may be a or b exactly (in place); a partial overlap is refused
+  const size_t nb = (size_t)n * 2;
+  if ((out != a && ranges_overlap(out, nb, a, nb)) || (out != b && ranges_overlap(out, nb, b, nb)))
+    return fail(LSN_E_ARG, "add_bf16: out partially overlaps an input");
+  lsn_status st = require_gfx950();
+  if (st != LSN_OK) return st;
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(k_add_bf16, dim3((unsigned)((n8 + kGlueThreads - 1) / kGlueThreads)), dim3(kGlueThreads), 0,
+                     (hipStream_t)stream, n8, a, b, out);
+  return check_hip(hipGetLastError(), "k_add_bf16 launch");
+}
+
+lsn_status convert_f32_bf16(int64_t n, const float *in, uint16_t *out, void *stream) {
+  if (n < 8 || n % 8 || n > ((int64_t)1 << 40)) return fail(LSN_E_ARG, "convert_f32_bf16: need n a positive multiple of 8, at most 2^40");
+  if (!in || !out || !a16(in) || !a16(out)) return fail(LSN_E_ARG, "convert_f32_bf16: null or misaligned pointer");
+  if (ranges_overlap(out, (size_t)n * 2, in, (size_t)n * 4)) return fail(LSN_E_ARG, "convert_f32_bf16: out overlaps in");
+  lsn_status st = require_gfx950();
+  if (st != LSN_OK) return st;
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(k_f32_to_bf16, dim3((unsigned)((n8 + kGlueThreads - 1) / kGlueThreads)), dim3(kGlueThreads), 0,
+                     (hipStream_t)stream, n8, in, out);
+  return check_hip(hipGetLastError(), "k_f32_to_bf16 launch");
+}
+
+lsn_status convert_bf16_f32(int64_t n, const uint16_t *in, float *out, void *stream) {
+  if (n < 8 || n % 8 || n > ((int64_t)1 << 40)) return fail(LSN_E_ARG, "convert_bf16_f32: need n a positive multiple of 8, at most 2^40");
+  if (!in || !out || !a16(in) || !a16(out)) return fail(LSN_E_ARG, "convert_bf16_f32: null or misaligned pointer");
+  if (ranges_overlap(out, (size_t)n * 4, in, (size_t)n * 2)) return fail(LSN_E_ARG, "convert_bf16_f32: out overlaps in");
+  lsn_status st = require_gfx950();
+  if (st != LSN_OK) return st;
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(k_bf16_to_f32, dim3((unsigned)((n8 + kGlueThreads - 1) / kGlueThreads)), dim3(kGlueThreads), 0,
+                     (hipStream_t)stream, n8, in, out);
+  return check_hip(hipGetLastError(), "k_bf16_to_f32 launch");
 }
 
 }  // extern "C"

@@ -37,6 +37,7 @@ EXPORTS = (
     "lm_head_ce_ws_bytes", "lm_head_ce", "embedding_gather",
     "rmsnorm_fwd", "rmsnorm_bwd", "rope_apply", "swiglu_fwd", "swiglu_bwd",
     "attention_fwd", "attention_bwd_ws_bytes", "attention_bwd",
+    "add_bf16", "convert_f32_bf16", "convert_bf16_f32",
 )
 
 
@@ -130,6 +131,9 @@ def load():
         "swiglu_bwd": (i32, [i64, vp, vp, vp, vp, vp, vp]),
         "attention_fwd": (i32, [i64, i64, i32, i32, i32, vp, i64, vp, i64, vp, i64, f32, vp, i64, vp, vp]),
         "attention_bwd_ws_bytes": (sz, [i64, i64, i32]),
+        "add_bf16": (i32, [i64, vp, vp, vp, vp]),
+        "convert_f32_bf16": (i32, [i64, vp, vp, vp]),
+        "convert_bf16_f32": (i32, [i64, vp, vp, vp]),
         "attention_bwd": (i32, [i64, i64, i32, i32, i32, vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, i64, f32,
                                 vp, i64, vp, i64, vp, i64, vp, sz, vp]),
     }
@@ -439,3 +443,19 @@ def attention_bwd(q, k, v, o, lse, dO, dq, dk, dv, ws, n_seq: int, n_q: int, n_k
                                _ptr(v), v.stride(0), _ptr(o), o.stride(0), _ptr(lse), _ptr(dO), dO.stride(0), sc,
                                _ptr(dq), dq.stride(0), _ptr(dk), dk.stride(0), _ptr(dv), dv.stride(0), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream_handle(stream)))
+
+
+def add_bf16(a, b, out, stream=None) -> None:
+    """out = bf16(a + b) elementwise (out may be a or b)."""
+    check(load().add_bf16(a.numel(), _ptr(a), _ptr(b), _ptr(out), _stream_handle(stream)))
+
+
+def convert(x, out, stream=None) -> None:
+    """fp32 -> bf16 (nearest even) or bf16 -> fp32 (exact), by the dtypes of x and out."""
+    torch = _torch()
+    if x.dtype == torch.float32 and out.dtype == torch.bfloat16:
+        check(load().convert_f32_bf16(x.numel(), _ptr(x), _ptr(out), _stream_handle(stream)))
+    elif x.dtype == torch.bfloat16 and out.dtype == torch.float32:
+        check(load().convert_bf16_f32(x.numel(), _ptr(x), _ptr(out), _stream_handle(stream)))
+    else:
+        raise TypeError(f"convert: {x.dtype} -> {out.dtype} not supported")

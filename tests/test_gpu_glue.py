@@ -323,3 +323,28 @@ def test_mlp_block_chain_parity(gpu, T, H, I):
         errs[k] = olora.rel_l2(got[k], want[k])
         assert errs[k] <= tol, f"{k}: rel L2 {errs[k]:.3e} > {tol:.0e}"
     print({k: f"{v:.2e}" for k, v in errs.items()})
+
+
+@pytest.mark.parametrize("n", [8, 4096 * 7 + 8])
+def test_residual_add_and_conversions_bit_exact(gpu, n):
+    """add_bf16 is bf16(fl32(a + b)); fp32 -> bf16 rounds to nearest even; bf16 -> fp32 is exact.
+    Also in place (out = a)."""
+    import torch
+    a = inputs.to_bf16_bits(inputs.host_normal((n,), 3.0, 0, "add", n, "a"))
+    b = inputs.to_bf16_bits(inputs.host_normal((n,), 1e-3, 0, "add", n, "b"))   # large exponent gaps
+    want = onf4.bf16_rne(f32(a) + f32(b))                  # fp32 sum, then one rounding
+    ad, bd = dev_bf16(a, torch), dev_bf16(b, torch)
+    out = torch.empty_like(ad)
+    lib.add_bf16(ad, bd, out)
+    lib.add_bf16(ad, bd, ad)                               # in place
+    x = inputs.host_normal((n,), 10.0, 0, "cvt", n)
+    xd = torch.from_numpy(x).cuda()
+    xb = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    lib.convert(xd, xb)
+    back = torch.empty(n, dtype=torch.float32, device="cuda")
+    lib.convert(xb, back)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(out).view(np.uint16), want)
+    np.testing.assert_array_equal(bits(ad).view(np.uint16), want)
+    np.testing.assert_array_equal(bits(xb).view(np.uint16), onf4.bf16_rne(x))
+    np.testing.assert_array_equal(back.cpu().numpy(), f32(onf4.bf16_rne(x)))
