@@ -63,20 +63,26 @@ __device__ __forceinline__ void transpose8(const u32x4_t (&in)[8], u32x4_t (&out
   }
 }
 
-// Stage the 64 x D block of rows row0.. (rows >= nvalid read as zeros) of a bf16 matrix (row
-// stride ld elements, head columns from `base`) into LDS: row-major into `rm` and/or transposed
-// into `tr`. `blk` in [0, NBLK): this thread's 8x8 block (8 rows of one 16-byte column chunk).
+// The 64 x D block of rows row0.. (rows >= nvalid read as zeros) of a bf16 matrix (row stride ld
+// elements, head columns from `base`) is staged into LDS in two halves so that the global loads
+// of the next block are in flight while the current one is computed: load_block fetches this
+// thread's 8x8 block (`blk` in [0, NBLK): 8 rows of one 16-byte column chunk) into registers,
+// store_block writes it row-major into `rm` and/or transposed into `tr`.
 template <int D>
-__device__ __forceinline__ void stage_block(const uint16_t *__restrict__ base, int64_t ld, int64_t row0, int nvalid,
-                                            int blk, char *rm, char *tr) {
+__device__ __forceinline__ void load_block(const uint16_t *__restrict__ base, int64_t ld, int64_t row0, int nvalid,
+                                           int blk, u32x4_t (&in)[8]) {
   const int rb = blk & 7, cb = blk >> 3;
-  u32x4_t in[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int row = 8 * rb + r;
     in[r] = row < nvalid ? *reinterpret_cast<const u32x4_t *>(base + (row0 + row) * ld + 8 * cb)
                          : u32x4_t{0u, 0u, 0u, 0u};
   }
+}
+
+template <int D>
+__device__ __forceinline__ void store_block(const u32x4_t (&in)[8], int blk, char *rm, char *tr) {
+  const int rb = blk & 7, cb = blk >> 3;
   if (rm) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) *reinterpret_cast<u32x4_t *>(rm + (8 * rb + r) * Tile<D>::RP + 16 * cb) = in[r];
@@ -87,6 +93,10 @@ __device__ __forceinline__ void stage_block(const uint16_t *__restrict__ base, i
 #pragma unroll
     for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4_t *>(tr + (8 * cb + e) * kTP + 16 * rb) = out[e];
   }
+}
+
+__device__ __forceinline__ int rows_left(int64_t S, int64_t blk) {
+  return (int)(S - blk * kB < kB ? S - blk * kB : kB);
 }
 
 // A/B fragment of a row-major tile: row `row`, reduction chunk `ch` (8 consecutive columns)
@@ -157,36 +167,43 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(AttnArgs a) {
   float m = -INFINITY, l = 0.0f;
   const float c2 = a.scale * kLog2e;
 
+  // threads 0..127 stage K (row-major), threads 128..255 stage V (transposed)
+  const int t = threadIdx.x;
+  const bool stK = t < Tile<D>::NBLK, stV = t >= 128 && t - 128 < Tile<D>::NBLK;
+  u32x4_t pre[8];
+  auto fetch = [&](int64_t kb) {
+    if (stK) load_block<D>(Kb, a.ldk, seq0 + kb * kB, rows_left(a.S, kb), t, pre);
+    else if (stV) load_block<D>(Vb, a.ldv, seq0 + kb * kB, rows_left(a.S, kb), t - 128, pre);
+  };
+  fetch(0);
   for (int64_t kb = 0; kb <= qb; ++kb) {
     __syncthreads();
-    const int nvalid = (int)(a.S - kb * kB < kB ? a.S - kb * kB : kB);
-    const int t = threadIdx.x;
-    if (t < Tile<D>::NBLK)
-      stage_block<D>(Kb, a.ldk, seq0 + kb * kB, nvalid, t, k_rm, nullptr);
-    else if (t - 128 < Tile<D>::NBLK && t >= 128)
-      stage_block<D>(Vb, a.ldv, seq0 + kb * kB, nvalid, t - 128, nullptr, v_tr);
+    if (stK) store_block<D>(pre, t, k_rm, nullptr);
+    else if (stV) store_block<D>(pre, t - 128, nullptr, v_tr);
     __syncthreads();
+    if (kb < qb) fetch(kb + 1);   // in flight while this block is computed
 
-    // S^T tile tt: keys 16 tt + 4 g + e (rows) x query `col`
+    // S^T tile tt: keys 16 tt + 4 g + e (rows) x query `col`; two tiles per half
     floatx4 s[4];
-    {
-      bf16x8 kf[4][D / 32];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+    for (int hf = 0; hf < 2; ++hf) {
+      bf16x8 kf[2][D / 32];
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) kf[tt][c] = rm_frag<D>(k_rm, 16 * tt + col, 4 * c + g);
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) kf[u][c] = rm_frag<D>(k_rm, 16 * (2 * hf + u) + col, 4 * c + g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        s[tt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int u = 0; u < 2; ++u) {
+        s[2 * hf + u] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) s[tt] = mfma(kf[tt][c], qf[c], s[tt]);
+        for (int c = 0; c < D / 32; ++c) s[2 * hf + u] = mfma(kf[u][c], qf[c], s[2 * hf + u]);
       }
       AT_MFMA_FENCE();
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) asm volatile("" ::"v"(kf[tt][c]));
+        for (int c = 0; c < D / 32; ++c) asm volatile("" ::"v"(kf[u][c]));
     }
     // online softmax in the exp2 domain
     float mx = -INFINITY;
@@ -218,26 +235,19 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
     // O^T += V^T P^T over the block's 64 keys (two reduction steps of 32)
-    {
-      bf16x8 pf[2], vf[2][D / 16];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        pf[c] = acc_frag(s[2 * c], s[2 * c + 1]);
+    for (int c = 0; c < 2; ++c) {
+      const bf16x8 pf = acc_frag(s[2 * c], s[2 * c + 1]);
+      bf16x8 vf[D / 16];
 #pragma unroll
-        for (int j = 0; j < D / 16; ++j) vf[c][j] = tr_frag(v_tr, 16 * j + col, c, g);
-      }
+      for (int jj = 0; jj < D / 16; ++jj) vf[jj] = tr_frag(v_tr, 16 * jj + col, c, g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j) acc[j] = mfma(vf[c][j], pf[c], acc[j]);
+      for (int jj = 0; jj < D / 16; ++jj) acc[jj] = mfma(vf[jj], pf, acc[jj]);
       AT_MFMA_FENCE();
+      asm volatile("" ::"v"(pf));
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        asm volatile("" ::"v"(pf[c]));
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j) asm volatile("" ::"v"(vf[c][j]));
-      }
+      for (int jj = 0; jj < D / 16; ++jj) asm volatile("" ::"v"(vf[jj]));
     }
   }
   if (q_in_seq < a.S) {
@@ -313,51 +323,68 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
   for (int j = 0; j < D / 16; ++j) dk[j] = dv[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   const float c2 = a.scale * kLog2e;
 
-  for (int hh = 0; hh < grp; ++hh) {
+  // threads 0..127 stage Q, threads 128..255 stage dO (both row-major and transposed), threads
+  // 0..63 the rows' lse and D; the next (head, query block)'s tiles are fetched while the current
+  // one is computed
+  const int t = threadIdx.x;
+  const bool stQ = t < Tile<D>::NBLK, stD = t >= 128 && t - 128 < Tile<D>::NBLK;
+  u32x4_t pre[8];
+  float pre_lse = INFINITY, pre_dot = 0.0f;
+  auto fetch = [&](int hh, int64_t qb) {
     const int h = hk * grp + hh;
+    const int nvalid = rows_left(a.S, qb);
+    if (stQ) load_block<D>(a.q + h * D, a.ldq, seq0 + qb * kB, nvalid, t, pre);
+    else if (stD) load_block<D>(a.dO + h * D, a.lddo, seq0 + qb * kB, nvalid, t - 128, pre);
+    if (t < kB) {
+      const bool ok = t < nvalid;
+      pre_lse = ok ? a.lse[(seq0 + qb * kB + t) * a.n_q + h] * kLog2e : INFINITY;
+      pre_dot = ok ? a.dot[(seq0 + qb * kB + t) * a.n_q + h] : 0.0f;
+    }
+  };
+  fetch(0, kb);
+  for (int hh = 0; hh < grp; ++hh) {
     for (int64_t qb = kb; qb < nb; ++qb) {
       __syncthreads();
-      const int nvalid = (int)(a.S - qb * kB < kB ? a.S - qb * kB : kB);
-      const int t = threadIdx.x;
-      if (t < Tile<D>::NBLK)
-        stage_block<D>(a.q + h * D, a.ldq, seq0 + qb * kB, nvalid, t, q_rm, q_tr);
-      else if (t >= 128 && t - 128 < Tile<D>::NBLK)
-        stage_block<D>(a.dO + h * D, a.lddo, seq0 + qb * kB, nvalid, t - 128, d_rm, d_tr);
+      if (stQ) store_block<D>(pre, t, q_rm, q_tr);
+      else if (stD) store_block<D>(pre, t - 128, d_rm, d_tr);
       if (t < kB) {
-        const bool ok = t < nvalid;
-        lse2_s[t] = ok ? a.lse[(seq0 + qb * kB + t) * a.n_q + h] * kLog2e : INFINITY;
-        dot_s[t] = ok ? a.dot[(seq0 + qb * kB + t) * a.n_q + h] : 0.0f;
+        lse2_s[t] = pre_lse;
+        dot_s[t] = pre_dot;
       }
       __syncthreads();
+      if (qb + 1 < nb) fetch(hh, qb + 1);
+      else if (hh + 1 < grp) fetch(hh + 1, kb);
 
-      // S and dP tiles tt: queries 16 tt + 4 g + e (rows) x key `col`
+      // S and dP tiles tt: queries 16 tt + 4 g + e (rows) x key `col`; two tiles per half
       floatx4 s[4], dp[4];
-      {
-        bf16x8 qa[4][D / 32], da[4][D / 32];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+      for (int hf = 0; hf < 2; ++hf) {
+        bf16x8 qa[2][D / 32], da[2][D / 32];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int c = 0; c < D / 32; ++c) {
-            qa[tt][c] = rm_frag<D>(q_rm, 16 * tt + col, 4 * c + g);
-            da[tt][c] = rm_frag<D>(d_rm, 16 * tt + col, 4 * c + g);
+            qa[u][c] = rm_frag<D>(q_rm, 16 * (2 * hf + u) + col, 4 * c + g);
+            da[u][c] = rm_frag<D>(d_rm, 16 * (2 * hf + u) + col, 4 * c + g);
           }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
+        for (int u = 0; u < 2; ++u) {
+          const int tt = 2 * hf + u;
           s[tt] = dp[tt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int c = 0; c < D / 32; ++c) {
-            s[tt] = mfma(qa[tt][c], kf[c], s[tt]);
-            dp[tt] = mfma(da[tt][c], vf[c], dp[tt]);
+            s[tt] = mfma(qa[u][c], kf[c], s[tt]);
+            dp[tt] = mfma(da[u][c], vf[c], dp[tt]);
           }
         }
         AT_MFMA_FENCE();
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int c = 0; c < D / 32; ++c) {
-            asm volatile("" ::"v"(qa[tt][c]));
-            asm volatile("" ::"v"(da[tt][c]));
+            asm volatile("" ::"v"(qa[u][c]));
+            asm volatile("" ::"v"(da[u][c]));
           }
       }
       // P and dS = P (dP - D)
@@ -371,37 +398,25 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
           s[tt][e] = p;
           dp[tt][e] = p * (dp[tt][e] - dot_s[qi]);
         }
-      // dV^T += dO^T P,  dK^T += Q^T dS  (reduction over the block's 64 queries)
-      {
-        bf16x8 pf[2], sf[2], da[2][D / 16], qa[2][D / 16];
+      // dV^T += dO^T P,  dK^T += Q^T dS  (reduction over the block's 64 queries, in two steps)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          pf[c] = acc_frag(s[2 * c], s[2 * c + 1]);
-          sf[c] = acc_frag(dp[2 * c], dp[2 * c + 1]);
+      for (int c = 0; c < 2; ++c) {
 #pragma unroll
-          for (int j = 0; j < D / 16; ++j) {
-            da[c][j] = tr_frag(d_tr, 16 * j + col, c, g);
-            qa[c][j] = tr_frag(q_tr, 16 * j + col, c, g);
+        for (int which = 0; which < 2; ++which) {
+          const bf16x8 bf = which == 0 ? acc_frag(s[2 * c], s[2 * c + 1]) : acc_frag(dp[2 * c], dp[2 * c + 1]);
+          bf16x8 af[D / 16];
+#pragma unroll
+          for (int jj = 0; jj < D / 16; ++jj) af[jj] = tr_frag(which == 0 ? d_tr : q_tr, 16 * jj + col, c, g);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int jj = 0; jj < D / 16; ++jj) {
+            if (which == 0) dv[jj] = mfma(af[jj], bf, dv[jj]);
+            else dk[jj] = mfma(af[jj], bf, dk[jj]);
           }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+          AT_MFMA_FENCE();
+          asm volatile("" ::"v"(bf));
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int j = 0; j < D / 16; ++j) {
-            dv[j] = mfma(da[c][j], pf[c], dv[j]);
-            dk[j] = mfma(qa[c][j], sf[c], dk[j]);
-          }
-        AT_MFMA_FENCE();
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          asm volatile("" ::"v"(pf[c]));
-          asm volatile("" ::"v"(sf[c]));
-#pragma unroll
-          for (int j = 0; j < D / 16; ++j) {
-            asm volatile("" ::"v"(da[c][j]));
-            asm volatile("" ::"v"(qa[c][j]));
-          }
+          for (int jj = 0; jj < D / 16; ++jj) asm volatile("" ::"v"(af[jj]));
         }
       }
     }
@@ -453,44 +468,52 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_q(AttnArgs a) {
   for (int j = 0; j < D / 16; ++j) acc[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   const float c2 = a.scale * kLog2e;
 
+  // threads 0..127 stage K (row-major and transposed), threads 128..255 stage V (row-major)
+  const int t = threadIdx.x;
+  const bool stK = t < Tile<D>::NBLK, stV = t >= 128 && t - 128 < Tile<D>::NBLK;
+  u32x4_t pre[8];
+  auto fetch = [&](int64_t kb) {
+    if (stK) load_block<D>(a.k + hk * D, a.ldk, seq0 + kb * kB, rows_left(a.S, kb), t, pre);
+    else if (stV) load_block<D>(a.v + hk * D, a.ldv, seq0 + kb * kB, rows_left(a.S, kb), t - 128, pre);
+  };
+  fetch(0);
   for (int64_t kb = 0; kb <= qb; ++kb) {
     __syncthreads();
-    const int nvalid = (int)(a.S - kb * kB < kB ? a.S - kb * kB : kB);
-    const int t = threadIdx.x;
-    if (t < Tile<D>::NBLK)
-      stage_block<D>(a.k + hk * D, a.ldk, seq0 + kb * kB, nvalid, t, k_rm, k_tr);
-    else if (t >= 128 && t - 128 < Tile<D>::NBLK)
-      stage_block<D>(a.v + hk * D, a.ldv, seq0 + kb * kB, nvalid, t - 128, v_rm, nullptr);
+    if (stK) store_block<D>(pre, t, k_rm, k_tr);
+    else if (stV) store_block<D>(pre, t - 128, v_rm, nullptr);
     __syncthreads();
+    if (kb < qb) fetch(kb + 1);
 
-    // S^T and dP^T tiles tt: keys 16 tt + 4 g + e (rows) x query `col`
+    // S^T and dP^T tiles tt: keys 16 tt + 4 g + e (rows) x query `col`; two tiles per half
     floatx4 s[4], dp[4];
-    {
-      bf16x8 ka[4][D / 32], va[4][D / 32];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+    for (int hf = 0; hf < 2; ++hf) {
+      bf16x8 ka[2][D / 32], va[2][D / 32];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
-          ka[tt][c] = rm_frag<D>(k_rm, 16 * tt + col, 4 * c + g);
-          va[tt][c] = rm_frag<D>(v_rm, 16 * tt + col, 4 * c + g);
+          ka[u][c] = rm_frag<D>(k_rm, 16 * (2 * hf + u) + col, 4 * c + g);
+          va[u][c] = rm_frag<D>(v_rm, 16 * (2 * hf + u) + col, 4 * c + g);
         }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
+      for (int u = 0; u < 2; ++u) {
+        const int tt = 2 * hf + u;
         s[tt] = dp[tt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
-          s[tt] = mfma(ka[tt][c], qf[c], s[tt]);
-          dp[tt] = mfma(va[tt][c], df[c], dp[tt]);
+          s[tt] = mfma(ka[u][c], qf[c], s[tt]);
+          dp[tt] = mfma(va[u][c], df[c], dp[tt]);
         }
       }
       AT_MFMA_FENCE();
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
-          asm volatile("" ::"v"(ka[tt][c]));
-          asm volatile("" ::"v"(va[tt][c]));
+          asm volatile("" ::"v"(ka[u][c]));
+          asm volatile("" ::"v"(va[u][c]));
         }
     }
 #pragma unroll
@@ -501,27 +524,20 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_q(AttnArgs a) {
         if (kb == qb && kb * kB + 16 * tt + 4 * g + e > q_in_seq) p = 0.0f;
         dp[tt][e] = p * (dp[tt][e] - dq_dot);
       }
-    // dQ^T += K^T dS^T over the block's 64 keys
-    {
-      bf16x8 sf[2], ka[2][D / 16];
+    // dQ^T += K^T dS^T over the block's 64 keys (two steps of 32)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        sf[c] = acc_frag(dp[2 * c], dp[2 * c + 1]);
+    for (int c = 0; c < 2; ++c) {
+      const bf16x8 sf = acc_frag(dp[2 * c], dp[2 * c + 1]);
+      bf16x8 ka[D / 16];
 #pragma unroll
-        for (int j = 0; j < D / 16; ++j) ka[c][j] = tr_frag(k_tr, 16 * j + col, c, g);
-      }
+      for (int jj = 0; jj < D / 16; ++jj) ka[jj] = tr_frag(k_tr, 16 * jj + col, c, g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j) acc[j] = mfma(ka[c][j], sf[c], acc[j]);
+      for (int jj = 0; jj < D / 16; ++jj) acc[jj] = mfma(ka[jj], sf, acc[jj]);
       AT_MFMA_FENCE();
+      asm volatile("" ::"v"(sf));
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        asm volatile("" ::"v"(sf[c]));
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j) asm volatile("" ::"v"(ka[c][j]));
-      }
+      for (int jj = 0; jj < D / 16; ++jj) asm volatile("" ::"v"(ka[jj]));
     }
   }
   if (qvalid) {
