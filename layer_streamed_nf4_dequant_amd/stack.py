@@ -196,7 +196,11 @@ class Stack:
         # "staged_t": as "staged", but the backward visit also stages W^T [K][N] and the dX
         #             product reads that (both operands N-contiguous);
         # "fused":    the GEMMs dequantise their W tiles straight into LDS (no staging buffer).
-        # All three hand the matrix cores the same bf16 fragments, so all give identical bits.
+        # All three hand the matrix cores the same bf16 fragments: the forward outputs and every
+        # single-projection backward are identical bits. The grouped backward of the projections
+        # that share X_h sums their input gradients in a different order (staged: one GEMM over
+        # their concatenated reduction; fused: member by member), so dX_h, and what depends on it,
+        # agree across modes to fp32 rounding.
         if dequant not in ("staged", "staged_t", "fused"):
             raise ValueError(dequant)
         self.dequant = dequant if cfg.base == "nf4" else "fused"

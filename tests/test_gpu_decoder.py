@@ -158,3 +158,4 @@ def test_decoder_gradient_accumulation(gpu):
     for a, b in zip(one, two):
         assert torch.equal(2 * a, b)
     m.close()
+
