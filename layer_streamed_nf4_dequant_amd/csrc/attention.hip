@@ -119,6 +119,11 @@ __device__ __forceinline__ bf16x8 acc_frag(floatx4 t0, floatx4 t1) {
                        pack_bf16x2(t1[2], t1[3])});
 }
 
+// 2^x on the hardware exponential (v_exp_f32). Softmax weights below 2^-126 are of no
+// consequence next to the row's largest (weight 1), so the library's denormal range handling
+// is not needed; -inf gives 0.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Keep MFMA source registers from being reused before the MFMAs have read them.
 #define AT_MFMA_FENCE()                    \
   do {                                     \
@@ -219,21 +224,24 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(AttnArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m, mx);
-    const float alpha = exp2f(m - m_new);
+    const float alpha = ex2(m - m_new);
     float rs = 0.0f;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        s[tt][e] = exp2f(s[tt][e] - m_new);
+        s[tt][e] = ex2(s[tt][e] - m_new);
         rs += s[tt][e];
       }
     rs += __shfl_xor(rs, 16);
     rs += __shfl_xor(rs, 32);
     l = l * alpha + rs;
     m = m_new;
+    // rescale only when some lane's running max moved (multiplying by exactly 1 changes nothing)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
+      for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
+    }
     // O^T += V^T P^T over the block's 64 keys (two reduction steps of 32)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -393,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int qi = 16 * tt + 4 * g + e;
-          float p = exp2f(s[tt][e] * c2 - lse2_s[qi]);
+          float p = ex2(s[tt][e] * c2 - lse2_s[qi]);
           if (qb == kb && qb * kB + qi < k_in_seq) p = 0.0f;
           s[tt][e] = p;
           dp[tt][e] = p * (dp[tt][e] - dot_s[qi]);
@@ -520,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_q(AttnArgs a) {
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float p = exp2f(s[tt][e] * c2 - lse2);
+        float p = ex2(s[tt][e] * c2 - lse2);
         if (kb == qb && kb * kB + 16 * tt + 4 * g + e > q_in_seq) p = 0.0f;
         dp[tt][e] = p * (dp[tt][e] - dq_dot);
       }
