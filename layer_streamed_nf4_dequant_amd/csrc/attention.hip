@@ -37,6 +37,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kB = 64;                       // rows per block (queries or keys)
 constexpr int kTP = kB * 2 + 16;             // pitch (bytes) of a transposed tile: [D][64] + pad
+constexpr int kFwdThreads = 512;             // forward: 8 waves of 16 queries share each K/V tile
+constexpr int kFwdQ = 128;                   // queries per forward workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
@@ -144,19 +146,21 @@ struct AttnArgs {
 };
 
 // ------------------------------------------------------------------------------------------
-// Forward: one workgroup per (query block, sequence, query head), heaviest blocks first.
+// Forward: one workgroup of 8 waves per (128-query block, sequence, query head), heaviest blocks
+// first; a wave skips the key blocks that lie entirely after its 16 queries.
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_attn_fwd(AttnArgs a) {
+__global__ __launch_bounds__(kFwdThreads) void k_attn_fwd(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char k_rm[Tile<D>::RM_BYTES];
   __shared__ __attribute__((aligned(16))) char v_tr[Tile<D>::TR_BYTES];
-  const int64_t nqb = (a.S + kB - 1) / kB;
+  const int64_t nqb = (a.S + kFwdQ - 1) / kFwdQ, nkb = (a.S + kB - 1) / kB;
   const int64_t per = a.n_seq * a.n_q;
   const int64_t qb = nqb - 1 - blockIdx.x / per;
   const int64_t rest = blockIdx.x % per;
   const int64_t b = rest / a.n_q;
   const int h = (int)(rest % a.n_q), hk = h / (a.n_q / a.n_kv);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
-  const int64_t q_in_seq = qb * kB + 16 * wave + col;
+  const int64_t wq0 = qb * kFwdQ + 16 * wave;   // this wave's first query
+  const int64_t q_in_seq = wq0 + col;
   const int64_t seq0 = b * a.S;
   const uint16_t *Kb = a.k + hk * D, *Vb = a.v + hk * D;
 
@@ -172,21 +176,26 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(AttnArgs a) {
   float m = -INFINITY, l = 0.0f;
   const float c2 = a.scale * kLog2e;
 
-  // threads 0..127 stage K (row-major), threads 128..255 stage V (transposed)
+  // threads 0..127 stage K (row-major), threads 128..255 stage V (transposed); the key blocks
+  // run up to the one holding the workgroup's last query
   const int t = threadIdx.x;
   const bool stK = t < Tile<D>::NBLK, stV = t >= 128 && t - 128 < Tile<D>::NBLK;
+  const int64_t kb_end = ((qb + 1) * kFwdQ < a.S ? (qb + 1) * kFwdQ : a.S);   // one past the last query
+  const int64_t kb_last = (kb_end - 1) / kB < nkb - 1 ? (kb_end - 1) / kB : nkb - 1;
   u32x4_t pre[8];
   auto fetch = [&](int64_t kb) {
     if (stK) load_block<D>(Kb, a.ldk, seq0 + kb * kB, rows_left(a.S, kb), t, pre);
     else if (stV) load_block<D>(Vb, a.ldv, seq0 + kb * kB, rows_left(a.S, kb), t - 128, pre);
   };
   fetch(0);
-  for (int64_t kb = 0; kb <= qb; ++kb) {
+  for (int64_t kb = 0; kb <= kb_last; ++kb) {
     __syncthreads();
     if (stK) store_block<D>(pre, t, k_rm, nullptr);
     else if (stV) store_block<D>(pre, t - 128, nullptr, v_tr);
     __syncthreads();
-    if (kb < qb) fetch(kb + 1);   // in flight while this block is computed
+    if (kb < kb_last) fetch(kb + 1);   // in flight while this block is computed
+    if (kb * kB > wq0 + 15) continue;  // every key of the block is after this wave's queries
+    const bool diag = kb * kB + kB - 1 > wq0;   // some key of the block is after some query here
 
     // S^T tile tt: keys 16 tt + 4 g + e (rows) x query `col`; two tiles per half
     floatx4 s[4];
@@ -217,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x = s[tt][e] * c2;
-        if (kb == qb && kb * kB + 16 * tt + 4 * g + e > q_in_seq) x = -INFINITY;
+        if (diag && kb * kB + 16 * tt + 4 * g + e > q_in_seq) x = -INFINITY;
         s[tt][e] = x;
         mx = fmaxf(mx, x);
       }
@@ -447,18 +456,19 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
 // dQ: one workgroup per (query block, sequence, query head), heaviest blocks first; a wave owns
 // 16 queries (lane column = query) and loops over the key blocks up to its own.
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_attn_bwd_q(AttnArgs a) {
+__global__ __launch_bounds__(kFwdThreads) void k_attn_bwd_q(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char k_rm[Tile<D>::RM_BYTES];
   __shared__ __attribute__((aligned(16))) char k_tr[Tile<D>::TR_BYTES];
   __shared__ __attribute__((aligned(16))) char v_rm[Tile<D>::RM_BYTES];
-  const int64_t nqb = (a.S + kB - 1) / kB;
+  const int64_t nqb = (a.S + kFwdQ - 1) / kFwdQ, nkb = (a.S + kB - 1) / kB;
   const int64_t per = a.n_seq * a.n_q;
   const int64_t qb = nqb - 1 - blockIdx.x / per;
   const int64_t rest = blockIdx.x % per;
   const int64_t b = rest / a.n_q;
   const int h = (int)(rest % a.n_q), hk = h / (a.n_q / a.n_kv);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
-  const int64_t q_in_seq = qb * kB + 16 * wave + col;
+  const int64_t wq0 = qb * kFwdQ + 16 * wave;   // this wave's first query
+  const int64_t q_in_seq = wq0 + col;
   const int64_t seq0 = b * a.S;
   const bool qvalid = q_in_seq < a.S;
   bf16x8 qf[D / 32], df[D / 32];   // B operands: query `col`, dims 32 c + 8 g ..
@@ -484,13 +494,17 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_q(AttnArgs a) {
     if (stK) load_block<D>(a.k + hk * D, a.ldk, seq0 + kb * kB, rows_left(a.S, kb), t, pre);
     else if (stV) load_block<D>(a.v + hk * D, a.ldv, seq0 + kb * kB, rows_left(a.S, kb), t - 128, pre);
   };
+  const int64_t kb_end = ((qb + 1) * kFwdQ < a.S ? (qb + 1) * kFwdQ : a.S);   // one past the last query
+  const int64_t kb_last = (kb_end - 1) / kB < nkb - 1 ? (kb_end - 1) / kB : nkb - 1;
   fetch(0);
-  for (int64_t kb = 0; kb <= qb; ++kb) {
+  for (int64_t kb = 0; kb <= kb_last; ++kb) {
     __syncthreads();
     if (stK) store_block<D>(pre, t, k_rm, k_tr);
     else if (stV) store_block<D>(pre, t - 128, v_rm, nullptr);
     __syncthreads();
-    if (kb < qb) fetch(kb + 1);
+    if (kb < kb_last) fetch(kb + 1);
+    if (kb * kB > wq0 + 15) continue;  // every key of the block is after this wave's queries
+    const bool diag = kb * kB + kB - 1 > wq0;
 
     // S^T and dP^T tiles tt: keys 16 tt + 4 g + e (rows) x query `col`; two tiles per half
     floatx4 s[4], dp[4];
@@ -529,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_q(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float p = ex2(s[tt][e] * c2 - lse2);
-        if (kb == qb && kb * kB + 16 * tt + 4 * g + e > q_in_seq) p = 0.0f;
+        if (diag && kb * kB + 16 * tt + 4 * g + e > q_in_seq) p = 0.0f;
         dp[tt][e] = p * (dp[tt][e] - dq_dot);
       }
     // dQ^T += K^T dS^T over the block's 64 keys (two steps of 32)
@@ -634,11 +648,11 @@ lsn_status attention_fwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, in
   a.lse = lse;
   a.out_o = o;
   a.ld_out_o = ldo;
-  const unsigned grid = (unsigned)(((S + kB - 1) / kB) * n_seq * n_q);
+  const unsigned grid = (unsigned)(((S + kFwdQ - 1) / kFwdQ) * n_seq * n_q);
   if (head_dim == 128)
-    hipLaunchKernelGGL(k_attn_fwd<128>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(k_attn_fwd<128>, dim3(grid), dim3(kFwdThreads), 0, (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL(k_attn_fwd<64>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(k_attn_fwd<64>, dim3(grid), dim3(kFwdThreads), 0, (hipStream_t)stream, a);
   return check_hip(hipGetLastError(), "k_attn_fwd launch");
 }
 
@@ -704,15 +718,16 @@ lsn_status attention_bwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, in
   const hipStream_t hs = (hipStream_t)stream;
   const int64_t nb = (S + kB - 1) / kB;
   const unsigned dot_grid = (unsigned)((T * n_q * (D / 8) + kThreads - 1) / kThreads);
-  const unsigned kv_grid = (unsigned)(nb * n_seq * n_kv), q_grid = (unsigned)(nb * n_seq * n_q);
+  const unsigned kv_grid = (unsigned)(nb * n_seq * n_kv);
+  const unsigned q_grid = (unsigned)(((S + kFwdQ - 1) / kFwdQ) * n_seq * n_q);
   if (head_dim == 128) {
     hipLaunchKernelGGL(k_attn_dot<128>, dim3(dot_grid), dim3(kThreads), 0, hs, a, static_cast<float *>(ws));
     hipLaunchKernelGGL(k_attn_bwd_kv<128>, dim3(kv_grid), dim3(kThreads), 0, hs, a);
-    hipLaunchKernelGGL(k_attn_bwd_q<128>, dim3(q_grid), dim3(kThreads), 0, hs, a);
+    hipLaunchKernelGGL(k_attn_bwd_q<128>, dim3(q_grid), dim3(kFwdThreads), 0, hs, a);
   } else {
     hipLaunchKernelGGL(k_attn_dot<64>, dim3(dot_grid), dim3(kThreads), 0, hs, a, static_cast<float *>(ws));
     hipLaunchKernelGGL(k_attn_bwd_kv<64>, dim3(kv_grid), dim3(kThreads), 0, hs, a);
-    hipLaunchKernelGGL(k_attn_bwd_q<64>, dim3(q_grid), dim3(kThreads), 0, hs, a);
+    hipLaunchKernelGGL(k_attn_bwd_q<64>, dim3(q_grid), dim3(kFwdThreads), 0, hs, a);
   }
   return check_hip(hipGetLastError(), "attention backward launch");
 }
