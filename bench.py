@@ -153,30 +153,6 @@ def lm_head_figure(cfg, vocab: int = 128256, chunk: int = 512, iters: int = 5):
     return out
 
 
-def decoder_figure(cfg, vocab: int = 128256, steps: int = 3):
-    """The whole decoder training step (embedding, every layer's glue, attention and seven LoRA
-    projections on the streamed NF4 base, final norm, LM-head cross-entropy, backward with
-    per-layer recompute) at the workload's shape with a Llama-3.1 vocabulary: tokens/s over
-    `steps` timed steps after one warm-up, streamed through the same 2-slot pool."""
-    import torch
-    from layer_streamed_nf4_dequant_amd.decoder import DecoderModel
-    m = DecoderModel(cfg, vocab=vocab, modes=("streamed",))
-    m.step("streamed")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        m.step("streamed")
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    out = {"layers": m.L, "vocab": vocab, "tokens_per_step": cfg.T, "seq_len": cfg.seq_len,
-           "tokens_per_s": round(cfg.T * steps / wall, 1), "ms_per_step": round(wall * 1e3 / steps, 1),
-           "mean_loss": round(m.mean_loss(), 4)}
-    m.close()
-    del m
-    torch.cuda.empty_cache()
-    return out
-
-
 def hipblaslt_ceiling(cfg, iters: int = 10):
     """Same-session reference: torch.matmul (hipBLASLt) bf16 X W^T at the stack's projection shapes
     and T, TFLOP/s per shape (no LoRA term)."""
@@ -276,7 +252,7 @@ def main():
 
     import torch
     from layer_streamed_nf4_dequant_amd import configs, lib
-    from layer_streamed_nf4_dequant_amd.microbench import attention_figure, glue_figure
+    from layer_streamed_nf4_dequant_amd.microbench import attention_figure, decoder_figure, glue_figure
     from layer_streamed_nf4_dequant_amd.stack import Stack
 
     lib.load()
@@ -453,8 +429,8 @@ def main():
         other["attention"] = attention_figure(cfg)
         print(f"[bench] attention: {other['attention']}", flush=True)
         if cfg.base == "nf4" and not cfg.single:
-            other["decoder_step_streamed"] = decoder_figure(cfg)
-            print(f"[bench] decoder step: {other['decoder_step_streamed']}", flush=True)
+            other["decoder_step"] = decoder_figure(cfg)
+            print(f"[bench] decoder step: {other['decoder_step']}", flush=True)
 
     tokens = cfg.T * args.steps
     value = tokens / wall

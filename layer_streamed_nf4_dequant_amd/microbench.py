@@ -3,6 +3,7 @@ glue (RMSNorm, rotary embedding, SwiGLU) and causal attention, at a stack config
 count, widths and heads.
 
     python -m layer_streamed_nf4_dequant_amd.microbench [--config C3] [--iters 20]
+    python -m layer_streamed_nf4_dequant_amd.microbench --decoder [--config C3] [--steps 3]
 
 prints one JSON object: per kernel, microseconds per call (HIP events around a replayed HIP graph
 of back-to-back calls) and the algorithmic HBM rate against the 8 TB/s peak. bench.py reports
@@ -135,14 +136,48 @@ def attention_figure(cfg, iters: int = 10):
     return out
 
 
+def decoder_figure(cfg, vocab: int = 128256, steps: int = 3, modes=("streamed", "resident")):
+    """The whole decoder training step (embedding, every layer's glue, attention and seven LoRA
+    projections on the NF4 base, final norm, LM-head cross-entropy, backward with per-layer
+    recompute) at the configuration's shape with a Llama-3.1 vocabulary: tokens/s over `steps`
+    timed steps after one warm-up, streamed through the 2-slot pool and with every layer
+    resident (same kernels, no copies)."""
+    import time
+
+    import torch
+    from layer_streamed_nf4_dequant_amd.decoder import DecoderModel
+    m = DecoderModel(cfg, vocab=vocab, modes=tuple(modes))
+    out = {"layers": m.L, "vocab": vocab, "tokens_per_step": cfg.T, "seq_len": cfg.seq_len}
+    for mode in modes:
+        m.step(mode)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            m.step(mode)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        out[mode] = {"tokens_per_s": round(cfg.T * steps / wall, 1), "ms_per_step": round(wall * 1e3 / steps, 1)}
+    out["mean_loss"] = round(m.mean_loss(), 4)
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> None:
     from layer_streamed_nf4_dequant_amd import configs
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--config", default="C3")
     ap.add_argument("--iters", type=int, default=20)
+    ap.add_argument("--decoder", action="store_true",
+                    help="time the whole decoder training step (streamed, then resident) instead")
+    ap.add_argument("--steps", type=int, default=3, help="timed decoder steps per mode")
     args = ap.parse_args()
     cfg = getattr(configs, args.config)
-    print(json.dumps({"glue": glue_figure(cfg, args.iters), "attention": attention_figure(cfg)}), flush=True)
+    if args.decoder:
+        print(json.dumps({"decoder_step": decoder_figure(cfg, steps=args.steps)}), flush=True)
+    else:
+        print(json.dumps({"glue": glue_figure(cfg, args.iters), "attention": attention_figure(cfg)}), flush=True)
 
 
 if __name__ == "__main__":
