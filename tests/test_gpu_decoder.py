@@ -7,7 +7,8 @@ cross-entropy, backward with per-layer recompute):
     gradient;
   * streamed == resident bit for bit (loss, final hidden state, every dA and dB), each layer's
     recompute equal to its forward, at the Qwen2.5-0.5B shape with four layers;
-  * two micro-batches of the same rows give exactly twice every gradient.
+  * two micro-batches of the same rows give exactly twice every gradient;
+  * the GEMMs dequantising NF4 tiles into LDS agree with the staged dequant to fp32 rounding.
 """
 
 import numpy as np
@@ -159,3 +160,21 @@ def test_decoder_gradient_accumulation(gpu):
         assert torch.equal(2 * a, b)
     m.close()
 
+
+
+def test_decoder_fused_dequant_matches_staged(gpu):
+    """The GEMMs that dequantise NF4 tiles into LDS ("fused") against the staged dequant: the
+    forward GEMMs and every single-projection backward see the same bf16 operands; only the
+    grouped backward's input-gradient sum runs in another order (member by member), so the step
+    agrees to fp32 rounding."""
+    import torch
+    res = {}
+    for dq in ("staged", "fused"):
+        m = DecoderModel(TINY, vocab=512, modes=("resident",), dequant=dq)
+        m.step("resident")
+        res[dq] = (hb(m.loss), [hb(t) for l in range(m.L) for t in m.dA[l] + m.dB[l]])
+        m.close()
+    assert olora.rel_l2(res["fused"][0], res["staged"][0]) <= 1e-4
+    for a, b in zip(res["fused"][1], res["staged"][1]):
+        assert olora.rel_l2(a, b) <= 1e-3
+    torch.cuda.synchronize()
