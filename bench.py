@@ -119,7 +119,7 @@ def clock_sampler():
     return finish
 
 
-def lm_head_figure(cfg, vocab: int = 128256, chunk: int = 512, iters: int = 5):
+def lm_head_figure(cfg, vocab: int = 128256, chunk: int = 2048, iters: int = 5):
     """The resident LM head's cross-entropy (lm_head_ce) at the workload's T and hidden width with
     a Llama-3.1 vocabulary: time per call, its two GEMMs' rate (4 T V H FLOPs per call), and the
     workspace per logit element of a chunk."""

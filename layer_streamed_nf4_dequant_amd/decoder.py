@@ -38,7 +38,7 @@ class DecoderModel:
 
     def __init__(self, cfg: StackConfig, vocab: int, layers: int | None = None, seed: int = 0,
                  modes=("streamed",), dequant: str = "staged", eps: float = EPS, theta: float = THETA,
-                 ce_chunk: int = 512):
+                 ce_chunk: int = 2048):
         import torch
         self.torch = torch
         self.cfg, self.V, self.seed = cfg, vocab, seed
