@@ -164,9 +164,11 @@ def test_decoder_gradient_accumulation(gpu):
 
 def test_decoder_fused_dequant_matches_staged(gpu):
     """The GEMMs that dequantise NF4 tiles into LDS ("fused") against the staged dequant: the
-    forward GEMMs and every single-projection backward see the same bf16 operands; only the
-    grouped backward's input-gradient sum runs in another order (member by member), so the step
-    agrees to fp32 rounding."""
+    forward GEMMs and every single-projection backward see the same bf16 operands, so the
+    forward (and the loss) is identical; only the grouped backward's input-gradient sum runs in
+    another order (member by member). That fp32 rounding difference can flip the bf16 rounding
+    of an activation gradient further down (one element by 2^-8), and such flips travel through
+    the layers below, so the gradients agree to 5e-3 rel-L2 (half the oracle bar)."""
     import torch
     res = {}
     for dq in ("staged", "fused"):
@@ -174,7 +176,7 @@ def test_decoder_fused_dequant_matches_staged(gpu):
         m.step("resident")
         res[dq] = (hb(m.loss), [hb(t) for l in range(m.L) for t in m.dA[l] + m.dB[l]])
         m.close()
-    assert olora.rel_l2(res["fused"][0], res["staged"][0]) <= 1e-4
+    assert np.array_equal(res["fused"][0], res["staged"][0])
     for a, b in zip(res["fused"][1], res["staged"][1]):
-        assert olora.rel_l2(a, b) <= 1e-3
+        assert olora.rel_l2(a, b) <= 5e-3
     torch.cuda.synchronize()
