@@ -313,9 +313,11 @@ lsn_status rmsnorm_fwd(int64_t T, int64_t H, const uint16_t *x, const uint16_t *
  * x [T][H] bf16; gain [H] bf16; rstd [T] fp32 from rmsnorm_fwd; dy [T][H] fp32 (the normalised
  * input's gradient as the projections' fp32 dX modes leave it); dx [T][H] fp32, stored
  * (accumulate = 0) or added to what it holds (accumulate != 0: the residual stream's gradient).
+ * dx_bf16 (device, may be NULL): also receives bf16(dx) as stored (round to nearest even), the
+ * operand the next projection backward reads, so no separate conversion pass is needed.
  */
 lsn_status rmsnorm_bwd(int64_t T, int64_t H, const uint16_t *x, const uint16_t *gain, const float *rstd,
-                       const float *dy, float *dx, int32_t accumulate, void *stream);
+                       const float *dy, float *dx, int32_t accumulate, uint16_t *dx_bf16, void *stream);
 
 /*
  * rope_apply - rotary position embedding, in place, on n_heads heads of width head_dim at the

@@ -90,7 +90,7 @@ template <int NT>
 __global__ __launch_bounds__(NT) void k_rmsnorm_bwd(int64_t H, const uint16_t *__restrict__ x,
                                                     const uint16_t *__restrict__ g, const float *__restrict__ rstd,
                                                     const float *__restrict__ dy, float *__restrict__ dx,
-                                                    int accumulate) {
+                                                    int accumulate, uint16_t *__restrict__ dx16) {
   __shared__ float scratch[NT / 64];
   const int64_t row = blockIdx.x;
   const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x + row * H);
@@ -121,13 +121,19 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_bwd(int64_t H, const uint16_t *_
       const float gd = __fmul_rn(bf16f((uint16_t)(gv[q] >> h)), e < 4 ? d0[e & 3] : d1[e & 3]);
       res[e] = __fsub_rn(__fmul_rn(r, gd), __fmul_rn(bf16f((uint16_t)(v[q] >> h)), k));
     }
+    floatx4_t cur[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      floatx4_t cur = accumulate ? o[2 * c + half] : floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      cur[half] = accumulate ? o[2 * c + half] : floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) cur[e] = accumulate ? __fadd_rn(cur[e], res[4 * half + e]) : res[4 * half + e];
-      o[2 * c + half] = cur;
+      for (int e = 0; e < 4; ++e)
+        cur[half][e] = accumulate ? __fadd_rn(cur[half][e], res[4 * half + e]) : res[4 * half + e];
+      o[2 * c + half] = cur[half];
     }
+    if (dx16)   // the bf16 copy of the stored gradient, for the operand that reads it next
+      reinterpret_cast<u32x4_t *>(dx16 + row * H)[c] =
+          u32x4_t{pack_bf16x2(cur[0][0], cur[0][1]), pack_bf16x2(cur[0][2], cur[0][3]),
+                  pack_bf16x2(cur[1][0], cur[1][1]), pack_bf16x2(cur[1][2], cur[1][3])};
   }
 }
 
@@ -380,7 +386,7 @@ lsn_status rmsnorm_fwd(int64_t T, int64_t H, const uint16_t *x, const uint16_t *
 }
 
 lsn_status rmsnorm_bwd(int64_t T, int64_t H, const uint16_t *x, const uint16_t *gain, const float *rstd,
-                       const float *dy, float *dx, int32_t accumulate, void *stream) {
+                       const float *dy, float *dx, int32_t accumulate, uint16_t *dx_bf16, void *stream) {
   if (T < 1 || T > 0x7fffffff || H < 8 || H % 8)
     return fail(LSN_E_ARG, "rmsnorm_bwd: need 1 <= T < 2^31 and H a positive multiple of 8");
   if (!x || !gain || !rstd || !dy || !dx || !a16(x) || !a16(gain) || !a16(dy) || !a16(dx))
@@ -389,19 +395,26 @@ lsn_status rmsnorm_bwd(int64_t T, int64_t H, const uint16_t *x, const uint16_t *
   if (ranges_overlap(dx, fb, x, (size_t)(T * H * 2)) || ranges_overlap(dx, fb, dy, fb) ||
       ranges_overlap(dx, fb, rstd, (size_t)T * 4))
     return fail(LSN_E_ARG, "rmsnorm_bwd: dx overlaps an input");
+  if (dx_bf16) {
+    const size_t hb = (size_t)(T * H * 2);
+    if (!a16(dx_bf16) || ranges_overlap(dx_bf16, hb, x, hb) || ranges_overlap(dx_bf16, hb, dy, fb) ||
+        ranges_overlap(dx_bf16, hb, dx, fb) || ranges_overlap(dx_bf16, hb, rstd, (size_t)T * 4) ||
+        ranges_overlap(dx_bf16, hb, gain, (size_t)H * 2))
+      return fail(LSN_E_ARG, "rmsnorm_bwd: dx_bf16 misaligned or overlapping");
+  }
   lsn_status st = require_gfx950();
   if (st != LSN_OK) return st;
   const hipStream_t hs = (hipStream_t)stream;
   const int acc = accumulate ? 1 : 0;
   switch (rms_team(H)) {
     case 64:
-      hipLaunchKernelGGL(k_rmsnorm_bwd<64>, dim3((unsigned)T), dim3(64), 0, hs, H, x, gain, rstd, dy, dx, acc);
+      hipLaunchKernelGGL(k_rmsnorm_bwd<64>, dim3((unsigned)T), dim3(64), 0, hs, H, x, gain, rstd, dy, dx, acc, dx_bf16);
       break;
     case 128:
-      hipLaunchKernelGGL(k_rmsnorm_bwd<128>, dim3((unsigned)T), dim3(128), 0, hs, H, x, gain, rstd, dy, dx, acc);
+      hipLaunchKernelGGL(k_rmsnorm_bwd<128>, dim3((unsigned)T), dim3(128), 0, hs, H, x, gain, rstd, dy, dx, acc, dx_bf16);
       break;
     default:
-      hipLaunchKernelGGL(k_rmsnorm_bwd<256>, dim3((unsigned)T), dim3(256), 0, hs, H, x, gain, rstd, dy, dx, acc);
+      hipLaunchKernelGGL(k_rmsnorm_bwd<256>, dim3((unsigned)T), dim3(256), 0, hs, H, x, gain, rstd, dy, dx, acc, dx_bf16);
   }
   return check_hip(hipGetLastError(), "k_rmsnorm_bwd launch");
 }

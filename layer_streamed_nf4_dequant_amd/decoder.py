@@ -208,10 +208,10 @@ class DecoderModel:
         lib.add_bf16(self.h, self.dproj, y, stream=s)
 
     def _layer_bwd(self, base: int, l: int, x, s, grad_mode: int):
-        """self.dy (fp32, the gradient of the layer's output) becomes the gradient of its input x;
-        dA, dB of the layer's seven projections are set (GRAD_SET) or added to (GRAD_ADD)."""
+        """self.dy (fp32, the gradient of the layer's output; self.dy_b its bf16 copy) becomes the
+        gradient of its input x (and self.dy_b that one's bf16 copy); dA, dB of the layer's seven
+        projections are set (GRAD_SET) or added to (GRAD_ADD)."""
         J, U, dA, dB = self.j, self.U, self.dA[l], self.dB[l]
-        lib.convert(self.dy, self.dy_b, stream=s)
         lib.lora_linear_bwd(self._desc(base, l, "down"), self.m, self.dy_b, U[J["down"]], self.dm, dA[J["down"]],
                             dB[J["down"]], dx_mode=lib.DX_BF16_SET, grad_mode=grad_mode, ws=self.ws, stream=s)
         lib.swiglu_bwd(self.gate, self.up, self.dm, self.dgate, self.dup, stream=s)
@@ -219,8 +219,8 @@ class DecoderModel:
         lib.lora_linear_bwd_group([self._desc(base, l, n) for n in gu], self.n2, [self.dgate, self.dup],
                                   [U[J[n]] for n in gu], self.dn, [dA[J[n]] for n in gu], [dB[J[n]] for n in gu],
                                   dx_mode=lib.DX_F32_SET, grad_mode=grad_mode, ws=self.ws, stream=s)
-        lib.rmsnorm_bwd(self.h, self.g2[l], self.rstd2, self.dn, self.dy, accumulate=True, stream=s)   # dy = dh
-        lib.convert(self.dy, self.dh_b, stream=s)
+        lib.rmsnorm_bwd(self.h, self.g2[l], self.rstd2, self.dn, self.dy, accumulate=True, dx_bf16=self.dh_b,
+                        stream=s)                                                                   # dy = dh
         lib.lora_linear_bwd(self._desc(base, l, "o"), self.o_att, self.dh_b, U[J["o"]], self.do_att, dA[J["o"]],
                             dB[J["o"]], dx_mode=lib.DX_BF16_SET, grad_mode=grad_mode, ws=self.ws, stream=s)
         lib.attention_bwd(self.q, self.k, self.v, self.o_att, self.lse, self.do_att, self.dq, self.dk, self.dv,
@@ -231,7 +231,8 @@ class DecoderModel:
         lib.lora_linear_bwd_group([self._desc(base, l, n) for n in qkv], self.n1, [self.dq, self.dk, self.dv],
                                   [U[J[n]] for n in qkv], self.dn, [dA[J[n]] for n in qkv], [dB[J[n]] for n in qkv],
                                   dx_mode=lib.DX_F32_SET, grad_mode=grad_mode, ws=self.ws, stream=s)
-        lib.rmsnorm_bwd(x, self.g1[l], self.rstd1, self.dn, self.dy, accumulate=True, stream=s)      # dy = dx
+        lib.rmsnorm_bwd(x, self.g1[l], self.rstd1, self.dn, self.dy, accumulate=True, dx_bf16=self.dy_b,
+                        stream=s)                                                                   # dy = dx
 
     # -------------------------------------------------------------------------------------------
     def step(self, mode: str = "streamed", micro_batches: int = 1, check_recompute: bool = False) -> float:
@@ -262,7 +263,8 @@ class DecoderModel:
                 lib.lm_head_ce(self.n_f, self.W_head, self.labels, 1.0 / self.n_counted, self.loss, self.dn_f,
                                self.ce_chunk, self.ws_ce, stream=s)
                 lib.convert(self.dn_f, self.dn, stream=s)
-                lib.rmsnorm_bwd(xL, self.g_final, self.rstd_f, self.dn, self.dy, accumulate=False, stream=s)
+                lib.rmsnorm_bwd(xL, self.g_final, self.rstd_f, self.dn, self.dy, accumulate=False,
+                                dx_bf16=self.dy_b, stream=s)
                 for l in reversed(range(self.L)):
                     base = self._base(mode, l, sh, forward=False)
                     self._stage(base, l, s)

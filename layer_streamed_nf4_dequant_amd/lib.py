@@ -125,7 +125,7 @@ def load():
         "lm_head_ce": (i32, [i64, i64, i64, vp, vp, vp, f32, vp, vp, i64, vp, sz, vp]),
         "embedding_gather": (i32, [i64, i64, i64, vp, vp, vp, vp, vp]),
         "rmsnorm_fwd": (i32, [i64, i64, vp, vp, f32, vp, vp, vp]),
-        "rmsnorm_bwd": (i32, [i64, i64, vp, vp, vp, vp, vp, i32, vp]),
+        "rmsnorm_bwd": (i32, [i64, i64, vp, vp, vp, vp, vp, i32, vp, vp]),
         "rope_apply": (i32, [i64, i32, i32, vp, i64, vp, f32, i32, vp]),
         "swiglu_fwd": (i32, [i64, vp, vp, vp, vp]),
         "swiglu_bwd": (i32, [i64, vp, vp, vp, vp, vp, vp]),
@@ -393,11 +393,12 @@ def rmsnorm_fwd(x, gain, eps: float, y, rstd, stream=None) -> None:
     check(load().rmsnorm_fwd(T, H, _ptr(x), _ptr(gain), float(eps), _ptr(y), _ptr(rstd), _stream_handle(stream)))
 
 
-def rmsnorm_bwd(x, gain, rstd, dy, dx, accumulate: bool = False, stream=None) -> None:
-    """dx (fp32) = gradient of rmsnorm_fwd with respect to x, stored or added into dx."""
+def rmsnorm_bwd(x, gain, rstd, dy, dx, accumulate: bool = False, dx_bf16=None, stream=None) -> None:
+    """dx (fp32) = gradient of rmsnorm_fwd with respect to x, stored or added into dx; dx_bf16 (optional)
+    also receives bf16(dx)."""
     T, H = x.shape
     check(load().rmsnorm_bwd(T, H, _ptr(x), _ptr(gain), _ptr(rstd), _ptr(dy), _ptr(dx), int(bool(accumulate)),
-                             _stream_handle(stream)))
+                             _ptr(dx_bf16), _stream_handle(stream)))
 
 
 def rope_apply(x, positions, n_heads: int, head_dim: int, theta: float, inverse: bool = False, stream=None) -> None:

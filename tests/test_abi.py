@@ -71,7 +71,7 @@ def test_glue_argument_errors_without_gpu():
     L = lib.load()
     assert L.rmsnorm_fwd(4, 12, None, None, 1e-5, None, None, None) == lib.LSN_E_ARG
     assert b"multiple of 8" in L.lsn_last_error()
-    assert L.rmsnorm_bwd(0, 64, None, None, None, None, None, 0, None) == lib.LSN_E_ARG
+    assert L.rmsnorm_bwd(0, 64, None, None, None, None, None, 0, None, None) == lib.LSN_E_ARG
     assert L.rope_apply(1, 1, 3, None, 3, None, 10000.0, 0, None) == lib.LSN_E_ARG
     assert L.rope_apply(1, 1, 1026, None, 1026, None, 10000.0, 0, None) == lib.LSN_E_ARG
     assert L.rope_apply(2, 2, 64, None, 100, None, 10000.0, 0, None) == lib.LSN_E_ARG

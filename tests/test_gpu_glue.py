@@ -107,8 +107,11 @@ def test_rmsnorm_bwd_parity(gpu, T, H, eps, accumulate):
     rstd = torch.empty(T, dtype=torch.float32, device="cuda")
     lib.rmsnorm_fwd(xd, gd, eps, y, rstd)
     dx = torch.from_numpy(dx0.copy()).cuda() if accumulate else torch.full((T, H), float("nan"), device="cuda")
-    lib.rmsnorm_bwd(xd, gd, rstd, torch.from_numpy(dy).cuda(), dx, accumulate=accumulate)
+    dx16 = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    lib.rmsnorm_bwd(xd, gd, rstd, torch.from_numpy(dy).cuda(), dx, accumulate=accumulate, dx_bf16=dx16)
     torch.cuda.synchronize()
+    # the bf16 copy is the stored fp32 gradient rounded to nearest even
+    np.testing.assert_array_equal(bits(dx16).view(np.uint16), onf4.bf16_rne(dx.cpu().numpy()))
     x, g, dy64 = f32(xb), f32(gb), dy.astype(np.float64)
     ref = og.rmsnorm_bwd(x, g, dy64, eps) + (dx0 if accumulate else 0.0)
     # fp32 error: the first term to a few ulps, the row sum to ~30 ulps of the sum of |terms|
