@@ -134,6 +134,7 @@ class DecoderModel:
         self.ws_ce = e((lib.lm_head_ce_ws_bytes(ce_chunk, H, vocab),), torch.uint8)
         self.w_stage = [e((p.N, p.K)) for p in self.layout] if dequant == "staged" else None
         self.recompute_ok = []
+        self.x_ref = self.loss_ref = None
 
         # ---- pool ----
         self.pool, self.slots = None, None
@@ -184,27 +185,33 @@ class DecoderModel:
         return self.resident[l].data_ptr()
 
     # -------------------------------------------------------------------------------------------
-    def _layer_fwd(self, base: int, l: int, x, y, s):
-        """y = layer l applied to x (keeps the intermediates the backward needs)."""
+    def _layer_fwd(self, base: int, l: int, x, y, s, adapters: bool = True):
+        """y = layer l applied to x (keeps the intermediates the backward needs). adapters=False:
+        the frozen base alone (the reference model), U untouched."""
         J, U = self.j, self.U
+        mode = lib.ADAPTERS_U_READY if adapters else lib.ADAPTERS_OFF
         lib.rmsnorm_fwd(x, self.g1[l], self.eps, self.n1, self.rstd1, stream=s)
         qkv = ("q", "k", "v")
-        lib.lora_down(self.n1, [self.A[l][J[n]] for n in qkv], [U[J[n]] for n in qkv], stream=s)
+        if adapters:
+            lib.lora_down(self.n1, [self.A[l][J[n]] for n in qkv], [U[J[n]] for n in qkv], stream=s)
         lib.lora_linear_fwd_group([self._desc(base, l, n) for n in qkv], self.n1, [self.q, self.k, self.v],
-                                  [U[J[n]] for n in qkv], adapters=lib.ADAPTERS_U_READY, ws=self.ws, stream=s)
+                                  [U[J[n]] for n in qkv] if adapters else None, adapters=mode, ws=self.ws, stream=s)
         lib.rope_apply(self.q, self.positions, self.nq, self.d, self.theta, stream=s)
         lib.rope_apply(self.k, self.positions, self.nkv, self.d, self.theta, stream=s)
         lib.attention_fwd(self.q, self.k, self.v, self.o_att, self.lse, self.n_seq, self.nq, self.nkv, self.d,
                           stream=s)
-        lib.lora_linear_fwd(self._desc(base, l, "o"), self.o_att, self.a, U[J["o"]], ws=self.ws, stream=s)
+        lib.lora_linear_fwd(self._desc(base, l, "o"), self.o_att, self.a, U[J["o"]] if adapters else None,
+                            adapters=adapters, ws=self.ws, stream=s)
         lib.add_bf16(x, self.a, self.h, stream=s)
         lib.rmsnorm_fwd(self.h, self.g2[l], self.eps, self.n2, self.rstd2, stream=s)
         gu = ("gate", "up")
-        lib.lora_down(self.n2, [self.A[l][J[n]] for n in gu], [U[J[n]] for n in gu], stream=s)
+        if adapters:
+            lib.lora_down(self.n2, [self.A[l][J[n]] for n in gu], [U[J[n]] for n in gu], stream=s)
         lib.lora_linear_fwd_group([self._desc(base, l, n) for n in gu], self.n2, [self.gate, self.up],
-                                  [U[J[n]] for n in gu], adapters=lib.ADAPTERS_U_READY, ws=self.ws, stream=s)
+                                  [U[J[n]] for n in gu] if adapters else None, adapters=mode, ws=self.ws, stream=s)
         lib.swiglu_fwd(self.gate, self.up, self.m, stream=s)
-        lib.lora_linear_fwd(self._desc(base, l, "down"), self.m, self.dproj, U[J["down"]], ws=self.ws, stream=s)
+        lib.lora_linear_fwd(self._desc(base, l, "down"), self.m, self.dproj, U[J["down"]] if adapters else None,
+                            adapters=adapters, ws=self.ws, stream=s)
         lib.add_bf16(self.h, self.dproj, y, stream=s)
 
     def _layer_bwd(self, base: int, l: int, x, s, grad_mode: int):
@@ -235,12 +242,18 @@ class DecoderModel:
                         stream=s)                                                                   # dy = dx
 
     # -------------------------------------------------------------------------------------------
-    def step(self, mode: str = "streamed", micro_batches: int = 1, check_recompute: bool = False) -> float:
+    def step(self, mode: str = "streamed", micro_batches: int = 1, check_recompute: bool = False,
+             reference: bool = False) -> float:
         """One training step (forward, loss, backward with per-layer recompute); returns its time in
         ms on the compute stream. The mean loss over counted rows is self.mean_loss().
         micro_batches=k: k passes over the same rows, the first setting dA, dB, the others adding.
         check_recompute: compare each recomputed layer output with the forward's checkpoint of the
-        next layer's input, bit for bit (device flags in self.recompute_ok; waits for nothing)."""
+        next layer's input, bit for bit (device flags in self.recompute_ok; waits for nothing).
+        reference=True first streams every layer once more with the adapters off (the frozen
+        reference model of DPO-style objectives, "An 8B Fine-Tune Now Fits in 4 GB of VRAM": no
+        second copy of the weights, more layer reads) and leaves its per-row loss in
+        self.loss_ref (the reference log-likelihood of each label is -loss_ref). It changes no
+        training state."""
         torch = self.torch
         s = self.compute
         sh = s.cuda_stream
@@ -248,6 +261,8 @@ class DecoderModel:
         self.recompute_ok = []
         with torch.cuda.stream(s):
             e0.record(s)
+            if reference:
+                self._reference_sweep(mode, s)
             for mb in range(micro_batches):
                 grad_mode = lib.GRAD_SET if mb == 0 else lib.GRAD_ADD
                 lib.embedding_gather(self.ids, self.E, self.x[0], stream=s)
@@ -277,6 +292,24 @@ class DecoderModel:
             e1.record(s)
         e1.synchronize()
         return e0.elapsed_time(e1)
+
+    def _reference_sweep(self, mode: str, s):
+        sh = s.cuda_stream
+        torch = self.torch
+        if self.x_ref is None:
+            self.x_ref = [torch.empty_like(self.x[0]) for _ in range(2)]
+            self.loss_ref = torch.empty_like(self.loss)
+        lib.embedding_gather(self.ids, self.E, self.x_ref[0], stream=s)
+        for l in range(self.L):
+            base = self._base(mode, l, sh, forward=True)
+            self._stage(base, l, s)
+            self._layer_fwd(base, l, self.x_ref[l % 2], self.x_ref[(l + 1) % 2], s, adapters=False)
+            if mode == "streamed":
+                self.pool.release(l, sh)
+        xL = self.x_ref[self.L % 2]
+        lib.rmsnorm_fwd(xL, self.g_final, self.eps, self.n_f, self.rstd_f, stream=s)
+        lib.lm_head_ce(self.n_f, self.W_head, self.labels, 1.0 / self.n_counted, self.loss_ref, self.dn_f,
+                       self.ce_chunk, self.ws_ce, stream=s)
 
     def mean_loss(self) -> float:
         return float(self.loss.sum() / self.n_counted)
