@@ -140,23 +140,31 @@ def decoder_figure(cfg, vocab: int = 128256, steps: int = 3, modes=("streamed", 
     """The whole decoder training step (embedding, every layer's glue, attention and seven LoRA
     projections on the NF4 base, final norm, LM-head cross-entropy, backward with per-layer
     recompute) at the configuration's shape with a Llama-3.1 vocabulary: tokens/s over `steps`
-    timed steps after one warm-up, streamed through the 2-slot pool and with every layer
-    resident (same kernels, no copies)."""
+    timed steps after one warm-up, streamed through the 2-slot pool, with every layer resident
+    (same kernels, no copies), and streamed with the adapters-off reference sweep in front (the
+    reference model of DPO-style objectives: one more read of every layer per step)."""
     import time
 
     import torch
     from layer_streamed_nf4_dequant_amd.decoder import DecoderModel
     m = DecoderModel(cfg, vocab=vocab, modes=tuple(modes))
     out = {"layers": m.L, "vocab": vocab, "tokens_per_step": cfg.T, "seq_len": cfg.seq_len}
-    for mode in modes:
-        m.step(mode)
+    runs = [(mode, mode, False) for mode in modes]
+    if "streamed" in modes:
+        runs.append(("streamed_with_reference_sweep", "streamed", True))
+    for name, mode, ref in runs:
+        m.step(mode, reference=ref)
         torch.cuda.synchronize()
+        copied0 = m.pool.stats()["bytes_copied"] if mode == "streamed" else 0
         t0 = time.perf_counter()
         for _ in range(steps):
-            m.step(mode)
+            m.step(mode, reference=ref)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        out[mode] = {"tokens_per_s": round(cfg.T * steps / wall, 1), "ms_per_step": round(wall * 1e3 / steps, 1)}
+        out[name] = {"tokens_per_s": round(cfg.T * steps / wall, 1), "ms_per_step": round(wall * 1e3 / steps, 1)}
+        if mode == "streamed":
+            out[name]["layer_reads_per_step"] = round((m.pool.stats()["bytes_copied"] - copied0)
+                                                      / (steps * m.image_bytes), 2)
     out["mean_loss"] = round(m.mean_loss(), 4)
     m.close()
     del m
