@@ -254,6 +254,9 @@ class DecoderModel:
         second copy of the weights, more layer reads) and leaves its per-row loss in
         self.loss_ref (the reference log-likelihood of each label is -loss_ref). It changes no
         training state."""
+        if mode == "streamed" and self.pool is None or mode == "resident" and self.resident is None \
+                or mode not in ("streamed", "resident"):
+            raise ValueError(f"mode {mode!r} was not built for this model")
         torch = self.torch
         s = self.compute
         sh = s.cuda_stream
