@@ -18,7 +18,8 @@ Every kernel call goes through the C ABI (layer_streamed_nf4_dequant_amd.lib); t
 allocates memory, provides streams and times them.
 
 The synthetic stack (the projections are the path; attention, norms and the MLP activation
-sit outside it): every layer reads the same seeded inputs X_h (attention input, read by q, k,
+sit outside it here, and decoder.py runs them around the same kernels and pool): every layer
+reads the same seeded inputs X_h (attention input, read by q, k,
 v, gate, up), X_o (attention output, read by o) and X_d (MLP intermediate, read by down); W, A
 and B are distinct per layer. Upstream gradients: q, k, v and o always get their own seeded
 dY; the top layer's gate, up and down do too, but below it the backward is chained the way a
