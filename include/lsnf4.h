@@ -417,8 +417,8 @@ lsn_status attention_bwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, in
  * LSN_POOL_HOST_SIM runs the same state machine on host memory (memcpy, no GPU).
  * File tier (LSN_POOL_FILE_TIER; "Soup v0.73.0 benchmarks README", record index, the disk tier;
  * "An 8B Fine-Tune Now Fits in 4 GB of VRAM": the base stays in host RAM, or on NVMe when RAM is
- * short): layer_pool_create then also allocates two pinned bounce buffers of slot_bytes and
- * starts an I/O thread. Layers registered with layer_pool_register_file are read by that thread
+ * short): the caller then also hands layer_pool_create two pinned bounce buffers of slot_bytes,
+ * and the pool starts an I/O thread. Layers registered with layer_pool_register_file are read by that thread
  * (8 reader threads per image) into the bounce buffers, alternately, and copied from there on
  * the copy stream; prefetch() posts the read and returns, and acquire() blocks the calling
  * host thread until the layer's copy has been enqueued. An I/O failure is reported by the
@@ -447,18 +447,40 @@ typedef struct {
   uint64_t audit_failures;
 } lsn_pool_stats;
 
+/* Caller-owned memory the pool uses besides its slots (the pool allocates no device or pinned
+ * memory; it owns only its host-side state, its events and, with the file tier, its I/O thread):
+ *   audit_sums      LSN_POOL_AUDIT: an 8-byte aligned device array (host array under
+ *                   LSN_POOL_HOST_SIM) of audit_capacity checksums, not overlapping a slot;
+ *                   layer_pool_create and layer_pool_audit zero it; 2 checksums per layer
+ *                   visit are recorded between two layer_pool_audit calls, more: LSN_E_STATE.
+ *   bounce[0..1]    LSN_POOL_FILE_TIER: two non-overlapping buffers of slot_bytes each, in
+ *                   pinned host memory (hipHostMalloc; plain host memory under HOST_SIM).
+ * Unused fields may be NULL / 0; the whole struct may be NULL when neither flag is set. The
+ * memory must outlive the pool (until layer_pool_destroy returns). */
+typedef struct {
+  unsigned long long *audit_sums;
+  size_t audit_capacity;
+  void *bounce[2];
+} lsn_pool_buffers;
+
 /* slots: n_slots device pointers of slot_bytes each (caller-owned, 256-byte aligned);
- * copy_stream: the stream the copies run on (must differ from the compute streams). */
+ * n_layers: the layer indices the pool serves are 0 .. n_layers-1 (each registered once
+ * before its first prefetch); copy_stream: the stream the copies run on (must differ from the
+ * compute streams); bufs: see lsn_pool_buffers. LSN_E_ARG on a missing, misaligned, overlapping
+ * or (file tier) unpinned buffer. Synchronises (zeroing the checksum array). */
 lsn_status layer_pool_create(int32_t n_slots, size_t slot_bytes, void *const *slots,
                              int32_t n_layers, void *copy_stream, uint32_t flags,
-                             lsn_pool **out);
-/* host_image: pinned host memory (hipHostMalloc), bytes <= slot_bytes; not modified after. */
+                             const lsn_pool_buffers *bufs, lsn_pool **out);
+/* host_image: pinned host memory (hipHostMalloc), bytes <= slot_bytes; not modified after.
+ * Registering a layer again replaces its image: refused (LSN_E_STATE) while the layer is
+ * prefetched or acquired; a free slot still holding the old bytes is never reused for it. */
 lsn_status layer_pool_register(lsn_pool *pool, int32_t layer, const void *host_image,
                                size_t bytes);
 /* File tier only: the layer's image is `bytes` at `offset` of the file at `path` (opened
  * read-only and kept open until layer_pool_destroy; the file must not change meanwhile).
  * LSN_E_ARG if it cannot be opened or is too short; LSN_E_NOFIT if bytes > slot_bytes;
- * LSN_E_STATE on a pool without LSN_POOL_FILE_TIER or while the layer is in flight. */
+ * LSN_E_STATE on a pool without LSN_POOL_FILE_TIER or while the layer is in flight. On any
+ * error the layer keeps its previous registration. */
 lsn_status layer_pool_register_file(lsn_pool *pool, int32_t layer, const char *path,
                                     uint64_t offset, size_t bytes);
 lsn_status layer_pool_prefetch(lsn_pool *pool, int32_t layer);
@@ -469,8 +491,8 @@ lsn_status layer_pool_stats(const lsn_pool *pool, lsn_pool_stats *out);
 /* Synchronises; compares every recorded slot checksum with its layer's host checksum.
  * LSN_E_AUDIT (with the first mismatching layer and visit in the message) on any mismatch. */
 lsn_status layer_pool_audit(lsn_pool *pool);
-/* Finishes the posted reads, waits for in-flight copies, destroys events, frees the bounce
- * buffers and closes the files; never frees caller memory. */
+/* Finishes the posted reads, waits for in-flight copies, destroys events and closes the files;
+ * never frees caller memory (slots, checksum array, bounce buffers). */
 lsn_status layer_pool_destroy(lsn_pool *pool);
 
 #ifdef __cplusplus

@@ -72,7 +72,7 @@ class StackConfig:
 C1 = StackConfig("single-linear-896", layers=1, hidden=896, kv=896, inter=896, T=512, single=True,
                  pool_slots=1, head_dim=64)
 C2 = StackConfig("qwen2.5-0.5b-shape", layers=24, hidden=896, kv=128, inter=4864, T=2048, head_dim=64)
-C3 = StackConfig("llama-3.1-8b-shape", layers=32, hidden=4096, kv=1024, inter=14336, T=4096)
+C3 = StackConfig("llama-3.1-8b-shape", layers=32, hidden=4096, kv=1024, inter=14336, T=4096, seq_len=2048)
 C4 = StackConfig("qwen2.5-3b-shape-bf16", layers=36, hidden=2048, kv=256, inter=11008, T=2048,
                  base="bf16")
 C5 = StackConfig("qwen2.5-72b-shape", layers=80, hidden=8192, kv=1024, inter=29568, T=2048)

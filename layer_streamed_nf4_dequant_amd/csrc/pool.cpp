@@ -14,6 +14,10 @@
 // Two backends share the state machine: HIP (device slots, hipMemcpyAsync on the copy stream,
 // hipEvents) and HOST_SIM (host slots, memcpy, no events) for tests without a GPU.
 //
+// Memory: the slots, the audit's checksum array and the file tier's two pinned bounce buffers
+// are the caller's (lsn_pool_buffers); the pool owns only its host state, its events and the
+// I/O thread, and allocates no device or pinned memory.
+//
 // File tier (LSN_POOL_FILE_TIER; "Soup v0.73.0 benchmarks README", record index: the disk tier,
 // and "An 8B Fine-Tune Now Fits in 4 GB of VRAM": the frozen base stays in host RAM, or on NVMe
 // when RAM is short): a layer registered from a file is read by the pool's I/O thread, split
@@ -88,8 +92,6 @@ struct AuditRecord {
   int at_release;           // 0 = taken at acquire, 1 = at release
 };
 
-constexpr size_t kAuditCapacity = 16384;
-
 }  // namespace
 
 struct lsn_pool {
@@ -104,12 +106,12 @@ struct lsn_pool {
   lsn_pool_stats stats{};
   uint64_t tick = 0;
   // audit
-  unsigned long long *d_sums = nullptr;      // device checksums, one per record
-  std::vector<uint64_t> h_sums;              // host-sim checksums
+  unsigned long long *sums = nullptr;        // caller's checksum array (device; host under HOST_SIM)
+  size_t audit_capacity = 0;
   std::vector<AuditRecord> records;
   // file tier
   bool file_tier = false;
-  void *bounce[2] = {nullptr, nullptr};      // pinned (host-sim: plain) read buffers
+  void *bounce[2] = {nullptr, nullptr};      // caller's pinned (host-sim: plain) read buffers
   hipEvent_t bounce_free[2] = {nullptr, nullptr};
   bool bounce_used[2] = {false, false};
   int next_bounce = 0;
@@ -146,18 +148,25 @@ int find_slot(const lsn_pool *p, int layer, SlotState st) {
   return -1;
 }
 
+// A layer registered anew: a free slot still holding its old bytes must not serve it again
+// (KEEP_AT_TURN reuse would skip the copy).
+void forget_copies(lsn_pool *p, int layer) {
+  for (Slot &s : p->slots)
+    if (s.layer == layer && s.state == FREE) s.valid = false;
+}
+
 lsn_status record_checksum(lsn_pool *p, const void *mem, size_t bytes, int layer, int at_release,
                            hipStream_t s) {
-  if (p->records.size() >= kAuditCapacity)
+  if (p->records.size() >= p->audit_capacity)
     return fail(LSN_E_STATE, "audit capacity (%zu checksums) exhausted: call layer_pool_audit",
-                kAuditCapacity);
+                p->audit_capacity);
   const size_t idx = p->records.size();
   p->records.push_back({layer, p->layers[layer].visits, at_release});
   if (p->sim) {
-    p->h_sums[idx] = checksum_host(mem, bytes);
+    p->sums[idx] = checksum_host(mem, bytes);
     return LSN_OK;
   }
-  return check_hip(launch_checksum(mem, bytes, p->d_sums + idx, s), "audit checksum launch");
+  return check_hip(launch_checksum(mem, bytes, p->sums + idx, s), "audit checksum launch");
 }
 
 lsn_status do_prefetch(lsn_pool *p, int layer) {
@@ -292,12 +301,27 @@ void io_loop(lsn_pool *p) {
   }
 }
 
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+bool is_pinned_host(const void *ptr) {
+  hipPointerAttribute_t attr;
+  const hipError_t e = hipPointerGetAttributes(&attr, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return attr.type == hipMemoryTypeHost;
+}
+
 }  // namespace
 
 extern "C" {
 
 lsn_status layer_pool_create(int32_t n_slots, size_t slot_bytes, void *const *slots, int32_t n_layers,
-                             void *copy_stream, uint32_t flags, lsn_pool **out) {
+                             void *copy_stream, uint32_t flags, const lsn_pool_buffers *bufs, lsn_pool **out) {
   if (!out) return fail(LSN_E_ARG, "layer_pool_create: null out");
   *out = nullptr;
   if (n_slots < 1 || n_layers < 1 || slot_bytes == 0 || !slots)
@@ -306,17 +330,36 @@ lsn_status layer_pool_create(int32_t n_slots, size_t slot_bytes, void *const *sl
   for (int i = 0; i < n_slots; ++i) {
     if (!slots[i] || ((uintptr_t)slots[i] & 255))
       return fail(LSN_E_ARG, "layer_pool_create: slot %d is null or not 256-byte aligned", i);
-    for (int j = 0; j < i; ++j) {
-      const uintptr_t a = (uintptr_t)slots[i], b = (uintptr_t)slots[j];
-      if (a < b + slot_bytes && b < a + slot_bytes)
+    for (int j = 0; j < i; ++j)
+      if (overlaps(slots[i], slot_bytes, slots[j], slot_bytes))
         return fail(LSN_E_ARG, "layer_pool_create: slots %d and %d overlap", j, i);
-    }
   }
   const bool sim = (flags & LSN_POOL_HOST_SIM) != 0;
+  const bool audit = (flags & LSN_POOL_AUDIT) != 0, file_tier = (flags & LSN_POOL_FILE_TIER) != 0;
   if (!sim) {
     lsn_status st = require_gfx950();
     if (st != LSN_OK) return st;
     if (!copy_stream) return fail(LSN_E_ARG, "layer_pool_create: the copy stream must be a created stream");
+  }
+  if ((audit || file_tier) && !bufs)
+    return fail(LSN_E_ARG, "layer_pool_create: LSN_POOL_AUDIT and LSN_POOL_FILE_TIER need the caller's buffers");
+  if (audit) {
+    if (!bufs->audit_sums || bufs->audit_capacity < 1 || ((uintptr_t)bufs->audit_sums & 7))
+      return fail(LSN_E_ARG, "layer_pool_create: LSN_POOL_AUDIT needs an 8-byte aligned checksum array "
+                  "of audit_capacity >= 1 entries");
+    for (int i = 0; i < n_slots; ++i)
+      if (overlaps(bufs->audit_sums, bufs->audit_capacity * 8, slots[i], slot_bytes))
+        return fail(LSN_E_ARG, "layer_pool_create: the checksum array overlaps slot %d", i);
+  }
+  if (file_tier) {
+    for (int b = 0; b < 2; ++b) {
+      if (!bufs->bounce[b])
+        return fail(LSN_E_ARG, "layer_pool_create: LSN_POOL_FILE_TIER needs two bounce buffers of slot_bytes");
+      if (!sim && !is_pinned_host(bufs->bounce[b]))
+        return fail(LSN_E_ARG, "layer_pool_create: bounce buffer %d is not pinned host memory", b);
+    }
+    if (overlaps(bufs->bounce[0], slot_bytes, bufs->bounce[1], slot_bytes))
+      return fail(LSN_E_ARG, "layer_pool_create: the two bounce buffers overlap");
   }
   lsn_pool *p = new lsn_pool();
   p->file_tier = (flags & LSN_POOL_FILE_TIER) != 0;
@@ -329,31 +372,25 @@ lsn_status layer_pool_create(int32_t n_slots, size_t slot_bytes, void *const *sl
   p->slots.resize(n_slots);
   p->layers.resize(n_layers);
   for (int i = 0; i < n_slots; ++i) p->slots[i].mem = slots[i];
+  if (audit) {
+    p->sums = bufs->audit_sums;
+    p->audit_capacity = bufs->audit_capacity;
+  }
+  if (file_tier) p->bounce[0] = bufs->bounce[0], p->bounce[1] = bufs->bounce[1];
   hipError_t e = hipSuccess;
   if (!sim) {
     for (int i = 0; i < n_slots && e == hipSuccess; ++i) {
       e = hipEventCreateWithFlags(&p->slots[i].ready, hipEventDisableTiming);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&p->slots[i].released, hipEventDisableTiming);
     }
-    if (e == hipSuccess && audit_on(p)) {
-      e = hipMalloc(&p->d_sums, kAuditCapacity * sizeof(unsigned long long));
-      if (e == hipSuccess) e = hipMemset(p->d_sums, 0, kAuditCapacity * sizeof(unsigned long long));
-    }
-  } else if (audit_on(p)) {
-    p->h_sums.assign(kAuditCapacity, 0);
+    // the checksums are added into with integer atomics: they start at zero
+    if (e == hipSuccess && audit) e = hipMemset(p->sums, 0, p->audit_capacity * sizeof(unsigned long long));
+    for (int b = 0; b < 2 && e == hipSuccess && file_tier; ++b)
+      e = hipEventCreateWithFlags(&p->bounce_free[b], hipEventDisableTiming);
+  } else if (audit) {
+    std::memset(p->sums, 0, p->audit_capacity * sizeof(unsigned long long));
   }
-  if (e == hipSuccess && p->file_tier) {
-    for (int b = 0; b < 2 && e == hipSuccess; ++b) {
-      if (sim) {
-        p->bounce[b] = std::malloc(slot_bytes);
-        if (!p->bounce[b]) e = hipErrorOutOfMemory;
-      } else {
-        e = hipHostMalloc(&p->bounce[b], slot_bytes, hipHostMallocDefault);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&p->bounce_free[b], hipEventDisableTiming);
-      }
-    }
-    if (e == hipSuccess) p->io = std::thread(io_loop, p);
-  }
+  if (e == hipSuccess && file_tier) p->io = std::thread(io_loop, p);
   if (e != hipSuccess) {
     lsn_status st = check_hip(e, "layer_pool_create");
     layer_pool_destroy(p);
@@ -381,6 +418,9 @@ lsn_status layer_pool_register(lsn_pool *p, int32_t layer, const void *host_imag
       return fail(LSN_E_ARG, "layer_pool_register: layer %d image is not pinned host memory", layer);
     }
   }
+  if (find_slot(p, layer, PENDING) >= 0 || find_slot(p, layer, ACQUIRED) >= 0)
+    return fail(LSN_E_STATE, "layer_pool_register: layer %d is in flight", layer);
+  forget_copies(p, layer);
   LayerInfo &L = p->layers[layer];
   if (L.fd >= 0) {
     close(L.fd);
@@ -414,6 +454,17 @@ lsn_status layer_pool_register_file(lsn_pool *p, int32_t layer, const char *path
     return fail(LSN_E_ARG, "layer_pool_register_file: %s holds %lld B, the image needs %llu B at offset %llu",
                 path, (long long)end, (unsigned long long)bytes, (unsigned long long)offset);
   }
+  uint64_t checksum = 0;
+  if (audit_on(p)) {
+    std::vector<uint64_t> tmp(bytes / 8);
+    std::string err;
+    if (!read_parallel(fd, offset, bytes, tmp.data(), err)) {
+      close(fd);                             // the layer keeps its previous registration
+      return fail(LSN_E_ARG, "layer_pool_register_file: reading %s: %s", path, err.c_str());
+    }
+    checksum = checksum_host(tmp.data(), bytes);
+  }
+  forget_copies(p, layer);
   LayerInfo &L = p->layers[layer];
   if (L.fd >= 0) close(L.fd);
   L.host = nullptr;
@@ -421,14 +472,7 @@ lsn_status layer_pool_register_file(lsn_pool *p, int32_t layer, const char *path
   L.file_off = offset;
   L.bytes = bytes;
   L.visits = 0;
-  L.checksum = 0;
-  if (audit_on(p)) {
-    std::vector<uint64_t> tmp(bytes / 8);
-    std::string err;
-    if (!read_parallel(fd, offset, bytes, tmp.data(), err))
-      return fail(LSN_E_ARG, "layer_pool_register_file: reading %s: %s", path, err.c_str());
-    L.checksum = checksum_host(tmp.data(), bytes);
-  }
+  L.checksum = checksum;
   return LSN_OK;
 }
 
@@ -525,11 +569,12 @@ lsn_status layer_pool_audit(lsn_pool *p) {
   const size_t n = p->records.size();
   std::vector<uint64_t> sums(n);
   if (p->sim) {
-    for (size_t i = 0; i < n; ++i) sums[i] = p->h_sums[i];
+    for (size_t i = 0; i < n; ++i) sums[i] = p->sums[i];
+    std::memset(p->sums, 0, n * 8);
   } else if (n > 0) {
     hipError_t e = hipDeviceSynchronize();
-    if (e == hipSuccess) e = hipMemcpy(sums.data(), p->d_sums, n * 8, hipMemcpyDeviceToHost);
-    if (e == hipSuccess) e = hipMemset(p->d_sums, 0, n * 8);
+    if (e == hipSuccess) e = hipMemcpy(sums.data(), p->sums, n * 8, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemset(p->sums, 0, n * 8);
     if (e != hipSuccess) return check_hip(e, "layer_pool_audit");
   }
   uint64_t failures = 0;
@@ -571,13 +616,8 @@ lsn_status layer_pool_destroy(lsn_pool *p) {
       if (s.ready) (void)hipEventDestroy(s.ready);
       if (s.released) (void)hipEventDestroy(s.released);
     }
-    if (p->d_sums) (void)hipFree(p->d_sums);
-    for (int b = 0; b < 2; ++b) {
-      if (p->bounce[b]) (void)hipHostFree(p->bounce[b]);
+    for (int b = 0; b < 2; ++b)
       if (p->bounce_free[b]) (void)hipEventDestroy(p->bounce_free[b]);
-    }
-  } else {
-    for (int b = 0; b < 2; ++b) std::free(p->bounce[b]);
   }
   delete p;
   return check_hip(e, "layer_pool_destroy");

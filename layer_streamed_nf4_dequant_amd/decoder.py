@@ -26,7 +26,7 @@ import numpy as np
 
 from . import inputs, lib
 from .configs import StackConfig
-from .stack import layer_layout
+from .stack import layer_layout, make_pool
 
 EPS = 1e-5
 THETA = 500000.0
@@ -38,7 +38,10 @@ class DecoderModel:
 
     def __init__(self, cfg: StackConfig, vocab: int, layers: int | None = None, seed: int = 0,
                  modes=("streamed",), dequant: str = "staged", eps: float = EPS, theta: float = THETA,
-                 ce_chunk: int = 2048):
+                 ce_chunk: int = 2048, label_rows: int | None = None):
+        """label_rows: keep the next-token label on only this many rows (a seeded sample of the
+        rows that have one) and ignore the rest, so that the loss, and the gradient flowing back
+        from it, come from a sample of positions."""
         import torch
         self.torch = torch
         self.cfg, self.V, self.seed = cfg, vocab, seed
@@ -105,8 +108,14 @@ class DecoderModel:
         self.ids = ids
         lab = torch.roll(ids, -1)
         lab[cfg.seq_len - 1::cfg.seq_len] = -1
+        if label_rows is not None:
+            order = torch.randperm(T, generator=inputs.device_generator(seed, *key0, "label rows"), device=dev)
+            has = order[lab[order] >= 0][:label_rows]
+            keep = torch.zeros(T, dtype=torch.bool, device=dev)
+            keep[has] = True
+            lab = torch.where(keep, lab, torch.full_like(lab, -1))
         self.labels = lab.contiguous()
-        self.n_counted = T - self.n_seq
+        self.n_counted = int((self.labels >= 0).sum())
         self.positions = (torch.arange(T, device=dev, dtype=torch.int32) % cfg.seq_len).contiguous()
 
         # ---- activations and gradients ----
@@ -140,8 +149,7 @@ class DecoderModel:
         self.pool, self.slots = None, None
         if "streamed" in modes:
             self.slots = [torch.empty(self.image_bytes, dtype=torch.uint8, device=dev) for _ in range(cfg.pool_slots)]
-            self.pool = lib.LayerPool([t.data_ptr() for t in self.slots], self.image_bytes, self.L,
-                                      self.copy_stream.cuda_stream, 0)
+            self.pool = make_pool(self.slots, self.image_bytes, self.L, self.copy_stream, 0)
             for l in range(self.L):
                 self.pool.register(l, self.host_images[l].data_ptr(), self.image_bytes)
         torch.cuda.synchronize()

@@ -74,6 +74,12 @@ class PoolStats(ctypes.Structure):
 _lib = None
 
 
+class PoolBuffers(ctypes.Structure):
+    """lsn_pool_buffers: the caller's checksum array (audit) and pinned bounce buffers (file tier)."""
+    _fields_ = [("audit_sums", ctypes.c_void_p), ("audit_capacity", ctypes.c_size_t),
+                ("bounce", ctypes.c_void_p * 2)]
+
+
 def load():
     """Load liblsnf4.so once and declare its signatures. Raises if it is not built."""
     global _lib
@@ -112,7 +118,7 @@ def load():
                                         ctypes.POINTER(vp), vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32,
                                         vp, sz, vp]),
         "layer_pool_create": (i32, [i32, sz, ctypes.POINTER(vp), i32, vp, ctypes.c_uint32,
-                                    ctypes.POINTER(vp)]),
+                                    ctypes.POINTER(PoolBuffers), ctypes.POINTER(vp)]),
         "layer_pool_register": (i32, [vp, i32, vp, sz]),
         "layer_pool_register_file": (i32, [vp, i32, ctypes.c_char_p, ctypes.c_uint64, sz]),
         "layer_pool_prefetch": (i32, [vp, i32]),
@@ -318,14 +324,21 @@ def lora_linear_bwd_group(descs, X, dY_list, U_list, dX, dA_list, dB_list, dx_mo
 
 
 class LayerPool:
-    """Owner of an lsn_pool handle. Slots are caller memory (torch tensors or host buffers)."""
+    """Owner of an lsn_pool handle. Slots, the audit's checksum array and the file tier's bounce
+    buffers are caller memory (torch tensors or host buffers), passed as addresses: audit_sums =
+    (address, capacity in checksums), bounce = (address, address)."""
 
     def __init__(self, slot_ptrs, slot_bytes: int, n_layers: int, copy_stream_handle: int | None,
-                 flags: int = 0):
+                 flags: int = 0, audit_sums: tuple[int, int] | None = None, bounce: tuple[int, int] | None = None):
         arr = (ctypes.c_void_p * len(slot_ptrs))(*slot_ptrs)
+        bufs = PoolBuffers()
+        if audit_sums is not None:
+            bufs.audit_sums, bufs.audit_capacity = audit_sums
+        if bounce is not None:
+            bufs.bounce[0], bufs.bounce[1] = bounce
         h = ctypes.c_void_p()
         check(load().layer_pool_create(len(slot_ptrs), slot_bytes, arr, n_layers, copy_stream_handle,
-                                       flags, ctypes.byref(h)))
+                                       flags, ctypes.byref(bufs), ctypes.byref(h)))
         self.h = h
         self.flags = flags
 

@@ -80,6 +80,28 @@ def layer_layout(cfg: StackConfig) -> tuple[list[ProjLayout], int]:
 
 
 MIB2 = 2 << 20
+AUDIT_CAPACITY = 16384          # pool checksums between two audits (2 per layer visit)
+
+
+def make_pool(slots, slot_bytes: int, n_layers: int, copy_stream, flags: int):
+    """A layer pool over the given device slots, with the caller-owned memory its flags need
+    allocated here: the audit's checksum array (device, LSN_POOL_AUDIT) and the file tier's two
+    pinned bounce buffers (LSN_POOL_FILE_TIER). The tensors stay referenced by the returned
+    pool object for its lifetime."""
+    import torch
+    keep, audit, bounce = [], None, None
+    if flags & lib.POOL_AUDIT:
+        sums = torch.zeros(AUDIT_CAPACITY, dtype=torch.int64, device="cuda")
+        keep.append(sums)
+        audit = (sums.data_ptr(), AUDIT_CAPACITY)
+    if flags & lib.POOL_FILE_TIER:
+        bufs = [torch.empty(slot_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        keep += bufs
+        bounce = (bufs[0].data_ptr(), bufs[1].data_ptr())
+    pool = lib.LayerPool([t.data_ptr() for t in slots], slot_bytes, n_layers, copy_stream.cuda_stream, flags,
+                         audit_sums=audit, bounce=bounce)
+    pool.memory = keep
+    return pool
 
 
 def workspace_bytes(cfg: StackConfig) -> int:
@@ -323,8 +345,7 @@ class Stack:
             flags |= lib.POOL_FILE_TIER
         elif source != "ram":
             raise ValueError(source)
-        self.pool = lib.LayerPool([t.data_ptr() for t in self.slots], self.image_bytes, self.L,
-                                  self.copy_stream.cuda_stream, flags)
+        self.pool = make_pool(self.slots, self.image_bytes, self.L, self.copy_stream, flags)
         for l in range(self.L):
             if source == "file":
                 self.pool.register_file(l, path, l * self.image_bytes, self.image_bytes)
@@ -441,7 +462,7 @@ class Stack:
             self.checks[(tag, l, j)] = (v.to(torch.int64) * self._wvec[:n]).sum()
 
     def step(self, mode: str = "streamed", gemm_events=None, dequant_events=None, wait: bool = True,
-             reference: bool = False, micro_batches: int = 1):
+             reference: bool = False, micro_batches: int = 1, on_visit=None):
         """One training step of the projection stack; returns its time in ms (compute stream).
         gemm_events: optional list; (projections, start, end) HIP events around every forward
         GEMM launch (one per group of projections sharing an input) are appended to it.
@@ -451,15 +472,20 @@ class Stack:
         step's first layer copies can be queued while this step's last visits still run.
         reference=True first runs the frozen reference model's forward: one more streamed sweep
         over every layer with the adapters off, into Yref ("An 8B Fine-Tune Now Fits in 4 GB of
-        VRAM": for DPO-style objectives the streamed base with the adapters switched off is the
-        reference model, at the cost of more layer reads per step; here 3 per layer instead of 2).
+        VRAM", the DPO paragraph: preference objectives take their frozen reference model from
+        the same streamed base run without its adapters, so no second copy of the weights is
+        needed, only more layer reads per step; here 3 per layer instead of 2).
         It changes no training state: the step's outputs and gradients are those of a step
         without it.
         micro_batches=k: gradient accumulation ("Exact Layer Streaming", Abstract: accumulation is
         per-token I/O-neutral): k forward/backward passes, each streaming every layer twice, the
         first setting dA, dB and the others adding into them (a step then trains on k x T
         tokens). The stack's inputs are the same for every micro-batch, so after k = 2 each
-        gradient is exactly twice the single pass's (x + x is exact in fp32)."""
+        gradient is exactly twice the single pass's (x + x is exact in fp32).
+        on_visit: optional callable(visit, l), visit "fwd" or "bwd", called once the layer's work
+        of that visit is queued on the compute stream (and is the current stream), before the
+        layer is released: work it queues sees that visit's outputs (Y after "fwd"; Yre, dX_h
+        and the layer's dX_o / dX_d after "bwd") before the next layer overwrites them."""
         torch = self.torch
         s = self.compute
         sh = s.cuda_stream
@@ -492,6 +518,8 @@ class Stack:
                     self._forward_layer(base, l, self.Y, s, gemm_events)
                     if self.record:
                         self._record("fwd", l, self.Y)
+                    if on_visit is not None:
+                        on_visit("fwd", l)
                     if mode == "streamed":
                         self.pool.release(l, sh)
                 # ---- backward: layers L-1 .. 0, each re-read and recomputed ----
@@ -505,6 +533,8 @@ class Stack:
                     if self.record:
                         self._record("re", l, self.Yre)
                         self._record("dx", l, [self.dX_h, self.dX_o_pp[l % 2], self.dX_d_pp[l % 2]])
+                    if on_visit is not None:
+                        on_visit("bwd", l)
                     if mode == "streamed":
                         self.pool.release(l, sh)
             end.record(s)

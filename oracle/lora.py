@@ -14,9 +14,9 @@ the standard LoRA linear with rank r, scale s = alpha / r, no bias and no dropou
     dB = s dY^T U                                    ->  dB [N,r]
     dA = s G^T X                                     ->  dA [r,K]
 
-"Each layer is read twice per step, once going forward and once when the backward pass
-recomputes it" (same transcript, @7:32): the recomputed forward is the same function on
-the same bytes, so the oracle has no separate recompute.
+The same transcript (@7:32) has every layer fetched on two occasions in a step: for the
+forward and again when the backward recomputes that layer's forward. The recompute applies
+the same function to the same bytes, so the oracle has no separate recompute.
 
 All inputs are the exact values of bf16 (or fp32) tensors, widened to fp64; products use
 numpy's fp64 matmul as a library primitive.  Results are fp64, unrounded.

@@ -77,7 +77,11 @@ def oracle_step(m: DecoderModel):
         saved.append((x, n1, q, k, v, o, h, n2, gate, up, mm))
         x = y
     nf = r16(og.rmsnorm(x, gf, eps))
-    loss, _, dh = oce.cross_entropy(nf, hb(m.W_head), labels, 1.0 / m.n_counted)
+    # an ignored row has no loss and no gradient: the head runs on the counted rows alone
+    counted = labels >= 0
+    loss, dh = np.zeros(nf.shape[0]), np.zeros_like(nf)
+    loss[counted], _, dh[counted] = oce.cross_entropy(nf[counted], hb(m.W_head), labels[counted],
+                                                      1.0 / m.n_counted)
     dy = og.rmsnorm_bwd(x, gf, r16(dh), eps)
     grads = {}
     for l in reversed(range(L)):
@@ -105,6 +109,37 @@ def test_decoder_step_matches_oracle_chain(gpu):
     print("case: tiny decoder (2 layers, H 256, 4/2 heads of 64, 2 x 96 rows, V 512) vs oracle", flush=True)
     m = DecoderModel(TINY, vocab=512, modes=("resident",))
     m.step("resident")
+    loss_gpu = hb(m.loss)
+    grads_gpu = {(l, n, w): hb((m.dA if w == "A" else m.dB)[l][m.j[n]]) for l in range(m.L) for n in m.names
+                 for w in "AB"}
+    loss_ref, grads_ref = oracle_step(m)
+    counted = m.labels.cpu().numpy() >= 0
+    e_loss = olora.rel_l2(loss_gpu[counted], loss_ref[counted])
+    assert e_loss <= 1e-3, f"loss rel L2 {e_loss:.2e}"
+    assert np.all(loss_gpu[~counted] == 0.0)
+    worst = 0.0
+    for key, ref in grads_ref.items():
+        e = olora.rel_l2(grads_gpu[key], ref)
+        worst = max(worst, e)
+        assert e <= 1e-2, f"{key}: rel L2 {e:.2e}"
+    print(f"loss rel L2 {e_loss:.2e}, worst gradient rel L2 {worst:.2e}")
+    m.close()
+
+
+QWEN2 = StackConfig("qwen2.5-0.5b-shape", layers=2, hidden=896, kv=128, inter=4864, T=2048, head_dim=64,
+                    seq_len=1024)
+
+
+@pytest.mark.timeout(600)
+def test_decoder_step_matches_oracle_chain_qwen_width(gpu):
+    """The same chain at the Qwen2.5-0.5B width (hidden 896, 14 query and 2 key/value heads of 64,
+    MLP 4864, 2 x 1024-row sequences, vocabulary 151936) with two layers; the loss is taken on a
+    seeded sample of 96 rows (the rest ignored), so the oracle's LM head runs on those rows only."""
+    print("case: Qwen2.5-0.5B-width decoder (2 layers, H 896, 14/2 heads of 64, 2 x 1024 rows, "
+          "V 151936, 96 labelled rows) vs oracle", flush=True)
+    m = DecoderModel(QWEN2, vocab=151936, modes=("streamed",), label_rows=96)
+    assert m.n_counted == 96
+    m.step("streamed")
     loss_gpu = hb(m.loss)
     grads_gpu = {(l, n, w): hb((m.dA if w == "A" else m.dB)[l][m.j[n]]) for l in range(m.L) for n in m.names
                  for w in "AB"}

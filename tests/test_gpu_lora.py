@@ -338,10 +338,16 @@ def test_argument_validation(gpu):
 
 
 @pytest.mark.parametrize("label,T,K,N", [("8B gate", 4096, 4096, 14336), ("8B down", 4096, 14336, 4096),
-                                         ("72B k", 2048, 8192, 1024)])
+                                         ("72B q/o", 2048, 8192, 8192), ("72B k/v", 2048, 8192, 1024),
+                                         ("72B gate/up", 2048, 8192, 29568), ("72B down", 2048, 29568, 8192)])
 def test_full_size_sampled_parity(gpu, label, T, K, N):
-    """Full-size projections in the launch configuration the stack uses, checked on sampled
-    rows (Y, dX depend only on their own row) and sampled columns of dA, dB (full T)."""
+    """Full-size projections (every distinct shape of the 8B and 72B layers) in the launch
+    configuration the stack uses, against the oracle: Y and dX on sampled rows (a row of each
+    depends only on the same row of X or dY), dA and dB on sampled columns over all T rows. The
+    oracle's references come from olora.forward / olora.backward called on the sampled slices:
+    a row slice of X and dY gives those rows of Y and dX; a column slice of dY and B (with the
+    matching rows of W) leaves U = X A^T whole and gives those columns of dB; a column slice of
+    X, A and W leaves G = dY B whole and gives those columns of dA."""
     import torch
     print(f"case: {label} T={T} K={K} N={N}", flush=True)
     c = Case(T, K, N, tag="full")
@@ -356,23 +362,17 @@ def test_full_size_sampled_parity(gpu, label, T, K, N):
     assert _eq(dX, dX_w)
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(T, 48, replace=False))
-    from oracle import nf4 as onf4
-    Xr = onf4.bf16_to_f32(c.X[rows])
-    Wh = onf4.bf16_to_f32(c.W_hat_bits)
-    A, B = onf4.bf16_to_f32(c.A), onf4.bf16_to_f32(c.B)
-    Yo, _ = olora.forward(Xr, Wh, A, B, c.s)
-    assert_close("Y", to_np(Y)[rows], Yo)
-    dYr = onf4.bf16_to_f32(c.dY[rows])
-    dXo = dYr.astype(np.float64) @ Wh.astype(np.float64) + c.s * ((dYr.astype(np.float64) @ B) @ A)
-    assert_close("dX", to_np(dX)[rows], dXo)
-    assert_close("dX", to_np(dX_nn)[rows], dXo)
     cols_n = np.sort(rng.choice(N, 64, replace=False))
     cols_k = np.sort(rng.choice(K, 64, replace=False))
-    X = onf4.bf16_to_f32(c.X).astype(np.float64)
-    dY = onf4.bf16_to_f32(c.dY).astype(np.float64)
-    U_o = X @ A.T.astype(np.float64)
-    G_o = dY @ B.astype(np.float64)
-    dBo = c.s * (dY[:, cols_n].T @ U_o)
-    dAo = c.s * (G_o.T @ X[:, cols_k])
+    X, dY = onf4_f32(c.X), onf4_f32(c.dY)
+    Wh = onf4_f32(c.W_hat_bits)
+    A, B = onf4_f32(c.A), onf4_f32(c.B)
+    Yo, _ = olora.forward(X[rows], Wh, A, B, c.s)
+    assert_close("Y", to_np(Y)[rows], Yo)
+    dXo, _, _, _ = olora.backward(X[rows], dY[rows], Wh, A, B, c.s)
+    assert_close("dX", to_np(dX)[rows], dXo)
+    assert_close("dX", to_np(dX_nn)[rows], dXo)
+    _, _, dBo, _ = olora.backward(X, dY[:, cols_n], Wh[cols_n], A, B[cols_n], c.s)
     assert_close("dB", to_np(dB)[cols_n], dBo)
+    _, dAo, _, _ = olora.backward(X[:, cols_k], dY, Wh[:, cols_k], A[:, cols_k], B, c.s)
     assert_close("dA", to_np(dA)[:, cols_k], dAo)

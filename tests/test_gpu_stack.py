@@ -2,7 +2,8 @@
 of the same numerics, forward outputs and every LoRA gradient tensor checked separately
 ("Exact Layer Streaming", Abstract; Soup v0.73.0 benchmarks README, reading conventions), with
 same-process controls: planted pool defects must break the backward while the forward stays
-exact, and the aliasing audit must flag them.  Plus oracle parity on sampled layers.
+exact, and the aliasing audit must flag them. The stack's parity with the oracle is in
+test_gpu_stack_oracle.py.
 """
 
 import numpy as np
@@ -192,76 +193,4 @@ def test_streamed_equals_resident_full_stack(gpu, name):
     assert recompute_matches_forward(got[0], cfg.layers, 7)
     stats = st.pool.stats()
     assert stats["copies"] == 2 * cfg.layers and stats["misses"] == 0
-    st.close()
-
-
-def _oracle_stack(cfg, st, rows):
-    """Oracle forward (sampled rows) and backward of every projection of every layer, on the
-    stack's own inputs, with the same layer-to-layer chaining of upstream gradients (the
-    oracle's own dX_o / dX_d of layer l+1, rounded to bf16 at the same boundary)."""
-    import torch
-    from oracle import lora as olora
-    from oracle import nf4 as onf4
-    f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731  (bf16 values, exact)
-    to_bf16 = lambda a: onf4.bf16_to_f32(onf4.bf16_rne(a.astype(np.float32))).astype(np.float64)  # noqa: E731
-    L = st.L
-    out = {}
-    above = None                      # (dX_o, dX_d) of layer l+1 as bf16 values
-    for l in reversed(range(L)):
-        layer = {}
-        for j, p in enumerate(st.layout):
-            W = inputs.device_normal((p.N, p.K), inputs.STD["W"], st.seed, cfg.name, l, p.name, "W").cpu().numpy()
-            if cfg.base == "nf4":
-                Wh = onf4.bf16_to_f32(onf4.dequant_bf16(onf4.pack(W)))
-            else:
-                Wh = torch.from_numpy(W).to(torch.bfloat16).float().numpy()
-            X = f(st.X[PROJ_INPUT[p.name]])
-            if above is not None and p.name == "down":
-                dY = above[0]
-            elif above is not None and p.name in ("gate", "up"):
-                dY = above[1]
-            else:
-                dY = f(st.dY[j])
-            A, B = f(st.A[l][j]), f(st.B[l][j])
-            Y, _ = olora.forward(X[rows], Wh, A, B, cfg.scale)
-            dX, dA, dB, _ = olora.backward(X, dY, Wh, A, B, cfg.scale)
-            layer[p.name] = (Y, dX, dA, dB)
-        out[l] = layer
-        above = (to_bf16(layer["o"][1]), to_bf16(layer["down"][1]))
-    return out
-
-
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,layers", [("C2", 3), ("C4", 2)])
-def test_stack_matches_oracle_on_sampled_layers(gpu, name, layers):
-    """After one streamed step: layer L-1's forward outputs, layer 0's recomputed outputs and
-    input gradients, and every layer's dA, dB against the oracle on the same inputs."""
-    import torch
-    from oracle import lora as olora
-    cfg = configs.CONFIGS[name]
-    print(f"case: {cfg.name} first {layers} layers vs oracle", flush=True)
-    st = Stack(cfg, modes=("streamed",), layers=layers)
-    st.step("streamed")
-    torch.cuda.synchronize()
-    rows = np.arange(0, cfg.T, 7)
-    o = _oracle_stack(cfg, st, rows)
-    L = layers
-    dx_h = np.zeros((cfg.T, cfg.hidden))
-    errs = []
-    for j, p in enumerate(st.layout):
-        errs.append(olora.rel_l2(st.Y[j].float().cpu().numpy()[rows], o[L - 1][p.name][0]))
-        assert errs[-1] <= 5e-3, ("Y", p.name)
-        errs.append(olora.rel_l2(st.Yre[j].float().cpu().numpy()[rows], o[0][p.name][0]))
-        assert errs[-1] <= 5e-3, ("Yre", p.name)
-        for l in range(L):
-            errs.append(olora.rel_l2(st.dA[l][j].cpu().numpy(), o[l][p.name][2]))
-            assert errs[-1] <= 1e-2, ("dA", l, p.name)
-            errs.append(olora.rel_l2(st.dB[l][j].cpu().numpy(), o[l][p.name][3]))
-            assert errs[-1] <= 1e-2, ("dB", l, p.name)
-        if PROJ_INPUT[p.name] == "h":
-            dx_h += o[0][p.name][1]
-    assert olora.rel_l2(st.dX_h.cpu().numpy(), dx_h) <= 5e-3
-    assert olora.rel_l2(st.dX_o_pp[0].float().cpu().numpy(), o[0]["o"][1]) <= 5e-3
-    assert olora.rel_l2(st.dX_d_pp[0].float().cpu().numpy(), o[0]["down"][1]) <= 5e-3
-    print(f"max rel L2 over {len(errs)} tensors: {max(errs):.2e}")
     st.close()

@@ -77,3 +77,27 @@ def test_swiglu_special_values_and_backward():
     dg, du = glue.swiglu_bwd(g, uu, dm)
     np.testing.assert_allclose(dg, _fd(lambda z: (glue.swiglu(z, uu) * dm).sum(), g), rtol=1e-6, atol=1e-9)
     np.testing.assert_allclose(du, _fd(lambda z: (glue.swiglu(g, z) * dm).sum(), uu), rtol=1e-6, atol=1e-9)
+
+
+def test_rope_pair_frequencies_closed_form():
+    """The frequency of pair i is theta^(-2i/d). With theta = 10^4 and d = 8 the four pairs turn at
+    1, 1/10, 1/100 and 1/1000 radians per position, so pair i at position 10^i is rotated by exactly
+    one radian: a unit vector on the pair's first coordinate comes out as (cos 1, sin 1). A
+    frequency of theta^(-i/d), or a pairing of neighbours (2i, 2i+1), fails this."""
+    d, nh, theta = 8, 1, 10000.0
+    h = d // 2
+    for i in range(h):
+        x = np.zeros((1, d))
+        x[0, i] = 1.0
+        y = glue.rope(x, np.array([10 ** i]), nh, d, theta)[0]
+        want = np.zeros(d)
+        want[i], want[i + h] = np.cos(1.0), np.sin(1.0)
+        np.testing.assert_allclose(y, want, rtol=0, atol=1e-12)
+    # a second route to the angle: theta^(-2i/d) as exp(-(2i/d) ln theta), read back with atan2
+    for d, theta in ((128, 500000.0), (64, 1000000.0)):
+        for i in (d // 4, d // 2 - 1):
+            x = np.zeros((1, d))
+            x[0, i] = 1.0
+            y = glue.rope(x, np.array([1]), 1, d, theta)[0]
+            got = np.arctan2(y[i + d // 2], y[i])
+            assert abs(got - np.exp(-(2.0 * i / d) * np.log(theta))) < 1e-15

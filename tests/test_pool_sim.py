@@ -19,6 +19,22 @@ def aligned(n):
     return raw[off:off + n]
 
 
+def sim_pool(slots, n_layers, flags, keep):
+    """A host-simulated pool over the given slots, with the caller-owned memory its flags need
+    (a checksum array for the audit, two bounce buffers for the file tier) appended to keep."""
+    audit = bounce = None
+    if flags & lib.POOL_AUDIT:
+        sums = np.zeros(1024, dtype=np.uint64)
+        keep.append(sums)
+        audit = (sums.ctypes.data, sums.size)
+    if flags & lib.POOL_FILE_TIER:
+        b = [aligned(SLOT), aligned(SLOT)]
+        keep += b
+        bounce = (b[0].ctypes.data, b[1].ctypes.data)
+    return lib.LayerPool([s.ctypes.data for s in slots], SLOT, n_layers, None, flags | lib.POOL_HOST_SIM,
+                         audit_sums=audit, bounce=bounce)
+
+
 class SimPool:
     def __init__(self, n_slots=2, n_layers=4, flags=0, sizes=None):
         self.slots = [aligned(SLOT) for _ in range(n_slots)]
@@ -27,8 +43,8 @@ class SimPool:
         for l in range(n_layers):
             n = SLOT if sizes is None else sizes[l]
             self.images.append(rng.integers(0, 255, n, dtype=np.uint8))
-        self.pool = lib.LayerPool([s.ctypes.data for s in self.slots], SLOT, n_layers, None,
-                                  flags | lib.POOL_HOST_SIM)
+        self.keep = []
+        self.pool = sim_pool(self.slots, n_layers, flags, self.keep)
         for l, img in enumerate(self.images):
             self.pool.register(l, img.ctypes.data, img.size)
 
@@ -172,8 +188,8 @@ class FilePool(SimPool):
         for off, img in zip(self.offsets, self.images):
             blob[off:off + SLOT] = img
         blob.tofile(self.path)
-        self.pool = lib.LayerPool([s.ctypes.data for s in self.slots], SLOT, n_layers, None,
-                                  flags | lib.POOL_HOST_SIM | lib.POOL_FILE_TIER)
+        self.keep = []
+        self.pool = sim_pool(self.slots, n_layers, flags | lib.POOL_FILE_TIER, self.keep)
         for l, off in enumerate(self.offsets):
             self.pool.register_file(l, self.path, off, SLOT)
 
@@ -244,4 +260,78 @@ def test_file_tier_read_error_is_reported_by_acquire(tmp_path):
     with pytest.raises(lib.LsnError) as e:
         p.pool.acquire(1, None)
     assert e.value.status == lib.LSN_E_HIP and "end of file" in str(e.value)
+    p.pool.close()
+
+
+def test_create_needs_the_callers_audit_and_bounce_memory():
+    slots = [aligned(SLOT)]
+    for flags in (lib.POOL_AUDIT, lib.POOL_FILE_TIER):
+        with pytest.raises(lib.LsnError) as e:           # flag set, no buffers
+            lib.LayerPool([slots[0].ctypes.data], SLOT, 1, None, flags | lib.POOL_HOST_SIM)
+        assert e.value.status == lib.LSN_E_ARG
+    with pytest.raises(lib.LsnError):                    # checksum array inside a slot
+        lib.LayerPool([slots[0].ctypes.data], SLOT, 1, None, lib.POOL_AUDIT | lib.POOL_HOST_SIM,
+                      audit_sums=(slots[0].ctypes.data + 256, 8))
+    with pytest.raises(lib.LsnError):                    # zero capacity
+        sums = np.zeros(8, dtype=np.uint64)
+        lib.LayerPool([slots[0].ctypes.data], SLOT, 1, None, lib.POOL_AUDIT | lib.POOL_HOST_SIM,
+                      audit_sums=(sums.ctypes.data, 0))
+    b = aligned(2 * SLOT)
+    with pytest.raises(lib.LsnError):                    # the bounce buffers overlap
+        lib.LayerPool([slots[0].ctypes.data], SLOT, 1, None, lib.POOL_FILE_TIER | lib.POOL_HOST_SIM,
+                      bounce=(b.ctypes.data, b.ctypes.data + SLOT // 2))
+
+
+def test_audit_capacity_is_the_callers():
+    """Two checksums per visit: a capacity of 3 holds one visit, and the second visit's release
+    overflows it (LSN_E_STATE) until the audit empties it."""
+    slots = [aligned(SLOT), aligned(SLOT)]
+    keep = []
+    sums = np.zeros(3, dtype=np.uint64)
+    pool = lib.LayerPool([s.ctypes.data for s in slots], SLOT, 2, None, lib.POOL_AUDIT | lib.POOL_HOST_SIM,
+                         audit_sums=(sums.ctypes.data, 3))
+    img = [np.full(SLOT, l + 1, dtype=np.uint8) for l in range(2)]
+    keep += img
+    for l in range(2):
+        pool.register(l, img[l].ctypes.data, SLOT)
+    pool.acquire(0, None)
+    pool.release(0, None)
+    pool.acquire(1, None)
+    with pytest.raises(lib.LsnError) as e:
+        pool.release(1, None)
+    assert e.value.status == lib.LSN_E_STATE and "capacity" in str(e.value)
+    pool.audit()
+    assert np.all(sums == 0)                              # the audit zeroes what it read
+    pool.close()
+
+
+def test_register_again_replaces_the_image_and_refuses_while_in_flight():
+    """A layer registered anew must not be served from a free slot that still holds its old bytes
+    (KEEP_AT_TURN would otherwise reuse them without a copy); while the layer is prefetched or
+    acquired, registering it again is refused."""
+    p = SimPool(n_slots=2, n_layers=2, flags=lib.POOL_KEEP_AT_TURN)
+    np.testing.assert_array_equal(p.visit(0), p.images[0])
+    copies = p.pool.stats()["copies"]
+    new = np.random.default_rng(9).integers(0, 255, SLOT, dtype=np.uint8)
+    p.keep.append(new)
+    p.pool.register(0, new.ctypes.data, SLOT)
+    np.testing.assert_array_equal(p.visit(0), new)
+    assert p.pool.stats()["copies"] == copies + 1         # a fresh copy, not a reuse
+    p.pool.prefetch(1)
+    with pytest.raises(lib.LsnError) as e:
+        p.pool.register(1, new.ctypes.data, SLOT)
+    assert e.value.status == lib.LSN_E_STATE
+    p.pool.acquire(1, None)
+    with pytest.raises(lib.LsnError) as e:
+        p.pool.register(1, new.ctypes.data, SLOT)
+    assert e.value.status == lib.LSN_E_STATE
+    p.pool.release(1, None)
+    np.testing.assert_array_equal(p.visit(1), p.images[1])
+
+
+def test_file_tier_register_again_replaces_the_image(tmp_path):
+    p = FilePool(tmp_path, n_slots=2, n_layers=2, flags=lib.POOL_KEEP_AT_TURN)
+    np.testing.assert_array_equal(p.visit(0), p.images[0])
+    p.pool.register_file(0, p.path, p.offsets[1], SLOT)   # layer 0 now names layer 1's bytes
+    np.testing.assert_array_equal(p.visit(0), p.images[1])
     p.pool.close()
