@@ -232,6 +232,23 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
                            const uint16_t *U, void *dX, int32_t dx_mode, float *dA, float *dB,
                            int32_t grad_mode, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * lora_linear_bwd_noalloc - lora_linear_bwd without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, modes, kernels and results (bit-identical to
+ * lora_linear_bwd) as above; the workspace is the library's own static device array of
+ * lora_linear_bwd_noalloc_max_ws_bytes() bytes (32 MiB), one per GPU, created with the
+ * library's code object on each device it runs on and held until the process ends. Shapes whose
+ * lora_linear_ws_bytes exceeds it give LSN_E_ARG. Calls no allocator. Every call on a GPU uses
+ * that GPU's one array: calls that overlap in time on one GPU (on different streams, or from
+ * different threads) race on it; calls in one stream order are safe. Async on `stream`.
+ */
+lsn_status lora_linear_bwd_noalloc(const lsn_lora_linear *L, const uint16_t *X, const uint16_t *dY,
+                                   const uint16_t *U, void *dX, int32_t dx_mode, float *dA, float *dB,
+                                   int32_t grad_mode, void *stream);
+/* The size of lora_linear_bwd_noalloc's static workspace, in bytes. */
+size_t lora_linear_bwd_noalloc_max_ws_bytes(void);
+
 /* Device workspace bytes lora_linear_bwd_group needs for these n linears. */
 size_t lora_linear_group_ws_bytes(int32_t n, const lsn_lora_linear *L);
 

@@ -9,6 +9,7 @@
 //                                                            (bf16 store or fp32 add)
 //           dB = s sum_t dY^T U ; dA = s sum_t G^T X         k_tn_partial + k_tn_reduce
 
+#include <mutex>
 #include <utility>
 
 #include "common.h"
@@ -308,23 +309,29 @@ lsn_status lora_linear_fwd_group(int32_t n, const lsn_lora_linear *L, int32_t ad
   return launch_gemm_direct(d, EPI_BF16, s);
 }
 
-lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const uint16_t *dY, const uint16_t *U,
-                           void *dX, int32_t dx_mode, float *dA, float *dB, int32_t grad_mode, void *ws,
-                           size_t ws_bytes, void *stream) {
-  lsn_status st = check_linear(L, "lora_linear_bwd");
+}  // extern "C"
+
+namespace {
+
+// The backward of one linear on the workspace `ws` (ws_bytes long); `what` names the entry point
+// in error messages.
+lsn_status bwd_impl(const char *what, const lsn_lora_linear *L, const uint16_t *X, const uint16_t *dY,
+                    const uint16_t *U, void *dX, int32_t dx_mode, float *dA, float *dB, int32_t grad_mode,
+                    void *ws, size_t ws_bytes, void *stream) {
+  lsn_status st = check_linear(L, what);
   if (st != LSN_OK) return st;
   const int64_t T = L->T, K = L->K, N = L->N, r = L->r;
   if (!X || !dY || !U || !dX || !dA || !dB || !ws)
-    return fail(LSN_E_ARG, "lora_linear_bwd: null pointer argument");
+    return fail(LSN_E_ARG, "%s: null pointer argument", what);
   if (!aligned16(X) || !aligned16(dY) || !aligned16(U) || !aligned16(dX) || ((uintptr_t)ws & 255))
-    return fail(LSN_E_ARG, "lora_linear_bwd: X, dY, U, dX must be 16-byte and ws 256-byte aligned");
+    return fail(LSN_E_ARG, "%s: X, dY, U, dX must be 16-byte and ws 256-byte aligned", what);
   if (dx_mode != LSN_DX_BF16_SET && dx_mode != LSN_DX_F32_ADD && dx_mode != LSN_DX_F32_SET)
-    return fail(LSN_E_ARG, "lora_linear_bwd: unknown dX mode %d", dx_mode);
+    return fail(LSN_E_ARG, "%s: unknown dX mode %d", what, dx_mode);
   if (grad_mode != LSN_GRAD_SET && grad_mode != LSN_GRAD_ADD)
-    return fail(LSN_E_ARG, "lora_linear_bwd: unknown gradient mode %d", grad_mode);
+    return fail(LSN_E_ARG, "%s: unknown gradient mode %d", what, grad_mode);
   const BwdWs need = bwd_layout(ws, T, K, N, r);
   if (ws_bytes < need.bytes)
-    return fail(LSN_E_ARG, "lora_linear_bwd: workspace too small (%zu < %zu)", ws_bytes, need.bytes);
+    return fail(LSN_E_ARG, "%s: workspace too small (%zu < %zu)", what, ws_bytes, need.bytes);
   const size_t dxb = (size_t)(T * K * (dx_mode == LSN_DX_BF16_SET ? 2 : 4));
   const void *outs[] = {dX, dA, dB, ws};
   const size_t outb[] = {dxb, (size_t)(r * K * 4), (size_t)(N * r * 4), need.bytes};
@@ -335,10 +342,10 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
   for (int o = 0; o < 4; ++o) {
     for (int i = 0; i < n_in; ++i)
       if (ranges_overlap(outs[o], outb[o], ins[i], inb[i]))
-        return fail(LSN_E_ARG, "lora_linear_bwd: an output overlaps an input");
+        return fail(LSN_E_ARG, "%s: an output overlaps an input", what);
     for (int p = 0; p < o; ++p)
       if (ranges_overlap(outs[o], outb[o], outs[p], outb[p]))
-        return fail(LSN_E_ARG, "lora_linear_bwd: two outputs overlap");
+        return fail(LSN_E_ARG, "%s: two outputs overlap", what);
   }
   if ((st = require_gfx950()) != LSN_OK) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -409,6 +416,75 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
   rj.job[0] = TnRedJob{need.part_dB, N, (int)r, L->scale, acc, 0, dB, 0};
   rj.job[1] = TnRedJob{need.part_dA, K, (int)r, L->scale, acc, 1, dA, 0};
   return launch_tn_reduce_jobs(nc, rj, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const uint16_t *dY, const uint16_t *U,
+                           void *dX, int32_t dx_mode, float *dA, float *dB, int32_t grad_mode, void *ws,
+                           size_t ws_bytes, void *stream) {
+  return bwd_impl("lora_linear_bwd", L, X, dY, U, dX, dx_mode, dA, dB, grad_mode, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- the backward without a caller workspace, for callers that cannot allocate ----
+// One file-scope device array per GPU (created with the library's code object on each device
+// it runs on, held until the process ends). In host code `scratch` names a host-side stand-in,
+// not device memory: its device address is looked up once per device with
+// hipGetSymbolAddress (that device current) and only that address is handed to kernels.
+static constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's address of `scratch`
+lsn_status scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return check_hip(e, "lora_linear_bwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LSN_E_ARG, "lora_linear_bwd_noalloc: device %d outside the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return check_hip(e, "lora_linear_bwd_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LSN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lora_linear_bwd_noalloc_max_ws_bytes(void) { return kNoAllocScratchBytes; }
+
+lsn_status lora_linear_bwd_noalloc(const lsn_lora_linear *L, const uint16_t *X, const uint16_t *dY,
+                                   const uint16_t *U, void *dX, int32_t dx_mode, float *dA, float *dB,
+                                   int32_t grad_mode, void *stream) {
+  lsn_status st = check_linear(L, "lora_linear_bwd_noalloc");
+  if (st != LSN_OK) return st;
+  const size_t need = bwd_layout(nullptr, L->T, L->K, L->N, L->r).bytes;
+  if (need > kNoAllocScratchBytes)
+    return fail(LSN_E_ARG, "lora_linear_bwd_noalloc: T=%lld K=%lld N=%lld r=%lld needs %zu B of workspace, more "
+                "than the library's static %zu B: use lora_linear_bwd with a caller workspace",
+                (long long)L->T, (long long)L->K, (long long)L->N, (long long)L->r, need, kNoAllocScratchBytes);
+  if ((st = require_gfx950()) != LSN_OK) return st;
+  void *ws = nullptr;
+  if ((st = scratch_address(&ws)) != LSN_OK) return st;
+  // every buffer the kernels use in the workspace (G, B^T, A^T, the partial sums) is written in
+  // full before it is read: nothing has to start at zero
+  return bwd_impl("lora_linear_bwd_noalloc", L, X, dY, U, dX, dx_mode, dA, dB, grad_mode, ws,
+                  kNoAllocScratchBytes, stream);
 }
 
 size_t lora_linear_group_ws_bytes(int32_t n, const lsn_lora_linear *L) {

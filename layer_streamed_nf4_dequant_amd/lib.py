@@ -32,6 +32,7 @@ EXPORTS = (
     "lsn_last_error", "lsn_abi_version", "lsn_nf4_codebook", "nf4_pack_ws_bytes", "nf4_pack",
     "nf4_dequant", "nf4_dequant_batch", "lora_down", "lora_linear_ws_bytes", "lora_linear_fwd", "lora_linear_fwd_group",
     "lora_linear_bwd", "lora_linear_group_ws_bytes", "lora_linear_bwd_group",
+    "lora_linear_bwd_noalloc", "lora_linear_bwd_noalloc_max_ws_bytes",
     "layer_pool_create", "layer_pool_register", "layer_pool_register_file", "layer_pool_prefetch", "layer_pool_acquire",
     "layer_pool_release", "layer_pool_stats", "layer_pool_audit", "layer_pool_destroy",
     "lm_head_ce_ws_bytes", "lm_head_ce", "embedding_gather",
@@ -113,6 +114,8 @@ def load():
                                         ctypes.POINTER(vp), vp, sz, vp]),
         "lora_linear_bwd": (i32, [ctypes.POINTER(LoraLinearDesc), vp, vp, vp, vp, i32, vp, vp, i32,
                                   vp, sz, vp]),
+        "lora_linear_bwd_noalloc": (i32, [ctypes.POINTER(LoraLinearDesc), vp, vp, vp, vp, i32, vp, vp, i32, vp]),
+        "lora_linear_bwd_noalloc_max_ws_bytes": (sz, []),
         "lora_linear_group_ws_bytes": (sz, [i32, ctypes.POINTER(LoraLinearDesc)]),
         "lora_linear_bwd_group": (i32, [i32, ctypes.POINTER(LoraLinearDesc), vp, ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32,
@@ -303,6 +306,17 @@ def lora_linear_bwd(desc: LoraLinearDesc, X, dY, U, dX, dA, dB, dx_mode: int = D
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     check(load().lora_linear_bwd(ctypes.byref(desc), _ptr(X), _ptr(dY), _ptr(U), _ptr(dX), dx_mode,
                                  _ptr(dA), _ptr(dB), grad_mode, _ptr(ws), nbytes, _stream_handle(stream)))
+
+
+def lora_linear_bwd_noalloc(desc: LoraLinearDesc, X, dY, U, dX, dA, dB, dx_mode: int = DX_BF16_SET,
+                            grad_mode: int = GRAD_SET, stream=None) -> None:
+    """lora_linear_bwd on the library's static per-GPU workspace (no workspace argument)."""
+    check(load().lora_linear_bwd_noalloc(ctypes.byref(desc), _ptr(X), _ptr(dY), _ptr(U), _ptr(dX), dx_mode,
+                                         _ptr(dA), _ptr(dB), grad_mode, _stream_handle(stream)))
+
+
+def noalloc_max_ws_bytes() -> int:
+    return int(load().lora_linear_bwd_noalloc_max_ws_bytes())
 
 
 def group_ws_bytes(descs) -> int:
