@@ -155,11 +155,13 @@ def lm_head_figure(cfg, vocab: int = 128256, chunk: int = 2048, iters: int = 5):
 
 def hipblaslt_ceiling(cfg, iters: int = 10):
     """Same-session reference: torch.matmul (hipBLASLt) bf16 X W^T at the stack's projection shapes
-    and T, TFLOP/s per shape (no LoRA term)."""
+    and T, TFLOP/s per (K, N) (no LoRA term): the forward shapes and the input-gradient shapes
+    (dY [T][N] times W: a product of shape (N, K))."""
     import torch
     res = {}
     seen = set()
-    for name, K, N in cfg.projections():
+    shapes = [(n, K, N) for n, K, N in cfg.projections()] + [(f"d{n}", N, K) for n, K, N in cfg.projections()]
+    for name, K, N in shapes:
         if (K, N) in seen:
             continue
         seen.add((K, N))
@@ -180,11 +182,13 @@ def hipblaslt_ceiling(cfg, iters: int = 10):
     return res
 
 
-def cpu_baseline(cfg, seed: int = 0, rows: int = 32):
-    """Oracle (numpy, fp64 LoRA + fp32 NF4) on one layer of the workload with `rows` token rows:
-    dequant of all 7 projections twice (forward and backward visit) plus forward, recomputed
-    forward and backward on the sampled rows. Scaled to the workload as
-    T / (L * (t_dequant + (T / rows) * t_rows))."""
+def cpu_baseline(cfg, seed: int = 0, rows: int | None = 32, layers: int = 1, n_max: int | None = None):
+    """Oracle (numpy, fp64 LoRA + fp32 NF4) on `layers` layers of the workload: the NF4 dequant of
+    all 7 projections twice (forward and backward visit; none for a bf16 base) plus forward,
+    recomputed forward and backward on `rows` token rows (None: all T). With n_max, each
+    projection is cut to its first n_max output rows and its times are scaled by N / n_max.
+    Derived tokens/s = T / ((L / layers) * (t_dequant + (T / rows) * t_rows)); a full step when
+    layers = L, rows = None and n_max = None."""
     import numpy as np
     from layer_streamed_nf4_dequant_amd import inputs
     from oracle import lora as olora
@@ -192,27 +196,37 @@ def cpu_baseline(cfg, seed: int = 0, rows: int = 32):
 
     cores = len(os.sched_getaffinity(0))
     rng = np.random.default_rng(seed)
+    n_rows = cfg.T if rows is None else rows
     t_deq = 0.0
     t_rows = 0.0
-    for name, K, N in cfg.projections():
-        W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
-        p = onf4.pack(W)
-        del W
-        t0 = time.perf_counter()
-        Wh = onf4.bf16_to_f32(onf4.dequant_bf16(p))          # forward visit
-        Wh = onf4.bf16_to_f32(onf4.dequant_bf16(p))          # backward visit (re-dequantised)
-        t_deq += time.perf_counter() - t0
-        A = onf4.bf16_to_f32(inputs.to_bf16_bits(rng.uniform(-K ** -0.5, K ** -0.5, (cfg.r, K)).astype(np.float32)))
-        B = onf4.bf16_to_f32(inputs.to_bf16_bits((rng.standard_normal((N, cfg.r)) * 0.01).astype(np.float32)))
-        X = onf4.bf16_to_f32(inputs.to_bf16_bits(rng.standard_normal((rows, K), dtype=np.float32)))
-        dY = onf4.bf16_to_f32(inputs.to_bf16_bits(rng.standard_normal((rows, N), dtype=np.float32)))
-        t0 = time.perf_counter()
-        olora.forward(X, Wh, A, B, cfg.scale)                # forward
-        olora.forward(X, Wh, A, B, cfg.scale)                # recomputed forward
-        olora.backward(X, dY, Wh, A, B, cfg.scale)           # backward
-        t_rows += time.perf_counter() - t0
-        del Wh
-    per_layer_full_T = t_deq + (cfg.T / rows) * t_rows
+    deq_bytes = 0.0
+    for _ in range(layers):
+        for name, K, N in cfg.projections():
+            Ns = N if n_max is None else min(N, n_max)
+            scale = N / Ns
+            W = rng.standard_normal((Ns, K), dtype=np.float32) * np.float32(0.02)
+            if cfg.base == "nf4":
+                p = onf4.pack(W)
+                del W
+                t0 = time.perf_counter()
+                Wh = onf4.bf16_to_f32(onf4.dequant_bf16(p))          # forward visit
+                Wh = onf4.bf16_to_f32(onf4.dequant_bf16(p))          # backward visit (re-dequantised)
+                t_deq += (time.perf_counter() - t0) * scale
+                deq_bytes += 2 * (K * N * 0.5 + K * N / 64 + 4 * K * N / 16384 + 2 * K * N)
+            else:
+                Wh = onf4.bf16_to_f32(onf4.bf16_rne(W))              # the bf16 base as stored
+                del W
+            A = onf4.bf16_to_f32(inputs.to_bf16_bits(rng.uniform(-K ** -0.5, K ** -0.5, (cfg.r, K)).astype(np.float32)))
+            B = onf4.bf16_to_f32(inputs.to_bf16_bits((rng.standard_normal((Ns, cfg.r)) * 0.01).astype(np.float32)))
+            X = onf4.bf16_to_f32(inputs.to_bf16_bits(rng.standard_normal((n_rows, K), dtype=np.float32)))
+            dY = onf4.bf16_to_f32(inputs.to_bf16_bits(rng.standard_normal((n_rows, Ns), dtype=np.float32)))
+            t0 = time.perf_counter()
+            olora.forward(X, Wh, A, B, cfg.scale)                # forward
+            olora.forward(X, Wh, A, B, cfg.scale)                # recomputed forward
+            olora.backward(X, dY, Wh, A, B, cfg.scale)           # backward
+            t_rows += (time.perf_counter() - t0) * scale
+            del Wh
+    per_layer_full_T = (t_deq + (cfg.T / n_rows) * t_rows) / layers
     tok_s = cfg.T / (cfg.layers * per_layer_full_T)
     cpu_model = None
     try:
@@ -220,13 +234,107 @@ def cpu_baseline(cfg, seed: int = 0, rows: int = 32):
             cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
     except OSError:
         pass
-    n_params = sum(K * N for _, K, N in cfg.projections())
-    deq_bytes = 2 * (cfg.nf4_bytes_per_layer() + 2 * n_params)
-    return {"value": round(tok_s, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "cpu_model": cpu_model, "dequant_GBs": round(deq_bytes / t_deq / 1e9, 3),
-            "sample": (f"1 of {cfg.layers} layers, {rows} of {cfg.T} token rows: NF4 dequant of all 7 "
-                       f"projections twice ({t_deq:.2f} s) + fp64 fwd/recompute/bwd on the sampled rows "
-                       f"({t_rows:.2f} s); derived tokens/s = T / (L * (t_dequant + T/rows * t_rows))")}
+    full = layers == cfg.layers and rows is None and n_max is None
+    sample = (f"{layers} of {cfg.layers} layers, {n_rows} of {cfg.T} token rows"
+              + (f", each projection cut to its first {n_max} output rows (times scaled by N / {n_max})" if n_max else "")
+              + (f": NF4 dequant of all {len(cfg.projections())} projections twice ({t_deq:.2f} s)" if cfg.base == "nf4"
+                 else ": no dequant (bf16 base)")
+              + f" + fp64 fwd/recompute/bwd on the sampled rows ({t_rows:.2f} s)"
+              + ("; a timed full step" if full else "; derived tokens/s = T / (L / layers * (t_dequant + T/rows * t_rows))"))
+    out = {"value": round(tok_s, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "cpu_model": cpu_model, "timed_full_step": full, "sample": sample}
+    if deq_bytes:
+        out["dequant_GBs"] = round(deq_bytes / t_deq / 1e9, 3)
+    return out
+
+
+def direct_io_dir():
+    """A directory whose file system accepts O_DIRECT reads: the temporary directory, else the
+    repository root (None if neither does)."""
+    import tempfile
+    for d in (tempfile.gettempdir(), ROOT):
+        path = None
+        try:
+            fd, path = tempfile.mkstemp(dir=d, prefix="lsnf4_direct_probe_")
+            os.write(fd, bytes(8192))
+            os.close(fd)
+            fd = os.open(path, os.O_RDONLY | os.O_DIRECT)
+            os.close(fd)
+            return d
+        except OSError:
+            continue
+        finally:
+            if path is not None and os.path.exists(path):
+                os.remove(path)
+    return None
+
+
+def fs_type(path) -> str | None:
+    """The mount's file system type and device for `path` (from /proc/mounts)."""
+    import tempfile
+    path = os.path.realpath(path or tempfile.gettempdir())
+    best = None
+    try:
+        with open("/proc/mounts") as f:
+            for ln in f:
+                dev, mnt, fs = ln.split()[:3]
+                if (path == mnt or path.startswith(mnt.rstrip("/") + "/")) and (best is None or len(mnt) > len(best[1])):
+                    best = (dev, mnt, fs)
+    except OSError:
+        return None
+    return None if best is None else f"{best[2]} on {best[0]} at {best[1]}"
+
+
+def timed_steps(stack, mode: str, steps: int) -> float:
+    """tokens/s of `steps` steps in `mode` after one untimed step (wall clock, synchronised)."""
+    import torch
+    stack.step(mode)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        stack.step(mode)
+    torch.cuda.synchronize()
+    return stack.cfg.T * steps / (time.perf_counter() - t0)
+
+
+# the CPU oracle's sample per configuration (kept to a few seconds each; see cpu_baseline)
+ORACLE_SAMPLE = {"C1": dict(rows=None, layers=1), "C2": dict(rows=None, layers=2),
+                 "C4": dict(rows=32, layers=1), "C5": dict(rows=32, layers=1, n_max=1024)}
+
+
+def config_figures(names=("C1", "C2", "C4", "C5"), steps: int = 3, cpu: bool = True):
+    """The other seeded configurations: tokens/s of the streamed, resident and no-H2D steps (same
+    kernels and pool as the headline), the streamed/resident ratio, and the CPU oracle on a
+    bounded sample of each."""
+    import torch
+    from layer_streamed_nf4_dequant_amd import configs
+    from layer_streamed_nf4_dequant_amd.stack import Stack
+    out = {}
+    for name in names:
+        cfg = configs.CONFIGS[name]
+        print(f"[bench] config {name} ({cfg.name}): {cfg.layers} layers, T={cfg.T}", flush=True)
+        modes = ("streamed", "resident", "no_h2d")
+        st = Stack(cfg, modes=modes)
+        res = {m: round(timed_steps(st, m, steps), 1) for m in modes}
+        st.close()
+        del st
+        torch.cuda.empty_cache()
+        fig = {"workload": cfg.name, "layers": cfg.layers, "tokens_per_step": cfg.T, "base": cfg.base,
+               "steps_timed": steps, "tokens_per_s": res,
+               "streamed_over_resident": round(res["streamed"] / res["resident"], 4),
+               "flops_per_step": cfg.flops_per_step(),
+               "streamed_tflops": round(cfg.flops_per_step() * res["streamed"] / cfg.T / 1e12, 1)}
+        if cpu:
+            fig["cpu_oracle"] = cpu_baseline(cfg, **ORACLE_SAMPLE[name])
+        print(f"[bench] config {name}: {fig['tokens_per_s']}", flush=True)
+        out[name] = fig
+    return out
+
+
+def _stats(values):
+    v = sorted(values)
+    return {"mean": round(sum(v) / len(v), 2), "median": round(v[len(v) // 2], 2),
+            "p90": round(v[min(len(v) - 1, int(0.9 * len(v)))], 2), "max": round(v[-1], 2)}
 
 
 def main():
@@ -240,6 +348,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-modes", action="store_true",
                     help="skip the resident and no-H2D comparison timings")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other seeded configurations (C1, C2, C4, C5)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, run one device-to-device copy of MIB MiB (a plain copy kernel of "
                          "known size, to scale hardware byte counters)")
@@ -279,7 +389,7 @@ def main():
     # the staging kernels are timed in a pass of their own below when that pass runs (their events
     # in the streamed pass would also count copy waits); the GEMM events stay in the timed steps
     dequant_separately = not args.no_other_modes and stack.slots is not None and stack.dequant != "fused"
-    gemm_events, dequant_events = [], ([] if not dequant_separately else None)
+    gemm_events, dequant_events = [], []
     torch.cuda.reset_peak_memory_stats()
     torch.cuda.synchronize()
     clocks_done = clock_sampler()
@@ -287,7 +397,6 @@ def main():
     step_ms = []
     for i in range(args.steps):
         step_ms.append(stack.step(args.mode, gemm_events=gemm_events, dequant_events=dequant_events))
-    dequant_events = dequant_events or []
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     peak_alloc = torch.cuda.max_memory_allocated()
@@ -298,12 +407,25 @@ def main():
 
     # dominant kernel: the fused forward GEMM launches of the timed steps
     dur_ms, flops = 0.0, 0
+    per_class = {}
     for js, e0, e1 in gemm_events:
-        dur_ms += e0.elapsed_time(e1)
+        ms = e0.elapsed_time(e1)
+        dur_ms += ms
+        f = 0
         for j in js:
             _, K, N = cfg.projections()[j]
-            flops += 2 * cfg.T * K * N + 2 * cfg.T * cfg.r * N
+            f += 2 * cfg.T * K * N + 2 * cfg.T * cfg.r * N
+        flops += f
+        name = "+".join(cfg.projections()[j][0] for j in js)
+        c = per_class.setdefault(name, {"us": [], "flops": f})
+        c["us"].append(ms * 1e3)
     n_launch = len(gemm_events)
+    launches = {}
+    for name, c in per_class.items():
+        st_ = _stats(c["us"])
+        st_["calls"] = len(c["us"])
+        st_["tflops_at_mean"] = round(c["flops"] / (st_["mean"] * 1e-6) / 1e12, 1)
+        launches[name] = st_
     achieved = flops / (dur_ms * 1e-3) / 1e12 if dur_ms > 0 else 0.0
     if cfg.base == "nf4" and stack.dequant == "fused":
         kernel = "k_gemm<NT,NF4> (fused NF4 dequant-into-LDS + bf16 MFMA + LoRA prologue)"
@@ -312,36 +434,29 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_from_profiles(),
                 "kernel": kernel, "launches": n_launch,
-                "avg_launch_us": round(dur_ms * 1e3 / max(n_launch, 1), 2)}
+                "avg_launch_us": round(dur_ms * 1e3 / max(n_launch, 1), 2),
+                "per_launch_us": launches,
+                "timed_in": f"{args.mode} timed steps (HIP events around every forward/recompute GEMM launch)"}
 
     # The staging events of the streamed pass start behind the compute stream's wait for the layer's
     # copy, and a HIP event takes its time stamp from the command before it, so in a copy-bound phase
-    # they would also count the wait. The staging kernels are therefore timed in a pass over layer
-    # images already in the pool slots (same kernels, same bytes, no copies), when that pass exists.
-    dequant_source = f"{args.mode} pass (events may include waits for layer copies)"
-    if dequant_separately:
-        stack.step("no_h2d")
-        dequant_events = []
-        for _ in range(max(2, args.steps // 2)):
-            stack.step("no_h2d", dequant_events=dequant_events)
-        torch.cuda.synchronize()
-        dequant_source = "no_h2d pass (layer images already in the pool slots; no copy waits)"
-    dequant = None
-    if dequant_events:
-        # algorithmic bytes per staged visit: read the NF4 image, write bf16 W (and bf16 W^T on the
-        # backward visit)
-        n_params = sum(K * N for _, K, N in cfg.projections())
-        nf4_b = cfg.nf4_bytes_per_layer()
-        d_ms, d_bytes = 0.0, 0
-        for (visit, with_t), e0, e1 in dequant_events:
-            d_ms += e0.elapsed_time(e1)
-            d_bytes += (2 if with_t else 1) * (nf4_b + 2 * n_params)
+    # they also count the wait. The headline dequant figure is therefore taken in a pass over layer
+    # images already in the pool slots (same kernels, same bytes, no copies), when that pass exists;
+    # the streamed step's own events are reported beside it.
+    n_params = sum(K * N for _, K, N in cfg.projections())
+    nf4_b = cfg.nf4_bytes_per_layer()
+
+    def dequant_figure(events):
+        """Algorithmic bytes per staged visit (read the NF4 image, write bf16 W; with staged_t the
+        backward visit also writes bf16 W^T) over the summed event durations, per visit kind too."""
+        if not events:
+            return None
+        d_ms = sum(e0.elapsed_time(e1) for _, e0, e1 in events)
+        d_bytes = sum((2 if with_t else 1) * (nf4_b + 2 * n_params) for (_, with_t), _, _ in events)
         gbs = d_bytes / (d_ms * 1e-3) / 1e9
-        # per visit kind: the row-major staging runs on every visit; with --dequant staged_t the
-        # backward visit adds the transposed one (its events then cover both launches)
         per_kernel = {}
         for visit in ("fwd", "bwd"):
-            ev = [(with_t, e0.elapsed_time(e1)) for (v, with_t), e0, e1 in dequant_events if v == visit]
+            ev = [(with_t, e0.elapsed_time(e1)) for (v, with_t), e0, e1 in events if v == visit]
             if not ev:
                 continue
             b = sum((2 if with_t else 1) * (nf4_b + 2 * n_params) for with_t, _ in ev)
@@ -349,11 +464,30 @@ def main():
             name = "k_dequant + k_dequant_t" if any(w for w, _ in ev) else "k_dequant"
             label = "forward" if visit == "fwd" else "backward"
             per_kernel[f"{name} ({label} visits)"] = {"achieved": round(g, 1), "frac": round(g / PEAK_HBM_GBS, 4)}
+        return {"achieved": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "visits": len(events),
+                "avg_visit_us": round(d_ms * 1e3 / len(events), 2), "by_visit": per_kernel}
+
+    in_step = dequant_figure(dequant_events)
+    head = in_step
+    dequant_source = f"{args.mode} timed steps (events may include waits for layer copies)"
+    if dequant_separately:
+        stack.step("no_h2d")
+        no_h2d_events = []
+        for _ in range(max(2, args.steps // 2)):
+            stack.step("no_h2d", dequant_events=no_h2d_events)
+        torch.cuda.synchronize()
+        head = dequant_figure(no_h2d_events)
+        dequant_source = "no_h2d pass (layer images already in the pool slots; no copy waits)"
+    dequant = None
+    if head is not None:
         kernels = ("k_dequant + k_dequant_t" if stack.dequant == "staged_t" else "k_dequant") + " (per-visit staging)"
-        dequant = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                   "frac": round(gbs / PEAK_HBM_GBS, 4), "kernels": kernels,
-                   "bytes_per_param": round(nf4_b / n_params + 2, 4), "visits": len(dequant_events),
-                   "by_visit": per_kernel, "timed_in": dequant_source}
+        dequant = {"bound": "hbm", "achieved": head["achieved"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": head["frac"], "kernels": kernels, "bytes_per_param": round(nf4_b / n_params + 2, 4),
+                   "visits": head["visits"], "avg_visit_us": head["avg_visit_us"], "by_visit": head["by_visit"],
+                   "timed_in": dequant_source}
+        if dequant_separately and in_step is not None:
+            dequant["in_timed_steps"] = dict(in_step, timed_in=f"{args.mode} timed steps (events may include "
+                                                                 "waits for layer copies)")
 
     other = {}
     if not args.no_other_modes:
@@ -408,18 +542,21 @@ def main():
             other["streamed_2_micro_batches"] = round(2 * cfg.T * n / (time.perf_counter() - t0), 1)
             print(f"[bench] streamed, 2 micro-batches per step: {other['streamed_2_micro_batches']} tokens/s",
                   flush=True)
-            # the layers streamed from one file through the pool's file tier (just written, so
-            # the reads come from the page cache)
-            stack.reset_pool(0, source="file")
-            stack.step("streamed")
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(n):
-                stack.step("streamed")
-            torch.cuda.synchronize()
-            other["streamed_from_file_page_cached"] = round(cfg.T * n / (time.perf_counter() - t0), 1)
-            print(f"[bench] streamed from a file: {other['streamed_from_file_page_cached']} tokens/s", flush=True)
-            stack.reset_pool(0)
+            # the layers streamed from one file through the pool's file tier: buffered reads (the
+            # file was just written, so they come from the page cache: a RAM-speed read), then
+            # O_DIRECT reads (past the page cache: the storage device's rate), where the file
+            # system allows them
+            stack.image_dir = direct_io_dir()
+            for key, direct in (("streamed_from_file_page_cached", False), ("streamed_from_file_direct", True)):
+                try:
+                    stack.reset_pool(0, source="file", direct=direct)
+                except lib.LsnError as e:
+                    other[key] = f"unavailable: {e}"
+                    continue
+                other[key] = round(timed_steps(stack, "streamed", n), 1)
+                print(f"[bench] {key}: {other[key]} tokens/s", flush=True)
+            other["file_tier_directory_fs"] = fs_type(stack.image_dir)
+            stack.reset_pool(0, source="ram")
         if stack.slots is not None:
             other["h2d_GBs"] = round(stack.h2d_rate(), 1)
         other["lm_head_ce"] = lm_head_figure(cfg)
@@ -467,12 +604,28 @@ def main():
     if clocks:
         context["gpu_clocks_during_timed_steps"] = clocks
     if not args.no_other_modes:
-        context["hipblaslt_bf16_tflops_same_shapes"] = hipblaslt_ceiling(cfg)
+        rates = hipblaslt_ceiling(cfg)
+        context["hipblaslt_bf16_tflops_same_shapes"] = rates
+        # the pages' protocol: the step against its same-session GEMM ceiling, i.e. the time the
+        # step's base GEMMs (forward, recompute and dX, no LoRA term) would take at hipBLASLt's
+        # rate for each shape, over the measured step time
+        by_shape = {tuple(int(x) for x in k.split(" ")[1].split("->")): v for k, v in rates.items()}
+        t_ceiling = cfg.layers * sum(2 * 2 * cfg.T * K * N / (by_shape[(K, N)] * 1e12) +
+                                     2 * cfg.T * K * N / (by_shape[(N, K)] * 1e12)
+                                     for _, K, N in cfg.projections())
+        context["step_fraction_of_gemm_ceiling"] = {
+            "value": round(t_ceiling / (wall / args.steps), 4), "ceiling_ms": round(t_ceiling * 1e3, 2),
+            "step_ms": round(wall * 1e3 / args.steps, 2),
+            "definition": "time of the step's base GEMMs at the same-session hipBLASLt rate per shape / step time"}
     out["context"] = context
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg)
     stack.close()
+    del stack
+    torch.cuda.empty_cache()
+    if not args.no_other_modes and not args.no_configs and args.config == "C3":
+        out["configs"] = config_figures(cpu=not args.no_cpu_baseline)
     print(json.dumps(out), flush=True)
 
 

@@ -440,7 +440,12 @@ lsn_status attention_bwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, in
  * the copy stream; prefetch() posts the read and returns, and acquire() blocks the calling
  * host thread until the layer's copy has been enqueued. An I/O failure is reported by the
  * acquire that needs it (LSN_E_HIP, with the reason). Planted faults and the audit behave as
- * for host images.
+ * for host images. With LSN_POOL_FILE_DIRECT as well, the tier reads with O_DIRECT, bypassing
+ * the page cache (each fill is a read of the storage device) into the caller's plain staging
+ * buffers (lsn_pool_buffers.direct_stage), which the readers copy on to the bounce buffers:
+ * slot_bytes and the staging buffers must be 4096-byte aligned, each image's offset too, and
+ * the file must hold the image's bytes rounded up to a whole 4096 (the padding is read and not
+ * copied to the slot).
  * ---------------------------------------------------------------------------------------- */
 typedef struct lsn_pool lsn_pool;
 
@@ -449,6 +454,7 @@ enum {
   LSN_POOL_KEEP_AT_TURN = 1u << 1,
   LSN_POOL_HOST_SIM = 1u << 2,
   LSN_POOL_FILE_TIER = 1u << 3,
+  LSN_POOL_FILE_DIRECT = 1u << 4,      /* file tier reads bypass the page cache (O_DIRECT) */
   LSN_FAULT_STALE_REFETCH = 1u << 8,   /* a layer's second visit skips its copy (stale slot) */
   LSN_FAULT_WRONG_SLOT = 1u << 9       /* a layer's second visit returns another slot */
 };
@@ -472,12 +478,17 @@ typedef struct {
  *                   visit are recorded between two layer_pool_audit calls, more: LSN_E_STATE.
  *   bounce[0..1]    LSN_POOL_FILE_TIER: two non-overlapping buffers of slot_bytes each, in
  *                   pinned host memory (hipHostMalloc; plain host memory under HOST_SIM).
+ *   direct_stage[0..1]  LSN_POOL_FILE_DIRECT: two non-overlapping buffers of slot_bytes each in
+ *                   plain (pageable) host memory, 4096-byte aligned: the O_DIRECT reads land
+ *                   there (direct I/O cannot target pinned driver memory) and are copied on to
+ *                   the bounce buffers by the reader threads.
  * Unused fields may be NULL / 0; the whole struct may be NULL when neither flag is set. The
  * memory must outlive the pool (until layer_pool_destroy returns). */
 typedef struct {
   unsigned long long *audit_sums;
   size_t audit_capacity;
   void *bounce[2];
+  void *direct_stage[2];
 } lsn_pool_buffers;
 
 /* slots: n_slots device pointers of slot_bytes each (caller-owned, 256-byte aligned);

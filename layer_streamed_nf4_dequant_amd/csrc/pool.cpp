@@ -26,6 +26,11 @@
 // crosses the link; a bounce buffer is reused only after its copy's event. prefetch() posts the
 // fill and returns; acquire() waits (on the host) until the I/O thread has enqueued that fill's
 // copy and recorded its ready event, then makes the compute stream wait for the event.
+// With LSN_POOL_FILE_DIRECT the reads bypass the page cache (O_DIRECT): every read is a read
+// of the storage device, in 4096-byte aligned pieces (the image's file region padded to whole
+// 4 KiB blocks), so the tier's rate is the disk's, not RAM's. Direct I/O cannot target the
+// driver's pinned host memory (the kernel refuses to map it for the transfer), so each reader
+// reads its piece into a plain host staging buffer and copies it into the pinned bounce buffer.
 
 #include <fcntl.h>
 #include <unistd.h>
@@ -73,6 +78,7 @@ struct LayerInfo {
   int fd = -1;              // file tier: the image is bytes at file_off of this file
   uint64_t file_off = 0;
   size_t bytes = 0;
+  size_t span = 0;          // file tier: bytes read per fill (bytes, or rounded up to 4 KiB with O_DIRECT)
   uint64_t checksum = 0;
   int visits = 0;           // prefetches so far (a layer's first visit is 1)
 };
@@ -85,6 +91,7 @@ struct FillJob {
 };
 
 constexpr int kReaders = 8;
+constexpr size_t kDirectAlign = 4096;       // O_DIRECT: offset, length and buffer alignment
 
 struct AuditRecord {
   int layer;
@@ -112,6 +119,7 @@ struct lsn_pool {
   // file tier
   bool file_tier = false;
   void *bounce[2] = {nullptr, nullptr};      // caller's pinned (host-sim: plain) read buffers
+  void *stage[2] = {nullptr, nullptr};       // caller's plain host buffers for O_DIRECT reads
   hipEvent_t bounce_free[2] = {nullptr, nullptr};
   bool bounce_used[2] = {false, false};
   int next_bounce = 0;
@@ -230,17 +238,21 @@ lsn_status do_prefetch(lsn_pool *p, int layer) {
   return LSN_OK;
 }
 
-// Reads bytes at off of fd into dst, split over kReaders threads; false (with errno text in
-// err) on a short or failed read.
-bool read_parallel(int fd, uint64_t off, size_t bytes, void *dst, std::string &err) {
+// Reads bytes at off of fd into dst, split over kReaders threads in pieces that are multiples of
+// `align` (for O_DIRECT); with `stage`, each piece is read into the same place of stage and then
+// copied to dst. False (with errno text in err) on a short or failed read.
+bool read_parallel(int fd, uint64_t off, size_t bytes, void *dst, std::string &err, size_t align = 1,
+                   void *stage = nullptr) {
   std::atomic<bool> ok{true};
   std::string first_err;
   std::mutex emu;
   auto part = [&](int k) {
-    const size_t chunk = (bytes + kReaders - 1) / kReaders;
+    const size_t chunk = ((bytes + kReaders - 1) / kReaders + align - 1) / align * align;
     size_t a = (size_t)k * chunk, b = a + chunk < bytes ? a + chunk : bytes;
+    char *into = static_cast<char *>(stage ? stage : dst);
+    const size_t a0 = a;
     while (a < b) {
-      const ssize_t n = pread(fd, static_cast<char *>(dst) + a, b - a, (off_t)(off + a));
+      const ssize_t n = pread(fd, into + a, b - a, (off_t)(off + a));
       if (n <= 0) {
         std::lock_guard<std::mutex> g(emu);
         if (first_err.empty()) first_err = n == 0 ? "unexpected end of file" : std::strerror(errno);
@@ -249,6 +261,7 @@ bool read_parallel(int fd, uint64_t off, size_t bytes, void *dst, std::string &e
       }
       a += (size_t)n;
     }
+    if (stage && b > a0) std::memcpy(static_cast<char *>(dst) + a0, into + a0, b - a0);
   };
   std::vector<std::thread> th;
   for (int k = 1; k < kReaders; ++k) th.emplace_back(part, k);
@@ -278,7 +291,10 @@ void io_loop(lsn_pool *p) {
       const int b = p->next_bounce;
       p->next_bounce ^= 1;
       if (!p->sim && p->bounce_used[b]) e = hipEventSynchronize(p->bounce_free[b]);
-      if (e == hipSuccess && !read_parallel(L.fd, L.file_off, L.bytes, p->bounce[b], err)) err = "read: " + err;
+      const bool direct = (p->flags & LSN_POOL_FILE_DIRECT) != 0;
+      if (e == hipSuccess && !read_parallel(L.fd, L.file_off, L.span, p->bounce[b], err, direct ? kDirectAlign : 1,
+                                            direct ? p->stage[b] : nullptr))
+        err = "read: " + err;
       if (err.empty() && e == hipSuccess) {
         if (p->sim) {
           std::memcpy(s.mem, p->bounce[b], L.bytes);
@@ -361,6 +377,15 @@ lsn_status layer_pool_create(int32_t n_slots, size_t slot_bytes, void *const *sl
     if (overlaps(bufs->bounce[0], slot_bytes, bufs->bounce[1], slot_bytes))
       return fail(LSN_E_ARG, "layer_pool_create: the two bounce buffers overlap");
   }
+  if (flags & LSN_POOL_FILE_DIRECT) {
+    if (!file_tier) return fail(LSN_E_ARG, "layer_pool_create: LSN_POOL_FILE_DIRECT needs LSN_POOL_FILE_TIER");
+    if (slot_bytes % kDirectAlign || !bufs->direct_stage[0] || !bufs->direct_stage[1] ||
+        ((uintptr_t)bufs->direct_stage[0] % kDirectAlign) || ((uintptr_t)bufs->direct_stage[1] % kDirectAlign))
+      return fail(LSN_E_ARG, "layer_pool_create: LSN_POOL_FILE_DIRECT needs slot_bytes a multiple of %zu and "
+                  "two staging buffers of slot_bytes aligned to it", kDirectAlign);
+    if (overlaps(bufs->direct_stage[0], slot_bytes, bufs->direct_stage[1], slot_bytes))
+      return fail(LSN_E_ARG, "layer_pool_create: the two staging buffers overlap");
+  }
   lsn_pool *p = new lsn_pool();
   p->file_tier = (flags & LSN_POOL_FILE_TIER) != 0;
   p->n_slots = n_slots;
@@ -377,6 +402,7 @@ lsn_status layer_pool_create(int32_t n_slots, size_t slot_bytes, void *const *sl
     p->audit_capacity = bufs->audit_capacity;
   }
   if (file_tier) p->bounce[0] = bufs->bounce[0], p->bounce[1] = bufs->bounce[1];
+  if (flags & LSN_POOL_FILE_DIRECT) p->stage[0] = bufs->direct_stage[0], p->stage[1] = bufs->direct_stage[1];
   hipError_t e = hipSuccess;
   if (!sim) {
     for (int i = 0; i < n_slots && e == hipSuccess; ++i) {
@@ -446,22 +472,34 @@ lsn_status layer_pool_register_file(lsn_pool *p, int32_t layer, const char *path
                 layer, bytes, p->slot_bytes);
   if (find_slot(p, layer, PENDING) >= 0 || find_slot(p, layer, ACQUIRED) >= 0)
     return fail(LSN_E_STATE, "layer_pool_register_file: layer %d is in flight", layer);
-  const int fd = open(path, O_RDONLY | O_CLOEXEC);
-  if (fd < 0) return fail(LSN_E_ARG, "layer_pool_register_file: cannot open %s: %s", path, std::strerror(errno));
+  const bool direct = (p->flags & LSN_POOL_FILE_DIRECT) != 0;
+  if (direct && offset % kDirectAlign)
+    return fail(LSN_E_ARG, "layer_pool_register_file: LSN_POOL_FILE_DIRECT needs the offset aligned to %zu",
+                kDirectAlign);
+  const size_t span = direct ? (bytes + kDirectAlign - 1) / kDirectAlign * kDirectAlign : bytes;
+  const int fd = open(path, O_RDONLY | O_CLOEXEC | (direct ? O_DIRECT : 0));
+  if (fd < 0)
+    return fail(LSN_E_ARG, "layer_pool_register_file: cannot open %s%s: %s", path, direct ? " with O_DIRECT" : "",
+                std::strerror(errno));
   const off_t end = lseek(fd, 0, SEEK_END);
-  if (end < 0 || (uint64_t)end < offset + bytes) {
+  if (end < 0 || (uint64_t)end < offset + span) {
     close(fd);
     return fail(LSN_E_ARG, "layer_pool_register_file: %s holds %lld B, the image needs %llu B at offset %llu",
-                path, (long long)end, (unsigned long long)bytes, (unsigned long long)offset);
+                path, (long long)end, (unsigned long long)span, (unsigned long long)offset);
   }
   uint64_t checksum = 0;
   if (audit_on(p)) {
+    // (through the page cache, into plain host memory: the checksum read is not a fill)
+    const int cfd = open(path, O_RDONLY | O_CLOEXEC);
     std::vector<uint64_t> tmp(bytes / 8);
     std::string err;
-    if (!read_parallel(fd, offset, bytes, tmp.data(), err)) {
+    if (cfd < 0 || !read_parallel(cfd, offset, bytes, tmp.data(), err)) {
+      if (cfd >= 0) close(cfd);
       close(fd);                             // the layer keeps its previous registration
-      return fail(LSN_E_ARG, "layer_pool_register_file: reading %s: %s", path, err.c_str());
+      return fail(LSN_E_ARG, "layer_pool_register_file: reading %s: %s", path,
+                  cfd < 0 ? std::strerror(errno) : err.c_str());
     }
+    close(cfd);
     checksum = checksum_host(tmp.data(), bytes);
   }
   forget_copies(p, layer);
@@ -471,6 +509,7 @@ lsn_status layer_pool_register_file(lsn_pool *p, int32_t layer, const char *path
   L.fd = fd;
   L.file_off = offset;
   L.bytes = bytes;
+  L.span = span;
   L.visits = 0;
   L.checksum = checksum;
   return LSN_OK;

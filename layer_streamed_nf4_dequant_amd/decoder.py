@@ -26,10 +26,89 @@ import numpy as np
 
 from . import inputs, lib
 from .configs import StackConfig
-from .stack import layer_layout, make_pool
+from .stack import arena_offsets, layer_layout, make_pool
 
 EPS = 1e-5
 THETA = 500000.0
+
+
+def activation_shapes(cfg: StackConfig, layers: int, nq: int) -> dict:
+    """Per-visit activations and gradients of the decoder step (one set, reused by every layer):
+    name -> (shape, dtype)."""
+    T, H, I, kv = cfg.T, cfg.hidden, cfg.inter, cfg.kv
+    th, ti, tk = (T, H), (T, I), (T, kv)
+    out = {n: (th, "bf16") for n in ("y_re", "n1", "n2", "h", "a", "dproj", "q", "o_att", "dy_b", "dh_b",
+                                     "do_att", "dq", "n_f", "dn_f")}
+    out.update({n: (tk, "bf16") for n in ("k", "v", "dk", "dv")})
+    out.update({n: (ti, "bf16") for n in ("gate", "up", "m", "dm", "dgate", "dup")})
+    out.update({n: ((T,), "f32") for n in ("rstd1", "rstd2", "rstd_f", "loss")})
+    out.update({"lse": ((T, nq), "f32"), "dy": (th, "f32"), "dn": (th, "f32")})
+    return out
+
+
+def decoder_workspaces(cfg: StackConfig, vocab: int, ce_chunk: int) -> dict:
+    """Device workspace bytes of the step's library calls: the projections' backward (single and
+    grouped), attention's backward and the chunked LM-head cross-entropy."""
+    T, r = cfg.T, cfg.r
+    layout, _ = layer_layout(cfg)
+    descs = [lib.LoraLinearDesc(T, p.K, p.N, r, cfg.scale, lib.WeightDesc(), None, None) for p in layout]
+    ws = max(lib.ws_bytes(T, p.K, p.N, r) for p in layout)
+    ws = max(ws, lib.group_ws_bytes(descs[0:3]), lib.group_ws_bytes(descs[4:6]))
+    n_seq, nq = T // cfg.seq_len, cfg.hidden // cfg.head_dim
+    return {"ws": ws, "ws_att": lib.attention_bwd_ws_bytes(n_seq, cfg.seq_len, nq),
+            "ws_ce": lib.lm_head_ce_ws_bytes(ce_chunk, cfg.hidden, vocab)}
+
+
+def decoder_buffer_plan(cfg: StackConfig, vocab: int, layers: int | None = None, modes=("streamed",),
+                        dequant: str = "staged", ce_chunk: int = 2048, reference: bool = False) -> list:
+    """Every device buffer a decoder training step uses, in arena order: [(key, part, nbytes)]."""
+    L = cfg.layers if layers is None else layers
+    layout, image = layer_layout(cfg)
+    T, H, r = cfg.T, cfg.hidden, cfg.r
+    nq = H // cfg.head_dim
+    sz = {"bf16": 2, "f32": 4, "u8": 1}
+    plan = [(("E",), "embedding_and_head", vocab * H * 2), (("head",), "embedding_and_head", vocab * H * 2),
+            (("g_final",), "norm_gains", H * 2)]
+    for l in range(L):
+        plan += [(("g1", l), "norm_gains", H * 2), (("g2", l), "norm_gains", H * 2)]
+        for j, p in enumerate(layout):
+            plan += [(("A", l, j), "adapters", r * p.K * 2), (("B", l, j), "adapters", p.N * r * 2),
+                     (("dA", l, j), "adapter_grads", r * p.K * 4), (("dB", l, j), "adapter_grads", p.N * r * 4)]
+    plan += [((k,), "tokens", T * 4) for k in ("ids", "labels", "positions")]
+    plan += [(("x", i), "layer_checkpoints", T * H * 2) for i in range(L + 1)]
+    for key, (shape, dt) in activation_shapes(cfg, L, nq).items():
+        plan.append(((key,), "activations", int(np.prod(shape)) * sz[dt]))
+    plan += [(("U", j), "activations", T * r * 2) for j, _ in enumerate(layout)]
+    plan += [((k,), "workspaces", n) for k, n in decoder_workspaces(cfg, vocab, ce_chunk).items()]
+    if dequant == "staged":
+        plan += [(("w_stage", j), "staging", p.N * p.K * 2) for j, p in enumerate(layout)]
+    if reference:
+        plan += [(("x_ref", i), "reference", T * H * 2) for i in range(2)] + [(("loss_ref",), "reference", T * 4)]
+    if "streamed" in modes:
+        plan += [(("slot", i), "pool_slots", image) for i in range(cfg.pool_slots)]
+    if "resident" in modes:
+        plan += [(("resident", l), "resident_images", image) for l in range(L)]
+    return plan
+
+
+def predict_decoder_bytes(cfg: StackConfig, vocab: int, layers: int | None = None, modes=("streamed",),
+                          dequant: str = "staged", ce_chunk: int = 2048, reference: bool = False) -> dict:
+    """Peak device memory of a decoder training step, from the shapes alone ("Soup v0.73.0
+    benchmarks README", record index: a peak-VRAM predictor whose fit decision refuses): the step
+    allocates nothing beyond its arena, so the step's peak is the arena. Also returned: the
+    set-up's largest extra temporaries (the embedding or head drawn in fp32 and rounded to bf16,
+    or one base weight in fp32 with its layer image and the packing workspace), which the fit
+    decision adds. Returns the parts, their "total" and "setup_extra"."""
+    plan = decoder_buffer_plan(cfg, vocab, layers, modes, dequant, ce_chunk, reference)
+    parts = {}
+    for _, part, nbytes in plan:
+        parts[part] = parts.get(part, 0) + nbytes
+    _, parts["total"] = arena_offsets(plan)
+    layout, image = layer_layout(cfg)
+    big = max(layout, key=lambda p: p.K * p.N)
+    pack = big.K * big.N * 4 + lib.load().nf4_pack_ws_bytes(big.N, big.K) + (image if "resident" not in modes else 0)
+    parts["setup_extra"] = max(vocab * cfg.hidden * (4 + 2), pack)
+    return parts
 
 
 class DecoderModel:
@@ -38,10 +117,15 @@ class DecoderModel:
 
     def __init__(self, cfg: StackConfig, vocab: int, layers: int | None = None, seed: int = 0,
                  modes=("streamed",), dequant: str = "staged", eps: float = EPS, theta: float = THETA,
-                 ce_chunk: int = 2048, label_rows: int | None = None):
+                 ce_chunk: int = 2048, label_rows: int | None = None, hbm_budget: int | None = None,
+                 reference: bool = False):
         """label_rows: keep the next-token label on only this many rows (a seeded sample of the
         rows that have one) and ignore the rest, so that the loss, and the gradient flowing back
-        from it, come from a sample of positions."""
+        from it, come from a sample of positions. hbm_budget: device bytes the model may take
+        (default: the free memory the device reports); the predicted arena plus the set-up's
+        temporaries (predict_decoder_bytes) must fit, else MemoryError before anything is
+        allocated. reference: also place the reference sweep's buffers in the arena (otherwise
+        the first reference step allocates them)."""
         import torch
         self.torch = torch
         self.cfg, self.V, self.seed = cfg, vocab, seed
@@ -55,28 +139,50 @@ class DecoderModel:
         self.dequant = dequant
         self.n_seq, self.nq, self.nkv, self.d = T // cfg.seq_len, H // d, cfg.kv // d, d
         self.dev = torch.device("cuda")
-        self.compute = torch.cuda.Stream()
-        self.copy_stream = torch.cuda.Stream()
         self.layout, self.image_bytes = layer_layout(cfg)
         self.names = [p.name for p in self.layout]
         self.j = {n: i for i, n in enumerate(self.names)}
         bf16, f32 = torch.bfloat16, torch.float32
         dev = self.dev
         key0 = ("decoder", cfg.name, vocab)
+        self.ce_chunk = ce_chunk
+
+        # ---- the fit decision, then every step buffer carved from one arena allocated first ----
+        pred = predict_decoder_bytes(cfg, vocab, self.L, modes, dequant, ce_chunk, reference)
+        need = pred["total"] + pred["setup_extra"]
+        budget = hbm_budget if hbm_budget is not None else torch.cuda.mem_get_info()[0]
+        if need > budget:
+            raise MemoryError(f"{cfg.name} decoder: needs {need} B of device memory (predicted: {pred['total']} B "
+                              f"arena + {pred['setup_extra']} B during set-up), {budget} B available: refused")
+        self.compute = torch.cuda.Stream()
+        self.copy_stream = torch.cuda.Stream()
+        plan = decoder_buffer_plan(cfg, vocab, self.L, modes, dequant, ce_chunk, reference)
+        offsets, arena_bytes = arena_offsets(plan)
+        self.arena = torch.empty(arena_bytes, dtype=torch.uint8, device=dev)
+        sizes = {key: nbytes for key, _, nbytes in plan}
+
+        def buf(key, shape, dtype):
+            o = offsets[key]
+            return self.arena[o:o + sizes[key]].view(dtype).view(shape)
 
         # ---- frozen base: per-layer NF4 images in pinned host memory (and on the device) ----
         self.means = np.zeros((self.L, len(self.layout)), dtype=np.float32)
         self.host_images, self.resident = [], ([] if "resident" in modes else None)
+        big = max(self.layout, key=lambda p: p.K * p.N)
+        ws_pack = torch.empty(lib.load().nf4_pack_ws_bytes(big.N, big.K), dtype=torch.uint8, device=dev)
         for l in range(self.L):
-            dev_img = torch.zeros(self.image_bytes, dtype=torch.uint8, device=dev)
+            if self.resident is not None:
+                dev_img = buf(("resident", l), (self.image_bytes,), torch.uint8)
+                dev_img.zero_()
+            else:
+                dev_img = torch.zeros(self.image_bytes, dtype=torch.uint8, device=dev)
             for j, p in enumerate(self.layout):
                 w = self.base_weight(l, p.name)
                 n = p.K * p.N
-                ws = torch.empty(lib.load().nf4_pack_ws_bytes(p.N, p.K), dtype=torch.uint8, device=dev)
                 self.means[l, j] = lib.nf4_pack_into(
                     w, dev_img[p.codes:p.codes + n // 2], dev_img[p.qabsmax:p.qabsmax + n // 64].view(torch.int8),
-                    dev_img[p.absmax2:p.absmax2 + 4 * (n // 16384)].view(f32), ws)
-                del w, ws
+                    dev_img[p.absmax2:p.absmax2 + 4 * (n // 16384)].view(f32), ws_pack)
+                del w
             img = torch.empty(self.image_bytes, dtype=torch.uint8, pin_memory=True)
             img.copy_(dev_img)
             self.host_images.append(img)
@@ -84,28 +190,39 @@ class DecoderModel:
                 self.resident.append(dev_img)
             else:
                 del dev_img
+        del ws_pack
         torch.cuda.synchronize()
 
         # ---- resident frozen parts and trainable adapters (seeded, synthetic) ----
-        self.E = inputs.device_normal((vocab, H), 1.0, seed, *key0, "E", dtype=bf16)
-        self.W_head = inputs.device_normal((vocab, H), 0.02, seed, *key0, "head", dtype=bf16)
-        self.g_final = self._gain(H, "g_final")
-        self.g1 = [self._gain(H, "g1", l) for l in range(self.L)]
-        self.g2 = [self._gain(H, "g2", l) for l in range(self.L)]
+        self.E = buf(("E",), (vocab, H), bf16)
+        self.E.copy_(inputs.device_normal((vocab, H), 1.0, seed, *key0, "E", dtype=bf16))
+        self.W_head = buf(("head",), (vocab, H), bf16)
+        self.W_head.copy_(inputs.device_normal((vocab, H), 0.02, seed, *key0, "head", dtype=bf16))
+        self.g_final = buf(("g_final",), (H,), bf16)
+        self.g_final.copy_(self._gain(H, "g_final"))
+        self.g1, self.g2 = [], []
+        for l in range(self.L):
+            self.g1.append(buf(("g1", l), (H,), bf16))
+            self.g1[-1].copy_(self._gain(H, "g1", l))
+            self.g2.append(buf(("g2", l), (H,), bf16))
+            self.g2[-1].copy_(self._gain(H, "g2", l))
         self.A, self.B, self.dA, self.dB = [], [], [], []
         for l in range(self.L):
             key = ("decoder", cfg.name, l)
-            self.A.append([inputs.device_uniform((r, p.K), 1.0 / np.sqrt(p.K), seed, *key, p.name, "A", dtype=bf16)
-                           for p in self.layout])
-            self.B.append([inputs.device_normal((p.N, r), inputs.STD["B"], seed, *key, p.name, "B", dtype=bf16)
-                           for p in self.layout])
-            self.dA.append([torch.zeros((r, p.K), dtype=f32, device=dev) for p in self.layout])
-            self.dB.append([torch.zeros((p.N, r), dtype=f32, device=dev) for p in self.layout])
+            Al, Bl = [], []
+            for j, p in enumerate(self.layout):
+                Al.append(buf(("A", l, j), (r, p.K), bf16))
+                Al[-1].copy_(inputs.device_uniform((r, p.K), 1.0 / np.sqrt(p.K), seed, *key, p.name, "A", dtype=bf16))
+                Bl.append(buf(("B", l, j), (p.N, r), bf16))
+                Bl[-1].copy_(inputs.device_normal((p.N, r), inputs.STD["B"], seed, *key, p.name, "B", dtype=bf16))
+            self.A.append(Al)
+            self.B.append(Bl)
+            self.dA.append([buf(("dA", l, j), (r, p.K), f32).zero_() for j, p in enumerate(self.layout)])
+            self.dB.append([buf(("dB", l, j), (p.N, r), f32).zero_() for j, p in enumerate(self.layout)])
 
         # ---- tokens: packed sequences, next-token labels (the last row of a sequence ignored) ----
         ids = torch.randint(0, vocab, (T,), generator=inputs.device_generator(seed, *key0, "ids"), device=dev,
                             dtype=torch.int32)
-        self.ids = ids
         lab = torch.roll(ids, -1)
         lab[cfg.seq_len - 1::cfg.seq_len] = -1
         if label_rows is not None:
@@ -114,41 +231,34 @@ class DecoderModel:
             keep = torch.zeros(T, dtype=torch.bool, device=dev)
             keep[has] = True
             lab = torch.where(keep, lab, torch.full_like(lab, -1))
-        self.labels = lab.contiguous()
+        self.ids = buf(("ids",), (T,), torch.int32)
+        self.ids.copy_(ids)
+        self.labels = buf(("labels",), (T,), torch.int32)
+        self.labels.copy_(lab)
+        del ids, lab
         self.n_counted = int((self.labels >= 0).sum())
-        self.positions = (torch.arange(T, device=dev, dtype=torch.int32) % cfg.seq_len).contiguous()
+        self.positions = buf(("positions",), (T,), torch.int32)
+        self.positions.copy_(torch.arange(T, device=dev, dtype=torch.int32) % cfg.seq_len)
 
         # ---- activations and gradients ----
-        e = lambda shape, dt=bf16: torch.empty(shape, dtype=dt, device=dev)  # noqa: E731
-        self.x = [e((T, H)) for _ in range(self.L + 1)]          # checkpoints: layer inputs, final hidden
-        self.y_re = e((T, H))                                    # the recompute's layer output
-        self.n1, self.n2, self.h, self.a, self.dproj = e((T, H)), e((T, H)), e((T, H)), e((T, H)), e((T, H))
-        self.rstd1, self.rstd2, self.rstd_f = e((T,), f32), e((T,), f32), e((T,), f32)
-        self.q, self.k, self.v = e((T, H)), e((T, cfg.kv)), e((T, cfg.kv))
-        self.o_att, self.lse = e((T, H)), e((T, self.nq), f32)
-        self.gate, self.up, self.m = e((T, I)), e((T, I)), e((T, I))
-        self.U = [e((T, r)) for _ in self.layout]
-        self.dy, self.dn = e((T, H), f32), e((T, H), f32)
-        self.dy_b, self.dh_b, self.do_att = e((T, H)), e((T, H)), e((T, H))
-        self.dm, self.dgate, self.dup = e((T, I)), e((T, I)), e((T, I))
-        self.dq, self.dk, self.dv = e((T, H)), e((T, cfg.kv)), e((T, cfg.kv))
-        self.n_f, self.dn_f = e((T, H)), e((T, H))
-        self.loss = e((T,), f32)
-        self.ce_chunk = ce_chunk
-        descs = [lib.LoraLinearDesc(T, p.K, p.N, r, cfg.scale, lib.WeightDesc(), None, None) for p in self.layout]
-        ws = max(lib.ws_bytes(T, p.K, p.N, r) for p in self.layout)
-        ws = max(ws, lib.group_ws_bytes(descs[0:3]), lib.group_ws_bytes(descs[4:6]))
-        self.ws = e((ws,), torch.uint8)
-        self.ws_att = e((lib.attention_bwd_ws_bytes(self.n_seq, cfg.seq_len, self.nq),), torch.uint8)
-        self.ws_ce = e((lib.lm_head_ce_ws_bytes(ce_chunk, H, vocab),), torch.uint8)
-        self.w_stage = [e((p.N, p.K)) for p in self.layout] if dequant == "staged" else None
+        for key, (shape, dt) in activation_shapes(cfg, self.L, self.nq).items():
+            setattr(self, key, buf((key,), shape, {"bf16": bf16, "f32": f32, "u8": torch.uint8}[dt]))
+        self.x = [buf(("x", i), (T, H), bf16) for i in range(self.L + 1)]   # layer inputs, final hidden
+        self.U = [buf(("U", j), (T, r), bf16) for j, _ in enumerate(self.layout)]
+        for key in ("ws", "ws_att", "ws_ce"):
+            setattr(self, key, buf((key,), (sizes[(key,)],), torch.uint8))
+        self.w_stage = ([buf(("w_stage", j), (p.N, p.K), bf16) for j, p in enumerate(self.layout)]
+                        if dequant == "staged" else None)
         self.recompute_ok = []
         self.x_ref = self.loss_ref = None
+        if reference:
+            self.x_ref = [buf(("x_ref", i), (T, H), bf16) for i in range(2)]
+            self.loss_ref = buf(("loss_ref",), (T,), f32)
 
         # ---- pool ----
         self.pool, self.slots = None, None
         if "streamed" in modes:
-            self.slots = [torch.empty(self.image_bytes, dtype=torch.uint8, device=dev) for _ in range(cfg.pool_slots)]
+            self.slots = [buf(("slot", i), (self.image_bytes,), torch.uint8) for i in range(cfg.pool_slots)]
             self.pool = make_pool(self.slots, self.image_bytes, self.L, self.copy_stream, 0)
             for l in range(self.L):
                 self.pool.register(l, self.host_images[l].data_ptr(), self.image_bytes)

@@ -25,7 +25,7 @@ OUT_BF16, OUT_F32, OUT_BF16_T = 0, 1, 2
 ADAPTERS_OFF, ADAPTERS_ON, ADAPTERS_U_READY = 0, 1, 2
 DX_BF16_SET, DX_F32_ADD, DX_F32_SET = 0, 1, 2
 GRAD_SET, GRAD_ADD = 0, 1
-POOL_AUDIT, POOL_KEEP_AT_TURN, POOL_HOST_SIM, POOL_FILE_TIER = 1, 2, 4, 8
+POOL_AUDIT, POOL_KEEP_AT_TURN, POOL_HOST_SIM, POOL_FILE_TIER, POOL_FILE_DIRECT = 1, 2, 4, 8, 16
 FAULT_STALE_REFETCH, FAULT_WRONG_SLOT = 1 << 8, 1 << 9
 
 EXPORTS = (
@@ -78,7 +78,7 @@ _lib = None
 class PoolBuffers(ctypes.Structure):
     """lsn_pool_buffers: the caller's checksum array (audit) and pinned bounce buffers (file tier)."""
     _fields_ = [("audit_sums", ctypes.c_void_p), ("audit_capacity", ctypes.c_size_t),
-                ("bounce", ctypes.c_void_p * 2)]
+                ("bounce", ctypes.c_void_p * 2), ("direct_stage", ctypes.c_void_p * 2)]
 
 
 def load():
@@ -340,16 +340,20 @@ def lora_linear_bwd_group(descs, X, dY_list, U_list, dX, dA_list, dB_list, dx_mo
 class LayerPool:
     """Owner of an lsn_pool handle. Slots, the audit's checksum array and the file tier's bounce
     buffers are caller memory (torch tensors or host buffers), passed as addresses: audit_sums =
-    (address, capacity in checksums), bounce = (address, address)."""
+    (address, capacity in checksums), bounce = (address, address), direct_stage = (address,
+    address) (plain host memory for the O_DIRECT reads)."""
 
     def __init__(self, slot_ptrs, slot_bytes: int, n_layers: int, copy_stream_handle: int | None,
-                 flags: int = 0, audit_sums: tuple[int, int] | None = None, bounce: tuple[int, int] | None = None):
+                 flags: int = 0, audit_sums: tuple[int, int] | None = None, bounce: tuple[int, int] | None = None,
+                 direct_stage: tuple[int, int] | None = None):
         arr = (ctypes.c_void_p * len(slot_ptrs))(*slot_ptrs)
         bufs = PoolBuffers()
         if audit_sums is not None:
             bufs.audit_sums, bufs.audit_capacity = audit_sums
         if bounce is not None:
             bufs.bounce[0], bufs.bounce[1] = bounce
+        if direct_stage is not None:
+            bufs.direct_stage[0], bufs.direct_stage[1] = direct_stage
         h = ctypes.c_void_p()
         check(load().layer_pool_create(len(slot_ptrs), slot_bytes, arr, n_layers, copy_stream_handle,
                                        flags, ctypes.byref(bufs), ctypes.byref(h)))

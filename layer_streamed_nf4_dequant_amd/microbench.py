@@ -146,8 +146,13 @@ def decoder_figure(cfg, vocab: int = 128256, steps: int = 3, modes=("streamed", 
     import time
 
     import torch
-    from layer_streamed_nf4_dequant_amd.decoder import DecoderModel
-    m = DecoderModel(cfg, vocab=vocab, modes=tuple(modes))
+    from layer_streamed_nf4_dequant_amd.decoder import DecoderModel, predict_decoder_bytes
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    ref = "streamed" in modes
+    m = DecoderModel(cfg, vocab=vocab, modes=tuple(modes), reference=ref)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
     out = {"layers": m.L, "vocab": vocab, "tokens_per_step": cfg.T, "seq_len": cfg.seq_len}
     runs = [(mode, mode, False) for mode in modes]
     if "streamed" in modes:
@@ -166,6 +171,10 @@ def decoder_figure(cfg, vocab: int = 128256, steps: int = 3, modes=("streamed", 
             out[name]["layer_reads_per_step"] = round((m.pool.stats()["bytes_copied"] - copied0)
                                                       / (steps * m.image_bytes), 2)
     out["mean_loss"] = round(m.mean_loss(), 4)
+    # the fit predictor: the device memory the steps above held against the prediction
+    out["peak_hbm_GB"] = round((torch.cuda.max_memory_allocated() - before) / 1e9, 4)
+    out["predicted_peak_hbm_GB"] = round(predict_decoder_bytes(cfg, vocab, modes=tuple(modes),
+                                                               reference=ref)["total"] / 1e9, 4)
     m.close()
     del m
     torch.cuda.empty_cache()

@@ -81,15 +81,69 @@ def layer_layout(cfg: StackConfig) -> tuple[list[ProjLayout], int]:
 
 MIB2 = 2 << 20
 AUDIT_CAPACITY = 16384          # pool checksums between two audits (2 per layer visit)
+FILE_ALIGN = 4096               # layer images in the file tier's file start on 4 KiB boundaries
+
+
+def file_stride(image_bytes: int) -> int:
+    """Bytes per layer in the file tier's file: the image padded to whole 4 KiB blocks (what an
+    O_DIRECT read needs; a buffered read ignores the padding)."""
+    return (image_bytes + FILE_ALIGN - 1) // FILE_ALIGN * FILE_ALIGN
+
+
+def host_memory_available() -> int:
+    """Host RAM the kernel reports as available for new allocations (MemAvailable)."""
+    with open("/proc/meminfo") as f:
+        for ln in f:
+            if ln.startswith("MemAvailable:"):
+                return int(ln.split()[1]) * 1024
+    raise OSError("no MemAvailable in /proc/meminfo")
+
+
+def predict_host_bytes(cfg: StackConfig, source: str, layers=None) -> dict:
+    """Host memory and disk a stack's frozen base needs per tier: "ram" keeps every layer image in
+    pinned host memory; "file" keeps them in one file (disk) and pins only the file tier's two
+    bounce buffers (plus, during set-up, one layer image on its way to the file)."""
+    L = cfg.layers if layers is None else layers
+    _, image = layer_layout(cfg)
+    if source == "ram":
+        return {"pinned": L * image, "disk": 0}
+    if source == "file":
+        return {"pinned": 2 * file_stride(image), "setup_extra": image, "disk": L * file_stride(image)}
+    raise ValueError(source)
+
+
+def choose_source(cfg: StackConfig, source: str, host_budget: int | None = None, disk_free: int | None = None,
+                  layers=None) -> str:
+    """The host tier of the frozen base ("An 8B Fine-Tune Now Fits in 4 GB of VRAM", the adoption
+    settings: the stream source picks RAM when the images fit and NVMe when they do not; "Soup
+    v0.73.0 benchmarks README", reading conventions: a fit decision refuses rather than warns).
+    source "ram" or "file" is taken as given; "auto" picks "ram" when every pinned image fits
+    the host budget (default: MemAvailable), else "file" when its bounce buffers fit the budget
+    and the images fit the free disk space, else raises MemoryError before anything is
+    allocated."""
+    if source in ("ram", "file"):
+        return source
+    if source != "auto":
+        raise ValueError(source)
+    budget = host_memory_available() if host_budget is None else host_budget
+    ram = predict_host_bytes(cfg, "ram", layers)
+    if ram["pinned"] <= budget:
+        return "ram"
+    f = predict_host_bytes(cfg, "file", layers)
+    if f["pinned"] + f["setup_extra"] <= budget and (disk_free is None or f["disk"] <= disk_free):
+        return "file"
+    raise MemoryError(f"{cfg.name}: the frozen base needs {ram['pinned']} B of pinned host memory, or "
+                      f"{f['pinned'] + f['setup_extra']} B of host memory and {f['disk']} B of disk "
+                      f"({budget} B of host memory and {disk_free} B of disk available): refused")
 
 
 def make_pool(slots, slot_bytes: int, n_layers: int, copy_stream, flags: int):
     """A layer pool over the given device slots, with the caller-owned memory its flags need
-    allocated here: the audit's checksum array (device, LSN_POOL_AUDIT) and the file tier's two
-    pinned bounce buffers (LSN_POOL_FILE_TIER). The tensors stay referenced by the returned
-    pool object for its lifetime."""
+    allocated here: the audit's checksum array (device, LSN_POOL_AUDIT), the file tier's two
+    pinned bounce buffers (LSN_POOL_FILE_TIER) and, for O_DIRECT reads, two plain staging buffers
+    (LSN_POOL_FILE_DIRECT). They stay referenced by the returned pool object for its lifetime."""
     import torch
-    keep, audit, bounce = [], None, None
+    keep, audit, bounce, stage = [], None, None, None
     if flags & lib.POOL_AUDIT:
         sums = torch.zeros(AUDIT_CAPACITY, dtype=torch.int64, device="cuda")
         keep.append(sums)
@@ -98,8 +152,16 @@ def make_pool(slots, slot_bytes: int, n_layers: int, copy_stream, flags: int):
         bufs = [torch.empty(slot_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
         keep += bufs
         bounce = (bufs[0].data_ptr(), bufs[1].data_ptr())
+    if flags & lib.POOL_FILE_DIRECT:
+        # plain host memory, 4 KiB aligned, for the O_DIRECT reads (pinned memory cannot take them)
+        st = []
+        for _ in range(2):
+            raw = np.empty(slot_bytes + FILE_ALIGN, dtype=np.uint8)
+            st.append(raw[(-raw.ctypes.data) % FILE_ALIGN:][:slot_bytes])
+        keep += st
+        stage = (st[0].ctypes.data, st[1].ctypes.data)
     pool = lib.LayerPool([t.data_ptr() for t in slots], slot_bytes, n_layers, copy_stream.cuda_stream, flags,
-                         audit_sums=audit, bounce=bounce)
+                         audit_sums=audit, bounce=bounce, direct_stage=stage)
     pool.memory = keep
     return pool
 
@@ -192,15 +254,27 @@ class Stack:
 
     def __init__(self, cfg: StackConfig, seed: int = 0, modes=("streamed",), audit: bool = False,
                  keep_at_turn: bool = False, fault: int = 0, record: bool = False, layers=None,
-                 dequant: str = "staged", hbm_budget: int | None = None, reference: bool = False):
+                 dequant: str = "staged", hbm_budget: int | None = None, reference: bool = False,
+                 source: str = "ram", host_budget: int | None = None, image_dir: str | None = None):
         """hbm_budget: device bytes the stack may take; by default the free memory the device
         reports. The predicted arena plus the set-up's temporaries (predict_device_bytes) must
         fit, else MemoryError before anything is allocated. reference: also place the reference
-        sweep's outputs in the arena (otherwise the first reference step allocates them)."""
+        sweep's outputs in the arena (otherwise the first reference step allocates them).
+        source: the host tier of the frozen base, "ram" (pinned images), "file" (one file read
+        by the pool's file tier; nothing but its bounce buffers pinned) or "auto" (choose_source
+        with host_budget, default MemAvailable); image_dir: where the file goes (default: a new
+        temporary directory)."""
         import torch
         self.torch = torch
         self.cfg = cfg
         self.L = cfg.layers if layers is None else layers
+        self.image_dir = image_dir
+        disk_free = None
+        if source == "auto":
+            import shutil
+            import tempfile
+            disk_free = shutil.disk_usage(image_dir or tempfile.gettempdir()).free
+        self.source = choose_source(cfg, source, host_budget, disk_free, self.L)
         pred = predict_device_bytes(cfg, modes, dequant, self.L, reference)
         need = pred["total"] + pred["setup_extra"]
         budget = hbm_budget if hbm_budget is not None else torch.cuda.mem_get_info()[0]
@@ -243,12 +317,14 @@ class Stack:
             return self.arena[o:o + sizes[key]].view(dtype).view(shape)
 
         # ---- frozen base: generated on the device per layer, packed, kept in pinned host images
+        # (source "ram") or written to the file tier's file (source "file")
         self.means = np.zeros((self.L, len(self.layout)), dtype=np.float32)
-        self.host_images = []
+        self.host_images = [] if self.source == "ram" else None
+        self.image_file = None
+        out_file = self._open_image_file() if self.source == "file" else None
         self.resident = [] if "resident" in modes else None
         scratch_w = None
         for l in range(self.L):
-            img = torch.empty(self.image_bytes, dtype=torch.uint8, pin_memory=True)
             if self.resident is not None:
                 dev_img = buf(("resident", l), (self.image_bytes,), torch.uint8)
                 dev_img.zero_()
@@ -268,12 +344,18 @@ class Stack:
                 else:
                     dev_img[p.w16:p.w16 + 2 * p.K * p.N].view(bf16).copy_(w.view(-1).to(bf16))
                 del w
-            img.copy_(dev_img)
-            self.host_images.append(img)
+            if out_file is None:
+                img = torch.empty(self.image_bytes, dtype=torch.uint8, pin_memory=True)
+                img.copy_(dev_img)
+                self.host_images.append(img)
+            else:
+                self._write_layer(out_file, dev_img.cpu().numpy())
             if self.resident is not None:
                 self.resident.append(dev_img)
             else:
                 del dev_img
+        if out_file is not None:
+            out_file.close()
         torch.cuda.synchronize()
 
         # ---- trainable adapters and their gradients (resident) ----
@@ -329,40 +411,63 @@ class Stack:
         self.checks = {}
         torch.cuda.synchronize()
 
-    def reset_pool(self, flags: int = 0, n_slots: int | None = None, source: str = "ram"):
+    def reset_pool(self, flags: int = 0, n_slots: int | None = None, source: str | None = None,
+                   direct: bool = False):
         """(Re)create the layer pool with the given flags and slot count over the same images.
         source "ram": the pinned host images; "file": the same bytes in one file (the pool's
-        file tier reads them; the file is written on first use, see write_image_file)."""
+        file tier reads them; written on first use from the pinned images when the stack keeps
+        them, see write_image_file); None: the stack's own tier. direct: the file tier reads with
+        O_DIRECT (past the page cache: a read of the storage device)."""
         torch = self.torch
         torch.cuda.synchronize()
         if self.pool is not None:
             self.pool.close()
+            self.pool = None
         if n_slots is not None and n_slots != len(self.slots):
             self.slots = [torch.empty(self.image_bytes, dtype=torch.uint8, device=self.dev)
                           for _ in range(n_slots)]
+        source = self.source if source is None else source
         if source == "file":
             path = self.write_image_file()
-            flags |= lib.POOL_FILE_TIER
-        elif source != "ram":
-            raise ValueError(source)
-        self.pool = make_pool(self.slots, self.image_bytes, self.L, self.copy_stream, flags)
+            flags |= lib.POOL_FILE_TIER | (lib.POOL_FILE_DIRECT if direct else 0)
+        elif source != "ram" or self.host_images is None:
+            raise ValueError(f"source {source!r} is not available for this stack (its tier: {self.source})")
+        # O_DIRECT reads whole 4 KiB blocks into the bounce buffers and slots are 4 KiB multiples
+        slot_bytes = file_stride(self.image_bytes) if direct else self.image_bytes
+        if direct and any(t.numel() < slot_bytes or t.data_ptr() % FILE_ALIGN for t in self.slots):
+            self.slots = [torch.empty(slot_bytes + FILE_ALIGN, dtype=torch.uint8, device=self.dev)
+                          for _ in self.slots]
+            self.slots = [t[(-t.data_ptr()) % FILE_ALIGN:][:slot_bytes] for t in self.slots]
+        self.pool = make_pool(self.slots, slot_bytes, self.L, self.copy_stream, flags)
+        stride = file_stride(self.image_bytes)
         for l in range(self.L):
             if source == "file":
-                self.pool.register_file(l, path, l * self.image_bytes, self.image_bytes)
+                self.pool.register_file(l, path, l * stride, self.image_bytes)
             else:
                 self.pool.register(l, self.host_images[l].data_ptr(), self.image_bytes)
 
-    def write_image_file(self, directory: str | None = None) -> str:
-        """Writes the layer images, back to back, to one file (in `directory`, else a new
-        temporary directory) for the pool's file tier; returns its path. Removed by close()."""
-        if getattr(self, "image_file", None) is None:
-            import tempfile
-            d = tempfile.mkdtemp(prefix="lsnf4_images_", dir=directory)
-            path = os.path.join(d, "layers.bin")
-            with open(path, "wb") as f:
+    def _open_image_file(self):
+        import tempfile
+        d = tempfile.mkdtemp(prefix="lsnf4_images_", dir=self.image_dir)
+        self.image_file = os.path.join(d, "layers.bin")
+        return open(self.image_file, "wb")
+
+    def _write_layer(self, f, img: np.ndarray) -> None:
+        """Appends one layer image and its padding to whole 4 KiB blocks."""
+        f.write(memoryview(img))
+        pad = file_stride(img.size) - img.size
+        if pad:
+            f.write(bytes(pad))
+
+    def write_image_file(self) -> str:
+        """The file tier's file: the layer images, each at a 4 KiB aligned offset (l * stride,
+        the image padded to whole 4 KiB blocks), in `image_dir` (else a new temporary directory);
+        written from the pinned images on first use, or at set-up when the stack keeps no pinned
+        images. Removed by close()."""
+        if self.image_file is None:
+            with self._open_image_file() as f:
                 for img in self.host_images:
-                    f.write(memoryview(img.numpy()))
-            self.image_file = path
+                    self._write_layer(f, img.numpy())
         return self.image_file
 
     # ------------------------------------------------------------------------------------------
@@ -568,11 +673,14 @@ class Stack:
         """Host-to-device bandwidth (GB/s) of one layer image into a slot on the copy stream."""
         torch = self.torch
         torch.cuda.synchronize()
+        src = self.host_images
+        if src is None:                          # file tier: one pinned buffer of an image's size
+            src = [torch.empty(self.image_bytes, dtype=torch.uint8, pin_memory=True)]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(self.copy_stream):
             e0.record(self.copy_stream)
             for i in range(reps):
-                self.slots[i % len(self.slots)].copy_(self.host_images[i % self.L], non_blocking=True)
+                self.slots[i % len(self.slots)][:self.image_bytes].copy_(src[i % len(src)], non_blocking=True)
             e1.record(self.copy_stream)
         e1.synchronize()
         return reps * self.image_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9

@@ -58,10 +58,15 @@ def test_toy_8b_shapes_exactness_and_controls(gpu):
     variants = [("2 slots", 0, None, "ram"), ("1 slot", 0, 1, "ram"), ("3 slots", 0, 3, "ram"),
                 ("keep at turn", lib.POOL_KEEP_AT_TURN, 2, "ram"), ("audit", lib.POOL_AUDIT, 2, "ram"),
                 ("file", 0, 2, "file"), ("file, audit", lib.POOL_AUDIT, 2, "file"),
-                ("file, 1 slot, keep at turn", lib.POOL_KEEP_AT_TURN, 1, "file")]
+                ("file, 1 slot, keep at turn", lib.POOL_KEEP_AT_TURN, 1, "file"),
+                ("file, O_DIRECT", 0, 2, "file direct"), ("file, O_DIRECT, audit", lib.POOL_AUDIT, 2, "file direct")]
     for name, flags, n_slots, source in variants:
         print(f"  variant {name}", flush=True)
-        st.reset_pool(flags, n_slots, source)
+        direct = source == "file direct"
+        if direct and not _direct_io_supported(st):
+            print("    (skipped: no O_DIRECT on this file system)", flush=True)
+            continue
+        st.reset_pool(flags, n_slots, source.split()[0], direct=direct)
         st.step("streamed")
         if flags & lib.POOL_AUDIT:
             st.pool.audit()
@@ -85,6 +90,38 @@ def test_toy_8b_shapes_exactness_and_controls(gpu):
             st.pool.audit()
         assert e.value.status == lib.LSN_E_AUDIT
         snapshot(st)
+    st.close()
+
+
+def _direct_io_supported(st) -> bool:
+    import os
+    path = st.write_image_file()
+    try:
+        fd = os.open(path, os.O_RDONLY | os.O_DIRECT)
+    except OSError:
+        return False
+    os.close(fd)
+    return True
+
+
+def test_auto_source_streams_from_the_file_tier(gpu):
+    """source="auto" with a host budget too small for the pinned images: the stack keeps its base
+    in the file tier (no pinned images), and the streamed step equals the resident one bit for bit."""
+    cfg = configs.C3
+    L = 4
+    print(f"case: {L}-layer 8B-shaped toy, auto source with a small host budget", flush=True)
+    from layer_streamed_nf4_dequant_amd.stack import predict_host_bytes
+    f = predict_host_bytes(cfg, "file", layers=L)
+    budget = f["pinned"] + f["setup_extra"]          # enough for the file tier, not for L pinned images
+    assert budget < predict_host_bytes(cfg, "ram", layers=L)["pinned"]
+    st = Stack(cfg, modes=("streamed", "resident"), record=True, layers=L, source="auto", host_budget=budget)
+    assert st.source == "file" and st.host_images is None and st.image_file is not None
+    st.step("resident")
+    ref = snapshot(st)
+    st.step("streamed")
+    fwd, re, dx, eq, n = compare(ref, snapshot(st))
+    assert fwd and re and dx and eq == n == 2 * 7 * L
+    assert st.pool.stats()["copies"] == 2 * L
     st.close()
 
 

@@ -335,3 +335,58 @@ def test_file_tier_register_again_replaces_the_image(tmp_path):
     p.pool.register_file(0, p.path, p.offsets[1], SLOT)   # layer 0 now names layer 1's bytes
     np.testing.assert_array_equal(p.visit(0), p.images[1])
     p.pool.close()
+
+
+def aligned4k(n):
+    raw = np.zeros(n + 4096, dtype=np.uint8)
+    off = (-raw.ctypes.data) % 4096
+    return raw[off:off + n]
+
+
+def test_file_tier_direct_reads(tmp_path):
+    """LSN_POOL_FILE_DIRECT: the fills read the file with O_DIRECT (4 KiB aligned offsets, each
+    image's region padded to whole 4 KiB blocks); every visit still sees exactly its layer's bytes,
+    the padding is never copied, and misaligned offsets or buffers are refused."""
+    n_layers, img_bytes = 4, SLOT - 256          # the images do not fill a 4 KiB block: padding is read
+    rng = np.random.default_rng(3)
+    images = [rng.integers(0, 255, img_bytes, dtype=np.uint8) for _ in range(n_layers)]
+    path = str(tmp_path / "direct.bin")
+    blob = np.full(n_layers * SLOT + SLOT, 0xAB, dtype=np.uint8)   # padding bytes that must not appear
+    offsets = [SLOT + l * SLOT for l in range(n_layers)]
+    for off, img in zip(offsets, images):
+        blob[off:off + img_bytes] = img
+    blob.tofile(path)
+    slots = [aligned4k(SLOT) for _ in range(2)]
+    bounce = [aligned4k(SLOT) for _ in range(2)]
+    stage = [aligned4k(SLOT) for _ in range(2)]
+    flags = lib.POOL_HOST_SIM | lib.POOL_FILE_TIER | lib.POOL_FILE_DIRECT
+    try:
+        pool = lib.LayerPool([s.ctypes.data for s in slots], SLOT, n_layers, None, flags,
+                             bounce=(bounce[0].ctypes.data, bounce[1].ctypes.data),
+                             direct_stage=(stage[0].ctypes.data, stage[1].ctypes.data))
+        pool.register_file(0, path, offsets[0], img_bytes)
+    except lib.LsnError as e:
+        if "O_DIRECT" in str(e):
+            pytest.skip(f"the file system under {tmp_path} does not support O_DIRECT: {e}")
+        raise
+    for l in range(1, n_layers):
+        pool.register_file(l, path, offsets[l], img_bytes)
+    for s in slots:
+        s[:] = 0
+    for l in list(range(n_layers)) + list(reversed(range(n_layers))):
+        ptr = pool.acquire(l, None)
+        got = np.ctypeslib.as_array((ctypes.c_uint8 * SLOT).from_address(ptr)).copy()
+        pool.release(l, None)
+        np.testing.assert_array_equal(got[:img_bytes], images[l])
+        assert not np.any(got[img_bytes:] == 0xAB), "the O_DIRECT padding must not be copied into a slot"
+    with pytest.raises(lib.LsnError) as e:              # an offset that is not 4 KiB aligned
+        pool.register_file(0, path, offsets[0] + 256, img_bytes)
+    assert e.value.status == lib.LSN_E_ARG
+    pool.close()
+    with pytest.raises(lib.LsnError):                    # staging buffers not 4 KiB aligned
+        lib.LayerPool([s.ctypes.data for s in slots], SLOT, n_layers, None, flags,
+                      bounce=(bounce[0].ctypes.data, bounce[1].ctypes.data),
+                      direct_stage=(stage[0].ctypes.data + 256, stage[1].ctypes.data))
+    with pytest.raises(lib.LsnError):                    # no staging buffers
+        lib.LayerPool([s.ctypes.data for s in slots], SLOT, n_layers, None, flags,
+                      bounce=(bounce[0].ctypes.data, bounce[1].ctypes.data))
