@@ -146,28 +146,110 @@ struct AttnArgs {
 };
 
 // ------------------------------------------------------------------------------------------
+// Row-major tiles staged by direct-to-LDS loads. A 64-row tile of D bf16 columns is 64 rows of
+// 2D bytes; 16-byte chunk c of row r sits at physical chunk c ^ swz(r), so that a fragment read
+// (16 consecutive rows, one chunk each) and a transpose read (4 consecutive rows, 32 bytes each)
+// both touch every bank at most once. A direct load (one wave instruction) fills one 1 KB LDS
+// segment, lane l writing bytes 16 l .. 16 l + 15: lane l loads the global chunk that belongs at
+// its slot. Rows past the block's valid rows load the last valid row (finite values: the keys
+// they stand for are masked, and their P is exactly 0).
+// ------------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);   // 16 chunks per row
+  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);                // 8 chunks; two rows per bank line
+}
+
+template <int D>
+struct DTile {
+  static constexpr int ROW = 2 * D;              // bytes per row
+  static constexpr int BYTES = kB * ROW;          // one 64-row tile
+  static constexpr int SEGS = BYTES / 1024;       // direct loads per tile
+  static constexpr int CH = D / 8;                // 16-byte chunks per row
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base, int64_t bytes) {
+  // raw buffer, no stride; loads past num_records return 0 (never fault)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Byte offset (from the tile's first row in global memory) of the chunk lane `lane` loads for
+// segment `seg`; rows at or past `nvalid` read row nvalid - 1.
+template <int D>
+__device__ __forceinline__ uint32_t seg_voff(int seg, int lane, int64_t ld, int nvalid) {
+  constexpr int RPS = 1024 / DTile<D>::ROW;      // rows per segment
+  const int row = seg * RPS + lane / DTile<D>::CH;
+  const int c = (lane % DTile<D>::CH) ^ swz<D>(row);
+  const int grow = row < nvalid ? row : nvalid - 1;
+  return (uint32_t)((grow * ld + 8 * c) * 2);
+}
+
+__device__ __forceinline__ void direct_load(__amdgpu_buffer_rsrc_t rs, char *lds_seg, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)lds_seg, 16, voff, soff, 0, 0);
+}
+
+// the wave's loads of this block must have landed and its reads of the stage about to be
+// refilled must have returned; then all waves meet
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0070);            // vmcnt(0), lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// A/B fragment of a row-major tile: row `row`, 8 columns of chunk `ch`
+template <int D>
+__device__ __forceinline__ bf16x8 sw_frag(const char *tile, int row, int ch) {
+  return as_bf(*reinterpret_cast<const u32x4_t *>(tile + row * DTile<D>::ROW + ((ch ^ swz<D>(row)) << 4)));
+}
+
+// Transposed fragment from a row-major tile: this lane's column 16 j + (lane % 16) at the rows
+// of reduction step c that the accumulator layout pairs with lane group g: rows 32 c + 4 g + i
+// (i < 4) and 32 c + 16 + 4 g + i - 4 (i >= 4), read with the gfx950 LDS transpose read (each
+// 16-lane group reads a 4-row x 16-column block; lane l points at row l / 4, columns 4 (l % 4)
+// .. + 3, and receives column l of the 4 rows).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag_rm(const char *tile, int j, int c, int g, int lane) {
+  const int sl = lane & 15;
+  const int ch = 2 * j + ((sl & 3) >> 1);
+  const int r0 = 32 * c + 4 * g + (sl >> 2), r1 = r0 + 16;
+  lds_char *p0 = (lds_char *)(tile + r0 * DTile<D>::ROW + ((ch ^ swz<D>(r0)) << 4) + 8 * (sl & 1));
+  lds_char *p1 = (lds_char *)(tile + r1 * DTile<D>::ROW + ((ch ^ swz<D>(r1)) << 4) + 8 * (sl & 1));
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p1);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ------------------------------------------------------------------------------------------
 // Forward: one workgroup of 8 waves per (128-query block, sequence, query head), heaviest blocks
-// first; a wave skips the key blocks that lie entirely after its 16 queries.
+// first; a wave skips the key blocks that lie entirely after its 16 queries. K and V blocks of
+// 64 keys stream through two LDS stages by direct-to-LDS loads (each wave issues its share of
+// the next block right after the barrier that frees its stage), so the workgroup meets once per
+// block and no thread spends instructions on staging.
 template <int D>
 __global__ __launch_bounds__(kFwdThreads) void k_attn_fwd(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char k_rm[Tile<D>::RM_BYTES];
-  __shared__ __attribute__((aligned(16))) char v_tr[Tile<D>::TR_BYTES];
-  const int64_t nqb = (a.S + kFwdQ - 1) / kFwdQ, nkb = (a.S + kB - 1) / kB;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * DTile<D>::BYTES];   // [stage][K, V]
+  const int nqb = (int)((a.S + kFwdQ - 1) / kFwdQ);
   const int64_t per = a.n_seq * a.n_q;
-  const int64_t qb = nqb - 1 - blockIdx.x / per;
+  const int qb = nqb - 1 - (int)(blockIdx.x / per);
   const int64_t rest = blockIdx.x % per;
   const int64_t b = rest / a.n_q;
   const int h = (int)(rest % a.n_q), hk = h / (a.n_q / a.n_kv);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
-  const int64_t wq0 = qb * kFwdQ + 16 * wave;   // this wave's first query
-  const int64_t q_in_seq = wq0 + col;
+  const int S = (int)a.S;
+  const int wq0 = qb * kFwdQ + 16 * wave;          // this wave's first query
+  const int q_in_seq = wq0 + col;
   const int64_t seq0 = b * a.S;
-  const uint16_t *Kb = a.k + hk * D, *Vb = a.v + hk * D;
 
   bf16x8 qf[D / 32];   // B operand of S^T = K Q^T: query `col`, dims 32 c + 8 g ..
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
-    qf[c] = q_in_seq < a.S
+    qf[c] = q_in_seq < S
                 ? as_bf(*reinterpret_cast<const u32x4_t *>(a.q + (seq0 + q_in_seq) * a.ldq + h * D + 32 * c + 8 * g))
                 : as_bf(u32x4_t{0u, 0u, 0u, 0u});
   floatx4 acc[D / 16];   // O^T: dims 16 j + 4 g + e of query `col`
@@ -176,26 +258,32 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_fwd(AttnArgs a) {
   float m = -INFINITY, l = 0.0f;
   const float c2 = a.scale * kLog2e;
 
-  // threads 0..127 stage K (row-major), threads 128..255 stage V (transposed); the key blocks
-  // run up to the one holding the workgroup's last query
-  const int t = threadIdx.x;
-  const bool stK = t < Tile<D>::NBLK, stV = t >= 128 && t - 128 < Tile<D>::NBLK;
-  const int64_t kb_end = ((qb + 1) * kFwdQ < a.S ? (qb + 1) * kFwdQ : a.S);   // one past the last query
-  const int64_t kb_last = (kb_end - 1) / kB < nkb - 1 ? (kb_end - 1) / kB : nkb - 1;
-  u32x4_t pre[8];
-  auto fetch = [&](int64_t kb) {
-    if (stK) load_block<D>(Kb, a.ldk, seq0 + kb * kB, rows_left(a.S, kb), t, pre);
-    else if (stV) load_block<D>(Vb, a.ldv, seq0 + kb * kB, rows_left(a.S, kb), t - 128, pre);
+  // the key blocks run up to the one holding the workgroup's last query
+  const int q_end = (qb + 1) * kFwdQ < S ? (qb + 1) * kFwdQ : S;   // one past the last query
+  const int kb_last = (q_end - 1) / kB;
+  const __amdgpu_buffer_rsrc_t rk = rsrc_of(a.k + seq0 * a.ldk + hk * D, a.S * a.ldk * 2);
+  const __amdgpu_buffer_rsrc_t rv = rsrc_of(a.v + seq0 * a.ldv + hk * D, a.S * a.ldv * 2);
+  constexpr int SEGW = DTile<D>::SEGS / 8;        // segments of each tile per wave
+  // the wave's share of block kb: segments wave * SEGW .. of the K tile and of the V tile
+  auto issue = [&](int kb) {
+    const int nvalid = S - kb * kB < kB ? S - kb * kB : kB;
+    char *st = smem + (kb & 1) * 2 * DTile<D>::BYTES;
+#pragma unroll
+    for (int i = 0; i < SEGW; ++i) {
+      const int sg = wave * SEGW + i;
+      direct_load(rk, st + sg * 1024, seg_voff<D>(sg, lane, a.ldk, nvalid), (uint32_t)(kb * kB * a.ldk * 2));
+      direct_load(rv, st + DTile<D>::BYTES + sg * 1024, seg_voff<D>(sg, lane, a.ldv, nvalid),
+                  (uint32_t)(kb * kB * a.ldv * 2));
+    }
   };
-  fetch(0);
-  for (int64_t kb = 0; kb <= kb_last; ++kb) {
-    __syncthreads();
-    if (stK) store_block<D>(pre, t, k_rm, nullptr);
-    else if (stV) store_block<D>(pre, t - 128, nullptr, v_tr);
-    __syncthreads();
-    if (kb < kb_last) fetch(kb + 1);   // in flight while this block is computed
-    if (kb * kB > wq0 + 15) continue;  // every key of the block is after this wave's queries
-    const bool diag = kb * kB + kB - 1 > wq0;   // some key of the block is after some query here
+  issue(0);
+  for (int kb = 0; kb <= kb_last; ++kb) {
+    tile_barrier();                                // block kb has landed; stage (kb+1)&1 is free
+    if (kb < kb_last) issue(kb + 1);
+    if (kb * kB > wq0 + 15) continue;              // every key of the block is after this wave's queries
+    const bool diag = kb * kB + kB - 1 > wq0;      // some key of the block is after some query here
+    const char *k_t = smem + (kb & 1) * 2 * DTile<D>::BYTES;
+    const char *v_t = k_t + DTile<D>::BYTES;
 
     // S^T tile tt: keys 16 tt + 4 g + e (rows) x query `col`; two tiles per half
     floatx4 s[4];
@@ -205,7 +293,7 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_fwd(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) kf[u][c] = rm_frag<D>(k_rm, 16 * (2 * hf + u) + col, 4 * c + g);
+        for (int c = 0; c < D / 32; ++c) kf[u][c] = sw_frag<D>(k_t, 16 * (2 * hf + u) + col, 4 * c + g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -221,12 +309,13 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_fwd(AttnArgs a) {
     }
     // online softmax in the exp2 domain
     float mx = -INFINITY;
+    const int key0 = kb * kB + 4 * g;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x = s[tt][e] * c2;
-        if (diag && kb * kB + 16 * tt + 4 * g + e > q_in_seq) x = -INFINITY;
+        if (diag && key0 + 16 * tt + e > q_in_seq) x = -INFINITY;
         s[tt][e] = x;
         mx = fmaxf(mx, x);
       }
@@ -251,13 +340,14 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_fwd(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
     }
-    // O^T += V^T P^T over the block's 64 keys (two reduction steps of 32)
+    // O^T += V^T P^T over the block's 64 keys (two reduction steps of 32); V^T fragments come
+    // from the row-major V tile by transpose reads
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const bf16x8 pf = acc_frag(s[2 * c], s[2 * c + 1]);
       bf16x8 vf[D / 16];
 #pragma unroll
-      for (int jj = 0; jj < D / 16; ++jj) vf[jj] = tr_frag(v_tr, 16 * jj + col, c, g);
+      for (int jj = 0; jj < D / 16; ++jj) vf[jj] = tr_frag_rm<D>(v_t, jj, c, g, lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int jj = 0; jj < D / 16; ++jj) acc[jj] = mfma(vf[jj], pf, acc[jj]);
@@ -267,7 +357,7 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_fwd(AttnArgs a) {
       for (int jj = 0; jj < D / 16; ++jj) asm volatile("" ::"v"(vf[jj]));
     }
   }
-  if (q_in_seq < a.S) {
+  if (q_in_seq < S) {
     const float inv = 1.0f / l;
     uint16_t *orow = a.out_o + (seq0 + q_in_seq) * a.ld_out_o + h * D;
 #pragma unroll
@@ -625,6 +715,8 @@ lsn_status attention_fwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, in
     return fail(LSN_E_ARG, "attention_fwd: q, k, v, o need 16-byte aligned rows (ld a multiple of 8)");
   if (ldq < n_q * D || ldk < n_kv * D || ldv < n_kv * D || ldo < n_q * D)
     return fail(LSN_E_ARG, "attention_fwd: a row stride is smaller than its heads");
+  if (S * ldk * 2 >= ((int64_t)1 << 31) || S * ldv * 2 >= ((int64_t)1 << 31))
+    return fail(LSN_E_ARG, "attention_fwd: one sequence of k or v spans 2 GiB or more");
   const Strided ins[] = {{q, ldq, n_q * D, 2}, {k, ldk, n_kv * D, 2}, {v, ldv, n_kv * D, 2}};
   const Strided outs[] = {{o, ldo, n_q * D, 2}, {lse, n_q, n_q, 4}};
   for (const Strided &out : outs)
