@@ -399,24 +399,24 @@ __global__ __launch_bounds__(kThreads) void k_attn_dot(AttnArgs a, float *__rest
 // ------------------------------------------------------------------------------------------
 // dK, dV: one workgroup per (key block, sequence, key/value head), heaviest (first) blocks
 // first; a wave owns 16 keys (lane column = key) and loops over the group's query heads and the
-// query blocks at or after its key block.
+// query blocks at or after its key block. Each (head, query block)'s Q and dO tiles and the rows'
+// log-sum-exp and D stream through two LDS stages by direct-to-LDS loads (Q^T and dO^T
+// fragments by transpose reads of the row-major tiles).
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char q_rm[Tile<D>::RM_BYTES];
-  __shared__ __attribute__((aligned(16))) char q_tr[Tile<D>::TR_BYTES];
-  __shared__ __attribute__((aligned(16))) char d_rm[Tile<D>::RM_BYTES];
-  __shared__ __attribute__((aligned(16))) char d_tr[Tile<D>::TR_BYTES];
-  __shared__ float lse2_s[kB], dot_s[kB];
-  const int64_t nb = (a.S + kB - 1) / kB;
+  constexpr int STAGE = 2 * DTile<D>::BYTES + 2 * kB * 4;                      // Q, dO, lse, D
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  const int nb = (int)((a.S + kB - 1) / kB);
   const int64_t per = a.n_seq * a.n_kv;
-  const int64_t kb = blockIdx.x / per;
+  const int kb = (int)(blockIdx.x / per);
   const int64_t rest = blockIdx.x % per;
   const int64_t b = rest / a.n_kv;
   const int hk = (int)(rest % a.n_kv), grp = a.n_q / a.n_kv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
-  const int64_t k_in_seq = kb * kB + 16 * wave + col;
+  const int S = (int)a.S;
+  const int k_in_seq = kb * kB + 16 * wave + col;
   const int64_t seq0 = b * a.S;
-  const bool kvalid = k_in_seq < a.S;
+  const bool kvalid = k_in_seq < S;
   bf16x8 kf[D / 32], vf[D / 32];   // B operands: key `col`, dims 32 c + 8 g ..
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
@@ -430,101 +430,108 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
   for (int j = 0; j < D / 16; ++j) dk[j] = dv[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   const float c2 = a.scale * kLog2e;
 
-  // threads 0..127 stage Q, threads 128..255 stage dO (both row-major and transposed), threads
-  // 0..63 the rows' lse and D; the next (head, query block)'s tiles are fetched while the current
-  // one is computed
-  const int t = threadIdx.x;
-  const bool stQ = t < Tile<D>::NBLK, stD = t >= 128 && t - 128 < Tile<D>::NBLK;
-  u32x4_t pre[8];
-  float pre_lse = INFINITY, pre_dot = 0.0f;
-  auto fetch = [&](int hh, int64_t qb) {
-    const int h = hk * grp + hh;
-    const int nvalid = rows_left(a.S, qb);
-    if (stQ) load_block<D>(a.q + h * D, a.ldq, seq0 + qb * kB, nvalid, t, pre);
-    else if (stD) load_block<D>(a.dO + h * D, a.lddo, seq0 + qb * kB, nvalid, t - 128, pre);
-    if (t < kB) {
-      const bool ok = t < nvalid;
-      pre_lse = ok ? a.lse[(seq0 + qb * kB + t) * a.n_q + h] * kLog2e : INFINITY;
-      pre_dot = ok ? a.dot[(seq0 + qb * kB + t) * a.n_q + h] : 0.0f;
+  const __amdgpu_buffer_rsrc_t rq = rsrc_of(a.q + seq0 * a.ldq, a.S * a.ldq * 2);
+  const __amdgpu_buffer_rsrc_t rd = rsrc_of(a.dO + seq0 * a.lddo, a.S * a.lddo * 2);
+  const __amdgpu_buffer_rsrc_t rl = rsrc_of(a.lse + seq0 * a.n_q, a.S * a.n_q * 4);
+  const __amdgpu_buffer_rsrc_t rt = rsrc_of(a.dot + seq0 * a.n_q, a.S * a.n_q * 4);
+  constexpr int SEGW = DTile<D>::SEGS / 4;        // segments of each tile per wave (4 waves)
+  // iteration it = hh * (nb - kb) + (qb - kb) visits query head hk * grp + hh, query block qb
+  const int nqb = nb - kb, n_it = grp * nqb;
+  auto issue = [&](int it) {
+    const int hh = it / nqb, qb = kb + it % nqb, h = hk * grp + hh;
+    const int nvalid = S - qb * kB < kB ? S - qb * kB : kB;
+    char *st = smem + (it & 1) * STAGE;
+#pragma unroll
+    for (int i = 0; i < SEGW; ++i) {
+      const int sg = wave * SEGW + i;
+      direct_load(rq, st + sg * 1024, seg_voff<D>(sg, lane, a.ldq, nvalid) + h * D * 2,
+                  (uint32_t)(qb * kB * a.ldq * 2));
+      direct_load(rd, st + DTile<D>::BYTES + sg * 1024, seg_voff<D>(sg, lane, a.lddo, nvalid) + h * D * 2,
+                  (uint32_t)(qb * kB * a.lddo * 2));
+    }
+    if (wave < 2) {   // the rows' lse (wave 0) and D (wave 1), 4 bytes per lane
+      const int row = lane < nvalid ? lane : nvalid - 1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? rl : rt,
+                                               (lds_void *)(st + 2 * DTile<D>::BYTES + wave * kB * 4), 4,
+                                               (uint32_t)((row * a.n_q + h) * 4), (uint32_t)(qb * kB * a.n_q * 4),
+                                               0, 0);
     }
   };
-  fetch(0, kb);
-  for (int hh = 0; hh < grp; ++hh) {
-    for (int64_t qb = kb; qb < nb; ++qb) {
-      __syncthreads();
-      if (stQ) store_block<D>(pre, t, q_rm, q_tr);
-      else if (stD) store_block<D>(pre, t - 128, d_rm, d_tr);
-      if (t < kB) {
-        lse2_s[t] = pre_lse;
-        dot_s[t] = pre_dot;
-      }
-      __syncthreads();
-      if (qb + 1 < nb) fetch(hh, qb + 1);
-      else if (hh + 1 < grp) fetch(hh + 1, kb);
+  issue(0);
+  for (int it = 0; it < n_it; ++it) {
+    tile_barrier();
+    if (it + 1 < n_it) issue(it + 1);
+    const int qb = kb + it % nqb;
+    const char *q_t = smem + (it & 1) * STAGE;
+    const char *d_t = q_t + DTile<D>::BYTES;
+    const float *lse_s = reinterpret_cast<const float *>(q_t + 2 * DTile<D>::BYTES);
+    const float *dot_s = lse_s + kB;
 
-      // S and dP tiles tt: queries 16 tt + 4 g + e (rows) x key `col`; two tiles per half
-      floatx4 s[4], dp[4];
+    // S and dP tiles tt: queries 16 tt + 4 g + e (rows) x key `col`; two tiles per half
+    floatx4 s[4], dp[4];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        bf16x8 qa[2][D / 32], da[2][D / 32];
+    for (int hf = 0; hf < 2; ++hf) {
+      bf16x8 qa[2][D / 32], da[2][D / 32];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int c = 0; c < D / 32; ++c) {
-            qa[u][c] = rm_frag<D>(q_rm, 16 * (2 * hf + u) + col, 4 * c + g);
-            da[u][c] = rm_frag<D>(d_rm, 16 * (2 * hf + u) + col, 4 * c + g);
-          }
+        for (int c = 0; c < D / 32; ++c) {
+          qa[u][c] = sw_frag<D>(q_t, 16 * (2 * hf + u) + col, 4 * c + g);
+          da[u][c] = sw_frag<D>(d_t, 16 * (2 * hf + u) + col, 4 * c + g);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int tt = 2 * hf + u;
+        s[tt] = dp[tt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+          s[tt] = mfma(qa[u][c], kf[c], s[tt]);
+          dp[tt] = mfma(da[u][c], vf[c], dp[tt]);
+        }
+      }
+      AT_MFMA_FENCE();
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+          asm volatile("" ::"v"(qa[u][c]));
+          asm volatile("" ::"v"(da[u][c]));
+        }
+    }
+    // P and dS = P (dP - D); queries before the key (first block) or past S (padding rows of the
+    // last block, which hold copies of row S - 1) contribute nothing
+    const int q0 = qb * kB + 4 * g;
+    const bool edge = qb == kb || qb * kB + kB > S;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int qi = 16 * tt + 4 * g + e;
+        float p = ex2(s[tt][e] * c2 - lse_s[qi] * kLog2e);
+        if (edge && (q0 + 16 * tt + e < k_in_seq || q0 + 16 * tt + e >= S)) p = 0.0f;
+        s[tt][e] = p;
+        dp[tt][e] = p * (dp[tt][e] - dot_s[qi]);
+      }
+    // dV^T += dO^T P,  dK^T += Q^T dS  (reduction over the block's 64 queries, in two steps)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        const bf16x8 bf = which == 0 ? acc_frag(s[2 * c], s[2 * c + 1]) : acc_frag(dp[2 * c], dp[2 * c + 1]);
+        bf16x8 af[D / 16];
+#pragma unroll
+        for (int jj = 0; jj < D / 16; ++jj) af[jj] = tr_frag_rm<D>(which == 0 ? d_t : q_t, jj, c, g, lane);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int tt = 2 * hf + u;
-          s[tt] = dp[tt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int c = 0; c < D / 32; ++c) {
-            s[tt] = mfma(qa[u][c], kf[c], s[tt]);
-            dp[tt] = mfma(da[u][c], vf[c], dp[tt]);
-          }
+        for (int jj = 0; jj < D / 16; ++jj) {
+          if (which == 0) dv[jj] = mfma(af[jj], bf, dv[jj]);
+          else dk[jj] = mfma(af[jj], bf, dk[jj]);
         }
         AT_MFMA_FENCE();
+        asm volatile("" ::"v"(bf));
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int c = 0; c < D / 32; ++c) {
-            asm volatile("" ::"v"(qa[u][c]));
-            asm volatile("" ::"v"(da[u][c]));
-          }
-      }
-      // P and dS = P (dP - D)
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int qi = 16 * tt + 4 * g + e;
-          float p = ex2(s[tt][e] * c2 - lse2_s[qi]);
-          if (qb == kb && qb * kB + qi < k_in_seq) p = 0.0f;
-          s[tt][e] = p;
-          dp[tt][e] = p * (dp[tt][e] - dot_s[qi]);
-        }
-      // dV^T += dO^T P,  dK^T += Q^T dS  (reduction over the block's 64 queries, in two steps)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int which = 0; which < 2; ++which) {
-          const bf16x8 bf = which == 0 ? acc_frag(s[2 * c], s[2 * c + 1]) : acc_frag(dp[2 * c], dp[2 * c + 1]);
-          bf16x8 af[D / 16];
-#pragma unroll
-          for (int jj = 0; jj < D / 16; ++jj) af[jj] = tr_frag(which == 0 ? d_tr : q_tr, 16 * jj + col, c, g);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int jj = 0; jj < D / 16; ++jj) {
-            if (which == 0) dv[jj] = mfma(af[jj], bf, dv[jj]);
-            else dk[jj] = mfma(af[jj], bf, dk[jj]);
-          }
-          AT_MFMA_FENCE();
-          asm volatile("" ::"v"(bf));
-#pragma unroll
-          for (int jj = 0; jj < D / 16; ++jj) asm volatile("" ::"v"(af[jj]));
-        }
+        for (int jj = 0; jj < D / 16; ++jj) asm volatile("" ::"v"(af[jj]));
       }
     }
   }
@@ -544,23 +551,24 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
 
 // ------------------------------------------------------------------------------------------
 // dQ: one workgroup per (query block, sequence, query head), heaviest blocks first; a wave owns
-// 16 queries (lane column = query) and loops over the key blocks up to its own.
+// 16 queries (lane column = query) and loops over the key blocks up to its own. K and V blocks
+// stream through two LDS stages by direct-to-LDS loads (row-major; K^T fragments by transpose
+// reads), as in the forward.
 template <int D>
 __global__ __launch_bounds__(kFwdThreads) void k_attn_bwd_q(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char k_rm[Tile<D>::RM_BYTES];
-  __shared__ __attribute__((aligned(16))) char k_tr[Tile<D>::TR_BYTES];
-  __shared__ __attribute__((aligned(16))) char v_rm[Tile<D>::RM_BYTES];
-  const int64_t nqb = (a.S + kFwdQ - 1) / kFwdQ, nkb = (a.S + kB - 1) / kB;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * DTile<D>::BYTES];   // [stage][K, V]
+  const int nqb = (int)((a.S + kFwdQ - 1) / kFwdQ);
   const int64_t per = a.n_seq * a.n_q;
-  const int64_t qb = nqb - 1 - blockIdx.x / per;
+  const int qb = nqb - 1 - (int)(blockIdx.x / per);
   const int64_t rest = blockIdx.x % per;
   const int64_t b = rest / a.n_q;
   const int h = (int)(rest % a.n_q), hk = h / (a.n_q / a.n_kv);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
-  const int64_t wq0 = qb * kFwdQ + 16 * wave;   // this wave's first query
-  const int64_t q_in_seq = wq0 + col;
+  const int S = (int)a.S;
+  const int wq0 = qb * kFwdQ + 16 * wave;          // this wave's first query
+  const int q_in_seq = wq0 + col;
   const int64_t seq0 = b * a.S;
-  const bool qvalid = q_in_seq < a.S;
+  const bool qvalid = q_in_seq < S;
   bf16x8 qf[D / 32], df[D / 32];   // B operands: query `col`, dims 32 c + 8 g ..
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
@@ -576,25 +584,30 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_bwd_q(AttnArgs a) {
   for (int j = 0; j < D / 16; ++j) acc[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   const float c2 = a.scale * kLog2e;
 
-  // threads 0..127 stage K (row-major and transposed), threads 128..255 stage V (row-major)
-  const int t = threadIdx.x;
-  const bool stK = t < Tile<D>::NBLK, stV = t >= 128 && t - 128 < Tile<D>::NBLK;
-  u32x4_t pre[8];
-  auto fetch = [&](int64_t kb) {
-    if (stK) load_block<D>(a.k + hk * D, a.ldk, seq0 + kb * kB, rows_left(a.S, kb), t, pre);
-    else if (stV) load_block<D>(a.v + hk * D, a.ldv, seq0 + kb * kB, rows_left(a.S, kb), t - 128, pre);
+  const int q_end = (qb + 1) * kFwdQ < S ? (qb + 1) * kFwdQ : S;   // one past the last query
+  const int kb_last = (q_end - 1) / kB;
+  const __amdgpu_buffer_rsrc_t rk = rsrc_of(a.k + seq0 * a.ldk + hk * D, a.S * a.ldk * 2);
+  const __amdgpu_buffer_rsrc_t rv = rsrc_of(a.v + seq0 * a.ldv + hk * D, a.S * a.ldv * 2);
+  constexpr int SEGW = DTile<D>::SEGS / 8;
+  auto issue = [&](int kb) {
+    const int nvalid = S - kb * kB < kB ? S - kb * kB : kB;
+    char *st = smem + (kb & 1) * 2 * DTile<D>::BYTES;
+#pragma unroll
+    for (int i = 0; i < SEGW; ++i) {
+      const int sg = wave * SEGW + i;
+      direct_load(rk, st + sg * 1024, seg_voff<D>(sg, lane, a.ldk, nvalid), (uint32_t)(kb * kB * a.ldk * 2));
+      direct_load(rv, st + DTile<D>::BYTES + sg * 1024, seg_voff<D>(sg, lane, a.ldv, nvalid),
+                  (uint32_t)(kb * kB * a.ldv * 2));
+    }
   };
-  const int64_t kb_end = ((qb + 1) * kFwdQ < a.S ? (qb + 1) * kFwdQ : a.S);   // one past the last query
-  const int64_t kb_last = (kb_end - 1) / kB < nkb - 1 ? (kb_end - 1) / kB : nkb - 1;
-  fetch(0);
-  for (int64_t kb = 0; kb <= kb_last; ++kb) {
-    __syncthreads();
-    if (stK) store_block<D>(pre, t, k_rm, k_tr);
-    else if (stV) store_block<D>(pre, t - 128, v_rm, nullptr);
-    __syncthreads();
-    if (kb < kb_last) fetch(kb + 1);
+  issue(0);
+  for (int kb = 0; kb <= kb_last; ++kb) {
+    tile_barrier();
+    if (kb < kb_last) issue(kb + 1);
     if (kb * kB > wq0 + 15) continue;  // every key of the block is after this wave's queries
     const bool diag = kb * kB + kB - 1 > wq0;
+    const char *k_t = smem + (kb & 1) * 2 * DTile<D>::BYTES;
+    const char *v_t = k_t + DTile<D>::BYTES;
 
     // S^T and dP^T tiles tt: keys 16 tt + 4 g + e (rows) x query `col`; two tiles per half
     floatx4 s[4], dp[4];
@@ -605,8 +618,8 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_bwd_q(AttnArgs a) {
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
-          ka[u][c] = rm_frag<D>(k_rm, 16 * (2 * hf + u) + col, 4 * c + g);
-          va[u][c] = rm_frag<D>(v_rm, 16 * (2 * hf + u) + col, 4 * c + g);
+          ka[u][c] = sw_frag<D>(k_t, 16 * (2 * hf + u) + col, 4 * c + g);
+          va[u][c] = sw_frag<D>(v_t, 16 * (2 * hf + u) + col, 4 * c + g);
         }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -628,21 +641,23 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_bwd_q(AttnArgs a) {
           asm volatile("" ::"v"(va[u][c]));
         }
     }
+    const int key0 = kb * kB + 4 * g;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float p = ex2(s[tt][e] * c2 - lse2);
-        if (diag && kb * kB + 16 * tt + 4 * g + e > q_in_seq) p = 0.0f;
+        if (diag && key0 + 16 * tt + e > q_in_seq) p = 0.0f;
         dp[tt][e] = p * (dp[tt][e] - dq_dot);
       }
-    // dQ^T += K^T dS^T over the block's 64 keys (two steps of 32)
+    // dQ^T += K^T dS^T over the block's 64 keys (two steps of 32); K^T fragments by transpose
+    // reads of the row-major K tile
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const bf16x8 sf = acc_frag(dp[2 * c], dp[2 * c + 1]);
       bf16x8 ka[D / 16];
 #pragma unroll
-      for (int jj = 0; jj < D / 16; ++jj) ka[jj] = tr_frag(k_tr, 16 * jj + col, c, g);
+      for (int jj = 0; jj < D / 16; ++jj) ka[jj] = tr_frag_rm<D>(k_t, jj, c, g, lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int jj = 0; jj < D / 16; ++jj) acc[jj] = mfma(ka[jj], sf, acc[jj]);
@@ -771,6 +786,9 @@ lsn_status attention_bwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, in
     return fail(LSN_E_ARG, "attention_bwd: a row stride is smaller than its heads");
   if (ws_bytes < attention_bwd_ws_bytes(n_seq, S, n_q))
     return fail(LSN_E_ARG, "attention_bwd: workspace smaller than attention_bwd_ws_bytes");
+  if (S * ldq * 2 >= ((int64_t)1 << 31) || S * ldk * 2 >= ((int64_t)1 << 31) || S * ldv * 2 >= ((int64_t)1 << 31) ||
+      S * lddo * 2 >= ((int64_t)1 << 31))
+    return fail(LSN_E_ARG, "attention_bwd: one sequence of q, k, v or dO spans 2 GiB or more");
   const Strided ins[] = {{q, ldq, n_q * D, 2}, {k, ldk, n_kv * D, 2}, {v, ldv, n_kv * D, 2},
                          {o, ldo, n_q * D, 2}, {lse, n_q, n_q, 4},       {dO, lddo, n_q * D, 2}};
   const Strided outs[] = {{dq, lddq, n_q * D, 2}, {dk, lddk, n_kv * D, 2}, {dv, lddv, n_kv * D, 2},
