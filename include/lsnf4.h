@@ -271,6 +271,67 @@ lsn_status lora_linear_bwd_group(int32_t n, const lsn_lora_linear *L, const uint
                                  void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Projections with the decoder-layer glue in their GEMM's epilogue. Each result is bit-identical
+ * to the projection entry point followed by the glue entry point named (the same fp32 arithmetic
+ * on the same rounded bf16 product), and costs no separate pass over HBM: the epilogue applies
+ * the glue to the output tile it has just computed. Used in every forward and recomputed
+ * forward of a decoder layer ("Exact Layer Streaming", Abstract: the recompute is part of the
+ * step). All pointers are device pointers unless said otherwise; overlaps give LSN_E_ARG.
+ * ---------------------------------------------------------------------------------------- */
+
+/* The rotary embedding a fused epilogue applies: a table written by rope_table (below). */
+typedef struct {
+  const float *cs;           /* table from rope_table (device, 16-byte aligned) */
+  int32_t n_pos;             /* its rows */
+  int32_t head_dim;          /* its head width: 64 or 128 */
+  const int32_t *positions;  /* device int32 [T]: the position (table row) of each token row;
+                                values outside [0, n_pos) are clamped into it (a wrong rotation,
+                                never an out-of-bounds read) */
+} lsn_rope;
+
+/*
+ * lora_linear_fwd_group_epi - lora_linear_fwd_group with, per member g:
+ *   residual != NULL and residual[g] != NULL: Y_g = bf16( residual[g] + P_g ), P_g the plain
+ *     output bf16(X W_g^T + s U_g B_g^T): add_bf16(P_g, residual[g]) (the residual stream's
+ *     addition after the o and down projections). Y_g may be residual[g] itself.
+ *   bit g of rope_mask: Y_g = rope_apply(P_g) with the table, head width and positions of *rope
+ *     (q and k); N_g a multiple of rope->head_dim. Not together with a residual.
+ * residual: NULL or a host array of n device pointers (entries may be NULL); rope: host pointer,
+ * may be NULL when rope_mask is 0. NF4 members run as lora_linear_fwd (the residual added in its
+ * epilogue, the rotation by a table-driven pass after it). Async on `stream`.
+ */
+lsn_status lora_linear_fwd_group_epi(int32_t n, const lsn_lora_linear *L, int32_t adapters, const uint16_t *X,
+                                     uint16_t *const *Y, uint16_t *const *U, const uint16_t *const *residual,
+                                     uint32_t rope_mask, const lsn_rope *rope, void *ws, size_t ws_bytes,
+                                     void *stream);
+
+/*
+ * lora_linear_fwd_swiglu - the gate and up projections of a gated MLP and the SwiGLU between
+ * them, for descriptors Lg and Lu sharing T, K, N, r and the scale:
+ *   gate = bf16(X Wg^T + s Ug Bg^T), up = bf16(X Wu^T + s Uu Bu^T), M = swiglu_fwd(gate, up).
+ * Adapters as lora_linear_fwd (Ug, Uu device [T][r]). gate and up (device [T][N]) may be NULL
+ * when both weights are bf16: then they are not stored (a forward whose backward recomputes
+ * them). With bf16 weights one GEMM launch computes 128 gate and the same 128 up columns per
+ * tile and the SwiGLU in its epilogue; with NF4 weights gate and up are required and the call
+ * runs lora_linear_fwd_group, then swiglu_fwd. N a multiple of 8. Async on `stream`.
+ */
+lsn_status lora_linear_fwd_swiglu(const lsn_lora_linear *Lg, const lsn_lora_linear *Lu, int32_t adapters,
+                                  const uint16_t *X, uint16_t *gate, uint16_t *up, uint16_t *M, uint16_t *Ug,
+                                  uint16_t *Uu, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * lora_linear_bwd_swiglu - lora_linear_bwd of the down projection (input X = M, the SwiGLU's
+ * output) followed by swiglu_bwd: dM = bf16(dY W + s G A) is not stored; the epilogue writes
+ * dgate = bf16( dM up sigma(gate) (1 + gate (1 - sigma(gate))) ) and dup = bf16( dM silu(gate) )
+ * (gate, up, dgate, dup: device bf16 [T][K]). dA, dB and grad_mode, ws as lora_linear_bwd.
+ * Bit-identical to lora_linear_bwd (LSN_DX_BF16_SET) then swiglu_bwd. Async on `stream`.
+ */
+lsn_status lora_linear_bwd_swiglu(const lsn_lora_linear *L, const uint16_t *X, const uint16_t *dY,
+                                  const uint16_t *U, const uint16_t *gate, const uint16_t *up, uint16_t *dgate,
+                                  uint16_t *dup, float *dA, float *dB, int32_t grad_mode, void *ws, size_t ws_bytes,
+                                  void *stream);
+
+/* ------------------------------------------------------------------------------------------
  * The resident ends of the stack ("Can You Fine-Tune a 27B Model on a Laptop? (I Did the
  * Math)", transcript @7:42-7:55: the embedding table and the output head stay resident and
  * unquantised; "Exact Layer Streaming", Abstract: the cross-entropy logits term, 14 bytes per
@@ -371,6 +432,16 @@ lsn_status convert_f32_bf16(int64_t n, const float *in, uint16_t *out, void *str
 lsn_status convert_bf16_f32(int64_t n, const uint16_t *in, float *out, void *stream);
 
 /*
+ * rope_table - the cosines and sines every rotation of rope_apply uses, as a table:
+ * cs[p][i] = (cos a, sin a), a = fl32(p * f_i), f_i = fl32(theta^(-2i/head_dim)), for
+ * p < n_pos, i < head_dim/2, with rope_apply's arithmetic, so a rotation driven by the table has
+ * rope_apply's bits. cs: device fp32 [n_pos][head_dim/2][2], 16-byte aligned. head_dim even and
+ * <= 512; 1 <= n_pos <= 2^24; theta finite and > 1.
+ */
+lsn_status rope_table(int32_t n_pos, int32_t head_dim, float theta, float *cs, void *stream);
+
+
+/*
  * attention_fwd - causal scaled dot-product attention with grouped key/value heads (the
  * attention of the Llama-3.1 and Qwen2.5 layers the pages train; they print no formula):
  * n_seq packed sequences of S rows each (T = n_seq x S rows; sequence b is rows b S .. b S + S - 1);
@@ -407,6 +478,21 @@ lsn_status attention_bwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, in
                          const float *lse, const uint16_t *dO, int64_t lddo, float scale,
                          uint16_t *dq, int64_t lddq, uint16_t *dk, int64_t lddk, uint16_t *dv,
                          int64_t lddv, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * attention_bwd_rope - attention_bwd for a q and k that the forward received rotated by the rotary
+ * embedding (rope_apply, or lora_linear_fwd_group_epi's rotation): dq and dk come out rotated
+ * back, i.e. as the gradients of the unrotated projection outputs, bit-identical to attention_bwd
+ * followed by rope_apply(inverse) on dq and dk with the same table (rope->head_dim equal to
+ * head_dim; rope->positions [n_seq S]). The rotation is applied to each gradient row as it is
+ * stored: no extra pass over dq or dk. rope: host pointer. Async on `stream`.
+ */
+lsn_status attention_bwd_rope(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                              const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk,
+                              const uint16_t *v, int64_t ldv, const uint16_t *o, int64_t ldo,
+                              const float *lse, const uint16_t *dO, int64_t lddo, float scale,
+                              uint16_t *dq, int64_t lddq, uint16_t *dk, int64_t lddk, uint16_t *dv,
+                              int64_t lddv, void *ws, size_t ws_bytes, const lsn_rope *rope, void *stream);
 
 /* ------------------------------------------------------------------------------------------
  * Layer pool ("Exact Layer Streaming", Abstract; transcript @7:11-7:32; "An 8B Fine-Tune

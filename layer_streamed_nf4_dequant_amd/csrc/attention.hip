@@ -23,6 +23,7 @@
 #include <cmath>
 
 #include "common.h"
+#include "glue_math.h"
 
 namespace lsn {
 lsn_status require_gfx950();
@@ -143,7 +144,47 @@ struct AttnArgs {
   const float *dot;  // [T][n_q]  D_i = dO_i . O_i
   uint16_t *out_o, *dq, *dk, *dv;
   int64_t ld_out_o, lddq, lddk, lddv;
+  // rope != 0: dq and dk are rotated back (the inverse rotary embedding) before they are stored
+  int rope, rope_n_pos;
+  const float *rope_cs;        // (cos, sin) table [rope_n_pos][D / 2]
+  const int32_t *rope_pos;     // [T] table row of each token row
 };
+
+// Store one row's gradient (dims 16 j + 4 g + e of the row held by the lane, g = lane / 16):
+// bf16( acc * mul ); with rot, each pair (i, i + D/2) of the rounded values is then turned back
+// by its angle (rope_apply's inverse rotation, the same arithmetic), and rounded again. Pair
+// partners sit in the same lane: dims 16 j + .. and 16 (j + D/32) + ..
+template <int D>
+__device__ __forceinline__ void store_grad_row(uint16_t *dst, const floatx4 (&acc)[D / 16], float mul, bool rot,
+                                               const AttnArgs &a, int64_t row, int g) {
+  float v[D / 16][4];
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[j][e] = acc[j][e] * mul;
+  if (rot) {
+    const int pos = min(max(a.rope_pos[row], 0), a.rope_n_pos - 1);
+    const float *cs = a.rope_cs + (int64_t)pos * D;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+      const int f0 = 16 * j + 4 * g;   // pair index of v[j][0]
+      const floatx4 c01 = *reinterpret_cast<const floatx4 *>(cs + 2 * f0);
+      const floatx4 c23 = *reinterpret_cast<const floatx4 *>(cs + 2 * f0 + 4);
+      const float cv[4] = {c01[0], c01[2], c23[0], c23[2]};
+      const float sv[4] = {c01[1], c01[3], c23[1], c23[3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x1 = bf16f(f2bf(v[j][e])), x2 = bf16f(f2bf(v[j + D / 32][e]));
+        rope_pair(x1, x2, cv[e], __fmul_rn(-1.0f, sv[e]), v[j][e], v[j + D / 32][e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    const u32x2 w = {pack_bf16x2(v[j][0], v[j][1]), pack_bf16x2(v[j][2], v[j][3])};
+    *reinterpret_cast<u32x2 *>(dst + 16 * j + 4 * g) = w;
+  }
+}
 
 // ------------------------------------------------------------------------------------------
 // Row-major tiles staged by direct-to-LDS loads. A 64-row tile of D bf16 columns is 64 rows of
@@ -536,16 +577,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
     }
   }
   if (kvalid) {
-    uint16_t *krow = a.dk + (seq0 + k_in_seq) * a.lddk + hk * D;
-    uint16_t *vrow = a.dv + (seq0 + k_in_seq) * a.lddv + hk * D;
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      const u32x2 wk = {pack_bf16x2(dk[j][0] * a.scale, dk[j][1] * a.scale),
-                        pack_bf16x2(dk[j][2] * a.scale, dk[j][3] * a.scale)};
-      const u32x2 wv = {pack_bf16x2(dv[j][0], dv[j][1]), pack_bf16x2(dv[j][2], dv[j][3])};
-      *reinterpret_cast<u32x2 *>(krow + 16 * j + 4 * g) = wk;
-      *reinterpret_cast<u32x2 *>(vrow + 16 * j + 4 * g) = wv;
-    }
+    store_grad_row<D>(a.dk + (seq0 + k_in_seq) * a.lddk + hk * D, dk, a.scale, a.rope != 0, a, seq0 + k_in_seq, g);
+    store_grad_row<D>(a.dv + (seq0 + k_in_seq) * a.lddv + hk * D, dv, 1.0f, false, a, seq0 + k_in_seq, g);
   }
 }
 
@@ -667,15 +700,8 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_bwd_q(AttnArgs a) {
       for (int jj = 0; jj < D / 16; ++jj) asm volatile("" ::"v"(ka[jj]));
     }
   }
-  if (qvalid) {
-    uint16_t *row = a.dq + (seq0 + q_in_seq) * a.lddq + h * D;
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      const u32x2 w = {pack_bf16x2(acc[j][0] * a.scale, acc[j][1] * a.scale),
-                       pack_bf16x2(acc[j][2] * a.scale, acc[j][3] * a.scale)};
-      *reinterpret_cast<u32x2 *>(row + 16 * j + 4 * g) = w;
-    }
-  }
+  if (qvalid)
+    store_grad_row<D>(a.dq + (seq0 + q_in_seq) * a.lddq + h * D, acc, a.scale, a.rope != 0, a, seq0 + q_in_seq, g);
 }
 
 bool al16(const void *p, int64_t ld) { return ((uintptr_t)p & 15) == 0 && ld % 8 == 0; }
@@ -768,36 +794,53 @@ size_t attention_bwd_ws_bytes(int64_t n_seq, int64_t S, int32_t n_q) {
   return (size_t)(n_seq * S * n_q) * 4;
 }
 
-lsn_status attention_bwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, int32_t head_dim, const uint16_t *q,
-                         int64_t ldq, const uint16_t *k, int64_t ldk, const uint16_t *v, int64_t ldv,
-                         const uint16_t *o, int64_t ldo, const float *lse, const uint16_t *dO, int64_t lddo,
-                         float scale, uint16_t *dq, int64_t lddq, uint16_t *dk, int64_t lddk, uint16_t *dv,
-                         int64_t lddv, void *ws, size_t ws_bytes, void *stream) {
-  lsn_status st = check_common(n_seq, S, n_q, n_kv, head_dim, scale, "attention_bwd");
+}  // extern "C"
+
+namespace {
+
+// attention_bwd, and with rope (may be null) attention_bwd_rope; `who` names the entry point
+lsn_status attn_bwd_impl(const char *who, int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                         const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk, const uint16_t *v,
+                         int64_t ldv, const uint16_t *o, int64_t ldo, const float *lse, const uint16_t *dO,
+                         int64_t lddo, float scale, uint16_t *dq, int64_t lddq, uint16_t *dk, int64_t lddk,
+                         uint16_t *dv, int64_t lddv, void *ws, size_t ws_bytes, const lsn_rope *rope, void *stream) {
+  lsn_status st = check_common(n_seq, S, n_q, n_kv, head_dim, scale, who);
   if (st != LSN_OK) return st;
   const int64_t D = head_dim, T = n_seq * S;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !ws)
-    return fail(LSN_E_ARG, "attention_bwd: null pointer");
+    return fail(LSN_E_ARG, "%s: null pointer", who);
+  if (rope && (!rope->cs || ((uintptr_t)rope->cs & 15) || !rope->positions || rope->n_pos < 1 ||
+               rope->head_dim != head_dim))
+    return fail(LSN_E_ARG, "%s: the rotation needs a 16-byte aligned table of this head width, positions and "
+                           "n_pos >= 1", who);
   if (!al16(q, ldq) || !al16(k, ldk) || !al16(v, ldv) || !al16(o, ldo) || !al16(dO, lddo) || !al16(dq, lddq) ||
       !al16(dk, lddk) || !al16(dv, lddv) || ((uintptr_t)ws & 15))
-    return fail(LSN_E_ARG, "attention_bwd: tensors need 16-byte aligned rows (ld a multiple of 8)");
+    return fail(LSN_E_ARG, "%s: tensors need 16-byte aligned rows (ld a multiple of 8)", who);
   if (ldq < n_q * D || ldk < n_kv * D || ldv < n_kv * D || ldo < n_q * D || lddo < n_q * D || lddq < n_q * D ||
       lddk < n_kv * D || lddv < n_kv * D)
-    return fail(LSN_E_ARG, "attention_bwd: a row stride is smaller than its heads");
+    return fail(LSN_E_ARG, "%s: a row stride is smaller than its heads", who);
   if (ws_bytes < attention_bwd_ws_bytes(n_seq, S, n_q))
-    return fail(LSN_E_ARG, "attention_bwd: workspace smaller than attention_bwd_ws_bytes");
+    return fail(LSN_E_ARG, "%s: workspace smaller than attention_bwd_ws_bytes", who);
   if (S * ldq * 2 >= ((int64_t)1 << 31) || S * ldk * 2 >= ((int64_t)1 << 31) || S * ldv * 2 >= ((int64_t)1 << 31) ||
       S * lddo * 2 >= ((int64_t)1 << 31))
-    return fail(LSN_E_ARG, "attention_bwd: one sequence of q, k, v or dO spans 2 GiB or more");
+    return fail(LSN_E_ARG, "%s: one sequence of q, k, v or dO spans 2 GiB or more", who);
   const Strided ins[] = {{q, ldq, n_q * D, 2}, {k, ldk, n_kv * D, 2}, {v, ldv, n_kv * D, 2},
                          {o, ldo, n_q * D, 2}, {lse, n_q, n_q, 4},       {dO, lddo, n_q * D, 2}};
   const Strided outs[] = {{dq, lddq, n_q * D, 2}, {dk, lddk, n_kv * D, 2}, {dv, lddv, n_kv * D, 2},
                           {ws, n_q, n_q, 4}};
+  if (rope) {
+    for (int i = 0; i < 4; ++i) {
+      const size_t ob = span(T, outs[i].ld, outs[i].width, outs[i].elt);
+      if (ranges_overlap(outs[i].p, ob, rope->cs, (size_t)rope->n_pos * D * 4) ||
+          ranges_overlap(outs[i].p, ob, rope->positions, (size_t)T * 4))
+        return fail(LSN_E_ARG, "%s: an output overlaps the rotation inputs", who);
+    }
+  }
   for (int i = 0; i < 4; ++i) {
     for (const Strided &in : ins)
-      if (overlap(outs[i], in, T)) return fail(LSN_E_ARG, "attention_bwd: an output or the workspace overlaps an input");
+      if (overlap(outs[i], in, T)) return fail(LSN_E_ARG, "%s: an output or the workspace overlaps an input", who);
     for (int j = i + 1; j < 4; ++j)
-      if (overlap(outs[i], outs[j], T)) return fail(LSN_E_ARG, "attention_bwd: outputs overlap");
+      if (overlap(outs[i], outs[j], T)) return fail(LSN_E_ARG, "%s: outputs overlap", who);
   }
   st = require_gfx950();
   if (st != LSN_OK) return st;
@@ -825,6 +868,12 @@ lsn_status attention_bwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, in
   a.lddq = lddq;
   a.lddk = lddk;
   a.lddv = lddv;
+  if (rope) {
+    a.rope = 1;
+    a.rope_n_pos = rope->n_pos;
+    a.rope_cs = rope->cs;
+    a.rope_pos = rope->positions;
+  }
   const hipStream_t hs = (hipStream_t)stream;
   const int64_t nb = (S + kB - 1) / kB;
   const unsigned dot_grid = (unsigned)((T * n_q * (D / 8) + kThreads - 1) / kThreads);
@@ -840,6 +889,30 @@ lsn_status attention_bwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, in
     hipLaunchKernelGGL(k_attn_bwd_q<64>, dim3(q_grid), dim3(kFwdThreads), 0, hs, a);
   }
   return check_hip(hipGetLastError(), "attention backward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+lsn_status attention_bwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, int32_t head_dim, const uint16_t *q,
+                         int64_t ldq, const uint16_t *k, int64_t ldk, const uint16_t *v, int64_t ldv,
+                         const uint16_t *o, int64_t ldo, const float *lse, const uint16_t *dO, int64_t lddo,
+                         float scale, uint16_t *dq, int64_t lddq, uint16_t *dk, int64_t lddk, uint16_t *dv,
+                         int64_t lddv, void *ws, size_t ws_bytes, void *stream) {
+  return attn_bwd_impl("attention_bwd", n_seq, S, n_q, n_kv, head_dim, q, ldq, k, ldk, v, ldv, o, ldo, lse, dO, lddo,
+                       scale, dq, lddq, dk, lddk, dv, lddv, ws, ws_bytes, nullptr, stream);
+}
+
+lsn_status attention_bwd_rope(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                              const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk, const uint16_t *v,
+                              int64_t ldv, const uint16_t *o, int64_t ldo, const float *lse, const uint16_t *dO,
+                              int64_t lddo, float scale, uint16_t *dq, int64_t lddq, uint16_t *dk, int64_t lddk,
+                              uint16_t *dv, int64_t lddv, void *ws, size_t ws_bytes, const lsn_rope *rope,
+                              void *stream) {
+  if (!rope) return fail(LSN_E_ARG, "attention_bwd_rope: null rotation");
+  return attn_bwd_impl("attention_bwd_rope", n_seq, S, n_q, n_kv, head_dim, q, ldq, k, ldk, v, ldv, o, ldo, lse, dO,
+                       lddo, scale, dq, lddq, dk, lddk, dv, lddv, ws, ws_bytes, rope, stream);
 }
 
 }  // extern "C"

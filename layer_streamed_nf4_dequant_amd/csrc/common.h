@@ -56,5 +56,10 @@ lsn_status launch_pack_second(const float *absmax, int64_t n_blocks, float mu, i
 // dequantise n (<= kMaxDqJobs) tensors into out[g] in one launch (all in the same layout)
 constexpr int kMaxDqJobs = 8;
 lsn_status launch_dequant(int n, const lsn_nf4 *w, void *const *out, int out_dtype, hipStream_t s);
+// rotary embedding in place from a (cos, sin) table [n_pos][head_dim / 2] (rope_table), on
+// n_heads heads at the start of each of T rows (row stride ld); sign -1: the inverse rotation.
+// head_dim / 2 a multiple of 8, ld a multiple of 8, x and cs 16-byte aligned.
+lsn_status launch_rope_tab(int64_t T, int n_heads, int head_dim, uint16_t *x, int64_t ld, const int32_t *positions,
+                           const float *cs, int n_pos, float sign, hipStream_t s);
 
 }  // namespace lsn

@@ -8,7 +8,28 @@ namespace lsn {
 
 enum { GEMM_NT = 0, GEMM_NN = 1 };        // forward Y = act W^T ; backward dX = act W
 enum { W_IS_NF4 = 0, W_IS_BF16 = 1 };
-enum { EPI_BF16 = 0, EPI_F32_ADD = 1, EPI_F32_SET = 2 };   // bf16 store, fp32 add into, fp32 store
+// output epilogues: bf16 store, fp32 add into, fp32 store; and two that apply the SwiGLU of a
+// decoder layer's MLP to a bf16 result (see EpiOps)
+enum { EPI_BF16 = 0, EPI_F32_ADD = 1, EPI_F32_SET = 2, EPI_SWIGLU = 3, EPI_SWIGLU_BWD = 4 };
+
+// Operands of the decoder-glue epilogues (bf16 outputs only). Every one of them applies to the
+// rounded bf16 product exactly what the standalone glue kernel would apply to the stored product,
+// with the same arithmetic (glue_math.h), so fused and unfused results have the same bits.
+struct EpiOps {
+  // rotary embedding of the rounded output, on segments flagged `rope` (columns = whole heads)
+  const float *rope_cs;        // (cos, sin) table [n_pos][rope_dim / 2], 16-byte aligned
+  const int32_t *positions;    // [M]: table row of each output row (clamped to [0, n_pos))
+  int n_pos, rope_dim;         // rope_dim 64 or 128
+  // EPI_SWIGLU: the one segment is the gate member of a gate/up pair sharing the activation; a
+  // tile computes 128 gate and the same 128 up columns; out (gate) and out2 (up) may be null
+  const uint16_t *w2, *lr_w2, *lr_act2;   // the up member's W [N][K], B [N][r], U [M][r]
+  uint16_t *out2;              // up [M][N] or null
+  uint16_t *mout;              // bf16( silu(gate) up ) [M][N]
+  // EPI_SWIGLU_BWD: the product is dm (the gradient of the SwiGLU output, rounded to bf16, not
+  // stored); the epilogue stores the gradients of its inputs
+  const uint16_t *gate, *up;   // [M][N]
+  uint16_t *dgate, *dup;       // [M][N]
+};
 
 struct GemmArgs {
   int64_t M;            // rows of act and out (tokens)
@@ -31,6 +52,8 @@ struct GemmArgs {
   float scale;
   int adapters;
   void *out;            // bf16 or fp32 [M][Nout]
+  const uint16_t *res;  // EPI_BF16: null, or bf16 [M][Nout] added to the rounded product
+  EpiOps x;             // EPI_SWIGLU_BWD operands (the rotary and SwiGLU-forward ones are unused)
 };
 
 lsn_status launch_gemm(int layout, int wkind, int epi, GemmArgs a, hipStream_t s);
@@ -45,6 +68,8 @@ struct GemmSeg {
   const uint16_t *lr_w;    // LoRA B [N][r]
   const uint16_t *lr_act;  // U [M][r]
   void *out;               // [M][N]
+  const uint16_t *res;     // EPI_BF16: null, or bf16 [M][N] added to the rounded product
+  int rope;                // EPI_BF16: rotary embedding of the rounded product (DirectArgs x)
 };
 // reduction segments: out = sum_p ( act_p W_p^T + s lr_act_p lr_w_p^T ), one output, the K-steps
 // of the segments run back to back (each K_p % 64 == 0)
@@ -69,6 +94,7 @@ struct DirectArgs {
   int b_red_major;       // B operand stored [K][N] (N contiguous) instead of [N][K]
   int ksplit;            // > 1: split-K into fp32 partials out + s M N (reduction-major B, fp32 store)
   int scale_pow2;        // set by launch_gemm_direct
+  EpiOps x;
 };
 lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s);
 // zero bytes (a multiple of 16) at p, with a kernel (no memset node in captured graphs)

@@ -33,6 +33,7 @@
 
 #include "common.h"
 #include "gemm.h"
+#include "glue_math.h"
 
 namespace lsn {
 namespace {
@@ -427,7 +428,21 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs a) {
             uint2 o;
             o.x = pack_bf16x2(v0, v1);
             o.y = pack_bf16x2(v2, v3);
+            if (a.res) {
+              const uint2 r = *reinterpret_cast<const uint2 *>(a.res + m * a.Nout + n);
+              o.x = add_bf16_word(r.x, o.x);
+              o.y = add_bf16_word(r.y, o.y);
+            }
             *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + m * a.Nout + n) = o;
+          } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+            const uint2 dm = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            const uint2 gv = *reinterpret_cast<const uint2 *>(a.x.gate + m * a.Nout + n);
+            const uint2 uv = *reinterpret_cast<const uint2 *>(a.x.up + m * a.Nout + n);
+            uint2 dg, du;
+            swiglu_bwd_word(gv.x, uv.x, dm.x, dg.x, du.x);
+            swiglu_bwd_word(gv.y, uv.y, dm.y, dg.y, du.y);
+            *reinterpret_cast<uint2 *>(a.x.dgate + m * a.Nout + n) = dg;
+            *reinterpret_cast<uint2 *>(a.x.dup + m * a.Nout + n) = du;
           } else {
             floatx4_t *o = reinterpret_cast<floatx4_t *>(reinterpret_cast<float *>(a.out) + m * a.Nout + n);
             floatx4_t cur = *o;
@@ -588,8 +603,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     if (q < a.nseg && nt >= a.seg[q].ntile0) sidx = q;
   const GemmSeg sg = a.seg[sidx];
   nt -= sg.ntile0;
+  // a gate/up pair: the tile's B rows 0..127 are gate rows n0.., rows 128..255 the same up rows
+  constexpr bool PAIR = EPI == EPI_SWIGLU;
+  static_assert(!PAIR || (!KSEG && !BT && !SPLIT), "the gate/up pair is a plain forward product");
   const int64_t m0 = mt * BM;
-  const int64_t n0 = nt * BN;
+  const int64_t n0 = nt * (PAIR ? BN / 2 : BN);
 
   floatx16_t acc[4][4];
 #pragma unroll
@@ -616,15 +634,17 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     rs_b = make_rsrc(a.kseg[0].w, sg.N * a.kseg[0].K * 2);
     make_direct_rows8(da, a.M, a.kseg[0].K, m0, wave, lane);
   } else {
+    // (pair: waves 0-1 fill the gate half of the B tile, waves 2-3 the up half)
+    const uint16_t *wb = PAIR && wave >= 2 ? a.x.w2 : sg.w;
     rs_a = make_rsrc(a.act + kt0 * DBK, a.M * a.K * 2 - kt0 * DBK * 2);
-    rs_b = BT ? make_rsrc(sg.w + kt0 * DBK * sg.N, (a.K - kt0 * DBK) * sg.N * 2)
-              : make_rsrc(sg.w + kt0 * DBK, sg.N * a.K * 2 - kt0 * DBK * 2);
+    rs_b = BT ? make_rsrc(wb + kt0 * DBK * sg.N, (a.K - kt0 * DBK) * sg.N * 2)
+              : make_rsrc(wb + kt0 * DBK, sg.N * a.K * 2 - kt0 * DBK * 2);
     make_direct_rows8(da, a.M, a.K, m0, wave, lane);
   }
   if constexpr (BT)
     make_direct_rows8_t(db, sg.N, n0, wave, lane);   // the same for every reduction segment
-  else
-    make_direct_rows8(db, sg.N, KSEG ? a.kseg[0].K : a.K, n0, wave, lane);
+  else   // (pair: the up half's LDS rows 128.. hold up rows n0..)
+    make_direct_rows8(db, sg.N, KSEG ? a.kseg[0].K : a.K, PAIR && wave >= 2 ? n0 - 128 : n0, wave, lane);
   // bytes from one K-step of B to the next
   const int64_t b_step_bytes = BT ? (int64_t)DBK * sg.N * 2 : (int64_t)DBK * 2;
   // byte offset along K of global step `step` inside its segment (moving pa / pb forward)
@@ -664,8 +684,10 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   if (a.adapters) {
 #pragma unroll 1
    for (int p = 0; p < (KSEG ? a.nkseg : 1); ++p) {
-    const uint16_t *lr_act = KSEG ? a.kseg[p].lr_act : sg.lr_act;
-    const uint16_t *lr_w = KSEG ? a.kseg[p].lr_w : sg.lr_w;
+    // (pair: the waves of the up half (wn = 1) take the up member's U and B)
+    const uint16_t *lr_act = KSEG ? a.kseg[p].lr_act : PAIR && wn ? a.x.lr_act2 : sg.lr_act;
+    const uint16_t *lr_w = KSEG ? a.kseg[p].lr_w : PAIR && wn ? a.x.lr_w2 : sg.lr_w;
+    const int64_t nw0 = PAIR ? n0 : n0 + wn * 128;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (16 * h >= a.r) break;
@@ -680,7 +702,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int64_t n = n0 + wn * 128 + 32 * j + (lane & 31);
+        const int64_t n = nw0 + 32 * j + (lane & 31);
         u32x4_t v = {0, 0, 0, 0};
         if (n < sg.N && jl < a.r) v = *reinterpret_cast<const u32x4_t *>(lr_w + n * a.r + jl);
         lb[j] = as_bf16x8(v);
@@ -796,7 +818,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   wait_vm_all();
 
   // ---- epilogue: lane holds row m = 32 i + lane%32, columns 32 j + 8 g + 4 (lane/32) .. +3 ----
-  if constexpr (EPI == EPI_BF16) {
+  if constexpr (EPI == EPI_BF16 || EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD) {
     // through LDS (free once every wave is past the loop): the 256 x 256 bf16 tile is written
     // with 8-byte stores at a 528-byte row pitch (2-way bank conflicts at most), then read back
     // as 16-byte row chunks so that every global store is a 16-byte piece of a 512-byte row run
@@ -817,15 +839,80 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
         }
     }
     __syncthreads();
+    if constexpr (EPI == EPI_SWIGLU) {
+      // row r of the tile: gate columns n0 .. n0+127 in chunks 0-15, the same up columns in
+      // chunks 16-31; a thread takes chunk c of both halves, 16 rows per pass
+      const int c = t & 15;
+      const int64_t n = n0 + 8 * c;
+#pragma unroll 4
+      for (int p = 0; p < BM / (NT / 16); ++p) {
+        const int r = p * (NT / 16) + (t >> 4);
+        const int64_t m = m0 + r;
+        const u32x4_t gv = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + c * 16);
+        const u32x4_t uv = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + (c + 16) * 16);
+        if (m < a.M && n < sg.N) {
+          const int64_t o = m * sg.N + n;
+          if (sg.out) __builtin_nontemporal_store(gv, reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(sg.out) + o));
+          if (a.x.out2) __builtin_nontemporal_store(uv, reinterpret_cast<u32x4_t *>(a.x.out2 + o));
+          __builtin_nontemporal_store(swiglu8(gv, uv), reinterpret_cast<u32x4_t *>(a.x.mout + o));
+        }
+      }
+      return;
+    }
+    if constexpr (EPI == EPI_BF16) {
+      if (sg.rope) {
+        // rotary embedding of the rounded tile (columns = whole heads of D): thread k = t % 16
+        // of a row takes 8 pairs of one head, the chunk at column c1 and its partner D/2 to the
+        // right; 16 rows per pass
+        const int D = a.x.rope_dim, half = D / 2, cph = half / 8, k = t & 15;
+        const int c1 = (k / cph) * D + 8 * (k % cph), c2 = c1 + half;
+        const int64_t n1 = n0 + c1;
+#pragma unroll 2
+        for (int p = 0; p < BM / (NT / 16); ++p) {
+          const int r = p * (NT / 16) + (t >> 4);
+          const int64_t m = m0 + r;
+          const u32x4_t x1 = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + c1 * 2);
+          const u32x4_t x2 = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + c2 * 2);
+          if (m < a.M && n1 < sg.N) {
+            const int pos = min(max(a.x.positions[m], 0), a.x.n_pos - 1);
+            float cv[8], sv[8];
+            rope_load8(a.x.rope_cs + (int64_t)pos * D + 16 * (k % cph), 1.0f, cv, sv);
+            u32x4_t y1, y2;
+            rope_chunk8(x1, x2, cv, sv, y1, y2);
+            uint16_t *o = reinterpret_cast<uint16_t *>(sg.out) + m * sg.N + n1;
+            __builtin_nontemporal_store(y1, reinterpret_cast<u32x4_t *>(o));
+            __builtin_nontemporal_store(y2, reinterpret_cast<u32x4_t *>(o + half));
+          }
+        }
+        return;
+      }
+    }
     const int chunk = t & 31;
     const int64_t n = n0 + 8 * chunk;
 #pragma unroll 4
     for (int p = 0; p < BM / (NT / 32); ++p) {
       const int r = p * (NT / 32) + (t >> 5);
       const int64_t m = m0 + r;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + chunk * 16);
-      if (m < a.M && n < sg.N)
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(sg.out) + m * sg.N + n));
+      u32x4_t v = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + chunk * 16);
+      if (m < a.M && n < sg.N) {
+        const int64_t o = m * sg.N + n;
+        if constexpr (EPI == EPI_SWIGLU_BWD) {
+          // v is dm; the gradients of the SwiGLU's inputs at the same elements
+          const u32x4_t gv = *reinterpret_cast<const u32x4_t *>(a.x.gate + o);
+          const u32x4_t uv = *reinterpret_cast<const u32x4_t *>(a.x.up + o);
+          u32x4_t dg, du;
+          swiglu8_bwd(gv, uv, v, dg, du);
+          __builtin_nontemporal_store(dg, reinterpret_cast<u32x4_t *>(a.x.dgate + o));
+          __builtin_nontemporal_store(du, reinterpret_cast<u32x4_t *>(a.x.dup + o));
+        } else {
+          if (sg.res) {
+            const u32x4_t rv = *reinterpret_cast<const u32x4_t *>(sg.res + o);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = add_bf16_word(rv[q], v[q]);
+          }
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(sg.out) + o));
+        }
+      }
     }
     return;
   }
@@ -862,6 +949,12 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
 constexpr size_t kDirectSmemBytes = 256 * kEpiPitch > 4 * DTILE ? 256 * kEpiPitch : 4 * DTILE;
 static_assert(256 * kEpiPitch <= kDirectSmemBytes, "the epilogue tile must fit in the ring's LDS");
 
+// N tiles of a segment (a gate/up pair: 128 columns of each member per tile)
+int64_t seg_ntiles(int64_t N, int epi) {
+  const int64_t w = epi == EPI_SWIGLU ? BN / 2 : BN;
+  return (N + w - 1) / w;
+}
+
 template <int EPI, bool KSEG, bool BT, bool SPLIT = false>
 lsn_status launch_direct_one(const DirectArgs &a, hipStream_t s) {
   static bool attr_set = false;
@@ -872,7 +965,7 @@ lsn_status launch_direct_one(const DirectArgs &a, hipStream_t s) {
     attr_set = true;
   }
   int64_t ntiles_n = 0;
-  for (int q = 0; q < a.nseg; ++q) ntiles_n += (a.seg[q].N + BN - 1) / BN;
+  for (int q = 0; q < a.nseg; ++q) ntiles_n += seg_ntiles(a.seg[q].N, EPI);
   const int64_t tiles = ((a.M + BM - 1) / BM) * ntiles_n * (SPLIT ? a.ksplit : 1);
   hipLaunchKernelGGL((k_gemm_direct<EPI, KSEG, BT, SPLIT>), dim3((unsigned)tiles), dim3(NT), kDirectSmemBytes, s, a);
   return check_hip(hipGetLastError(), "k_gemm_direct launch");
@@ -901,6 +994,13 @@ template <bool KSEG, bool BT>
 lsn_status launch_direct_epi(const DirectArgs &a, int epi, hipStream_t s) {
   if (epi == EPI_BF16) return launch_direct_one<EPI_BF16, KSEG, BT>(a, s);
   if (epi == EPI_F32_ADD) return launch_direct_one<EPI_F32_ADD, KSEG, BT>(a, s);
+  if constexpr (!KSEG) {
+    if (epi == EPI_SWIGLU_BWD) return launch_direct_one<EPI_SWIGLU_BWD, false, BT>(a, s);
+    if constexpr (!BT) {
+      if (epi == EPI_SWIGLU) return launch_direct_one<EPI_SWIGLU, false, false>(a, s);
+    }
+  }
+  if (epi != EPI_F32_SET) return fail(LSN_E_ARG, "gemm_direct: epilogue %d not available for this operand layout", epi);
   return launch_direct_one<EPI_F32_SET, KSEG, BT>(a, s);
 }
 }  // namespace
@@ -915,8 +1015,13 @@ lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s) {
   int64_t t0 = 0;
   for (int q = 0; q < a.nseg; ++q) {
     a.seg[q].ntile0 = t0;
-    t0 += (a.seg[q].N + BN - 1) / BN;
+    t0 += seg_ntiles(a.seg[q].N, epi);
   }
+  // the glue epilogues: SwiGLU on one plain forward segment, its backward on one segment
+  if ((epi == EPI_SWIGLU || epi == EPI_SWIGLU_BWD) && (a.nseg != 1 || a.nkseg > 0 || a.ksplit > 1))
+    return fail(LSN_E_ARG, "gemm_direct: the SwiGLU epilogues take one plain segment");
+  if (epi == EPI_SWIGLU && a.b_red_major)
+    return fail(LSN_E_ARG, "gemm_direct: the SwiGLU forward epilogue needs W as [N][K]");
   if (a.nkseg > 0) {
     int64_t step = 0;
     for (int p = 0; p < a.nkseg; ++p) {
@@ -982,6 +1087,9 @@ lsn_status launch_gemm(int layout, int wkind, int epi, GemmArgs a, hipStream_t s
     if (wkind == W_IS_NF4) return launch_one<GEMM_NT, W_IS_NF4, EPI_BF16>(a, s);
     return launch_one<GEMM_NT, W_IS_BF16, EPI_BF16>(a, s);
   }
+  if (epi == EPI_SWIGLU_BWD)
+    return wkind == W_IS_NF4 ? launch_one<GEMM_NN, W_IS_NF4, EPI_SWIGLU_BWD>(a, s)
+                             : launch_one<GEMM_NN, W_IS_BF16, EPI_SWIGLU_BWD>(a, s);
   if (wkind == W_IS_NF4)
     return epi == EPI_BF16 ? launch_one<GEMM_NN, W_IS_NF4, EPI_BF16>(a, s) : launch_one<GEMM_NN, W_IS_NF4, EPI_F32_ADD>(a, s);
   return epi == EPI_BF16 ? launch_one<GEMM_NN, W_IS_BF16, EPI_BF16>(a, s) : launch_one<GEMM_NN, W_IS_BF16, EPI_F32_ADD>(a, s);

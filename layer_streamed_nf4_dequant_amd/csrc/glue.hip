@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "common.h"
+#include "glue_math.h"
 
 namespace lsn {
 lsn_status require_gfx950();
@@ -20,8 +21,6 @@ namespace {
 constexpr int kGlueThreads = 256;
 constexpr int kMaxRopePairs = 256;   // head_dim <= 512
 
-__device__ __forceinline__ float bf16f(uint16_t h) { return bf16_bits_to_f32(h); }
-__device__ __forceinline__ uint16_t f2bf(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu); }
 
 // sum over the NT threads of a workgroup: a fixed butterfly in each wave (every lane of a wave
 // ends with the same bits: each level adds the same two values on both lanes of a pair), then
@@ -147,11 +146,6 @@ struct RopeTable {
   float inv_freq[kMaxRopePairs];
 };
 
-__device__ __forceinline__ void rope_pair(float x1, float x2, float c, float s, float &y1, float &y2) {
-  y1 = __fsub_rn(__fmul_rn(x1, c), __fmul_rn(x2, s));
-  y2 = __fadd_rn(__fmul_rn(x2, c), __fmul_rn(x1, s));
-}
-
 // In place on n_heads heads of width 2 half in each row (row stride ld elements): pair
 // (i, i + half) of a head turns by pos * inv_freq[i] (minus that for the backward).
 // Vector form (half % 8 == 0, 16-byte aligned rows): a thread takes 8 consecutive pairs of
@@ -173,9 +167,8 @@ __global__ __launch_bounds__(kGlueThreads) void k_rope_v(int64_t T, int n_heads,
   float c[8], sn[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float a = __fmul_rn(p, tab.inv_freq[blk * 8 + e]);
     float sv, cv;
-    sincosf(a, &sv, &cv);
+    rope_cos_sin(p, tab.inv_freq[blk * 8 + e], cv, sv);
     c[e] = cv;
     sn[e] = __fmul_rn(sign, sv);
   }
@@ -184,23 +177,52 @@ __global__ __launch_bounds__(kGlueThreads) void k_rope_v(int64_t T, int n_heads,
     uint16_t *base = x + row * ld + (int64_t)h * 2 * half + blk * 8;
     u32x4_t *p1 = reinterpret_cast<u32x4_t *>(base);
     u32x4_t *p2 = reinterpret_cast<u32x4_t *>(base + half);
-    const u32x4_t v1 = *p1, v2 = *p2;
     u32x4_t o1, o2;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float y1[2], y2[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int e = 2 * q + hh;
-        rope_pair(bf16f((uint16_t)(v1[q] >> (16 * hh))), bf16f((uint16_t)(v2[q] >> (16 * hh))), c[e], sn[e],
-                  y1[hh], y2[hh]);
-      }
-      o1[q] = pack_bf16x2(y1[0], y1[1]);
-      o2[q] = pack_bf16x2(y2[0], y2[1]);
-    }
+    rope_chunk8(*p1, *p2, c, sn, o1, o2);
     *p1 = o1;
     *p2 = o2;
   }
+}
+
+// (cos, sin) of every position's angles: cs[p][i] = (cos a, sin a), a = fl32(p f_i), for
+// p < n_pos, i < half; the same arithmetic as the kernels above, so rotations driven by the table
+// give their bits
+__global__ __launch_bounds__(kGlueThreads) void k_rope_table(int64_t n, int half, RopeTable tab,
+                                                             float *__restrict__ cs) {
+  const int64_t item = (int64_t)blockIdx.x * kGlueThreads + threadIdx.x;
+  if (item >= n) return;
+  const int64_t p = item / half;
+  const int i = (int)(item - p * half);
+  float c, sv;
+  rope_cos_sin((float)p, tab.inv_freq[i], c, sv);
+  cs[2 * item] = c;
+  cs[2 * item + 1] = sv;
+}
+
+// In place, driven by a (cos, sin) table [n_pos][half]: a thread takes 8 consecutive pairs of one
+// head of one row (half % 8 == 0, 16-byte aligned rows); positions outside the table are clamped
+// to it (they only guard the table read).
+__global__ __launch_bounds__(kGlueThreads) void k_rope_tab(int64_t T, int n_heads, int half, int64_t ld,
+                                                           uint16_t *__restrict__ x,
+                                                           const int32_t *__restrict__ positions,
+                                                           const float *__restrict__ cs, int n_pos, float sign) {
+  const int nblk = half / 8;
+  const int64_t per_row = (int64_t)n_heads * nblk;
+  const int64_t item = (int64_t)blockIdx.x * kGlueThreads + threadIdx.x;
+  if (item >= T * per_row) return;
+  const int64_t row = item / per_row;
+  const int rem = (int)(item - row * per_row);
+  const int h = rem / nblk, blk = rem - h * nblk;
+  const int pos = min(max(positions[row], 0), n_pos - 1);
+  float c[8], sn[8];
+  rope_load8(cs + ((int64_t)pos * half + blk * 8) * 2, sign, c, sn);
+  uint16_t *base = x + row * ld + (int64_t)h * 2 * half + blk * 8;
+  u32x4_t *p1 = reinterpret_cast<u32x4_t *>(base);
+  u32x4_t *p2 = reinterpret_cast<u32x4_t *>(base + half);
+  u32x4_t o1, o2;
+  rope_chunk8(*p1, *p2, c, sn, o1, o2);
+  *p1 = o1;
+  *p2 = o2;
 }
 
 // Scalar form for any even head width: one thread per pair.
@@ -214,9 +236,8 @@ __global__ __launch_bounds__(kGlueThreads) void k_rope_s(int64_t T, int n_heads,
   const int64_t row = item / per_row;
   const int p = (int)(item - row * per_row);
   const int head = p / half, i = p - head * half;
-  const float a = __fmul_rn((float)positions[row], tab.inv_freq[i]);
   float sv, cv;
-  sincosf(a, &sv, &cv);
+  rope_cos_sin((float)positions[row], tab.inv_freq[i], cv, sv);
   uint16_t *xr = x + row * ld + (int64_t)head * 2 * half;
   float y1, y2;
   rope_pair(bf16f(xr[i]), bf16f(xr[i + half]), cv, __fmul_rn(sign, sv), y1, y2);
@@ -224,24 +245,7 @@ __global__ __launch_bounds__(kGlueThreads) void k_rope_s(int64_t T, int n_heads,
   xr[i + half] = f2bf(y2);
 }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return __fdiv_rn(1.0f, __fadd_rn(1.0f, expf(-z))); }
-
 constexpr int kEltChunks = 2;   // SwiGLU: 16-byte chunks (8 values) per thread, loads issued together
-
-__device__ __forceinline__ u32x4_t swiglu8(u32x4_t gv, u32x4_t uv) {
-  u32x4_t o;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float t[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float z = bf16f((uint16_t)(gv[q] >> (16 * h)));
-      t[h] = __fmul_rn(__fmul_rn(z, sigmoidf_(z)), bf16f((uint16_t)(uv[q] >> (16 * h))));
-    }
-    o[q] = pack_bf16x2(t[0], t[1]);
-  }
-  return o;
-}
 
 // m = bf16( silu(g) u ); thread chunks c0 and c0 + kGlueThreads of its workgroup's range
 __global__ __launch_bounds__(kGlueThreads) void k_swiglu_fwd(int64_t n8, const uint16_t *__restrict__ g,
@@ -261,25 +265,6 @@ __global__ __launch_bounds__(kGlueThreads) void k_swiglu_fwd(int64_t n8, const u
   for (int k = 0; k < kEltChunks; ++k) {
     const int64_t c = c0 + k * kGlueThreads;
     if (c < n8) reinterpret_cast<u32x4_t *>(m)[c] = swiglu8(gv[k], uv[k]);
-  }
-}
-
-__device__ __forceinline__ void swiglu8_bwd(u32x4_t gv, u32x4_t uv, u32x4_t dv, u32x4_t &og, u32x4_t &ou) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float tg[2], tu[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float z = bf16f((uint16_t)(gv[q] >> (16 * h)));
-      const float uu = bf16f((uint16_t)(uv[q] >> (16 * h)));
-      const float d = bf16f((uint16_t)(dv[q] >> (16 * h)));
-      const float sg = sigmoidf_(z);
-      const float dsilu = __fmul_rn(sg, __fadd_rn(1.0f, __fmul_rn(z, __fsub_rn(1.0f, sg))));
-      tg[h] = __fmul_rn(__fmul_rn(d, uu), dsilu);
-      tu[h] = __fmul_rn(d, __fmul_rn(z, sg));
-    }
-    og[q] = pack_bf16x2(tg[0], tg[1]);
-    ou[q] = pack_bf16x2(tu[0], tu[1]);
   }
 }
 
@@ -321,9 +306,7 @@ __global__ __launch_bounds__(kGlueThreads) void k_add_bf16(int64_t n8, const uin
   const u32x4_t x = reinterpret_cast<const u32x4_t *>(a)[c], y = reinterpret_cast<const u32x4_t *>(b)[c];
   u32x4_t o;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    o[q] = pack_bf16x2(__fadd_rn(bf16f((uint16_t)x[q]), bf16f((uint16_t)y[q])),
-                       __fadd_rn(bf16f((uint16_t)(x[q] >> 16)), bf16f((uint16_t)(y[q] >> 16))));
+  for (int q = 0; q < 4; ++q) o[q] = add_bf16_word(x[q], y[q]);
   reinterpret_cast<u32x4_t *>(out)[c] = o;
 }
 
@@ -419,6 +402,45 @@ lsn_status rmsnorm_bwd(int64_t T, int64_t H, const uint16_t *x, const uint16_t *
   return check_hip(hipGetLastError(), "k_rmsnorm_bwd launch");
 }
 
+}  // extern "C"
+
+namespace lsn {
+namespace {
+// f_i = theta^(-2i/d) in fp64, rounded to fp32 (the frequencies every rotation uses)
+RopeTable rope_freqs(float theta, int head_dim) {
+  RopeTable tab{};
+  for (int i = 0; i < head_dim / 2; ++i) tab.inv_freq[i] = (float)std::pow((double)theta, -2.0 * i / head_dim);
+  return tab;
+}
+}  // namespace
+
+lsn_status launch_rope_tab(int64_t T, int n_heads, int head_dim, uint16_t *x, int64_t ld, const int32_t *positions,
+                           const float *cs, int n_pos, float sign, hipStream_t s) {
+  const int half = head_dim / 2;
+  if (half % 8 || ld % 8 || ((uintptr_t)x & 15) || ((uintptr_t)cs & 15) || n_pos < 1) return LSN_E_ARG;
+  const int64_t items = T * n_heads * (half / 8);
+  hipLaunchKernelGGL(k_rope_tab, dim3((unsigned)((items + kGlueThreads - 1) / kGlueThreads)), dim3(kGlueThreads), 0, s,
+                     T, n_heads, half, ld, x, positions, cs, n_pos, sign);
+  return check_hip(hipGetLastError(), "k_rope_tab launch");
+}
+}  // namespace lsn
+
+extern "C" {
+
+lsn_status rope_table(int32_t n_pos, int32_t head_dim, float theta, float *cs, void *stream) {
+  if (n_pos < 1 || n_pos > (1 << 24) || head_dim < 2 || head_dim % 2 || head_dim / 2 > kMaxRopePairs)
+    return fail(LSN_E_ARG, "rope_table: need 1 <= n_pos <= 2^24 and an even head_dim <= %d", 2 * kMaxRopePairs);
+  if (!cs || ((uintptr_t)cs & 15)) return fail(LSN_E_ARG, "rope_table: cs null or not 16-byte aligned");
+  if (!(theta > 1.0f) || !std::isfinite(theta)) return fail(LSN_E_ARG, "rope_table: theta must be finite and > 1");
+  lsn_status st = require_gfx950();
+  if (st != LSN_OK) return st;
+  const int half = head_dim / 2;
+  const int64_t n = (int64_t)n_pos * half;
+  hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + kGlueThreads - 1) / kGlueThreads)), dim3(kGlueThreads), 0,
+                     (hipStream_t)stream, n, half, rope_freqs(theta, head_dim), cs);
+  return check_hip(hipGetLastError(), "k_rope_table launch");
+}
+
 lsn_status rope_apply(int64_t T, int32_t n_heads, int32_t head_dim, uint16_t *x, int64_t ld, const int32_t *positions,
                       float theta, int32_t inverse, void *stream) {
   if (T < 1 || n_heads < 1 || head_dim < 2 || head_dim % 2 || head_dim / 2 > kMaxRopePairs)
@@ -430,9 +452,8 @@ lsn_status rope_apply(int64_t T, int32_t n_heads, int32_t head_dim, uint16_t *x,
     return fail(LSN_E_ARG, "rope_apply: more than 2^37 pairs in one call");
   lsn_status st = require_gfx950();
   if (st != LSN_OK) return st;
-  RopeTable tab{};
+  const RopeTable tab = rope_freqs(theta, head_dim);
   const int half = head_dim / 2;
-  for (int i = 0; i < half; ++i) tab.inv_freq[i] = (float)std::pow((double)theta, -2.0 * i / head_dim);
   const bool vec = half % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x & 15) == 0;
   if (vec) {
     // heads per thread: as many as keep the grid at >= 2048 workgroups (up to 8), so the sine

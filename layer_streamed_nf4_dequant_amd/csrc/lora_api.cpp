@@ -153,21 +153,26 @@ size_t lora_linear_ws_bytes(int64_t T, int64_t K, int64_t N, int64_t r) {
   return bwd_layout(nullptr, T, K, N, r).bytes;
 }
 
-lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uint16_t *X, uint16_t *Y,
-                           uint16_t *U, void *ws, size_t ws_bytes, void *stream) {
-  (void)ws;
-  (void)ws_bytes;
-  lsn_status st = check_linear(L, "lora_linear_fwd");
+}  // extern "C"
+
+namespace {
+
+// The forward of one linear; res (may be null): the residual added to the rounded product in the
+// epilogue (res == Y allowed, in place).
+lsn_status fwd_impl(const char *what, const lsn_lora_linear *L, int32_t adapters, const uint16_t *X, uint16_t *Y,
+                    uint16_t *U, const uint16_t *res, hipStream_t s) {
+  lsn_status st = check_linear(L, what);
   if (st != LSN_OK) return st;
   if (L->W.kind == LSN_W_BF16_T)
-    return fail(LSN_E_ARG, "lora_linear_fwd: the transposed bf16 layout is for the backward only");
+    return fail(LSN_E_ARG, "%s: the transposed bf16 layout is for the backward only", what);
   const int64_t T = L->T, K = L->K, N = L->N, r = L->r;
   if (!X || !Y || !aligned16(X) || !aligned16(Y))
-    return fail(LSN_E_ARG, "lora_linear_fwd: X and Y must be non-null and 16-byte aligned");
+    return fail(LSN_E_ARG, "%s: X and Y must be non-null and 16-byte aligned", what);
   if (adapters != LSN_ADAPTERS_OFF && adapters != LSN_ADAPTERS_ON && adapters != LSN_ADAPTERS_U_READY)
-    return fail(LSN_E_ARG, "lora_linear_fwd: unknown adapters mode %d", adapters);
+    return fail(LSN_E_ARG, "%s: unknown adapters mode %d", what, adapters);
   if (adapters && (!U || !aligned16(U)))
-    return fail(LSN_E_ARG, "lora_linear_fwd: U must be non-null and 16-byte aligned when adapters are on");
+    return fail(LSN_E_ARG, "%s: U must be non-null and 16-byte aligned when adapters are on", what);
+  if (res && !aligned16(res)) return fail(LSN_E_ARG, "%s: residual not 16-byte aligned", what);
   const size_t yb = (size_t)(T * N * 2), ub = (size_t)(T * r * 2);
   const void *ins[6] = {X, L->A, L->B};
   size_t inb[6] = {(size_t)(T * K * 2), (size_t)(r * K * 2), (size_t)(N * r * 2)};
@@ -175,11 +180,13 @@ lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uin
   for (int i = 0; i < n_in; ++i) {
     if (ranges_overlap(Y, yb, ins[i], inb[i]) ||
         (adapters == LSN_ADAPTERS_ON && ranges_overlap(U, ub, ins[i], inb[i])))
-      return fail(LSN_E_ARG, "lora_linear_fwd: an output overlaps an input");
+      return fail(LSN_E_ARG, "%s: an output overlaps an input", what);
   }
-  if (adapters && ranges_overlap(Y, yb, U, ub)) return fail(LSN_E_ARG, "lora_linear_fwd: Y overlaps U");
+  if (adapters && ranges_overlap(Y, yb, U, ub)) return fail(LSN_E_ARG, "%s: Y overlaps U", what);
+  if (res && ((res != Y && ranges_overlap(res, yb, Y, yb)) ||
+              (adapters == LSN_ADAPTERS_ON && ranges_overlap(res, yb, U, ub))))
+    return fail(LSN_E_ARG, "%s: the residual overlaps an output (other than being Y itself)", what);
   if ((st = require_gfx950()) != LSN_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
   if (adapters == LSN_ADAPTERS_ON && (st = launch_rowproj(X, T, K, L->A, (int)r, U, s)) != LSN_OK) return st;
   if (L->W.kind == LSN_W_BF16) {
     DirectArgs d{};
@@ -192,6 +199,7 @@ lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uin
     d.seg[0].lr_w = L->B;
     d.seg[0].lr_act = U;
     d.seg[0].out = Y;
+    d.seg[0].res = res;
     d.r = (int)r;
     d.scale = L->scale;
     d.adapters = adapters ? 1 : 0;
@@ -207,67 +215,99 @@ lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uin
   a.lr_w = L->B;
   a.adapters = adapters ? 1 : 0;
   a.out = Y;
+  a.res = res;
   return launch_gemm(GEMM_NT, W_IS_NF4, EPI_BF16, a, s);
 }
 
-lsn_status lora_linear_fwd_group(int32_t n, const lsn_lora_linear *L, int32_t adapters, const uint16_t *X,
-                                 uint16_t *const *Y, uint16_t *const *U, void *ws, size_t ws_bytes, void *stream) {
+bool valid_rope(const lsn_rope *rope) {
+  return rope && rope->cs && aligned16(rope->cs) && rope->positions && rope->n_pos >= 1 &&
+         (rope->head_dim == 64 || rope->head_dim == 128);
+}
+
+// The forwards of n linears sharing X; residual (may be null, entries may be null) and rope_mask
+// as lora_linear_fwd_group_epi.
+lsn_status fwd_group_impl(const char *what, int32_t n, const lsn_lora_linear *L, int32_t adapters, const uint16_t *X,
+                          uint16_t *const *Y, uint16_t *const *U, const uint16_t *const *residual,
+                          uint32_t rope_mask, const lsn_rope *rope, void *ws, size_t ws_bytes, hipStream_t s) {
+  (void)ws;
+  (void)ws_bytes;
   if (n < 1 || n > kMaxSegs || !L || !Y || (adapters && !U))
-    return fail(LSN_E_ARG, "lora_linear_fwd_group: need 1 <= n <= %d and non-null arrays", kMaxSegs);
+    return fail(LSN_E_ARG, "%s: need 1 <= n <= %d and non-null arrays", what, kMaxSegs);
+  if (rope_mask >> n) return fail(LSN_E_ARG, "%s: rope_mask names members past n", what);
+  if (rope_mask && !valid_rope(rope))
+    return fail(LSN_E_ARG, "%s: the rotation needs a 16-byte aligned table, positions, n_pos >= 1 and a head width "
+                           "of 64 or 128", what);
   bool all_bf16 = true;
   for (int g = 0; g < n; ++g) {
-    lsn_status st = check_linear(&L[g], "lora_linear_fwd_group");
+    lsn_status st = check_linear(&L[g], what);
     if (st != LSN_OK) return st;
     if (L[g].T != L[0].T || L[g].K != L[0].K || L[g].r != L[0].r || L[g].scale != L[0].scale)
-      return fail(LSN_E_ARG, "lora_linear_fwd_group: members must share T, K, r and the scale");
+      return fail(LSN_E_ARG, "%s: members must share T, K, r and the scale", what);
     if (L[g].W.kind == LSN_W_BF16_T)
-      return fail(LSN_E_ARG, "lora_linear_fwd_group: the transposed bf16 layout is for the backward only");
+      return fail(LSN_E_ARG, "%s: the transposed bf16 layout is for the backward only", what);
     all_bf16 = all_bf16 && L[g].W.kind == LSN_W_BF16;
+    const uint16_t *res = residual ? residual[g] : nullptr;
+    if (res && !aligned16(res)) return fail(LSN_E_ARG, "%s: residual[%d] not 16-byte aligned", what, g);
+    if ((rope_mask >> g) & 1) {
+      if (res) return fail(LSN_E_ARG, "%s: member %d has both a residual and a rotation", what, g);
+      if (L[g].N % rope->head_dim)
+        return fail(LSN_E_ARG, "%s: member %d's width %lld is not whole heads of %d", what, g, (long long)L[g].N,
+                    rope->head_dim);
+    }
   }
   if (adapters != LSN_ADAPTERS_OFF && adapters != LSN_ADAPTERS_ON && adapters != LSN_ADAPTERS_U_READY)
-    return fail(LSN_E_ARG, "lora_linear_fwd_group: unknown adapters mode %d", adapters);
+    return fail(LSN_E_ARG, "%s: unknown adapters mode %d", what, adapters);
   const int64_t T = L[0].T, K = L[0].K, r = L[0].r;
-  if (!X || !aligned16(X)) return fail(LSN_E_ARG, "lora_linear_fwd_group: X null or not 16-byte aligned");
+  if (!X || !aligned16(X)) return fail(LSN_E_ARG, "%s: X null or not 16-byte aligned", what);
   // every output against every input, and the outputs pairwise
   const void *outs[2 * kMaxSegs];
   size_t outb[2 * kMaxSegs];
   int n_out = 0;
   for (int g = 0; g < n; ++g) {
-    if (!Y[g] || !aligned16(Y[g])) return fail(LSN_E_ARG, "lora_linear_fwd_group: Y[%d] null or not 16-byte aligned", g);
+    if (!Y[g] || !aligned16(Y[g])) return fail(LSN_E_ARG, "%s: Y[%d] null or not 16-byte aligned", what, g);
     outs[n_out] = Y[g];
     outb[n_out++] = (size_t)(T * L[g].N * 2);
     if (adapters) {
       if (!U[g] || !aligned16(U[g]))
-        return fail(LSN_E_ARG, "lora_linear_fwd_group: U[%d] null or not 16-byte aligned", g);
+        return fail(LSN_E_ARG, "%s: U[%d] null or not 16-byte aligned", what, g);
       if (adapters == LSN_ADAPTERS_ON) {
         outs[n_out] = U[g];
         outb[n_out++] = (size_t)(T * r * 2);
       }
     }
   }
+  const size_t tab_b = rope_mask ? (size_t)rope->n_pos * rope->head_dim * 4 : 0;
   for (int o = 0; o < n_out; ++o) {
     if (ranges_overlap(outs[o], outb[o], X, (size_t)(T * K * 2)))
-      return fail(LSN_E_ARG, "lora_linear_fwd_group: an output overlaps X");
+      return fail(LSN_E_ARG, "%s: an output overlaps X", what);
+    if (rope_mask && (ranges_overlap(outs[o], outb[o], rope->cs, tab_b) ||
+                      ranges_overlap(outs[o], outb[o], rope->positions, (size_t)T * 4)))
+      return fail(LSN_E_ARG, "%s: an output overlaps the rotation table or the positions", what);
     for (int p = 0; p < o; ++p)
       if (ranges_overlap(outs[o], outb[o], outs[p], outb[p]))
-        return fail(LSN_E_ARG, "lora_linear_fwd_group: two outputs overlap");
+        return fail(LSN_E_ARG, "%s: two outputs overlap", what);
     for (int g = 0; g < n; ++g) {
       const void *ins[5] = {L[g].A, L[g].B};
       size_t inb[5] = {(size_t)(r * K * 2), (size_t)(L[g].N * r * 2)};
       const int n_in = 2 + w_ranges(&L[g], ins + 2, inb + 2);
       for (int i = 0; i < n_in; ++i)
         if (ranges_overlap(outs[o], outb[o], ins[i], inb[i]))
-          return fail(LSN_E_ARG, "lora_linear_fwd_group: an output overlaps an input");
+          return fail(LSN_E_ARG, "%s: an output overlaps an input", what);
+      // a residual may be its own member's output, nothing else
+      const uint16_t *res = residual ? residual[g] : nullptr;
+      if (res && outs[o] != (const void *)Y[g] && ranges_overlap(outs[o], outb[o], res, (size_t)(T * L[g].N * 2)))
+        return fail(LSN_E_ARG, "%s: residual[%d] overlaps an output other than Y[%d]", what, g, g);
+      if (res && outs[o] == (const void *)Y[g] && res != Y[g] && ranges_overlap(Y[g], outb[o], res, outb[o]))
+        return fail(LSN_E_ARG, "%s: residual[%d] partially overlaps Y[%d]", what, g, g);
     }
   }
   if (adapters == LSN_ADAPTERS_U_READY)
     for (int g = 0; g < n; ++g)
       for (int h = 0; h < n; ++h)
         if (ranges_overlap(Y[g], (size_t)(T * L[g].N * 2), U[h], (size_t)(T * r * 2)))
-          return fail(LSN_E_ARG, "lora_linear_fwd_group: a Y overlaps a U");
+          return fail(LSN_E_ARG, "%s: a Y overlaps a U", what);
   lsn_status st = require_gfx950();
   if (st != LSN_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
   if (adapters == LSN_ADAPTERS_ON) {
     // the down-projections in as few passes over X as the 128-column limit of one pass allows
     for (int g0 = 0; g0 < n;) {
@@ -286,9 +326,16 @@ lsn_status lora_linear_fwd_group(int32_t n, const lsn_lora_linear *L, int32_t ad
   }
   const int mode = adapters ? LSN_ADAPTERS_U_READY : LSN_ADAPTERS_OFF;
   if (!all_bf16) {
-    for (int g = 0; g < n; ++g)
-      if ((st = lora_linear_fwd(&L[g], mode, X, Y[g], adapters ? U[g] : nullptr, ws, ws_bytes, stream)) != LSN_OK)
+    for (int g = 0; g < n; ++g) {
+      if ((st = fwd_impl(what, &L[g], mode, X, Y[g], adapters ? U[g] : nullptr, residual ? residual[g] : nullptr,
+                         s)) != LSN_OK)
         return st;
+      if ((rope_mask >> g) & 1) {
+        st = launch_rope_tab(T, (int)(L[g].N / rope->head_dim), rope->head_dim, Y[g], L[g].N, rope->positions,
+                             rope->cs, rope->n_pos, 1.0f, s);
+        if (st != LSN_OK) return st;
+      }
+    }
     return LSN_OK;
   }
   DirectArgs d{};
@@ -302,6 +349,14 @@ lsn_status lora_linear_fwd_group(int32_t n, const lsn_lora_linear *L, int32_t ad
     d.seg[g].lr_w = L[g].B;
     d.seg[g].lr_act = adapters ? U[g] : nullptr;
     d.seg[g].out = Y[g];
+    d.seg[g].res = residual ? residual[g] : nullptr;
+    d.seg[g].rope = (int)((rope_mask >> g) & 1);
+  }
+  if (rope_mask) {
+    d.x.rope_cs = rope->cs;
+    d.x.positions = rope->positions;
+    d.x.n_pos = rope->n_pos;
+    d.x.rope_dim = rope->head_dim;
   }
   d.r = (int)r;
   d.scale = L[0].scale;
@@ -309,21 +364,148 @@ lsn_status lora_linear_fwd_group(int32_t n, const lsn_lora_linear *L, int32_t ad
   return launch_gemm_direct(d, EPI_BF16, s);
 }
 
+}  // namespace
+
+extern "C" {
+
+lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uint16_t *X, uint16_t *Y,
+                           uint16_t *U, void *ws, size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return fwd_impl("lora_linear_fwd", L, adapters, X, Y, U, nullptr, (hipStream_t)stream);
+}
+
+lsn_status lora_linear_fwd_group(int32_t n, const lsn_lora_linear *L, int32_t adapters, const uint16_t *X,
+                                 uint16_t *const *Y, uint16_t *const *U, void *ws, size_t ws_bytes, void *stream) {
+  return fwd_group_impl("lora_linear_fwd_group", n, L, adapters, X, Y, U, nullptr, 0u, nullptr, ws, ws_bytes,
+                        (hipStream_t)stream);
+}
+
+lsn_status lora_linear_fwd_group_epi(int32_t n, const lsn_lora_linear *L, int32_t adapters, const uint16_t *X,
+                                     uint16_t *const *Y, uint16_t *const *U, const uint16_t *const *residual,
+                                     uint32_t rope_mask, const lsn_rope *rope, void *ws, size_t ws_bytes,
+                                     void *stream) {
+  return fwd_group_impl("lora_linear_fwd_group_epi", n, L, adapters, X, Y, U, residual, rope_mask, rope, ws,
+                        ws_bytes, (hipStream_t)stream);
+}
+
+lsn_status lora_linear_fwd_swiglu(const lsn_lora_linear *Lg, const lsn_lora_linear *Lu, int32_t adapters,
+                                  const uint16_t *X, uint16_t *gate, uint16_t *up, uint16_t *M, uint16_t *Ug,
+                                  uint16_t *Uu, void *ws, size_t ws_bytes, void *stream) {
+  const char *what = "lora_linear_fwd_swiglu";
+  lsn_status st;
+  if ((st = check_linear(Lg, what)) != LSN_OK || (st = check_linear(Lu, what)) != LSN_OK) return st;
+  if (Lg->T != Lu->T || Lg->K != Lu->K || Lg->N != Lu->N || Lg->r != Lu->r || Lg->scale != Lu->scale)
+    return fail(LSN_E_ARG, "%s: gate and up must share T, K, N, r and the scale", what);
+  if (Lg->W.kind == LSN_W_BF16_T || Lu->W.kind == LSN_W_BF16_T)
+    return fail(LSN_E_ARG, "%s: the transposed bf16 layout is for the backward only", what);
+  const bool bf16 = Lg->W.kind == LSN_W_BF16 && Lu->W.kind == LSN_W_BF16;
+  if (!bf16 && (!gate || !up))
+    return fail(LSN_E_ARG, "%s: with NF4 weights gate and up must be given", what);
+  if (adapters != LSN_ADAPTERS_OFF && adapters != LSN_ADAPTERS_ON && adapters != LSN_ADAPTERS_U_READY)
+    return fail(LSN_E_ARG, "%s: unknown adapters mode %d", what, adapters);
+  const int64_t T = Lg->T, K = Lg->K, N = Lg->N, r = Lg->r;
+  if (!X || !M || !aligned16(X) || !aligned16(M) || (gate && !aligned16(gate)) || (up && !aligned16(up)))
+    return fail(LSN_E_ARG, "%s: X and M must be non-null, and X, M, gate, up 16-byte aligned", what);
+  if (adapters && (!Ug || !Uu || !aligned16(Ug) || !aligned16(Uu)))
+    return fail(LSN_E_ARG, "%s: Ug and Uu must be non-null and 16-byte aligned when adapters are on", what);
+  const size_t yb = (size_t)(T * N * 2), ub = (size_t)(T * r * 2);
+  const void *outs[5] = {M, gate, up};
+  size_t outb[5] = {yb, yb, yb};
+  int n_out = 3;
+  if (adapters == LSN_ADAPTERS_ON) {
+    outs[n_out] = Ug;
+    outb[n_out++] = ub;
+    outs[n_out] = Uu;
+    outb[n_out++] = ub;
+  }
+  const void *ins[12] = {X, Lg->A, Lg->B, Lu->A, Lu->B};
+  size_t inb[12] = {(size_t)(T * K * 2), (size_t)(r * K * 2), (size_t)(N * r * 2), (size_t)(r * K * 2),
+                    (size_t)(N * r * 2)};
+  int n_in = 5;
+  n_in += w_ranges(Lg, ins + n_in, inb + n_in);
+  n_in += w_ranges(Lu, ins + n_in, inb + n_in);
+  if (adapters == LSN_ADAPTERS_U_READY) {
+    ins[n_in] = Ug;
+    inb[n_in++] = ub;
+    ins[n_in] = Uu;
+    inb[n_in++] = ub;
+  }
+  for (int o = 0; o < n_out; ++o) {
+    if (!outs[o]) continue;
+    for (int i = 0; i < n_in; ++i)
+      if (ranges_overlap(outs[o], outb[o], ins[i], inb[i]))
+        return fail(LSN_E_ARG, "%s: an output overlaps an input", what);
+    for (int p = 0; p < o; ++p)
+      if (outs[p] && ranges_overlap(outs[o], outb[o], outs[p], outb[p]))
+        return fail(LSN_E_ARG, "%s: two outputs overlap", what);
+  }
+  if ((st = require_gfx950()) != LSN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (!bf16) {
+    const lsn_lora_linear Ls[2] = {*Lg, *Lu};
+    uint16_t *Ys[2] = {gate, up};
+    uint16_t *Us[2] = {Ug, Uu};
+    if ((st = fwd_group_impl(what, 2, Ls, adapters, X, Ys, Us, nullptr, 0u, nullptr, ws, ws_bytes, s)) != LSN_OK)
+      return st;
+    return swiglu_fwd(T * N, gate, up, M, stream);
+  }
+  if (adapters == LSN_ADAPTERS_ON) {
+    RowProjSet set{};
+    set.n = 2;
+    set.P[0] = Lg->A;
+    set.P[1] = Lu->A;
+    set.out[0] = Ug;
+    set.out[1] = Uu;
+    set.r[0] = set.r[1] = (int)r;
+    set.start[1] = (int)r;
+    set.total = (int)(2 * r);
+    if ((st = launch_rowproj(X, T, K, set, s)) != LSN_OK) return st;
+  }
+  DirectArgs d{};
+  d.M = T;
+  d.K = K;
+  d.act = X;
+  d.nseg = 1;
+  d.seg[0].N = N;
+  d.seg[0].w = Lg->W.bf16;
+  d.seg[0].lr_w = Lg->B;
+  d.seg[0].lr_act = adapters ? Ug : nullptr;
+  d.seg[0].out = gate;
+  d.x.w2 = Lu->W.bf16;
+  d.x.lr_w2 = Lu->B;
+  d.x.lr_act2 = adapters ? Uu : nullptr;
+  d.x.out2 = up;
+  d.x.mout = M;
+  d.r = (int)r;
+  d.scale = Lg->scale;
+  d.adapters = adapters ? 1 : 0;
+  return launch_gemm_direct(d, EPI_SWIGLU, s);
+}
+
 }  // extern "C"
 
 namespace {
 
 // The backward of one linear on the workspace `ws` (ws_bytes long); `what` names the entry point
-// in error messages.
+// in error messages. sw (may be null): the SwiGLU's inputs (gate, up) and gradient outputs
+// (dgate, dup) when the linear is the down projection after a SwiGLU: dX is then dm, not stored
+// (dX unused, dx_mode LSN_DX_BF16_SET), and the epilogue writes dgate and dup.
 lsn_status bwd_impl(const char *what, const lsn_lora_linear *L, const uint16_t *X, const uint16_t *dY,
                     const uint16_t *U, void *dX, int32_t dx_mode, float *dA, float *dB, int32_t grad_mode,
-                    void *ws, size_t ws_bytes, void *stream) {
+                    void *ws, size_t ws_bytes, void *stream, const EpiOps *sw = nullptr) {
   lsn_status st = check_linear(L, what);
   if (st != LSN_OK) return st;
   const int64_t T = L->T, K = L->K, N = L->N, r = L->r;
-  if (!X || !dY || !U || !dX || !dA || !dB || !ws)
+  if (sw) {
+    if (!sw->gate || !sw->up || !sw->dgate || !sw->dup || !aligned16(sw->gate) || !aligned16(sw->up) ||
+        !aligned16(sw->dgate) || !aligned16(sw->dup))
+      return fail(LSN_E_ARG, "%s: gate, up, dgate, dup must be non-null and 16-byte aligned", what);
+    dx_mode = LSN_DX_BF16_SET;
+  }
+  if (!X || !dY || !U || (!dX && !sw) || !dA || !dB || !ws)
     return fail(LSN_E_ARG, "%s: null pointer argument", what);
-  if (!aligned16(X) || !aligned16(dY) || !aligned16(U) || !aligned16(dX) || ((uintptr_t)ws & 255))
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(U) || (dX && !aligned16(dX)) || ((uintptr_t)ws & 255))
     return fail(LSN_E_ARG, "%s: X, dY, U, dX must be 16-byte and ws 256-byte aligned", what);
   if (dx_mode != LSN_DX_BF16_SET && dx_mode != LSN_DX_F32_ADD && dx_mode != LSN_DX_F32_SET)
     return fail(LSN_E_ARG, "%s: unknown dX mode %d", what, dx_mode);
@@ -333,13 +515,20 @@ lsn_status bwd_impl(const char *what, const lsn_lora_linear *L, const uint16_t *
   if (ws_bytes < need.bytes)
     return fail(LSN_E_ARG, "%s: workspace too small (%zu < %zu)", what, ws_bytes, need.bytes);
   const size_t dxb = (size_t)(T * K * (dx_mode == LSN_DX_BF16_SET ? 2 : 4));
-  const void *outs[] = {dX, dA, dB, ws};
-  const size_t outb[] = {dxb, (size_t)(r * K * 4), (size_t)(N * r * 4), need.bytes};
-  const void *ins[8] = {X, dY, U, L->A, L->B};
-  size_t inb[8] = {(size_t)(T * K * 2), (size_t)(T * N * 2), (size_t)(T * r * 2), (size_t)(r * K * 2),
-                   (size_t)(N * r * 2)};
-  const int n_in = 5 + w_ranges(L, ins + 5, inb + 5);
-  for (int o = 0; o < 4; ++o) {
+  const void *outs[5] = {dA, dB, ws, sw ? (const void *)sw->dgate : dX, sw ? (const void *)sw->dup : nullptr};
+  const size_t outb[5] = {(size_t)(r * K * 4), (size_t)(N * r * 4), need.bytes, dxb, dxb};
+  const int n_out = sw ? 5 : 4;
+  const void *ins[10] = {X, dY, U, L->A, L->B};
+  size_t inb[10] = {(size_t)(T * K * 2), (size_t)(T * N * 2), (size_t)(T * r * 2), (size_t)(r * K * 2),
+                    (size_t)(N * r * 2)};
+  int n_in = 5 + w_ranges(L, ins + 5, inb + 5);
+  if (sw) {
+    ins[n_in] = sw->gate;
+    inb[n_in++] = dxb;
+    ins[n_in] = sw->up;
+    inb[n_in++] = dxb;
+  }
+  for (int o = 0; o < n_out; ++o) {
     for (int i = 0; i < n_in; ++i)
       if (ranges_overlap(outs[o], outb[o], ins[i], inb[i]))
         return fail(LSN_E_ARG, "%s: an output overlaps an input", what);
@@ -367,7 +556,8 @@ lsn_status bwd_impl(const char *what, const lsn_lora_linear *L, const uint16_t *
     if ((st = launch_transpose_many(ts, s)) != LSN_OK) return st;
   }
   if ((st = launch_rowproj(dY, T, N, need.Bt, (int)r, need.G, s)) != LSN_OK) return st;
-  const int epi = dx_mode == LSN_DX_F32_ADD ? EPI_F32_ADD : dx_mode == LSN_DX_F32_SET ? EPI_F32_SET : EPI_BF16;
+  const int epi = sw ? EPI_SWIGLU_BWD
+                     : dx_mode == LSN_DX_F32_ADD ? EPI_F32_ADD : dx_mode == LSN_DX_F32_SET ? EPI_F32_SET : EPI_BF16;
   if (L->W.kind != LSN_W_NF4) {
     // dX = dY W + s G (A^T)^T, a product over N: from W^T [K][N] both operands are N-contiguous;
     // from W [N][K] the GEMM reads its B operand reduction-major (same fragments, same bits)
@@ -385,6 +575,7 @@ lsn_status bwd_impl(const char *what, const lsn_lora_linear *L, const uint16_t *
     d.scale = L->scale;
     d.adapters = 1;
     d.b_red_major = L->W.kind == LSN_W_BF16;
+    if (sw) d.x = *sw;
     if ((st = launch_gemm_direct(d, epi, s)) != LSN_OK) return st;
   } else {
     GemmArgs a = base_args(L);
@@ -397,6 +588,7 @@ lsn_status bwd_impl(const char *what, const lsn_lora_linear *L, const uint16_t *
     a.lr_w = L->A;
     a.adapters = 1;
     a.out = dX;
+    if (sw) a.x = *sw;
     // (this kernel adds or stores bf16: an fp32 store is a zero fill and an add)
     if (epi == EPI_F32_SET && (st = launch_fill_zero(dX, dxb, s)) != LSN_OK) return st;
     if ((st = launch_gemm(GEMM_NN, L->W.kind == LSN_W_NF4 ? W_IS_NF4 : W_IS_BF16,
@@ -426,6 +618,19 @@ lsn_status lora_linear_bwd(const lsn_lora_linear *L, const uint16_t *X, const ui
                            void *dX, int32_t dx_mode, float *dA, float *dB, int32_t grad_mode, void *ws,
                            size_t ws_bytes, void *stream) {
   return bwd_impl("lora_linear_bwd", L, X, dY, U, dX, dx_mode, dA, dB, grad_mode, ws, ws_bytes, stream);
+}
+
+lsn_status lora_linear_bwd_swiglu(const lsn_lora_linear *L, const uint16_t *X, const uint16_t *dY,
+                                  const uint16_t *U, const uint16_t *gate, const uint16_t *up, uint16_t *dgate,
+                                  uint16_t *dup, float *dA, float *dB, int32_t grad_mode, void *ws, size_t ws_bytes,
+                                  void *stream) {
+  EpiOps sw{};
+  sw.gate = gate;
+  sw.up = up;
+  sw.dgate = dgate;
+  sw.dup = dup;
+  return bwd_impl("lora_linear_bwd_swiglu", L, X, dY, U, nullptr, LSN_DX_BF16_SET, dA, dB, grad_mode, ws, ws_bytes,
+                  stream, &sw);
 }
 
 }  // extern "C"

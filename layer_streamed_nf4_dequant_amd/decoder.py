@@ -32,15 +32,16 @@ EPS = 1e-5
 THETA = 500000.0
 
 
-def activation_shapes(cfg: StackConfig, layers: int, nq: int) -> dict:
+def activation_shapes(cfg: StackConfig, layers: int, nq: int, fuse_glue: bool = True) -> dict:
     """Per-visit activations and gradients of the decoder step (one set, reused by every layer):
-    name -> (shape, dtype)."""
+    name -> (shape, dtype). With the glue fused into the projections' epilogues the o and down
+    outputs before the residual add and the SwiGLU output's gradient are never stored."""
     T, H, I, kv = cfg.T, cfg.hidden, cfg.inter, cfg.kv
     th, ti, tk = (T, H), (T, I), (T, kv)
-    out = {n: (th, "bf16") for n in ("y_re", "n1", "n2", "h", "a", "dproj", "q", "o_att", "dy_b", "dh_b",
-                                     "do_att", "dq", "n_f", "dn_f")}
+    out = {n: (th, "bf16") for n in ("y_re", "n1", "n2", "h", "q", "o_att", "dy_b", "dh_b", "do_att", "dq",
+                                     "n_f", "dn_f") + (() if fuse_glue else ("a", "dproj"))}
     out.update({n: (tk, "bf16") for n in ("k", "v", "dk", "dv")})
-    out.update({n: (ti, "bf16") for n in ("gate", "up", "m", "dm", "dgate", "dup")})
+    out.update({n: (ti, "bf16") for n in ("gate", "up", "m", "dgate", "dup") + (() if fuse_glue else ("dm",))})
     out.update({n: ((T,), "f32") for n in ("rstd1", "rstd2", "rstd_f", "loss")})
     out.update({"lse": ((T, nq), "f32"), "dy": (th, "f32"), "dn": (th, "f32")})
     return out
@@ -60,7 +61,8 @@ def decoder_workspaces(cfg: StackConfig, vocab: int, ce_chunk: int) -> dict:
 
 
 def decoder_buffer_plan(cfg: StackConfig, vocab: int, layers: int | None = None, modes=("streamed",),
-                        dequant: str = "staged", ce_chunk: int = 2048, reference: bool = False) -> list:
+                        dequant: str = "staged", ce_chunk: int = 2048, reference: bool = False,
+                        fuse_glue: bool = True) -> list:
     """Every device buffer a decoder training step uses, in arena order: [(key, part, nbytes)]."""
     L = cfg.layers if layers is None else layers
     layout, image = layer_layout(cfg)
@@ -75,8 +77,9 @@ def decoder_buffer_plan(cfg: StackConfig, vocab: int, layers: int | None = None,
             plan += [(("A", l, j), "adapters", r * p.K * 2), (("B", l, j), "adapters", p.N * r * 2),
                      (("dA", l, j), "adapter_grads", r * p.K * 4), (("dB", l, j), "adapter_grads", p.N * r * 4)]
     plan += [((k,), "tokens", T * 4) for k in ("ids", "labels", "positions")]
+    plan += [(("rope_cs",), "tokens", cfg.seq_len * cfg.head_dim * 4)]
     plan += [(("x", i), "layer_checkpoints", T * H * 2) for i in range(L + 1)]
-    for key, (shape, dt) in activation_shapes(cfg, L, nq).items():
+    for key, (shape, dt) in activation_shapes(cfg, L, nq, fuse_glue).items():
         plan.append(((key,), "activations", int(np.prod(shape)) * sz[dt]))
     plan += [(("U", j), "activations", T * r * 2) for j, _ in enumerate(layout)]
     plan += [((k,), "workspaces", n) for k, n in decoder_workspaces(cfg, vocab, ce_chunk).items()]
@@ -92,23 +95,37 @@ def decoder_buffer_plan(cfg: StackConfig, vocab: int, layers: int | None = None,
 
 
 def predict_decoder_bytes(cfg: StackConfig, vocab: int, layers: int | None = None, modes=("streamed",),
-                          dequant: str = "staged", ce_chunk: int = 2048, reference: bool = False) -> dict:
+                          dequant: str = "staged", ce_chunk: int = 2048, reference: bool = False,
+                          fuse_glue: bool = True) -> dict:
     """Peak device memory of a decoder training step, from the shapes alone ("Soup v0.73.0
     benchmarks README", record index: a peak-VRAM predictor whose fit decision refuses): the step
     allocates nothing beyond its arena, so the step's peak is the arena. Also returned: the
     set-up's largest extra temporaries (the embedding or head drawn in fp32 and rounded to bf16,
     or one base weight in fp32 with its layer image and the packing workspace), which the fit
     decision adds. Returns the parts, their "total" and "setup_extra"."""
-    plan = decoder_buffer_plan(cfg, vocab, layers, modes, dequant, ce_chunk, reference)
+    plan = decoder_buffer_plan(cfg, vocab, layers, modes, dequant, ce_chunk, reference, fuse_glue)
     parts = {}
     for _, part, nbytes in plan:
         parts[part] = parts.get(part, 0) + nbytes
     _, parts["total"] = arena_offsets(plan)
     layout, image = layer_layout(cfg)
     big = max(layout, key=lambda p: p.K * p.N)
-    pack = big.K * big.N * 4 + lib.load().nf4_pack_ws_bytes(big.N, big.K) + (image if "resident" not in modes else 0)
-    parts["setup_extra"] = max(vocab * cfg.hidden * (4 + 2), pack)
+    pack = (allocator_block_bytes(big.K * big.N * 4) + allocator_block_bytes(lib.load().nf4_pack_ws_bytes(big.N, big.K))
+            + (allocator_block_bytes(image) if "resident" not in modes else 0))
+    emb = allocator_block_bytes(vocab * cfg.hidden * 4) + allocator_block_bytes(vocab * cfg.hidden * 2)
+    parts["setup_extra"] = max(emb, pack)
     return parts
+
+
+def allocator_block_bytes(n: int) -> int:
+    """Bytes torch's caching allocator books for a fresh n-byte device allocation: the size
+    rounded to 512 B; a large one gets a segment of whole 2 MiB, and when less than 1 MiB of that
+    segment would remain the block keeps all of it (the remainder is too small to split off)."""
+    size = (n + 511) // 512 * 512
+    if size <= (1 << 20):
+        return size
+    seg = (size + (2 << 20) - 1) // (2 << 20) * (2 << 20)
+    return seg if seg - size < (1 << 20) else size
 
 
 class DecoderModel:
@@ -118,14 +135,17 @@ class DecoderModel:
     def __init__(self, cfg: StackConfig, vocab: int, layers: int | None = None, seed: int = 0,
                  modes=("streamed",), dequant: str = "staged", eps: float = EPS, theta: float = THETA,
                  ce_chunk: int = 2048, label_rows: int | None = None, hbm_budget: int | None = None,
-                 reference: bool = False):
+                 reference: bool = False, fuse_glue: bool = True):
         """label_rows: keep the next-token label on only this many rows (a seeded sample of the
         rows that have one) and ignore the rest, so that the loss, and the gradient flowing back
         from it, come from a sample of positions. hbm_budget: device bytes the model may take
         (default: the free memory the device reports); the predicted arena plus the set-up's
         temporaries (predict_decoder_bytes) must fit, else MemoryError before anything is
         allocated. reference: also place the reference sweep's buffers in the arena (otherwise
-        the first reference step allocates them)."""
+        the first reference step allocates them). fuse_glue: the rotary embedding, the residual
+        adds and the SwiGLU (forward and backward) run in the epilogues of the projections and
+        of attention's backward (the same bits as the separate glue kernels, which
+        fuse_glue=False runs)."""
         import torch
         self.torch = torch
         self.cfg, self.V, self.seed = cfg, vocab, seed
@@ -137,6 +157,7 @@ class DecoderModel:
         if dequant not in ("staged", "fused"):
             raise ValueError(dequant)
         self.dequant = dequant
+        self.fuse = bool(fuse_glue)
         self.n_seq, self.nq, self.nkv, self.d = T // cfg.seq_len, H // d, cfg.kv // d, d
         self.dev = torch.device("cuda")
         self.layout, self.image_bytes = layer_layout(cfg)
@@ -148,7 +169,7 @@ class DecoderModel:
         self.ce_chunk = ce_chunk
 
         # ---- the fit decision, then every step buffer carved from one arena allocated first ----
-        pred = predict_decoder_bytes(cfg, vocab, self.L, modes, dequant, ce_chunk, reference)
+        pred = predict_decoder_bytes(cfg, vocab, self.L, modes, dequant, ce_chunk, reference, self.fuse)
         need = pred["total"] + pred["setup_extra"]
         budget = hbm_budget if hbm_budget is not None else torch.cuda.mem_get_info()[0]
         if need > budget:
@@ -156,7 +177,7 @@ class DecoderModel:
                               f"arena + {pred['setup_extra']} B during set-up), {budget} B available: refused")
         self.compute = torch.cuda.Stream()
         self.copy_stream = torch.cuda.Stream()
-        plan = decoder_buffer_plan(cfg, vocab, self.L, modes, dequant, ce_chunk, reference)
+        plan = decoder_buffer_plan(cfg, vocab, self.L, modes, dequant, ce_chunk, reference, self.fuse)
         offsets, arena_bytes = arena_offsets(plan)
         self.arena = torch.empty(arena_bytes, dtype=torch.uint8, device=dev)
         sizes = {key: nbytes for key, _, nbytes in plan}
@@ -239,9 +260,12 @@ class DecoderModel:
         self.n_counted = int((self.labels >= 0).sum())
         self.positions = buf(("positions",), (T,), torch.int32)
         self.positions.copy_(torch.arange(T, device=dev, dtype=torch.int32) % cfg.seq_len)
+        self.rope_cs = buf(("rope_cs",), (cfg.seq_len, d // 2, 2), f32)
+        lib.rope_table(cfg.seq_len, d, theta, out=self.rope_cs)
+        self.rope = lib.rope_desc(self.rope_cs, cfg.seq_len, d, self.positions)
 
         # ---- activations and gradients ----
-        for key, (shape, dt) in activation_shapes(cfg, self.L, self.nq).items():
+        for key, (shape, dt) in activation_shapes(cfg, self.L, self.nq, self.fuse).items():
             setattr(self, key, buf((key,), shape, {"bf16": bf16, "f32": f32, "u8": torch.uint8}[dt]))
         self.x = [buf(("x", i), (T, H), bf16) for i in range(self.L + 1)]   # layer inputs, final hidden
         self.U = [buf(("U", j), (T, r), bf16) for j, _ in enumerate(self.layout)]
@@ -303,57 +327,93 @@ class DecoderModel:
         return self.resident[l].data_ptr()
 
     # -------------------------------------------------------------------------------------------
-    def _layer_fwd(self, base: int, l: int, x, y, s, adapters: bool = True):
+    def _layer_fwd(self, base: int, l: int, x, y, s, adapters: bool = True, keep: bool = True):
         """y = layer l applied to x (keeps the intermediates the backward needs). adapters=False:
-        the frozen base alone (the reference model), U untouched."""
+        the frozen base alone (the reference model), U untouched. keep=False: a forward whose
+        backward recomputes the layer; the MLP's gate and up outputs need not be stored."""
         J, U = self.j, self.U
         mode = lib.ADAPTERS_U_READY if adapters else lib.ADAPTERS_OFF
+        d = lambda n: self._desc(base, l, n)  # noqa: E731
+        us = lambda names: [U[J[n]] for n in names] if adapters else None  # noqa: E731
         lib.rmsnorm_fwd(x, self.g1[l], self.eps, self.n1, self.rstd1, stream=s)
         qkv = ("q", "k", "v")
         if adapters:
-            lib.lora_down(self.n1, [self.A[l][J[n]] for n in qkv], [U[J[n]] for n in qkv], stream=s)
-        lib.lora_linear_fwd_group([self._desc(base, l, n) for n in qkv], self.n1, [self.q, self.k, self.v],
-                                  [U[J[n]] for n in qkv] if adapters else None, adapters=mode, ws=self.ws, stream=s)
-        lib.rope_apply(self.q, self.positions, self.nq, self.d, self.theta, stream=s)
-        lib.rope_apply(self.k, self.positions, self.nkv, self.d, self.theta, stream=s)
+            lib.lora_down(self.n1, [self.A[l][J[n]] for n in qkv], us(qkv), stream=s)
+        if self.fuse:
+            # q and k leave the GEMM rotated
+            lib.lora_linear_fwd_group_epi([d(n) for n in qkv], self.n1, [self.q, self.k, self.v], us(qkv),
+                                          adapters=mode, rope_mask=0b011, rope=self.rope, ws=self.ws, stream=s)
+        else:
+            lib.lora_linear_fwd_group([d(n) for n in qkv], self.n1, [self.q, self.k, self.v], us(qkv),
+                                      adapters=mode, ws=self.ws, stream=s)
+            lib.rope_apply(self.q, self.positions, self.nq, self.d, self.theta, stream=s)
+            lib.rope_apply(self.k, self.positions, self.nkv, self.d, self.theta, stream=s)
         lib.attention_fwd(self.q, self.k, self.v, self.o_att, self.lse, self.n_seq, self.nq, self.nkv, self.d,
                           stream=s)
-        lib.lora_linear_fwd(self._desc(base, l, "o"), self.o_att, self.a, U[J["o"]] if adapters else None,
-                            adapters=adapters, ws=self.ws, stream=s)
-        lib.add_bf16(x, self.a, self.h, stream=s)
+        if self.fuse:
+            # h = x + o-projection, added in the GEMM's epilogue
+            # (U of o, and of down below, is computed by the call itself: ADAPTERS_ON)
+            lib.lora_linear_fwd_group_epi([d("o")], self.o_att, [self.h], us(("o",)), adapters=adapters,
+                                          residual=[x], ws=self.ws, stream=s)
+        else:
+            lib.lora_linear_fwd(d("o"), self.o_att, self.a, U[J["o"]] if adapters else None, adapters=adapters,
+                                ws=self.ws, stream=s)
+            lib.add_bf16(x, self.a, self.h, stream=s)
         lib.rmsnorm_fwd(self.h, self.g2[l], self.eps, self.n2, self.rstd2, stream=s)
         gu = ("gate", "up")
         if adapters:
-            lib.lora_down(self.n2, [self.A[l][J[n]] for n in gu], [U[J[n]] for n in gu], stream=s)
-        lib.lora_linear_fwd_group([self._desc(base, l, n) for n in gu], self.n2, [self.gate, self.up],
-                                  [U[J[n]] for n in gu] if adapters else None, adapters=mode, ws=self.ws, stream=s)
-        lib.swiglu_fwd(self.gate, self.up, self.m, stream=s)
-        lib.lora_linear_fwd(self._desc(base, l, "down"), self.m, self.dproj, U[J["down"]] if adapters else None,
-                            adapters=adapters, ws=self.ws, stream=s)
-        lib.add_bf16(self.h, self.dproj, y, stream=s)
+            lib.lora_down(self.n2, [self.A[l][J[n]] for n in gu], us(gu), stream=s)
+        if self.fuse:
+            # m = silu(gate) up in the gate/up GEMM's epilogue (gate and up stored when kept)
+            store = keep or self.dequant != "staged"
+            Ug, Uu = us(gu) if adapters else (None, None)
+            lib.lora_linear_fwd_swiglu(d("gate"), d("up"), self.n2, self.m, gate=self.gate if store else None,
+                                       up=self.up if store else None, Ug=Ug, Uu=Uu, adapters=mode, ws=self.ws,
+                                       stream=s)
+            lib.lora_linear_fwd_group_epi([d("down")], self.m, [y], us(("down",)), adapters=adapters,
+                                          residual=[self.h], ws=self.ws, stream=s)
+        else:
+            lib.lora_linear_fwd_group([d(n) for n in gu], self.n2, [self.gate, self.up], us(gu), adapters=mode,
+                                      ws=self.ws, stream=s)
+            lib.swiglu_fwd(self.gate, self.up, self.m, stream=s)
+            lib.lora_linear_fwd(d("down"), self.m, self.dproj, U[J["down"]] if adapters else None,
+                                adapters=adapters, ws=self.ws, stream=s)
+            lib.add_bf16(self.h, self.dproj, y, stream=s)
 
     def _layer_bwd(self, base: int, l: int, x, s, grad_mode: int):
         """self.dy (fp32, the gradient of the layer's output; self.dy_b its bf16 copy) becomes the
         gradient of its input x (and self.dy_b that one's bf16 copy); dA, dB of the layer's seven
         projections are set (GRAD_SET) or added to (GRAD_ADD)."""
         J, U, dA, dB = self.j, self.U, self.dA[l], self.dB[l]
-        lib.lora_linear_bwd(self._desc(base, l, "down"), self.m, self.dy_b, U[J["down"]], self.dm, dA[J["down"]],
-                            dB[J["down"]], dx_mode=lib.DX_BF16_SET, grad_mode=grad_mode, ws=self.ws, stream=s)
-        lib.swiglu_bwd(self.gate, self.up, self.dm, self.dgate, self.dup, stream=s)
+        d = lambda n: self._desc(base, l, n)  # noqa: E731
+        jd = J["down"]
+        if self.fuse:
+            # the SwiGLU's backward in the down projection's dX epilogue
+            lib.lora_linear_bwd_swiglu(d("down"), self.m, self.dy_b, U[jd], self.gate, self.up, self.dgate, self.dup,
+                                       dA[jd], dB[jd], grad_mode=grad_mode, ws=self.ws, stream=s)
+        else:
+            lib.lora_linear_bwd(d("down"), self.m, self.dy_b, U[jd], self.dm, dA[jd], dB[jd],
+                                dx_mode=lib.DX_BF16_SET, grad_mode=grad_mode, ws=self.ws, stream=s)
+            lib.swiglu_bwd(self.gate, self.up, self.dm, self.dgate, self.dup, stream=s)
         gu = ("gate", "up")
-        lib.lora_linear_bwd_group([self._desc(base, l, n) for n in gu], self.n2, [self.dgate, self.dup],
+        lib.lora_linear_bwd_group([d(n) for n in gu], self.n2, [self.dgate, self.dup],
                                   [U[J[n]] for n in gu], self.dn, [dA[J[n]] for n in gu], [dB[J[n]] for n in gu],
                                   dx_mode=lib.DX_F32_SET, grad_mode=grad_mode, ws=self.ws, stream=s)
         lib.rmsnorm_bwd(self.h, self.g2[l], self.rstd2, self.dn, self.dy, accumulate=True, dx_bf16=self.dh_b,
                         stream=s)                                                                   # dy = dh
-        lib.lora_linear_bwd(self._desc(base, l, "o"), self.o_att, self.dh_b, U[J["o"]], self.do_att, dA[J["o"]],
+        lib.lora_linear_bwd(d("o"), self.o_att, self.dh_b, U[J["o"]], self.do_att, dA[J["o"]],
                             dB[J["o"]], dx_mode=lib.DX_BF16_SET, grad_mode=grad_mode, ws=self.ws, stream=s)
-        lib.attention_bwd(self.q, self.k, self.v, self.o_att, self.lse, self.do_att, self.dq, self.dk, self.dv,
-                          self.ws_att, self.n_seq, self.nq, self.nkv, self.d, stream=s)
-        lib.rope_apply(self.dq, self.positions, self.nq, self.d, self.theta, inverse=True, stream=s)
-        lib.rope_apply(self.dk, self.positions, self.nkv, self.d, self.theta, inverse=True, stream=s)
+        if self.fuse:
+            # dq and dk rotated back as attention's backward stores them
+            lib.attention_bwd_rope(self.q, self.k, self.v, self.o_att, self.lse, self.do_att, self.dq, self.dk,
+                                   self.dv, self.ws_att, self.n_seq, self.nq, self.nkv, self.d, self.rope, stream=s)
+        else:
+            lib.attention_bwd(self.q, self.k, self.v, self.o_att, self.lse, self.do_att, self.dq, self.dk, self.dv,
+                              self.ws_att, self.n_seq, self.nq, self.nkv, self.d, stream=s)
+            lib.rope_apply(self.dq, self.positions, self.nq, self.d, self.theta, inverse=True, stream=s)
+            lib.rope_apply(self.dk, self.positions, self.nkv, self.d, self.theta, inverse=True, stream=s)
         qkv = ("q", "k", "v")
-        lib.lora_linear_bwd_group([self._desc(base, l, n) for n in qkv], self.n1, [self.dq, self.dk, self.dv],
+        lib.lora_linear_bwd_group([d(n) for n in qkv], self.n1, [self.dq, self.dk, self.dv],
                                   [U[J[n]] for n in qkv], self.dn, [dA[J[n]] for n in qkv], [dB[J[n]] for n in qkv],
                                   dx_mode=lib.DX_F32_SET, grad_mode=grad_mode, ws=self.ws, stream=s)
         lib.rmsnorm_bwd(x, self.g1[l], self.rstd1, self.dn, self.dy, accumulate=True, dx_bf16=self.dy_b,
@@ -390,7 +450,7 @@ class DecoderModel:
                 for l in range(self.L):
                     base = self._base(mode, l, sh, forward=True)
                     self._stage(base, l, s)
-                    self._layer_fwd(base, l, self.x[l], self.x[l + 1], s)
+                    self._layer_fwd(base, l, self.x[l], self.x[l + 1], s, keep=False)
                     if mode == "streamed":
                         self.pool.release(l, sh)
                 # final norm, LM head and cross-entropy (mean over counted rows)
@@ -424,7 +484,7 @@ class DecoderModel:
         for l in range(self.L):
             base = self._base(mode, l, sh, forward=True)
             self._stage(base, l, s)
-            self._layer_fwd(base, l, self.x_ref[l % 2], self.x_ref[(l + 1) % 2], s, adapters=False)
+            self._layer_fwd(base, l, self.x_ref[l % 2], self.x_ref[(l + 1) % 2], s, adapters=False, keep=False)
             if mode == "streamed":
                 self.pool.release(l, sh)
         xL = self.x_ref[self.L % 2]

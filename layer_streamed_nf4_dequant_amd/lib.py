@@ -33,11 +33,12 @@ EXPORTS = (
     "nf4_dequant", "nf4_dequant_batch", "lora_down", "lora_linear_ws_bytes", "lora_linear_fwd", "lora_linear_fwd_group",
     "lora_linear_bwd", "lora_linear_group_ws_bytes", "lora_linear_bwd_group",
     "lora_linear_bwd_noalloc", "lora_linear_bwd_noalloc_max_ws_bytes",
+    "lora_linear_fwd_group_epi", "lora_linear_fwd_swiglu", "lora_linear_bwd_swiglu",
     "layer_pool_create", "layer_pool_register", "layer_pool_register_file", "layer_pool_prefetch", "layer_pool_acquire",
     "layer_pool_release", "layer_pool_stats", "layer_pool_audit", "layer_pool_destroy",
     "lm_head_ce_ws_bytes", "lm_head_ce", "embedding_gather",
-    "rmsnorm_fwd", "rmsnorm_bwd", "rope_apply", "swiglu_fwd", "swiglu_bwd",
-    "attention_fwd", "attention_bwd_ws_bytes", "attention_bwd",
+    "rmsnorm_fwd", "rmsnorm_bwd", "rope_apply", "rope_table", "swiglu_fwd", "swiglu_bwd",
+    "attention_fwd", "attention_bwd_ws_bytes", "attention_bwd", "attention_bwd_rope",
     "add_bf16", "convert_f32_bf16", "convert_bf16_f32",
 )
 
@@ -61,6 +62,12 @@ class LoraLinearDesc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
                 ("r", ctypes.c_int64), ("scale", ctypes.c_float), ("W", WeightDesc),
                 ("A", ctypes.c_void_p), ("B", ctypes.c_void_p)]
+
+
+class RopeDesc(ctypes.Structure):
+    """lsn_rope: a rope_table table, its rows and head width, and the rows' positions."""
+    _fields_ = [("cs", ctypes.c_void_p), ("n_pos", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("positions", ctypes.c_void_p)]
 
 
 class PoolStats(ctypes.Structure):
@@ -114,6 +121,13 @@ def load():
                                         ctypes.POINTER(vp), vp, sz, vp]),
         "lora_linear_bwd": (i32, [ctypes.POINTER(LoraLinearDesc), vp, vp, vp, vp, i32, vp, vp, i32,
                                   vp, sz, vp]),
+        "lora_linear_fwd_group_epi": (i32, [i32, ctypes.POINTER(LoraLinearDesc), i32, vp, ctypes.POINTER(vp),
+                                            ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_uint32,
+                                            ctypes.POINTER(RopeDesc), vp, sz, vp]),
+        "lora_linear_fwd_swiglu": (i32, [ctypes.POINTER(LoraLinearDesc), ctypes.POINTER(LoraLinearDesc), i32, vp,
+                                         vp, vp, vp, vp, vp, vp, sz, vp]),
+        "lora_linear_bwd_swiglu": (i32, [ctypes.POINTER(LoraLinearDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                         vp, sz, vp]),
         "lora_linear_bwd_noalloc": (i32, [ctypes.POINTER(LoraLinearDesc), vp, vp, vp, vp, i32, vp, vp, i32, vp]),
         "lora_linear_bwd_noalloc_max_ws_bytes": (sz, []),
         "lora_linear_group_ws_bytes": (sz, [i32, ctypes.POINTER(LoraLinearDesc)]),
@@ -136,6 +150,7 @@ def load():
         "rmsnorm_fwd": (i32, [i64, i64, vp, vp, f32, vp, vp, vp]),
         "rmsnorm_bwd": (i32, [i64, i64, vp, vp, vp, vp, vp, i32, vp, vp]),
         "rope_apply": (i32, [i64, i32, i32, vp, i64, vp, f32, i32, vp]),
+        "rope_table": (i32, [i32, i32, f32, vp, vp]),
         "swiglu_fwd": (i32, [i64, vp, vp, vp, vp]),
         "swiglu_bwd": (i32, [i64, vp, vp, vp, vp, vp, vp]),
         "attention_fwd": (i32, [i64, i64, i32, i32, i32, vp, i64, vp, i64, vp, i64, f32, vp, i64, vp, vp]),
@@ -145,6 +160,8 @@ def load():
         "convert_bf16_f32": (i32, [i64, vp, vp, vp]),
         "attention_bwd": (i32, [i64, i64, i32, i32, i32, vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, i64, f32,
                                 vp, i64, vp, i64, vp, i64, vp, sz, vp]),
+        "attention_bwd_rope": (i32, [i64, i64, i32, i32, i32, vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, i64, f32,
+                                     vp, i64, vp, i64, vp, i64, vp, sz, ctypes.POINTER(RopeDesc), vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -299,6 +316,59 @@ def lora_linear_fwd_group(descs, X, Y_list, U_list=None, adapters=True, ws=None,
     U = (ctypes.c_void_p * n)(*[_ptr(u) for u in U_list]) if U_list is not None else None
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     check(load().lora_linear_fwd_group(n, arr, mode, _ptr(X), Y, U, _ptr(ws), nbytes, _stream_handle(stream)))
+
+
+def _mode(adapters) -> int:
+    return adapters if isinstance(adapters, int) and not isinstance(adapters, bool) else (
+        ADAPTERS_ON if adapters else ADAPTERS_OFF)
+
+
+def rope_desc(cs, n_pos: int, head_dim: int, positions) -> RopeDesc:
+    """The rotation a fused epilogue applies: a rope_table table (fp32 [n_pos][head_dim/2][2])
+    and the rows' positions (int32 [T])."""
+    return RopeDesc(_ptr(cs), int(n_pos), int(head_dim), _ptr(positions))
+
+
+def rope_table(n_pos: int, head_dim: int, theta: float, out=None, stream=None):
+    """cs[p][i] = (cos, sin) of rope_apply's angle for position p, pair i (fp32 [n_pos][head_dim/2][2])."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((n_pos, head_dim // 2, 2), dtype=torch.float32, device="cuda")
+    check(load().rope_table(int(n_pos), int(head_dim), float(theta), _ptr(out), _stream_handle(stream)))
+    return out
+
+
+def lora_linear_fwd_group_epi(descs, X, Y_list, U_list=None, adapters=True, residual=None, rope_mask: int = 0,
+                              rope: RopeDesc | None = None, ws=None, stream=None) -> None:
+    """lora_linear_fwd_group with the residual add (residual: a list with None entries) and the
+    rotary embedding (members in rope_mask) applied in the GEMM's epilogue."""
+    n = len(descs)
+    arr = (LoraLinearDesc * n)(*descs)
+    Y = (ctypes.c_void_p * n)(*[_ptr(y) for y in Y_list])
+    U = (ctypes.c_void_p * n)(*[_ptr(u) for u in U_list]) if U_list is not None else None
+    R = (ctypes.c_void_p * n)(*[_ptr(r) for r in residual]) if residual is not None else None
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    check(load().lora_linear_fwd_group_epi(n, arr, _mode(adapters), _ptr(X), Y, U, R, int(rope_mask),
+                                           ctypes.byref(rope) if rope is not None else None, _ptr(ws), nbytes,
+                                           _stream_handle(stream)))
+
+
+def lora_linear_fwd_swiglu(desc_gate: LoraLinearDesc, desc_up: LoraLinearDesc, X, M, gate=None, up=None, Ug=None,
+                           Uu=None, adapters=True, ws=None, stream=None) -> None:
+    """gate, up projections and M = bf16(silu(gate) up) in one launch (gate / up stored if given)."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    check(load().lora_linear_fwd_swiglu(ctypes.byref(desc_gate), ctypes.byref(desc_up), _mode(adapters), _ptr(X),
+                                        _ptr(gate), _ptr(up), _ptr(M), _ptr(Ug), _ptr(Uu), _ptr(ws), nbytes,
+                                        _stream_handle(stream)))
+
+
+def lora_linear_bwd_swiglu(desc: LoraLinearDesc, X, dY, U, gate, up, dgate, dup, dA, dB, grad_mode: int = GRAD_SET,
+                           ws=None, stream=None) -> None:
+    """The down projection's backward with the SwiGLU backward in its epilogue: dgate, dup instead of dX."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    check(load().lora_linear_bwd_swiglu(ctypes.byref(desc), _ptr(X), _ptr(dY), _ptr(U), _ptr(gate), _ptr(up),
+                                        _ptr(dgate), _ptr(dup), _ptr(dA), _ptr(dB), grad_mode, _ptr(ws), nbytes,
+                                        _stream_handle(stream)))
 
 
 def lora_linear_bwd(desc: LoraLinearDesc, X, dY, U, dX, dA, dB, dx_mode: int = DX_BF16_SET,
@@ -475,6 +545,19 @@ def attention_bwd(q, k, v, o, lse, dO, dq, dk, dv, ws, n_seq: int, n_q: int, n_k
                                _ptr(v), v.stride(0), _ptr(o), o.stride(0), _ptr(lse), _ptr(dO), dO.stride(0), sc,
                                _ptr(dq), dq.stride(0), _ptr(dk), dk.stride(0), _ptr(dv), dv.stride(0), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream_handle(stream)))
+
+
+def attention_bwd_rope(q, k, v, o, lse, dO, dq, dk, dv, ws, n_seq: int, n_q: int, n_kv: int, head_dim: int,
+                       rope: RopeDesc, scale: float | None = None, stream=None) -> None:
+    """attention_bwd with dq and dk rotated back by the inverse rotary embedding as they are stored."""
+    T = q.shape[0]
+    S = T // n_seq
+    sc = 1.0 / float(head_dim) ** 0.5 if scale is None else float(scale)
+    check(load().attention_bwd_rope(n_seq, S, n_q, n_kv, head_dim, _ptr(q), q.stride(0), _ptr(k), k.stride(0),
+                                    _ptr(v), v.stride(0), _ptr(o), o.stride(0), _ptr(lse), _ptr(dO), dO.stride(0),
+                                    sc, _ptr(dq), dq.stride(0), _ptr(dk), dk.stride(0), _ptr(dv), dv.stride(0),
+                                    _ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(rope),
+                                    _stream_handle(stream)))
 
 
 def add_bf16(a, b, out, stream=None) -> None:
