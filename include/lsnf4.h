@@ -409,15 +409,17 @@ lsn_status rope_apply(int64_t T, int32_t n_heads, int32_t head_dim, uint16_t *x,
                       const int32_t *positions, float theta, int32_t inverse, void *stream);
 
 /*
- * swiglu_fwd - m = bf16( silu(g) u ), silu(z) = z / (1 + e^-z), elementwise over n values
+ * swiglu_fwd - m = bf16( silu(g) u ), silu(z) = z / (1 + e^-z), elementwise over n values;
+ * the sigmoid from the hardware's base-2 exponential and reciprocal (within (|z| + 4) 2^-24
+ * relative; it may come out as 0 for z < -87, where its exact value is below 1e-38)
  * (the gated MLP's gate and up projections in, the down projection's input out).
  * g, u, m: bf16 [n], n a multiple of 8.
  */
 lsn_status swiglu_fwd(int64_t n, const uint16_t *g, const uint16_t *u, uint16_t *m, void *stream);
 
 /*
- * swiglu_bwd - dg = bf16( dm u sigma(g) (1 + g (1 - sigma(g))) ), du = bf16( dm silu(g) ).
- * g, u, dm, dg, du: bf16 [n], n a multiple of 8.
+ * swiglu_bwd - dg = bf16( dm u sigma(g) (1 + g (1 - sigma(g))) ), du = bf16( dm silu(g) ),
+ * sigma as in swiglu_fwd. g, u, dm, dg, du: bf16 [n], n a multiple of 8.
  */
 lsn_status swiglu_bwd(int64_t n, const uint16_t *g, const uint16_t *u, const uint16_t *dm, uint16_t *dg,
                       uint16_t *du, void *stream);

@@ -8,9 +8,12 @@ namespace lsn {
 
 enum { GEMM_NT = 0, GEMM_NN = 1 };        // forward Y = act W^T ; backward dX = act W
 enum { W_IS_NF4 = 0, W_IS_BF16 = 1 };
-// output epilogues: bf16 store, fp32 add into, fp32 store; and two that apply the SwiGLU of a
-// decoder layer's MLP to a bf16 result (see EpiOps)
-enum { EPI_BF16 = 0, EPI_F32_ADD = 1, EPI_F32_SET = 2, EPI_SWIGLU = 3, EPI_SWIGLU_BWD = 4 };
+// output epilogues: bf16 store, fp32 add into, fp32 store; and the decoder glue on a bf16 result
+// (see EpiOps): the SwiGLU forward on a gate/up pair, its backward, the residual add and the
+// rotary embedding (the launchers pick the last two from EPI_BF16 when a segment asks for them,
+// so the plain bf16 kernel carries none of their code)
+enum { EPI_BF16 = 0, EPI_F32_ADD = 1, EPI_F32_SET = 2, EPI_SWIGLU = 3, EPI_SWIGLU_BWD = 4, EPI_BF16_RES = 5,
+       EPI_BF16_ROPE = 6 };
 
 // Operands of the decoder-glue epilogues (bf16 outputs only). Every one of them applies to the
 // rounded bf16 product exactly what the standalone glue kernel would apply to the stored product,

@@ -424,11 +424,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs a) {
         if (m < a.M && n < a.Nout) {
           const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1], v2 = acc[i][j][4 * g + 2],
                       v3 = acc[i][j][4 * g + 3];
-          if constexpr (EPI == EPI_BF16) {
+          if constexpr (EPI == EPI_BF16 || EPI == EPI_BF16_RES) {
             uint2 o;
             o.x = pack_bf16x2(v0, v1);
             o.y = pack_bf16x2(v2, v3);
-            if (a.res) {
+            if constexpr (EPI == EPI_BF16_RES) {
               const uint2 r = *reinterpret_cast<const uint2 *>(a.res + m * a.Nout + n);
               o.x = add_bf16_word(r.x, o.x);
               o.y = add_bf16_word(r.y, o.y);
@@ -818,11 +818,53 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   wait_vm_all();
 
   // ---- epilogue: lane holds row m = 32 i + lane%32, columns 32 j + 8 g + 4 (lane/32) .. +3 ----
-  if constexpr (EPI == EPI_BF16 || EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD) {
-    // through LDS (free once every wave is past the loop): the 256 x 256 bf16 tile is written
+  if constexpr (EPI == EPI_BF16 || EPI == EPI_BF16_RES || EPI == EPI_BF16_ROPE || EPI == EPI_SWIGLU ||
+                EPI == EPI_SWIGLU_BWD) {
+    // Through LDS (free once every wave is past the loop): the 256 x 256 bf16 tile is written
     // with 8-byte stores at a 528-byte row pitch (2-way bank conflicts at most), then read back
     // as 16-byte row chunks so that every global store is a 16-byte piece of a 512-byte row run
-    // (non-temporal: the tile is not read again by this kernel; measured 1-2% faster)
+    // (non-temporal: the tile is not read again by this kernel; measured 1-2% faster).
+    // The glue operands the epilogue reads from global memory (the residual, the rows'
+    // positions, the SwiGLU's inputs) are requested before the tile goes through LDS, or a batch
+    // ahead of their use, so that one wave per SIMD does not wait out their latency row by row.
+    constexpr int RPP = NT / 32;                  // rows per pass of a 32-chunk row loop
+    constexpr int NP = BM / RPP;                  // its passes
+    const int chunk = t & 31;
+    const int64_t n = n0 + 8 * chunk;
+    const bool n_ok = n < sg.N;
+    auto row_of = [&](int p) { return m0 + p * RPP + (t >> 5); };
+    u32x4_t pre[NP];                              // the residual's chunks of this thread's rows
+    int posv[BM / (NT / 16)];                     // the rotation's table rows (16-chunk loop)
+    if constexpr (EPI == EPI_BF16_ROPE) {
+      if (sg.rope) {
+#pragma unroll
+        for (int p = 0; p < BM / (NT / 16); ++p) {
+          const int64_t m = m0 + p * (NT / 16) + (t >> 4);
+          posv[p] = m < a.M ? min(max(a.x.positions[m], 0), a.x.n_pos - 1) : 0;
+        }
+      }
+    }
+    if constexpr (EPI == EPI_BF16_RES) {
+      if (sg.res) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const int64_t m = row_of(p);
+          pre[p] = m < a.M && n_ok ? *reinterpret_cast<const u32x4_t *>(sg.res + m * sg.N + n) : u32x4_t{0, 0, 0, 0};
+        }
+      }
+    }
+    constexpr int SB = 8;                         // SwiGLU backward: rows per batch
+    u32x4_t gbuf[2][SB], ubuf[2][SB];
+    auto fetch_gu = [&](int buf, int b) {
+#pragma unroll
+      for (int q = 0; q < SB; ++q) {
+        const int64_t m = row_of(b * SB + q);
+        const bool ok = m < a.M && n_ok;
+        gbuf[buf][q] = ok ? *reinterpret_cast<const u32x4_t *>(a.x.gate + m * sg.N + n) : u32x4_t{0, 0, 0, 0};
+        ubuf[buf][q] = ok ? *reinterpret_cast<const u32x4_t *>(a.x.up + m * sg.N + n) : u32x4_t{0, 0, 0, 0};
+      }
+    };
+    if constexpr (EPI == EPI_SWIGLU_BWD) fetch_gu(0, 0);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -843,15 +885,15 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       // row r of the tile: gate columns n0 .. n0+127 in chunks 0-15, the same up columns in
       // chunks 16-31; a thread takes chunk c of both halves, 16 rows per pass
       const int c = t & 15;
-      const int64_t n = n0 + 8 * c;
+      const int64_t nc = n0 + 8 * c;
 #pragma unroll 4
       for (int p = 0; p < BM / (NT / 16); ++p) {
         const int r = p * (NT / 16) + (t >> 4);
         const int64_t m = m0 + r;
         const u32x4_t gv = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + c * 16);
         const u32x4_t uv = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + (c + 16) * 16);
-        if (m < a.M && n < sg.N) {
-          const int64_t o = m * sg.N + n;
+        if (m < a.M && nc < sg.N) {
+          const int64_t o = m * sg.N + nc;
           if (sg.out) __builtin_nontemporal_store(gv, reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(sg.out) + o));
           if (a.x.out2) __builtin_nontemporal_store(uv, reinterpret_cast<u32x4_t *>(a.x.out2 + o));
           __builtin_nontemporal_store(swiglu8(gv, uv), reinterpret_cast<u32x4_t *>(a.x.mout + o));
@@ -859,24 +901,65 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       }
       return;
     }
-    if constexpr (EPI == EPI_BF16) {
-      if (sg.rope) {
-        // rotary embedding of the rounded tile (columns = whole heads of D): thread k = t % 16
-        // of a row takes 8 pairs of one head, the chunk at column c1 and its partner D/2 to the
-        // right; 16 rows per pass
-        const int D = a.x.rope_dim, half = D / 2, cph = half / 8, k = t & 15;
-        const int c1 = (k / cph) * D + 8 * (k % cph), c2 = c1 + half;
-        const int64_t n1 = n0 + c1;
-#pragma unroll 2
-        for (int p = 0; p < BM / (NT / 16); ++p) {
-          const int r = p * (NT / 16) + (t >> 4);
+    if constexpr (EPI == EPI_SWIGLU_BWD) {
+      // the tile is dm; the gradients of the SwiGLU's inputs at the same elements, a batch of
+      // rows' gate and up in flight while the previous batch is computed
+#pragma unroll
+      for (int b = 0; b < NP / SB; ++b) {
+        if (b + 1 < NP / SB) fetch_gu((b + 1) & 1, b + 1);
+#pragma unroll
+        for (int q = 0; q < SB; ++q) {
+          const int p = b * SB + q;
+          const int r = p * RPP + (t >> 5);
+          const int64_t m = m0 + r;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + chunk * 16);
+          if (m < a.M && n_ok) {
+            const int64_t o = m * sg.N + n;
+            u32x4_t dg, du;
+            swiglu8_bwd(gbuf[b & 1][q], ubuf[b & 1][q], v, dg, du);
+            __builtin_nontemporal_store(dg, reinterpret_cast<u32x4_t *>(a.x.dgate + o));
+            __builtin_nontemporal_store(du, reinterpret_cast<u32x4_t *>(a.x.dup + o));
+          }
+        }
+      }
+      return;
+    }
+    if (EPI == EPI_BF16_ROPE && sg.rope) {   // (a constant false in the other kernels)
+      // rotary embedding of the rounded tile (columns = whole heads of D): thread k = t % 16
+      // of a row takes 8 pairs of one head, the chunk at column c1 and its partner D/2 to the
+      // right; 16 rows per pass; the table rows of a batch of 4 passes are loaded a batch ahead
+      const int D = a.x.rope_dim, half = D / 2, cph = half / 8, k = t & 15;
+      const int c1 = (k / cph) * D + 8 * (k % cph), c2 = c1 + half;
+      const int64_t n1 = n0 + c1;
+      const float *cs = a.x.rope_cs + 16 * (k % cph);
+      constexpr int PB = 4, NPR = BM / (NT / 16);
+      floatx4_t tb[2][PB][4];
+      auto fetch_cs = [&](int buf, int b) {
+#pragma unroll
+        for (int q = 0; q < PB; ++q)
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            tb[buf][q][w] = *reinterpret_cast<const floatx4_t *>(cs + (int64_t)posv[b * PB + q] * D + 4 * w);
+      };
+      fetch_cs(0, 0);
+#pragma unroll
+      for (int b = 0; b < NPR / PB; ++b) {
+        if (b + 1 < NPR / PB) fetch_cs((b + 1) & 1, b + 1);
+#pragma unroll
+        for (int q = 0; q < PB; ++q) {
+          const int r = (b * PB + q) * (NT / 16) + (t >> 4);
           const int64_t m = m0 + r;
           const u32x4_t x1 = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + c1 * 2);
           const u32x4_t x2 = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + c2 * 2);
           if (m < a.M && n1 < sg.N) {
-            const int pos = min(max(a.x.positions[m], 0), a.x.n_pos - 1);
             float cv[8], sv[8];
-            rope_load8(a.x.rope_cs + (int64_t)pos * D + 16 * (k % cph), 1.0f, cv, sv);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              cv[2 * w] = tb[b & 1][q][w][0];
+              sv[2 * w] = tb[b & 1][q][w][1];
+              cv[2 * w + 1] = tb[b & 1][q][w][2];
+              sv[2 * w + 1] = tb[b & 1][q][w][3];
+            }
             u32x4_t y1, y2;
             rope_chunk8(x1, x2, cv, sv, y1, y2);
             uint16_t *o = reinterpret_cast<uint16_t *>(sg.out) + m * sg.N + n1;
@@ -884,35 +967,32 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
             __builtin_nontemporal_store(y2, reinterpret_cast<u32x4_t *>(o + half));
           }
         }
+      }
+      return;
+    }
+    if constexpr (EPI == EPI_BF16_RES) {
+      if (sg.res) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const int r = p * RPP + (t >> 5);
+          const int64_t m = m0 + r;
+          u32x4_t v = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + chunk * 16);
+          if (m < a.M && n_ok) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = add_bf16_word(pre[p][q], v[q]);
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(sg.out) + m * sg.N + n));
+          }
+        }
         return;
       }
     }
-    const int chunk = t & 31;
-    const int64_t n = n0 + 8 * chunk;
 #pragma unroll 4
-    for (int p = 0; p < BM / (NT / 32); ++p) {
-      const int r = p * (NT / 32) + (t >> 5);
+    for (int p = 0; p < NP; ++p) {
+      const int r = p * RPP + (t >> 5);
       const int64_t m = m0 + r;
-      u32x4_t v = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + chunk * 16);
-      if (m < a.M && n < sg.N) {
-        const int64_t o = m * sg.N + n;
-        if constexpr (EPI == EPI_SWIGLU_BWD) {
-          // v is dm; the gradients of the SwiGLU's inputs at the same elements
-          const u32x4_t gv = *reinterpret_cast<const u32x4_t *>(a.x.gate + o);
-          const u32x4_t uv = *reinterpret_cast<const u32x4_t *>(a.x.up + o);
-          u32x4_t dg, du;
-          swiglu8_bwd(gv, uv, v, dg, du);
-          __builtin_nontemporal_store(dg, reinterpret_cast<u32x4_t *>(a.x.dgate + o));
-          __builtin_nontemporal_store(du, reinterpret_cast<u32x4_t *>(a.x.dup + o));
-        } else {
-          if (sg.res) {
-            const u32x4_t rv = *reinterpret_cast<const u32x4_t *>(sg.res + o);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = add_bf16_word(rv[q], v[q]);
-          }
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(sg.out) + o));
-        }
-      }
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(smem + r * kEpiPitch + chunk * 16);
+      if (m < a.M && n_ok)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(sg.out) + m * sg.N + n));
     }
     return;
   }
@@ -992,7 +1072,19 @@ lsn_status launch_one(const GemmArgs &a, hipStream_t s) {
 namespace {
 template <bool KSEG, bool BT>
 lsn_status launch_direct_epi(const DirectArgs &a, int epi, hipStream_t s) {
-  if (epi == EPI_BF16) return launch_direct_one<EPI_BF16, KSEG, BT>(a, s);
+  if (epi == EPI_BF16) {
+    bool res = false, rope = false;
+    for (int q = 0; q < a.nseg; ++q) {
+      res = res || a.seg[q].res;
+      rope = rope || a.seg[q].rope;
+    }
+    if constexpr (!KSEG && !BT) {
+      if (rope) return launch_direct_one<EPI_BF16_ROPE, false, false>(a, s);
+      if (res) return launch_direct_one<EPI_BF16_RES, false, false>(a, s);
+    }
+    if (res || rope) return fail(LSN_E_ARG, "gemm_direct: the residual and rotary epilogues are forward-only");
+    return launch_direct_one<EPI_BF16, KSEG, BT>(a, s);
+  }
   if (epi == EPI_F32_ADD) return launch_direct_one<EPI_F32_ADD, KSEG, BT>(a, s);
   if constexpr (!KSEG) {
     if (epi == EPI_SWIGLU_BWD) return launch_direct_one<EPI_SWIGLU_BWD, false, BT>(a, s);
@@ -1084,7 +1176,8 @@ lsn_status launch_gemm(int layout, int wkind, int epi, GemmArgs a, hipStream_t s
   const Nf4Table &tab = nf4_table();
   for (int i = 0; i < 16; ++i) a.q[i] = tab.q[i];
   if (layout == GEMM_NT) {
-    if (wkind == W_IS_NF4) return launch_one<GEMM_NT, W_IS_NF4, EPI_BF16>(a, s);
+    if (wkind == W_IS_NF4)
+      return a.res ? launch_one<GEMM_NT, W_IS_NF4, EPI_BF16_RES>(a, s) : launch_one<GEMM_NT, W_IS_NF4, EPI_BF16>(a, s);
     return launch_one<GEMM_NT, W_IS_BF16, EPI_BF16>(a, s);
   }
   if (epi == EPI_SWIGLU_BWD)

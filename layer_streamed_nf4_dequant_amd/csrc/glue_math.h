@@ -63,7 +63,16 @@ __device__ __forceinline__ uint32_t add_bf16_word(uint32_t r, uint32_t v) {
 }
 
 // ---- SwiGLU --------------------------------------------------------------------------------
-__device__ __forceinline__ float sigmoid_f32(float z) { return __fdiv_rn(1.0f, __fadd_rn(1.0f, expf(-z))); }
+// sigma(z) = 1 / (1 + e^-z) from the hardware's base-2 exponential and reciprocal (v_exp_f32,
+// v_rcp_f32, each within 1 ulp): e^-z = 2^(-z log2 e), whose argument rounding adds a relative
+// error of about |z| 2^-24, so sigma is within (|z| + 4) 2^-24 relative of its exact value - far
+// inside the bf16 rounding of every output (a sigma below the fp32 normal range, z < -87, may come
+// out as 0). Five instructions against about thirty for the correctly rounded exp and division,
+// which matters where the SwiGLU runs in a GEMM's epilogue.
+__device__ __forceinline__ float sigmoid_f32(float z) {
+  const float e = __builtin_amdgcn_exp2f(__fmul_rn(z, -1.44269504088896340736f));
+  return __builtin_amdgcn_rcpf(__fadd_rn(1.0f, e));
+}
 
 // m = bf16( silu(g) u ) on eight bf16 pairs
 __device__ __forceinline__ u32x4_t swiglu8(u32x4_t gv, u32x4_t uv) {
