@@ -362,7 +362,8 @@ def main():
 
     import torch
     from layer_streamed_nf4_dequant_amd import configs, lib
-    from layer_streamed_nf4_dequant_amd.microbench import attention_figure, decoder_figure, glue_figure
+    from layer_streamed_nf4_dequant_amd.microbench import (attention_figure, decoder_figure, fused_glue_figure,
+                                                           glue_figure)
     from layer_streamed_nf4_dequant_amd.stack import Stack
 
     lib.load()
@@ -563,6 +564,9 @@ def main():
         print(f"[bench] lm_head_ce: {other['lm_head_ce']}", flush=True)
         other["glue"] = glue_figure(cfg)   # layer_streamed_nf4_dequant_amd/microbench.py
         print(f"[bench] glue: {other['glue']}", flush=True)
+        if not cfg.single:
+            other["fused_glue"] = fused_glue_figure(cfg)
+            print(f"[bench] fused glue: {other['fused_glue']}", flush=True)
         other["attention"] = attention_figure(cfg)
         print(f"[bench] attention: {other['attention']}", flush=True)
         if cfg.base == "nf4" and not cfg.single:

@@ -540,6 +540,15 @@ __device__ __forceinline__ void issue_direct1(char *lds_tile, __amdgpu_buffer_rs
 template <int N>
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14)); }
 
+// Workgroup barrier for LDS traffic only: orders the waves' LDS accesses across it (each wave
+// waits for its own LDS operations) but, unlike __syncthreads(), leaves the wave's global loads in
+// flight, so operands an epilogue has requested keep arriving while the tile goes through LDS.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Workgroup barrier of the double buffer: each wave waits for its own direct loads (the stage
 // about to be read) and its own LDS reads (of the stage about to be refilled), then meets the
 // others. __syncthreads() is not used because its memory fence is not needed here; the
@@ -865,7 +874,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       }
     };
     if constexpr (EPI == EPI_SWIGLU_BWD) fetch_gu(0, 0);
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 128 + 32 * i + (lane & 31);
@@ -880,7 +889,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
           *reinterpret_cast<uint2 *>(smem + r * kEpiPitch + c * 2) = o;
         }
     }
-    __syncthreads();
+    lds_barrier();
     if constexpr (EPI == EPI_SWIGLU) {
       // row r of the tile: gate columns n0 .. n0+127 in chunks 0-15, the same up columns in
       // chunks 16-31; a thread takes chunk c of both halves, 16 rows per pass

@@ -1,6 +1,6 @@
 """Micro-benchmarks of kernels that sit beside the streamed projection step: the decoder-layer
-glue (RMSNorm, rotary embedding, SwiGLU) and causal attention, at a stack configuration's token
-count, widths and heads.
+glue (RMSNorm, rotary embedding, SwiGLU; standalone and in the projections' epilogues) and causal
+attention, at a stack configuration's token count, widths and heads.
 
     python -m layer_streamed_nf4_dequant_amd.microbench [--config C3] [--iters 20]
     python -m layer_streamed_nf4_dequant_amd.microbench --decoder [--config C3] [--steps 3]
@@ -101,6 +101,84 @@ def glue_figure(cfg, iters: int = 20):
     return out
 
 
+def fused_glue_figure(cfg, iters: int = 10):
+    """The glue the decoder step runs in its projections' epilogues, at the workload's shapes with
+    bf16 (staged) weights: per fused call, its time, the plain projection's time and the
+    standalone glue kernel's time (HIP events over replayed HIP graphs), and what the fusion saves
+    (plain + glue - fused, microseconds per call)."""
+    import torch
+    from layer_streamed_nf4_dequant_amd import inputs, lib
+    T, H, I, KV, r, d = cfg.T, cfg.hidden, cfg.inter, cfg.kv, cfg.r, cfg.head_dim
+    nq, nkv = H // d, KV // d
+    theta = 500000.0
+    bf = dict(dtype=torch.bfloat16)
+    key = ("bench fused glue", cfg.name)
+
+    def lin(K, N, name):
+        W = inputs.device_normal((N, K), 0.02, 0, *key, name, "W", **bf)
+        A = inputs.device_normal((r, K), 0.01, 0, *key, name, "A", **bf)
+        B = inputs.device_normal((N, r), 0.01, 0, *key, name, "B", **bf)
+        return (W, A, B), lib.linear_desc(T, K, N, r, cfg.scale, W, A, B)
+
+    X = inputs.device_normal((T, H), 1.0, 0, *key, "X", **bf)
+    Xi = inputs.device_normal((T, I), 1.0, 0, *key, "Xi", **bf)
+    dY = inputs.device_normal((T, H), 1.0, 0, *key, "dY", **bf)
+    keep, D = [], {}
+    for name, K, N in (("q", H, H), ("k", H, KV), ("v", H, KV), ("o", H, H), ("gate", H, I), ("up", H, I),
+                       ("down", I, H)):
+        t, D[name] = lin(K, N, name)
+        keep.append(t)
+    U = [inputs.device_normal((T, r), 1.0, 0, *key, "U", j, **bf) for j in range(7)]
+    q, k, v, o = (torch.empty((T, n), **bf, device="cuda") for n in (H, KV, KV, H))
+    gate, up, m, dm, dg, du = (torch.empty((T, I), **bf, device="cuda") for _ in range(6))
+    res = inputs.device_normal((T, H), 1.0, 0, *key, "residual", **bf)
+    pos = torch.arange(T, dtype=torch.int32, device="cuda") % cfg.seq_len
+    tab = lib.rope_table(cfg.seq_len, d, theta)
+    rope = lib.rope_desc(tab, cfg.seq_len, d, pos)
+    dA = torch.empty((r, I), dtype=torch.float32, device="cuda")
+    dB = torch.empty((H, r), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lib.ws_bytes(T, I, H, r), dtype=torch.uint8, device="cuda")
+    RD = lib.ADAPTERS_U_READY
+    cases = {
+        "rope_in_qkv": (
+            lambda: lib.lora_linear_fwd_group_epi([D["q"], D["k"], D["v"]], X, [q, k, v], U[:3], adapters=RD,
+                                                  rope_mask=0b011, rope=rope),
+            lambda: lib.lora_linear_fwd_group([D["q"], D["k"], D["v"]], X, [q, k, v], U[:3], adapters=RD),
+            lambda: (lib.rope_apply(q, pos, nq, d, theta), lib.rope_apply(k, pos, nkv, d, theta))),
+        "residual_in_o": (
+            lambda: lib.lora_linear_fwd_group_epi([D["o"]], X, [o], U[3:4], adapters=RD, residual=[res]),
+            lambda: lib.lora_linear_fwd_group([D["o"]], X, [o], U[3:4], adapters=RD),
+            lambda: lib.add_bf16(res, o, q)),
+        "swiglu_in_gate_up_m_only": (
+            lambda: lib.lora_linear_fwd_swiglu(D["gate"], D["up"], X, m, Ug=U[4], Uu=U[5], adapters=RD),
+            lambda: lib.lora_linear_fwd_group([D["gate"], D["up"]], X, [gate, up], U[4:6], adapters=RD),
+            lambda: lib.swiglu_fwd(gate, up, m)),
+        "swiglu_in_gate_up_stored": (
+            lambda: lib.lora_linear_fwd_swiglu(D["gate"], D["up"], X, m, gate=gate, up=up, Ug=U[4], Uu=U[5],
+                                               adapters=RD),
+            lambda: lib.lora_linear_fwd_group([D["gate"], D["up"]], X, [gate, up], U[4:6], adapters=RD),
+            lambda: lib.swiglu_fwd(gate, up, m)),
+        "swiglu_bwd_in_down_dx": (
+            lambda: lib.lora_linear_bwd_swiglu(D["down"], Xi, dY, U[6], gate, up, dg, du, dA, dB, ws=ws),
+            lambda: lib.lora_linear_bwd(D["down"], Xi, dY, U[6], dm, dA, dB, ws=ws),
+            lambda: lib.swiglu_bwd(gate, up, dm, dg, du)),
+    }
+    out = {"timing": "graph"}
+    for name, fns in cases.items():
+        t = []
+        for fn in fns:
+            us = _time_calls(fn, iters)
+            if us is None:
+                out["timing"] = "eager"
+                us = _time_calls(fn, iters, graph=False)
+            t.append(us)
+        out[name] = {"fused_us": round(t[0], 1), "plain_us": round(t[1], 1), "glue_kernel_us": round(t[2], 1),
+                     "saved_us": round(t[1] + t[2] - t[0], 1)}
+    del keep, X, Xi, dY, U, q, k, v, o, gate, up, m, dm, dg, du, res, pos, tab, dA, dB, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def attention_figure(cfg, iters: int = 10):
     """Causal grouped-query attention at the configuration's T rows as T / seq_len sequences, its
     heads and head width: microseconds per forward and per backward call (graph-replayed) and
@@ -194,7 +272,8 @@ def main() -> None:
     if args.decoder:
         print(json.dumps({"decoder_step": decoder_figure(cfg, steps=args.steps)}), flush=True)
     else:
-        print(json.dumps({"glue": glue_figure(cfg, args.iters), "attention": attention_figure(cfg)}), flush=True)
+        print(json.dumps({"glue": glue_figure(cfg, args.iters), "fused_glue": fused_glue_figure(cfg),
+                          "attention": attention_figure(cfg)}), flush=True)
 
 
 if __name__ == "__main__":
