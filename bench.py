@@ -517,7 +517,20 @@ def main():
             torch.cuda.synchronize()
             other["streamed_keep_at_turn"] = round(cfg.T * n / (time.perf_counter() - t0), 1)
             print(f"[bench] streamed, keep at turn: {other['streamed_keep_at_turn']} tokens/s", flush=True)
-            stack.reset_pool(0)
+            # the same with an 8-slot pool (7 layers in flight ahead of the compute, 7 kept at each
+            # turn; 0.9 GB of slots at the 8B shape): how much of the streaming overhead a slightly
+            # larger pool removes
+            if cfg.layers >= 16:
+                stack.reset_pool(lib.POOL_KEEP_AT_TURN, n_slots=8)
+                c0 = stack.pool.stats()["copies"]
+                other["streamed_keep_at_turn_8_slots"] = round(timed_steps(stack, "streamed", n), 1)
+                other["streamed_keep_at_turn_8_slots_copies_per_step"] = round(
+                    (stack.pool.stats()["copies"] - c0) / (n + 1), 1)
+                print(f"[bench] streamed, keep at turn, 8 slots: {other['streamed_keep_at_turn_8_slots']} tokens/s "
+                      f"({other['streamed_keep_at_turn_8_slots_copies_per_step']} copies per step)", flush=True)
+                stack.reset_pool(0, n_slots=cfg.pool_slots)
+            else:
+                stack.reset_pool(0)
             # a DPO-style step: the frozen reference model's forward (one more streamed sweep with
             # the adapters off) before the training step
             torch.cuda.reset_peak_memory_stats()

@@ -215,8 +215,14 @@ def test_decoder_fused_dequant_matches_staged(gpu):
         res[dq] = (hb(m.loss), [hb(t) for l in range(m.L) for t in m.dA[l] + m.dB[l]])
         m.close()
     assert np.array_equal(res["fused"][0], res["staged"][0])
-    for a, b in zip(res["fused"][1], res["staged"][1]):
-        assert olora.rel_l2(a, b) <= 5e-3
+    errs = [olora.rel_l2(a, b) for a, b in zip(res["fused"][1], res["staged"][1])]
+    # per layer (bottom first), the dA then dB of q, k, v, o, gate, up, down: the top layer's
+    # down/gate/up gradients come before the first differing sum and agree bit for bit
+    n = len(errs) // TINY.layers
+    for l in range(TINY.layers):
+        print(f"  layer {l}: dA/dB rel-L2 fused vs staged " + " ".join(f"{e:.1e}" for e in errs[l * n:(l + 1) * n]),
+              flush=True)
+    assert max(errs) <= 5e-3
     torch.cuda.synchronize()
 
 
