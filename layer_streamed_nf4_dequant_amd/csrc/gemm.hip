@@ -482,6 +482,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs a) {
 constexpr int DBK = 64;
 constexpr int DTILE = 256 * DBK * 2;           // 32 KB: one operand, one stage
 constexpr int kEpiPitch = 256 * 2 + 16;        // bytes per LDS row of the bf16 output tile
+constexpr int kPosOffset = 256 * kEpiPitch;     // the rotary epilogue: the tile rows' positions (1 KB)
 
 __device__ __forceinline__ int dlds_off(int row, int chunk) {
   return (row * 8 + (chunk ^ ((row ^ (row >> 3)) & 7))) * 16;
@@ -682,6 +683,13 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     }
   };
 
+  if constexpr (EPI == EPI_BF16_ROPE) {
+    // the tile rows' table rows, for the epilogue (an LDS area of their own, past the tile)
+    if (sg.rope) {
+      const int64_t m = min(m0 + t, a.M - 1);
+      reinterpret_cast<int *>(smem + kPosOffset)[t] = min(max(a.x.positions[m], 0), a.x.n_pos - 1);
+    }
+  }
   // stage 0 <- step 0 (first, so that its latency overlaps the LoRA prologue)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -847,10 +855,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     if constexpr (EPI == EPI_BF16_ROPE) {
       if (sg.rope) {
 #pragma unroll
-        for (int p = 0; p < BM / (NT / 16); ++p) {
-          const int64_t m = m0 + p * (NT / 16) + (t >> 4);
-          posv[p] = m < a.M ? min(max(a.x.positions[m], 0), a.x.n_pos - 1) : 0;
-        }
+        for (int p = 0; p < BM / (NT / 16); ++p)
+          posv[p] = reinterpret_cast<const int *>(smem + kPosOffset)[p * (NT / 16) + (t >> 4)];
       }
     }
     if constexpr (EPI == EPI_BF16_RES) {
@@ -861,6 +867,25 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
           pre[p] = m < a.M && n_ok ? *reinterpret_cast<const u32x4_t *>(sg.res + m * sg.N + n) : u32x4_t{0, 0, 0, 0};
         }
       }
+    }
+    // rotary embedding (EPI_BF16_ROPE): thread k = t % 16 of a row takes 8 pairs of one head, the
+    // chunk at column c1 and its partner D/2 to the right, 16 rows per pass; the (cos, sin) table
+    // rows of a batch of 4 passes are loaded a batch ahead, the first batch before the LDS pass
+    const int D = EPI == EPI_BF16_ROPE ? a.x.rope_dim : 128, half = D / 2, cph = half / 8, k = t & 15;
+    const int c1 = (k / cph) * D + 8 * (k % cph), c2 = c1 + half;
+    const int64_t n1 = n0 + c1;
+    const float *cs = a.x.rope_cs + 16 * (k % cph);
+    constexpr int PB = 4, NPR = BM / (NT / 16);
+    floatx4_t tb[2][PB][4];
+    auto fetch_cs = [&](int buf, int b) {
+#pragma unroll
+      for (int q = 0; q < PB; ++q)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          tb[buf][q][w] = *reinterpret_cast<const floatx4_t *>(cs + (int64_t)posv[b * PB + q] * D + 4 * w);
+    };
+    if constexpr (EPI == EPI_BF16_ROPE) {
+      if (sg.rope) fetch_cs(0, 0);
     }
     constexpr int SB = 8;                         // SwiGLU backward: rows per batch
     u32x4_t gbuf[2][SB], ubuf[2][SB];
@@ -934,23 +959,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       return;
     }
     if (EPI == EPI_BF16_ROPE && sg.rope) {   // (a constant false in the other kernels)
-      // rotary embedding of the rounded tile (columns = whole heads of D): thread k = t % 16
-      // of a row takes 8 pairs of one head, the chunk at column c1 and its partner D/2 to the
-      // right; 16 rows per pass; the table rows of a batch of 4 passes are loaded a batch ahead
-      const int D = a.x.rope_dim, half = D / 2, cph = half / 8, k = t & 15;
-      const int c1 = (k / cph) * D + 8 * (k % cph), c2 = c1 + half;
-      const int64_t n1 = n0 + c1;
-      const float *cs = a.x.rope_cs + 16 * (k % cph);
-      constexpr int PB = 4, NPR = BM / (NT / 16);
-      floatx4_t tb[2][PB][4];
-      auto fetch_cs = [&](int buf, int b) {
-#pragma unroll
-        for (int q = 0; q < PB; ++q)
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            tb[buf][q][w] = *reinterpret_cast<const floatx4_t *>(cs + (int64_t)posv[b * PB + q] * D + 4 * w);
-      };
-      fetch_cs(0, 0);
+      // the rotary embedding of the rounded tile (columns = whole heads of D)
 #pragma unroll
       for (int b = 0; b < NPR / PB; ++b) {
         if (b + 1 < NPR / PB) fetch_cs((b + 1) & 1, b + 1);
@@ -1046,17 +1055,19 @@ int64_t seg_ntiles(int64_t N, int epi) {
 
 template <int EPI, bool KSEG, bool BT, bool SPLIT = false>
 lsn_status launch_direct_one(const DirectArgs &a, hipStream_t s) {
+  constexpr size_t smem_bytes = kDirectSmemBytes + (EPI == EPI_BF16_ROPE ? 256 * sizeof(int) : 0);
+  static_assert(EPI != EPI_BF16_ROPE || kPosOffset == (int)kDirectSmemBytes, "positions past the tile");
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_direct<EPI, KSEG, BT, SPLIT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDirectSmemBytes);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_bytes);
     if (e != hipSuccess) return check_hip(e, "gemm_direct smem attribute");
     attr_set = true;
   }
   int64_t ntiles_n = 0;
   for (int q = 0; q < a.nseg; ++q) ntiles_n += seg_ntiles(a.seg[q].N, EPI);
   const int64_t tiles = ((a.M + BM - 1) / BM) * ntiles_n * (SPLIT ? a.ksplit : 1);
-  hipLaunchKernelGGL((k_gemm_direct<EPI, KSEG, BT, SPLIT>), dim3((unsigned)tiles), dim3(NT), kDirectSmemBytes, s, a);
+  hipLaunchKernelGGL((k_gemm_direct<EPI, KSEG, BT, SPLIT>), dim3((unsigned)tiles), dim3(NT), smem_bytes, s, a);
   return check_hip(hipGetLastError(), "k_gemm_direct launch");
 }
 

@@ -206,7 +206,10 @@ def test_decoder_fused_dequant_matches_staged(gpu):
     forward (and the loss) is identical; only the grouped backward's input-gradient sum runs in
     another order (member by member). That fp32 rounding difference can flip the bf16 rounding
     of an activation gradient further down (one element by 2^-8), and such flips travel through
-    the layers below, so the gradients agree to 5e-3 rel-L2 (half the oracle bar)."""
+    the layers below. Measured (deterministic, the same on every box): the top layer's gate, up
+    and down gradients, computed before the first differing sum, are bit-identical; its q, k, v
+    and o gradients differ by 1e-6 to 4e-4 and the bottom layer's by up to 7.4e-4 rel-L2. The
+    bar is 2e-3 (a fifth of the oracle bar)."""
     import torch
     res = {}
     for dq in ("staged", "fused"):
@@ -222,7 +225,9 @@ def test_decoder_fused_dequant_matches_staged(gpu):
     for l in range(TINY.layers):
         print(f"  layer {l}: dA/dB rel-L2 fused vs staged " + " ".join(f"{e:.1e}" for e in errs[l * n:(l + 1) * n]),
               flush=True)
-    assert max(errs) <= 5e-3
+    top = errs[(TINY.layers - 1) * n:]
+    assert all(top[j] == 0.0 for j in (4, 5, 6, 11, 12, 13))   # gate, up, down: dA and dB
+    assert max(errs) <= 2e-3
     torch.cuda.synchronize()
 
 
