@@ -165,6 +165,10 @@ lsn_status nf4_dequant_batch(int32_t n, const lsn_nf4 *w, void *const *out, int3
  * dX [T][K], dA [r][K] fp32, dB [N][r] fp32. W is re-dequantised on every call from the
  * bytes the descriptor points at (a pool slot or a resident buffer): nothing is cached.
  * Requirements: T >= 1, K % 64 == 0, N % 64 == 0, r in {8, 16, 24, 32}, and the NF4 rules for W.
+ * The scale enters the GEMMs' LoRA terms on the bf16 operand, as (bf16(s U)) B^T and
+ * (bf16(s G)) A: exact, i.e. s (U B^T) and s (G A) with their fp32 sums' rounding, when s is a
+ * power of two (alpha and r powers of two, as in every configuration here); another s rounds
+ * s u to bf16 once per element. dA and dB scale their fp32 sums.
  * ---------------------------------------------------------------------------------------- */
 typedef struct {
   int64_t T, K, N, r;

@@ -96,7 +96,6 @@ struct DirectArgs {
   int adapters;
   int b_red_major;       // B operand stored [K][N] (N contiguous) instead of [N][K]
   int ksplit;            // > 1: split-K into fp32 partials out + s M N (reduction-major B, fp32 store)
-  int scale_pow2;        // set by launch_gemm_direct
   EpiOps x;
 };
 lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s);

@@ -20,10 +20,12 @@
 // chunk ^ ((row ^ row >> 3) & 7), so both the row-wise writes and the 32-row fragment reads
 // hit distinct banks.
 //
-// The LoRA term runs first: the accumulators start as s * (U B^T) (forward) or s * (G A)
-// (backward), from r-wide MFMA steps whose operands come straight from global memory, and
-// the base product accumulates on top. With adapters off they start at +0, which is also
-// what B = 0 gives, so adapters-off and B = 0 produce identical bits.
+// The LoRA term runs first: the accumulators start as (s U) B^T (forward) or (s G) A
+// (backward), from r-wide MFMA steps whose operands come straight from global memory, with the
+// scale applied to the bf16 U (or G) fragments, bf16(s u): exact for a power-of-two s, so the
+// result is then s (U B^T) in the fp32 sum's own rounding; any other s rounds s u to bf16 once.
+// The base product accumulates on top. With adapters off the accumulators start at +0, which is
+// also what B = 0 gives, so adapters-off and B = 0 produce identical bits.
 //
 // Determinism: the reduction order is fixed by the tiling (which depends only on shapes);
 // there are no atomics.
@@ -324,17 +326,16 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs a) {
       for (int i = 0; i < 4; ++i) fa[i] = lora_act_frag(a, m0 + wm * 128 + 32 * i + (lane & 31), j0, lane);
 #pragma unroll
       for (int j = 0; j < 4; ++j) fb[j] = lora_w_frag<LAYOUT>(a, n0 + wn * 128 + 32 * j + (lane & 31), j0, lane);
+      // the scale on the activation-side fragments: bf16(s u), as the direct-load GEMM does
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fa[i][e] = (__bf16)((float)fa[i][e] * a.scale);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = __fmul_rn(a.scale, acc[i][j][e]);
   }
 
   const int nk = (int)(a.Kred / BK);
@@ -724,32 +725,19 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
         if (n < sg.N && jl < a.r) v = *reinterpret_cast<const u32x4_t *>(lr_w + n * a.r + jl);
         lb[j] = as_bf16x8(v);
       }
-      if (a.scale_pow2) {
-        // s = 2^e: scaling the bf16 U fragments is exact (as are all the fp32 partial sums of
-        // the products), so the result is bit-identical to scaling the fp32 sum afterwards
+      // the scale on the U fragments, bf16(s u): for s a power of two (alpha / r with both powers
+      // of two, the usual case) exact, as are then all the fp32 partial sums, so the result is
+      // bit-identical to scaling the fp32 sum; any other s rounds s u to bf16 once
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) la[i][e] = (__bf16)((float)la[i][e] * a.scale);
-      }
+        for (int e = 0; e < 8; ++e) la[i][e] = (__bf16)((float)la[i][e] * a.scale);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lb[j], la[i], acc[i][j], 0, 0, 0);
     }
    }
-    if (!a.scale_pow2) {
-      // one accumulator block at a time (the fences keep the compiler from moving all 256
-      // accumulators into vector registers at once)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[i][j][e] = __fmul_rn(a.scale, acc[i][j][e]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    }
   }
 
   // fragment q of sub-step s2 (16 K-columns) of a stage, in consumption order: 0 -> fa0,
@@ -1118,12 +1106,6 @@ lsn_status launch_direct_epi(const DirectArgs &a, int epi, hipStream_t s) {
 }  // namespace
 
 lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s) {
-  // a power-of-two scale s >= 1 (s = alpha / r with alpha and r powers of two, the usual case)
-  // is applied exactly to the bf16 U fragments instead of to the fp32 accumulators
-  int e2 = 0;
-  // (s >= 1, so no scaled bf16 value can lose bits by turning subnormal; exact unless s * U
-  // overflows)
-  a.scale_pow2 = std::isfinite(a.scale) && a.scale >= 1.0f && std::frexp(a.scale, &e2) == 0.5f && e2 <= 64;
   int64_t t0 = 0;
   for (int q = 0; q < a.nseg; ++q) {
     a.seg[q].ntile0 = t0;

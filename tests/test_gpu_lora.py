@@ -167,6 +167,33 @@ def test_fused_nf4_equals_bf16_gemm_on_dequantised_weights(gpu, T, K, N):
         assert _eq(a, b)
 
 
+@pytest.mark.parametrize("scale", [1.5, 0.75, 4.0])
+def test_scale_not_one_or_two(gpu, scale):
+    """Scales other than the configurations' 2 (alpha = 24, 12 or 64 at r = 16): the oracle's s U B^T
+    against the GEMMs' (bf16(s U)) B^T, the dequant-into-LDS GEMM bit-identical to the bf16 one on
+    the dequantised weights, and the bf16 path with a power-of-two s bit-identical to scaling by
+    hand: s = 4 on (U, B) equals s = 1 on (4 U, B), 4 U being exact in bf16."""
+    import torch
+    print(f"case: scale {scale}", flush=True)
+    c = Case(300, 512, 640, scale=scale, tag="scale")
+    _full_parity(c)
+    w16 = lib.nf4_dequant(c.Wd, "bf16")
+    Y1, U1 = c.gpu_fwd()
+    Y2, U2 = c.gpu_fwd(W=w16)
+    dX1, dA1, dB1 = c.gpu_bwd(U1)
+    dX2, dA2, dB2 = c.gpu_bwd(U2, W=w16)
+    torch.cuda.synchronize()
+    for a, b in ((Y1, Y2), (U1, U2), (dX1, dX2), (dA1, dA2), (dB1, dB2)):
+        assert _eq(a, b)
+    if scale == 4.0:
+        Y3 = torch.empty_like(Y2)
+        U4 = (U2.float() * 4.0).to(torch.bfloat16)
+        d1 = lib.linear_desc(c.T, c.K, c.N, c.r, 1.0, w16, c.Ad, c.Bd)
+        lib.lora_linear_fwd(d1, c.Xd, Y3, U4, adapters=lib.ADAPTERS_U_READY, ws=c.ws)
+        torch.cuda.synchronize()
+        assert _eq(Y2, Y3)
+
+
 @pytest.mark.parametrize("base", ["nf4", "bf16"])
 def test_grouped_forward_equals_single_forwards(gpu, base):
     """Five linears sharing one input (a decoder layer's q, k, v, gate, up at small widths),
