@@ -38,8 +38,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kB = 64;                       // rows per block (queries or keys)
 constexpr int kTP = kB * 2 + 16;             // pitch (bytes) of a transposed tile: [D][64] + pad
-constexpr int kFwdThreads = 512;             // forward: 8 waves of 16 queries share each K/V tile
-constexpr int kFwdQ = 128;                   // queries per forward workgroup
+constexpr int kFwdThreads = 512;             // dQ: 8 waves of 16 queries share each K/V tile
+constexpr int kFwdQ = 128;                   // queries per forward / dQ workgroup
+constexpr int kFwd2Threads = 256;            // forward: 4 waves of 32 queries (two groups of 16)
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
@@ -267,14 +268,17 @@ __device__ __forceinline__ bf16x8 tr_frag_rm(const char *tile, int j, int c, int
 }
 
 // ------------------------------------------------------------------------------------------
-// Forward: one workgroup of 8 waves per (128-query block, sequence, query head), heaviest blocks
-// first; a wave skips the key blocks that lie entirely after its 16 queries. K and V blocks of
-// 64 keys stream through two LDS stages by direct-to-LDS loads (each wave issues its share of
-// the next block right after the barrier that frees its stage), so the workgroup meets once per
-// block and no thread spends instructions on staging.
+// Forward: one workgroup of 4 waves per (128-query block, sequence, query head), heaviest blocks
+// first. A wave owns 32 queries as two groups of 16 (one query of each group per MFMA lane
+// column), so every K and V fragment it reads from LDS feeds the MFMAs of both groups: half the
+// LDS reads per MFMA of 16-query waves. A wave skips the key blocks that lie entirely after its
+// queries. K and V blocks of 64 keys stream through two LDS stages by direct-to-LDS loads (each
+// wave issues its share of the next block right after the barrier that frees its stage), so the
+// workgroup meets once per block and no thread spends instructions on staging.
 template <int D>
-__global__ __launch_bounds__(kFwdThreads) void k_attn_fwd(AttnArgs a) {
+__global__ __launch_bounds__(kFwd2Threads, 2) void k_attn_fwd(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * DTile<D>::BYTES];   // [stage][K, V]
+  constexpr int NG = 2;                            // query groups of 16 per wave
   const int nqb = (int)((a.S + kFwdQ - 1) / kFwdQ);
   const int64_t per = a.n_seq * a.n_q;
   const int qb = nqb - 1 - (int)(blockIdx.x / per);
@@ -283,20 +287,30 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_fwd(AttnArgs a) {
   const int h = (int)(rest % a.n_q), hk = h / (a.n_q / a.n_kv);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
   const int S = (int)a.S;
-  const int wq0 = qb * kFwdQ + 16 * wave;          // this wave's first query
-  const int q_in_seq = wq0 + col;
+  const int wq0 = qb * kFwdQ + 16 * NG * wave;     // this wave's first query
   const int64_t seq0 = b * a.S;
+  int qis[NG];                                     // the lane's query of each group
+#pragma unroll
+  for (int u = 0; u < NG; ++u) qis[u] = wq0 + 16 * u + col;
 
-  bf16x8 qf[D / 32];   // B operand of S^T = K Q^T: query `col`, dims 32 c + 8 g ..
+  bf16x8 qf[NG][D / 32];   // B operands of S^T = K Q^T: query qis[u], dims 32 c + 8 g ..
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c)
-    qf[c] = q_in_seq < S
-                ? as_bf(*reinterpret_cast<const u32x4_t *>(a.q + (seq0 + q_in_seq) * a.ldq + h * D + 32 * c + 8 * g))
-                : as_bf(u32x4_t{0u, 0u, 0u, 0u});
-  floatx4 acc[D / 16];   // O^T: dims 16 j + 4 g + e of query `col`
+  for (int u = 0; u < NG; ++u)
 #pragma unroll
-  for (int j = 0; j < D / 16; ++j) acc[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY, l = 0.0f;
+    for (int c = 0; c < D / 32; ++c)
+      qf[u][c] = qis[u] < S ? as_bf(*reinterpret_cast<const u32x4_t *>(a.q + (seq0 + qis[u]) * a.ldq + h * D + 32 * c + 8 * g))
+                            : as_bf(u32x4_t{0u, 0u, 0u, 0u});
+  floatx4 acc[NG][D / 16];   // O^T: dims 16 j + 4 g + e of query qis[u]
+#pragma unroll
+  for (int u = 0; u < NG; ++u)
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) acc[u][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m[NG], l[NG];
+#pragma unroll
+  for (int u = 0; u < NG; ++u) {
+    m[u] = -INFINITY;
+    l[u] = 0.0f;
+  }
   const float c2 = a.scale * kLog2e;
 
   // the key blocks run up to the one holding the workgroup's last query
@@ -304,7 +318,8 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_fwd(AttnArgs a) {
   const int kb_last = (q_end - 1) / kB;
   const __amdgpu_buffer_rsrc_t rk = rsrc_of(a.k + seq0 * a.ldk + hk * D, a.S * a.ldk * 2);
   const __amdgpu_buffer_rsrc_t rv = rsrc_of(a.v + seq0 * a.ldv + hk * D, a.S * a.ldv * 2);
-  constexpr int SEGW = DTile<D>::SEGS / 8;        // segments of each tile per wave
+  constexpr int NW = kFwd2Threads / 64;
+  constexpr int SEGW = DTile<D>::SEGS / NW;       // segments of each tile per wave
   // the wave's share of block kb: segments wave * SEGW .. of the K tile and of the V tile
   auto issue = [&](int kb) {
     const int nvalid = S - kb * kB < kB ? S - kb * kB : kB;
@@ -321,92 +336,111 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_fwd(AttnArgs a) {
   for (int kb = 0; kb <= kb_last; ++kb) {
     tile_barrier();                                // block kb has landed; stage (kb+1)&1 is free
     if (kb < kb_last) issue(kb + 1);
-    if (kb * kB > wq0 + 15) continue;              // every key of the block is after this wave's queries
+    if (kb * kB > wq0 + 16 * NG - 1) continue;     // every key of the block is after this wave's queries
     const bool diag = kb * kB + kB - 1 > wq0;      // some key of the block is after some query here
     const char *k_t = smem + (kb & 1) * 2 * DTile<D>::BYTES;
     const char *v_t = k_t + DTile<D>::BYTES;
 
-    // S^T tile tt: keys 16 tt + 4 g + e (rows) x query `col`; two tiles per half
-    floatx4 s[4];
+    // S^T tile tt of group u: keys 16 tt + 4 g + e (rows) x query qis[u]; two key tiles per half
+    floatx4 s[NG][4];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       bf16x8 kf[2][D / 32];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) kf[u][c] = sw_frag<D>(k_t, 16 * (2 * hf + u) + col, 4 * c + g);
+        for (int c = 0; c < D / 32; ++c) kf[t][c] = sw_frag<D>(k_t, 16 * (2 * hf + t) + col, 4 * c + g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        s[2 * hf + u] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) s[2 * hf + u] = mfma(kf[u][c], qf[c], s[2 * hf + u]);
-      }
+        for (int u = 0; u < NG; ++u) {
+          s[u][2 * hf + t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c) s[u][2 * hf + t] = mfma(kf[t][c], qf[u][c], s[u][2 * hf + t]);
+        }
       AT_MFMA_FENCE();
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) asm volatile("" ::"v"(kf[u][c]));
+        for (int c = 0; c < D / 32; ++c) asm volatile("" ::"v"(kf[t][c]));
     }
-    // online softmax in the exp2 domain
-    float mx = -INFINITY;
+    // online softmax in the exp2 domain, per group
     const int key0 = kb * kB + 4 * g;
+    bool moved = false;
+    float alpha[NG];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int u = 0; u < NG; ++u) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = s[tt][e] * c2;
-        if (diag && key0 + 16 * tt + e > q_in_seq) x = -INFINITY;
-        s[tt][e] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = ex2(m - m_new);
-    float rs = 0.0f;
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+        for (int e = 0; e < 4; ++e) {
+          float x = s[u][tt][e] * c2;
+          if (diag && key0 + 16 * tt + e > qis[u]) x = -INFINITY;
+          s[u][tt][e] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m[u], mx);
+      alpha[u] = ex2(m[u] - m_new);
+      float rs = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[tt][e] = ex2(s[tt][e] - m_new);
-        rs += s[tt][e];
-      }
-    rs += __shfl_xor(rs, 16);
-    rs += __shfl_xor(rs, 32);
-    l = l * alpha + rs;
-    m = m_new;
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[u][tt][e] = ex2(s[u][tt][e] - m_new);
+          rs += s[u][tt][e];
+        }
+      rs += __shfl_xor(rs, 16);
+      rs += __shfl_xor(rs, 32);
+      l[u] = l[u] * alpha[u] + rs;
+      m[u] = m_new;
+      moved = moved || alpha[u] != 1.0f;
+    }
     // rescale only when some lane's running max moved (multiplying by exactly 1 changes nothing)
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
-      for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
+      for (int u = 0; u < NG; ++u)
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) acc[u][j] *= alpha[u];
     }
     // O^T += V^T P^T over the block's 64 keys (two reduction steps of 32); V^T fragments come
-    // from the row-major V tile by transpose reads
+    // from the row-major V tile by transpose reads and serve both groups
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const bf16x8 pf = acc_frag(s[2 * c], s[2 * c + 1]);
+      bf16x8 pf[NG];
+#pragma unroll
+      for (int u = 0; u < NG; ++u) pf[u] = acc_frag(s[u][2 * c], s[u][2 * c + 1]);
       bf16x8 vf[D / 16];
 #pragma unroll
       for (int jj = 0; jj < D / 16; ++jj) vf[jj] = tr_frag_rm<D>(v_t, jj, c, g, lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int jj = 0; jj < D / 16; ++jj) acc[jj] = mfma(vf[jj], pf, acc[jj]);
+      for (int jj = 0; jj < D / 16; ++jj)
+#pragma unroll
+        for (int u = 0; u < NG; ++u) acc[u][jj] = mfma(vf[jj], pf[u], acc[u][jj]);
       AT_MFMA_FENCE();
-      asm volatile("" ::"v"(pf));
+#pragma unroll
+      for (int u = 0; u < NG; ++u) asm volatile("" ::"v"(pf[u]));
 #pragma unroll
       for (int jj = 0; jj < D / 16; ++jj) asm volatile("" ::"v"(vf[jj]));
     }
   }
-  if (q_in_seq < S) {
-    const float inv = 1.0f / l;
-    uint16_t *orow = a.out_o + (seq0 + q_in_seq) * a.ld_out_o + h * D;
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      const u32x2 w = {pack_bf16x2(acc[j][0] * inv, acc[j][1] * inv), pack_bf16x2(acc[j][2] * inv, acc[j][3] * inv)};
-      *reinterpret_cast<u32x2 *>(orow + 16 * j + 4 * g) = w;
+  for (int u = 0; u < NG; ++u) {
+    if (qis[u] < S) {
+      const float inv = 1.0f / l[u];
+      uint16_t *orow = a.out_o + (seq0 + qis[u]) * a.ld_out_o + h * D;
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) {
+        const u32x2 w = {pack_bf16x2(acc[u][j][0] * inv, acc[u][j][1] * inv),
+                         pack_bf16x2(acc[u][j][2] * inv, acc[u][j][3] * inv)};
+        *reinterpret_cast<u32x2 *>(orow + 16 * j + 4 * g) = w;
+      }
+      if (g == 0) a.lse[(seq0 + qis[u]) * a.n_q + h] = (m[u] + log2f(l[u])) * 0.69314718055994531f;
     }
-    if (g == 0) a.lse[(seq0 + q_in_seq) * a.n_q + h] = (m + log2f(l)) * 0.69314718055994531f;
   }
 }
 
@@ -783,9 +817,9 @@ lsn_status attention_fwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, in
   a.ld_out_o = ldo;
   const unsigned grid = (unsigned)(((S + kFwdQ - 1) / kFwdQ) * n_seq * n_q);
   if (head_dim == 128)
-    hipLaunchKernelGGL(k_attn_fwd<128>, dim3(grid), dim3(kFwdThreads), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(k_attn_fwd<128>, dim3(grid), dim3(kFwd2Threads), 0, (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL(k_attn_fwd<64>, dim3(grid), dim3(kFwdThreads), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(k_attn_fwd<64>, dim3(grid), dim3(kFwd2Threads), 0, (hipStream_t)stream, a);
   return check_hip(hipGetLastError(), "k_attn_fwd launch");
 }
 
