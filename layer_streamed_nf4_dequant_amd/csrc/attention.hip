@@ -41,6 +41,11 @@ constexpr int kTP = kB * 2 + 16;             // pitch (bytes) of a transposed ti
 constexpr int kFwdThreads = 512;             // dQ: 8 waves of 16 queries share each K/V tile
 constexpr int kFwdQ = 128;                   // queries per forward / dQ workgroup
 constexpr int kFwd2Threads = 256;            // forward: 4 waves of 32 queries (two groups of 16)
+// dQ: groups of 16 queries per wave. Two groups (4 waves of 32 queries) need 327 registers per
+// lane without spilling, so one wave per SIMD, and the whole backward ran 13% slower at the 8B
+// shape than with one group (8 waves of 16, two per SIMD); squeezed into two waves per SIMD they
+// spill 64 bytes per lane and the backward ran 2.5% faster. One group, without spills.
+constexpr int kDqGroups = 1;
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
@@ -618,11 +623,13 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
 
 // ------------------------------------------------------------------------------------------
 // dQ: one workgroup per (query block, sequence, query head), heaviest blocks first; a wave owns
-// 16 queries (lane column = query) and loops over the key blocks up to its own. K and V blocks
+// 16 NG queries as NG groups of 16 (lane column = one query of each group) and loops over the key
+// blocks up to its own; every K and V fragment it reads serves all its groups. K and V blocks
 // stream through two LDS stages by direct-to-LDS loads (row-major; K^T fragments by transpose
 // reads), as in the forward.
-template <int D>
-__global__ __launch_bounds__(kFwdThreads) void k_attn_bwd_q(AttnArgs a) {
+template <int D, int NG>
+__global__ __launch_bounds__(kFwdQ / NG * 4) void k_attn_bwd_q(AttnArgs a) {
+  constexpr int NT = kFwdQ / NG * 4;               // 8 waves of 16 queries, or 4 of 32
   __shared__ __attribute__((aligned(1024))) char smem[4 * DTile<D>::BYTES];   // [stage][K, V]
   const int nqb = (int)((a.S + kFwdQ - 1) / kFwdQ);
   const int64_t per = a.n_seq * a.n_q;
@@ -632,30 +639,35 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_bwd_q(AttnArgs a) {
   const int h = (int)(rest % a.n_q), hk = h / (a.n_q / a.n_kv);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
   const int S = (int)a.S;
-  const int wq0 = qb * kFwdQ + 16 * wave;          // this wave's first query
-  const int q_in_seq = wq0 + col;
+  const int wq0 = qb * kFwdQ + 16 * NG * wave;     // this wave's first query
   const int64_t seq0 = b * a.S;
-  const bool qvalid = q_in_seq < S;
-  bf16x8 qf[D / 32], df[D / 32];   // B operands: query `col`, dims 32 c + 8 g ..
+  int qis[NG];
+  bf16x8 qf[NG][D / 32], df[NG][D / 32];   // B operands: query qis[u], dims 32 c + 8 g ..
+  float lse2[NG], dq_dot[NG];
+  floatx4 acc[NG][D / 16];   // dQ^T: dims 16 j + 4 g + e of query qis[u]
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c) {
-    qf[c] = qvalid ? as_bf(*reinterpret_cast<const u32x4_t *>(a.q + (seq0 + q_in_seq) * a.ldq + h * D + 32 * c + 8 * g))
-                   : as_bf(u32x4_t{0u, 0u, 0u, 0u});
-    df[c] = qvalid ? as_bf(*reinterpret_cast<const u32x4_t *>(a.dO + (seq0 + q_in_seq) * a.lddo + h * D + 32 * c + 8 * g))
-                   : as_bf(u32x4_t{0u, 0u, 0u, 0u});
+  for (int u = 0; u < NG; ++u) {
+    qis[u] = wq0 + 16 * u + col;
+    const bool qvalid = qis[u] < S;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      qf[u][c] = qvalid ? as_bf(*reinterpret_cast<const u32x4_t *>(a.q + (seq0 + qis[u]) * a.ldq + h * D + 32 * c + 8 * g))
+                        : as_bf(u32x4_t{0u, 0u, 0u, 0u});
+      df[u][c] = qvalid ? as_bf(*reinterpret_cast<const u32x4_t *>(a.dO + (seq0 + qis[u]) * a.lddo + h * D + 32 * c + 8 * g))
+                        : as_bf(u32x4_t{0u, 0u, 0u, 0u});
+    }
+    lse2[u] = qvalid ? a.lse[(seq0 + qis[u]) * a.n_q + h] * kLog2e : INFINITY;
+    dq_dot[u] = qvalid ? a.dot[(seq0 + qis[u]) * a.n_q + h] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) acc[u][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  const float lse2 = qvalid ? a.lse[(seq0 + q_in_seq) * a.n_q + h] * kLog2e : INFINITY;
-  const float dq_dot = qvalid ? a.dot[(seq0 + q_in_seq) * a.n_q + h] : 0.0f;
-  floatx4 acc[D / 16];   // dQ^T: dims 16 j + 4 g + e of query `col`
-#pragma unroll
-  for (int j = 0; j < D / 16; ++j) acc[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   const float c2 = a.scale * kLog2e;
 
   const int q_end = (qb + 1) * kFwdQ < S ? (qb + 1) * kFwdQ : S;   // one past the last query
   const int kb_last = (q_end - 1) / kB;
   const __amdgpu_buffer_rsrc_t rk = rsrc_of(a.k + seq0 * a.ldk + hk * D, a.S * a.ldk * 2);
   const __amdgpu_buffer_rsrc_t rv = rsrc_of(a.v + seq0 * a.ldv + hk * D, a.S * a.ldv * 2);
-  constexpr int SEGW = DTile<D>::SEGS / 8;
+  constexpr int SEGW = DTile<D>::SEGS / (NT / 64);
   auto issue = [&](int kb) {
     const int nvalid = S - kb * kB < kB ? S - kb * kB : kB;
     char *st = smem + (kb & 1) * 2 * DTile<D>::BYTES;
@@ -671,71 +683,76 @@ __global__ __launch_bounds__(kFwdThreads) void k_attn_bwd_q(AttnArgs a) {
   for (int kb = 0; kb <= kb_last; ++kb) {
     tile_barrier();
     if (kb < kb_last) issue(kb + 1);
-    if (kb * kB > wq0 + 15) continue;  // every key of the block is after this wave's queries
+    if (kb * kB > wq0 + 16 * NG - 1) continue;  // every key of the block is after this wave's queries
     const bool diag = kb * kB + kB - 1 > wq0;
     const char *k_t = smem + (kb & 1) * 2 * DTile<D>::BYTES;
     const char *v_t = k_t + DTile<D>::BYTES;
 
-    // S^T and dP^T tiles tt: keys 16 tt + 4 g + e (rows) x query `col`; two tiles per half
-    floatx4 s[4], dp[4];
+    // S^T and dP^T tiles tt of group u: keys 16 tt + 4 g + e (rows) x query qis[u]; one key tile
+    // at a time
+    floatx4 s[NG][4], dp[NG][4];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      bf16x8 ka[2][D / 32], va[2][D / 32];
+    for (int tt = 0; tt < 4; ++tt) {
+      bf16x8 ka[D / 32], va[D / 32];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
-          ka[u][c] = sw_frag<D>(k_t, 16 * (2 * hf + u) + col, 4 * c + g);
-          va[u][c] = sw_frag<D>(v_t, 16 * (2 * hf + u) + col, 4 * c + g);
-        }
+      for (int c = 0; c < D / 32; ++c) {
+        ka[c] = sw_frag<D>(k_t, 16 * tt + col, 4 * c + g);
+        va[c] = sw_frag<D>(v_t, 16 * tt + col, 4 * c + g);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int tt = 2 * hf + u;
-        s[tt] = dp[tt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int u = 0; u < NG; ++u) {
+        s[u][tt] = dp[u][tt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
-          s[tt] = mfma(ka[u][c], qf[c], s[tt]);
-          dp[tt] = mfma(va[u][c], df[c], dp[tt]);
+          s[u][tt] = mfma(ka[c], qf[u][c], s[u][tt]);
+          dp[u][tt] = mfma(va[c], df[u][c], dp[u][tt]);
         }
       }
       AT_MFMA_FENCE();
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
-          asm volatile("" ::"v"(ka[u][c]));
-          asm volatile("" ::"v"(va[u][c]));
-        }
+      for (int c = 0; c < D / 32; ++c) {
+        asm volatile("" ::"v"(ka[c]));
+        asm volatile("" ::"v"(va[c]));
+      }
     }
     const int key0 = kb * kB + 4 * g;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int u = 0; u < NG; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float p = ex2(s[tt][e] * c2 - lse2);
-        if (diag && key0 + 16 * tt + e > q_in_seq) p = 0.0f;
-        dp[tt][e] = p * (dp[tt][e] - dq_dot);
-      }
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float p = ex2(s[u][tt][e] * c2 - lse2[u]);
+          if (diag && key0 + 16 * tt + e > qis[u]) p = 0.0f;
+          dp[u][tt][e] = p * (dp[u][tt][e] - dq_dot[u]);
+        }
     // dQ^T += K^T dS^T over the block's 64 keys (two steps of 32); K^T fragments by transpose
-    // reads of the row-major K tile
+    // reads of the row-major K tile, serving every group
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const bf16x8 sf = acc_frag(dp[2 * c], dp[2 * c + 1]);
+      bf16x8 sf[NG];
+#pragma unroll
+      for (int u = 0; u < NG; ++u) sf[u] = acc_frag(dp[u][2 * c], dp[u][2 * c + 1]);
       bf16x8 ka[D / 16];
 #pragma unroll
       for (int jj = 0; jj < D / 16; ++jj) ka[jj] = tr_frag_rm<D>(k_t, jj, c, g, lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int jj = 0; jj < D / 16; ++jj) acc[jj] = mfma(ka[jj], sf, acc[jj]);
+      for (int jj = 0; jj < D / 16; ++jj)
+#pragma unroll
+        for (int u = 0; u < NG; ++u) acc[u][jj] = mfma(ka[jj], sf[u], acc[u][jj]);
       AT_MFMA_FENCE();
-      asm volatile("" ::"v"(sf));
+#pragma unroll
+      for (int u = 0; u < NG; ++u) asm volatile("" ::"v"(sf[u]));
 #pragma unroll
       for (int jj = 0; jj < D / 16; ++jj) asm volatile("" ::"v"(ka[jj]));
     }
   }
-  if (qvalid)
-    store_grad_row<D>(a.dq + (seq0 + q_in_seq) * a.lddq + h * D, acc, a.scale, a.rope != 0, a, seq0 + q_in_seq, g);
+#pragma unroll
+  for (int u = 0; u < NG; ++u)
+    if (qis[u] < S)
+      store_grad_row<D>(a.dq + (seq0 + qis[u]) * a.lddq + h * D, acc[u], a.scale, a.rope != 0, a, seq0 + qis[u], g);
 }
 
 bool al16(const void *p, int64_t ld) { return ((uintptr_t)p & 15) == 0 && ld % 8 == 0; }
@@ -916,11 +933,11 @@ lsn_status attn_bwd_impl(const char *who, int64_t n_seq, int64_t S, int32_t n_q,
   if (head_dim == 128) {
     hipLaunchKernelGGL(k_attn_dot<128>, dim3(dot_grid), dim3(kThreads), 0, hs, a, static_cast<float *>(ws));
     hipLaunchKernelGGL(k_attn_bwd_kv<128>, dim3(kv_grid), dim3(kThreads), 0, hs, a);
-    hipLaunchKernelGGL(k_attn_bwd_q<128>, dim3(q_grid), dim3(kFwdThreads), 0, hs, a);
+    hipLaunchKernelGGL((k_attn_bwd_q<128, kDqGroups>), dim3(q_grid), dim3(kFwdQ / kDqGroups * 4), 0, hs, a);
   } else {
     hipLaunchKernelGGL(k_attn_dot<64>, dim3(dot_grid), dim3(kThreads), 0, hs, a, static_cast<float *>(ws));
     hipLaunchKernelGGL(k_attn_bwd_kv<64>, dim3(kv_grid), dim3(kThreads), 0, hs, a);
-    hipLaunchKernelGGL(k_attn_bwd_q<64>, dim3(q_grid), dim3(kFwdThreads), 0, hs, a);
+    hipLaunchKernelGGL((k_attn_bwd_q<64, kDqGroups>), dim3(q_grid), dim3(kFwdQ / kDqGroups * 4), 0, hs, a);
   }
   return check_hip(hipGetLastError(), "attention backward launch");
 }
