@@ -363,7 +363,7 @@ def main():
     import torch
     from layer_streamed_nf4_dequant_amd import configs, lib
     from layer_streamed_nf4_dequant_amd.microbench import (attention_figure, decoder_figure, fused_glue_figure,
-                                                           glue_figure)
+                                                           glue_figure, nf4_gemm_figure)
     from layer_streamed_nf4_dequant_amd.stack import Stack
 
     lib.load()
@@ -580,6 +580,9 @@ def main():
         if not cfg.single:
             other["fused_glue"] = fused_glue_figure(cfg)
             print(f"[bench] fused glue: {other['fused_glue']}", flush=True)
+        if cfg.base == "nf4" and not cfg.single:
+            other["nf4_in_gemm"] = nf4_gemm_figure(cfg)
+            print(f"[bench] nf4 decoded in the GEMM vs staged: {other['nf4_in_gemm']}", flush=True)
         other["attention"] = attention_figure(cfg)
         print(f"[bench] attention: {other['attention']}", flush=True)
         if cfg.base == "nf4" and not cfg.single:

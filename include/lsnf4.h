@@ -199,6 +199,8 @@ lsn_status lora_down(int64_t T, int64_t K, const uint16_t *X, int32_t n, const u
  *   adapters == LSN_ADAPTERS_U_READY: U already holds bf16(X A^T) (from lora_down): one GEMM;
  *   adapters == LSN_ADAPTERS_OFF:     the adapter is skipped and Y = bf16(X W^T), bit-identical
  *                                     to the adapters-on result with B = 0; U is ignored.
+ * An NF4 W is decoded tile by tile inside the GEMM (never to HBM), bit for bit the bf16 operand
+ * nf4_dequant writes, so the result equals the forward on that dequantised W.
  * ws: device, at least lora_linear_ws_bytes(T, K, N, r) (may be NULL for the forward).
  * Async on `stream`.
  */
@@ -211,9 +213,11 @@ lsn_status lora_linear_fwd(const lsn_lora_linear *L, int32_t adapters, const uin
  * @1:25-1:58 puts an adapter on each): Y_g = bf16(X W_g^T + s U_g B_g^T) for g < n, bit-identical
  * to n calls of lora_linear_fwd. L is an array of n descriptors that share T, K, r and the scale
  * (their N and weights differ); Y and U are host arrays of n device pointers (U ignored with
- * adapters off). With bf16 weights the n products run as one GEMM launch over the concatenated
- * output columns (fewer, fuller waves of tiles); with any NF4 member each runs on its own.
- * Output/input overlaps give LSN_E_ARG. Async on `stream`.
+ * adapters off). With bf16 weights, or with NF4 weights whose codes are 16-byte and whose constant
+ * arrays are 4-byte aligned (each K-step's blocks then decoded into the GEMM's LDS stage), the n
+ * products run as one GEMM launch over the concatenated output columns (fewer, fuller waves of
+ * tiles); with a mix, or other NF4 alignments, each runs on its own. Output/input overlaps give
+ * LSN_E_ARG. Async on `stream`.
  */
 lsn_status lora_linear_fwd_group(int32_t n, const lsn_lora_linear *L, int32_t adapters, const uint16_t *X,
                                  uint16_t *const *Y, uint16_t *const *U, void *ws, size_t ws_bytes,

@@ -38,7 +38,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kB = 64;                       // rows per block (queries or keys)
 constexpr int kTP = kB * 2 + 16;             // pitch (bytes) of a transposed tile: [D][64] + pad
-constexpr int kFwdThreads = 512;             // dQ: 8 waves of 16 queries share each K/V tile
 constexpr int kFwdQ = 128;                   // queries per forward / dQ workgroup
 constexpr int kFwd2Threads = 256;            // forward: 4 waves of 32 queries (two groups of 16)
 // dQ: groups of 16 queries per wave. Two groups (4 waves of 32 queries) need 327 registers per

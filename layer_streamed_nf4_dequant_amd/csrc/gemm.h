@@ -73,6 +73,11 @@ struct GemmSeg {
   void *out;               // [M][N]
   const uint16_t *res;     // EPI_BF16: null, or bf16 [M][N] added to the rounded product
   int rope;                // EPI_BF16: rotary embedding of the rounded product (DirectArgs x)
+  // NF4 W (DirectArgs nf4 != 0; w unused): the packed weight [N][K] of the segment
+  const uint8_t *codes;
+  const int8_t *qabsmax;
+  const float *absmax2;
+  float mean;
 };
 // reduction segments: out = sum_p ( act_p W_p^T + s lr_act_p lr_w_p^T ), one output, the K-steps
 // of the segments run back to back (each K_p % 64 == 0)
@@ -97,6 +102,8 @@ struct DirectArgs {
   int b_red_major;       // B operand stored [K][N] (N contiguous) instead of [N][K]
   int ksplit;            // > 1: split-K into fp32 partials out + s M N (reduction-major B, fp32 store)
   EpiOps x;
+  int nf4;               // W of every segment is NF4 (GemmSeg codes ..), decoded into LDS per K-step
+  float nf4_q[16];       // the NF4 levels (filled by launch_gemm_direct)
 };
 lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s);
 // zero bytes (a multiple of 16) at p, with a kernel (no memset node in captured graphs)

@@ -584,11 +584,74 @@ __device__ __forceinline__ void tile_coords(int64_t b, int64_t ntiles, int64_t t
   nt = in / gm;
 }
 
+// NF4 W in the direct kernel (template flag NF4W, forward layout): the B stage of a K-step is
+// decoded from the packed weight instead of loaded. A K-step of 64 columns is exactly one NF4 block
+// per W row; thread t owns half t % 2 (32 codes, 16 bytes) of the block of tile rows t / 2 and
+// 128 + t / 2. Its codes, the word holding each block's quantised constant and the block's
+// second-level scale come by direct-to-LDS loads (each lane lands its own data) into one of two
+// staging buffers, two K-steps ahead, and the thread writes its rows as four 16-byte chunks of
+// bf16 into the stage, at the slots the fragment reads expect. Per row it first forms the 16
+// products bf16(q_i c) of its block constant c (the values the staging dequantisation would store
+// for the 16 codes), as byte planes, so that each code then costs a byte permute instead of a table
+// read and a multiply: w = bf16_RNE(fl32(q[code] c)), bit for bit the staged operand.
+constexpr int kNf4TabOffset = 256 * kEpiPitch + 1024;   // 255 floats: fl32(v / 127), v = -127 .. 127
+constexpr int kNf4StageOffset = kNf4TabOffset + 1024;   // two staging buffers
+constexpr int kNf4Buf = 12288;   // codes [2][256][16 B], constant words [2][256][4 B], scales [2][256][4 B]
+// products bf16(q_i c), i = 0 .. 15, as byte planes: lo[j] / hi[j] hold the low / high bytes of
+// entries 4j .. 4j+3
+struct Nf4Planes {
+  uint32_t lo[4], hi[4];
+};
+__device__ __forceinline__ void nf4_planes_half(Nf4Planes &pl, const float *q, float c, int h) {
+#pragma unroll
+  for (int j = 2 * h; j < 2 * h + 2; ++j) {
+    const uint32_t p0 = pack_bf16x2(__fmul_rn(q[4 * j], c), __fmul_rn(q[4 * j + 1], c));
+    const uint32_t p1 = pack_bf16x2(__fmul_rn(q[4 * j + 2], c), __fmul_rn(q[4 * j + 3], c));
+    pl.lo[j] = __builtin_amdgcn_perm(p1, p0, 0x06040200u);
+    pl.hi[j] = __builtin_amdgcn_perm(p1, p0, 0x07050301u);
+  }
+}
+// (m & x) | (~m & y), one v_bfi_b32
+__device__ __forceinline__ uint32_t nf4_sel(uint32_t m, uint32_t x, uint32_t y) { return (m & x) | (~m & y); }
+// four codes at once: byte j of c7 = code_j & 7, byte j of m = 0xff where code_j >= 8; returns the
+// low bytes (lo) and high bytes (hi) of the four products
+__device__ __forceinline__ void nf4_look4(const Nf4Planes &pl, uint32_t c7, uint32_t m, uint32_t &lo, uint32_t &hi) {
+  lo = nf4_sel(m, __builtin_amdgcn_perm(pl.lo[3], pl.lo[2], c7), __builtin_amdgcn_perm(pl.lo[1], pl.lo[0], c7));
+  hi = nf4_sel(m, __builtin_amdgcn_perm(pl.hi[3], pl.hi[2], c7), __builtin_amdgcn_perm(pl.hi[1], pl.hi[0], c7));
+}
+// The eight codes of word w in two halves (for the scheduling of the K-step): the even elements
+// (high nibbles) give their bf16 values as (e0, e2) and (e4, e6) ...
+__device__ __forceinline__ void nf4_even(const Nf4Planes &pl, uint32_t w, uint32_t &e01, uint32_t &e23) {
+  const uint32_t c7 = (w >> 4) & 0x07070707u;
+  // byte j's bit 7 (code 2j's bit 3) replicated over byte j: permute selectors 8 - 11 copy the
+  // sign bits of bytes 1 and 3 of either source
+  const uint32_t m = __builtin_amdgcn_perm(w, w << 8, 0x0b090a08u);
+  uint32_t lo, hi;
+  nf4_look4(pl, c7, m, lo, hi);
+  e01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  e23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+// ... the odd ones (low nibbles) give their low and high bytes ...
+__device__ __forceinline__ void nf4_odd(const Nf4Planes &pl, uint32_t w, uint32_t &lo, uint32_t &hi) {
+  const uint32_t c7 = w & 0x07070707u;
+  const uint32_t m = __builtin_amdgcn_perm(w << 4, w << 12, 0x0b090a08u);
+  nf4_look4(pl, c7, m, lo, hi);
+}
+// ... and the two complete the chunk: bf16 elements 0 .. 7 in order
+__device__ __forceinline__ u32x4_t nf4_chunk(uint32_t e01, uint32_t e23, uint32_t lo, uint32_t hi) {
+  const uint32_t o01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  const uint32_t o23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+  return u32x4_t{__builtin_amdgcn_perm(o01, e01, 0x05040100u), __builtin_amdgcn_perm(o01, e01, 0x07060302u),
+                 __builtin_amdgcn_perm(o23, e23, 0x05040100u), __builtin_amdgcn_perm(o23, e23, 0x07060302u)};
+}
+
 // SPLIT (split-K): the grid holds a.ksplit copies of the tile grid; copy s reduces over K-steps
 // [s nk / S, (s+1) nk / S) and stores its fp32 partial product to out + s M N (the caller adds
 // the partials in split order). Used where a product has few output tiles and a long reduction.
-template <int EPI, bool KSEG, bool BT, bool SPLIT>
+template <int EPI, bool KSEG, bool BT, bool SPLIT, bool NF4W>
 __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
+  static_assert(!NF4W || (!KSEG && !BT && !SPLIT && EPI != EPI_SWIGLU && EPI != EPI_SWIGLU_BWD),
+                "NF4 W: plain forward products");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char *lds_a = smem;                               // 2 stages
   char *lds_b = smem + 2 * DTILE;                   // 2 stages
@@ -648,14 +711,99 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     // (pair: waves 0-1 fill the gate half of the B tile, waves 2-3 the up half)
     const uint16_t *wb = PAIR && wave >= 2 ? a.x.w2 : sg.w;
     rs_a = make_rsrc(a.act + kt0 * DBK, a.M * a.K * 2 - kt0 * DBK * 2);
-    rs_b = BT ? make_rsrc(wb + kt0 * DBK * sg.N, (a.K - kt0 * DBK) * sg.N * 2)
-              : make_rsrc(wb + kt0 * DBK, sg.N * a.K * 2 - kt0 * DBK * 2);
+    if constexpr (NF4W)
+      rs_b = rs_a;   // (no B loads: the B stage is decoded from the packed weight)
+    else
+      rs_b = BT ? make_rsrc(wb + kt0 * DBK * sg.N, (a.K - kt0 * DBK) * sg.N * 2)
+                : make_rsrc(wb + kt0 * DBK, sg.N * a.K * 2 - kt0 * DBK * 2);
     make_direct_rows8(da, a.M, a.K, m0, wave, lane);
   }
   if constexpr (BT)
     make_direct_rows8_t(db, sg.N, n0, wave, lane);   // the same for every reduction segment
-  else   // (pair: the up half's LDS rows 128.. hold up rows n0..)
+  else if constexpr (!NF4W)   // (pair: the up half's LDS rows 128.. hold up rows n0..)
     make_direct_rows8(db, sg.N, KSEG ? a.kseg[0].K : a.K, PAIR && wave >= 2 ? n0 - 128 : n0, wave, lane);
+
+  // NF4 W: this thread's two half-rows of every K-step's block (rows past N read row N - 1: they
+  // feed only unstored outputs), staged in buffer k % 2 from two K-steps before the decode of
+  // K-step k until the barrier after it; the row's product planes and the decode's intermediates
+  __amdgpu_buffer_rsrc_t rs_codes, rs_qa, rs_s2;
+  uint32_t nf_voff[2], nf_brow[2];
+  Nf4Planes nfp;
+  u32x4_t nf_codes[2];
+  uint32_t nf_qw[2];
+  float nf_s2[2], nf_c8[2], nf_c = 0.0f;
+  uint32_t nf_e01 = 0, nf_e23 = 0, nf_lo = 0, nf_hi = 0;
+  char *const nf_lds = smem + kNf4StageOffset;
+  const float *nf_tab = reinterpret_cast<const float *>(smem + kNf4TabOffset);
+  if constexpr (NF4W) {
+    const int64_t kb = a.K / DBK;                       // blocks per row
+    rs_codes = make_rsrc(sg.codes, sg.N * a.K / 2);
+    rs_qa = make_rsrc(sg.qabsmax, sg.N * kb);
+    rs_s2 = make_rsrc(sg.absmax2, (sg.N * kb + 255) / 256 * 4);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int64_t row = min(n0 + p * 128 + (t >> 1), sg.N - 1);
+      nf_voff[p] = (uint32_t)(row * a.K / 2 + 16 * (t & 1));
+      nf_brow[p] = (uint32_t)(row * kb);
+    }
+    if (t < 255) reinterpret_cast<float *>(smem + kNf4TabOffset)[t] = int8_level(t - 127);
+  }
+  // K-step k's codes, constant words and scales of this wave's lanes into staging buffer `buf`
+  // (lane l of wave w lands at 16 (64 w + l) or 4 (64 w + l) of its array: its own thread's slots).
+  // The constant is read as the aligned word holding its byte (N K / 64 is a multiple of 4, so the
+  // word never reaches past the array).
+  auto nf4_issue = [&](int buf, int k) {
+    char *b = nf_lds + buf * kNf4Buf;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const uint32_t blk = nf_brow[p] + (uint32_t)k;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_codes, (lds_void_t *)(b + p * 4096 + wave * 1024), 16, nf_voff[p],
+                                               (uint32_t)k * 32, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_qa, (lds_void_t *)(b + 8192 + p * 1024 + wave * 256), 4, blk & ~3u,
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s2, (lds_void_t *)(b + 10240 + p * 1024 + wave * 256), 4,
+                                               (blk >> 8) * 4, 0, 0, 0);
+    }
+  };
+  // Piece p (0 .. 31) of decoding K-step k from staging buffer `buf` into the B area of stage
+  // `buf`: the staged words (0, 1) and the level table (1), per row the block constant and product
+  // planes (two pieces), then per word of codes three pieces: the even elements, the odd ones, the
+  // chunk's assembly and store. The pieces go one per fragment group: 0 - 7 in the sub-step after
+  // the ring barrier that frees the stage, 8 - 31 in the three sub-steps before the next one.
+  auto nf4_piece = [&](int p, int buf, int k) {
+    const char *b = nf_lds + buf * kNf4Buf;
+    if (p == 0) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        nf_qw[r] = *reinterpret_cast<const uint32_t *>(b + 8192 + r * 1024 + 4 * t);
+        nf_s2[r] = *reinterpret_cast<const float *>(b + 10240 + r * 1024 + 4 * t);
+      }
+    } else if (p == 1) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int v = (int)(int8_t)(nf_qw[r] >> (8 * ((nf_brow[r] + (uint32_t)k) & 3u)));
+        nf_c8[r] = nf_tab[v + 127];
+        nf_codes[r] = *reinterpret_cast<const u32x4_t *>(b + r * 4096 + 16 * t);
+      }
+    } else if (p == 2 || p == 16) {
+      const int r = p == 2 ? 0 : 1;
+      nf_c = decode_absmax(nf_c8[r], nf_s2[r], sg.mean);
+      nf4_planes_half(nfp, a.nf4_q, nf_c, 0);
+    } else if (p == 3 || p == 17) {
+      nf4_planes_half(nfp, a.nf4_q, nf_c, 1);
+    } else if ((p >= 4 && p <= 15) || (p >= 18 && p <= 29)) {
+      const int r = p <= 15 ? 0 : 1, i = p - (r ? 18 : 4), d = i / 3, part = i % 3;
+      const uint32_t w = nf_codes[r][d];
+      if (part == 0) {
+        nf4_even(nfp, w, nf_e01, nf_e23);
+      } else if (part == 1) {
+        nf4_odd(nfp, w, nf_lo, nf_hi);
+      } else {
+        char *dst = lds_b + buf * DTILE + dlds_off(r * 128 + (t >> 1), 4 * (t & 1) + d);
+        *reinterpret_cast<u32x4_t *>(dst) = nf4_chunk(nf_e01, nf_e23, nf_lo, nf_hi);
+      }
+    }
+  };
   // bytes from one K-step of B to the next
   const int64_t b_step_bytes = BT ? (int64_t)DBK * sg.N * 2 : (int64_t)DBK * 2;
   // byte offset along K of global step `step` inside its segment (moving pa / pb forward)
@@ -692,10 +840,14 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     }
   }
   // stage 0 <- step 0 (first, so that its latency overlaps the LoRA prologue)
+  if constexpr (NF4W) {
+    nf4_issue(0, 0);
+    nf4_issue(1, min(1, k_last));
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     issue_direct1(lds_a, rs_a, da, 0, wave, i);
-    issue_direct1(lds_b, rs_b, db, 0, wave, i);
+    if constexpr (!NF4W) issue_direct1(lds_b, rs_b, db, 0, wave, i);
   }
   // ---- LoRA prologue: acc = s * (B_seg . U_seg^T) over r (B_seg [N][r], U_seg [M][r]) ----
   // (reduction-segment mode: the sum of the segments' terms, in segment order)
@@ -769,8 +921,10 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   // sub-step that follows is read into (nA, nB) from stage `rstage` at K-slice `rs2`, and, when
   // `lhalf` >= 0, one of the 8 direct loads of half `lhalf` (0: operand A, 1: operand B) of a
   // K-step goes out to stage `lstage`; each group is fenced so the interleaving holds.
+  // (NF4 W: with np0 >= 0, pieces np0 .. np0+7 of decoding staging buffer nset, K-step nk_dec, go
+  // one per group)
   auto substep = [&](int rstage, int rs2, int lhalf, int lstage, uint32_t kb, bf16x8 (&cA)[4], bf16x8 (&cB)[4],
-                     bf16x8 (&nA)[4], bf16x8 (&nB)[4]) {
+                     bf16x8 (&nA)[4], bf16x8 (&nB)[4], int np0 = -1, int nset = 0, int nk_dec = 0) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       read_frag(rstage, rs2, q, nA, nB);
@@ -779,10 +933,36 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
       acc[i][j0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cB[j0 + 1], cA[i], acc[i][j0 + 1], 0, 0, 0);
       if (lhalf == 0) issue_direct1(lds_a + lstage * DTILE, rs_a, da, kb, wave, q);
       if (lhalf == 1) issue_direct1(lds_b + lstage * DTILE, rs_b, db, kb, wave, q);
+      if constexpr (NF4W) {
+        if (np0 >= 0) {
+          nf4_piece(np0 + q, nset, nk_dec);
+          // the group's order: LDS reads, an MFMA, half of the decode's VALU work, the other MFMA,
+          // the rest, then the direct load and the chunk store, so that the VALU work runs beside
+          // the matrix cores instead of after them
+          __builtin_amdgcn_sched_group_barrier(0x0100, 8, 0);    // DS read
+          __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);    // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x0002, 8, 0);    // VALU
+          __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);    // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x0002, 32, 0);   // VALU
+          __builtin_amdgcn_sched_group_barrier(0x0010, 1, 0);    // VMEM
+          __builtin_amdgcn_sched_group_barrier(0x0200, 1, 0);    // DS write
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  if constexpr (NF4W) {
+    wait_vm_all();   // this thread's staged K-steps 0 and 1
+    lds_barrier();   // the level table is written
+#pragma unroll
+    for (int p = 0; p < 32; ++p) nf4_piece(p, 0, 0);
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // buffer 0 read: refill it
+    nf4_issue(0, min(2, k_last));
+    // the first pieces of K-step 1's decode, as the sub-step after a ring barrier does in the loop
+#pragma unroll
+    for (int p = 0; p < 8; ++p) nf4_piece(p, 1, min(1, k_last));
+  }
   // operand A of step 1 to stage 1 (free); then wait for step 0 only, and read its first fragments
   {
     const uint32_t kb = a_kb(min(1, k_last));
@@ -790,7 +970,12 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
     for (int i = 0; i < 8; ++i) issue_direct1(lds_a + DTILE, rs_a, da, kb, wave, i);
   }
   __builtin_amdgcn_sched_barrier(0);
-  wait_vm<8>();
+  if constexpr (NF4W) {
+    wait_vm<14>();   // all but K-step 2's staging (6) and operand A of step 1 (8)
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0): stage 0's W written
+  } else {
+    wait_vm<8>();
+  }
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   bf16x8 ca[4], cb[4], na[4], nb[4];
@@ -806,19 +991,37 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_direct(DirectArgs a) {
   // Every load has at least two sub-steps to land. The last steps re-load the last K-step into
   // stages that are never read again, so the loop needs no branch.
   // (unrolled by two so that the stage of each step is a constant)
+  // NF4 W: the three sub-steps before the barrier finish decoding step kt+1 (staging buffer nx) into
+  // stage nx in place of its B loads; after the barrier, buffer nx is free and takes step kt+3's
+  // data (which the barrier of step kt+1 waits for, a step before its decode starts), and the
+  // sub-step after it starts decoding step kt+2 (buffer st, landed) into stage st, which the
+  // barrier has just freed.
   auto step = [&](int kt, int st) {
     const int nx = st ^ 1;
-    const uint32_t kb1 = b_kb(min(kt + 1, k_last));
+    const uint32_t kb1 = NF4W ? 0u : b_kb(min(kt + 1, k_last));
     const uint32_t kb2 = a_kb(min(kt + 2, k_last));
-    substep(st, 1, 1, nx, kb1, ca, cb, na, nb);
-    substep(st, 2, -1, 0, 0, na, nb, ca, cb);
-    substep(st, 3, -1, 0, 0, ca, cb, na, nb);
+    const int kd = min(kt + 1, k_last);
+    substep(st, 1, NF4W ? -1 : 1, nx, kb1, ca, cb, na, nb, NF4W ? 8 : -1, nx, kd);
+    substep(st, 2, -1, 0, 0, na, nb, ca, cb, NF4W ? 16 : -1, nx, kd);
+    substep(st, 3, -1, 0, 0, ca, cb, na, nb, NF4W ? 24 : -1, nx, kd);
     ring_barrier();
-    substep(nx, 0, 0, st, kb2, na, nb, ca, cb);
+    if constexpr (NF4W) nf4_issue(nx, min(kt + 3, k_last));
+    substep(nx, 0, 0, st, kb2, na, nb, ca, cb, NF4W ? 0 : -1, st, min(kt + 2, k_last));
   };
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, 0);
-    if (kt + 1 < nk) step(kt + 1, 1);
+  if constexpr (NF4W) {
+    // (the loop is re-entered only after its second step: a path from the first step back to the
+    // top would make the compiler wait there for the codes that step has just requested)
+    for (int kt = 0;; kt += 2) {
+      step(kt, 0);
+      if (kt + 1 >= nk) break;
+      step(kt + 1, 1);
+      if (kt + 2 >= nk) break;
+    }
+  } else {
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(kt, 0);
+      if (kt + 1 < nk) step(kt + 1, 1);
+    }
   }
   wait_vm_all();
 
@@ -1041,13 +1244,18 @@ int64_t seg_ntiles(int64_t N, int epi) {
   return (N + w - 1) / w;
 }
 
-template <int EPI, bool KSEG, bool BT, bool SPLIT = false>
+template <int EPI, bool KSEG, bool BT, bool SPLIT = false, bool NF4W = false>
 lsn_status launch_direct_one(const DirectArgs &a, hipStream_t s) {
-  constexpr size_t smem_bytes = kDirectSmemBytes + (EPI == EPI_BF16_ROPE ? 256 * sizeof(int) : 0);
+  // (past the tile: the rotary epilogue's positions, 1 KB; then the NF4 level table, 1 KB, and the
+  // NF4 staging buffers)
+  constexpr size_t smem_bytes =
+      kDirectSmemBytes + (NF4W ? 2048 + 2 * kNf4Buf : EPI == EPI_BF16_ROPE ? 256 * sizeof(int) : 0);
   static_assert(EPI != EPI_BF16_ROPE || kPosOffset == (int)kDirectSmemBytes, "positions past the tile");
+  static_assert(!NF4W || kNf4StageOffset + 2 * kNf4Buf == (int)smem_bytes, "the NF4 areas past the positions");
+  static_assert(smem_bytes <= 160 * 1024, "LDS of one workgroup");
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_direct<EPI, KSEG, BT, SPLIT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_direct<EPI, KSEG, BT, SPLIT, NF4W>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_bytes);
     if (e != hipSuccess) return check_hip(e, "gemm_direct smem attribute");
     attr_set = true;
@@ -1055,7 +1263,7 @@ lsn_status launch_direct_one(const DirectArgs &a, hipStream_t s) {
   int64_t ntiles_n = 0;
   for (int q = 0; q < a.nseg; ++q) ntiles_n += seg_ntiles(a.seg[q].N, EPI);
   const int64_t tiles = ((a.M + BM - 1) / BM) * ntiles_n * (SPLIT ? a.ksplit : 1);
-  hipLaunchKernelGGL((k_gemm_direct<EPI, KSEG, BT, SPLIT>), dim3((unsigned)tiles), dim3(NT), smem_bytes, s, a);
+  hipLaunchKernelGGL((k_gemm_direct<EPI, KSEG, BT, SPLIT, NF4W>), dim3((unsigned)tiles), dim3(NT), smem_bytes, s, a);
   return check_hip(hipGetLastError(), "k_gemm_direct launch");
 }
 
@@ -1080,6 +1288,20 @@ lsn_status launch_one(const GemmArgs &a, hipStream_t s) {
 namespace {
 template <bool KSEG, bool BT>
 lsn_status launch_direct_epi(const DirectArgs &a, int epi, hipStream_t s) {
+  if constexpr (!KSEG && !BT) {
+    if (a.nf4) {
+      if (epi != EPI_BF16) return fail(LSN_E_ARG, "gemm_direct: NF4 W takes the bf16 epilogues");
+      bool res = false, rope = false;
+      for (int q = 0; q < a.nseg; ++q) {
+        res = res || a.seg[q].res;
+        rope = rope || a.seg[q].rope;
+      }
+      if (rope) return launch_direct_one<EPI_BF16_ROPE, false, false, false, true>(a, s);
+      if (res) return launch_direct_one<EPI_BF16_RES, false, false, false, true>(a, s);
+      return launch_direct_one<EPI_BF16, false, false, false, true>(a, s);
+    }
+  }
+  if (a.nf4) return fail(LSN_E_ARG, "gemm_direct: NF4 W is for the plain forward layout");
   if (epi == EPI_BF16) {
     bool res = false, rope = false;
     for (int q = 0; q < a.nseg; ++q) {
@@ -1106,6 +1328,12 @@ lsn_status launch_direct_epi(const DirectArgs &a, int epi, hipStream_t s) {
 }  // namespace
 
 lsn_status launch_gemm_direct(DirectArgs a, int epi, hipStream_t s) {
+  if (a.nf4) {
+    const Nf4Table &tab = nf4_table();
+    for (int i = 0; i < 16; ++i) a.nf4_q[i] = tab.q[i];
+    if (a.nkseg > 0 || a.ksplit > 1 || a.b_red_major || a.K % DBK)
+      return fail(LSN_E_ARG, "gemm_direct: NF4 W needs a plain forward product with K %% 64 == 0");
+  }
   int64_t t0 = 0;
   for (int q = 0; q < a.nseg; ++q) {
     a.seg[q].ntile0 = t0;

@@ -157,6 +157,20 @@ size_t lora_linear_ws_bytes(int64_t T, int64_t K, int64_t N, int64_t r) {
 
 namespace {
 
+// NF4 W decoded inside the direct-load GEMM: its codes 16-byte and its constant arrays 4-byte
+// aligned (the kernel stages them by 16- and 4-byte direct loads)
+bool nf4_direct_ok(const lsn_weight &w) {
+  return w.kind == LSN_W_NF4 && ((uintptr_t)w.nf4.codes & 15) == 0 && ((uintptr_t)w.nf4.qabsmax & 3) == 0 &&
+         ((uintptr_t)w.nf4.absmax2 & 3) == 0;
+}
+
+void set_nf4_seg(GemmSeg &g, const lsn_weight &w) {
+  g.codes = w.nf4.codes;
+  g.qabsmax = w.nf4.qabsmax;
+  g.absmax2 = w.nf4.absmax2;
+  g.mean = w.nf4.mean;
+}
+
 // The forward of one linear; res (may be null): the residual added to the rounded product in the
 // epilogue (res == Y allowed, in place).
 lsn_status fwd_impl(const char *what, const lsn_lora_linear *L, int32_t adapters, const uint16_t *X, uint16_t *Y,
@@ -188,7 +202,7 @@ lsn_status fwd_impl(const char *what, const lsn_lora_linear *L, int32_t adapters
     return fail(LSN_E_ARG, "%s: the residual overlaps an output (other than being Y itself)", what);
   if ((st = require_gfx950()) != LSN_OK) return st;
   if (adapters == LSN_ADAPTERS_ON && (st = launch_rowproj(X, T, K, L->A, (int)r, U, s)) != LSN_OK) return st;
-  if (L->W.kind == LSN_W_BF16) {
+  if (L->W.kind == LSN_W_BF16 || nf4_direct_ok(L->W)) {
     DirectArgs d{};
     d.M = T;
     d.K = K;
@@ -196,6 +210,10 @@ lsn_status fwd_impl(const char *what, const lsn_lora_linear *L, int32_t adapters
     d.nseg = 1;
     d.seg[0].N = N;
     d.seg[0].w = L->W.bf16;
+    if (L->W.kind == LSN_W_NF4) {
+      d.nf4 = 1;
+      set_nf4_seg(d.seg[0], L->W);
+    }
     d.seg[0].lr_w = L->B;
     d.seg[0].lr_act = U;
     d.seg[0].out = Y;
@@ -237,7 +255,7 @@ lsn_status fwd_group_impl(const char *what, int32_t n, const lsn_lora_linear *L,
   if (rope_mask && !valid_rope(rope))
     return fail(LSN_E_ARG, "%s: the rotation needs a 16-byte aligned table, positions, n_pos >= 1 and a head width "
                            "of 64 or 128", what);
-  bool all_bf16 = true;
+  bool all_bf16 = true, all_nf4 = true;
   for (int g = 0; g < n; ++g) {
     lsn_status st = check_linear(&L[g], what);
     if (st != LSN_OK) return st;
@@ -246,6 +264,7 @@ lsn_status fwd_group_impl(const char *what, int32_t n, const lsn_lora_linear *L,
     if (L[g].W.kind == LSN_W_BF16_T)
       return fail(LSN_E_ARG, "%s: the transposed bf16 layout is for the backward only", what);
     all_bf16 = all_bf16 && L[g].W.kind == LSN_W_BF16;
+    all_nf4 = all_nf4 && nf4_direct_ok(L[g].W);
     const uint16_t *res = residual ? residual[g] : nullptr;
     if (res && !aligned16(res)) return fail(LSN_E_ARG, "%s: residual[%d] not 16-byte aligned", what, g);
     if ((rope_mask >> g) & 1) {
@@ -325,7 +344,7 @@ lsn_status fwd_group_impl(const char *what, int32_t n, const lsn_lora_linear *L,
     }
   }
   const int mode = adapters ? LSN_ADAPTERS_U_READY : LSN_ADAPTERS_OFF;
-  if (!all_bf16) {
+  if (!all_bf16 && !all_nf4) {
     for (int g = 0; g < n; ++g) {
       if ((st = fwd_impl(what, &L[g], mode, X, Y[g], adapters ? U[g] : nullptr, residual ? residual[g] : nullptr,
                          s)) != LSN_OK)
@@ -346,6 +365,7 @@ lsn_status fwd_group_impl(const char *what, int32_t n, const lsn_lora_linear *L,
   for (int g = 0; g < n; ++g) {
     d.seg[g].N = L[g].N;
     d.seg[g].w = L[g].W.bf16;
+    if (all_nf4) set_nf4_seg(d.seg[g], L[g].W);
     d.seg[g].lr_w = L[g].B;
     d.seg[g].lr_act = adapters ? U[g] : nullptr;
     d.seg[g].out = Y[g];
@@ -361,6 +381,7 @@ lsn_status fwd_group_impl(const char *what, int32_t n, const lsn_lora_linear *L,
   d.r = (int)r;
   d.scale = L[0].scale;
   d.adapters = adapters ? 1 : 0;
+  d.nf4 = all_nf4 ? 1 : 0;
   return launch_gemm_direct(d, EPI_BF16, s);
 }
 

@@ -1,5 +1,6 @@
 """Micro-benchmarks of kernels that sit beside the streamed projection step: the decoder-layer
-glue (RMSNorm, rotary embedding, SwiGLU; standalone and in the projections' epilogues) and causal
+glue (RMSNorm, rotary embedding, SwiGLU; standalone and in the projections' epilogues), the
+forward GEMM decoding NF4 weights itself against staging plus the bf16 GEMM, and causal
 attention, at a stack configuration's token count, widths and heads.
 
     python -m layer_streamed_nf4_dequant_amd.microbench [--config C3] [--iters 20]
@@ -179,6 +180,61 @@ def fused_glue_figure(cfg, iters: int = 10):
     return out
 
 
+def nf4_gemm_figure(cfg, iters: int = 10):
+    """The forward launches of one layer with NF4 base weights, two ways: the weights staged by
+    nf4_dequant (one launch for the layer's weights of the launch) and then the bf16 GEMM, against
+    the GEMM that decodes each K-step's NF4 blocks into LDS itself. Per launch (the grouped
+    q/k/v/gate/up, o, down): microseconds (HIP events over replayed HIP graphs) and the GEMM's
+    TFLOP/s (2 T K N + 2 T r N per member)."""
+    import torch
+    from layer_streamed_nf4_dequant_amd import inputs, lib
+    T, H, I, KV, r = cfg.T, cfg.hidden, cfg.inter, cfg.kv, cfg.r
+    bf = dict(dtype=torch.bfloat16)
+    key = ("bench nf4 gemm", cfg.name)
+    launches = {"qkv_gate_up": (H, [("q", H), ("k", KV), ("v", KV), ("gate", I), ("up", I)]),
+                "o": (H, [("o", H)]), "down": (I, [("down", H)])}
+    out = {"timing": "graph"}
+    for lname, (K, members) in launches.items():
+        X = inputs.device_normal((T, K), 1.0, 0, *key, lname, "X", **bf)
+        nf, st, w16s, ys, us, keep = [], [], [], [], [], []
+        for name, N in members:
+            Wf = inputs.device_normal((N, K), 0.02, 0, *key, name, "W", dtype=torch.float32)
+            P = lib.nf4_pack(Wf)
+            del Wf
+            A = inputs.device_normal((r, K), 0.01, 0, *key, name, "A", **bf)
+            B = inputs.device_normal((N, r), 0.01, 0, *key, name, "B", **bf)
+            w16 = torch.empty((N, K), **bf, device="cuda")
+            keep += [P, A, B]
+            w16s.append(w16)
+            nf.append(lib.linear_desc(T, K, N, r, cfg.scale, P, A, B))
+            st.append(lib.linear_desc(T, K, N, r, cfg.scale, w16, A, B))
+            ys.append(torch.empty((T, N), **bf, device="cuda"))
+            us.append(inputs.device_normal((T, r), 1.0, 0, *key, name, "U", **bf))
+        pdescs = [P.desc() for P in keep[0::3]]
+        RD = lib.ADAPTERS_U_READY
+        fns = {
+            "nf4_in_gemm": lambda: lib.lora_linear_fwd_group(nf, X, ys, us, adapters=RD),
+            "dequant": lambda: lib.nf4_dequant_batch(pdescs, w16s, "bf16"),
+            "bf16_gemm": lambda: lib.lora_linear_fwd_group(st, X, ys, us, adapters=RD),
+        }
+        t = {}
+        for name, fn in fns.items():
+            us_ = _time_calls(fn, iters)
+            if us_ is None:
+                out["timing"] = "eager"
+                us_ = _time_calls(fn, iters, graph=False)
+            t[name] = us_
+        flop = sum(2 * T * K * N + 2 * T * r * N for _, N in members)
+        out[lname] = {"nf4_in_gemm_us": round(t["nf4_in_gemm"], 1),
+                      "staged_us": round(t["dequant"] + t["bf16_gemm"], 1),
+                      "dequant_us": round(t["dequant"], 1), "bf16_gemm_us": round(t["bf16_gemm"], 1),
+                      "nf4_in_gemm_TFLOPs": round(flop / t["nf4_in_gemm"] / 1e6, 1),
+                      "bf16_gemm_TFLOPs": round(flop / t["bf16_gemm"] / 1e6, 1)}
+        del X, nf, st, w16s, ys, us, keep, pdescs
+        torch.cuda.empty_cache()
+    return out
+
+
 def attention_figure(cfg, iters: int = 10):
     """Causal grouped-query attention at the configuration's T rows as T / seq_len sequences, its
     heads and head width: microseconds per forward and per backward call (graph-replayed) and
@@ -273,7 +329,7 @@ def main() -> None:
         print(json.dumps({"decoder_step": decoder_figure(cfg, steps=args.steps)}), flush=True)
     else:
         print(json.dumps({"glue": glue_figure(cfg, args.iters), "fused_glue": fused_glue_figure(cfg),
-                          "attention": attention_figure(cfg)}), flush=True)
+                          "nf4_gemm": nf4_gemm_figure(cfg), "attention": attention_figure(cfg)}), flush=True)
 
 
 if __name__ == "__main__":
