@@ -130,7 +130,13 @@ def allocator_block_bytes(n: int) -> int:
 
 class DecoderModel:
     """Frozen NF4 base (streamed or resident), LoRA adapters on all seven projections, resident
-    embedding / final norm / LM head, packed sequences of cfg.seq_len rows."""
+    embedding / final norm / LM head, packed sequences of cfg.seq_len rows.
+
+    Streaming overlaps a layer's copy (on the copy stream) with the compute of the layers before
+    it only while the two streams sit on different hardware queues of the process: a copy's
+    completion marker on a queue shared with compute work blocks the kernels queued behind it.
+    HIP maps streams onto GPU_MAX_HW_QUEUES queues (4 by default); a process that creates many
+    streams should raise it (bench.py and the microbenchmarks take 16) before its first HIP call."""
 
     def __init__(self, cfg: StackConfig, vocab: int, layers: int | None = None, seed: int = 0,
                  modes=("streamed",), dequant: str = "staged", eps: float = EPS, theta: float = THETA,

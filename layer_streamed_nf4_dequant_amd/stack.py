@@ -250,7 +250,13 @@ def predict_device_bytes(cfg: StackConfig, modes=("streamed",), dequant: str = "
 
 
 class Stack:
-    """Owns the host images, device state and buffers of one configuration."""
+    """Owns the host images, device state and buffers of one configuration.
+
+    Streaming overlaps a layer's copy (on the copy stream) with the compute of the layers before
+    it only while the two streams sit on different hardware queues of the process: a copy's
+    completion marker on a queue shared with compute work blocks the kernels queued behind it.
+    HIP maps streams onto GPU_MAX_HW_QUEUES queues (4 by default); a process that creates many
+    streams should raise it (bench.py and the microbenchmarks take 16) before its first HIP call."""
 
     def __init__(self, cfg: StackConfig, seed: int = 0, modes=("streamed",), audit: bool = False,
                  keep_at_turn: bool = False, fault: int = 0, record: bool = False, layers=None,
@@ -688,12 +694,17 @@ class Stack:
     def grads(self):
         return self.dA, self.dB
 
-    def close(self):
-        if self.pool is not None:
-            self.pool.close()
-            self.pool = None
+    def drop_image_file(self):
+        """Removes the file tier's file (written by write_image_file), when the pool no longer
+        reads it (a stack whose own tier is the file keeps it)."""
         path = getattr(self, "image_file", None)
         if path is not None:
             os.remove(path)
             os.rmdir(os.path.dirname(path))
             self.image_file = None
+
+    def close(self):
+        if self.pool is not None:
+            self.pool.close()
+            self.pool = None
+        self.drop_image_file()
