@@ -470,8 +470,11 @@ lsn_status attention_fwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, in
                          const uint16_t *v, int64_t ldv, float scale, uint16_t *o, int64_t ldo,
                          float *lse, void *stream);
 
-/* Device workspace bytes attention_bwd needs: T x n_q fp32 (the row dots D_i = dO_i . o_i). */
-size_t attention_bwd_ws_bytes(int64_t n_seq, int64_t S, int32_t n_q);
+/* Device workspace bytes attention_bwd needs: T x n_q fp32 (the row dots D_i = dO_i . o_i), and,
+ * when a key/value head serves an even number of query heads (its dk, dv then summed from two
+ * halves of them in a fixed order), 4 x T x n_kv x head_dim fp32 of partial sums. 0 for invalid
+ * arguments (n_kv not dividing n_q). */
+size_t attention_bwd_ws_bytes(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, int32_t head_dim);
 
 /*
  * attention_bwd - gradients of attention_fwd for an upstream gradient dO (bf16, like o):
@@ -480,7 +483,8 @@ size_t attention_bwd_ws_bytes(int64_t n_seq, int64_t S, int32_t n_q);
  * with dk and dv of a shared key/value head summed over its query heads (bf16 outputs dq like
  * q, dk and dv like k and v, each with its own row stride; stored, not accumulated). o and lse
  * are attention_fwd's outputs. ws: device, 16-byte aligned, at least attention_bwd_ws_bytes.
- * Deterministic: dk and dv have one writer per row, dq is computed by a separate pass.
+ * Deterministic: dk and dv have one writer per row (or two fp32 partial sums over fixed halves of
+ * the query heads, added in a fixed order), dq is computed by a separate pass.
  */
 lsn_status attention_bwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, int32_t head_dim,
                          const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk,

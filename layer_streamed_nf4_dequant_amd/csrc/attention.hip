@@ -153,6 +153,10 @@ struct AttnArgs {
   int rope, rope_n_pos;
   const float *rope_cs;        // (cos, sin) table [rope_n_pos][D / 2]
   const int32_t *rope_pos;     // [T] table row of each token row
+  // dK, dV pass split over the group's query heads (kv_split workgroups per key block, 1 or 2);
+  // with 2, each writes fp32 partial sums [part][dK, dV][T][n_kv][D] to kv_part
+  int kv_split;
+  float *kv_part;
 };
 
 // Store one row's gradient (dims 16 j + 4 g + e of the row held by the lane, g = lane / 16):
@@ -269,6 +273,13 @@ __device__ __forceinline__ bf16x8 tr_frag_rm(const char *tile, int j, int c, int
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p1);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// One row's fp32 partial sum (dims 16 j + 4 g + e of the row held by the lane), unscaled.
+template <int D>
+__device__ __forceinline__ void store_part_row(float *dst, const floatx4 (&acc)[D / 16], int g) {
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) *reinterpret_cast<floatx4 *>(dst + 16 * j + 4 * g) = acc[j];
 }
 
 // ------------------------------------------------------------------------------------------
@@ -476,21 +487,28 @@ __global__ __launch_bounds__(kThreads) void k_attn_dot(AttnArgs a, float *__rest
 }
 
 // ------------------------------------------------------------------------------------------
-// dK, dV: one workgroup per (key block, sequence, key/value head), heaviest (first) blocks
-// first; a wave owns 16 keys (lane column = key) and loops over the group's query heads and the
-// query blocks at or after its key block. Each (head, query block)'s Q and dO tiles and the rows'
-// log-sum-exp and D stream through two LDS stages by direct-to-LDS loads (Q^T and dO^T
-// fragments by transpose reads of the row-major tiles).
+// dK, dV: one workgroup per (key block, sequence, key/value head, part), heaviest (first) blocks
+// first; a wave owns 16 keys (lane column = key) and loops over its part of the group's query
+// heads (all of them, or one half with a.kv_split = 2) and the query blocks at or after its key
+// block. Each (head, query block)'s Q and dO tiles and the rows' log-sum-exp and D stream through
+// two LDS stages by direct-to-LDS loads (Q^T and dO^T fragments by transpose reads of the
+// row-major tiles). A key block's work falls from 2 n_blocks (head, query block) pairs for the
+// first block to 2 for the last: unsplit, the first blocks' workgroups set the pass's time while
+// the last ones finish early (all of them fit on the device at once); split in two, twice as many
+// workgroups of half the work queue up heaviest first and the light ones fill in behind. The
+// split pass stores fp32 partial sums, which k_attn_kv_reduce adds in a fixed order.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
   constexpr int STAGE = 2 * DTile<D>::BYTES + 2 * kB * 4;                      // Q, dO, lse, D
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
   const int nb = (int)((a.S + kB - 1) / kB);
-  const int64_t per = a.n_seq * a.n_kv;
+  const int nsplit = a.kv_split;
+  const int64_t per = a.n_seq * a.n_kv * nsplit;
   const int kb = (int)(blockIdx.x / per);
   const int64_t rest = blockIdx.x % per;
-  const int64_t b = rest / a.n_kv;
-  const int hk = (int)(rest % a.n_kv), grp = a.n_q / a.n_kv;
+  const int part = (int)(rest % nsplit);
+  const int64_t b = rest / nsplit / a.n_kv;
+  const int hk = (int)(rest / nsplit % a.n_kv), grp = a.n_q / a.n_kv, hpw = grp / nsplit;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
   const int S = (int)a.S;
   const int k_in_seq = kb * kB + 16 * wave + col;
@@ -514,10 +532,11 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t rl = rsrc_of(a.lse + seq0 * a.n_q, a.S * a.n_q * 4);
   const __amdgpu_buffer_rsrc_t rt = rsrc_of(a.dot + seq0 * a.n_q, a.S * a.n_q * 4);
   constexpr int SEGW = DTile<D>::SEGS / 4;        // segments of each tile per wave (4 waves)
-  // iteration it = hh * (nb - kb) + (qb - kb) visits query head hk * grp + hh, query block qb
-  const int nqb = nb - kb, n_it = grp * nqb;
+  // iteration it = hh * (nb - kb) + (qb - kb) visits query head hk * grp + part * hpw + hh, query
+  // block qb
+  const int nqb = nb - kb, n_it = hpw * nqb;
   auto issue = [&](int it) {
-    const int hh = it / nqb, qb = kb + it % nqb, h = hk * grp + hh;
+    const int hh = it / nqb, qb = kb + it % nqb, h = hk * grp + part * hpw + hh;
     const int nvalid = S - qb * kB < kB ? S - qb * kB : kB;
     char *st = smem + (it & 1) * STAGE;
 #pragma unroll
@@ -615,8 +634,63 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
     }
   }
   if (kvalid) {
-    store_grad_row<D>(a.dk + (seq0 + k_in_seq) * a.lddk + hk * D, dk, a.scale, a.rope != 0, a, seq0 + k_in_seq, g);
-    store_grad_row<D>(a.dv + (seq0 + k_in_seq) * a.lddv + hk * D, dv, 1.0f, false, a, seq0 + k_in_seq, g);
+    const int64_t row = seq0 + k_in_seq;
+    if (nsplit == 1) {
+      store_grad_row<D>(a.dk + row * a.lddk + hk * D, dk, a.scale, a.rope != 0, a, row, g);
+      store_grad_row<D>(a.dv + row * a.lddv + hk * D, dv, 1.0f, false, a, row, g);
+    } else {
+      const int64_t T = a.n_seq * a.S;
+      store_part_row<D>(a.kv_part + ((2 * part * T + row) * a.n_kv + hk) * D, dk, g);
+      store_part_row<D>(a.kv_part + (((2 * part + 1) * T + row) * a.n_kv + hk) * D, dv, g);
+    }
+  }
+}
+
+// dK and dV from the split pass's partial sums, added in a fixed order (part 0, then part 1), and
+// stored as the unsplit pass stores its sums: dk = bf16(scale (p0 + p1)), with rope each pair
+// (i, i + D/2) of the rounded values then turned back by its angle (the same arithmetic as
+// store_grad_row), dv = bf16(p0 + p1). A thread takes pairs f0 .. f0+3 of one row and head.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_attn_kv_reduce(AttnArgs a) {
+  constexpr int TPR = D / 8;
+  const int64_t T = a.n_seq * a.S;
+  const int64_t item = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t rh = item / TPR;
+  if (rh >= T * a.n_kv) return;
+  const int f0 = (int)(item % TPR) * 4;
+  const int64_t row = rh / a.n_kv;
+  const int hk = (int)(rh % a.n_kv);
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const float *p0 = a.kv_part + ((which * T + row) * a.n_kv + hk) * D;
+    const float *p1 = a.kv_part + (((2 + which) * T + row) * a.n_kv + hk) * D;
+    const floatx4 l0 = *reinterpret_cast<const floatx4 *>(p0 + f0);
+    const floatx4 h0 = *reinterpret_cast<const floatx4 *>(p0 + f0 + D / 2);
+    const floatx4 l1 = *reinterpret_cast<const floatx4 *>(p1 + f0);
+    const floatx4 h1 = *reinterpret_cast<const floatx4 *>(p1 + f0 + D / 2);
+    const float mul = which == 0 ? a.scale : 1.0f;
+    float v1[4], v2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v1[e] = __fmul_rn(__fadd_rn(l0[e], l1[e]), mul);
+      v2[e] = __fmul_rn(__fadd_rn(h0[e], h1[e]), mul);
+    }
+    if (which == 0 && a.rope) {
+      const int pos = min(max(a.rope_pos[row], 0), a.rope_n_pos - 1);
+      const float *cs = a.rope_cs + (int64_t)pos * D;
+      const floatx4 c01 = *reinterpret_cast<const floatx4 *>(cs + 2 * f0);
+      const floatx4 c23 = *reinterpret_cast<const floatx4 *>(cs + 2 * f0 + 4);
+      const float cv[4] = {c01[0], c01[2], c23[0], c23[2]};
+      const float sv[4] = {c01[1], c01[3], c23[1], c23[3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x1 = bf16f(f2bf(v1[e])), x2 = bf16f(f2bf(v2[e]));
+        rope_pair(x1, x2, cv[e], __fmul_rn(-1.0f, sv[e]), v1[e], v2[e]);
+      }
+    }
+    uint16_t *dst = (which == 0 ? a.dk + row * a.lddk : a.dv + row * a.lddv) + hk * D;
+    *reinterpret_cast<u32x2 *>(dst + f0) = u32x2{pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
+    *reinterpret_cast<u32x2 *>(dst + f0 + D / 2) = u32x2{pack_bf16x2(v2[0], v2[1]), pack_bf16x2(v2[2], v2[3])};
   }
 }
 
@@ -754,6 +828,10 @@ __global__ __launch_bounds__(kFwdQ / NG * 4) void k_attn_bwd_q(AttnArgs a) {
       store_grad_row<D>(a.dq + (seq0 + qis[u]) * a.lddq + h * D, acc[u], a.scale, a.rope != 0, a, seq0 + qis[u], g);
 }
 
+// workgroups per key block of the dK/dV pass: the group's query heads in two halves when their
+// number is even (the partial sums then go through the workspace), else all in one
+int kv_split(int32_t n_q, int32_t n_kv) { return (n_q / n_kv) % 2 == 0 ? 2 : 1; }
+
 bool al16(const void *p, int64_t ld) { return ((uintptr_t)p & 15) == 0 && ld % 8 == 0; }
 
 lsn_status check_common(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, int32_t head_dim, float scale,
@@ -839,9 +917,10 @@ lsn_status attention_fwd(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, in
   return check_hip(hipGetLastError(), "k_attn_fwd launch");
 }
 
-size_t attention_bwd_ws_bytes(int64_t n_seq, int64_t S, int32_t n_q) {
-  if (n_seq < 1 || S < 1 || n_q < 1) return 0;
-  return (size_t)(n_seq * S * n_q) * 4;
+size_t attention_bwd_ws_bytes(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_kv, int32_t head_dim) {
+  if (n_seq < 1 || S < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv || head_dim < 1) return 0;
+  const size_t dots = ((size_t)(n_seq * S * n_q) * 4 + 255) / 256 * 256;
+  return dots + (kv_split(n_q, n_kv) == 2 ? (size_t)4 * n_seq * S * n_kv * head_dim * 4 : 0);
 }
 
 }  // extern "C"
@@ -869,29 +948,36 @@ lsn_status attn_bwd_impl(const char *who, int64_t n_seq, int64_t S, int32_t n_q,
   if (ldq < n_q * D || ldk < n_kv * D || ldv < n_kv * D || ldo < n_q * D || lddo < n_q * D || lddq < n_q * D ||
       lddk < n_kv * D || lddv < n_kv * D)
     return fail(LSN_E_ARG, "%s: a row stride is smaller than its heads", who);
-  if (ws_bytes < attention_bwd_ws_bytes(n_seq, S, n_q))
-    return fail(LSN_E_ARG, "%s: workspace smaller than attention_bwd_ws_bytes", who);
+  const size_t ws_need = attention_bwd_ws_bytes(n_seq, S, n_q, n_kv, head_dim);
+  if (ws_bytes < ws_need) return fail(LSN_E_ARG, "%s: workspace smaller than attention_bwd_ws_bytes", who);
   if (S * ldq * 2 >= ((int64_t)1 << 31) || S * ldk * 2 >= ((int64_t)1 << 31) || S * ldv * 2 >= ((int64_t)1 << 31) ||
       S * lddo * 2 >= ((int64_t)1 << 31))
     return fail(LSN_E_ARG, "%s: one sequence of q, k, v or dO spans 2 GiB or more", who);
   const Strided ins[] = {{q, ldq, n_q * D, 2}, {k, ldk, n_kv * D, 2}, {v, ldv, n_kv * D, 2},
                          {o, ldo, n_q * D, 2}, {lse, n_q, n_q, 4},       {dO, lddo, n_q * D, 2}};
-  const Strided outs[] = {{dq, lddq, n_q * D, 2}, {dk, lddk, n_kv * D, 2}, {dv, lddv, n_kv * D, 2},
-                          {ws, n_q, n_q, 4}};
+  const Strided outs[] = {{dq, lddq, n_q * D, 2}, {dk, lddk, n_kv * D, 2}, {dv, lddv, n_kv * D, 2}};
   if (rope) {
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 3; ++i) {
       const size_t ob = span(T, outs[i].ld, outs[i].width, outs[i].elt);
       if (ranges_overlap(outs[i].p, ob, rope->cs, (size_t)rope->n_pos * D * 4) ||
           ranges_overlap(outs[i].p, ob, rope->positions, (size_t)T * 4))
         return fail(LSN_E_ARG, "%s: an output overlaps the rotation inputs", who);
     }
+    if (ranges_overlap(ws, ws_need, rope->cs, (size_t)rope->n_pos * D * 4) ||
+        ranges_overlap(ws, ws_need, rope->positions, (size_t)T * 4))
+      return fail(LSN_E_ARG, "%s: the workspace overlaps the rotation inputs", who);
   }
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 3; ++i) {
     for (const Strided &in : ins)
-      if (overlap(outs[i], in, T)) return fail(LSN_E_ARG, "%s: an output or the workspace overlaps an input", who);
-    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], in, T)) return fail(LSN_E_ARG, "%s: an output overlaps an input", who);
+    for (int j = i + 1; j < 3; ++j)
       if (overlap(outs[i], outs[j], T)) return fail(LSN_E_ARG, "%s: outputs overlap", who);
+    if (ranges_overlap(ws, ws_need, outs[i].p, span(T, outs[i].ld, outs[i].width, outs[i].elt)))
+      return fail(LSN_E_ARG, "%s: the workspace overlaps an output", who);
   }
+  for (const Strided &in : ins)
+    if (ranges_overlap(ws, ws_need, in.p, span(T, in.ld, in.width, in.elt)))
+      return fail(LSN_E_ARG, "%s: the workspace overlaps an input", who);
   st = require_gfx950();
   if (st != LSN_OK) return st;
   AttnArgs a{};
@@ -918,6 +1004,10 @@ lsn_status attn_bwd_impl(const char *who, int64_t n_seq, int64_t S, int32_t n_q,
   a.lddq = lddq;
   a.lddk = lddk;
   a.lddv = lddv;
+  a.kv_split = kv_split(n_q, n_kv);
+  a.kv_part = a.kv_split == 2
+                  ? reinterpret_cast<float *>(static_cast<char *>(ws) + ((size_t)(T * n_q) * 4 + 255) / 256 * 256)
+                  : nullptr;
   if (rope) {
     a.rope = 1;
     a.rope_n_pos = rope->n_pos;
@@ -927,15 +1017,18 @@ lsn_status attn_bwd_impl(const char *who, int64_t n_seq, int64_t S, int32_t n_q,
   const hipStream_t hs = (hipStream_t)stream;
   const int64_t nb = (S + kB - 1) / kB;
   const unsigned dot_grid = (unsigned)((T * n_q * (D / 8) + kThreads - 1) / kThreads);
-  const unsigned kv_grid = (unsigned)(nb * n_seq * n_kv);
+  const unsigned kv_grid = (unsigned)(nb * n_seq * n_kv * a.kv_split);
   const unsigned q_grid = (unsigned)(((S + kFwdQ - 1) / kFwdQ) * n_seq * n_q);
+  const unsigned red_grid = (unsigned)((T * n_kv * (D / 8) + kThreads - 1) / kThreads);
   if (head_dim == 128) {
     hipLaunchKernelGGL(k_attn_dot<128>, dim3(dot_grid), dim3(kThreads), 0, hs, a, static_cast<float *>(ws));
     hipLaunchKernelGGL(k_attn_bwd_kv<128>, dim3(kv_grid), dim3(kThreads), 0, hs, a);
+    if (a.kv_split == 2) hipLaunchKernelGGL(k_attn_kv_reduce<128>, dim3(red_grid), dim3(kThreads), 0, hs, a);
     hipLaunchKernelGGL((k_attn_bwd_q<128, kDqGroups>), dim3(q_grid), dim3(kFwdQ / kDqGroups * 4), 0, hs, a);
   } else {
     hipLaunchKernelGGL(k_attn_dot<64>, dim3(dot_grid), dim3(kThreads), 0, hs, a, static_cast<float *>(ws));
     hipLaunchKernelGGL(k_attn_bwd_kv<64>, dim3(kv_grid), dim3(kThreads), 0, hs, a);
+    if (a.kv_split == 2) hipLaunchKernelGGL(k_attn_kv_reduce<64>, dim3(red_grid), dim3(kThreads), 0, hs, a);
     hipLaunchKernelGGL((k_attn_bwd_q<64, kDqGroups>), dim3(q_grid), dim3(kFwdQ / kDqGroups * 4), 0, hs, a);
   }
   return check_hip(hipGetLastError(), "attention backward launch");

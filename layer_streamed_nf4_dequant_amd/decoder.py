@@ -56,7 +56,7 @@ def decoder_workspaces(cfg: StackConfig, vocab: int, ce_chunk: int) -> dict:
     ws = max(lib.ws_bytes(T, p.K, p.N, r) for p in layout)
     ws = max(ws, lib.group_ws_bytes(descs[0:3]), lib.group_ws_bytes(descs[4:6]))
     n_seq, nq = T // cfg.seq_len, cfg.hidden // cfg.head_dim
-    return {"ws": ws, "ws_att": lib.attention_bwd_ws_bytes(n_seq, cfg.seq_len, nq),
+    return {"ws": ws, "ws_att": lib.attention_bwd_ws_bytes(n_seq, cfg.seq_len, nq, cfg.kv // cfg.head_dim, cfg.head_dim),
             "ws_ce": lib.lm_head_ce_ws_bytes(ce_chunk, cfg.hidden, vocab)}
 
 

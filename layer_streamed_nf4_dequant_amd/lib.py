@@ -154,7 +154,7 @@ def load():
         "swiglu_fwd": (i32, [i64, vp, vp, vp, vp]),
         "swiglu_bwd": (i32, [i64, vp, vp, vp, vp, vp, vp]),
         "attention_fwd": (i32, [i64, i64, i32, i32, i32, vp, i64, vp, i64, vp, i64, f32, vp, i64, vp, vp]),
-        "attention_bwd_ws_bytes": (sz, [i64, i64, i32]),
+        "attention_bwd_ws_bytes": (sz, [i64, i64, i32, i32, i32]),
         "add_bf16": (i32, [i64, vp, vp, vp, vp]),
         "convert_f32_bf16": (i32, [i64, vp, vp, vp]),
         "convert_bf16_f32": (i32, [i64, vp, vp, vp]),
@@ -531,8 +531,8 @@ def attention_fwd(q, k, v, o, lse, n_seq: int, n_q: int, n_kv: int, head_dim: in
                                _ptr(v), v.stride(0), sc, _ptr(o), o.stride(0), _ptr(lse), _stream_handle(stream)))
 
 
-def attention_bwd_ws_bytes(n_seq: int, S: int, n_q: int) -> int:
-    return int(load().attention_bwd_ws_bytes(n_seq, S, n_q))
+def attention_bwd_ws_bytes(n_seq: int, S: int, n_q: int, n_kv: int, head_dim: int) -> int:
+    return int(load().attention_bwd_ws_bytes(n_seq, S, n_q, n_kv, head_dim))
 
 
 def attention_bwd(q, k, v, o, lse, dO, dq, dk, dv, ws, n_seq: int, n_q: int, n_kv: int, head_dim: int,

@@ -254,7 +254,7 @@ def attention_figure(cfg, iters: int = 10):
     dO = inputs.device_normal((T, nq * d), 1.0, 0, "bench attention", "dO", dtype=torch.bfloat16)
     g = torch.empty_like(qkv)
     dq, dk, dv = g[:, : nq * d], g[:, nq * d:(nq + nkv) * d], g[:, (nq + nkv) * d:]
-    ws = torch.empty(lib.attention_bwd_ws_bytes(n_seq, S, nq), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(lib.attention_bwd_ws_bytes(n_seq, S, nq, nkv, d), dtype=torch.uint8, device="cuda")
     fwd = lambda: lib.attention_fwd(q, k, v, o, lse, n_seq, nq, nkv, d)  # noqa: E731
     bwd = lambda: lib.attention_bwd(q, k, v, o, lse, dO, dq, dk, dv, ws, n_seq, nq, nkv, d)  # noqa: E731
     flops_f = 2 * n_seq * nq * S * S * d

@@ -103,4 +103,9 @@ def test_attention_argument_errors_without_gpu():
     assert L.attention_bwd(*bwd(dq, dk, dv)) not in (lib.LSN_OK, lib.LSN_E_ARG)
     assert L.attention_bwd(*bwd(dq, dq + 64, dv)) == lib.LSN_E_ARG     # dk overlaps dq's columns
     assert b"overlap" in L.lsn_last_error()
-    assert L.attention_bwd_ws_bytes(2, 4, nq) == 2 * 4 * nq * 4
+    # the row dots (rounded up to 256 bytes), and with an even number of query heads per key/value
+    # head the dk, dv partial sums of the two halves of them
+    assert L.attention_bwd_ws_bytes(2, 4, nq, nkv, d) == 256 + 4 * (2 * 4) * nkv * d * 4
+    assert L.attention_bwd_ws_bytes(2, 4, 3, 1, d) == 256
+    assert L.attention_bwd_ws_bytes(2, 100, 3, 1, d) == (2 * 100 * 3 * 4 + 255) // 256 * 256
+    assert L.attention_bwd_ws_bytes(2, 4, 4, 3, d) == 0

@@ -67,7 +67,7 @@ class AttnCase:
         q, k, v = self.slices(self.qkvd)
         g = torch.full_like(self.qkvd, float("nan"))
         dq, dk, dv = self.slices(g)
-        ws = torch.empty(lib.attention_bwd_ws_bytes(self.n_seq, self.S, self.n_q), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(lib.attention_bwd_ws_bytes(self.n_seq, self.S, self.n_q, self.n_kv, self.d), dtype=torch.uint8, device="cuda")
         lib.attention_bwd(q, k, v, o, lse, self.dOd, dq, dk, dv, ws, self.n_seq, self.n_q, self.n_kv, self.d)
         return g
 

@@ -280,7 +280,7 @@ def test_attention_backward_rope_epilogue(gpu, n_seq, S, nq, nkv, d, theta):
     pos = (np.arange(T) % S).astype(np.int32)
     posd = torch.from_numpy(pos).cuda()
     tab = lib.rope_table(S, d, theta)
-    ws = torch.empty(lib.attention_bwd_ws_bytes(n_seq, S, nq), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(lib.attention_bwd_ws_bytes(n_seq, S, nq, nkv, d), dtype=torch.uint8, device="cuda")
     outs = [[torch.empty((T, n * d), dtype=torch.bfloat16, device="cuda") for n in (nq, nkv, nkv)] for _ in range(2)]
     lib.attention_bwd_rope(q, k, v, o, lse, dO, *outs[0], ws, n_seq, nq, nkv, d, lib.rope_desc(tab, S, d, posd))
     lib.attention_bwd(q, k, v, o, lse, dO, *outs[1], ws, n_seq, nq, nkv, d)
