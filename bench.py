@@ -17,6 +17,9 @@ prologue): achieved = algorithmic FLOPs of its launches in the timed steps / the
 durations, measured with HIP events recorded around every launch on the compute stream; traffic =
 the calibrated byte counters of the same launches from the committed profile summary. `cpu_baseline` times the CPU oracle on a
 bounded sample (one layer, a subset of token rows) and scales it to the workload.
+
+The figures after the headline free their buffers into torch's cache, never back to the driver:
+memory handed back (torch.cuda.empty_cache) slowed the next second of kernels by up to 18%.
 """
 
 from __future__ import annotations
@@ -149,7 +152,6 @@ def lm_head_figure(cfg, vocab: int = 128256, chunk: int = 2048, iters: int = 5):
            "logits_bytes_per_logit_element": 6,
            "mean_loss": round(float(loss.mean()), 4)}
     del h, W, labels, loss, dh, ws
-    torch.cuda.empty_cache()
     return out
 
 
@@ -318,7 +320,6 @@ def config_figures(names=("C1", "C2", "C4", "C5"), steps: int = 3, cpu: bool = T
         res = {m: round(timed_steps(st, m, steps), 1) for m in modes}
         st.close()
         del st
-        torch.cuda.empty_cache()
         fig = {"workload": cfg.name, "layers": cfg.layers, "tokens_per_step": cfg.T, "base": cfg.base,
                "steps_timed": steps, "tokens_per_s": res,
                "streamed_over_resident": round(res["streamed"] / res["resident"], 4),
@@ -647,7 +648,6 @@ def main():
         out["cpu_baseline"] = cpu_baseline(cfg)
     stack.close()
     del stack
-    torch.cuda.empty_cache()
     if not args.no_other_modes and not args.no_configs and args.config == "C3":
         out["configs"] = config_figures(cpu=not args.no_cpu_baseline)
     print(json.dumps(out), flush=True)

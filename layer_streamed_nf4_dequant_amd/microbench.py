@@ -9,6 +9,11 @@ attention, at a stack configuration's token count, widths and heads.
 prints one JSON object: per kernel, microseconds per call (HIP events around a replayed HIP graph
 of back-to-back calls) and the algorithmic HBM rate against the 8 TB/s peak. bench.py reports
 the same figure beside its headline line.
+
+The figures free their buffers into torch's cache and do not hand them back to the driver
+(torch.cuda.empty_cache): after a release of 12 GB that way, the projection stack's next steps
+ran up to 18% slower for about a second (165 -> 194 ms per streamed step, measured on MI355X),
+which skewed whatever was timed next. The device has room to keep them.
 """
 
 from __future__ import annotations
@@ -99,7 +104,6 @@ def glue_figure(cfg, iters: int = 20):
         gbs = nbytes / (us * 1e-6) / 1e9
         out[name] = {"us": round(us, 1), "bytes": nbytes, "GBs": round(gbs, 1), "frac": round(gbs / 8000.0, 3)}
     del x, g, y, rstd, dy, dx, qk, pos, gt, up, dm, m, dgt, dup
-    torch.cuda.empty_cache()
     return out
 
 
@@ -177,7 +181,6 @@ def fused_glue_figure(cfg, iters: int = 10):
         out[name] = {"fused_us": round(t[0], 1), "plain_us": round(t[1], 1), "glue_kernel_us": round(t[2], 1),
                      "saved_us": round(t[1] + t[2] - t[0], 1)}
     del keep, X, Xi, dY, U, q, k, v, o, gate, up, m, dm, dg, du, res, pos, tab, dA, dB, ws
-    torch.cuda.empty_cache()
     return out
 
 
@@ -232,7 +235,6 @@ def nf4_gemm_figure(cfg, iters: int = 10):
                       "nf4_in_gemm_TFLOPs": round(flop / t["nf4_in_gemm"] / 1e6, 1),
                       "bf16_gemm_TFLOPs": round(flop / t["bf16_gemm"] / 1e6, 1)}
         del X, nf, st, w16s, ys, us, keep, pdescs
-        torch.cuda.empty_cache()
     return out
 
 
@@ -267,7 +269,6 @@ def attention_figure(cfg, iters: int = 10):
         tf = fl / (us * 1e-6) / 1e12
         out[name] = {"us": round(us, 1), "flops": fl, "TFLOPs": round(tf, 1), "frac": round(tf / 2500.0, 3)}
     del qkv, o, lse, dO, g, ws
-    torch.cuda.empty_cache()
     return out
 
 
@@ -323,7 +324,6 @@ def decoder_figure(cfg, vocab: int = 128256, steps: int = 3, modes=("streamed", 
                                                                reference=ref)["total"] / 1e9, 4)
     m.close()
     del m
-    torch.cuda.empty_cache()
     return out
 
 
