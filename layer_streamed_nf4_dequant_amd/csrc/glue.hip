@@ -6,6 +6,7 @@
 // bf16 tensors, every product and sum separately rounded (no contraction), and every row
 // reduction in a fixed order, so the bits depend only on the inputs.
 
+#include <algorithm>
 #include <cmath>
 #include <vector>
 
@@ -148,35 +149,40 @@ struct RopeTable {
 
 // In place on n_heads heads of width 2 half in each row (row stride ld elements): pair
 // (i, i + half) of a head turns by pos * inv_freq[i] (minus that for the backward).
-// Vector form (half % 8 == 0, 16-byte aligned rows): a thread takes 8 consecutive pairs of
-// up to `hg` heads of one row, computes the 8 angles' sine and cosine once and applies them to
-// each of its heads with 16-byte loads and stores; threads are ordered pair-block fastest, so
-// neighbouring lanes cover a head's two contiguous halves.
-__global__ __launch_bounds__(kGlueThreads) void k_rope_v(int64_t T, int n_heads, int half, int hg, int64_t ld,
-                                                         uint16_t *__restrict__ x,
-                                                         const int32_t *__restrict__ positions, RopeTable tab,
-                                                         float sign) {
-  const int nblk = half / 8, ngroups = (n_heads + hg - 1) / hg;
-  const int64_t per_row = (int64_t)ngroups * nblk;
-  const int64_t item = (int64_t)blockIdx.x * kGlueThreads + threadIdx.x;
-  if (item >= T * per_row) return;
-  const int64_t row = item / per_row;
-  const int rem = (int)(item - row * per_row);
-  const int group = rem / nblk, blk = rem - group * nblk;
-  const float p = (float)positions[row];
-  float c[8], sn[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float sv, cv;
-    rope_cos_sin(p, tab.inv_freq[blk * 8 + e], cv, sv);
-    c[e] = cv;
-    sn[e] = __fmul_rn(sign, sv);
+// Vector form (half % 8 == 0, 16-byte aligned rows): a workgroup takes `rows` consecutive rows
+// (rows x half <= kRopeRowPairs), computes the sine and cosine of each of those rows' pairs once
+// into LDS (one pair per thread), then rotates 8 consecutive pairs of one head per thread and
+// round with 16-byte loads and stores, threads ordered pair-block fastest so that neighbouring
+// lanes cover a head's two contiguous halves. Every head of a row reuses the row's angles.
+constexpr int kRopeRowPairs = 1024;
+__global__ __launch_bounds__(kGlueThreads) void k_rope_rows(int64_t T, int n_heads, int half, int rows, int64_t ld,
+                                                            uint16_t *__restrict__ x,
+                                                            const int32_t *__restrict__ positions, RopeTable tab,
+                                                            float sign) {
+  __shared__ float2 cs[kRopeRowPairs];
+  const int64_t r0 = (int64_t)blockIdx.x * rows;
+  const int nr = (int)min((int64_t)rows, T - r0);
+  for (int i = threadIdx.x; i < nr * half; i += kGlueThreads) {
+    const int r = i / half, j = i - r * half;
+    float c, s;
+    rope_cos_sin((float)positions[r0 + r], tab.inv_freq[j], c, s);
+    cs[i] = float2{c, __fmul_rn(sign, s)};
   }
-  const int h1 = min(n_heads, (group + 1) * hg);
-  for (int h = group * hg; h < h1; ++h) {
-    uint16_t *base = x + row * ld + (int64_t)h * 2 * half + blk * 8;
+  __syncthreads();
+  const int nblk = half / 8, per_row = n_heads * nblk;
+  for (int it = threadIdx.x; it < nr * per_row; it += kGlueThreads) {
+    const int r = it / per_row, rem = it - r * per_row;
+    const int h = rem / nblk, blk = rem - h * nblk;
+    uint16_t *base = x + (r0 + r) * ld + (int64_t)h * 2 * half + blk * 8;
     u32x4_t *p1 = reinterpret_cast<u32x4_t *>(base);
     u32x4_t *p2 = reinterpret_cast<u32x4_t *>(base + half);
+    float c[8], sn[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float2 t = cs[r * half + blk * 8 + e];
+      c[e] = t.x;
+      sn[e] = t.y;
+    }
     u32x4_t o1, o2;
     rope_chunk8(*p1, *p2, c, sn, o1, o2);
     *p1 = o1;
@@ -456,14 +462,12 @@ lsn_status rope_apply(int64_t T, int32_t n_heads, int32_t head_dim, uint16_t *x,
   const int half = head_dim / 2;
   const bool vec = half % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x & 15) == 0;
   if (vec) {
-    // heads per thread: as many as keep the grid at >= 2048 workgroups (up to 8), so the sine
-    // and cosine of a row's angles are shared by several heads
-    const int64_t nblk = half / 8;
-    int hg = 8;
-    while (hg > 1 && T * nblk * ((n_heads + hg - 1) / hg) < 2048LL * kGlueThreads) hg /= 2;
-    const int64_t items = T * nblk * ((n_heads + hg - 1) / hg);
-    hipLaunchKernelGGL(k_rope_v, dim3((unsigned)((items + kGlueThreads - 1) / kGlueThreads)), dim3(kGlueThreads), 0,
-                       (hipStream_t)stream, T, (int)n_heads, half, hg, ld, x, positions, tab, inverse ? -1.0f : 1.0f);
+    // rows per workgroup: about one head chunk per thread, within the LDS for the rows' angles
+    const int64_t per_row = (int64_t)n_heads * (half / 8);
+    const int rows = (int)std::min<int64_t>(std::max<int64_t>(1, kGlueThreads / per_row), kRopeRowPairs / half);
+    hipLaunchKernelGGL(k_rope_rows, dim3((unsigned)((T + rows - 1) / rows)), dim3(kGlueThreads), 0,
+                       (hipStream_t)stream, T, (int)n_heads, half, rows, ld, x, positions, tab,
+                       inverse ? -1.0f : 1.0f);
   } else {
     const int64_t items = T * n_heads * half;
     hipLaunchKernelGGL(k_rope_s, dim3((unsigned)((items + kGlueThreads - 1) / kGlueThreads)), dim3(kGlueThreads), 0,
