@@ -122,10 +122,11 @@ def test_rmsnorm_bwd_parity(gpu, T, H, eps, accumulate):
 
 
 ROPE_CASES = [  # n_q, n_kv, head_dim, theta, T, first position, extra columns per row
-    (32, 8, 128, 500000.0, 300, 0, 0),        # vector form (8 pairs per thread, heads grouped)
-    (14, 2, 64, 1000000.0, 129, 7000, 0),
+    (32, 8, 128, 500000.0, 300, 0, 0),        # vector form: q one row per workgroup, k four rows
+    (14, 2, 64, 1000000.0, 129, 7000, 0),     # a last workgroup with fewer rows than the others
     (4, 4, 512, 10000.0, 33, 123, 0),
-    (40, 8, 128, 500000.0, 3000, 0, 0),       # many rows: one head per thread group split differently
+    (40, 8, 128, 500000.0, 3000, 0, 0),       # more head chunks per row than threads: two rounds
+    (1, 1, 512, 10000.0, 9, 3, 0),            # rows per workgroup capped by the LDS for their angles
     (1, 1, 2, 10000.0, 1, 8191, 0),           # scalar form (head width 2)
     (3, 1, 16, 10000.0, 17, 5, 4),            # scalar form (row stride not a multiple of 8)
 ]
