@@ -184,6 +184,26 @@ def hipblaslt_ceiling(cfg, iters: int = 10):
     return res
 
 
+def device_copy_rate(nbytes: int = 1 << 30, iters: int = 10) -> dict:
+    """Same-session reference for the HBM-bound kernels: a device-to-device copy of `nbytes`
+    (torch copy_, the runtime's blit kernel), counted as nbytes read plus nbytes written."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return {"GBs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_copy": 2 * nbytes,
+            "what": "torch copy_ of 1 GiB on the device (the runtime's blit kernel), read + written"}
+
+
 def cpu_baseline(cfg, seed: int = 0, rows: int | None = 32, layers: int = 1, n_max: int | None = None):
     """Oracle (numpy, fp64 LoRA + fp32 NF4) on `layers` layers of the workload: the NF4 dequant of
     all 7 projections twice (forward and backward visit; none for a bf16 base) plus forward,
@@ -642,6 +662,10 @@ def main():
             "value": round(t_ceiling / (wall / args.steps), 4), "ceiling_ms": round(t_ceiling * 1e3, 2),
             "step_ms": round(wall * 1e3 / args.steps, 2),
             "definition": "time of the step's base GEMMs at the same-session hipBLASLt rate per shape / step time"}
+        copy = device_copy_rate()
+        if dequant is not None:
+            copy["dequant_over_copy"] = round(dequant["achieved"] / copy["GBs"], 4)
+        context["device_copy_reference"] = copy
     out["context"] = context
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", flush=True)
