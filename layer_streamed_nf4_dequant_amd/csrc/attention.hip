@@ -22,6 +22,8 @@
 
 #include <cmath>
 
+#include <type_traits>
+
 #include "common.h"
 #include "glue_math.h"
 
@@ -290,6 +292,7 @@ __device__ __forceinline__ void store_part_row(float *dst, const floatx4 (&acc)[
 // queries. K and V blocks of 64 keys stream through two LDS stages by direct-to-LDS loads (each
 // wave issues its share of the next block right after the barrier that frees its stage), so the
 // workgroup meets once per block and no thread spends instructions on staging.
+constexpr float kLazy = 8.0f;   // log2 of the largest probability between rescales
 template <int D>
 __global__ __launch_bounds__(kFwd2Threads, 2) void k_attn_fwd(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * DTile<D>::BYTES];   // [stage][K, V]
@@ -300,7 +303,9 @@ __global__ __launch_bounds__(kFwd2Threads, 2) void k_attn_fwd(AttnArgs a) {
   const int64_t rest = blockIdx.x % per;
   const int64_t b = rest / a.n_q;
   const int h = (int)(rest % a.n_q), hk = h / (a.n_q / a.n_kv);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
+  // (the wave index in a scalar register, so that the direct loads' LDS destinations are scalar)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), g = lane >> 4,
+            col = lane & 15;
   const int S = (int)a.S;
   const int wq0 = qb * kFwdQ + 16 * NG * wave;     // this wave's first query
   const int64_t seq0 = b * a.S;
@@ -335,16 +340,24 @@ __global__ __launch_bounds__(kFwd2Threads, 2) void k_attn_fwd(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t rv = rsrc_of(a.v + seq0 * a.ldv + hk * D, a.S * a.ldv * 2);
   constexpr int NW = kFwd2Threads / 64;
   constexpr int SEGW = DTile<D>::SEGS / NW;       // segments of each tile per wave
-  // the wave's share of block kb: segments wave * SEGW .. of the K tile and of the V tile
+  // the wave's share of block kb: segments wave * SEGW .. of the K tile and of the V tile (the
+  // lanes' offsets of a whole block computed once; the last, partial block clamps its rows)
+  uint32_t vk_full[SEGW], vv_full[SEGW];
+#pragma unroll
+  for (int i = 0; i < SEGW; ++i) {
+    vk_full[i] = seg_voff<D>(wave * SEGW + i, lane, a.ldk, kB);
+    vv_full[i] = seg_voff<D>(wave * SEGW + i, lane, a.ldv, kB);
+  }
   auto issue = [&](int kb) {
     const int nvalid = S - kb * kB < kB ? S - kb * kB : kB;
     char *st = smem + (kb & 1) * 2 * DTile<D>::BYTES;
+    const uint32_t sk = (uint32_t)(kb * kB * a.ldk * 2), sv = (uint32_t)(kb * kB * a.ldv * 2);
 #pragma unroll
     for (int i = 0; i < SEGW; ++i) {
       const int sg = wave * SEGW + i;
-      direct_load(rk, st + sg * 1024, seg_voff<D>(sg, lane, a.ldk, nvalid), (uint32_t)(kb * kB * a.ldk * 2));
-      direct_load(rv, st + DTile<D>::BYTES + sg * 1024, seg_voff<D>(sg, lane, a.ldv, nvalid),
-                  (uint32_t)(kb * kB * a.ldv * 2));
+      const bool full = nvalid == kB;
+      direct_load(rk, st + sg * 1024, full ? vk_full[i] : seg_voff<D>(sg, lane, a.ldk, nvalid), sk);
+      direct_load(rv, st + DTile<D>::BYTES + sg * 1024, full ? vv_full[i] : seg_voff<D>(sg, lane, a.ldv, nvalid), sv);
     }
   };
   issue(0);
@@ -380,46 +393,68 @@ __global__ __launch_bounds__(kFwd2Threads, 2) void k_attn_fwd(AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) asm volatile("" ::"v"(kf[t][c]));
     }
-    // online softmax in the exp2 domain, per group
+    // online softmax in the exp2 domain, per group; the causal mask only on blocks that reach past
+    // a query (a uniform branch: the other blocks skip its compares and selects). The block's
+    // maximum is taken over the raw scores (x -> fl32(x c2) is monotone for c2 > 0, so it scales
+    // to the maximum of the scaled ones exactly), and p = 2^fma(s, c2, -m). m is the row's
+    // reference maximum: it moves, and the output and sum are rescaled, only when some row's
+    // maximum exceeds its reference by more than kLazy (so p <= 2^kLazy in between).
     const int key0 = kb * kB + 4 * g;
-    bool moved = false;
-    float alpha[NG];
+    float mxs[NG];
+    auto block_max = [&](auto masked) {
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (decltype(masked)::value) {
+              if (key0 + 16 * tt + e > qis[u]) s[u][tt][e] = -INFINITY;
+            }
+            mx = fmaxf(mx, s[u][tt][e]);
+          }
+        mxs[u] = mx;
+      }
+    };
+    if (diag)
+      block_max(std::true_type{});
+    else
+      block_max(std::false_type{});
+    bool grow = false;
+    float m_cand[NG];
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = s[u][tt][e] * c2;
-          if (diag && key0 + 16 * tt + e > qis[u]) x = -INFINITY;
-          s[u][tt][e] = x;
-          mx = fmaxf(mx, x);
-        }
+      float mx = mxs[u];
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m[u], mx);
-      alpha[u] = ex2(m[u] - m_new);
+      m_cand[u] = fmaxf(m[u], mx * c2);
+      grow = grow || m_cand[u] > m[u] + kLazy;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        const float alpha = ex2(m[u] - m_cand[u]);
+        l[u] *= alpha;
+        m[u] = m_cand[u];
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) acc[u][j] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const float nm = -m[u];
       float rs = 0.0f;
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s[u][tt][e] = ex2(s[u][tt][e] - m_new);
+          s[u][tt][e] = ex2(__builtin_fmaf(s[u][tt][e], c2, nm));
           rs += s[u][tt][e];
         }
       rs += __shfl_xor(rs, 16);
       rs += __shfl_xor(rs, 32);
-      l[u] = l[u] * alpha[u] + rs;
-      m[u] = m_new;
-      moved = moved || alpha[u] != 1.0f;
-    }
-    // rescale only when some lane's running max moved (multiplying by exactly 1 changes nothing)
-    if (__builtin_amdgcn_ballot_w64(moved) != 0) {
-#pragma unroll
-      for (int u = 0; u < NG; ++u)
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j) acc[u][j] *= alpha[u];
+      l[u] += rs;
     }
     // O^T += V^T P^T over the block's 64 keys (two reduction steps of 32); V^T fragments come
     // from the row-major V tile by transpose reads and serve both groups
@@ -509,7 +544,9 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
   const int part = (int)(rest % nsplit);
   const int64_t b = rest / nsplit / a.n_kv;
   const int hk = (int)(rest / nsplit % a.n_kv), grp = a.n_q / a.n_kv, hpw = grp / nsplit;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
+  // (the wave index in a scalar register, so that the direct loads' LDS destinations are scalar)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), g = lane >> 4,
+            col = lane & 15;
   const int S = (int)a.S;
   const int k_in_seq = kb * kB + 16 * wave + col;
   const int64_t seq0 = b * a.S;
@@ -535,16 +572,24 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
   // iteration it = hh * (nb - kb) + (qb - kb) visits query head hk * grp + part * hpw + hh, query
   // block qb
   const int nqb = nb - kb, n_it = hpw * nqb;
+  uint32_t vq_full[SEGW], vd_full[SEGW];     // the lanes' offsets within a whole block
+#pragma unroll
+  for (int i = 0; i < SEGW; ++i) {
+    vq_full[i] = seg_voff<D>(wave * SEGW + i, lane, a.ldq, kB);
+    vd_full[i] = seg_voff<D>(wave * SEGW + i, lane, a.lddo, kB);
+  }
   auto issue = [&](int it) {
     const int hh = it / nqb, qb = kb + it % nqb, h = hk * grp + part * hpw + hh;
     const int nvalid = S - qb * kB < kB ? S - qb * kB : kB;
+    const bool full = nvalid == kB;
     char *st = smem + (it & 1) * STAGE;
 #pragma unroll
     for (int i = 0; i < SEGW; ++i) {
       const int sg = wave * SEGW + i;
-      direct_load(rq, st + sg * 1024, seg_voff<D>(sg, lane, a.ldq, nvalid) + h * D * 2,
+      direct_load(rq, st + sg * 1024, (full ? vq_full[i] : seg_voff<D>(sg, lane, a.ldq, nvalid)) + h * D * 2,
                   (uint32_t)(qb * kB * a.ldq * 2));
-      direct_load(rd, st + DTile<D>::BYTES + sg * 1024, seg_voff<D>(sg, lane, a.lddo, nvalid) + h * D * 2,
+      direct_load(rd, st + DTile<D>::BYTES + sg * 1024,
+                  (full ? vd_full[i] : seg_voff<D>(sg, lane, a.lddo, nvalid)) + h * D * 2,
                   (uint32_t)(qb * kB * a.lddo * 2));
     }
     if (wave < 2) {   // the rows' lse (wave 0) and D (wave 1), 4 bytes per lane
@@ -599,18 +644,27 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_kv(AttnArgs a) {
     }
     // P and dS = P (dP - D); queries before the key (first block) or past S (padding rows of the
     // last block, which hold copies of row S - 1) contribute nothing
+    // (the masked form only on those blocks: a uniform branch)
     const int q0 = qb * kB + 4 * g;
     const bool edge = qb == kb || qb * kB + kB > S;
+    auto probs = [&](auto masked) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int qi = 16 * tt + 4 * g + e;
-        float p = ex2(s[tt][e] * c2 - lse_s[qi] * kLog2e);
-        if (edge && (q0 + 16 * tt + e < k_in_seq || q0 + 16 * tt + e >= S)) p = 0.0f;
-        s[tt][e] = p;
-        dp[tt][e] = p * (dp[tt][e] - dot_s[qi]);
-      }
+        for (int e = 0; e < 4; ++e) {
+          const int qi = 16 * tt + 4 * g + e;
+          float p = ex2(s[tt][e] * c2 - lse_s[qi] * kLog2e);
+          if constexpr (decltype(masked)::value) {
+            if (q0 + 16 * tt + e < k_in_seq || q0 + 16 * tt + e >= S) p = 0.0f;
+          }
+          s[tt][e] = p;
+          dp[tt][e] = p * (dp[tt][e] - dot_s[qi]);
+        }
+    };
+    if (edge)
+      probs(std::true_type{});
+    else
+      probs(std::false_type{});
     // dV^T += dO^T P,  dK^T += Q^T dS  (reduction over the block's 64 queries, in two steps)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -710,7 +764,9 @@ __global__ __launch_bounds__(kFwdQ / NG * 4) void k_attn_bwd_q(AttnArgs a) {
   const int64_t rest = blockIdx.x % per;
   const int64_t b = rest / a.n_q;
   const int h = (int)(rest % a.n_q), hk = h / (a.n_q / a.n_kv);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
+  // (the wave index in a scalar register, so that the direct loads' LDS destinations are scalar)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), g = lane >> 4,
+            col = lane & 15;
   const int S = (int)a.S;
   const int wq0 = qb * kFwdQ + 16 * NG * wave;     // this wave's first query
   const int64_t seq0 = b * a.S;
@@ -789,17 +845,26 @@ __global__ __launch_bounds__(kFwdQ / NG * 4) void k_attn_bwd_q(AttnArgs a) {
         asm volatile("" ::"v"(va[c]));
       }
     }
+    // (the causal mask only on blocks that reach past a query: a uniform branch)
     const int key0 = kb * kB + 4 * g;
+    auto dscores = [&](auto masked) {
 #pragma unroll
-    for (int u = 0; u < NG; ++u)
+      for (int u = 0; u < NG; ++u)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float p = ex2(s[u][tt][e] * c2 - lse2[u]);
-          if (diag && key0 + 16 * tt + e > qis[u]) p = 0.0f;
-          dp[u][tt][e] = p * (dp[u][tt][e] - dq_dot[u]);
-        }
+          for (int e = 0; e < 4; ++e) {
+            float p = ex2(s[u][tt][e] * c2 - lse2[u]);
+            if constexpr (decltype(masked)::value) {
+              if (key0 + 16 * tt + e > qis[u]) p = 0.0f;
+            }
+            dp[u][tt][e] = p * (dp[u][tt][e] - dq_dot[u]);
+          }
+    };
+    if (diag)
+      dscores(std::true_type{});
+    else
+      dscores(std::false_type{});
     // dQ^T += K^T dS^T over the block's 64 keys (two steps of 32); K^T fragments by transpose
     // reads of the row-major K tile, serving every group
 #pragma unroll
