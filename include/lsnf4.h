@@ -16,7 +16,7 @@
  *    (frozen base plus a thin pair of trainable matrices), @2:19-2:29 (NF4 and the second
  *    quantisation pass over the block constants), @7:11-7:32 (one layer at a time is copied
  *    into a small on-card buffer on a separate stream while the previous layer computes;
- *    each layer is read twice per step, forward and backward recompute).
+ *    every layer crosses the host link two times in a step: forward and backward recompute).
  *  - "An 8B Fine-Tune Now Fits in 4 GB of VRAM": layers stream through pre-allocated device
  *    buffers; only the adapters and their gradients stay resident.
  *  - Soup v0.73.0 benchmarks README, reading conventions: the fit decision refuses instead
@@ -520,9 +520,9 @@ lsn_status attention_bwd_rope(int64_t n_seq, int64_t S, int32_t n_q, int32_t n_k
  *                device address; a layer not prefetched is prefetched first (a miss).
  *   release(l)   records the slot's release event on the compute stream; the slot may be
  *                refilled only after that event. Releasing a layer not held: LSN_E_STATE.
- * Every visit copies the layer again (each layer is read twice per step) unless
+ * Every visit copies the layer again (two host reads of every layer per step) unless
  * LSN_POOL_KEEP_AT_TURN is set, in which case a layer still in a free slot is reused.
- * Refusal (Soup benchmarks README: the fit decision refuses rather than warns): the slots are
+ * Refusal (Soup benchmarks README, reading conventions: a run that does not fit is stopped): the slots are
  * caller memory, so whether n_slots x slot_bytes fits in free device memory is decided (and
  * refused) by the caller before it allocates them; register returns LSN_E_NOFIT for an image
  * larger than slot_bytes. Nothing ever spills to host-mapped memory.

@@ -4,7 +4,7 @@
 // "Can You Fine-Tune a 27B Model on a Laptop? (I Did the Math)", transcript @7:11-7:32: the
 // frozen base sits in host RAM; one decoder layer at a time is copied into a small on-card
 // buffer on a separate stream, so the copy lands while the previous layer computes; each
-// layer is read twice per step (forward, and the backward's recompute). "An 8B Fine-Tune Now
+// layer crosses the host link two times in a step (forward, and the backward's recompute). "An 8B Fine-Tune Now
 // Fits in 4 GB of VRAM": the buffers are pre-allocated. "Exact Layer Streaming", Abstract:
 // the silent wrong-gradient defect at large layer sizes was aliasing, not a race; the audit
 // below checks that every visit reads exactly its own layer's bytes.

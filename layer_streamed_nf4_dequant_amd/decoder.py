@@ -5,8 +5,8 @@ head, and cross-entropy on next-token labels, forward and backward.
 "Exact Layer Streaming", Abstract, and "An 8B Fine-Tune Now Fits in 4 GB of VRAM": the decoder
 layers stream through a small pool of device slots from host RAM; only the adapters, their
 gradients, the embedding and the output head stay resident ("Can You Fine-Tune a 27B Model on a
-Laptop?", transcript @7:42-7:55); each layer is read twice per step, forward and the backward's
-recompute (transcript @7:32). The layer is the Llama-3.1 / Qwen2.5 decoder layer, whose formulas
+Laptop?", transcript @7:42-7:55); every layer crosses the host link two times in a step, for the
+forward and again for the backward's recompute (transcript @7:32). The layer is the Llama-3.1 / Qwen2.5 decoder layer, whose formulas
 the pages do not print (the published definitions):
 
     n1 = RMSNorm(x; g1);  q, k, v = LoRA projections of n1;  RoPE on q and k

@@ -4,8 +4,8 @@ streamed through a small device pool.
 
 "Can You Fine-Tune a 27B Model on a Laptop? (I Did the Math)", transcript @7:11-7:32: the
 frozen base sits in host RAM, one decoder layer at a time is copied into a small on-card
-buffer on a separate stream while the previous layer computes, and each layer is read twice
-per step (forward, and the backward's recompute). "Exact Layer Streaming", Abstract: the
+buffer on a separate stream while the previous layer computes, and every layer crosses the
+host link two times in a step (for the forward, and again for the backward's recompute). "Exact Layer Streaming", Abstract: the
 streamed run must be bit-identical to a resident run of the same numerics, forward and every
 LoRA gradient checked separately; the pages' own probe deletes every host-to-device byte.
 
@@ -116,7 +116,7 @@ def choose_source(cfg: StackConfig, source: str, host_budget: int | None = None,
                   layers=None) -> str:
     """The host tier of the frozen base ("An 8B Fine-Tune Now Fits in 4 GB of VRAM", the adoption
     settings: the stream source picks RAM when the images fit and NVMe when they do not; "Soup
-    v0.73.0 benchmarks README", reading conventions: a fit decision refuses rather than warns).
+    v0.73.0 benchmarks README", reading conventions: a run that does not fit is stopped, not merely warned about).
     source "ram" or "file" is taken as given; "auto" picks "ram" when every pinned image fits
     the host budget (default: MemAvailable), else "file" when its bounce buffers fit the budget
     and the images fit the free disk space, else raises MemoryError before anything is
