@@ -8,15 +8,17 @@
 // and the backward dV = P^T dO, dS = P (dO V^T - D), D_i = dO_i.O_i, dQ = scale dS K,
 // dK = scale dS^T Q (dK, dV of a shared head summed over its query heads).
 //
-// Layout of the work (all kernels 4 waves; a wave owns 16 rows of its block):
+// Layout of the work (forward: 4 waves of 32 queries as two groups of 16; dK/dV: 4 waves of 16
+// keys; dQ: 8 waves of 16 queries):
 //  * one MFMA lane column = one query (forward, dQ) or one key (dK/dV), so the softmax row
 //    statistics and the rescaling stay inside a lane; the row max and sum need two shuffles;
 //  * scores are computed transposed where that keeps the probabilities in registers as the
 //    next product's operand: the MFMA reduction index k = 8 g + i (lane group g = lane / 16)
 //    is mapped to rows 4 g + i (i < 4) and 16 + 4 g + i - 4 (i >= 4) of a 32-row step on both
 //    operands, which is the register layout of two accumulator tiles;
-//  * the operand that has to be read along the other dimension (V in the forward, Q, dO and K
-//    in the backward) is staged in LDS transposed as well, by 8x8 register transposes.
+//  * K, V, Q and dO blocks are staged row-major in LDS by direct-to-LDS loads, and the operand
+//    that has to be read along the other dimension (V in the forward, Q, dO and K in the
+//    backward) comes from the same tile by the gfx950 LDS transpose read.
 // Every sum runs in a fixed order and no kernel uses atomics: the results depend only on the
 // inputs. Keys and queries at or past S read as zeros and are never stored.
 
