@@ -12,6 +12,10 @@
 //   w = bf16_RNE( fl32( q[code] * fl32( fl32(v/127 * s2) + mu ) ) ).
 // Every visit re-dequantises from the bytes the descriptor points at; nothing is cached.
 //
+// Two kernels: k_gemm_direct (further down: every bf16-weight product, and the forward of NF4
+// weights whose arrays are aligned for direct loads, decoded in the kernel) and k_gemm, the
+// register-staged kernel described here, which serves NF4 weights in the input-gradient product
+// (the NN layout) and in the forward when their arrays are not aligned for direct loads.
 // Tiling: one 256-thread workgroup (4 waves, 2 x 2) computes a 256 x 256 output tile; each
 // wave owns 128 x 128 (4 x 4 MFMA 32x32x16 tiles, 256 fp32 accumulators per lane). K-steps of
 // 64 (one NF4 block per W row) are double-buffered in LDS: the global loads of step k+1 are in
@@ -460,7 +464,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(GemmArgs a) {
 }
 
 // =============================================================================================
-// Direct-load NT GEMM (both operands bf16 and K-contiguous): out_seg = act W_seg^T (+ LoRA term)
+// Direct-load NT GEMM (both operands K-contiguous; W bf16, or NF4 decoded into the stage as
+// described further down): out_seg = act W_seg^T (+ LoRA term)
 // for up to kMaxSegs output segments that share the activation (e.g. q, k, v, gate and up of a
 // layer read the same input). K-steps of 64 stream through two LDS stages (64 KB each:
 // 256 rows x 128 B per operand); buffer_load...lds fills the next stage while the matrix cores
