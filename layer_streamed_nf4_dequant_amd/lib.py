@@ -94,8 +94,7 @@ def load():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
-                          "(or python -m layer_streamed_nf4_dequant_amd.build)")
+        raise ImportError(f"{LIB_PATH} is not built: run python -m layer_streamed_nf4_dequant_amd.build")
     # One HIP runtime per process: torch ships its own copy of libamdhip64 under the same soname
     # as the system one this library links. Loaded after torch, the library binds to torch's
     # copy; loaded first, it would pull in the system copy and torch would later load its own,
