@@ -327,6 +327,50 @@ def decoder_figure(cfg, vocab: int = 128256, steps: int = 3, modes=("streamed", 
     return out
 
 
+def gemm_vs_hipblaslt(cfg, iters: int = 5):
+    """Our forward GEMM (bf16 weights, with the LoRA term) against hipBLASLt (torch.matmul on the
+    same X and W, no LoRA term) on the q (H -> H), gate (H -> inter) and down (inter -> H) shapes
+    at the configuration's T, for kernel traces and byte counters of the two side by side. A
+    1 GiB device-to-device copy runs first (a plain copy kernel of known size, to scale the
+    hardware byte counters). Each product runs `iters` times back to back, ours first; returns
+    per shape the two mean times in microseconds (HIP events) and TFLOP/s."""
+    import torch
+    from layer_streamed_nf4_dequant_amd import inputs, lib
+    T, H, I, r = cfg.T, cfg.hidden, cfg.inter, cfg.r
+    bf = dict(dtype=torch.bfloat16)
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    torch.empty_like(src).copy_(src)
+    del src
+    key = ("gemm vs hipblaslt", cfg.name)
+    out = {}
+    for name, K, N in (("q", H, H), ("gate", H, I), ("down", I, H)):
+        X = inputs.device_normal((T, K), 1.0, 0, *key, name, "X", **bf)
+        W = inputs.device_normal((N, K), 0.02, 0, *key, name, "W", **bf)
+        A = inputs.device_normal((r, K), 0.01, 0, *key, name, "A", **bf)
+        B = inputs.device_normal((N, r), 0.01, 0, *key, name, "B", **bf)
+        U = inputs.device_normal((T, r), 1.0, 0, *key, name, "U", **bf)
+        Y = torch.empty((T, N), **bf, device="cuda")
+        desc = lib.linear_desc(T, K, N, r, 2.0, W, A, B)
+        Wt = W.t()
+        res = {}
+        for who, fn in (("ours", lambda: lib.lora_linear_fwd(desc, X, Y, U, adapters=lib.ADAPTERS_U_READY)),
+                        ("hipblaslt", lambda: torch.matmul(X, Wt))):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / iters
+            flop = 2 * T * K * N + (2 * T * r * N if who == "ours" else 0)
+            res[who] = {"us": round(us, 1), "TFLOPs": round(flop / (us * 1e-6) / 1e12, 1)}
+        out[f"{name} {K}->{N}"] = res
+        del X, W, A, B, U, Y, desc, Wt
+    return out
+
+
 def main() -> None:
     from layer_streamed_nf4_dequant_amd import configs
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
@@ -335,9 +379,13 @@ def main() -> None:
     ap.add_argument("--decoder", action="store_true",
                     help="time the whole decoder training step (streamed, then resident) instead")
     ap.add_argument("--steps", type=int, default=3, help="timed decoder steps per mode")
+    ap.add_argument("--gemm-vs-hipblaslt", action="store_true",
+                    help="run the forward GEMM and hipBLASLt on the q, gate and down shapes instead")
     args = ap.parse_args()
     cfg = getattr(configs, args.config)
-    if args.decoder:
+    if args.gemm_vs_hipblaslt:
+        print(json.dumps({"gemm_vs_hipblaslt": gemm_vs_hipblaslt(cfg)}), flush=True)
+    elif args.decoder:
         print(json.dumps({"decoder_step": decoder_figure(cfg, steps=args.steps)}), flush=True)
     else:
         print(json.dumps({"glue": glue_figure(cfg, args.iters), "fused_glue": fused_glue_figure(cfg),
