@@ -105,6 +105,47 @@ def test_attention_parity(gpu, n_seq, S, n_q, n_kv, d, qs):
         assert e <= 1e-2, f"{n}: rel L2 {e:.2e}"
 
 
+def test_attention_growing_row_maxima(gpu):
+    """Scores that climb along the keys: over the first half of the sequence each 64-key block
+    lifts a row's maximum by about 3 in log2 units, which the forward absorbs without rescaling
+    its output (the probabilities stay below 2^8 until the maximum has moved by more than 8),
+    and over the second half by about 12 per block, a rescale at every block. o and lse against
+    the oracle at the usual bars, and dV = P^T dO, whose probabilities the backward rebuilds from
+    that lse. (dQ and dK are not compared on this input: its keys are nearly parallel and grow
+    along the sequence, so dQ = scale dS K is a difference of terms about 3000 times its size,
+    and rounding dS to bf16 for the matrix cores alone moves it by 6% rel-L2 in an fp64
+    computation.)"""
+    import torch
+    n_seq, S, n_q, n_kv, d = 1, 640, 2, 1, 64
+    print(f"case: attention with growing row maxima S={S} n_q={n_q} d={d}", flush=True)
+    c = AttnCase(n_seq, S, n_q, n_kv, d, seed=11)
+    key = ("attn growing maxima",)
+    u = inputs.host_normal((d,), 1.0, 11, *key, "u").astype(np.float64)
+    u /= np.linalg.norm(u)
+    j = np.arange(S, dtype=np.float64)
+    # log2-domain growth per block: 64 * slope * |q.u| * scale * log2(e), with |q.u| = 8 and
+    # scale = 1/8: about 92 * slope
+    f = np.where(j < 320, 0.0325 * j, 0.0325 * 320 + 0.13 * (j - 320))
+    q = np.tile(8.0 * u, (S, n_q))
+    k = f[:, None] * u[None, :] + inputs.host_normal((S, d), 0.05, 11, *key, "k")
+    v = inputs.host_normal((S, d), 1.0, 11, *key, "v")
+    c.qkv = inputs.to_bf16_bits(np.concatenate([q, k, v], axis=1).astype(np.float32))
+    c.qkvd = dev_bf16(c.qkv, torch)
+    obuf, o, lse = c.gpu_fwd()
+    g = c.gpu_bwd(o, lse)
+    torch.cuda.synchronize()
+    qh, kh, vh = c.host_qkv()
+    O_ref, L_ref = oatt.forward(qh, kh, vh, n_seq, n_q, n_kv, d)
+    err_o = olora.rel_l2(host(o), O_ref)
+    assert L_ref.max() > 40.0          # the scores did climb (lse in natural-log units)
+    assert err_o <= 5e-3, f"o rel L2 {err_o:.2e}"
+    assert np.abs(lse.cpu().numpy() - L_ref).max() <= 2e-4
+    _, _, dv_ref = oatt.backward(qh, kh, vh, f32(c.dO), n_seq, n_q, n_kv, d)
+    e = olora.rel_l2(host(c.slices(g)[2]), dv_ref)
+    print(f"o {err_o:.2e} dv {e:.2e}")
+    assert e <= 1e-2, f"dv: rel L2 {e:.2e}"
+
+
 def test_attention_bitwise_reproducible(gpu):
     import torch
     c = AttnCase(2, 257, 8, 2, 128, 1.0, seed=3)
