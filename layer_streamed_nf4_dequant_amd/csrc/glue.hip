@@ -44,30 +44,30 @@ __device__ __forceinline__ float team_sum(float v, float *scratch) {
 }
 
 // y = bf16( (x * rstd) * g ), rstd = 1 / sqrt(mean x^2 + eps). One workgroup of NT threads per
-// row (NT sized to the row: 8 values per thread step); the second pass re-reads the row (L2).
+// row (NT sized to the row: 8 values per thread step). A row of at most kRmsChunks chunks per
+// thread is held in registers, with the gain requested beside it before the reduction, so the
+// second pass reads nothing; a longer row is re-read (L2) in the second pass. Both forms sum in
+// the same order.
+constexpr int kRmsChunks = 2;
 template <int NT>
 __global__ __launch_bounds__(NT) void k_rmsnorm_fwd(int64_t H, const uint16_t *__restrict__ x,
                                                     const uint16_t *__restrict__ g, float eps,
                                                     uint16_t *__restrict__ y, float *__restrict__ rstd) {
   __shared__ float scratch[NT / 64];
   const int64_t row = blockIdx.x;
+  const int64_t nc = H / 8;
   const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x + row * H);
-  float ss = 0.0f;
-  for (int64_t c = threadIdx.x; c < H / 8; c += NT) {
-    const u32x4_t v = xr[c];
+  const u32x4_t *gr = reinterpret_cast<const u32x4_t *>(g);
+  u32x4_t *yr = reinterpret_cast<u32x4_t *>(y + row * H);
+  auto sq8 = [](float ss, const u32x4_t &v) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float f = bf16f((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
       ss = __fadd_rn(ss, __fmul_rn(f, f));
     }
-  }
-  ss = team_sum<NT>(ss, scratch);
-  const float r = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(ss, (float)H), eps)));
-  if (threadIdx.x == 0) rstd[row] = r;
-  const u32x4_t *gr = reinterpret_cast<const u32x4_t *>(g);
-  u32x4_t *yr = reinterpret_cast<u32x4_t *>(y + row * H);
-  for (int64_t c = threadIdx.x; c < H / 8; c += NT) {
-    const u32x4_t v = xr[c], gv = gr[c];
+    return ss;
+  };
+  auto out8 = [](const u32x4_t &v, const u32x4_t &gv, float r) {
     u32x4_t o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -80,12 +80,45 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_fwd(int64_t H, const uint16_t *_
       }
       o[q] = pack_bf16x2(t[0], t[1]);
     }
-    yr[c] = o;
+    return o;
+  };
+  auto rstd_of = [&](float ss) { return __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(ss, (float)H), eps))); };
+  if (nc <= (int64_t)NT * kRmsChunks) {
+    u32x4_t xv[kRmsChunks], gv[kRmsChunks];
+#pragma unroll
+    for (int i = 0; i < kRmsChunks; ++i) {
+      const int64_t c = threadIdx.x + (int64_t)i * NT;
+      if (c < nc) {
+        xv[i] = xr[c];
+        gv[i] = gr[c];
+      }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRmsChunks; ++i)
+      if (threadIdx.x + (int64_t)i * NT < nc) ss = sq8(ss, xv[i]);
+    ss = team_sum<NT>(ss, scratch);
+    const float r = rstd_of(ss);
+    if (threadIdx.x == 0) rstd[row] = r;
+#pragma unroll
+    for (int i = 0; i < kRmsChunks; ++i) {
+      const int64_t c = threadIdx.x + (int64_t)i * NT;
+      if (c < nc) yr[c] = out8(xv[i], gv[i], r);
+    }
+    return;
   }
+  float ss = 0.0f;
+  for (int64_t c = threadIdx.x; c < nc; c += NT) ss = sq8(ss, xr[c]);
+  ss = team_sum<NT>(ss, scratch);
+  const float r = rstd_of(ss);
+  if (threadIdx.x == 0) rstd[row] = r;
+  for (int64_t c = threadIdx.x; c < nc; c += NT) yr[c] = out8(xr[c], gr[c], r);
 }
 
 // dx = rstd (g dy) - x rstd^3 (sum_j g_j dy_j x_j) / H; dy and dx fp32, dx stored or added to.
-// One workgroup of NT threads per row.
+// One workgroup of NT threads per row; a row of at most kRmsChunks chunks per thread is held in
+// registers (x, g, dy, and the dx being added to, all requested before the reduction), a longer
+// one re-read in the second pass. Both forms sum in the same order.
 template <int NT>
 __global__ __launch_bounds__(NT) void k_rmsnorm_bwd(int64_t H, const uint16_t *__restrict__ x,
                                                     const uint16_t *__restrict__ g, const float *__restrict__ rstd,
@@ -93,27 +126,24 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_bwd(int64_t H, const uint16_t *_
                                                     int accumulate, uint16_t *__restrict__ dx16) {
   __shared__ float scratch[NT / 64];
   const int64_t row = blockIdx.x;
+  const int64_t nc = H / 8;
   const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x + row * H);
   const floatx4_t *dr = reinterpret_cast<const floatx4_t *>(dy + row * H);
   const u32x4_t *gr = reinterpret_cast<const u32x4_t *>(g);
-  float dot = 0.0f;
-  for (int64_t c = threadIdx.x; c < H / 8; c += NT) {
-    const u32x4_t v = xr[c], gv = gr[c];
-    const floatx4_t d0 = dr[2 * c], d1 = dr[2 * c + 1];
+  floatx4_t *o = reinterpret_cast<floatx4_t *>(dx + row * H);
+  auto dot8 = [](float dot, const u32x4_t &v, const u32x4_t &gv, const floatx4_t &d0, const floatx4_t &d1) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int q = e >> 1, h = 16 * (e & 1);
       const float gd = __fmul_rn(bf16f((uint16_t)(gv[q] >> h)), e < 4 ? d0[e & 3] : d1[e & 3]);
       dot = __fadd_rn(dot, __fmul_rn(gd, bf16f((uint16_t)(v[q] >> h))));
     }
-  }
-  dot = team_sum<NT>(dot, scratch);
-  const float r = rstd[row];
-  const float k = __fdiv_rn(__fmul_rn(__fmul_rn(__fmul_rn(r, r), r), dot), (float)H);
-  floatx4_t *o = reinterpret_cast<floatx4_t *>(dx + row * H);
-  for (int64_t c = threadIdx.x; c < H / 8; c += NT) {
-    const u32x4_t v = xr[c], gv = gr[c];
-    const floatx4_t d0 = dr[2 * c], d1 = dr[2 * c + 1];
+    return dot;
+  };
+  // chunk c's gradient, added to `prev` (the stored values) when accumulating, stored (and its
+  // bf16 copy, for the operand that reads it next)
+  auto store8 = [&](int64_t c, const u32x4_t &v, const u32x4_t &gv, const floatx4_t &d0, const floatx4_t &d1,
+                    float r, float k, const floatx4_t (&prev)[2]) {
     float res[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -124,16 +154,59 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_bwd(int64_t H, const uint16_t *_
     floatx4_t cur[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      cur[half] = accumulate ? o[2 * c + half] : floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        cur[half][e] = accumulate ? __fadd_rn(cur[half][e], res[4 * half + e]) : res[4 * half + e];
+        cur[half][e] = accumulate ? __fadd_rn(prev[half][e], res[4 * half + e]) : res[4 * half + e];
       o[2 * c + half] = cur[half];
     }
-    if (dx16)   // the bf16 copy of the stored gradient, for the operand that reads it next
+    if (dx16)
       reinterpret_cast<u32x4_t *>(dx16 + row * H)[c] =
           u32x4_t{pack_bf16x2(cur[0][0], cur[0][1]), pack_bf16x2(cur[0][2], cur[0][3]),
                   pack_bf16x2(cur[1][0], cur[1][1]), pack_bf16x2(cur[1][2], cur[1][3])};
+  };
+  const float r = rstd[row];
+  auto k_of = [&](float dot) { return __fdiv_rn(__fmul_rn(__fmul_rn(__fmul_rn(r, r), r), dot), (float)H); };
+  if (nc <= (int64_t)NT * kRmsChunks) {
+    u32x4_t xv[kRmsChunks], gv[kRmsChunks];
+    floatx4_t dv[kRmsChunks][2], pv[kRmsChunks][2];
+#pragma unroll
+    for (int i = 0; i < kRmsChunks; ++i) {
+      const int64_t c = threadIdx.x + (int64_t)i * NT;
+      if (c < nc) {
+        xv[i] = xr[c];
+        gv[i] = gr[c];
+        dv[i][0] = dr[2 * c];
+        dv[i][1] = dr[2 * c + 1];
+        if (accumulate) {
+          pv[i][0] = o[2 * c];
+          pv[i][1] = o[2 * c + 1];
+        }
+      }
+    }
+    float dot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRmsChunks; ++i)
+      if (threadIdx.x + (int64_t)i * NT < nc) dot = dot8(dot, xv[i], gv[i], dv[i][0], dv[i][1]);
+    dot = team_sum<NT>(dot, scratch);
+    const float k = k_of(dot);
+#pragma unroll
+    for (int i = 0; i < kRmsChunks; ++i) {
+      const int64_t c = threadIdx.x + (int64_t)i * NT;
+      if (c < nc) store8(c, xv[i], gv[i], dv[i][0], dv[i][1], r, k, pv[i]);
+    }
+    return;
+  }
+  float dot = 0.0f;
+  for (int64_t c = threadIdx.x; c < nc; c += NT) dot = dot8(dot, xr[c], gr[c], dr[2 * c], dr[2 * c + 1]);
+  dot = team_sum<NT>(dot, scratch);
+  const float k = k_of(dot);
+  for (int64_t c = threadIdx.x; c < nc; c += NT) {
+    floatx4_t prev[2] = {floatx4_t{0.0f, 0.0f, 0.0f, 0.0f}, floatx4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+    if (accumulate) {
+      prev[0] = o[2 * c];
+      prev[1] = o[2 * c + 1];
+    }
+    store8(c, xr[c], gr[c], dr[2 * c], dr[2 * c + 1], r, k, prev);
   }
 }
 
