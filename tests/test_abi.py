@@ -109,3 +109,29 @@ def test_attention_argument_errors_without_gpu():
     assert L.attention_bwd_ws_bytes(2, 4, 3, 1, d) == 256
     assert L.attention_bwd_ws_bytes(2, 100, 3, 1, d) == (2 * 100 * 3 * 4 + 255) // 256 * 256
     assert L.attention_bwd_ws_bytes(2, 4, 4, 3, d) == 0
+
+
+def test_lora_argument_errors_without_gpu():
+    """The LoRA entry points refuse an empty token batch, a reduction or output width that is
+    not a multiple of 64 and an unsupported rank before any device call (the pointers here are
+    never dereferenced)."""
+    L = lib.load()
+    p = 1 << 20   # a 16-byte aligned stand-in address
+
+    def desc(T, K, N, r):
+        return lib.LoraLinearDesc(T, K, N, r, 2.0, lib.WeightDesc(lib.W_BF16, lib.NF4Desc(), p), p, p)
+
+    for (T, K, N, r), msg in (((0, 128, 128, 16), b"T >= 1"), ((64, 100, 128, 16), b"multiples of 64"),
+                              ((64, 128, 96, 16), b"multiples of 64"), ((64, 128, 128, 12), b"rank r")):
+        d = desc(T, K, N, r)
+        assert L.lora_linear_fwd(ctypes.byref(d), lib.ADAPTERS_ON, p, p, p, p, 1 << 30, None) == lib.LSN_E_ARG
+        assert msg in L.lsn_last_error()
+        assert L.lora_linear_bwd(ctypes.byref(d), p, p, p, p, lib.DX_BF16_SET, p, p, lib.GRAD_SET, p, 1 << 30,
+                                 None) == lib.LSN_E_ARG
+        assert msg in L.lsn_last_error()
+        assert L.lora_linear_bwd_noalloc(ctypes.byref(d), p, p, p, p, lib.DX_BF16_SET, p, p, lib.GRAD_SET,
+                                         None) == lib.LSN_E_ARG
+        assert msg in L.lsn_last_error()
+    assert L.lora_down(0, 128, p, 1, (ctypes.c_void_p * 1)(p), (ctypes.c_int32 * 1)(16),
+                       (ctypes.c_void_p * 1)(p), None) == lib.LSN_E_ARG
+    assert b"T >= 1" in L.lsn_last_error()
